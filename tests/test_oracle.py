@@ -1,0 +1,347 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test ties one oracle function to something other than itself: a closed
+form, a special case that reduces to a textbook routine (torch's scaled
+dot-product attention in float64), a dense-mask brute force written along a
+different route (tests/brute.py), an invariant, or the pages' own numbers.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import brute
+import oracle
+from sparse_attention_long_fwd_amd import accounting, synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+P = dict(cmp_block=32, cmp_stride=16, sel_block=64, top_n=4, n_init=1, n_local=2, window=128, scale=0.0)
+
+
+def rnd(seed, *shape):
+    return synth.normal(seed, shape).numpy().astype(np.float32)
+
+
+def small_params(**kw):
+    p = dict(cmp_block=8, cmp_stride=4, sel_block=16, top_n=4, n_init=1, n_local=2, window=24, scale=0.0)
+    p.update(kw)
+    return p
+
+
+# --------------------------------------------------------------------------- generator
+def test_splitmix64_matches_definition():
+    # The first output of SplitMix64 seeded with 0, and the plain big-int definition.
+    assert synth.splitmix64_reference(0, 1)[0] == 0xE220A8397B1DCDAF
+    for seed in (0, 1, 12345, 2**63 + 7):
+        ref = synth.splitmix64_reference(seed, 257)
+        got = [int(x) & (2**64 - 1) for x in synth.splitmix64_words(seed, 0, 257)]
+        assert got == ref
+    # counter-based: a window starting mid-stream equals the same slice
+    ref = synth.splitmix64_reference(99, 40)
+    got = [int(x) & (2**64 - 1) for x in synth.splitmix64_words(99, 30, 10)]
+    assert got == ref[30:40]
+
+
+def test_box_muller_moments_and_chunking():
+    x = synth.normal(5, (400000,)).numpy()
+    assert abs(x.mean()) < 0.01 and abs(x.std() - 1) < 0.01
+    assert abs(np.mean(x ** 3)) < 0.03 and abs(np.mean(x ** 4) - 3) < 0.05
+    # odd offsets inside a chunk give the same numbers as a whole draw
+    a = synth.normal(6, (11,)).numpy()
+    b = synth.normal(6, (12,)).numpy()
+    assert np.array_equal(a, b[:11])
+
+
+# --------------------------------------------------------------------------- compression
+def test_compress_closed_forms():
+    T, H, D, l, d = 200, 2, 8, 32, 16
+    x = rnd(11, T, H, D)
+    Nc = oracle.num_cmp_blocks(T, l, d)
+    assert Nc == (T - l) // d + 1 == 11
+    for m in (0, 5, 31):
+        w = np.zeros(l, np.float32)
+        w[m] = 1
+        kc = oracle.compress(x, w, l, d)
+        assert np.array_equal(kc, x[m: m + d * Nc: d].astype(np.float64))
+    kc = oracle.compress(x, np.full(l, 1.0 / l, np.float32), l, d)
+    ref = np.stack([x[i * d:i * d + l].astype(np.float64).mean(0) for i in range(Nc)])
+    assert np.allclose(kc, ref, atol=1e-6)  # 1/32 is exact in float32
+    w1, w2 = rnd(12, l), rnd(13, l)
+    lin = oracle.compress(x, w1, l, d) * 2 - oracle.compress(x, w2, l, d) * 3
+    ref = oracle.compress(x, (2.0 * w1.astype(np.float64) - 3.0 * w2).astype(np.float32), l, d)
+    assert np.allclose(lin, ref, atol=1e-5)
+    assert np.allclose(oracle.compress(x, w1, l, d), brute.compress(x, w1, l, d), atol=1e-12)
+    assert oracle.num_cmp_blocks(31, 32, 16) == 0 and oracle.compress(x[:31], w1, l, d).shape[0] == 0
+
+
+# --------------------------------------------------------------------------- compression branch
+def test_cmp_against_brute_force_and_closed_forms():
+    T, Hq, Hkv, D = 150, 4, 2, 16
+    p = small_params()
+    l, d, ls = p["cmp_block"], p["cmp_stride"], p["sel_block"]
+    q, k, v, w = rnd(21, T, Hq, D), rnd(22, T, Hkv, D), rnd(23, T, Hkv, D), rnd(24, l)
+    kc, vc = oracle.compress(k, w, l, d), oracle.compress(v, w, l, d)
+    pos = np.arange(T)
+    s = 1 / math.sqrt(D)
+    o, lse, imp = oracle.cmp_rows(q, pos, kc, vc, Hq, l, d, ls, T, s)
+    Nc = kc.shape[0]
+    mask = (np.arange(Nc)[None] * d + l - 1) <= pos[:, None]
+    Om = brute.overlap_matrix(T, l, d, ls)
+    imp_ref = np.zeros_like(imp)
+    for h in range(Hq):
+        ob, pb = brute.masked_attention(q[:, h].astype(np.float64), kc[:, h // 2], vc[:, h // 2], mask, s)
+        assert np.allclose(o[:, h], ob, atol=1e-12)
+        imp_ref[:, h // 2] += pb @ Om
+    assert np.allclose(imp, imp_ref, atol=1e-12)
+    # rows before the first complete block see nothing
+    assert np.all(o[: l - 1] == 0) and np.all(np.isneginf(lse[: l - 1])) and np.all(imp[: l - 1] == 0)
+    # importance sums to the group size on every row that sees a block
+    G = Hq // Hkv
+    assert np.allclose(imp[l - 1:].sum(-1), G, atol=1e-12)
+    # Q = 0: uniform weights, the mean of the visible compressed values
+    o0, lse0, _ = oracle.cmp_rows(np.zeros_like(q), pos, kc, vc, Hq, l, d, ls, T, s)
+    for t in (l - 1, 77, T - 1):
+        nv = (t + 1 - l) // d + 1
+        assert np.allclose(o0[t, 0], vc[:nv, 0].mean(0), atol=1e-12)
+        assert abs(lse0[t, 0] - math.log(nv)) < 1e-12
+    # constant V = c gives (sum w) * c
+    vconst = np.full_like(v, 0.75)
+    oc, _, _ = oracle.cmp_rows(q, pos, kc, oracle.compress(vconst, w, l, d), Hq, l, d, ls, T, s)
+    assert np.allclose(oc[l - 1:], 0.75 * w.astype(np.float64).sum(), atol=1e-12)
+
+
+def test_importance_weights_and_identity_case():
+    # l = 32, d = 16, ls = 64: block i = 4j-1 .. 4j+3 contributes 1/2, 1, 1, 1, 1/2 to block j
+    Om = brute.overlap_matrix(64 * 6, 32, 16, 64)
+    j = 3
+    assert np.allclose(Om[4 * j - 1: 4 * j + 4, j], [0.5, 1, 1, 1, 0.5])
+    assert np.allclose(Om.sum(1), 1.0)
+    # l = d = ls: compressed blocks are the selection blocks, so imp = sum over heads of p
+    T, Hq, Hkv, D, l = 96, 4, 1, 8, 16
+    q, k, v = rnd(31, T, Hq, D), rnd(32, T, Hkv, D), rnd(33, T, Hkv, D)
+    w = rnd(34, l)
+    kc, vc = oracle.compress(k, w, l, l), oracle.compress(v, w, l, l)
+    pos = np.arange(T)
+    o, lse, imp = oracle.cmp_rows(q, pos, kc, vc, Hq, l, l, l, T, 0.3)
+    Nc = kc.shape[0]
+    psum = np.zeros((T, Nc))
+    for h in range(Hq):
+        z = 0.3 * q[:, h].astype(np.float64) @ kc[:, 0].T
+        vis = (np.arange(Nc)[None] * l + l - 1) <= pos[:, None]
+        psum += np.where(vis, np.exp(z - lse[:, h:h + 1]), 0.0)
+    assert np.allclose(imp[:, 0, :Nc], psum, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- top-n
+def test_topk_worked_example_with_ties():
+    ls, n = 64, 6
+    t = 64 * 12 + 5          # block of t is 12; forced {0, 11, 12}; 3 free places
+    imp = np.zeros((1, 1, 16))
+    imp[0, 0, [1, 2, 3, 4, 5, 6, 7, 13]] = [0.5, 0.9, 0.9, 0.1, 0.9, 0.3, 0.9, 5.0]
+    idx, gap = oracle.topk_rows(imp, np.array([t]), ls, n, 1, 2)
+    # 0.9 is shared by 2, 3, 5, 7: the lower indices win; block 13 lies beyond t
+    assert idx[0, 0].tolist() == [0, 2, 3, 5, 11, 12]
+    assert gap[0, 0] == 0.0
+    # every candidate fits: all blocks up to t, padded
+    idx, gap = oracle.topk_rows(imp, np.array([64 * 3 + 1]), ls, n, 1, 2)
+    assert idx[0, 0].tolist() == [0, 1, 2, 3, -1, -1] and np.isinf(gap[0, 0])
+
+
+def test_topk_against_stable_sort():
+    rng = np.random.default_rng(0)
+    Ns, ls = 40, 16
+    imp = np.round(rng.random((300, 2, Ns)), 1)  # coarse values: many planted ties
+    pos = rng.integers(0, Ns * ls, 300)
+    for n, n_init, n_local in ((4, 1, 2), (8, 2, 1), (16, 1, 2), (40, 1, 2)):
+        idx, gap = oracle.topk_rows(imp, pos, ls, n, n_init, n_local)
+        for r in range(300):
+            for g in range(2):
+                ref = brute.topk(imp[r, g], pos[r], ls, n, n_init, n_local)
+                assert idx[r, g].tolist() == ref
+                jt = pos[r] // ls
+                forced = {j for j in range(jt + 1) if j < n_init or j > jt - n_local}
+                assert forced <= set(idx[r, g].tolist())
+                if n >= jt + 1:
+                    assert sorted(x for x in idx[r, g] if x >= 0) == list(range(jt + 1))
+
+
+# --------------------------------------------------------------------------- selection / window / dense
+def _sdpa(q, k, v, mask, s):
+    qt = torch.from_numpy(q.astype(np.float64))[None]
+    kt = torch.from_numpy(k.astype(np.float64))[None]
+    vt = torch.from_numpy(v.astype(np.float64))[None]
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(mask),
+                                                            scale=s)[0].numpy()
+
+
+def test_dense_is_textbook_causal_attention():
+    T, Hq, Hkv, D = 90, 6, 2, 16
+    q, k, v = rnd(41, T, Hq, D), rnd(42, T, Hkv, D), rnd(43, T, Hkv, D)
+    s = 1 / math.sqrt(D)
+    o, lse = oracle.dense_rows(q, np.arange(T), k, v, s)
+    causal = np.tril(np.ones((T, T), dtype=bool))
+    for h in range(Hq):
+        ref = _sdpa(q[:, h], k[:, h // 3], v[:, h // 3], causal, s)
+        assert np.allclose(o[:, h], ref, atol=1e-12)
+    z = s * q[5, 0].astype(np.float64) @ k[:6, 0].T.astype(np.float64)
+    assert abs(lse[5, 0] - np.log(np.exp(z).sum())) < 1e-12
+
+
+def test_slc_and_swa_reduce_to_dense_and_brute_force():
+    T, Hq, Hkv, D, ls = 130, 4, 1, 8, 16
+    q, k, v = rnd(51, T, Hq, D), rnd(52, T, Hkv, D), rnd(53, T, Hkv, D)
+    pos = np.arange(T)
+    s = 0.4
+    dense, _ = oracle.dense_rows(q, pos, k, v, s)
+    Ns = (T + ls - 1) // ls
+    # every block chosen and a window spanning the sequence: both equal dense causal attention
+    allidx = np.tile(np.arange(Ns, dtype=np.int32), (T, Hkv, 1))
+    o_slc, o_swa = oracle.sparse_rows(q, pos, k, v, allidx, ls, T, s)
+    assert np.allclose(o_slc, dense, atol=1e-12) and np.allclose(o_swa, dense, atol=1e-12)
+    # window 1: the row's own value
+    _, o1 = oracle.sparse_rows(q, pos, k, v, allidx, ls, 1, s, slc=False)
+    assert np.allclose(o1, np.repeat(v[:, :1].astype(np.float64), Hq, 1), atol=1e-15)
+    # random valid selections against a dense block mask
+    rng = np.random.default_rng(3)
+    idx = np.full((T, Hkv, 5), -1, dtype=np.int32)
+    for t in range(T):
+        jt = t // ls
+        cand = sorted(set([0, jt, max(jt - 1, 0)]) | set(rng.integers(0, jt + 1, 2).tolist()))
+        idx[t, 0, :len(cand)] = cand
+    o_slc, o_swa = oracle.sparse_rows(q, pos, k, v, idx, ls, 20, s)
+    u = np.arange(T)
+    sel = np.zeros((T, Ns), bool)
+    for t in range(T):
+        sel[t, idx[t, 0][idx[t, 0] >= 0]] = True
+    causal = u[None] <= pos[:, None]
+    for h in range(Hq):
+        ref, _ = brute.masked_attention(q[:, h].astype(np.float64), k[:, 0].astype(np.float64),
+                                        v[:, 0].astype(np.float64), causal & sel[:, u // ls], s)
+        assert np.allclose(o_slc[:, h], ref, atol=1e-12)
+        band = causal & (u[None] > pos[:, None] - 20)
+        ref = _sdpa(q[:, h], k[:, 0], v[:, 0], band, s)
+        assert np.allclose(o_swa[:, h], ref, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- whole layer
+def _tiny_inputs(seed, T, Hq, Hkv, D, p, lead=0, tail=0):
+    q, k, v = rnd(seed, T, Hq, D), rnd(seed + 1, T, Hkv, D), rnd(seed + 2, T, Hkv, D)
+    w = rnd(seed + 3, p["cmp_block"]) / np.float32(math.sqrt(p["cmp_block"]))
+    g = (1 / (1 + np.exp(-rnd(seed + 4, T, Hq, 3).astype(np.float64)))).astype(np.float32)
+    vid = np.zeros(T, np.uint8)
+    vid[lead:T - tail] = 1
+    return q, k, v, w, g, vid
+
+
+def test_layer_against_brute_force():
+    T, Hq, Hkv, D = 200, 6, 2, 16
+    p = small_params(top_n=5, window=30)
+    q, k, v, w, g, vid = _tiny_inputs(60, T, Hq, Hkv, D, p, lead=20, tail=12)
+    res = oracle.layer(q, k, v, w, w, g, vid, p)
+    ref = brute.layer(q, k, v, w, w, g, vid, p)
+    V = vid.astype(bool)
+    assert np.array_equal(res["idx"][V], ref["idx"][V])
+    for key in ("o_cmp", "o_slc", "o_swa", "imp"):
+        assert np.allclose(res[key][V], ref[key][V], atol=1e-12), key
+    assert np.allclose(res["out"], ref["out"], atol=1e-12)
+
+
+def test_layer_one_hot_gates_and_constant_values():
+    T, Hq, Hkv, D = 160, 4, 2, 8
+    p = small_params()
+    q, k, v, w, g, vid = _tiny_inputs(70, T, Hq, Hkv, D, p, lead=16, tail=16)
+    base = oracle.layer(q, k, v, w, w, g, vid, p)
+    V = vid.astype(bool)
+    for b, key in enumerate(("o_cmp", "o_slc", "o_swa")):
+        gh = np.zeros_like(g)
+        gh[..., b] = 1
+        r = oracle.layer(q, k, v, w, w, gh, vid, p)
+        assert np.allclose(r["out"][V], base[key][V], atol=0)
+        assert np.allclose(r["out"][~V], base["out"][~V], atol=0)  # text rows are ungated
+    c = 1.25
+    r = oracle.layer(q, k, np.full_like(v, c), w, w, g, vid, p)
+    t = np.arange(T)
+    seen = ((t + 1 - p["cmp_block"]) >= 0).astype(np.float64)[:, None]
+    expect = (g[..., 0] * w.astype(np.float64).sum() * seen + g[..., 1] + g[..., 2]) * c
+    assert np.allclose(r["out"][V], np.repeat(expect[V][..., None], D, -1), atol=1e-12)
+    assert np.allclose(r["out"][~V], c, atol=1e-12)
+
+
+def test_layer_text_rows_and_all_text():
+    T, Hq, Hkv, D = 120, 4, 1, 8
+    p = small_params()
+    q, k, v, w, g, vid = _tiny_inputs(80, T, Hq, Hkv, D, p, lead=40, tail=30)
+    res = oracle.layer(q, k, v, w, w, g, vid, p)
+    dense, _ = oracle.dense_rows(q, np.arange(T), k, v, 1 / math.sqrt(D))
+    assert np.allclose(res["out"][~vid.astype(bool)], dense[~vid.astype(bool)], atol=0)
+    res = oracle.layer(q, k, v, w, w, g, np.zeros(T, np.uint8), p)
+    assert np.allclose(res["out"], dense, atol=0)
+
+
+def test_layer_causality_and_head_permutation():
+    T, Hq, Hkv, D = 180, 6, 2, 8
+    p = small_params(top_n=6, window=20)
+    q, k, v, w, g, vid = _tiny_inputs(90, T, Hq, Hkv, D, p, lead=8, tail=8)
+    res = oracle.layer(q, k, v, w, w, g, vid, p)
+    t0 = 101
+    k2, v2, q2 = k.copy(), v.copy(), q.copy()
+    k2[t0 + 1:] += 3.0
+    v2[t0 + 1:] -= 2.0
+    q2[t0 + 1:] *= -1
+    res2 = oracle.layer(q2, k2, v2, w, w, g, vid, p)
+    assert np.array_equal(res["out"][: t0 + 1], res2["out"][: t0 + 1])
+    # permuting the heads inside a GQA group permutes the outputs
+    perm = np.array([2, 0, 1, 5, 3, 4])
+    res3 = oracle.layer(q[:, perm], k, v, w, w, g[:, perm], vid, p)
+    assert np.allclose(res3["out"], res["out"][:, perm], atol=1e-12)
+    assert np.array_equal(res3["idx"], res["idx"])
+
+
+def test_layer_rows_subset_and_q_start():
+    T, Hq, Hkv, D = 150, 4, 2, 8
+    p = small_params()
+    q, k, v, w, g, vid = _tiny_inputs(95, T, Hq, Hkv, D, p)
+    full = oracle.layer(q, k, v, w, w, g, vid, p)
+    rows = np.array([3, 40, 99, 149])
+    sub = oracle.layer(q, k, v, w, w, g, vid, p, rows=rows)
+    assert np.array_equal(sub["out"], full["out"][rows])
+    # decode form: one query row at the last position, precomputed compressed cache
+    last = oracle.layer(q[-1:], k, v, w, w, g[-1:], vid[-1:], p, q_start=T - 1,
+                        kc=full["kc"], vc=full["vc"])
+    assert np.allclose(last["out"][0], full["out"][-1], atol=0)
+
+
+# --------------------------------------------------------------------------- counting
+def test_pair_counts_against_key_lists_and_page_identity():
+    with open(os.path.join(GOLDEN, "page2_attention_counts.json")) as f:
+        page = json.load(f)
+    dense = accounting.dense_causal_pairs(page["tokens"])
+    assert float("%.2g" % dense) == page["dense_attention_computations"]
+    # the pages' own figures are consistent with each other
+    assert abs(100 * (1 - page["videonsa_attention_computations"] / page["dense_attention_computations"])
+               - page["saving_percent"]) < 0.1
+    # closed-form counts equal the number of mask entries the brute force attends
+    wl = synth.Workload(name="t", index=0, dtype="f32", batch=1, kv_len=300, q_len=300, q_start=0,
+                        num_q_heads=2, num_kv_heads=1, head_dim=8, top_n=3, window=40, text_lead=32,
+                        text_tail=20, cmp_block=8, cmp_stride=4, sel_block=16)
+    c = accounting.pair_counts(wl)
+    T = 300
+    pos = np.arange(T)
+    vid = (pos >= 32) & (pos < T - 20)
+    u = np.arange(T)
+    causal = u[None] <= pos[:, None]
+    Nc = (T - 8) // 4 + 1
+    cmask = (np.arange(Nc)[None] * 4 + 7) <= pos[:, None]
+    assert c["cmp"] == 2 * cmask[vid].sum()
+    assert c["swa"] == 2 * (causal & (u[None] > pos[:, None] - 40))[vid].sum()
+    assert c["text"] == 2 * causal[~vid].sum()
+    imp = np.random.default_rng(1).random((T, 1, (T + 15) // 16))
+    idx, _ = oracle.topk_rows(imp, pos, 16, 3, 1, 2)
+    nslc = 0
+    for t in pos[vid]:
+        sel = set(idx[t, 0][idx[t, 0] >= 0].tolist())
+        nslc += sum(1 for x in range(t + 1) if x // 16 in sel)
+    assert c["slc"] == 2 * nslc
