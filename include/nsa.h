@@ -1,0 +1,190 @@
+/*
+ * nsa.h -- C ABI of the MI355X (gfx950) forward pass of VideoNSA's hybrid
+ * attention layer: dense causal attention for text rows, Native Sparse
+ * Attention (three gated branches) for video rows.
+ *
+ * Sources (cited by page title and section):
+ *  [A] "VideoNSA: Native Sparse Attention Scales Video Understanding"
+ *      (shd-paper.top digest), English abstract: hardware-aware hybrid
+ *      attention, dense for text, NSA for video.
+ *  [B] top168.com digest of the same paper, section 一: the compression branch
+ *      merges neighbouring content into representative tokens; the selection
+ *      branch scores every segment by importance and attends to the chosen
+ *      ones in detail; the sliding-window branch keeps the latest tokens; a
+ *      learned weighting mixes the three per head.
+ *  [C] "VideoNSA：重新定义视频理解的稀疏注意力机制" (vcloud.csdn.net), section
+ *      2.2 (CMP / SLC / SWA) and section 3.1 (three gate values per head).
+ *  [D] mind-verse.de, "Innovative Ansätze zur Verbesserung des
+ *      Videoverständnisses in KI-Modellen", section "VideoNSA: Ein innovativer
+ *      Ansatz": dense attention for text, NSA for video.
+ * The pages name the branches but give no formulas; the exact definitions
+ * stated with each call below are the plain readings of them.
+ *
+ * General rules for every call
+ *  - Tensor pointers are DEVICE memory owned by the caller; the library never
+ *    allocates, frees, synchronises or prints.  Scratch memory, where needed,
+ *    is a caller-owned workspace whose size the matching *_workspace_size call
+ *    reports.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null
+ *    stream) and returns an nsa_status.  Arguments are validated before any
+ *    launch; on failure nothing is launched and nsa_last_error() describes it.
+ *  - Layouts are row-major and token-major:
+ *      q, o_* , out   [B, q_len, Hq, D]      (dtype)
+ *      k, v           [B, kv_len, Hkv, D]    (dtype)
+ *      k_cmp, v_cmp   [B, Nc, Hkv, D]        (dtype)
+ *      lse            [B, q_len, Hq]          fp32, natural log
+ *      importance     [B, q_len, Hkv, Ns]     fp32
+ *      block_idx      [B, q_len, Hkv, top_n]  int32, ascending, -1 padded
+ *      gates          [B, q_len, Hq, 3]       fp32 (cmp, slc, swa)
+ *      is_video       [B, q_len]              uint8 (non-zero = video row);
+ *                                             NULL means every row is video
+ *    with Nc = floor((kv_len - cmp_block) / cmp_stride) + 1 (0 when
+ *    kv_len < cmp_block) and Ns = ceil(kv_len / sel_block).
+ *  - Row r of q sits at absolute token position q_start + r.  Head h reads KV
+ *    head h / G with G = Hq / Hkv (GQA groups of consecutive heads).
+ *  - Calls are reentrant; concurrent calls must use disjoint outputs.
+ */
+#ifndef NSA_H
+#define NSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define NSA_OK 0
+#define NSA_ERR_INVALID_ARG (-1)         /* bad pointer, size or parameter */
+#define NSA_ERR_UNSUPPORTED (-2)         /* valid, but no kernel covers it   */
+#define NSA_ERR_HIP (-3)                 /* a HIP runtime / launch error     */
+#define NSA_ERR_WORKSPACE_TOO_SMALL (-4) /* workspace smaller than required  */
+
+/* Element types of q / k / v / compressed k, v / branch outputs. */
+#define NSA_F32 0
+#define NSA_BF16 1
+
+typedef struct {
+  int64_t batch;     /* B                                              */
+  int64_t q_len;     /* rows of q                                      */
+  int64_t kv_len;    /* tokens of k / v                                */
+  int64_t q_start;   /* absolute position of q's row 0; q_start + q_len <= kv_len */
+  int32_t num_q_heads;  /* Hq                                          */
+  int32_t num_kv_heads; /* Hkv, divides Hq                             */
+  int32_t head_dim;     /* D                                           */
+} nsa_shape;
+
+typedef struct {
+  int32_t cmp_block;  /* l: tokens per compressed block (e.g. 32)      */
+  int32_t cmp_stride; /* d: stride between compressed blocks (e.g. 16) */
+  int32_t sel_block;  /* l': tokens per selection block (e.g. 64)      */
+  int32_t top_n;      /* n: selection blocks per (row, KV group)       */
+  int32_t n_init;     /* leading blocks always selected (e.g. 1)       */
+  int32_t n_local;    /* most recent blocks always selected (e.g. 2)   */
+  int32_t window;     /* w: sliding-window length in tokens            */
+  float scale;        /* softmax scale; 0 means 1/sqrt(D)              */
+} nsa_params;
+
+/* Name of a status code (static string). */
+const char* nsa_status_string(int32_t status);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* nsa_last_error(void);
+
+/* Nc and Ns as defined above. */
+int64_t nsa_num_cmp_blocks(int64_t kv_len, int32_t cmp_block, int32_t cmp_stride);
+int64_t nsa_num_sel_blocks(int64_t kv_len, int32_t sel_block);
+
+/*
+ * nsa_compress_kv -- compression-branch keys and values ([B] section 一, [C]
+ * section 2.2: neighbouring tokens merged into one block token).
+ * Each compressed token is the positional weighted sum of its block:
+ *   k_cmp[b, i, h, :] = sum_{m < cmp_block} w_k[m] * k[b, i*cmp_stride + m, h, :]
+ * and likewise v_cmp with w_v.  Accumulation is fp32; results are rounded
+ * once to dtype.  w_k, w_v: device fp32 [cmp_block].  Writes Nc blocks; with
+ * Nc = 0 it launches nothing.  Supported: head_dim a multiple of 8, <= 256.
+ */
+int32_t nsa_compress_kv(const void* k, const void* v, int32_t dtype, int64_t batch, int64_t kv_len,
+                        int32_t num_kv_heads, int32_t head_dim, const float* w_k, const float* w_v,
+                        int32_t cmp_block, int32_t cmp_stride, void* k_cmp, void* v_cmp, void* stream);
+
+/*
+ * nsa_cmp_attn_scores -- compression-branch attention and block importance
+ * for the video rows ([B] section 一: the selection branch scores segments by
+ * importance; the score is taken from the compression branch's attention).
+ * For row t (absolute position) and head h:
+ *   C(t) = { i < Nc : i*cmp_stride + cmp_block - 1 <= t }   (whole block <= t)
+ *   p_i = softmax_i(scale * <q_t,h , k_cmp_i>) over C(t),  o_cmp = sum p_i v_cmp_i,
+ *   lse = log sum_i exp(scale * <q, k_cmp_i>);  C(t) empty -> o_cmp = 0, lse = -inf.
+ *   importance[t, g, j] = sum_{h in group g} sum_{i in C(t)} frac(i, j) * p_{h,i}
+ * where frac(i, j) is the share of compressed block i's tokens that lie in
+ * selection block j.  Every j < Ns of a video row is written (0 where nothing
+ * contributes).  Text rows are skipped: their outputs are left untouched.
+ * o_cmp and lse may be NULL.  importance may be NULL only if o_cmp is given.
+ * Supported: head_dim <= 256 and a multiple of 8; top_n <= 32 is not needed here.
+ */
+int32_t nsa_cmp_attn_scores(const void* q, const void* k_cmp, const void* v_cmp, int32_t dtype,
+                            const nsa_shape* shape, const nsa_params* params, const uint8_t* is_video,
+                            void* o_cmp, float* lse, float* importance, void* stream);
+
+/*
+ * nsa_topk_blocks -- selection of the top-n blocks per (video row, KV group).
+ * Candidates are J(t) = {0 .. t / sel_block}.  The forced blocks
+ *   F(t) = ({0 .. n_init-1} U {jt-n_local+1 .. jt}) intersected with J(t)
+ * are always taken and count inside top_n; the remaining places go to the
+ * free candidates by (importance descending, index ascending).  The set is
+ * written ascending and padded with -1.  Text rows are skipped.
+ * Errors: top_n < n_init + n_local, or top_n > 32 (UNSUPPORTED).
+ */
+int32_t nsa_topk_blocks(const float* importance, const nsa_shape* shape, const nsa_params* params,
+                        const uint8_t* is_video, int32_t* block_idx, void* stream);
+
+/*
+ * nsa_sparse_attn_fwd -- selection and sliding-window branches, the gated
+ * combine of the video rows, and dense causal attention of the text rows.
+ *  SLC: keys u <= t whose selection block u / sel_block is in block_idx[t, g]
+ *       ([B] section 一, [C] section 2.2: attend in full to the chosen blocks).
+ *  SWA: keys u in [max(0, t - window + 1), t] ([B] section 一).
+ *  out (video rows) = g_cmp*o_cmp + g_slc*o_slc + g_swa*o_swa with the given
+ *       gate values, no normalisation ([B] section 一, [C] section 3.1).
+ *  out (text rows)  = softmax(scale * q K_{<=t}^T) V_{<=t} over every token,
+ *       ungated ([A] abstract, [D]).
+ * o_slc, o_swa, out may each be NULL (at least one given).  out needs o_cmp
+ * and gates.  block_idx must hold valid sets (entries < Ns, ascending, the
+ * block of t among them) for every video row.
+ * workspace: device scratch of nsa_sparse_attn_workspace_size() bytes (may
+ * be NULL when that size is 0).
+ */
+size_t nsa_sparse_attn_workspace_size(const nsa_shape* shape, const nsa_params* params, int32_t dtype);
+int32_t nsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t dtype, const nsa_shape* shape,
+                            const nsa_params* params, const int32_t* block_idx, const uint8_t* is_video,
+                            const void* o_cmp, const float* gates, void* out, void* o_slc, void* o_swa,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * nsa_hybrid_layer_fwd -- the whole layer: compression (unless k_cmp_in and
+ * v_cmp_in give a precomputed compressed cache), compression-branch attention
+ * with block importance, top-n selection, selection and window branches, the
+ * gated combine for video rows, dense causal attention for text rows.
+ * Prefill: q_start = 0, q_len = kv_len.  Decode: q_len = 1,
+ * q_start = kv_len - 1 with the compressed cache passed in.
+ * out is required; o_cmp / o_slc / o_swa / block_idx_out may be NULL (when
+ * given they receive the branch outputs and the chosen blocks of the video
+ * rows).  workspace: nsa_hybrid_layer_workspace_size() bytes of device memory.
+ */
+size_t nsa_hybrid_layer_workspace_size(const nsa_shape* shape, const nsa_params* params, int32_t dtype);
+int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const void* k_cmp_in,
+                             const void* v_cmp_in, const float* w_k, const float* w_v, const float* gates,
+                             const uint8_t* is_video, int32_t dtype, const nsa_shape* shape,
+                             const nsa_params* params, void* out, void* o_cmp, void* o_slc, void* o_swa,
+                             int32_t* block_idx_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Debug / test switch: 1 forces the generic (non-MFMA) kernels, 0 restores the
+ * default dispatch.  Returns the previous value.  Process-wide. */
+int32_t nsa_set_force_generic(int32_t on);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NSA_H */

@@ -1,0 +1,324 @@
+// C ABI of the NSA library: argument validation, workspace layout and kernel
+// dispatch.  Every entry point validates all arguments before the first launch
+// and reports failures through a status code plus a thread-local message.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+#include <cmath>
+
+#include "../../include/nsa.h"
+#include "common.hpp"
+#include "fast.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+std::atomic<int> g_force_generic{0};
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(NSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int64_t ncmp(int64_t T, int l, int d) { return T < l ? 0 : (T - l) / d + 1; }
+int64_t nsel(int64_t T, int ls) { return (T + ls - 1) / ls; }
+
+size_t esize(int dtype) { return dtype == NSA_BF16 ? 2 : 4; }
+
+size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Shape/parameter validation shared by the attention entry points.
+int check_dims(const nsa_shape* sh, const nsa_params* pr, int32_t dtype, Dims* dm, bool need_params_topk) {
+  if (!sh || !pr) return fail(NSA_ERR_INVALID_ARG, "shape and params must not be NULL");
+  if (dtype != NSA_F32 && dtype != NSA_BF16) return fail(NSA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (sh->batch < 0 || sh->q_len < 0 || sh->kv_len < 0 || sh->q_start < 0)
+    return fail(NSA_ERR_INVALID_ARG, "negative size in shape");
+  if (sh->q_start + sh->q_len > sh->kv_len)
+    return fail(NSA_ERR_INVALID_ARG, "q_start + q_len (%lld) exceeds kv_len (%lld)",
+                (long long)(sh->q_start + sh->q_len), (long long)sh->kv_len);
+  if (sh->num_q_heads <= 0 || sh->num_kv_heads <= 0 || sh->num_q_heads % sh->num_kv_heads != 0)
+    return fail(NSA_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                sh->num_q_heads, sh->num_kv_heads);
+  if (sh->head_dim <= 0) return fail(NSA_ERR_INVALID_ARG, "head_dim must be positive");
+  if (sh->head_dim % 8 != 0 || sh->head_dim > 256)
+    return fail(NSA_ERR_UNSUPPORTED, "head_dim %d: kernels cover multiples of 8 up to 256", sh->head_dim);
+  if (pr->cmp_block <= 0 || pr->cmp_stride <= 0 || pr->sel_block <= 0)
+    return fail(NSA_ERR_INVALID_ARG, "block sizes must be positive");
+  if (pr->window <= 0) return fail(NSA_ERR_INVALID_ARG, "window must be positive");
+  if (pr->n_init < 0 || pr->n_local < 1) return fail(NSA_ERR_INVALID_ARG, "n_init must be >= 0 and n_local >= 1");
+  if (need_params_topk) {
+    if (pr->top_n < pr->n_init + pr->n_local)
+      return fail(NSA_ERR_INVALID_ARG, "top_n (%d) < n_init + n_local (%d)", pr->top_n, pr->n_init + pr->n_local);
+    if (pr->top_n > 32) return fail(NSA_ERR_UNSUPPORTED, "top_n %d > 32", pr->top_n);
+  }
+  if (!(pr->scale >= 0.f) || std::isinf(pr->scale)) return fail(NSA_ERR_INVALID_ARG, "scale must be finite, >= 0");
+  if (sh->kv_len > ((int64_t)1 << 31)) return fail(NSA_ERR_UNSUPPORTED, "kv_len above 2^31");
+  dm->B = sh->batch;
+  dm->Tq = sh->q_len;
+  dm->T = sh->kv_len;
+  dm->q0 = sh->q_start;
+  dm->Hq = sh->num_q_heads;
+  dm->Hkv = sh->num_kv_heads;
+  dm->D = sh->head_dim;
+  dm->G = sh->num_q_heads / sh->num_kv_heads;
+  dm->l = pr->cmp_block;
+  dm->d = pr->cmp_stride;
+  dm->ls = pr->sel_block;
+  dm->n = pr->top_n;
+  dm->n_init = pr->n_init;
+  dm->n_local = pr->n_local;
+  dm->w = pr->window;
+  dm->scale = pr->scale > 0.f ? pr->scale : 1.0f / sqrtf((float)sh->head_dim);
+  dm->Nc = ncmp(sh->kv_len, pr->cmp_block, pr->cmp_stride);
+  dm->Ns = nsel(sh->kv_len, pr->sel_block);
+  return NSA_OK;
+}
+
+bool use_fast(int32_t dtype, const Dims& dm) { return !g_force_generic.load() && fast_supported(dtype, dm); }
+
+// Workspace layout of nsa_sparse_attn_fwd.
+struct SparseWs {
+  size_t fast_bytes;
+  size_t total;
+};
+SparseWs sparse_ws(const Dims& dm, int32_t dtype) {
+  SparseWs w{};
+  w.fast_bytes = fast_supported(dtype, dm) ? round_up(fast_sparse_workspace(dm)) : 0;
+  w.total = w.fast_bytes;
+  return w;
+}
+
+struct LayerWs {
+  size_t kc, vc, o_cmp, lse, imp, idx, o_swa, sparse, total;
+};
+LayerWs layer_ws(const Dims& dm, int32_t dtype) {
+  LayerWs w{};
+  const size_t es = esize(dtype);
+  // compressed keys / values computed inside the layer stay fp32 (no extra rounding step)
+  w.kc = round_up((size_t)dm.B * dm.Nc * dm.Hkv * dm.D * 4);
+  w.vc = w.kc;
+  w.o_cmp = round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * es);
+  w.lse = round_up((size_t)dm.B * dm.Tq * dm.Hq * 4);
+  w.imp = round_up((size_t)dm.B * dm.Tq * dm.Hkv * dm.Ns * 4);
+  w.idx = round_up((size_t)dm.B * dm.Tq * dm.Hkv * dm.n * 4);
+  w.o_swa = round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * es);
+  w.sparse = sparse_ws(dm, dtype).total;
+  w.total = w.kc + w.vc + w.o_cmp + w.lse + w.imp + w.idx + w.o_swa + w.sparse;
+  return w;
+}
+
+int run_cmp(int32_t dtype, int32_t cdtype, const Dims& dm, const void* q, const void* kc, const void* vc,
+            const uint8_t* vid, void* o, float* lse, float* imp, hipStream_t s) {
+  hipError_t e = use_fast(dtype, dm) ? launch_cmp_fast(cdtype, dm, q, kc, vc, vid, o, lse, imp, s)
+                                     : launch_cmp_generic(dtype, cdtype, dm, q, kc, vc, vid, o, lse, imp, s);
+  if (e != hipSuccess) return hip_fail(e, "compression-branch kernel");
+  return NSA_OK;
+}
+
+int run_sparse(int32_t dtype, const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
+               const uint8_t* vid, const void* o_cmp, const float* gates, void* out, void* o_slc, void* o_swa,
+               void* ws, hipStream_t s) {
+  hipError_t e = use_fast(dtype, dm)
+                     ? launch_sparse_fast(dm, q, k, v, idx, vid, o_cmp, gates, out, o_slc, o_swa, ws, s)
+                     : launch_sparse_generic(dtype, dm, q, k, v, idx, vid, o_cmp, gates, out, o_slc, o_swa, s);
+  if (e != hipSuccess) return hip_fail(e, "selection/window kernel");
+  return NSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nsa_status_string(int32_t status) {
+  switch (status) {
+    case NSA_OK: return "NSA_OK";
+    case NSA_ERR_INVALID_ARG: return "NSA_ERR_INVALID_ARG";
+    case NSA_ERR_UNSUPPORTED: return "NSA_ERR_UNSUPPORTED";
+    case NSA_ERR_HIP: return "NSA_ERR_HIP";
+    case NSA_ERR_WORKSPACE_TOO_SMALL: return "NSA_ERR_WORKSPACE_TOO_SMALL";
+    default: return "NSA_UNKNOWN_STATUS";
+  }
+}
+
+const char* nsa_last_error(void) { return g_err; }
+
+int64_t nsa_num_cmp_blocks(int64_t kv_len, int32_t cmp_block, int32_t cmp_stride) {
+  if (kv_len < 0 || cmp_block <= 0 || cmp_stride <= 0) return -1;
+  return ncmp(kv_len, cmp_block, cmp_stride);
+}
+
+int64_t nsa_num_sel_blocks(int64_t kv_len, int32_t sel_block) {
+  if (kv_len < 0 || sel_block <= 0) return -1;
+  return nsel(kv_len, sel_block);
+}
+
+int32_t nsa_set_force_generic(int32_t on) { return g_force_generic.exchange(on ? 1 : 0); }
+
+int32_t nsa_compress_kv(const void* k, const void* v, int32_t dtype, int64_t batch, int64_t kv_len,
+                        int32_t num_kv_heads, int32_t head_dim, const float* w_k, const float* w_v,
+                        int32_t cmp_block, int32_t cmp_stride, void* k_cmp, void* v_cmp, void* stream) {
+  g_err[0] = 0;
+  if (dtype != NSA_F32 && dtype != NSA_BF16) return fail(NSA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (batch < 0 || kv_len < 0 || num_kv_heads <= 0 || head_dim <= 0 || cmp_block <= 0 || cmp_stride <= 0)
+    return fail(NSA_ERR_INVALID_ARG, "sizes must be positive (batch, kv_len >= 0)");
+  if (head_dim % 8 != 0 || head_dim > 256)
+    return fail(NSA_ERR_UNSUPPORTED, "head_dim %d: multiples of 8 up to 256", head_dim);
+  const int64_t Nc = ncmp(kv_len, cmp_block, cmp_stride);
+  if (Nc == 0 || batch == 0) return NSA_OK;
+  if (!k || !v || !w_k || !w_v || !k_cmp || !v_cmp) return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cmp) || !aligned16(v_cmp))
+    return fail(NSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_compress(dtype, dtype, k, w_k, k_cmp, batch, kv_len, num_kv_heads, head_dim, cmp_block,
+                                 cmp_stride, Nc, s);
+  if (e == hipSuccess)
+    e = launch_compress(dtype, dtype, v, w_v, v_cmp, batch, kv_len, num_kv_heads, head_dim, cmp_block, cmp_stride,
+                        Nc, s);
+  if (e != hipSuccess) return hip_fail(e, "compress kernel");
+  return NSA_OK;
+}
+
+int32_t nsa_cmp_attn_scores(const void* q, const void* k_cmp, const void* v_cmp, int32_t dtype,
+                            const nsa_shape* shape, const nsa_params* params, const uint8_t* is_video,
+                            void* o_cmp, float* lse, float* importance, void* stream) {
+  g_err[0] = 0;
+  Dims dm;
+  int st = check_dims(shape, params, dtype, &dm, false);
+  if (st != NSA_OK) return st;
+  if (!o_cmp && !importance) return fail(NSA_ERR_INVALID_ARG, "o_cmp and importance are both NULL");
+  if (dm.B == 0 || dm.Tq == 0) return NSA_OK;
+  if (!q || (dm.Nc > 0 && (!k_cmp || !v_cmp))) return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k_cmp) || !aligned16(v_cmp) || !aligned16(o_cmp))
+    return fail(NSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if (!use_fast(dtype, dm) && dm.Ns > 16384)
+    return fail(NSA_ERR_UNSUPPORTED, "generic kernel handles at most 16384 selection blocks");
+  return run_cmp(dtype, dtype, dm, q, k_cmp, v_cmp, is_video, o_cmp, lse, importance, (hipStream_t)stream);
+}
+
+int32_t nsa_topk_blocks(const float* importance, const nsa_shape* shape, const nsa_params* params,
+                        const uint8_t* is_video, int32_t* block_idx, void* stream) {
+  g_err[0] = 0;
+  Dims dm;
+  int st = check_dims(shape, params, NSA_F32, &dm, true);
+  if (st != NSA_OK) return st;
+  if (dm.B == 0 || dm.Tq == 0) return NSA_OK;
+  if (!importance || !block_idx) return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  hipError_t e = launch_topk(dm, importance, is_video, block_idx, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "top-n kernel");
+  return NSA_OK;
+}
+
+size_t nsa_sparse_attn_workspace_size(const nsa_shape* shape, const nsa_params* params, int32_t dtype) {
+  Dims dm;
+  if (check_dims(shape, params, dtype, &dm, true) != NSA_OK) return 0;
+  return sparse_ws(dm, dtype).total;
+}
+
+int32_t nsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t dtype, const nsa_shape* shape,
+                            const nsa_params* params, const int32_t* block_idx, const uint8_t* is_video,
+                            const void* o_cmp, const float* gates, void* out, void* o_slc, void* o_swa,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  Dims dm;
+  int st = check_dims(shape, params, dtype, &dm, true);
+  if (st != NSA_OK) return st;
+  if (!out && !o_slc && !o_swa) return fail(NSA_ERR_INVALID_ARG, "no output requested");
+  if (out && (!o_cmp || !gates)) return fail(NSA_ERR_INVALID_ARG, "out needs o_cmp and gates");
+  if (dm.B == 0 || dm.Tq == 0) return NSA_OK;
+  if (!q || !k || !v || !block_idx) return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_cmp) || !aligned16(out) ||
+      !aligned16(o_slc) || !aligned16(o_swa))
+    return fail(NSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  const SparseWs w = sparse_ws(dm, dtype);
+  const bool fast = use_fast(dtype, dm);
+  if (fast && workspace_bytes < w.total)
+    return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, w.total);
+  if (fast && w.total > 0 && !workspace) return fail(NSA_ERR_INVALID_ARG, "NULL workspace");
+  return run_sparse(dtype, dm, q, k, v, block_idx, is_video, o_cmp, gates, out, o_slc, o_swa, workspace,
+                    (hipStream_t)stream);
+}
+
+size_t nsa_hybrid_layer_workspace_size(const nsa_shape* shape, const nsa_params* params, int32_t dtype) {
+  Dims dm;
+  if (check_dims(shape, params, dtype, &dm, true) != NSA_OK) return 0;
+  return layer_ws(dm, dtype).total;
+}
+
+int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const void* k_cmp_in,
+                             const void* v_cmp_in, const float* w_k, const float* w_v, const float* gates,
+                             const uint8_t* is_video, int32_t dtype, const nsa_shape* shape,
+                             const nsa_params* params, void* out, void* o_cmp, void* o_slc, void* o_swa,
+                             int32_t* block_idx_out, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  Dims dm;
+  int st = check_dims(shape, params, dtype, &dm, true);
+  if (st != NSA_OK) return st;
+  if (!out) return fail(NSA_ERR_INVALID_ARG, "out must not be NULL");
+  if ((k_cmp_in == nullptr) != (v_cmp_in == nullptr))
+    return fail(NSA_ERR_INVALID_ARG, "give both k_cmp_in and v_cmp_in, or neither");
+  if (dm.B == 0 || dm.Tq == 0) return NSA_OK;
+  if (!q || !k || !v || !gates) return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!k_cmp_in && dm.Nc > 0 && (!w_k || !w_v)) return fail(NSA_ERR_INVALID_ARG, "NULL compression weights");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(o_cmp) ||
+      !aligned16(o_slc) || !aligned16(o_swa) || !aligned16(k_cmp_in) || !aligned16(v_cmp_in) ||
+      !aligned16(workspace))
+    return fail(NSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if (!use_fast(dtype, dm) && dm.Ns > 16384)
+    return fail(NSA_ERR_UNSUPPORTED, "generic kernels handle at most 16384 selection blocks");
+  const LayerWs w = layer_ws(dm, dtype);
+  if (workspace_bytes < w.total)
+    return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, w.total);
+  if (!workspace) return fail(NSA_ERR_INVALID_ARG, "NULL workspace");
+  hipStream_t s = (hipStream_t)stream;
+  char* p = (char*)workspace;
+  void* kc = p;
+  p += w.kc;
+  void* vc = p;
+  p += w.vc;
+  void* ocmp_ws = p;
+  p += w.o_cmp;
+  float* lse = (float*)p;
+  p += w.lse;
+  float* imp = (float*)p;
+  p += w.imp;
+  int32_t* idx_ws = (int32_t*)p;
+  p += w.idx;
+  void* oswa_ws = p;
+  p += w.o_swa;
+  void* sparse_ws_ptr = p;
+
+  const void* kc_use = k_cmp_in;
+  const void* vc_use = v_cmp_in;
+  int32_t cdtype = dtype;
+  if (!kc_use) {
+    hipError_t e = launch_compress(dtype, NSA_F32, k, w_k, kc, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d, dm.Nc, s);
+    if (e == hipSuccess)
+      e = launch_compress(dtype, NSA_F32, v, w_v, vc, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d, dm.Nc, s);
+    if (e != hipSuccess) return hip_fail(e, "compress kernel");
+    kc_use = kc;
+    vc_use = vc;
+    cdtype = NSA_F32;
+  }
+  void* ocmp = o_cmp ? o_cmp : ocmp_ws;
+  int32_t* idx = block_idx_out ? block_idx_out : idx_ws;
+  st = run_cmp(dtype, cdtype, dm, q, kc_use, vc_use, is_video, ocmp, lse, imp, s);
+  if (st != NSA_OK) return st;
+  hipError_t e = launch_topk(dm, imp, is_video, idx, s);
+  if (e != hipSuccess) return hip_fail(e, "top-n kernel");
+  void* oswa = o_swa ? o_swa : oswa_ws;
+  return run_sparse(dtype, dm, q, k, v, idx, is_video, ocmp, gates, out, o_slc, oswa, sparse_ws_ptr, s);
+}
+
+}  // extern "C"

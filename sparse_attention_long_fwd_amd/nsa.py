@@ -1,0 +1,209 @@
+"""Thin ctypes binding of libnsa.so: same entry-point names as include/nsa.h.
+
+Argument marshalling only.  Every step of the layer runs in the HIP kernels of
+libnsa.so; PyTorch supplies device memory and the current stream.  The library
+must be built (``python -m sparse_attention_long_fwd_amd.build``): loading
+raises if it is missing, and there is no other execution path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnsa.so")
+
+NSA_OK, NSA_ERR_INVALID_ARG, NSA_ERR_UNSUPPORTED, NSA_ERR_HIP, NSA_ERR_WORKSPACE_TOO_SMALL = 0, -1, -2, -3, -4
+NSA_F32, NSA_BF16 = 0, 1
+
+
+class NsaShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("q_len", ctypes.c_int64), ("kv_len", ctypes.c_int64),
+                ("q_start", ctypes.c_int64), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32)]
+
+
+class NsaParams(ctypes.Structure):
+    _fields_ = [("cmp_block", ctypes.c_int32), ("cmp_stride", ctypes.c_int32), ("sel_block", ctypes.c_int32),
+                ("top_n", ctypes.c_int32), ("n_init", ctypes.c_int32), ("n_local", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class NsaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s: %s" % (status_string(status) if _lib else status, msg))
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32, _I64, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_SH, _PR = ctypes.POINTER(NsaShape), ctypes.POINTER(NsaParams)
+
+EXPORTS = {
+    "nsa_status_string": (ctypes.c_char_p, [_I32]),
+    "nsa_last_error": (ctypes.c_char_p, []),
+    "nsa_num_cmp_blocks": (_I64, [_I64, _I32, _I32]),
+    "nsa_num_sel_blocks": (_I64, [_I64, _I32]),
+    "nsa_compress_kv": (_I32, [_P, _P, _I32, _I64, _I64, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _P]),
+    "nsa_cmp_attn_scores": (_I32, [_P, _P, _P, _I32, _SH, _PR, _P, _P, _P, _P, _P]),
+    "nsa_topk_blocks": (_I32, [_P, _SH, _PR, _P, _P, _P]),
+    "nsa_sparse_attn_workspace_size": (_SZ, [_SH, _PR, _I32]),
+    "nsa_sparse_attn_fwd": (_I32, [_P, _P, _P, _I32, _SH, _PR, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "nsa_hybrid_layer_workspace_size": (_SZ, [_SH, _PR, _I32]),
+    "nsa_hybrid_layer_fwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _SH, _PR, _P, _P, _P, _P, _P, _P,
+                                    _SZ, _P]),
+    "nsa_set_force_generic": (_I32, [_I32]),
+}
+
+
+def lib():
+    """Load libnsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libnsa.so is not built: run `python -m sparse_attention_long_fwd_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().nsa_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().nsa_last_error().decode()
+
+
+def _check(status: int):
+    if status != NSA_OK:
+        raise NsaError(status, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    assert t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors"
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return NSA_F32
+    if t.dtype == torch.bfloat16:
+        return NSA_BF16
+    raise TypeError("q/k/v must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def make_shape(batch, q_len, kv_len, q_start, num_q_heads, num_kv_heads, head_dim) -> NsaShape:
+    return NsaShape(batch, q_len, kv_len, q_start, num_q_heads, num_kv_heads, head_dim)
+
+
+def make_params(cmp_block=32, cmp_stride=16, sel_block=64, top_n=16, n_init=1, n_local=2, window=512,
+                scale=0.0) -> NsaParams:
+    return NsaParams(cmp_block, cmp_stride, sel_block, top_n, n_init, n_local, window, scale)
+
+
+def shape_of(q: torch.Tensor, k: torch.Tensor, q_start: int = 0) -> NsaShape:
+    B, Tq, Hq, D = q.shape
+    return make_shape(B, Tq, k.shape[1], q_start, Hq, k.shape[2], D)
+
+
+def num_cmp_blocks(kv_len: int, cmp_block: int, cmp_stride: int) -> int:
+    return int(lib().nsa_num_cmp_blocks(kv_len, cmp_block, cmp_stride))
+
+
+def num_sel_blocks(kv_len: int, sel_block: int) -> int:
+    return int(lib().nsa_num_sel_blocks(kv_len, sel_block))
+
+
+def set_force_generic(on: bool) -> bool:
+    return bool(lib().nsa_set_force_generic(1 if on else 0))
+
+
+def nsa_compress_kv(k, v, w_k, w_v, cmp_block=32, cmp_stride=16, k_cmp=None, v_cmp=None, stream=None):
+    B, T, H, D = k.shape
+    Nc = num_cmp_blocks(T, cmp_block, cmp_stride)
+    if k_cmp is None:
+        k_cmp = torch.empty(B, Nc, H, D, dtype=k.dtype, device=k.device)
+    if v_cmp is None:
+        v_cmp = torch.empty(B, Nc, H, D, dtype=v.dtype, device=v.device)
+    _check(lib().nsa_compress_kv(_ptr(k), _ptr(v), _dtype_code(k), B, T, H, D, _ptr(w_k), _ptr(w_v), cmp_block,
+                                 cmp_stride, _ptr(k_cmp), _ptr(v_cmp), _stream(stream)))
+    return k_cmp, v_cmp
+
+
+def nsa_cmp_attn_scores(q, k_cmp, v_cmp, shape: NsaShape, params: NsaParams, is_video=None, o_cmp=None,
+                        lse=None, importance=None, want=("o_cmp", "lse", "importance"), stream=None):
+    B, Tq, Hq, D = q.shape
+    Ns = num_sel_blocks(shape.kv_len, params.sel_block)
+    if o_cmp is None and "o_cmp" in want:
+        o_cmp = torch.zeros_like(q)
+    if lse is None and "lse" in want:
+        lse = torch.zeros(B, Tq, Hq, dtype=torch.float32, device=q.device)
+    if importance is None and "importance" in want:
+        importance = torch.zeros(B, Tq, shape.num_kv_heads, Ns, dtype=torch.float32, device=q.device)
+    _check(lib().nsa_cmp_attn_scores(_ptr(q), _ptr(k_cmp), _ptr(v_cmp), _dtype_code(q), ctypes.byref(shape),
+                                     ctypes.byref(params), _ptr(is_video), _ptr(o_cmp), _ptr(lse),
+                                     _ptr(importance), _stream(stream)))
+    return o_cmp, lse, importance
+
+
+def nsa_topk_blocks(importance, shape: NsaShape, params: NsaParams, is_video=None, block_idx=None, stream=None):
+    B, Tq, Hkv, _ = importance.shape
+    if block_idx is None:
+        block_idx = torch.full((B, Tq, Hkv, params.top_n), -1, dtype=torch.int32, device=importance.device)
+    _check(lib().nsa_topk_blocks(_ptr(importance), ctypes.byref(shape), ctypes.byref(params), _ptr(is_video),
+                                 _ptr(block_idx), _stream(stream)))
+    return block_idx
+
+
+def nsa_sparse_attn_workspace_size(shape: NsaShape, params: NsaParams, dtype_code: int) -> int:
+    return int(lib().nsa_sparse_attn_workspace_size(ctypes.byref(shape), ctypes.byref(params), dtype_code))
+
+
+def nsa_sparse_attn_fwd(q, k, v, shape: NsaShape, params: NsaParams, block_idx, is_video=None, o_cmp=None,
+                        gates=None, out=None, o_slc=None, o_swa=None, workspace=None, stream=None):
+    dt = _dtype_code(q)
+    ws_bytes = nsa_sparse_attn_workspace_size(shape, params, dt)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _check(lib().nsa_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), dt, ctypes.byref(shape), ctypes.byref(params),
+                                     _ptr(block_idx), _ptr(is_video), _ptr(o_cmp), _ptr(gates), _ptr(out),
+                                     _ptr(o_slc), _ptr(o_swa), _ptr(workspace),
+                                     0 if workspace is None else workspace.numel(), _stream(stream)))
+    return out, o_slc, o_swa
+
+
+def nsa_hybrid_layer_workspace_size(shape: NsaShape, params: NsaParams, dtype_code: int) -> int:
+    return int(lib().nsa_hybrid_layer_workspace_size(ctypes.byref(shape), ctypes.byref(params), dtype_code))
+
+
+def nsa_hybrid_layer_fwd(q, k, v, gates, shape: NsaShape, params: NsaParams, w_k=None, w_v=None, k_cmp_in=None,
+                         v_cmp_in=None, is_video=None, out=None, o_cmp=None, o_slc=None, o_swa=None,
+                         block_idx_out=None, workspace=None, stream=None):
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = torch.empty(nsa_hybrid_layer_workspace_size(shape, params, dt), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib().nsa_hybrid_layer_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cmp_in), _ptr(v_cmp_in), _ptr(w_k),
+                                      _ptr(w_v), _ptr(gates), _ptr(is_video), dt, ctypes.byref(shape),
+                                      ctypes.byref(params), _ptr(out), _ptr(o_cmp), _ptr(o_slc), _ptr(o_swa),
+                                      _ptr(block_idx_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out

@@ -1,0 +1,115 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments before launching anything (no GPU needed:
+every call here fails validation on the host)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_attention_long_fwd_amd import nsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nsa.h")
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nsa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = nsa.lib()
+    decl = declared_symbols()
+    assert len(decl) >= 12
+    out = subprocess.run(["nm", "-D", "--defined-only", nsa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for s in decl:
+        assert s in exported, s
+        assert hasattr(L, s)
+    assert set(nsa.EXPORTS) == set(decl)
+
+
+def test_status_strings_and_block_counts():
+    assert nsa.status_string(0) == "NSA_OK"
+    assert nsa.status_string(-4) == "NSA_ERR_WORKSPACE_TOO_SMALL"
+    assert nsa.status_string(99) == "NSA_UNKNOWN_STATUS"
+    assert nsa.num_cmp_blocks(131072, 32, 16) == 8191
+    assert nsa.num_cmp_blocks(31, 32, 16) == 0
+    assert nsa.num_cmp_blocks(36352, 32, 16) == 2271
+    assert nsa.num_sel_blocks(131072, 64) == 2048 and nsa.num_sel_blocks(36352, 64) == 568
+    assert nsa.num_sel_blocks(65, 64) == 2
+    assert nsa.num_cmp_blocks(-1, 32, 16) == -1
+
+
+def _shape(**kw):
+    d = dict(batch=1, q_len=1024, kv_len=1024, q_start=0, num_q_heads=4, num_kv_heads=1, head_dim=64)
+    d.update(kw)
+    return nsa.make_shape(**d)
+
+
+def _params(**kw):
+    d = dict(cmp_block=32, cmp_stride=16, sel_block=64, top_n=4, n_init=1, n_local=2, window=128, scale=0.0)
+    d.update(kw)
+    return nsa.make_params(**d)
+
+
+def _layer(shape, params, ws_bytes=1 << 40, out=FAKE, q=FAKE, dtype=nsa.NSA_F32, kc=None, vc=None):
+    L = nsa.lib()
+    return L.nsa_hybrid_layer_fwd(q, FAKE, FAKE, kc, vc, FAKE, FAKE, FAKE, None, dtype, ctypes.byref(shape),
+                                  ctypes.byref(params), out, None, None, None, None, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("shape_kw,params_kw,code", [
+    (dict(num_q_heads=6, num_kv_heads=4), {}, nsa.NSA_ERR_INVALID_ARG),
+    (dict(q_start=10), {}, nsa.NSA_ERR_INVALID_ARG),                      # q_start + q_len > kv_len
+    (dict(head_dim=60), {}, nsa.NSA_ERR_UNSUPPORTED),
+    (dict(head_dim=512), {}, nsa.NSA_ERR_UNSUPPORTED),
+    (dict(batch=-1), {}, nsa.NSA_ERR_INVALID_ARG),
+    ({}, dict(top_n=2), nsa.NSA_ERR_INVALID_ARG),                         # top_n < n_init + n_local
+    ({}, dict(top_n=33), nsa.NSA_ERR_UNSUPPORTED),
+    ({}, dict(window=0), nsa.NSA_ERR_INVALID_ARG),
+    ({}, dict(cmp_stride=0), nsa.NSA_ERR_INVALID_ARG),
+    ({}, dict(n_local=0), nsa.NSA_ERR_INVALID_ARG),
+    ({}, dict(scale=-1.0), nsa.NSA_ERR_INVALID_ARG),
+])
+def test_layer_rejects_bad_shapes_and_params(shape_kw, params_kw, code):
+    assert _layer(_shape(**shape_kw), _params(**params_kw)) == code
+    assert nsa.last_error() != ""
+
+
+def test_layer_rejects_null_and_small_workspace():
+    sh, pr = _shape(), _params()
+    assert _layer(sh, pr, out=None) == nsa.NSA_ERR_INVALID_ARG
+    assert _layer(sh, pr, q=None) == nsa.NSA_ERR_INVALID_ARG
+    assert _layer(sh, pr, kc=FAKE) == nsa.NSA_ERR_INVALID_ARG        # k_cmp_in without v_cmp_in
+    need = nsa.nsa_hybrid_layer_workspace_size(sh, pr, nsa.NSA_F32)
+    assert need > 0
+    assert _layer(sh, pr, ws_bytes=need - 1) == nsa.NSA_ERR_WORKSPACE_TOO_SMALL
+    assert "workspace" in nsa.last_error()
+    assert _layer(sh, pr, q=FAKE + 4) == nsa.NSA_ERR_INVALID_ARG     # misaligned
+    assert nsa.nsa_hybrid_layer_workspace_size(_shape(num_kv_heads=3), pr, nsa.NSA_F32) == 0
+
+
+def test_other_entry_points_validate_first():
+    L = nsa.lib()
+    sh, pr = _shape(), _params()
+    assert L.nsa_compress_kv(FAKE, FAKE, 7, 1, 1024, 1, 64, FAKE, FAKE, 32, 16, FAKE, FAKE, None) == -1
+    assert L.nsa_compress_kv(None, FAKE, 0, 1, 1024, 1, 64, FAKE, FAKE, 32, 16, FAKE, FAKE, None) == -1
+    assert L.nsa_compress_kv(FAKE, FAKE, 0, 1, 1024, 1, 60, FAKE, FAKE, 32, 16, FAKE, FAKE, None) == -2
+    # nothing to do: fewer tokens than one block
+    assert L.nsa_compress_kv(None, None, 0, 1, 31, 1, 64, None, None, 32, 16, None, None, None) == 0
+    assert L.nsa_cmp_attn_scores(FAKE, FAKE, FAKE, 0, ctypes.byref(sh), ctypes.byref(pr), None, None, None,
+                                 None, None) == -1
+    assert L.nsa_topk_blocks(FAKE, ctypes.byref(sh), ctypes.byref(_params(top_n=1)), None, FAKE, None) == -1
+    assert L.nsa_topk_blocks(None, ctypes.byref(sh), ctypes.byref(pr), None, FAKE, None) == -1
+    assert L.nsa_sparse_attn_fwd(FAKE, FAKE, FAKE, 0, ctypes.byref(sh), ctypes.byref(pr), FAKE, None, None, None,
+                                 None, None, None, None, 0, None) == -1       # no output
+    assert L.nsa_sparse_attn_fwd(FAKE, FAKE, FAKE, 0, ctypes.byref(sh), ctypes.byref(pr), FAKE, None, None, FAKE,
+                                 FAKE, None, None, None, 0, None) == -1       # out without o_cmp
+    # empty problems launch nothing and succeed
+    e = _shape(q_len=0)
+    assert L.nsa_topk_blocks(None, ctypes.byref(e), ctypes.byref(pr), None, None, None) == 0

@@ -1,0 +1,343 @@
+"""GPU parity: every entry point of libnsa.so against the fp64 oracle on seeded
+inputs, element by element, through the C ABI.
+
+Tolerances: max-abs 1e-4 (fp32 inputs) and 2e-2 (bf16 inputs) on branch and
+final outputs; chosen blocks identical wherever the oracle's selection gap
+exceeds 1e-3, and a valid selection everywhere else.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import GAP, TOL, check_indices, flush, host, maxabs
+from sparse_attention_long_fwd_amd import nsa, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(params=["default", "generic"])
+def path(request):
+    prev = nsa.set_force_generic(request.param == "generic")
+    yield request.param
+    nsa.set_force_generic(prev)
+
+
+def _rand(seed, shape, dtype, scale=1.0):
+    return synth.normal(seed, shape, DEV, scale=scale).to(dtype)
+
+
+def _wl(dtype="bf16", T=1024, Hq=28, Hkv=4, D=128, n=16, w=512, lead=0, tail=0, corr=True, B=1, q_start=0,
+        q_len=None, **kw):
+    return synth.Workload(name="test", index=9, dtype=dtype, batch=B, kv_len=T,
+                          q_len=T - q_start if q_len is None else q_len, q_start=q_start, num_q_heads=Hq,
+                          num_kv_heads=Hkv, head_dim=D, top_n=n, window=w, text_lead=lead, text_tail=tail,
+                          frame_corr=corr, **kw)
+
+
+# --------------------------------------------------------------------------- compression
+@pytest.mark.parametrize("dtype,B,T,H,D", [("f32", 1, 1024, 1, 64), ("bf16", 2, 1000, 4, 128),
+                                           ("bf16", 1, 36352, 4, 128), ("f32", 1, 47, 2, 8), ("bf16", 1, 31, 1, 16)])
+def test_compress_kv(dtype, B, T, H, D):
+    flush("compress %s B=%d T=%d H=%d D=%d" % (dtype, B, T, H, D))
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    k, v = _rand(101, (B, T, H, D), dt), _rand(102, (B, T, H, D), dt)
+    wk = _rand(103, (32,), torch.float32, 1 / math.sqrt(32))
+    wv = _rand(104, (32,), torch.float32, 1 / math.sqrt(32))
+    kc, vc = nsa.nsa_compress_kv(k, v, wk, wv, 32, 16)
+    torch.cuda.synchronize()
+    assert kc.shape[1] == nsa.num_cmp_blocks(T, 32, 16)
+    for b in range(B):
+        rk = oracle.compress(host(k[b]), host(wk), 32, 16)
+        rv = oracle.compress(host(v[b]), host(wv), 32, 16)
+        for got, ref in ((kc[b], rk), (vc[b], rv)):
+            g = host(got).astype(np.float64)
+            bound = (2.0 ** -8 * np.abs(ref) + 1e-5) if dtype == "bf16" else 1e-5
+            assert np.all(np.abs(g - ref) <= bound)
+
+
+# --------------------------------------------------------------------------- compression branch
+@pytest.mark.parametrize("dtype,T,Hq,Hkv,D,lead,tail,q_start", [
+    ("f32", 1024, 4, 1, 64, 0, 0, 0),
+    ("bf16", 1000, 14, 2, 128, 64, 40, 0),
+    ("bf16", 3000, 28, 4, 128, 128, 128, 0),
+    ("bf16", 5000, 28, 4, 128, 0, 0, 4900),
+])
+def test_cmp_attn_scores(dtype, T, Hq, Hkv, D, lead, tail, q_start, path):
+    flush("cmp %s T=%d Hq=%d path=%s" % (dtype, T, Hq, path))
+    wl = _wl(dtype, T, Hq, Hkv, D, lead=lead, tail=tail, q_start=q_start)
+    dt = wl.torch_dtype
+    Nc = nsa.num_cmp_blocks(T, 32, 16)
+    q = _rand(111, (1, wl.q_len, Hq, D), dt)
+    kc = _rand(112, (1, Nc, Hkv, D), dt)
+    vc = _rand(113, (1, Nc, Hkv, D), dt)
+    vid = synth.video_mask(wl, DEV)
+    sh = nsa.make_shape(1, wl.q_len, T, q_start, Hq, Hkv, D)
+    pr = nsa.make_params(top_n=16, window=512)
+    o, lse, imp = nsa.nsa_cmp_attn_scores(q, kc, vc, sh, pr, is_video=vid)
+    torch.cuda.synchronize()
+    pos = np.arange(q_start, q_start + wl.q_len)
+    ro, rl, ri = oracle.cmp_rows(host(q[0]), pos, host(kc[0]), host(vc[0]), Hq, 32, 16, 64, T, 1 / math.sqrt(D))
+    V = host(vid[0]).astype(bool)
+    assert maxabs(host(o[0])[V], ro[V]) <= TOL[dtype]
+    fin = np.isfinite(rl[V])
+    gl = host(lse[0])[V]
+    assert np.all(np.isneginf(gl[~fin]))
+    assert maxabs(gl[fin], rl[V][fin]) <= 1e-3
+    assert maxabs(host(imp[0])[V], ri[V]) <= 2e-4
+
+
+# --------------------------------------------------------------------------- top-n
+@pytest.mark.parametrize("n,n_init,n_local,Ns", [(4, 1, 2, 16), (16, 1, 2, 568), (16, 1, 2, 2048), (8, 2, 3, 300),
+                                                  (32, 1, 2, 2048), (3, 0, 3, 50)])
+def test_topk_blocks_exact(n, n_init, n_local, Ns):
+    flush("topk n=%d Ns=%d" % (n, Ns))
+    ls = 64
+    T = Ns * ls
+    R, Hkv = 700, 4
+    rng = np.random.default_rng(n * 1000 + Ns)
+    pos = np.sort(rng.integers(0, T, R))
+    pos[:3] = [0, 63, 64 * 5 + 1]
+    pos[-1] = T - 1
+    # coarse values: many exact ties, decided by the lower index on both sides
+    imp = (rng.integers(0, 40, (R, Hkv, Ns)) / 64.0).astype(np.float32)
+    # rows of q given explicitly: one batch element per row keeps arbitrary positions
+    sh = nsa.make_shape(R, 1, T, 0, Hkv, Hkv, 8)
+    imp_d = torch.from_numpy(imp).to(DEV).view(R, 1, Hkv, Ns)
+    got = []
+    for r0 in range(0, R, 100):
+        rows = list(range(r0, min(R, r0 + 100)))
+        for r in rows:
+            sh1 = nsa.make_shape(1, 1, T, int(pos[r]), Hkv, Hkv, 8)
+            got.append(nsa.nsa_topk_blocks(imp_d[r:r + 1], sh1, nsa.make_params(top_n=n, n_init=n_init,
+                                                                                 n_local=n_local)))
+    torch.cuda.synchronize()
+    got = np.concatenate([host(x).reshape(1, Hkv, n) for x in got])
+    ref, _ = oracle.topk_rows(imp.astype(np.float64), pos, ls, n, n_init, n_local)
+    assert np.array_equal(got, ref)
+
+
+def test_topk_blocks_many_rows():
+    T, Hkv, n = 36352, 4, 16
+    Ns = nsa.num_sel_blocks(T, 64)
+    wl = _wl(T=T, lead=256, tail=256)
+    rng = np.random.default_rng(5)
+    imp = rng.random((1, T, Hkv, Ns)).astype(np.float32)
+    vid = synth.video_mask(wl, DEV)
+    sh = nsa.make_shape(1, T, T, 0, 28, Hkv, 128)
+    got = nsa.nsa_topk_blocks(torch.from_numpy(imp).to(DEV), sh, nsa.make_params(top_n=n), is_video=vid)
+    torch.cuda.synchronize()
+    V = host(vid[0]).astype(bool)
+    rows = np.nonzero(V)[0][::37]
+    ref, _ = oracle.topk_rows(imp[0, rows].astype(np.float64), rows, 64, n, 1, 2)
+    assert np.array_equal(host(got[0])[rows], ref)
+    assert np.all(host(got[0])[~V] == -1)  # text rows untouched (initialised to -1)
+
+
+# --------------------------------------------------------------------------- selection / window / text rows
+def _random_idx(pos, Hkv, n, ls, seed):
+    rng = np.random.default_rng(seed)
+    R = len(pos)
+    idx = np.full((R, Hkv, n), -1, np.int32)
+    for r in range(R):
+        jt = int(pos[r]) // ls
+        for g in range(Hkv):
+            forced = {j for j in range(jt + 1) if j < 1 or j > jt - 2}
+            free = [j for j in range(jt + 1) if j not in forced]
+            k = min(n - len(forced), len(free))
+            pick = rng.choice(free, size=k, replace=False).tolist() if k > 0 else []
+            s = sorted(forced | set(pick))
+            idx[r, g, :len(s)] = s
+    return idx
+
+
+@pytest.mark.parametrize("dtype,T,Hq,Hkv,D,n,w,lead,tail,B", [
+    ("f32", 1024, 4, 1, 64, 4, 128, 0, 0, 1),
+    ("bf16", 1100, 14, 2, 128, 16, 512, 64, 76, 1),
+    ("bf16", 4096, 28, 4, 128, 16, 512, 256, 256, 1),
+    ("bf16", 700, 28, 4, 128, 8, 256, 0, 0, 2),
+])
+def test_sparse_attn_fwd(dtype, T, Hq, Hkv, D, n, w, lead, tail, B, path):
+    flush("sparse %s T=%d n=%d w=%d B=%d path=%s" % (dtype, T, n, w, B, path))
+    wl = _wl(dtype, T, Hq, Hkv, D, n=n, w=w, lead=lead, tail=tail, B=B)
+    dt = wl.torch_dtype
+    inp = synth.make_inputs(wl, DEV)
+    q, k, v, g, vid = inp["q"], inp["k"], inp["v"], inp["gates"], inp["is_video"]
+    ocmp = _rand(121, tuple(q.shape), dt)
+    pos = np.arange(T)
+    idx = np.stack([_random_idx(pos, Hkv, n, 64, 7 + b) for b in range(B)])
+    idx_d = torch.from_numpy(idx).to(DEV)
+    sh = nsa.shape_of(q, k)
+    pr = nsa.make_params(top_n=n, window=w)
+    out, o_slc, o_swa = torch.zeros_like(q), torch.zeros_like(q), torch.zeros_like(q)
+    nsa.nsa_sparse_attn_fwd(q, k, v, sh, pr, idx_d, is_video=vid, o_cmp=ocmp, gates=g, out=out, o_slc=o_slc,
+                            o_swa=o_swa)
+    torch.cuda.synchronize()
+    s = 1 / math.sqrt(D)
+    for b in range(B):
+        V = host(vid[b]).astype(bool)
+        vr = np.nonzero(V)[0]
+        tr = np.nonzero(~V)[0]
+        qh, kh, vh = host(q[b]), host(k[b]), host(v[b])
+        rs, rw = oracle.sparse_rows(qh[vr], vr, kh, vh, idx[b][vr], 64, w, s)
+        assert maxabs(host(o_slc[b])[vr], rs) <= TOL[dtype]
+        assert maxabs(host(o_swa[b])[vr], rw) <= TOL[dtype]
+        gg = host(g[b])[vr].astype(np.float64)
+        ref = gg[..., 0:1] * host(ocmp[b])[vr] + gg[..., 1:2] * rs + gg[..., 2:3] * rw
+        assert maxabs(host(out[b])[vr], ref) <= TOL[dtype]
+        if tr.size:
+            rd, _ = oracle.dense_rows(qh[tr], tr, kh, vh, s)
+            assert maxabs(host(out[b])[tr], rd) <= TOL[dtype]
+
+
+# --------------------------------------------------------------------------- whole layer
+def run_layer(wl, inp, **kw):
+    q = inp["q"]
+    B, Tq, Hq, D = q.shape
+    Hkv = inp["k"].shape[2]
+    sh = nsa.make_shape(B, Tq, wl.kv_len, wl.q_start, Hq, Hkv, D)
+    pr = nsa.make_params(**{k: v for k, v in wl.params().items()})
+    o_cmp, o_slc, o_swa = torch.zeros_like(q), torch.zeros_like(q), torch.zeros_like(q)
+    idx = torch.full((B, Tq, Hkv, wl.top_n), -1, dtype=torch.int32, device=DEV)
+    out = nsa.nsa_hybrid_layer_fwd(q, inp["k"], inp["v"], inp["gates"], sh, pr, w_k=inp["w_k"], w_v=inp["w_v"],
+                                   is_video=inp["is_video"], o_cmp=o_cmp, o_slc=o_slc, o_swa=o_swa,
+                                   block_idx_out=idx, **kw)
+    torch.cuda.synchronize()
+    return dict(out=out, o_cmp=o_cmp, o_slc=o_slc, o_swa=o_swa, idx=idx)
+
+
+def compare_layer(wl, inp, got, rows, b=0, kc=None, vc=None):
+    """Oracle on the chosen rows of batch element b; assert the parity rules."""
+    dtype = wl.dtype
+    q = host(inp["q"][b])
+    k, v = host(inp["k"][b]), host(inp["v"][b])
+    res = oracle.layer(q, k, v, host(inp["w_k"]), host(inp["w_v"]), host(inp["gates"][b]),
+                       host(inp["is_video"][b]), wl.params(), q_start=wl.q_start, rows=rows, kc=kc, vc=vc)
+    V = host(inp["is_video"][b])[rows].astype(bool)
+    pos = rows + wl.q_start
+    tol = TOL[dtype]
+    stats = {}
+    if V.any():
+        same = check_indices(host(got["idx"][b])[rows][V], res["idx"][V], res["gap"][V], res["imp"][V], pos[V],
+                             wl.sel_block, wl.top_n, wl.n_init, wl.n_local)
+        rows_same = same.all(axis=1)
+        stats["decided"] = float((res["gap"][V] > GAP).mean())
+        stats["idx_equal"] = float(same.mean())
+        e_cmp = maxabs(host(got["o_cmp"][b])[rows][V], res["o_cmp"][V])
+        e_swa = maxabs(host(got["o_swa"][b])[rows][V], res["o_swa"][V])
+        e_slc = maxabs(host(got["o_slc"][b])[rows][V][rows_same], res["o_slc"][V][rows_same])
+        e_out = maxabs(host(got["out"][b])[rows][V][rows_same], res["out"][V][rows_same])
+        stats.update(cmp=e_cmp, swa=e_swa, slc=e_slc, out=e_out)
+        ecmp_rows = np.abs(host(got["o_cmp"][b])[rows][V] - res["o_cmp"][V]).max(axis=(1, 2))
+        stats["cmp_worst_pos"] = int(pos[V][np.argmax(ecmp_rows)])
+        assert e_cmp <= tol and e_swa <= tol and e_slc <= tol and e_out <= tol, stats
+    if (~V).any():
+        e_txt = maxabs(host(got["out"][b])[rows][~V], res["out"][~V])
+        stats["text"] = e_txt
+        assert e_txt <= tol, stats
+    flush("  parity %s" % stats)
+    return stats
+
+
+@pytest.mark.parametrize("case", ["tiny", "bf16-4k", "bf16-ragged", "bf16-batch2"])
+def test_layer_small(case, path):
+    if case == "tiny":
+        wl = synth.WORKLOADS["tiny"]
+    elif case == "bf16-4k":
+        wl = _wl(T=4096, lead=256, tail=256)
+    elif case == "bf16-ragged":
+        wl = _wl(T=1000 + 37, Hq=14, Hkv=2, lead=64, tail=13, n=6, w=100)
+    else:
+        wl = _wl(T=900, B=2, lead=128, tail=0, n=8, w=256)
+    flush("layer %s path=%s" % (case, path))
+    inp = synth.make_inputs(wl, DEV)
+    got = run_layer(wl, inp)
+    for b in range(wl.batch):
+        compare_layer(wl, inp, got, np.arange(wl.q_len), b)
+
+
+def _sample_rows(wl, per_frame=1, seed=0, text=8, edge=64):
+    """Deterministic row sample: the first and last rows, a few text rows, and
+    one row per `stride` video rows at a seeded offset."""
+    T = wl.q_len
+    rng = np.random.default_rng(seed)
+    rows = set(range(min(edge, T))) | set(range(max(0, T - edge), T))
+    vid = host(synth.video_mask(wl))[0].astype(bool)
+    tr = np.nonzero(~vid)[0]
+    if tr.size:
+        rows |= set(rng.choice(tr, size=min(text, tr.size), replace=False).tolist())
+    stride = max(64, T // 400)
+    off = int(rng.integers(0, stride))
+    rows |= set(range(off, T, stride))
+    return np.array(sorted(r for r in rows if 0 <= r < T), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["36k", "128k"])
+def test_layer_full_size_sampled(name):
+    wl = synth.WORKLOADS[name]
+    flush("layer full-size %s" % name)
+    inp = synth.make_inputs(wl, DEV)
+    got = run_layer(wl, inp)
+    rows = _sample_rows(wl, seed=wl.index)
+    flush("  %d sampled rows" % len(rows))
+    compare_layer(wl, inp, got, rows)
+
+
+@pytest.mark.parametrize("variant", range(len(synth.SWEEP_VARIANTS)))
+def test_layer_sweep_sampled(variant):
+    n, w, gates = synth.SWEEP_VARIANTS[variant]
+    wl = synth.WORKLOADS["sweep"].with_(top_n=n, window=w, gates=gates)
+    flush("sweep n=%d w=%d gates=%s" % (n, w, gates))
+    inp = synth.make_inputs(wl, DEV)
+    got = run_layer(wl, inp)
+    rows = _sample_rows(wl, seed=variant, text=4, edge=16)[::3]
+    compare_layer(wl, inp, got, rows)
+
+
+def test_decode_with_compressed_cache():
+    wl = synth.WORKLOADS["decode"]
+    flush("decode B=%d L=%d" % (wl.batch, wl.kv_len))
+    inp = synth.make_inputs(wl, DEV)
+    # the compressed cache comes from the oracle, rounded to bf16, and feeds both sides
+    kcs, vcs = [], []
+    for b in range(wl.batch):
+        kcs.append(oracle.compress(host(inp["k"][b]), host(inp["w_k"]), 32, 16))
+        vcs.append(oracle.compress(host(inp["v"][b]), host(inp["w_v"]), 32, 16))
+    kc = torch.from_numpy(np.stack(kcs)).to(DEV).to(torch.bfloat16)
+    vc = torch.from_numpy(np.stack(vcs)).to(DEV).to(torch.bfloat16)
+    got = run_layer(wl, inp, k_cmp_in=kc, v_cmp_in=vc)
+    for b in range(wl.batch):
+        compare_layer(wl, inp, got, np.arange(1), b, kc=host(kc[b]).astype(np.float64),
+                      vc=host(vc[b]).astype(np.float64))
+
+
+@pytest.mark.parametrize("case", ["short", "no-cmp-block", "n-covers-all", "window-covers-all", "all-text"])
+def test_layer_edge_cases(case, path):
+    kw = dict(T=300, Hq=14, Hkv=2, lead=0, tail=0, n=8, w=64)
+    if case == "short":
+        kw.update(T=70)
+    elif case == "no-cmp-block":
+        kw.update(T=31)
+    elif case == "n-covers-all":
+        kw.update(T=500, n=16)
+    elif case == "window-covers-all":
+        kw.update(T=400, w=4096)
+    elif case == "all-text":
+        kw.update(lead=300)
+    wl = _wl(**kw)
+    flush("edge %s path=%s" % (case, path))
+    inp = synth.make_inputs(wl, DEV)
+    got = run_layer(wl, inp)
+    compare_layer(wl, inp, got, np.arange(wl.q_len))
+
+
+def test_layer_deterministic():
+    wl = _wl(T=3000, lead=128, tail=128)
+    inp = synth.make_inputs(wl, DEV)
+    a = run_layer(wl, inp)
+    b = run_layer(wl, inp)
+    for key in ("out", "o_cmp", "o_slc", "o_swa", "idx"):
+        assert torch.equal(a[key], b[key]), key
