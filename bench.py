@@ -1,0 +1,298 @@
+#!/usr/bin/env python
+"""Benchmark of the hybrid NSA layer forward pass on one MI355X.
+
+A step is one call of nsa_hybrid_layer_fwd (compression, compression-branch
+attention with block importance, top-n, selection and window branches, gated
+combine, dense text rows) on one batch of synthetic inputs already resident in
+HBM.  The headline workload is the 128K-token Qwen2.5-VL-7B-shaped prefill
+(tokens/s).  The same run also times the 16 x 64K decode step (GB/s of
+algorithmic bytes, rotating over independent caches so the working set is not
+served from the last-level cache), times each kernel family on its own with HIP
+events on the library's stream, and times the fp64 CPU oracle on a bounded row
+sample of the same prefill.
+
+Prints one JSON line.  Only N = 1 GPU is supported.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_MFMA = 2.5e15   # FLOP/s, MI355X dense bf16
+PEAK_HBM = 8.0e12         # B/s, MI355X HBM3E
+METRIC = "NSA layer prefill tokens/s @128K (MFMA util %); decode GB/s @64K"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="128k", choices=["128k", "36k", "sweep"])
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timing")
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--cpu-sample-rows", type=int, default=0, help="oracle row sample (0: auto)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def time_calls(fn, reps, stream):
+    """Average milliseconds per call of fn() over reps calls, HIP events on `stream`."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def prefill(args, wl):
+    import torch
+    from sparse_attention_long_fwd_amd import accounting, nsa, synth
+
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    log("generating %s inputs" % wl.name)
+    inp = synth.make_inputs(wl, dev)
+    q, k, v, g, vid = inp["q"], inp["k"], inp["v"], inp["gates"], inp["is_video"]
+    B, Tq, Hq, D = q.shape
+    Hkv = k.shape[2]
+    sh = nsa.make_shape(B, Tq, wl.kv_len, wl.q_start, Hq, Hkv, D)
+    pr = nsa.make_params(**wl.params())
+    dt = nsa.NSA_BF16 if wl.dtype == "bf16" else nsa.NSA_F32
+    ws = torch.empty(nsa.nsa_hybrid_layer_workspace_size(sh, pr, dt), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+
+    def step():
+        nsa.nsa_hybrid_layer_fwd(q, k, v, g, sh, pr, w_k=inp["w_k"], w_v=inp["w_v"], is_video=vid, out=out,
+                                 workspace=ws, stream=stream)
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("timing %d steps" % args.steps)
+    t0 = time.perf_counter()
+    ms = time_calls(step, args.steps, stream)
+    wall = time.perf_counter() - t0
+    fl = accounting.flops(wl)
+    res = dict(ms_per_step=ms, wall_s=wall, tokens_per_s=wl.q_len * wl.batch / (ms * 1e-3),
+               algo_flops=fl, mfma_util=fl["total"] / (ms * 1e-3) / PEAK_BF16_MFMA)
+    if not args.no_kernels:
+        res["kernels"] = kernel_times(args, wl, inp, sh, pr, stream)
+    del ws
+    return res, inp
+
+
+def kernel_times(args, wl, inp, sh, pr, stream):
+    """Each kernel family timed alone through its own entry point, same inputs."""
+    import torch
+    from sparse_attention_long_fwd_amd import accounting, nsa
+
+    q, k, v, g, vid = inp["q"], inp["k"], inp["v"], inp["gates"], inp["is_video"]
+    reps = max(2, args.steps)
+    kc, vc = nsa.nsa_compress_kv(k, v, inp["w_k"], inp["w_v"], wl.cmp_block, wl.cmp_stride)
+    t_cmpr = time_calls(lambda: nsa.nsa_compress_kv(k, v, inp["w_k"], inp["w_v"], wl.cmp_block, wl.cmp_stride,
+                                                    k_cmp=kc, v_cmp=vc, stream=stream), reps, stream)
+    o_cmp, lse, imp = nsa.nsa_cmp_attn_scores(q, kc, vc, sh, pr, is_video=vid)
+    t_cmp = time_calls(lambda: nsa.nsa_cmp_attn_scores(q, kc, vc, sh, pr, is_video=vid, o_cmp=o_cmp, lse=lse,
+                                                       importance=imp, stream=stream), reps, stream)
+    idx = nsa.nsa_topk_blocks(imp, sh, pr, is_video=vid)
+    t_topk = time_calls(lambda: nsa.nsa_topk_blocks(imp, sh, pr, is_video=vid, block_idx=idx, stream=stream),
+                        reps, stream)
+    out = torch.empty_like(q)
+    o_swa = torch.empty_like(q)
+    dt = nsa.NSA_BF16 if wl.dtype == "bf16" else nsa.NSA_F32
+    wsz = nsa.nsa_sparse_attn_workspace_size(sh, pr, dt)
+    ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=q.device)
+    t_sparse = time_calls(lambda: nsa.nsa_sparse_attn_fwd(q, k, v, sh, pr, idx, is_video=vid, o_cmp=o_cmp, gates=g,
+                                                          out=out, o_swa=o_swa, workspace=ws, stream=stream),
+                          reps, stream)
+    fl = accounting.flops(wl)
+    cmp_pf = fl["cmp"] / (t_cmp * 1e-3)
+    sp_pf = (fl["slc"] + fl["swa"] + fl["text"]) / (t_sparse * 1e-3)
+    kb = wl.batch * (wl.kv_len * wl.num_kv_heads * wl.head_dim * 2 * 2
+                     + 2 * nsa.num_cmp_blocks(wl.kv_len, wl.cmp_block, wl.cmp_stride) * wl.num_kv_heads
+                     * wl.head_dim * 2)
+    del ws, out, o_swa, imp
+    torch.cuda.empty_cache()
+    return {
+        "compress": dict(ms=t_cmpr, gbps=kb / (t_cmpr * 1e-3) / 1e9),
+        "cmp_attn_importance": dict(ms=t_cmp, algo_tflops=cmp_pf / 1e12, mfma_frac=cmp_pf / PEAK_BF16_MFMA),
+        "topk": dict(ms=t_topk),
+        "sparse_window_text_combine": dict(ms=t_sparse, algo_tflops=sp_pf / 1e12, mfma_frac=sp_pf / PEAK_BF16_MFMA),
+    }
+
+
+def decode(args):
+    """16 x 64K decode step, rotating over 4 independent caches."""
+    import torch
+    from sparse_attention_long_fwd_amd import nsa, synth
+
+    wl = synth.WORKLOADS["decode"]
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    sets = []
+    n_rot = 4
+    for r in range(n_rot):
+        log("decode cache %d" % r)
+        inp = synth.make_inputs(wl, dev, batch_offset=wl.batch * r)
+        kc, vc = nsa.nsa_compress_kv(inp["k"], inp["v"], inp["w_k"], inp["w_v"], wl.cmp_block, wl.cmp_stride)
+        inp["kc"], inp["vc"] = kc, vc
+        sets.append(inp)
+    q0 = sets[0]["q"]
+    B, Tq, Hq, D = q0.shape
+    Hkv = sets[0]["k"].shape[2]
+    sh = nsa.make_shape(B, Tq, wl.kv_len, wl.q_start, Hq, Hkv, D)
+    pr = nsa.make_params(**wl.params())
+    ws = torch.empty(nsa.nsa_hybrid_layer_workspace_size(sh, pr, nsa.NSA_BF16), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(s["q"]) for s in sets]
+    idxs = [torch.full((B, Tq, Hkv, wl.top_n), -1, dtype=torch.int32, device=dev) for _ in sets]
+    state = {"i": 0}
+
+    def step():
+        i = state["i"] % n_rot
+        s = sets[i]
+        nsa.nsa_hybrid_layer_fwd(s["q"], s["k"], s["v"], s["gates"], sh, pr, k_cmp_in=s["kc"], v_cmp_in=s["vc"],
+                                 is_video=s["is_video"], out=outs[i], block_idx_out=idxs[i], workspace=ws,
+                                 stream=stream)
+        state["i"] += 1
+
+    for _ in range(2 * n_rot):
+        step()
+    ms = time_calls(step, args.decode_steps, stream)
+    # algorithmic bytes: compressed cache + the union of selected-block and window tokens, each once,
+    # plus q, out and gates
+    L = wl.kv_len
+    t = wl.q_start
+    Nc = nsa.num_cmp_blocks(L, wl.cmp_block, wl.cmp_stride)
+    total = 0
+    for i in range(n_rot):
+        idx = idxs[i].cpu().numpy()
+        for b in range(B):
+            for g in range(Hkv):
+                toks = set(range(max(0, t - wl.window + 1), t + 1))
+                for j in idx[b, 0, g]:
+                    if j >= 0:
+                        toks |= set(range(j * wl.sel_block, min((j + 1) * wl.sel_block, t + 1)))
+                total += (2 * Nc + 2 * len(toks)) * D * 2
+    total = total / n_rot + B * Hq * D * 2 * 2 + B * Hq * 3 * 4
+    bw = total / (ms * 1e-3)
+    return dict(workload=wl.name, ms_per_step=ms, algo_bytes=total, gbps=bw / 1e9, hbm_frac=bw / PEAK_HBM,
+                rotating_caches=n_rot, steps=args.decode_steps)
+
+
+def cpu_baseline(args, wl, inp):
+    """The fp64 oracle on a bounded row sample of the same prefill (rank 0)."""
+    import torch
+    import oracle
+
+    def host(t):
+        return (t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy()
+
+    k, v = host(inp["k"][0]), host(inp["v"][0])
+    q = inp["q"][0]
+    vid = inp["is_video"][0].cpu().numpy().astype(bool)
+    T = wl.q_len
+    n_rows = args.cpu_sample_rows or 192
+    vr = np.nonzero(vid)[0]
+    tr = np.nonzero(~vid)[0]
+    rng = np.random.default_rng(wl.index)
+    stride = max(1, len(vr) // n_rows)
+    rows = vr[int(rng.integers(0, stride))::stride][:n_rows]
+    trows = tr[::max(1, len(tr) // 4)][:4] if tr.size else tr
+    sample = np.concatenate([rows, trows])
+    oracle.build()
+    t0 = time.perf_counter()
+    oracle.layer(host(q), k, v, host(inp["w_k"]), host(inp["w_v"]), host(inp["gates"][0]), vid.astype(np.uint8),
+                 wl.params(), rows=sample)
+    dt = time.perf_counter() - t0
+    # extrapolate: video rows and text rows timed together; scale by row counts
+    rows_per_s = len(sample) / dt
+    frac_text = len(trows) / max(1, len(sample))
+    return dict(value=rows_per_s, unit="tokens/s (rows/s, extrapolated from the sample)", cores=oracle.num_threads(),
+                kind="oracle", seconds=dt,
+                sample="%d video rows (every %d-th at a seeded offset) + %d text rows of the %d-row %s prefill, "
+                       "compression of the whole sequence included" % (len(rows), stride, len(trows), T, wl.name))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the layer shards by GQA group (up to 4 ways) and then by rows, "
+              "but no multi-GPU path is built; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparse_attention_long_fwd_amd import nsa, synth
+
+    nsa.lib()
+    torch.cuda.init()
+    wl = synth.WORKLOADS[args.workload]
+    res, inp = prefill(args, wl)
+    dec = None
+    ker = res.get("kernels", {})
+    dom_name, dom = None, None
+    for name, kk in ker.items():
+        if dom is None or kk["ms"] > dom["ms"]:
+            dom_name, dom = name, kk
+    roofline = None
+    if dom is not None:
+        if "algo_tflops" in dom:
+            roofline = dict(kernel=dom_name, bound="mfma", achieved=dom["algo_tflops"], peak=PEAK_BF16_MFMA / 1e12,
+                            unit="TFLOP/s", frac=dom["mfma_frac"], traffic=None)
+        else:
+            roofline = dict(kernel=dom_name, bound="hbm", achieved=dom.get("gbps"), peak=PEAK_HBM / 1e9,
+                            unit="GB/s", frac=(dom.get("gbps") or 0) * 1e9 / PEAK_HBM, traffic=None)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("oracle timing")
+        cpu = cpu_baseline(args, wl, inp)
+    del inp
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        log("decode")
+        dec = decode(args)
+    line = {
+        "metric": METRIC,
+        "value": res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64/Box-Muller; frame-correlated video K)",
+        "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.kv_len, "q_heads": wl.num_q_heads,
+                   "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "top_n": wl.top_n, "window": wl.window,
+                   "cmp_block": wl.cmp_block, "cmp_stride": wl.cmp_stride, "sel_block": wl.sel_block,
+                   "text_tokens": wl.text_lead + wl.text_tail, "parallelism": "single GPU"},
+        "mfma_util_algorithmic": res["mfma_util"],
+        "algo_flops": res["algo_flops"],
+        "kernels": ker,
+        "roofline": roofline,
+        "decode": dec,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

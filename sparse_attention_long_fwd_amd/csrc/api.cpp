@@ -107,7 +107,7 @@ LayerWs layer_ws(const Dims& dm, int32_t dtype) {
   LayerWs w{};
   const size_t es = esize(dtype);
   // compressed keys / values computed inside the layer stay fp32 (no extra rounding step)
-  w.kc = round_up((size_t)dm.B * dm.Nc * dm.Hkv * dm.D * 4);
+  w.kc = round_up((size_t)dm.B * dm.Nc * dm.Hkv * dm.D * 2) * 2;
   w.vc = w.kc;
   w.o_cmp = round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * es);
   w.lse = round_up((size_t)dm.B * dm.Tq * dm.Hq * 4);
@@ -119,9 +119,12 @@ LayerWs layer_ws(const Dims& dm, int32_t dtype) {
   return w;
 }
 
-int run_cmp(int32_t dtype, int32_t cdtype, const Dims& dm, const void* q, const void* kc, const void* vc,
-            const uint8_t* vid, void* o, float* lse, float* imp, hipStream_t s) {
-  hipError_t e = use_fast(dtype, dm) ? launch_cmp_fast(cdtype, dm, q, kc, vc, vid, o, lse, imp, s)
+// kc/vc: compressed keys/values (bf16 high parts on the MFMA path, or cdtype on the generic path);
+// kl/vl: low parts on the MFMA path when the layer compressed them itself.
+int run_cmp(int32_t dtype, int32_t cdtype, const Dims& dm, const void* q, const void* kc, const void* kl,
+            const void* vc, const void* vl, const uint8_t* vid, void* o, float* o32, float* lse, float* imp,
+            hipStream_t s) {
+  hipError_t e = use_fast(dtype, dm) ? launch_cmp_fast(dm, q, kc, kl, vc, vl, vid, o, o32, lse, imp, s)
                                      : launch_cmp_generic(dtype, cdtype, dm, q, kc, vc, vid, o, lse, imp, s);
   if (e != hipSuccess) return hip_fail(e, "compression-branch kernel");
   return NSA_OK;
@@ -181,11 +184,11 @@ int32_t nsa_compress_kv(const void* k, const void* v, int32_t dtype, int64_t bat
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_cmp) || !aligned16(v_cmp))
     return fail(NSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_compress(dtype, dtype, k, w_k, k_cmp, batch, kv_len, num_kv_heads, head_dim, cmp_block,
+  hipError_t e = launch_compress(dtype, 0, k, w_k, k_cmp, nullptr, batch, kv_len, num_kv_heads, head_dim, cmp_block,
                                  cmp_stride, Nc, s);
   if (e == hipSuccess)
-    e = launch_compress(dtype, dtype, v, w_v, v_cmp, batch, kv_len, num_kv_heads, head_dim, cmp_block, cmp_stride,
-                        Nc, s);
+    e = launch_compress(dtype, 0, v, w_v, v_cmp, nullptr, batch, kv_len, num_kv_heads, head_dim, cmp_block,
+                        cmp_stride, Nc, s);
   if (e != hipSuccess) return hip_fail(e, "compress kernel");
   return NSA_OK;
 }
@@ -204,7 +207,8 @@ int32_t nsa_cmp_attn_scores(const void* q, const void* k_cmp, const void* v_cmp,
     return fail(NSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
   if (!use_fast(dtype, dm) && dm.Ns > 16384)
     return fail(NSA_ERR_UNSUPPORTED, "generic kernel handles at most 16384 selection blocks");
-  return run_cmp(dtype, dtype, dm, q, k_cmp, v_cmp, is_video, o_cmp, lse, importance, (hipStream_t)stream);
+  return run_cmp(dtype, dtype, dm, q, k_cmp, nullptr, v_cmp, nullptr, is_video, o_cmp, nullptr, lse, importance,
+                 (hipStream_t)stream);
 }
 
 int32_t nsa_topk_blocks(const float* importance, const nsa_shape* shape, const nsa_params* params,
@@ -301,19 +305,30 @@ int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const 
 
   const void* kc_use = k_cmp_in;
   const void* vc_use = v_cmp_in;
+  const void* kl_use = nullptr;
+  const void* vl_use = nullptr;
   int32_t cdtype = dtype;
   if (!kc_use) {
-    hipError_t e = launch_compress(dtype, NSA_F32, k, w_k, kc, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d, dm.Nc, s);
+    // Compressed inside the layer, carried at fp32 precision: the MFMA path as bf16 high + low
+    // parts (both enter every product), the generic path as fp32.
+    const bool fast = use_fast(dtype, dm);
+    const size_t half = w.kc / 2;
+    void* kl = fast ? (char*)kc + half : nullptr;
+    void* vl = fast ? (char*)vc + half : nullptr;
+    hipError_t e = launch_compress(dtype, fast ? 2 : 1, k, w_k, kc, kl, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d,
+                                   dm.Nc, s);
     if (e == hipSuccess)
-      e = launch_compress(dtype, NSA_F32, v, w_v, vc, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d, dm.Nc, s);
+      e = launch_compress(dtype, fast ? 2 : 1, v, w_v, vc, vl, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d, dm.Nc, s);
     if (e != hipSuccess) return hip_fail(e, "compress kernel");
     kc_use = kc;
     vc_use = vc;
-    cdtype = NSA_F32;
+    kl_use = kl;
+    vl_use = vl;
+    cdtype = fast ? dtype : NSA_F32;
   }
   void* ocmp = o_cmp ? o_cmp : ocmp_ws;
   int32_t* idx = block_idx_out ? block_idx_out : idx_ws;
-  st = run_cmp(dtype, cdtype, dm, q, kc_use, vc_use, is_video, ocmp, lse, imp, s);
+  st = run_cmp(dtype, cdtype, dm, q, kc_use, kl_use, vc_use, vl_use, is_video, ocmp, nullptr, lse, imp, s);
   if (st != NSA_OK) return st;
   hipError_t e = launch_topk(dm, imp, is_video, idx, s);
   if (e != hipSuccess) return hip_fail(e, "top-n kernel");

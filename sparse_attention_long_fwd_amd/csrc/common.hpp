@@ -66,9 +66,9 @@ __device__ __forceinline__ float block_sum(float x, float* scratch) {
 
 // ---------------------------------------------------------------------------
 // Launchers (host side), one per kernel family.  dtype: 0 = fp32, 1 = bf16.
-// out_dtype: element type of the compressed output (the input's, or fp32).
-hipError_t launch_compress(int dtype, int out_dtype, const void* x, const float* w, void* out, int64_t B, int64_t T,
-                           int H, int D, int l, int d, int64_t Nc, hipStream_t s);
+// out_mode: 0 = the input's type, 1 = fp32, 2 = bf16 high part (out) + low part (out_lo).
+hipError_t launch_compress(int dtype, int out_mode, const void* x, const float* w, void* out, void* out_lo,
+                           int64_t B, int64_t T, int H, int D, int l, int d, int64_t Nc, hipStream_t s);
 
 // cdtype: element type of the compressed keys / values (dtype or fp32).
 hipError_t launch_cmp_generic(int dtype, int cdtype, const Dims& dm, const void* q, const void* kc, const void* vc,

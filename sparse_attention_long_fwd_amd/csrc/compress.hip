@@ -7,7 +7,9 @@
 // streams the block's tokens with 16-byte loads; neighbouring threads cover the
 // rest of the token row, so every load instruction of a wave reads whole
 // contiguous rows.  Blocks overlap by cmp_block - cmp_stride tokens; the second
-// read of a token hits in L2.
+// read of a token hits in L2.  Sums are fp32; the result is stored in the input
+// type, in fp32, or as a bf16 high part plus a bf16 low part (hi + lo carries
+// the fp32 sum to within 2^-16 relative), as the caller asks.
 #include "common.hpp"
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
@@ -33,10 +35,11 @@ __device__ __forceinline__ void store8(float* p, const float* f) {
   *(float4*)(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
 }
 
-template <typename T, typename TO>
+// MODE 0: output in TO; MODE 2: bf16 high part to out, low part to out_lo.
+template <typename T, typename TO, int MODE>
 __global__ void __launch_bounds__(256) compress_kernel(const T* __restrict__ x, const float* __restrict__ w,
-                                                       TO* __restrict__ out, int64_t T_len, int H, int D, int l,
-                                                       int d, int64_t Nc, int64_t total) {
+                                                       TO* __restrict__ out, bf16* __restrict__ out_lo, int64_t T_len,
+                                                       int H, int D, int l, int d, int64_t Nc, int64_t total) {
   extern __shared__ float ws[];
   for (int m = threadIdx.x; m < l; m += blockDim.x) ws[m] = w[m];
   __syncthreads();
@@ -59,21 +62,39 @@ __global__ void __launch_bounds__(256) compress_kernel(const T* __restrict__ x, 
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = fmaf(wm, f[e], acc[e]);
   }
-  store8(out + ((b * Nc + i) * H + h) * (int64_t)D + c * 8, acc);
+  const int64_t o = ((b * Nc + i) * H + h) * (int64_t)D + c * 8;
+  if constexpr (MODE == 2) {
+    bf16x8_t hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      hi[e] = (bf16)acc[e];
+      lo[e] = (bf16)(acc[e] - (float)hi[e]);
+    }
+    *(bf16x8_t*)((bf16*)out + o) = hi;
+    *(bf16x8_t*)(out_lo + o) = lo;
+  } else {
+    store8(out + o, acc);
+  }
 }
 
-hipError_t launch_compress(int dtype, int out_dtype, const void* x, const float* w, void* out, int64_t B, int64_t T,
-                           int H, int D, int l, int d, int64_t Nc, hipStream_t s) {
+hipError_t launch_compress(int dtype, int out_mode, const void* x, const float* w, void* out, void* out_lo,
+                           int64_t B, int64_t T, int H, int D, int l, int d, int64_t Nc, hipStream_t s) {
   if (Nc <= 0 || B <= 0) return hipSuccess;
   int64_t total = B * Nc * H * (D / 8);
   dim3 grid((unsigned)((total + 255) / 256)), block(256);
   size_t shm = sizeof(float) * (size_t)l;
-  if (dtype == 1 && out_dtype == 1)
-    compress_kernel<bf16, bf16><<<grid, block, shm, s>>>((const bf16*)x, w, (bf16*)out, T, H, D, l, d, Nc, total);
-  else if (dtype == 1)
-    compress_kernel<bf16, float><<<grid, block, shm, s>>>((const bf16*)x, w, (float*)out, T, H, D, l, d, Nc, total);
-  else
-    compress_kernel<float, float><<<grid, block, shm, s>>>((const float*)x, w, (float*)out, T, H, D, l, d, Nc,
-                                                           total);
+  if (dtype == 1) {
+    const bf16* xi = (const bf16*)x;
+    if (out_mode == 2)
+      compress_kernel<bf16, bf16, 2><<<grid, block, shm, s>>>(xi, w, (bf16*)out, (bf16*)out_lo, T, H, D, l, d, Nc,
+                                                             total);
+    else if (out_mode == 1)
+      compress_kernel<bf16, float, 0><<<grid, block, shm, s>>>(xi, w, (float*)out, nullptr, T, H, D, l, d, Nc, total);
+    else
+      compress_kernel<bf16, bf16, 0><<<grid, block, shm, s>>>(xi, w, (bf16*)out, nullptr, T, H, D, l, d, Nc, total);
+  } else {
+    compress_kernel<float, float, 0><<<grid, block, shm, s>>>((const float*)x, w, (float*)out, nullptr, T, H, D, l,
+                                                              d, Nc, total);
+  }
   return hipGetLastError();
 }

@@ -1,0 +1,60 @@
+// Helpers shared by the MFMA kernels: XCD-aware work mapping.
+#pragma once
+#include "fast.hpp"
+#include "mfma.hpp"
+
+// MI355X dispatches consecutive workgroups round-robin over its 8 XCDs, each
+// with a private L2.  Work is made of `units` independent (batch, KV group)
+// streams of `per_unit` items; the remap sends every XCD the items of as few
+// units as possible (a unit's compressed K/V stays in that XCD's L2) and keeps
+// each XCD's items in rank order, so rank 0 (the heaviest tile, by convention
+// of the callers) starts first everywhere.
+__host__ __device__ inline unsigned xcd_grid(int units, int per_unit) {
+  if (units <= 8 && 8 % units == 0) {
+    const int P = 8 / units;
+    return 8u * (unsigned)((per_unit + P - 1) / P);
+  }
+  return (unsigned)units * (unsigned)per_unit;
+}
+
+__device__ __forceinline__ bool xcd_remap(unsigned id, int units, int per_unit, int* unit, int* rank) {
+  const int xcd = (int)(id & 7u), k = (int)(id >> 3);
+  if (units <= 8 && 8 % units == 0) {
+    const int P = 8 / units;
+    *unit = xcd / P;
+    *rank = k * P + xcd % P;
+  } else if (units % 8 == 0) {
+    const int per = units / 8;
+    *unit = xcd * per + k % per;
+    *rank = k / per;
+  } else {
+    *unit = (int)(id % (unsigned)units);
+    *rank = (int)(id / (unsigned)units);
+  }
+  return *rank < per_unit;
+}
+
+// Element offset of (row, 16-byte chunk c) in an LDS tile of 128-element bf16
+// rows whose chunks are XOR-swizzled by the row: 16 consecutive rows reading
+// the same logical chunk land on 16 different chunk positions (banks).
+__device__ __forceinline__ int swz128(int row, int c) { return row * 128 + ((c ^ (row & 15)) << 3); }
+
+// Stage rows [key0, key0 + 64) of a [*, 128] bf16 array (row stride `stride`
+// elements) into a swizzled 64 x 128 LDS tile with direct global -> LDS loads
+// (16 bytes a lane, lane i of an instruction lands at base + 16 i).  Rows at or
+// past `nrows` repeat row nrows - 1: finite data that the callers' masks never
+// weight.  Instruction m of wave w covers LDS chunks [64 (w + nw m), +64), i.e.
+// four rows.  The caller waits (s_waitcnt vmcnt) and synchronises before use.
+__device__ __forceinline__ void stage_tile64(bf16* lds_tile, const bf16* src, int64_t stride, int64_t key0,
+                                             int64_t nrows, int w, int nw, int lane) {
+  for (int ins = w; ins < 16; ins += nw) {
+    const int p = ins * 64 + lane;  // LDS chunk position
+    const int row = p >> 4, cpos = p & 15;
+    const int c = cpos ^ (row & 15);  // logical chunk stored at this position
+    int64_t key = key0 + row;
+    if (key >= nrows) key = nrows - 1;
+    const bf16* gp = src + key * stride + c * 8;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gp,
+                                     (__attribute__((address_space(3))) void*)(lds_tile + ins * 512), 16, 0, 0);
+  }
+}

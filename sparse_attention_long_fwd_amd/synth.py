@@ -180,8 +180,12 @@ def video_mask(wl: Workload, device="cpu") -> torch.Tensor:
     return vid.to(torch.uint8).unsqueeze(0).expand(wl.batch, wl.q_len).contiguous()
 
 
-def make_inputs(wl: Workload, device="cpu") -> Dict[str, torch.Tensor]:
-    """All inputs of one workload, rounded to its dtype (gates and weights stay fp32)."""
+def make_inputs(wl: Workload, device="cpu", batch_offset: int = 0) -> Dict[str, torch.Tensor]:
+    """All inputs of one workload, rounded to its dtype (gates and weights stay fp32).
+
+    ``batch_offset`` shifts the batch index used in the seeds, so that several
+    independent copies of a workload (e.g. rotating decode caches) can be drawn.
+    """
     dt = wl.torch_dtype
     B, T, Tq, Hq, Hkv, D = wl.batch, wl.kv_len, wl.q_len, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     base = 1000 * wl.index
@@ -192,7 +196,7 @@ def make_inputs(wl: Workload, device="cpu") -> Dict[str, torch.Tensor]:
     n_video = T - wl.text_lead - wl.text_tail
     n_frames = (n_video + wl.frame - 1) // wl.frame
     for b in range(B):
-        sb = base + 100 * b
+        sb = base + 100 * (b + batch_offset)
         normal(sb + STREAM_Q, (Tq, Hq, D), device, out=q[b])
         normal(sb + STREAM_V, (T, Hkv, D), device, out=v[b])
         if wl.frame_corr and n_video > 0:
