@@ -109,11 +109,12 @@ LayerWs layer_ws(const Dims& dm, int32_t dtype) {
   // compressed keys / values computed inside the layer stay fp32 (no extra rounding step)
   w.kc = round_up((size_t)dm.B * dm.Nc * dm.Hkv * dm.D * 2) * 2;
   w.vc = w.kc;
-  w.o_cmp = round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * es);
+  // branch output of the compression path: fp32 on the MFMA path (read by the combine), dtype otherwise
+  w.o_cmp = round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * (fast_supported(dtype, dm) ? 4 : es));
   w.lse = round_up((size_t)dm.B * dm.Tq * dm.Hq * 4);
   w.imp = round_up((size_t)dm.B * dm.Tq * dm.Hkv * dm.Ns * 4);
   w.idx = round_up((size_t)dm.B * dm.Tq * dm.Hkv * dm.n * 4);
-  w.o_swa = round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * es);
+  w.o_swa = fast_supported(dtype, dm) ? 0 : round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * es);
   w.sparse = sparse_ws(dm, dtype).total;
   w.total = w.kc + w.vc + w.o_cmp + w.lse + w.imp + w.idx + w.o_swa + w.sparse;
   return w;
@@ -131,10 +132,10 @@ int run_cmp(int32_t dtype, int32_t cdtype, const Dims& dm, const void* q, const 
 }
 
 int run_sparse(int32_t dtype, const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
-               const uint8_t* vid, const void* o_cmp, const float* gates, void* out, void* o_slc, void* o_swa,
-               void* ws, hipStream_t s) {
+               const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out, void* o_slc,
+               void* o_swa, void* ws, hipStream_t s) {
   hipError_t e = use_fast(dtype, dm)
-                     ? launch_sparse_fast(dm, q, k, v, idx, vid, o_cmp, gates, out, o_slc, o_swa, ws, s)
+                     ? launch_sparse_fast(dm, q, k, v, idx, vid, o_cmp, ocmp_f32, gates, out, o_slc, o_swa, ws, s)
                      : launch_sparse_generic(dtype, dm, q, k, v, idx, vid, o_cmp, gates, out, o_slc, o_swa, s);
   if (e != hipSuccess) return hip_fail(e, "selection/window kernel");
   return NSA_OK;
@@ -250,7 +251,7 @@ int32_t nsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t
   if (fast && workspace_bytes < w.total)
     return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, w.total);
   if (fast && w.total > 0 && !workspace) return fail(NSA_ERR_INVALID_ARG, "NULL workspace");
-  return run_sparse(dtype, dm, q, k, v, block_idx, is_video, o_cmp, gates, out, o_slc, o_swa, workspace,
+  return run_sparse(dtype, dm, q, k, v, block_idx, is_video, o_cmp, false, gates, out, o_slc, o_swa, workspace,
                     (hipStream_t)stream);
 }
 
@@ -326,14 +327,18 @@ int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const 
     vl_use = vl;
     cdtype = fast ? dtype : NSA_F32;
   }
-  void* ocmp = o_cmp ? o_cmp : ocmp_ws;
+  const bool fast = use_fast(dtype, dm);
+  // MFMA path: the combine reads an fp32 copy of the compression output; the caller's bf16 copy is optional
+  void* ocmp = fast ? o_cmp : (o_cmp ? o_cmp : ocmp_ws);
+  float* ocmp32 = fast ? (float*)ocmp_ws : nullptr;
   int32_t* idx = block_idx_out ? block_idx_out : idx_ws;
-  st = run_cmp(dtype, cdtype, dm, q, kc_use, kl_use, vc_use, vl_use, is_video, ocmp, nullptr, lse, imp, s);
+  st = run_cmp(dtype, cdtype, dm, q, kc_use, kl_use, vc_use, vl_use, is_video, ocmp, ocmp32, lse, imp, s);
   if (st != NSA_OK) return st;
   hipError_t e = launch_topk(dm, imp, is_video, idx, s);
   if (e != hipSuccess) return hip_fail(e, "top-n kernel");
+  if (fast) return run_sparse(dtype, dm, q, k, v, idx, is_video, ocmp32, true, gates, out, o_slc, o_swa, sparse_ws_ptr, s);
   void* oswa = o_swa ? o_swa : oswa_ws;
-  return run_sparse(dtype, dm, q, k, v, idx, is_video, ocmp, gates, out, o_slc, oswa, sparse_ws_ptr, s);
+  return run_sparse(dtype, dm, q, k, v, idx, is_video, ocmp, false, gates, out, o_slc, oswa, sparse_ws_ptr, s);
 }
 
 }  // extern "C"

@@ -1,15 +1,33 @@
 // Dispatch of the MFMA path: coverage test, workspace sizes, launch order.
 #include "fast_common.hpp"
 
+hipError_t launch_flash_fast(const Dims& dm, const void* q, const void* k, const void* v, const uint8_t* vid,
+                             float* swa32, void* swa_bf, void* text, void* ws, hipStream_t s);
+size_t flash_workspace(const Dims& dm);
+hipError_t launch_slc_fast(const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
+                           const uint8_t* vid, const void* ocmp, bool ocmp_f32, const float* swa32,
+                           const float* gates, void* out, void* o_slc, hipStream_t s);
+
 bool fast_supported(int32_t dtype, const Dims& dm) {
   return dtype == 1 && dm.D == 128 && dm.l == 32 && dm.d == 16 && dm.ls == 64 && dm.G >= 4 && dm.G <= 8 &&
          dm.n <= 32;
 }
 
-size_t fast_sparse_workspace(const Dims& dm) { return 0; }
+static size_t rup(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// [window output, fp32][split partials of long text rows]
+size_t fast_sparse_workspace(const Dims& dm) {
+  return rup((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 4) + rup(flash_workspace(dm));
+}
 
 hipError_t launch_sparse_fast(const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
-                              const uint8_t* vid, const void* o_cmp, const float* gates, void* out, void* o_slc,
-                              void* o_swa, void* ws, hipStream_t s) {
-  return launch_sparse_generic(1, dm, q, k, v, idx, vid, o_cmp, gates, out, o_slc, o_swa, s);
+                              const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out,
+                              void* o_slc, void* o_swa, void* ws, hipStream_t s) {
+  float* swa32 = (float*)ws;
+  void* part = (char*)ws + rup((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 4);
+  // window branch (fp32 for the combine, bf16 copy if asked) and dense text rows
+  hipError_t e = launch_flash_fast(dm, q, k, v, vid, swa32, o_swa, out, part, s);
+  if (e != hipSuccess) return e;
+  // selection branch and the gated combine of video rows
+  return launch_slc_fast(dm, q, k, v, idx, vid, o_cmp, ocmp_f32, swa32, gates, out, o_slc, s);
 }
