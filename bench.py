@@ -2,14 +2,16 @@
 """Benchmark of the hybrid NSA layer forward pass on one MI355X.
 
 A step is one call of nsa_hybrid_layer_fwd (compression, compression-branch
-attention with block importance, top-n, selection and window branches, gated
-combine, dense text rows) on one batch of synthetic inputs already resident in
+attention with block importance, top-n, window and text rows, selection branch
+with the gated combine) on one batch of synthetic inputs already resident in
 HBM.  The headline workload is the 128K-token Qwen2.5-VL-7B-shaped prefill
-(tokens/s).  The same run also times the 16 x 64K decode step (GB/s of
-algorithmic bytes, rotating over independent caches so the working set is not
-served from the last-level cache), times each kernel family on its own with HIP
-events on the library's stream, and times the fp64 CPU oracle on a bounded row
-sample of the same prefill.
+(tokens/s).  The same run also
+
+* times every phase of the layer with HIP events recorded by the library on its
+  own stream (a second, profiled pass over the same steps),
+* times the 16 x 64K decode step (GB/s of algorithmic bytes), rotating over
+  independent caches so the working set is not served from the last-level cache,
+* times the fp64 CPU oracle on a bounded row sample of the same prefill.
 
 Prints one JSON line.  Only N = 1 GPU is supported.
 """
@@ -17,8 +19,6 @@ from __future__ import annotations
 
 import argparse
 import json
-import math
-import os
 import sys
 import time
 
@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--workload", default="128k", choices=["128k", "36k", "sweep"])
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timing")
+    ap.add_argument("--no-kernels", action="store_true", help="skip the per-phase timing pass")
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--cpu-sample-rows", type=int, default=0, help="oracle row sample (0: auto)")
     return ap.parse_args()
@@ -59,6 +59,42 @@ def time_calls(fn, reps, stream):
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / reps
+
+
+def phase_rates(wl, ms):
+    """Algorithmic rates per phase: FLOPs for the attention phases, bytes for the rest."""
+    from sparse_attention_long_fwd_amd import accounting, nsa
+
+    fl = accounting.flops(wl)
+    B, T, Tq, Hq, Hkv, D = wl.batch, wl.kv_len, wl.q_len, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    Nc = nsa.num_cmp_blocks(T, wl.cmp_block, wl.cmp_stride)
+    pos = np.arange(wl.q_start, wl.q_start + Tq)
+    vid = (pos >= wl.text_lead) & (pos < T - wl.text_tail)
+    # compress: read K and V once, write compressed keys and values (bf16 high + low parts)
+    b_cmpr = B * (2 * T * Hkv * D * 2 + 2 * 2 * Nc * Hkv * D * 2)
+    # top-n: read each video row's candidate importances (blocks 0 .. t / 64), write the chosen blocks
+    b_topk = B * Hkv * (int((pos[vid] // wl.sel_block + 1).sum()) * 4 + int(vid.sum()) * wl.top_n * 4)
+    # selection: the chosen blocks' K and V, per (video row, group)
+    slc_keys = accounting.slc_keys(pos[vid], wl.sel_block, wl.top_n).sum()
+    b_slc = B * Hkv * int(slc_keys) * D * 2 * 2
+    out = {}
+    names = ("compress", "cmp_attn_importance", "topk", "window_text", "selection_combine")
+    for name, t in zip(names, ms):
+        d = dict(ms=t)
+        if name == "compress":
+            d.update(bound="hbm", algo_bytes=b_cmpr, gbps=b_cmpr / (t * 1e-3) / 1e9)
+        elif name == "topk":
+            d.update(bound="hbm", algo_bytes=b_topk, gbps=b_topk / (t * 1e-3) / 1e9)
+        elif name == "cmp_attn_importance":
+            d.update(bound="mfma", algo_flops=fl["cmp"], tflops=fl["cmp"] / (t * 1e-3) / 1e12)
+        elif name == "window_text":
+            f = fl["swa"] + fl["text"]
+            d.update(bound="mfma", algo_flops=f, tflops=f / (t * 1e-3) / 1e12)
+        else:
+            d.update(bound="gather", algo_flops=fl["slc"], tflops=fl["slc"] / (t * 1e-3) / 1e12,
+                     gather_bytes=b_slc, gather_gbps=b_slc / (t * 1e-3) / 1e9)
+        out[name] = d
+    return out
 
 
 def prefill(args, wl):
@@ -94,49 +130,17 @@ def prefill(args, wl):
     res = dict(ms_per_step=ms, wall_s=wall, tokens_per_s=wl.q_len * wl.batch / (ms * 1e-3),
                algo_flops=fl, mfma_util=fl["total"] / (ms * 1e-3) / PEAK_BF16_MFMA)
     if not args.no_kernels:
-        res["kernels"] = kernel_times(args, wl, inp, sh, pr, stream)
+        log("per-phase timing (%d steps)" % args.steps)
+        nsa.profile_enable(True)
+        acc = None
+        for _ in range(args.steps):
+            step()
+            ph = np.array(nsa.profile_read())
+            acc = ph if acc is None else acc + ph
+        nsa.profile_enable(False)
+        res["kernels"] = phase_rates(wl, list(acc / args.steps))
     del ws
     return res, inp
-
-
-def kernel_times(args, wl, inp, sh, pr, stream):
-    """Each kernel family timed alone through its own entry point, same inputs."""
-    import torch
-    from sparse_attention_long_fwd_amd import accounting, nsa
-
-    q, k, v, g, vid = inp["q"], inp["k"], inp["v"], inp["gates"], inp["is_video"]
-    reps = max(2, args.steps)
-    kc, vc = nsa.nsa_compress_kv(k, v, inp["w_k"], inp["w_v"], wl.cmp_block, wl.cmp_stride)
-    t_cmpr = time_calls(lambda: nsa.nsa_compress_kv(k, v, inp["w_k"], inp["w_v"], wl.cmp_block, wl.cmp_stride,
-                                                    k_cmp=kc, v_cmp=vc, stream=stream), reps, stream)
-    o_cmp, lse, imp = nsa.nsa_cmp_attn_scores(q, kc, vc, sh, pr, is_video=vid)
-    t_cmp = time_calls(lambda: nsa.nsa_cmp_attn_scores(q, kc, vc, sh, pr, is_video=vid, o_cmp=o_cmp, lse=lse,
-                                                       importance=imp, stream=stream), reps, stream)
-    idx = nsa.nsa_topk_blocks(imp, sh, pr, is_video=vid)
-    t_topk = time_calls(lambda: nsa.nsa_topk_blocks(imp, sh, pr, is_video=vid, block_idx=idx, stream=stream),
-                        reps, stream)
-    out = torch.empty_like(q)
-    o_swa = torch.empty_like(q)
-    dt = nsa.NSA_BF16 if wl.dtype == "bf16" else nsa.NSA_F32
-    wsz = nsa.nsa_sparse_attn_workspace_size(sh, pr, dt)
-    ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=q.device)
-    t_sparse = time_calls(lambda: nsa.nsa_sparse_attn_fwd(q, k, v, sh, pr, idx, is_video=vid, o_cmp=o_cmp, gates=g,
-                                                          out=out, o_swa=o_swa, workspace=ws, stream=stream),
-                          reps, stream)
-    fl = accounting.flops(wl)
-    cmp_pf = fl["cmp"] / (t_cmp * 1e-3)
-    sp_pf = (fl["slc"] + fl["swa"] + fl["text"]) / (t_sparse * 1e-3)
-    kb = wl.batch * (wl.kv_len * wl.num_kv_heads * wl.head_dim * 2 * 2
-                     + 2 * nsa.num_cmp_blocks(wl.kv_len, wl.cmp_block, wl.cmp_stride) * wl.num_kv_heads
-                     * wl.head_dim * 2)
-    del ws, out, o_swa, imp
-    torch.cuda.empty_cache()
-    return {
-        "compress": dict(ms=t_cmpr, gbps=kb / (t_cmpr * 1e-3) / 1e9),
-        "cmp_attn_importance": dict(ms=t_cmp, algo_tflops=cmp_pf / 1e12, mfma_frac=cmp_pf / PEAK_BF16_MFMA),
-        "topk": dict(ms=t_topk),
-        "sparse_window_text_combine": dict(ms=t_sparse, algo_tflops=sp_pf / 1e12, mfma_frac=sp_pf / PEAK_BF16_MFMA),
-    }
 
 
 def decode(args):
@@ -178,9 +182,8 @@ def decode(args):
     ms = time_calls(step, args.decode_steps, stream)
     # algorithmic bytes: compressed cache + the union of selected-block and window tokens, each once,
     # plus q, out and gates
-    L = wl.kv_len
     t = wl.q_start
-    Nc = nsa.num_cmp_blocks(L, wl.cmp_block, wl.cmp_stride)
+    Nc = nsa.num_cmp_blocks(wl.kv_len, wl.cmp_block, wl.cmp_stride)
     total = 0
     for i in range(n_rot):
         idx = idxs[i].cpu().numpy()
@@ -194,7 +197,8 @@ def decode(args):
     total = total / n_rot + B * Hq * D * 2 * 2 + B * Hq * 3 * 4
     bw = total / (ms * 1e-3)
     return dict(workload=wl.name, ms_per_step=ms, algo_bytes=total, gbps=bw / 1e9, hbm_frac=bw / PEAK_HBM,
-                rotating_caches=n_rot, steps=args.decode_steps)
+                rotating_caches=n_rot, steps=args.decode_steps,
+                roofline=dict(bound="hbm", achieved=bw / 1e9, peak=PEAK_HBM / 1e9, unit="GB/s", frac=bw / PEAK_HBM))
 
 
 def cpu_baseline(args, wl, inp):
@@ -209,7 +213,7 @@ def cpu_baseline(args, wl, inp):
     q = inp["q"][0]
     vid = inp["is_video"][0].cpu().numpy().astype(bool)
     T = wl.q_len
-    n_rows = args.cpu_sample_rows or 192
+    n_rows = args.cpu_sample_rows or 4096
     vr = np.nonzero(vid)[0]
     tr = np.nonzero(~vid)[0]
     rng = np.random.default_rng(wl.index)
@@ -222,20 +226,17 @@ def cpu_baseline(args, wl, inp):
     oracle.layer(host(q), k, v, host(inp["w_k"]), host(inp["w_v"]), host(inp["gates"][0]), vid.astype(np.uint8),
                  wl.params(), rows=sample)
     dt = time.perf_counter() - t0
-    # extrapolate: video rows and text rows timed together; scale by row counts
-    rows_per_s = len(sample) / dt
-    frac_text = len(trows) / max(1, len(sample))
-    return dict(value=rows_per_s, unit="tokens/s (rows/s, extrapolated from the sample)", cores=oracle.num_threads(),
-                kind="oracle", seconds=dt,
-                sample="%d video rows (every %d-th at a seeded offset) + %d text rows of the %d-row %s prefill, "
+    return dict(value=len(sample) / dt, unit="tokens/s (query rows per second over the sample)",
+                cores=oracle.num_threads(), kind="oracle", seconds=dt,
+                sample="%d video rows (every %d-th, seeded offset) + %d text rows of the %d-row %s prefill; "
                        "compression of the whole sequence included" % (len(rows), stride, len(trows), T, wl.name))
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the layer shards by GQA group (up to 4 ways) and then by rows, "
-              "but no multi-GPU path is built; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the layer would shard by GQA group (up to 4 ways) and then by "
+              "query rows, but no multi-GPU path is built; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     from sparse_attention_long_fwd_amd import nsa, synth
@@ -244,26 +245,24 @@ def main():
     torch.cuda.init()
     wl = synth.WORKLOADS[args.workload]
     res, inp = prefill(args, wl)
-    dec = None
     ker = res.get("kernels", {})
-    dom_name, dom = None, None
-    for name, kk in ker.items():
-        if dom is None or kk["ms"] > dom["ms"]:
-            dom_name, dom = name, kk
     roofline = None
-    if dom is not None:
-        if "algo_tflops" in dom:
-            roofline = dict(kernel=dom_name, bound="mfma", achieved=dom["algo_tflops"], peak=PEAK_BF16_MFMA / 1e12,
-                            unit="TFLOP/s", frac=dom["mfma_frac"], traffic=None)
+    if ker:
+        dom_name = max(ker, key=lambda n: ker[n]["ms"])
+        dom = ker[dom_name]
+        if dom["bound"] == "hbm":
+            roofline = dict(kernel=dom_name, bound="hbm", achieved=dom["gbps"], peak=PEAK_HBM / 1e9, unit="GB/s",
+                            frac=dom["gbps"] * 1e9 / PEAK_HBM, traffic=None)
         else:
-            roofline = dict(kernel=dom_name, bound="hbm", achieved=dom.get("gbps"), peak=PEAK_HBM / 1e9,
-                            unit="GB/s", frac=(dom.get("gbps") or 0) * 1e9 / PEAK_HBM, traffic=None)
+            roofline = dict(kernel=dom_name, bound="mfma", achieved=dom["tflops"], peak=PEAK_BF16_MFMA / 1e12,
+                            unit="TFLOP/s", frac=dom["tflops"] * 1e12 / PEAK_BF16_MFMA, traffic=None)
     cpu = None
     if not args.no_cpu_baseline:
         log("oracle timing")
         cpu = cpu_baseline(args, wl, inp)
     del inp
     torch.cuda.empty_cache()
+    dec = None
     if not args.no_decode:
         log("decode")
         dec = decode(args)
@@ -279,7 +278,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded SplitMix64/Box-Muller; frame-correlated video K)",
+        "data": "synthetic (seeded SplitMix64 + Box-Muller; frame-correlated video K; no trained weights)",
         "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.kv_len, "q_heads": wl.num_q_heads,
                    "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "top_n": wl.top_n, "window": wl.window,
                    "cmp_block": wl.cmp_block, "cmp_stride": wl.cmp_stride, "sel_block": wl.sel_block,

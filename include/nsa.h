@@ -119,8 +119,9 @@ int32_t nsa_compress_kv(const void* k, const void* v, int32_t dtype, int64_t bat
  *   lse = log sum_i exp(scale * <q, k_cmp_i>);  C(t) empty -> o_cmp = 0, lse = -inf.
  *   importance[t, g, j] = sum_{h in group g} sum_{i in C(t)} frac(i, j) * p_{h,i}
  * where frac(i, j) is the share of compressed block i's tokens that lie in
- * selection block j.  Every j < Ns of a video row is written (0 where nothing
- * contributes).  Text rows are skipped: their outputs are left untouched.
+ * selection block j.  For a video row every candidate j <= t / sel_block is
+ * written (0 where nothing contributes); later blocks are left untouched.
+ * Text rows are skipped: their outputs are left untouched.
  * o_cmp and lse may be NULL.  importance may be NULL only if o_cmp is given.
  * Supported: head_dim <= 256 and a multiple of 8; top_n <= 32 is not needed here.
  */
@@ -183,6 +184,15 @@ int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const 
 /* Debug / test switch: 1 forces the generic (non-MFMA) kernels, 0 restores the
  * default dispatch.  Returns the previous value.  Process-wide. */
 int32_t nsa_set_force_generic(int32_t on);
+
+/* Measurement aid.  nsa_profile_enable(1) makes every later
+ * nsa_hybrid_layer_fwd record a HIP event on its stream at each phase
+ * boundary (compress | compression branch + importance | top-n | window and
+ * text rows | selection + combine); nsa_profile_read waits for the last event
+ * of the most recent call and writes the phase durations in ms (returns their
+ * count, or a negative status).  Process-wide, not for concurrent use. */
+int32_t nsa_profile_enable(int32_t on);
+int32_t nsa_profile_read(float* ms, int32_t max_phases);
 
 #ifdef __cplusplus
 }

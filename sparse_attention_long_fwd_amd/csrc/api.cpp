@@ -18,6 +18,16 @@ namespace {
 thread_local char g_err[512] = "";
 std::atomic<int> g_force_generic{0};
 
+// Phase timing of nsa_hybrid_layer_fwd (measurement aid): when enabled, the
+// call records a HIP event on its stream at each phase boundary.
+constexpr int kMaxMarks = 8;
+hipEvent_t g_marks[kMaxMarks];
+int g_nmarks = 0;        // events recorded by the last profiled call
+bool g_profiling = false;
+void prof_mark(hipStream_t s) {
+  if (g_profiling && g_nmarks < kMaxMarks) (void)hipEventRecord(g_marks[g_nmarks++], s);
+}
+
 int fail(int code, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -135,7 +145,8 @@ int run_sparse(int32_t dtype, const Dims& dm, const void* q, const void* k, cons
                const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out, void* o_slc,
                void* o_swa, void* ws, hipStream_t s) {
   hipError_t e = use_fast(dtype, dm)
-                     ? launch_sparse_fast(dm, q, k, v, idx, vid, o_cmp, ocmp_f32, gates, out, o_slc, o_swa, ws, s)
+                     ? launch_sparse_fast(dm, q, k, v, idx, vid, o_cmp, ocmp_f32, gates, out, o_slc, o_swa, ws, s,
+                                          prof_mark)
                      : launch_sparse_generic(dtype, dm, q, k, v, idx, vid, o_cmp, gates, out, o_slc, o_swa, s);
   if (e != hipSuccess) return hip_fail(e, "selection/window kernel");
   return NSA_OK;
@@ -169,6 +180,34 @@ int64_t nsa_num_sel_blocks(int64_t kv_len, int32_t sel_block) {
 }
 
 int32_t nsa_set_force_generic(int32_t on) { return g_force_generic.exchange(on ? 1 : 0); }
+
+int32_t nsa_profile_enable(int32_t on) {
+  g_err[0] = 0;
+  static bool created = false;
+  if (on && !created) {
+    for (int i = 0; i < kMaxMarks; ++i) {
+      hipError_t e = hipEventCreate(&g_marks[i]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    }
+    created = true;
+  }
+  g_profiling = on != 0;
+  g_nmarks = 0;
+  return NSA_OK;
+}
+
+int32_t nsa_profile_read(float* ms, int32_t max_phases) {
+  g_err[0] = 0;
+  if (!g_profiling || g_nmarks < 2) return 0;
+  hipError_t e = hipEventSynchronize(g_marks[g_nmarks - 1]);
+  if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+  int n = 0;
+  for (int i = 0; i + 1 < g_nmarks && n < max_phases; ++i, ++n) {
+    e = hipEventElapsedTime(&ms[n], g_marks[i], g_marks[i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+  }
+  return n;
+}
 
 int32_t nsa_compress_kv(const void* k, const void* v, int32_t dtype, int64_t batch, int64_t kv_len,
                         int32_t num_kv_heads, int32_t head_dim, const float* w_k, const float* w_v,
@@ -304,6 +343,8 @@ int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const 
   p += w.o_swa;
   void* sparse_ws_ptr = p;
 
+  g_nmarks = 0;
+  prof_mark(s);
   const void* kc_use = k_cmp_in;
   const void* vc_use = v_cmp_in;
   const void* kl_use = nullptr;
@@ -329,14 +370,21 @@ int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const 
   }
   const bool fast = use_fast(dtype, dm);
   // MFMA path: the combine reads an fp32 copy of the compression output; the caller's bf16 copy is optional
+  prof_mark(s);
   void* ocmp = fast ? o_cmp : (o_cmp ? o_cmp : ocmp_ws);
   float* ocmp32 = fast ? (float*)ocmp_ws : nullptr;
   int32_t* idx = block_idx_out ? block_idx_out : idx_ws;
   st = run_cmp(dtype, cdtype, dm, q, kc_use, kl_use, vc_use, vl_use, is_video, ocmp, ocmp32, lse, imp, s);
   if (st != NSA_OK) return st;
+  prof_mark(s);
   hipError_t e = launch_topk(dm, imp, is_video, idx, s);
   if (e != hipSuccess) return hip_fail(e, "top-n kernel");
-  if (fast) return run_sparse(dtype, dm, q, k, v, idx, is_video, ocmp32, true, gates, out, o_slc, o_swa, sparse_ws_ptr, s);
+  prof_mark(s);
+  if (fast) {
+    st = run_sparse(dtype, dm, q, k, v, idx, is_video, ocmp32, true, gates, out, o_slc, o_swa, sparse_ws_ptr, s);
+    prof_mark(s);
+    return st;
+  }
   void* oswa = o_swa ? o_swa : oswa_ws;
   return run_sparse(dtype, dm, q, k, v, idx, is_video, ocmp, false, gates, out, o_slc, oswa, sparse_ws_ptr, s);
 }

@@ -20,4 +20,5 @@ hipError_t launch_cmp_fast(const Dims& dm, const void* q, const void* kh, const 
 // fp32 when ocmp_f32, else bf16.  ws: fast_sparse_workspace(dm) bytes.
 hipError_t launch_sparse_fast(const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
                               const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out,
-                              void* o_slc, void* o_swa, void* ws, hipStream_t s);
+                              void* o_slc, void* o_swa, void* ws, hipStream_t s,
+                              void (*mark)(hipStream_t) = nullptr);

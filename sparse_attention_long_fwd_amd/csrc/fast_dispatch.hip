@@ -22,12 +22,13 @@ size_t fast_sparse_workspace(const Dims& dm) {
 
 hipError_t launch_sparse_fast(const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
                               const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out,
-                              void* o_slc, void* o_swa, void* ws, hipStream_t s) {
+                              void* o_slc, void* o_swa, void* ws, hipStream_t s, void (*mark)(hipStream_t)) {
   float* swa32 = (float*)ws;
   void* part = (char*)ws + rup((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 4);
   // window branch (fp32 for the combine, bf16 copy if asked) and dense text rows
   hipError_t e = launch_flash_fast(dm, q, k, v, vid, swa32, o_swa, out, part, s);
   if (e != hipSuccess) return e;
+  if (mark) mark(s);
   // selection branch and the gated combine of video rows
   return launch_slc_fast(dm, q, k, v, idx, vid, o_cmp, ocmp_f32, swa32, gates, out, o_slc, s);
 }

@@ -140,15 +140,16 @@ __global__ void __launch_bounds__(512) flash_fast_kernel(const bf16* __restrict_
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, hl = l >> 5, n = l & 31;
   const int nsplit = fo.nsplit;
+  // ranks [0, max_split * nsplit): (tile, chunk) of the split tiles; then one rank per remaining tile
+  const int nsr = fo.max_split * nsplit;
   int unit, rank;
-  if (!xcd_remap(blockIdx.x, (int)(dm.B * dm.Hkv), ntq * nsplit, &unit, &rank)) return;
-  const int chunk = rank % nsplit;
-  const int trank = rank / nsplit;  // tile rank, last tile first
+  if (!xcd_remap(blockIdx.x, (int)(dm.B * dm.Hkv), nsr + ntq - fo.max_split, &unit, &rank)) return;
+  const bool split = rank < nsr;
+  const int chunk = split ? rank % nsplit : 0;
+  const int trank = split ? rank / nsplit : fo.max_split + (rank - nsr);  // tile rank, last tile first
   const int64_t b = unit / dm.Hkv;
   const int g = unit % dm.Hkv;
   const int64_t rt0 = (int64_t)(ntq - 1 - trank) * FQ;
-  const bool split = trank < fo.max_split && nsplit > 1;
-  if (!split && chunk > 0) return;
 
   if (tid == 0) s_kind = 0;
   __syncthreads();
@@ -345,7 +346,7 @@ hipError_t launch_flash_fast(const Dims& dm, const void* q, const void* k, const
   const int do_swa = (swa32 || swa_bf) ? 1 : 0;
   const int do_text = text ? 1 : 0;
   if (!do_swa && !do_text) return hipSuccess;
-  dim3 grid(xcd_grid(units, ntq * fo.nsplit)), block(dm.G * 64);
+  dim3 grid(xcd_grid(units, fo.max_split * fo.nsplit + ntq - fo.max_split)), block(dm.G * 64);
   const size_t shm = (size_t)2 * 2 * TILE * 2;
   hipError_t e = hipFuncSetAttribute((const void*)flash_fast_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)shm);

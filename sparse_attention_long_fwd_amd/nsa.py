@@ -57,6 +57,8 @@ EXPORTS = {
     "nsa_hybrid_layer_fwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _SH, _PR, _P, _P, _P, _P, _P, _P,
                                     _SZ, _P]),
     "nsa_set_force_generic": (_I32, [_I32]),
+    "nsa_profile_enable": (_I32, [_I32]),
+    "nsa_profile_read": (_I32, [ctypes.POINTER(ctypes.c_float), _I32]),
 }
 
 
@@ -133,6 +135,22 @@ def num_sel_blocks(kv_len: int, sel_block: int) -> int:
 
 def set_force_generic(on: bool) -> bool:
     return bool(lib().nsa_set_force_generic(1 if on else 0))
+
+
+PHASES = ("compress", "cmp_attn_importance", "topk", "window_text", "selection_combine")
+
+
+def profile_enable(on: bool = True):
+    _check(lib().nsa_profile_enable(1 if on else 0))
+
+
+def profile_read():
+    """Phase durations (ms) of the last nsa_hybrid_layer_fwd, after profile_enable()."""
+    buf = (ctypes.c_float * 8)()
+    n = lib().nsa_profile_read(buf, 8)
+    if n < 0:
+        _check(n)
+    return list(buf[:n])
 
 
 def nsa_compress_kv(k, v, w_k, w_v, cmp_block=32, cmp_stride=16, k_cmp=None, v_cmp=None, stream=None):
