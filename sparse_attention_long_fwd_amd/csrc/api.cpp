@@ -111,11 +111,27 @@ SparseWs sparse_ws(const Dims& dm, int32_t dtype) {
 }
 
 struct LayerWs {
-  size_t kc, vc, o_cmp, lse, imp, idx, o_swa, sparse, total;
+  size_t kc, vc, o_cmp, lse, imp, idx, o_swa, sparse, dec, total;
 };
+// One query row per sequence on the MFMA path: the split decode kernels.
+bool use_decode(int32_t dtype, const Dims& dm) { return use_fast(dtype, dm) && decode_supported(dm); }
+
 LayerWs layer_ws(const Dims& dm, int32_t dtype) {
   LayerWs w{};
   const size_t es = esize(dtype);
+  if (fast_supported(dtype, dm) && decode_supported(dm)) {
+    w.kc = round_up((size_t)dm.B * dm.Nc * dm.Hkv * dm.D * 2) * 2;
+    w.vc = w.kc;
+    w.lse = round_up((size_t)dm.B * dm.Tq * dm.Hq * 4);
+    w.idx = round_up((size_t)dm.B * dm.Tq * dm.Hkv * dm.n * 4);
+    w.dec = round_up(decode_workspace(dm)) + round_up(flash_workspace(dm));
+    // the generic path may still run (test switch): keep its buffers too
+    w.o_cmp = round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 4);
+    w.imp = round_up((size_t)dm.B * dm.Tq * dm.Hkv * dm.Ns * 4);
+    w.o_swa = round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * es);
+    w.total = w.kc + w.vc + w.o_cmp + w.lse + w.imp + w.idx + w.o_swa + w.dec;
+    return w;
+  }
   // compressed keys / values computed inside the layer stay fp32 (no extra rounding step)
   w.kc = round_up((size_t)dm.B * dm.Nc * dm.Hkv * dm.D * 2) * 2;
   w.vc = w.kc;
@@ -367,6 +383,21 @@ int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const 
     kl_use = kl;
     vl_use = vl;
     cdtype = fast ? dtype : NSA_F32;
+  }
+  if (use_decode(dtype, dm)) {
+    // one row per sequence: phases = compress | compression branch + top-n | selection, window, combine
+    int32_t* didx = block_idx_out ? block_idx_out : idx_ws;
+    prof_mark(s);
+    hipError_t e = launch_decode_fast(dm, q, kc_use, kl_use, vc_use, vl_use, k, v, is_video, gates, out, o_cmp,
+                                      o_slc, o_swa, didx, lse, nullptr, sparse_ws_ptr, s, prof_mark);
+    if (e != hipSuccess) return hip_fail(e, "decode kernels");
+    if (is_video) {  // text rows: dense attention
+      e = launch_flash_fast(dm, q, k, v, is_video, nullptr, nullptr, out,
+                            (char*)sparse_ws_ptr + round_up(decode_workspace(dm)), s);
+      if (e != hipSuccess) return hip_fail(e, "text-row kernel");
+    }
+    prof_mark(s);
+    return NSA_OK;
   }
   const bool fast = use_fast(dtype, dm);
   // MFMA path: the combine reads an fp32 copy of the compression output; the caller's bf16 copy is optional

@@ -22,3 +22,17 @@ hipError_t launch_sparse_fast(const Dims& dm, const void* q, const void* k, cons
                               const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out,
                               void* o_slc, void* o_swa, void* ws, hipStream_t s,
                               void (*mark)(hipStream_t) = nullptr);
+
+// Window / text-row flash kernel: swa32 / swa_bf window outputs (either may be
+// NULL), text: output of text rows (NULL: skip them); ws: flash_workspace(dm).
+hipError_t launch_flash_fast(const Dims& dm, const void* q, const void* k, const void* v, const uint8_t* vid,
+                             float* swa32, void* swa_bf, void* text, void* ws, hipStream_t s);
+size_t flash_workspace(const Dims& dm);
+
+// Decode path (one query row per sequence, split over the compressed keys).
+bool decode_supported(const Dims& dm);
+size_t decode_workspace(const Dims& dm);
+hipError_t launch_decode_fast(const Dims& dm, const void* q, const void* kh, const void* kl, const void* vh,
+                              const void* vl, const void* k, const void* v, const uint8_t* vid, const float* gates,
+                              void* out, void* o_cmp, void* o_slc, void* o_swa, int32_t* idx, float* lse,
+                              float* imp, void* ws, hipStream_t s, void (*mark)(hipStream_t));

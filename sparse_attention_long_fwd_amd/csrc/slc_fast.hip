@@ -36,12 +36,18 @@ __global__ void __launch_bounds__(SW * 64) slc_fast_kernel(const bf16* __restric
                                                            const uint8_t* __restrict__ vid,
                                                            const void* __restrict__ ocmp, const float* __restrict__ swa,
                                                            const float* __restrict__ gates, bf16* __restrict__ out,
-                                                           bf16* __restrict__ o_slc, Dims dm, int nwg_per_unit) {
+                                                           bf16* __restrict__ o_slc, Dims dm, int nwg_per_unit,
+                                                           int64_t tok_stride, int64_t head_stride, int group_seq) {
   __shared__ __attribute__((aligned(16))) bf16 vtile[SW][SB * HD];
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int hn = l & 15, grp = l >> 4;  // head column, lane group (4 keys each)
   int unit, rank;
-  if (!xcd_remap(blockIdx.x, (int)(dm.B * dm.Hkv), nwg_per_unit, &unit, &rank)) return;
+  if (group_seq) {  // one (batch, group) after another: its K/V is the whole working set
+    unit = (int)(blockIdx.x / (unsigned)nwg_per_unit);
+    rank = (int)(blockIdx.x % (unsigned)nwg_per_unit);
+  } else if (!xcd_remap(blockIdx.x, (int)(dm.B * dm.Hkv), nwg_per_unit, &unit, &rank)) {
+    return;
+  }
   const int64_t b = unit / dm.Hkv;
   const int g = unit % dm.Hkv;
   const int64_t r = (int64_t)rank * SW + w;
@@ -63,9 +69,9 @@ __global__ void __launch_bounds__(SW * 64) slc_fast_kernel(const bf16* __restric
   }
   const int32_t* sel = idx + ((b * dm.Tq + r) * dm.Hkv + g) * dm.n;
   const int myj = l < dm.n ? sel[l] : -1;
-  const int64_t stride = (int64_t)dm.Hkv * HD;
-  const bf16* kbase = k + (b * dm.T * dm.Hkv + g) * (int64_t)HD;
-  const bf16* vbase = v + (b * dm.T * dm.Hkv + g) * (int64_t)HD;
+  const int64_t stride = tok_stride;
+  const bf16* kbase = k + b * dm.T * dm.Hkv * (int64_t)HD + g * head_stride;
+  const bf16* vbase = v + b * dm.T * dm.Hkv * (int64_t)HD + g * head_stride;
   bf16* vt = vtile[w];
 
   // K fragments of one block: A operand of S^T, lane holds K[16 kb + hn][32 ks + 8 grp .. +8]
@@ -204,18 +210,24 @@ __global__ void __launch_bounds__(SW * 64) slc_fast_kernel(const bf16* __restric
   }
 }
 
+// head_major: k/v are laid out [B, Hkv, T, D] instead of [B, T, Hkv, D].
 hipError_t launch_slc_fast(const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
                            const uint8_t* vid, const void* ocmp, bool ocmp_f32, const float* swa32,
-                           const float* gates, void* out, void* o_slc, hipStream_t s) {
+                           const float* gates, void* out, void* o_slc, hipStream_t s, bool head_major,
+                           bool group_seq) {
   if (dm.Tq <= 0 || dm.B <= 0 || (!out && !o_slc)) return hipSuccess;
   const int per_unit = (int)((dm.Tq + SW - 1) / SW);
   const int units = (int)(dm.B * dm.Hkv);
-  dim3 grid(xcd_grid(units, per_unit)), block(SW * 64);
+  dim3 grid(group_seq ? (unsigned)(units * per_unit) : xcd_grid(units, per_unit)), block(SW * 64);
+  const int64_t tok_stride = head_major ? HD : (int64_t)dm.Hkv * HD;
+  const int64_t head_stride = head_major ? dm.T * (int64_t)HD : HD;
   if (ocmp_f32)
     slc_fast_kernel<true><<<grid, block, 0, s>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, idx, vid, ocmp,
-                                                 swa32, gates, (bf16*)out, (bf16*)o_slc, dm, per_unit);
+                                                 swa32, gates, (bf16*)out, (bf16*)o_slc, dm, per_unit, tok_stride, head_stride,
+                                                 group_seq ? 1 : 0);
   else
     slc_fast_kernel<false><<<grid, block, 0, s>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, idx, vid, ocmp,
-                                                  swa32, gates, (bf16*)out, (bf16*)o_slc, dm, per_unit);
+                                                  swa32, gates, (bf16*)out, (bf16*)o_slc, dm, per_unit, tok_stride, head_stride,
+                                                 group_seq ? 1 : 0);
   return hipGetLastError();
 }

@@ -341,3 +341,24 @@ def test_layer_deterministic():
     b = run_layer(wl, inp)
     for key in ("out", "o_cmp", "o_slc", "o_swa", "idx"):
         assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("case", ["internal-compress", "text-row", "early-row", "batch3-mixed"])
+def test_decode_single_row(case, path):
+    """One query row per sequence (the split decode kernels), compressed inside the layer."""
+    T, B, q_start = 5000, 1, 4999
+    lead, tail = 0, 0
+    if case == "text-row":
+        tail = 1
+    elif case == "early-row":
+        T, q_start = 4000, 70
+    elif case == "batch3-mixed":
+        B, T, q_start = 3, 3000, 2500
+    wl = _wl(T=T, B=B, q_start=q_start, q_len=1, lead=lead, tail=tail)
+    flush("decode %s path=%s" % (case, path))
+    inp = synth.make_inputs(wl, DEV)
+    if case == "batch3-mixed":
+        inp["is_video"][1] = 0  # the middle sequence's row is a text row
+    got = run_layer(wl, inp)
+    for b in range(B):
+        compare_layer(wl, inp, got, np.arange(1), b)
