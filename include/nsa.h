@@ -172,7 +172,9 @@ int32_t nsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t
  * q_start = kv_len - 1 with the compressed cache passed in.
  * out is required; o_cmp / o_slc / o_swa / block_idx_out may be NULL (when
  * given they receive the branch outputs and the chosen blocks of the video
- * rows).  workspace: nsa_hybrid_layer_workspace_size() bytes of device memory.
+ * rows).  workspace: nsa_hybrid_layer_workspace_size() bytes of device memory;
+ * the size depends on the kernels the call dispatches to, so query it after
+ * any nsa_set_force_generic change.
  */
 size_t nsa_hybrid_layer_workspace_size(const nsa_shape* shape, const nsa_params* params, int32_t dtype);
 int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const void* k_cmp_in,

@@ -116,33 +116,33 @@ struct LayerWs {
 // One query row per sequence on the MFMA path: the split decode kernels.
 bool use_decode(int32_t dtype, const Dims& dm) { return use_fast(dtype, dm) && decode_supported(dm); }
 
+// Sized for the kernels the call will dispatch to (nsa_set_force_generic included).
 LayerWs layer_ws(const Dims& dm, int32_t dtype) {
   LayerWs w{};
   const size_t es = esize(dtype);
-  if (fast_supported(dtype, dm) && decode_supported(dm)) {
-    w.kc = round_up((size_t)dm.B * dm.Nc * dm.Hkv * dm.D * 2) * 2;
-    w.vc = w.kc;
-    w.lse = round_up((size_t)dm.B * dm.Tq * dm.Hq * 4);
-    w.idx = round_up((size_t)dm.B * dm.Tq * dm.Hkv * dm.n * 4);
-    w.dec = round_up(decode_workspace(dm)) + round_up(flash_workspace(dm));
-    // the generic path may still run (test switch): keep its buffers too
-    w.o_cmp = round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 4);
-    w.imp = round_up((size_t)dm.B * dm.Tq * dm.Hkv * dm.Ns * 4);
-    w.o_swa = round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * es);
-    w.total = w.kc + w.vc + w.o_cmp + w.lse + w.imp + w.idx + w.o_swa + w.dec;
-    return w;
-  }
-  // compressed keys / values computed inside the layer stay fp32 (no extra rounding step)
+  const bool fast = use_fast(dtype, dm);
+  // compressed keys / values computed inside the layer keep fp32 precision: bf16 high + low
+  // parts on the MFMA path, fp32 on the generic path (4 bytes per element either way)
   w.kc = round_up((size_t)dm.B * dm.Nc * dm.Hkv * dm.D * 2) * 2;
   w.vc = w.kc;
-  // branch output of the compression path: fp32 on the MFMA path (read by the combine), dtype otherwise
-  w.o_cmp = round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * (fast_supported(dtype, dm) ? 4 : es));
   w.lse = round_up((size_t)dm.B * dm.Tq * dm.Hq * 4);
-  w.imp = round_up((size_t)dm.B * dm.Tq * dm.Hkv * dm.Ns * 4);
   w.idx = round_up((size_t)dm.B * dm.Tq * dm.Hkv * dm.n * 4);
-  w.o_swa = fast_supported(dtype, dm) ? 0 : round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * es);
-  w.sparse = sparse_ws(dm, dtype).total;
-  w.total = w.kc + w.vc + w.o_cmp + w.lse + w.imp + w.idx + w.o_swa + w.sparse;
+  if (fast && decode_supported(dm)) {
+    w.dec = round_up(decode_workspace(dm)) + round_up(flash_workspace(dm));
+  } else if (fast) {
+    // values as V^T tiles (padded to whole 64-key tiles), high + low parts
+    const size_t vt = round_up(vt_tiles_bytes(dm)) * 2;
+    if (vt > w.vc) w.vc = vt;
+    // fp32 branch output of the compression path (read by the combine)
+    w.o_cmp = round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 4);
+    w.imp = round_up((size_t)dm.B * dm.Tq * dm.Hkv * dm.Ns * 4);
+    w.sparse = sparse_ws(dm, dtype).total;
+  } else {
+    w.o_cmp = round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * es);
+    w.imp = round_up((size_t)dm.B * dm.Tq * dm.Hkv * dm.Ns * 4);
+    w.o_swa = round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * es);
+  }
+  w.total = w.kc + w.vc + w.o_cmp + w.lse + w.imp + w.idx + w.o_swa + w.sparse + w.dec;
   return w;
 }
 
@@ -151,7 +151,8 @@ LayerWs layer_ws(const Dims& dm, int32_t dtype) {
 int run_cmp(int32_t dtype, int32_t cdtype, const Dims& dm, const void* q, const void* kc, const void* kl,
             const void* vc, const void* vl, const uint8_t* vid, void* o, float* o32, float* lse, float* imp,
             hipStream_t s) {
-  hipError_t e = use_fast(dtype, dm) ? launch_cmp_fast(dm, q, kc, kl, vc, vl, vid, o, o32, lse, imp, s)
+  // low parts come only from the layer's own compression, which writes V as V^T tiles
+  hipError_t e = use_fast(dtype, dm) ? launch_cmp_fast(dm, q, kc, kl, vc, vl, vid, o, o32, lse, imp, kl != nullptr, s)
                                      : launch_cmp_generic(dtype, cdtype, dm, q, kc, vc, vid, o, lse, imp, s);
   if (e != hipSuccess) return hip_fail(e, "compression-branch kernel");
   return NSA_OK;
@@ -369,14 +370,16 @@ int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const 
   if (!kc_use) {
     // Compressed inside the layer, carried at fp32 precision: the MFMA path as bf16 high + low
     // parts (both enter every product), the generic path as fp32.
+    // Prefill on the MFMA path takes the values as V^T tiles.
     const bool fast = use_fast(dtype, dm);
-    const size_t half = w.kc / 2;
-    void* kl = fast ? (char*)kc + half : nullptr;
-    void* vl = fast ? (char*)vc + half : nullptr;
+    const bool vt = fast && !decode_supported(dm);
+    void* kl = fast ? (char*)kc + w.kc / 2 : nullptr;
+    void* vl = fast ? (char*)vc + w.vc / 2 : nullptr;
     hipError_t e = launch_compress(dtype, fast ? 2 : 1, k, w_k, kc, kl, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d,
                                    dm.Nc, s);
     if (e == hipSuccess)
-      e = launch_compress(dtype, fast ? 2 : 1, v, w_v, vc, vl, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d, dm.Nc, s);
+      e = vt ? launch_compress_vt(dm, v, w_v, vc, vl, s)
+             : launch_compress(dtype, fast ? 2 : 1, v, w_v, vc, vl, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d, dm.Nc, s);
     if (e != hipSuccess) return hip_fail(e, "compress kernel");
     kc_use = kc;
     vc_use = vc;

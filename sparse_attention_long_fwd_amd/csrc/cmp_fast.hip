@@ -31,8 +31,10 @@
 // deterministic.
 //
 // Compressed K and V may come as bf16 high + low parts (compressed inside the
-// layer from an fp32 sum); both parts enter every product, so the compression
-// adds no bf16 rounding step to the scores or the value sum.
+// layer from an fp32 sum).  Both parts of K enter every score, so the scores
+// carry no bf16 rounding of the compression.  Both parts of V enter the value
+// sum for workgroups whose rows see fewer than kVloBelow compressed blocks;
+// longer rows use the high part alone (a sixth fewer products and staged bytes).
 #include "fast_common.hpp"
 
 namespace {
@@ -40,11 +42,30 @@ constexpr int CQ = 32;         // query rows per workgroup
 constexpr int CK = 64;         // compressed keys per tile
 constexpr int HD = 128;        // head dim
 constexpr int TILE = CK * HD;  // bf16 elements of one staged array
+// Rows that see fewer compressed blocks than this use the low parts of V too.  With few blocks
+// one block's value dominates the output, so the bf16 rounding of Vc shows in it undamped; from
+// a few hundred blocks on the softmax averages it down well below the bf16 output rounding.
+// Scores always use both parts of K: the block importance that decides the top-n moves by
+// up to a few 1e-3 with bf16 Kc.
+constexpr int64_t kVloBelow = 256;
 }  // namespace
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <bool SPLIT>
+// Compressed values as V^T tiles (the layout compress_vt_kernel writes): per (b, KV head) a run
+// of ceil(Nc / 64) tiles of [128 dims][64 keys], keys zero-padded past Nc.  Inside a 16-key
+// group the key at offset o sits at slot 8*((o>>2)&1) + 4*(o>>3) + (o&3): the eight keys one
+// lane half feeds to an MFMA step (C-register order of the score tile) are adjacent, and the
+// A operand of O^T += Vc^T P^T is one 16-byte read.  16-byte chunks are XOR-swizzled by
+// (dim & 7) so 8 consecutive dims hit distinct banks.  A tile is its own LDS image.
+__device__ __forceinline__ int vt_slot(int dim, int key) {
+  const int o = key & 15;
+  const int kidx = (key & ~15) + 8 * ((o >> 2) & 1) + 4 * (o >> 3) + (o & 3);
+  return dim * CK + ((((kidx >> 3) ^ (dim & 7))) << 3) + (kidx & 7);
+}
+
+// VT: values come as V^T tiles (high parts in vh, low parts in vl) instead of [B, Nc, Hkv, D].
+template <bool SPLIT, bool VT>
 __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kh,
                                                        const bf16* __restrict__ kl, const bf16* __restrict__ vh,
                                                        const bf16* __restrict__ vl, const uint8_t* __restrict__ vid,
@@ -94,6 +115,9 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
     for (int ks = 0; ks < 8; ++ks) qf[ks] = rvalid ? *(const bf16x8*)(qrow + 16 * ks) : zero8();
   }
 
+  // VLO: the low parts of V enter the value sum (see kVloBelow); a uniform choice per workgroup
+  auto body = [&](auto vlo_c) {
+  constexpr bool VLO = decltype(vlo_c)::value;
   const int64_t stride = (int64_t)dm.Hkv * HD;
   const int64_t base = (b * dm.Nc * dm.Hkv + g) * (int64_t)HD;
   auto arr = [&](int bufi, int a) { return buf0 + (bufi * NARR + a) * TILE; };
@@ -101,9 +125,17 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
     stage_tile64(arr(bufi, 0), kh + base, stride, (int64_t)tile * CK, dm.Nc, w, G, l);
     if constexpr (SPLIT) stage_tile64(arr(bufi, 1), kl + base, stride, (int64_t)tile * CK, dm.Nc, w, G, l);
   };
+  const int ntv = (int)((dm.Nc + CK - 1) / CK);
   auto stage_v = [&](int tile, int bufi) {
-    stage_tile64(arr(bufi, SPLIT ? 2 : 1), vh + base, stride, (int64_t)tile * CK, dm.Nc, w, G, l);
-    if constexpr (SPLIT) stage_tile64(arr(bufi, 3), vl + base, stride, (int64_t)tile * CK, dm.Nc, w, G, l);
+    if constexpr (VT) {
+      // past the last tile (only the importance carry is flushed there, every p is 0): restage it
+      const int64_t t0 = ((b * dm.Hkv + g) * ntv + (tile < ntv ? tile : ntv - 1)) * (int64_t)TILE;
+      stage_lin16k(arr(bufi, SPLIT ? 2 : 1), vh + t0, w, G, l);
+      if constexpr (VLO) stage_lin16k(arr(bufi, 3), vl + t0, w, G, l);
+    } else {
+      stage_tile64(arr(bufi, SPLIT ? 2 : 1), vh + base, stride, (int64_t)tile * CK, dm.Nc, w, G, l);
+      if constexpr (VLO) stage_tile64(arr(bufi, 3), vl + base, stride, (int64_t)tile * CK, dm.Nc, w, G, l);
+    }
   };
   // S^T block kb (32 keys) of the staged tile
   auto scores = [&](int bufi, int kb) {
@@ -168,6 +200,19 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
   }
 
   // ---- sweep 2: probabilities, value sum, importance
+  // Head-sum items of this thread: (row, block within the tile) = (i >> 4, i & 15) for
+  // i = tid, tid + nthr; jmax = the row's last block (-1: text row or past the end).
+  int64_t jmax[2];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const int i = tid + k2 * nthr;
+    const int64_t rr = rt0 + (i >> 4);
+    jmax[k2] = -1;
+    if (i < CQ * 16 && rr < dm.Tq && (!vid || vid[b * dm.Tq + rr])) {
+      const int64_t jt = (dm.q0 + rr) / dm.ls;
+      jmax[k2] = jt < dm.Ns ? jt : dm.Ns - 1;
+    }
+  }
   f32x16 oacc[4] = {};
   float carry = 0.f;  // half share of the previous run's last compressed block (hl == 0 lanes)
   const int nt2 = nvmax > 0 ? (int)(nvmax / CK) + 1 : 0;
@@ -223,12 +268,19 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
         const int vr = kb * 32 + 16 * st + 4 * (g16 >> 1) + (i16 >> 2);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
+          if constexpr (VT) {
+            // A operand: dims 32 db + n, the lane half's 8 keys of this 16-key step
+            const int off = (32 * db + n) * CK + (((2 * (2 * kb + st) + hl) ^ (n & 7)) << 3);
+            oacc[db] = mfma32(lds_read8(arr(bufi, SPLIT ? 2 : 1) + off), pb, oacc[db]);
+            if constexpr (VLO) oacc[db] = mfma32(lds_read8(arr(bufi, 3) + off), pb, oacc[db]);
+            continue;
+          }
           const int col = 32 * db + (g16 & 1) * 16 + 4 * (i16 & 3);
           const int o0 = swz128(vr, col >> 3) + (col & 7);
           const int o1 = swz128(vr + 8, col >> 3) + (col & 7);
           const bf16* vhs = arr(bufi, SPLIT ? 2 : 1);
           oacc[db] = mfma32(cat(lds_read_tr(vhs + o0), lds_read_tr(vhs + o1)), pb, oacc[db]);
-          if constexpr (SPLIT) {
+          if constexpr (VLO) {
             const bf16* vls = arr(bufi, 3);
             oacc[db] = mfma32(cat(lds_read_tr(vls + o0), lds_read_tr(vls + o1)), pb, oacc[db]);
           }
@@ -238,15 +290,15 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
     wait_loads();
     __syncthreads();
     // sum the group's heads in a fixed order; write the tile's 16 selection blocks
-    for (int idx = tid; idx < CQ * 16; idx += nthr) {
-      const int nn = idx >> 4, jj = idx & 15;
-      const int64_t rr = rt0 + nn;
-      if (rr >= dm.Tq || (vid && !vid[b * dm.Tq + rr])) continue;
-      const int64_t J = (int64_t)tile * 16 + jj;
-      if (J > (dm.q0 + rr) / dm.ls || J >= dm.Ns) continue;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int i = tid + k2 * nthr;
+      const int64_t J = (int64_t)tile * 16 + (i & 15);
+      if (J > jmax[k2]) continue;
+      const int nn = i >> 4;
       float sum = 0.f;
-      for (int ww = 0; ww < G; ++ww) sum += ipb[(ww * CQ + nn) * 16 + jj];
-      imp[((b * dm.Tq + rr) * dm.Hkv + g) * dm.Ns + J] = sum;
+      for (int ww = 0; ww < G; ++ww) sum += ipb[(ww * CQ + nn) * 16 + (i & 15)];
+      imp[((b * dm.Tq + rt0 + nn) * dm.Hkv + g) * dm.Ns + J] = sum;
     }
   }
   // blocks up to the row's own block that no compressed block reaches
@@ -277,6 +329,15 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
     }
   }
   if (lse && hl == 0) lse[(b * dm.Tq + r) * dm.Hq + h] = nv > 0 ? L2 * LN2_F : -INFINITY;
+  };
+  if constexpr (SPLIT) {
+    if (cmp_visible(dm.q0 + rt0, dm.l, dm.d, dm.Nc) < kVloBelow)
+      body(std::true_type{});
+    else
+      body(std::false_type{});
+  } else {
+    body(std::false_type{});
+  }
 }
 
 size_t cmp_fast_smem(const Dims& dm, bool split) {
@@ -285,26 +346,80 @@ size_t cmp_fast_smem(const Dims& dm, bool split) {
 
 hipError_t launch_cmp_fast(const Dims& dm, const void* q, const void* kh, const void* kl, const void* vh,
                            const void* vl, const uint8_t* vid, void* o, float* o32, float* lse, float* imp,
-                           hipStream_t s) {
+                           bool vt, hipStream_t s) {
   if (dm.Tq <= 0 || dm.B <= 0) return hipSuccess;
   const int ntq = (int)((dm.Tq + CQ - 1) / CQ);
   const int units = (int)(dm.B * dm.Hkv);
   dim3 grid(xcd_grid(units, ntq)), block(dm.G * 64);
   const bool split = kl != nullptr;
   const size_t shm = cmp_fast_smem(dm, split);
-  hipError_t e;
-  if (split) {
-    e = hipFuncSetAttribute((const void*)cmp_fast_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    if (e != hipSuccess) return e;
-    cmp_fast_kernel<true><<<grid, block, shm, s>>>((const bf16*)q, (const bf16*)kh, (const bf16*)kl,
-                                                   (const bf16*)vh, (const bf16*)vl, vid, (bf16*)o, o32, lse, imp,
-                                                   dm, ntq);
-  } else {
-    e = hipFuncSetAttribute((const void*)cmp_fast_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)shm);
-    if (e != hipSuccess) return e;
-    cmp_fast_kernel<false><<<grid, block, shm, s>>>((const bf16*)q, (const bf16*)kh, nullptr, (const bf16*)vh,
-                                                    nullptr, vid, (bf16*)o, o32, lse, imp, dm, ntq);
+  // the MFMA layer path always brings split parts with V^T tiles; standalone calls bring neither
+  if (split != vt) return hipErrorInvalidValue;
+  const void* fn = split ? (const void*)cmp_fast_kernel<true, true> : (const void*)cmp_fast_kernel<false, false>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  if (split)
+    cmp_fast_kernel<true, true><<<grid, block, shm, s>>>((const bf16*)q, (const bf16*)kh, (const bf16*)kl,
+                                                         (const bf16*)vh, (const bf16*)vl, vid, (bf16*)o, o32, lse,
+                                                         imp, dm, ntq);
+  else
+    cmp_fast_kernel<false, false><<<grid, block, shm, s>>>((const bf16*)q, (const bf16*)kh, nullptr,
+                                                           (const bf16*)vh, nullptr, vid, (bf16*)o, o32, lse, imp,
+                                                           dm, ntq);
+  return hipGetLastError();
+}
+
+// Compressed values as V^T tiles (high and low bf16 parts of the fp32 sum), one workgroup per
+// (b, KV head, 64-key tile).  Threads sum 8 channels of one compressed key (16 threads read a
+// token row with 16-byte loads), place the results at their tile slots in LDS and the tile
+// leaves as one contiguous 16 KB run per part.
+__global__ void __launch_bounds__(256) compress_vt_kernel(const bf16* __restrict__ x, const float* __restrict__ w,
+                                                          bf16* __restrict__ hi, bf16* __restrict__ lo, int64_t T_len,
+                                                          int H, int l, int d, int64_t Nc, int ntv) {
+  __shared__ float ws[64];
+  __shared__ __attribute__((aligned(16))) bf16 s_hi[TILE], s_lo[TILE];
+  const int tile = blockIdx.x % ntv;
+  const int64_t bh = blockIdx.x / ntv;
+  const int h = (int)(bh % H);
+  const int64_t b = bh / H;
+  for (int m = threadIdx.x; m < l; m += blockDim.x) ws[m] = w[m];
+  __syncthreads();
+  for (int it = threadIdx.x; it < CK * (HD / 8); it += blockDim.x) {
+    const int key = it >> 4, c8 = it & 15;
+    const int64_t i = (int64_t)tile * CK + key;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (i < Nc) {
+      const bf16* src = x + ((b * T_len + i * d) * H + h) * (int64_t)HD + c8 * 8;
+      for (int m = 0; m < l; ++m) {
+        const bf16x8 u = *(const bf16x8*)(src + (int64_t)m * H * HD);
+        const float wm = ws[m];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(wm, (float)u[e], acc[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bf16 vh = (bf16)acc[e];
+      const int slot = vt_slot(c8 * 8 + e, key);
+      s_hi[slot] = vh;
+      s_lo[slot] = (bf16)(acc[e] - (float)vh);
+    }
   }
+  __syncthreads();
+  const int64_t t0 = (bh * ntv + tile) * (int64_t)TILE;
+  for (int c = threadIdx.x; c < TILE / 8; c += blockDim.x) {
+    *(bf16x8*)(hi + t0 + c * 8) = *(const bf16x8*)(s_hi + c * 8);
+    *(bf16x8*)(lo + t0 + c * 8) = *(const bf16x8*)(s_lo + c * 8);
+  }
+}
+
+size_t vt_tiles_bytes(const Dims& dm) { return (size_t)dm.B * dm.Hkv * ((dm.Nc + CK - 1) / CK) * TILE * 2; }
+
+hipError_t launch_compress_vt(const Dims& dm, const void* v, const float* w_v, void* hi, void* lo, hipStream_t s) {
+  if (dm.Nc <= 0 || dm.B <= 0) return hipSuccess;
+  if (dm.D != HD || dm.l > 64) return hipErrorInvalidValue;
+  const int ntv = (int)((dm.Nc + CK - 1) / CK);
+  compress_vt_kernel<<<(unsigned)(dm.B * dm.Hkv * ntv), 256, 0, s>>>((const bf16*)v, w_v, (bf16*)hi, (bf16*)lo, dm.T,
+                                                                    dm.Hkv, dm.l, dm.d, dm.Nc, ntv);
   return hipGetLastError();
 }

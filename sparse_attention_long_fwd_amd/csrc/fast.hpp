@@ -10,11 +10,17 @@ bool fast_supported(int32_t dtype, const Dims& dm);
 size_t fast_sparse_workspace(const Dims& dm);
 
 // Compression branch + importance.  kh/vh: compressed keys/values (bf16); kl/vl:
-// their low parts when they come from an fp32 sum (both NULL otherwise).
+// their low parts when they come from an fp32 sum (both NULL otherwise).  vt: the
+// values come as V^T tiles from launch_compress_vt (required with low parts).
 // o (bf16) and o32 (fp32) are optional copies of the branch output.
 hipError_t launch_cmp_fast(const Dims& dm, const void* q, const void* kh, const void* kl, const void* vh,
                            const void* vl, const uint8_t* vid, void* o, float* o32, float* lse, float* imp,
-                           hipStream_t s);
+                           bool vt, hipStream_t s);
+
+// Compressed values (bf16 high + low parts of the fp32 sum) as the V^T tiles the
+// compression-branch kernel stages; each part takes vt_tiles_bytes(dm) bytes.
+size_t vt_tiles_bytes(const Dims& dm);
+hipError_t launch_compress_vt(const Dims& dm, const void* v, const float* w_v, void* hi, void* lo, hipStream_t s);
 
 // Window branch, text rows, selection branch and the gated combine.  o_cmp is
 // fp32 when ocmp_f32, else bf16.  ws: fast_sparse_workspace(dm) bytes.

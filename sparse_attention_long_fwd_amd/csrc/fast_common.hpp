@@ -58,3 +58,11 @@ __device__ __forceinline__ void stage_tile64(bf16* lds_tile, const bf16* src, in
                                      (__attribute__((address_space(3))) void*)(lds_tile + ins * 512), 16, 0, 0);
   }
 }
+
+// Copy a contiguous 16 KB run global -> LDS with the direct-to-LDS load: 16 instructions of
+// 64 lanes x 16 bytes, spread over the nw waves of the workgroup (wave w, lane `lane`).
+__device__ __forceinline__ void stage_lin16k(bf16* lds_tile, const bf16* src, int w, int nw, int lane) {
+  for (int ins = w; ins < 16; ins += nw)
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + (ins * 64 + lane) * 8),
+                                     (__attribute__((address_space(3))) void*)(lds_tile + ins * 512), 16, 0, 0);
+}

@@ -334,6 +334,20 @@ def test_layer_edge_cases(case, path):
     compare_layer(wl, inp, got, np.arange(wl.q_len))
 
 
+@pytest.mark.parametrize("n,n_init,n_local", [(32, 0, 1), (3, 1, 2), (12, 3, 4), (5, 0, 5), (6, 2, 1)])
+def test_layer_selection_params(n, n_init, n_local, path):
+    """Top-n inside the layer for other forced-block counts: no leading block, no free place
+    left (n = n_init + n_local), and enough rows past several 1024-token key tiles for the
+    candidate lists to be cut down many times."""
+    wl = _wl(T=5200, Hq=14, Hkv=2, lead=96, tail=40, n=n, w=256, n_init=n_init, n_local=n_local)
+    flush("selection n=%d n_init=%d n_local=%d path=%s" % (n, n_init, n_local, path))
+    inp = synth.make_inputs(wl, DEV)
+    got = run_layer(wl, inp)
+    rows = np.unique(np.concatenate([np.arange(0, 300), np.arange(300, wl.q_len, 7), np.arange(wl.q_len - 64,
+                                                                                               wl.q_len)]))
+    compare_layer(wl, inp, got, rows)
+
+
 def test_layer_deterministic():
     wl = _wl(T=3000, lead=128, tail=128)
     inp = synth.make_inputs(wl, DEV)
