@@ -64,18 +64,30 @@ __device__ __forceinline__ int vt_slot(int dim, int key) {
   return dim * CK + ((((kidx >> 3) ^ (dim & 7))) << 3) + (kidx & 7);
 }
 
+// Row stride (floats) of the per-head importance partials: 16 blocks + 1 pad, so 32 lanes
+// writing one block of 32 rows and 16 lanes reading the 16 blocks of a row hit distinct banks.
+constexpr int IPS = 17;
+
+// The other lane half's value (lane l gets lane l ^ 32), with gfx950's v_permlane32_swap.
+__device__ __forceinline__ float xchg32(float x, int hl) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(hl ? r[0] : r[1]);
+}
+
 // VT: values come as V^T tiles (high parts in vh, low parts in vl) instead of [B, Nc, Hkv, D].
+// ipart_bufs: 2 = importance partials double-buffered by tile parity, 1 = one buffer (one more
+// barrier a tile; used where two do not fit in LDS).
 template <bool SPLIT, bool VT>
 __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kh,
                                                        const bf16* __restrict__ kl, const bf16* __restrict__ vh,
                                                        const bf16* __restrict__ vl, const uint8_t* __restrict__ vid,
                                                        bf16* __restrict__ o_bf, float* __restrict__ o_f32,
                                                        float* __restrict__ lse, float* __restrict__ imp, Dims dm,
-                                                       int ntq) {
+                                                       int ntq, int ipart_bufs) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  constexpr int NARR = SPLIT ? 4 : 2;                   // staged arrays per buffer: K (hi, lo), V (hi, lo)
-  bf16* buf0 = (bf16*)smem;                              // buffer b, array a at buf0 + (b * NARR + a) * TILE
-  float* ipart = (float*)(smem + 2 * NARR * TILE * 2);  // [2][G][CQ][16]
+  constexpr int NARR = SPLIT ? 4 : 2;                    // staged arrays per buffer: K (hi, lo), V (hi, lo)
+  bf16* buf0 = (bf16*)smem;                               // buffer b, array a at buf0 + (b * NARR + a) * TILE
+  float* ipart0 = (float*)(smem + 2 * NARR * TILE * 2);  // [ipart_bufs][G][CQ][IPS]
   __shared__ int s_any;
 
   const int G = dm.G;
@@ -97,13 +109,15 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
   __syncthreads();
   if (!s_any) return;
 
+  // key counts fit in int: Nc < 2^27 for kv_len <= 2^31
   const int64_t rlast = (rt0 + CQ < dm.Tq ? rt0 + CQ : dm.Tq) - 1;
-  const int64_t nvmax = cmp_visible(dm.q0 + rlast, dm.l, dm.d, dm.Nc);
+  const int nvmax = (int)cmp_visible(dm.q0 + rlast, dm.l, dm.d, dm.Nc);
+  const int nvmin = (int)cmp_visible(dm.q0 + rt0, dm.l, dm.d, dm.Nc);  // row rt0 always exists
   const int64_t r = rt0 + n;
   const bool rvalid = r < dm.Tq;
   const bool isv = rvalid && (!vid || vid[b * dm.Tq + r]);
   const int64_t t = dm.q0 + r;
-  const int64_t nv = rvalid ? cmp_visible(t, dm.l, dm.d, dm.Nc) : 0;
+  const int nv = rvalid ? (int)cmp_visible(t, dm.l, dm.d, dm.Nc) : 0;
   const int h = g * G + w;
   const float c2 = dm.scale * LOG2E_F;
 
@@ -150,10 +164,39 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
     }
     return s;
   };
+  // key of score register j of block kb in tile `tile`
+  auto key_of = [&](int tile, int kb, int j) { return tile * CK + kb * 32 + 8 * (j >> 2) + 4 * hl + (j & 3); };
+  // tiles whose keys every row of the workgroup sees need no mask
+  auto full = [&](int tile) { return (tile + 1) * CK <= nvmin; };
 
-  // ---- sweep 1: log-sum-exp per (row, head) column, log2 domain
-  float m2 = -INFINITY, lsum = 0.f;
-  const int nt1 = (int)((nvmax + CK - 1) / CK);
+  // ---- sweep 1: log-sum-exp per (row, head) column.  mr: running maximum of the raw scores,
+  // lsum: sum of 2^((s - mr) c2)
+  float mr = -INFINITY, lsum = 0.f;
+  auto lse_tile = [&](int bufi, int tile, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s = scores(bufi, kb);
+      if constexpr (MASK) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (key_of(tile, kb, j) >= nv) s[j] = -INFINITY;
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[j]);
+      const float mnew = fmaxf(mr, mx);
+      if (mnew > -INFINITY) {
+        const float off = -mnew * c2;
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc += fexp2(fmaf(s[j], c2, off));
+        lsum = lsum * fexp2((mr - mnew) * c2) + acc;
+        mr = mnew;
+      }
+    }
+  };
+  const int nt1 = (nvmax + CK - 1) / CK;
   if (nt1 > 0) {
     stage_k(0, 0);
     wait_loads();
@@ -162,38 +205,21 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
   for (int tile = 0; tile < nt1; ++tile) {
     const int bufi = tile & 1;
     if (tile + 1 < nt1) stage_k(tile + 1, bufi ^ 1);
-    float x[32];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const f32x16 s = scores(bufi, kb);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int64_t key = (int64_t)tile * CK + kb * 32 + 8 * (j >> 2) + 4 * hl + (j & 3);
-        x[kb * 16 + j] = key < nv ? s[j] * c2 : -INFINITY;
-      }
-    }
-    float mx = x[0];
-#pragma unroll
-    for (int j = 1; j < 32; ++j) mx = fmaxf(mx, x[j]);
-    const float mnew = fmaxf(m2, mx);
-    if (mnew > -INFINITY) {
-      float acc = 0.f;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) acc += fexp2(x[j] - mnew);
-      lsum = lsum * fexp2(m2 - mnew) + acc;
-      m2 = mnew;
-    }
+    if (full(tile))
+      lse_tile(bufi, tile, std::false_type{});
+    else
+      lse_tile(bufi, tile, std::true_type{});
     wait_loads();
     __syncthreads();
   }
-  float L2;
+  float L2;  // log2-domain normaliser: p = 2^(s c2 - L2)
   {
-    const float mo = __shfl_xor(m2, 32, 64);
-    const float lo = __shfl_xor(lsum, 32, 64);
-    const float M = fmaxf(m2, mo);
+    const float mo = xchg32(mr, hl), lo = xchg32(lsum, hl);
+    const float M = fmaxf(mr, mo);
     if (M > -INFINITY) {
-      const float tot = (m2 > -INFINITY ? lsum * fexp2(m2 - M) : 0.f) + (mo > -INFINITY ? lo * fexp2(mo - M) : 0.f);
-      L2 = M + flog2(tot);
+      const float tot = (mr > -INFINITY ? lsum * fexp2((mr - M) * c2) : 0.f) +
+                        (mo > -INFINITY ? lo * fexp2((mo - M) * c2) : 0.f);
+      L2 = M * c2 + flog2(tot);
     } else {
       L2 = INFINITY;  // no visible block: every probability is zero
     }
@@ -215,36 +241,25 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
   }
   f32x16 oacc[4] = {};
   float carry = 0.f;  // half share of the previous run's last compressed block (hl == 0 lanes)
-  const int nt2 = nvmax > 0 ? (int)(nvmax / CK) + 1 : 0;
   const int g16 = l >> 4, i16 = l & 15;
-  if (nt2 > 0) {
-    stage_k(0, 0);
-    stage_v(0, 0);
-    wait_loads();
-  }
-  __syncthreads();
-  for (int tile = 0; tile < nt2; ++tile) {
-    const int bufi = tile & 1;
-    if (tile + 1 < nt2) {
-      stage_k(tile + 1, bufi ^ 1);
-      stage_v(tile + 1, bufi ^ 1);
-    }
-    float* ipb = ipart + bufi * G * CQ * 16;
+  auto pv_tile = [&](int bufi, int tile, float* ipb, bool mask) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const f32x16 s = scores(bufi, kb);
       float p[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int64_t key = (int64_t)tile * CK + kb * 32 + 8 * (j >> 2) + 4 * hl + (j & 3);
-        p[j] = key < nv ? fexp2(fmaf(s[j], c2, -L2)) : 0.f;
+      for (int j = 0; j < 16; ++j) p[j] = fexp2(fmaf(s[j], c2, -L2));
+      if (mask) {  // uniform: only tiles with keys past some row's last visible one
+#pragma unroll
+        for (int j = 0; j < 16; ++j) p[j] = key_of(tile, kb, j) < nv ? p[j] : 0.f;
       }
       // importance of the four selection blocks this lane covers in this 32-key run
       float a[4], oth[4];
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        a[qq] = p[4 * qq] + p[4 * qq + 1] + p[4 * qq + 2] + 0.5f * p[4 * qq + 3];
-        oth[qq] = __shfl_xor(0.5f * p[4 * qq + 3], 32, 64);
+        const float half = 0.5f * p[4 * qq + 3];
+        a[qq] = p[4 * qq] + p[4 * qq + 1] + p[4 * qq + 2] + half;
+        oth[qq] = xchg32(half, hl);
       }
       if (hl == 0) {
         a[0] += carry;
@@ -256,7 +271,7 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) a[qq] += oth[qq];
       }
-      float* ip = ipb + (w * CQ + n) * 16 + kb * 8 + hl;
+      float* ip = ipb + (w * CQ + n) * IPS + kb * 8 + hl;
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) ip[2 * qq] = a[qq];
       // O^T += Vc^T P^T in two 16-key steps
@@ -287,6 +302,22 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
         }
       }
     }
+  };
+  const int nt2 = nvmax > 0 ? nvmax / CK + 1 : 0;
+  if (nt2 > 0) {
+    stage_k(0, 0);
+    stage_v(0, 0);
+    wait_loads();
+  }
+  __syncthreads();
+  for (int tile = 0; tile < nt2; ++tile) {
+    const int bufi = tile & 1;
+    if (tile + 1 < nt2) {
+      stage_k(tile + 1, bufi ^ 1);
+      stage_v(tile + 1, bufi ^ 1);
+    }
+    float* ipb = ipart0 + (ipart_bufs == 2 ? bufi : 0) * G * CQ * IPS;
+    pv_tile(bufi, tile, ipb, !full(tile));
     wait_loads();
     __syncthreads();
     // sum the group's heads in a fixed order; write the tile's 16 selection blocks
@@ -297,9 +328,10 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
       if (J > jmax[k2]) continue;
       const int nn = i >> 4;
       float sum = 0.f;
-      for (int ww = 0; ww < G; ++ww) sum += ipb[(ww * CQ + nn) * 16 + (i & 15)];
+      for (int ww = 0; ww < G; ++ww) sum += ipb[(ww * CQ + nn) * IPS + (i & 15)];
       imp[((b * dm.Tq + rt0 + nn) * dm.Hkv + g) * dm.Ns + J] = sum;
     }
+    if (ipart_bufs == 1) __syncthreads();  // the partials are rewritten by the next tile
   }
   // blocks up to the row's own block that no compressed block reaches
   for (int idx = tid; idx < CQ * 16; idx += nthr) {
@@ -340,8 +372,14 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
   }
 }
 
-size_t cmp_fast_smem(const Dims& dm, bool split) {
-  return (size_t)2 * (split ? 4 : 2) * TILE * 2 + (size_t)2 * dm.G * CQ * 16 * 4;
+// Dynamic LDS: the staged K / V buffers, then 1 or 2 buffers of importance partials (2 when
+// they fit next to the static LDS of the kernel).
+static int cmp_ipart_bufs(const Dims& dm, bool split, size_t* bytes) {
+  const size_t stage = (size_t)2 * (split ? 4 : 2) * TILE * 2;
+  const size_t ip = (size_t)dm.G * CQ * IPS * 4;
+  const int bufs = stage + 2 * ip + 64 <= (size_t)160 * 1024 ? 2 : 1;
+  *bytes = stage + bufs * ip;
+  return bufs;
 }
 
 hipError_t launch_cmp_fast(const Dims& dm, const void* q, const void* kh, const void* kl, const void* vh,
@@ -352,7 +390,8 @@ hipError_t launch_cmp_fast(const Dims& dm, const void* q, const void* kh, const 
   const int units = (int)(dm.B * dm.Hkv);
   dim3 grid(xcd_grid(units, ntq)), block(dm.G * 64);
   const bool split = kl != nullptr;
-  const size_t shm = cmp_fast_smem(dm, split);
+  size_t shm;
+  const int bufs = cmp_ipart_bufs(dm, split, &shm);
   // the MFMA layer path always brings split parts with V^T tiles; standalone calls bring neither
   if (split != vt) return hipErrorInvalidValue;
   const void* fn = split ? (const void*)cmp_fast_kernel<true, true> : (const void*)cmp_fast_kernel<false, false>;
@@ -361,11 +400,11 @@ hipError_t launch_cmp_fast(const Dims& dm, const void* q, const void* kh, const 
   if (split)
     cmp_fast_kernel<true, true><<<grid, block, shm, s>>>((const bf16*)q, (const bf16*)kh, (const bf16*)kl,
                                                          (const bf16*)vh, (const bf16*)vl, vid, (bf16*)o, o32, lse,
-                                                         imp, dm, ntq);
+                                                         imp, dm, ntq, bufs);
   else
     cmp_fast_kernel<false, false><<<grid, block, shm, s>>>((const bf16*)q, (const bf16*)kh, nullptr,
                                                            (const bf16*)vh, nullptr, vid, (bf16*)o, o32, lse, imp,
-                                                           dm, ntq);
+                                                           dm, ntq, bufs);
   return hipGetLastError();
 }
 
