@@ -36,6 +36,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="128k", choices=["128k", "36k", "sweep"])
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--no-prefill", action="store_true", help="decode only (no headline value; for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-phase timing pass")
     ap.add_argument("--decode-steps", type=int, default=200)
@@ -274,6 +275,9 @@ def main():
     nsa.lib()
     torch.cuda.init()
     wl = synth.WORKLOADS[args.workload]
+    if args.no_prefill:
+        print(json.dumps({"decode": decode(args)}))
+        return
     res, inp = prefill(args, wl)
     ker = res.get("kernels", {})
     roofline = None

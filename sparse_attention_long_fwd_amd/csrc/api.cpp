@@ -152,7 +152,8 @@ int run_cmp(int32_t dtype, int32_t cdtype, const Dims& dm, const void* q, const 
             const void* vc, const void* vl, const uint8_t* vid, void* o, float* o32, float* lse, float* imp,
             hipStream_t s) {
   // low parts come only from the layer's own compression, which writes V as V^T tiles
-  hipError_t e = use_fast(dtype, dm) ? launch_cmp_fast(dm, q, kc, kl, vc, vl, vid, o, o32, lse, imp, kl != nullptr, s)
+  hipError_t e = use_fast(dtype, dm) ? launch_cmp_fast(dm, q, kc, kl, vc, vl, vid, o, o32, lse, imp,
+                                                       kl != nullptr, s)
                                      : launch_cmp_generic(dtype, cdtype, dm, q, kc, vc, vid, o, lse, imp, s);
   if (e != hipSuccess) return hip_fail(e, "compression-branch kernel");
   return NSA_OK;

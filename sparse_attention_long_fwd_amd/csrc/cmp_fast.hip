@@ -329,7 +329,7 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
       const int nn = i >> 4;
       float sum = 0.f;
       for (int ww = 0; ww < G; ++ww) sum += ipb[(ww * CQ + nn) * IPS + (i & 15)];
-      imp[((b * dm.Tq + rt0 + nn) * dm.Hkv + g) * dm.Ns + J] = sum;
+      if (imp) imp[((b * dm.Tq + rt0 + nn) * dm.Hkv + g) * dm.Ns + J] = sum;
     }
     if (ipart_bufs == 1) __syncthreads();  // the partials are rewritten by the next tile
   }
@@ -339,7 +339,7 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
     const int64_t rr = rt0 + nn;
     if (rr >= dm.Tq || (vid && !vid[b * dm.Tq + rr])) continue;
     const int64_t J = (int64_t)nt2 * 16 + jj;
-    if (J <= (dm.q0 + rr) / dm.ls && J < dm.Ns) imp[((b * dm.Tq + rr) * dm.Hkv + g) * dm.Ns + J] = 0.f;
+    if (imp && J <= (dm.q0 + rr) / dm.ls && J < dm.Ns) imp[((b * dm.Tq + rr) * dm.Hkv + g) * dm.Ns + J] = 0.f;
   }
 
   if (!isv) return;

@@ -12,7 +12,8 @@ size_t fast_sparse_workspace(const Dims& dm);
 // Compression branch + importance.  kh/vh: compressed keys/values (bf16); kl/vl:
 // their low parts when they come from an fp32 sum (both NULL otherwise).  vt: the
 // values come as V^T tiles from launch_compress_vt (required with low parts).
-// o (bf16) and o32 (fp32) are optional copies of the branch output.
+// o (bf16) and o32 (fp32) are optional copies of the branch output; imp (optional)
+// the block importance.
 hipError_t launch_cmp_fast(const Dims& dm, const void* q, const void* kh, const void* kl, const void* vh,
                            const void* vl, const uint8_t* vid, void* o, float* o32, float* lse, float* imp,
                            bool vt, hipStream_t s);

@@ -1,0 +1,190 @@
+// One wave selects the blocks of one (row, KV group): the forced blocks and the kk best free
+// candidates by (importance descending, block index ascending), written ascending and -1 padded
+// (top168.com digest of VideoNSA, section 一: the selection branch keeps the most important
+// segments).
+//
+// Threshold method: each lane takes up to TK_REG candidates (strided by 64).  The kk-th largest
+// of the 64 lane maxima, th, is a lower bound of the kk-th largest candidate (the kk lanes with
+// the largest maxima each hold a value >= th), so the candidates >= th contain the answer.  They
+// are compacted into LDS, one per lane (a wave prefix sum gives each lane its slots), and the
+// exact kk-th largest value among them is found by a bitwise search on order-preserving integer
+// keys with wave ballots; ties at that value go to the lower block indices.  Rows with more
+// candidates than the registers hold, or more than 64 values >= th (heavy ties), take kk rounds
+// of a wave-wide arg-max instead, each strictly after the previous pick.
+#pragma once
+#include "common.hpp"
+
+constexpr int TK_REG = 32;
+
+// (a, ja) ranks before (b, jb)
+__device__ __forceinline__ bool tk_before(float a, int ja, float b, int jb) { return a > b || (a == b && ja < jb); }
+
+// LDS scratch of one wave
+struct TopkScratch {
+  float v[64];
+  int j[64];
+  int sel[32];
+};
+
+__device__ __forceinline__ void tk_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Integer key with the order of the float (larger float <-> larger unsigned key).
+__device__ __forceinline__ uint32_t tk_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Largest key K with #{active lanes: key >= K} >= kk (the kk-th largest key); needs >= kk
+// active lanes.  Uniform result.
+__device__ __forceinline__ uint32_t tk_kth_key(uint32_t key, bool active, int kk) {
+  uint32_t res = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = res | (1u << bit);
+    if ((int)__popcll(__ballot(active && key >= cand)) >= kk) res = cand;
+  }
+  return res;
+}
+
+// x: importance indexed by block (global or LDS).  Free candidates [lo, hi); forced blocks
+// [0, lo) and [hi, nj); kk = places for free candidates (n minus the forced count); out: n
+// entries.  Whole wave, uniform arguments.
+__device__ inline void wave_select(const float* __restrict__ x, int lo, int hi, int nj, int kk, int n,
+                                   TopkScratch* sc, int32_t* __restrict__ out, int lane) {
+  uint64_t chosen = 0;  // lanes whose (sc_v, sc_j) entry is chosen (threshold path)
+  int cj = 0;           // this lane's entry index (threshold path)
+  int nsel = 0;         // chosen free blocks
+  bool in_sel = false;  // chosen blocks are in sc->sel (round / all paths) rather than lanes
+  const int nc = hi - lo;
+  if (kk > 0 && nc > 0) {
+    if (nc <= kk) {
+      if (lane < nc) sc->sel[lane] = lo + lane;
+      nsel = nc;
+      in_sel = true;
+    } else {
+      bool done = false;
+      if (nc <= 64 * TK_REG) {
+        float cv[TK_REG];
+        float lm = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < TK_REG; ++c) {
+          const int j = lo + lane + 64 * c;
+          cv[c] = j < hi ? x[j] : -INFINITY;
+          if (j < hi) lm = fmaxf(lm, cv[c]);
+        }
+        // th: the kk-th largest lane maximum (lanes without a candidate take no part)
+        const uint32_t thk = tk_kth_key(tk_key(lm), lane < nc, kk);
+        int cnt = 0;
+#pragma unroll
+        for (int c = 0; c < TK_REG; ++c) cnt += (lo + lane + 64 * c < hi && tk_key(cv[c]) >= thk) ? 1 : 0;
+        int incl = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += y;
+        }
+        const int total = __shfl(incl, 63, 64);
+        if (total <= 64) {
+          int pos = incl - cnt;
+#pragma unroll
+          for (int c = 0; c < TK_REG; ++c) {
+            const int j = lo + lane + 64 * c;
+            if (j < hi && tk_key(cv[c]) >= thk) {
+              sc->v[pos] = cv[c];
+              sc->j[pos] = j;
+              ++pos;
+            }
+          }
+          tk_wave_sync();
+          const bool act = lane < total;
+          const float v = act ? sc->v[lane] : -INFINITY;
+          cj = act ? sc->j[lane] : 0x7fffffff;
+          // exact kk-th largest value among the total (>= kk) entries, then ties by index
+          const uint32_t k = tk_key(v);
+          const uint32_t kth = tk_kth_key(k, act, kk);
+          const uint64_t gt = __ballot(act && k > kth);
+          uint64_t eq = __ballot(act && k == kth);
+          chosen = gt;
+          for (int need = kk - (int)__popcll(gt); need > 0; --need) {  // lowest indices among the ties
+            int best = 0x7fffffff, bl = 0;
+            for (uint64_t m = eq; m; m &= m - 1) {
+              const int ln = (int)__builtin_ctzll(m);
+              const int jl = __shfl(cj, ln, 64);
+              if (jl < best) {
+                best = jl;
+                bl = ln;
+              }
+            }
+            chosen |= 1ull << bl;
+            eq &= ~(1ull << bl);
+          }
+          nsel = kk;
+          done = true;
+        }
+      }
+      if (!done) {
+        float pv = INFINITY;
+        int pj = -1;
+        for (int round = 0; round < kk; ++round) {
+          float bv = -INFINITY;
+          int bj = 0x7fffffff;
+          for (int j = lo + lane; j < hi; j += 64) {
+            const float xv = x[j];
+            if (tk_before(pv, pj, xv, j) && tk_before(xv, j, bv, bj)) {
+              bv = xv;
+              bj = j;
+            }
+          }
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1) {
+            const float ov = __shfl_xor(bv, o, 64);
+            const int oj = __shfl_xor(bj, o, 64);
+            if (tk_before(ov, oj, bv, bj)) {
+              bv = ov;
+              bj = oj;
+            }
+          }
+          if (lane == 0) sc->sel[round] = bj;
+          pv = bv;
+          pj = bj;
+        }
+        nsel = kk;
+        in_sel = true;
+      }
+    }
+  }
+  tk_wave_sync();
+  // ascending: forced [0, lo), chosen (all inside [lo, hi)), forced [hi, nj), then -1
+  if (in_sel) {
+    if (lane < nsel) {
+      const int J = sc->sel[lane];
+      int pos = lo;
+      for (int c = 0; c < nsel; ++c) pos += sc->sel[c] < J ? 1 : 0;
+      out[pos] = J;
+    }
+  } else if (chosen) {
+    int pos = lo;
+    for (uint64_t m = chosen; m; m &= m - 1) pos += __shfl(cj, (int)__builtin_ctzll(m), 64) < cj ? 1 : 0;
+    if ((chosen >> lane) & 1) out[pos] = cj;
+  }
+  if (lane < lo) out[lane] = lane;
+  const int a = lo + nsel;
+  if (lane >= a && lane < n) out[lane] = lane - a < nj - hi ? hi + (lane - a) : -1;
+  tk_wave_sync();  // the scratch may be reused by the next call
+}
+
+// Forced-block bounds of the row at absolute position t: free candidates [*lo, *hi), forced
+// [0, *lo) and [*hi, *nj); returns kk.
+__device__ __forceinline__ int tk_bounds(int64_t t, int ls, int64_t Ns, int n, int n_init, int n_local, int* lo,
+                                         int* hi, int* nj) {
+  const int64_t jt = t / ls;
+  *nj = (int)(jt + 1 < Ns ? jt + 1 : Ns);
+  *lo = n_init < *nj ? n_init : *nj;
+  const int h0 = (int)jt - n_local + 1;
+  *hi = h0 < *lo ? *lo : h0;
+  return n - (*lo + (*nj > *hi ? *nj - *hi : 0));
+}

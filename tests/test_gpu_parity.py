@@ -90,6 +90,28 @@ def test_cmp_attn_scores(dtype, T, Hq, Hkv, D, lead, tail, q_start, path):
     assert maxabs(host(imp[0])[V], ri[V]) <= 2e-4
 
 
+@pytest.mark.parametrize("want", [("o_cmp",), ("importance",), ("o_cmp", "lse")])
+def test_cmp_attn_scores_optional_outputs(want, path):
+    """Outputs left NULL are not written; the given ones equal those of a full call."""
+    T, Hq, Hkv, D = 2100, 14, 2, 128
+    wl = _wl("bf16", T, Hq, Hkv, D, lead=64, tail=20)
+    Nc = nsa.num_cmp_blocks(T, 32, 16)
+    q = _rand(121, (1, T, Hq, D), torch.bfloat16)
+    kc = _rand(122, (1, Nc, Hkv, D), torch.bfloat16)
+    vc = _rand(123, (1, Nc, Hkv, D), torch.bfloat16)
+    vid = synth.video_mask(wl, DEV)
+    sh = nsa.make_shape(1, T, T, 0, Hq, Hkv, D)
+    pr = nsa.make_params(top_n=16, window=512)
+    full = nsa.nsa_cmp_attn_scores(q, kc, vc, sh, pr, is_video=vid)
+    part = nsa.nsa_cmp_attn_scores(q, kc, vc, sh, pr, is_video=vid, want=want)
+    torch.cuda.synchronize()
+    for name, a_, b_ in zip(("o_cmp", "lse", "importance"), full, part):
+        if name in want:
+            assert torch.equal(a_, b_), name
+        else:
+            assert b_ is None
+
+
 # --------------------------------------------------------------------------- top-n
 @pytest.mark.parametrize("n,n_init,n_local,Ns", [(4, 1, 2, 16), (16, 1, 2, 568), (16, 1, 2, 2048), (8, 2, 3, 300),
                                                   (32, 1, 2, 2048), (3, 0, 3, 50)])
@@ -242,7 +264,7 @@ def compare_layer(wl, inp, got, rows, b=0, kc=None, vc=None):
     return stats
 
 
-@pytest.mark.parametrize("case", ["tiny", "bf16-4k", "bf16-ragged", "bf16-batch2"])
+@pytest.mark.parametrize("case", ["tiny", "bf16-4k", "bf16-ragged", "bf16-batch2", "bf16-g4", "bf16-g8"])
 def test_layer_small(case, path):
     if case == "tiny":
         wl = synth.WORKLOADS["tiny"]
@@ -250,6 +272,10 @@ def test_layer_small(case, path):
         wl = _wl(T=4096, lead=256, tail=256)
     elif case == "bf16-ragged":
         wl = _wl(T=1000 + 37, Hq=14, Hkv=2, lead=64, tail=13, n=6, w=100)
+    elif case == "bf16-g4":  # 4 query heads per KV head
+        wl = _wl(T=2600, Hq=8, Hkv=2, lead=64, tail=30, n=8, w=256)
+    elif case == "bf16-g8":  # 8 query heads per KV head (one importance buffer in LDS)
+        wl = _wl(T=5000, Hq=16, Hkv=2, lead=64, tail=30, n=8, w=256)
     else:
         wl = _wl(T=900, B=2, lead=128, tail=0, n=8, w=256)
     flush("layer %s path=%s" % (case, path))
