@@ -128,7 +128,7 @@ LayerWs layer_ws(const Dims& dm, int32_t dtype) {
   w.lse = round_up((size_t)dm.B * dm.Tq * dm.Hq * 4);
   w.idx = round_up((size_t)dm.B * dm.Tq * dm.Hkv * dm.n * 4);
   if (fast && decode_supported(dm)) {
-    w.dec = round_up(decode_workspace(dm)) + round_up(flash_workspace(dm));
+    w.dec = round_up(decode_workspace(dm));
   } else if (fast) {
     // values as V^T tiles (padded to whole 64-key tiles), high + low parts
     const size_t vt = round_up(vt_tiles_bytes(dm)) * 2;
@@ -395,11 +395,6 @@ int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const 
     hipError_t e = launch_decode_fast(dm, q, kc_use, kl_use, vc_use, vl_use, k, v, is_video, gates, out, o_cmp,
                                       o_slc, o_swa, didx, lse, nullptr, sparse_ws_ptr, s, prof_mark);
     if (e != hipSuccess) return hip_fail(e, "decode kernels");
-    if (is_video) {  // text rows: dense attention
-      e = launch_flash_fast(dm, q, k, v, is_video, nullptr, nullptr, out,
-                            (char*)sparse_ws_ptr + round_up(decode_workspace(dm)), s);
-      if (e != hipSuccess) return hip_fail(e, "text-row kernel");
-    }
     prof_mark(s);
     return NSA_OK;
   }

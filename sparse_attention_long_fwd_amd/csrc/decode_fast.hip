@@ -11,15 +11,18 @@
 //     scores for the G heads (16x16x32 MFMA, heads on N), a local softmax, the
 //     value sum, and the importance of the chunk's 32 selection blocks, all in
 //     the chunk's own frame (max, sum), written as a partial.
-//  2. dcmp_merge: one workgroup per (sequence, group): merges the partials per
-//     head (log-sum-exp), rescales the importance partials to the final
-//     normaliser, sums them over the heads, and picks the top-n blocks.
-//  3. dsparse_blocks: one wave per (sequence, group, block of the union of the
-//     chosen blocks and the window): scores once, then a selection partial and
-//     a window partial with their own masks.
-//  4. dsparse_merge: merges the block partials per head and applies the gated
-//     combine.
+//  2. dsel: one workgroup per (sequence, group, 4 blocks of the union of the
+//     chosen blocks and the window).  Each workgroup merges the importance
+//     partials (rescaled to the final normaliser, summed over the heads) and
+//     picks the top-n blocks itself; a wave per block scores it once and keeps
+//     a selection partial and a window partial with their own masks.  The last
+//     workgroup of a (sequence, group) to finish merges the compression,
+//     selection and window partials per head and applies the gated combine.
+//     Text rows (dense causal attention, ungated): their split workgroups exit
+//     at once; in this kernel each wave runs an online softmax over every
+//     (4 x workgroups)-th block, and the last workgroup merges those.
 #include "fast_common.hpp"
+#include "topk_wave.hpp"
 
 namespace {
 constexpr int HD = 128;
@@ -37,7 +40,8 @@ template <bool SPLIT>
 __global__ void __launch_bounds__(256) dcmp_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kh,
                                                          const bf16* __restrict__ kl, const bf16* __restrict__ vh,
                                                          const bf16* __restrict__ vl, const uint8_t* __restrict__ vid,
-                                                         float* __restrict__ part, Dims dm, int nsplit) {
+                                                         float* __restrict__ part, int* __restrict__ cnt, Dims dm,
+                                                         int nsplit) {
   constexpr int NA = SPLIT ? 2 : 1;  // staged V arrays (hi, lo)
   // per wave: V rows; after the value products the same bytes hold the waves' outputs [4][16][HD] fp32
   __shared__ __attribute__((aligned(16))) unsigned char d_smem[4 * NA * 32 * HD * 2];
@@ -50,6 +54,8 @@ __global__ void __launch_bounds__(256) dcmp_split_kernel(const bf16* __restrict_
   const int unit = blockIdx.x / nsplit;
   const int64_t b = unit / dm.Hkv;
   const int g = unit % dm.Hkv;
+  if (blockIdx.x == 0)  // completion counters of the next kernel
+    for (int i = threadIdx.x; i < dm.B * dm.Hkv; i += blockDim.x) cnt[i] = 0;
   if (vid && !vid[b]) return;
   const int G = dm.G;
   const int64_t t = dm.q0;
@@ -191,188 +197,41 @@ __global__ void __launch_bounds__(256) dcmp_split_kernel(const bf16* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// 2. importance and top-n (one workgroup of 16 waves per (sequence, group))
-__device__ __forceinline__ bool dbefore(float a, int ja, float b, int jb) { return a > b || (a == b && ja < jb); }
+// 2. selection, window and the final merge
 
-// Per-head softmax statistics of the split partials, one wave per head:
+// Per-head softmax statistics of the split partials, one wave per head (waves loop over heads):
 // s_fac[h][s] = exp2(m_s - M_h) / L_h (0 for empty splits), s_M[h], s_L[h].
 __device__ __forceinline__ void dsplit_stats(const float* pu, int G, int nsplit, float* s_fac, float* s_M,
                                              float* s_L) {
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (wv >= G) return;
-  const int hh = wv;
-  float m = -INFINITY;
-  for (int s = lane; s < nsplit; s += 64) m = fmaxf(m, pu[(s * G + hh) * PSTRIDE]);
-  const float M = wave_max(m);
-  float l = 0.f;
-  for (int s = lane; s < nsplit; s += 64) {
-    const float ms = pu[(s * G + hh) * PSTRIDE];
-    if (ms > -INFINITY) l += pu[(s * G + hh) * PSTRIDE + 1] * fexp2(ms - M);
-  }
-  const float L = wave_sum(l);
-  for (int s = lane; s < nsplit; s += 64) {
-    const float ms = pu[(s * G + hh) * PSTRIDE];
-    s_fac[hh * nsplit + s] = (ms > -INFINITY && L > 0.f) ? fexp2(ms - M) / L : 0.f;
-  }
-  if (lane == 0) {
-    s_M[hh] = M;
-    s_L[hh] = L;
+  const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  for (int hh = threadIdx.x >> 6; hh < G; hh += nw) {
+    // one load round for up to 64 splits (the usual case); more splits loop
+    float m0 = -INFINITY, l0 = 0.f;
+    if (lane < nsplit) {
+      m0 = pu[(lane * G + hh) * PSTRIDE];
+      l0 = pu[(lane * G + hh) * PSTRIDE + 1];
+    }
+    float m = m0;
+    for (int s = lane + 64; s < nsplit; s += 64) m = fmaxf(m, pu[(s * G + hh) * PSTRIDE]);
+    const float M = wave_max(m);
+    float l = m0 > -INFINITY ? l0 * fexp2(m0 - M) : 0.f;
+    for (int s = lane + 64; s < nsplit; s += 64) {
+      const float ms = pu[(s * G + hh) * PSTRIDE];
+      if (ms > -INFINITY) l += pu[(s * G + hh) * PSTRIDE + 1] * fexp2(ms - M);
+    }
+    const float L = wave_sum(l);
+    if (lane < nsplit) s_fac[hh * nsplit + lane] = (m0 > -INFINITY && L > 0.f) ? fexp2(m0 - M) / L : 0.f;
+    for (int s = lane + 64; s < nsplit; s += 64) {
+      const float ms = pu[(s * G + hh) * PSTRIDE];
+      s_fac[hh * nsplit + s] = (ms > -INFINITY && L > 0.f) ? fexp2(ms - M) / L : 0.f;
+    }
+    if (lane == 0) {
+      s_M[hh] = M;
+      s_L[hh] = L;
+    }
   }
 }
 
-__global__ void __launch_bounds__(1024) dcmp_merge_kernel(const float* __restrict__ part, const uint8_t* __restrict__ vid,
-                                                          float* __restrict__ imp_out, int32_t* __restrict__ idx,
-                                                          Dims dm, int nsplit) {
-  extern __shared__ float dsm[];
-  float* s_imp = dsm;             // [Ns]
-  float* s_fac = dsm + dm.Ns;     // [G][nsplit]
-  __shared__ float s_M[16], s_L[16];
-  __shared__ float s_cv[4][32];   // per-wave candidates (value, index) for the final merge
-  __shared__ int s_cj[4][32];
-  __shared__ int s_items[64];
-  const int unit = blockIdx.x;
-  const int64_t b = unit / dm.Hkv;
-  const int g = unit % dm.Hkv;
-  if (vid && !vid[b]) return;
-  const int G = dm.G, tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-  const float* pu = part + (int64_t)unit * nsplit * G * PSTRIDE;
-  dsplit_stats(pu, G, nsplit, s_fac, s_M, s_L);
-  __syncthreads();
-  // importance of blocks 0 .. jt, heads summed in a fixed order
-  const int64_t t = dm.q0;
-  const int jt = (int)(t / dm.ls);
-  for (int j = tid; j <= jt; j += blockDim.x) {
-    const int s = j / DBLK, jb = j % DBLK;
-    float a[8], c[8];
-#pragma unroll
-    for (int hh = 0; hh < 8; ++hh) {
-      a[hh] = (hh < G && s < nsplit) ? pu[(s * G + hh) * PSTRIDE + 2 + HD + jb] : 0.f;
-      c[hh] = (hh < G && jb == 0 && s > 0) ? pu[((s - 1) * G + hh) * PSTRIDE + 2 + HD + DBLK] : 0.f;
-    }
-    float v = 0.f;
-#pragma unroll
-    for (int hh = 0; hh < 8; ++hh) {
-      if (hh < G && s < nsplit) v += s_fac[hh * nsplit + s] * a[hh];
-      if (hh < G && jb == 0 && s > 0) v += s_fac[hh * nsplit + s - 1] * c[hh];
-    }
-    s_imp[j] = v;
-    if (imp_out) imp_out[(b * dm.Hkv + g) * dm.Ns + j] = v;
-  }
-  __syncthreads();
-  // top-n: the free candidates [lo_cnt, hi0) are split over 4 waves; each wave keeps its best k
-  // (rounds of a wave-wide arg-max strictly below the previous pick), wave 0 merges the 4 lists.
-  const int nj = jt + 1 < dm.Ns ? jt + 1 : (int)dm.Ns;
-  const int lo_cnt = dm.n_init < nj ? dm.n_init : nj;
-  int hi0 = jt - dm.n_local + 1;
-  if (hi0 < lo_cnt) hi0 = lo_cnt;
-  const int nf = lo_cnt + (nj > hi0 ? nj - hi0 : 0);
-  const int k = dm.n - nf;
-  if (wv < 4) {
-    const int per = (hi0 - lo_cnt + 3) / 4;
-    const int c0 = lo_cnt + wv * per, c1 = c0 + per < hi0 ? c0 + per : hi0;
-    constexpr int NREG = 8;
-    float cache[NREG];
-#pragma unroll
-    for (int c = 0; c < NREG; ++c) {
-      const int j = c0 + lane + 64 * c;
-      cache[c] = j < c1 ? s_imp[j] : -INFINITY;
-    }
-    float pv = INFINITY;
-    int pj = -1;
-    for (int round = 0; round < k; ++round) {
-      float bv = -INFINITY;
-      int bj = 0x7fffffff;
-#pragma unroll
-      for (int c = 0; c < NREG; ++c) {
-        const int j = c0 + lane + 64 * c;
-        if (j < c1 && dbefore(pv, pj, cache[c], j) && dbefore(cache[c], j, bv, bj)) {
-          bv = cache[c];
-          bj = j;
-        }
-      }
-      for (int j = c0 + lane + 64 * NREG; j < c1; j += 64) {
-        const float x = s_imp[j];
-        if (dbefore(pv, pj, x, j) && dbefore(x, j, bv, bj)) {
-          bv = x;
-          bj = j;
-        }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oj = __shfl_xor(bj, o, 64);
-        if (dbefore(ov, oj, bv, bj)) {
-          bv = ov;
-          bj = oj;
-        }
-      }
-      if (lane == 0) {
-        s_cv[wv][round] = bv;
-        s_cj[wv][round] = bj;
-      }
-      pv = bv;
-      pj = bj;
-    }
-  }
-  __syncthreads();
-  if (wv != 0) return;
-  // merge: lane holds candidate (wave lane / 32... ) -- at most 4 x 32 entries, two per lane
-  float v0 = -INFINITY, v1 = -INFINITY;
-  int j0 = 0x7fffffff, j1 = 0x7fffffff;
-  {
-    const int w0 = lane >> 5, r0 = lane & 31;  // entries (w0, r0) and (w0 + 2, r0)
-    if (r0 < k) {
-      v0 = s_cv[w0][r0];
-      j0 = s_cj[w0][r0];
-      v1 = s_cv[w0 + 2][r0];
-      j1 = s_cj[w0 + 2][r0];
-    }
-  }
-  int ntot = 0;
-  for (int j = 0; j < lo_cnt; ++j) s_items[ntot++] = j;
-  for (int j = hi0; j < nj; ++j) s_items[ntot++] = j;
-  float pv = INFINITY;
-  int pj = -1;
-  for (int round = 0; round < k; ++round) {
-    float bv = -INFINITY;
-    int bj = 0x7fffffff;
-    if (j0 != 0x7fffffff && dbefore(pv, pj, v0, j0)) {
-      bv = v0;
-      bj = j0;
-    }
-    if (j1 != 0x7fffffff && dbefore(pv, pj, v1, j1) && dbefore(v1, j1, bv, bj)) {
-      bv = v1;
-      bj = j1;
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oj = __shfl_xor(bj, o, 64);
-      if (dbefore(ov, oj, bv, bj)) {
-        bv = ov;
-        bj = oj;
-      }
-    }
-    if (bj == 0x7fffffff) break;
-    if (lane == 0) s_items[ntot] = bj;
-    ++ntot;
-    pv = bv;
-    pj = bj;
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  int32_t* out = idx + (b * dm.Hkv + g) * dm.n;
-  if (lane < ntot) {
-    const int me = s_items[lane];
-    int rank = 0;
-    for (int c = 0; c < ntot; ++c) rank += (s_items[c] < me);
-    out[rank] = me;
-  } else if (lane < dm.n) {
-    out[lane] = -1;
-  }
-}
-// ---------------------------------------------------------------------------
-// 3. selection / window partials per block of the union
 // Slot k of a unit: the k-th block of (chosen blocks below the window) ++ (window blocks).
 __device__ __forceinline__ int64_t union_block(const int32_t* sel, int n, int64_t jt, int64_t wb0, int k, bool* in_sel,
                                                bool* in_win) {
@@ -395,197 +254,357 @@ __device__ __forceinline__ int64_t union_block(const int32_t* sel, int n, int64_
   return j;
 }
 
-__global__ void __launch_bounds__(256) dsparse_blocks_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                                             const bf16* __restrict__ v,
-                                                             const int32_t* __restrict__ idx,
-                                                             const uint8_t* __restrict__ vid,
-                                                             float* __restrict__ part3, Dims dm, int nslot) {
+// One workgroup per (unit, 4 slots of the union), a wave per slot.  Every workgroup of a unit
+// first merges the importance partials of the compression split and picks the unit's blocks
+// (the same deterministic result in each); then each wave scores its block once and keeps a
+// selection partial and a window partial (own masks, own local softmax).  The last workgroup
+// of the unit to finish (device-scope counter, zeroed by the split kernel) merges the
+// compression, selection and window partials per head and writes the gated outputs.
+__global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                   const bf16* __restrict__ v, const float* __restrict__ part,
+                                                   const uint8_t* __restrict__ vid, const float* __restrict__ gates,
+                                                   bf16* __restrict__ out, bf16* __restrict__ o_cmp,
+                                                   bf16* __restrict__ o_slc, bf16* __restrict__ o_swa,
+                                                   float* __restrict__ lse, int32_t* __restrict__ idx,
+                                                   float* __restrict__ imp_out, float* __restrict__ part3,
+                                                   float* __restrict__ ocmp32, int* __restrict__ cnt, Dims dm,
+                                                   int nsplit, int nslot, int wgs) {
+  extern __shared__ float dsm[];
+  const int G = dm.G;
+  float* s_imp = dsm;                   // [Ns] importance of the unit's blocks
+  float* s_fac = s_imp + dm.Ns;         // [G][nsplit] weights of the compression partials
   __shared__ __attribute__((aligned(16))) bf16 vt[4][SB * HD];
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, hn = l & 15, grp = l >> 4;
-  const int slots_per_wg = 4;
-  const int wgs = (nslot + slots_per_wg - 1) / slots_per_wg;
-  const int unit = blockIdx.x / wgs;
-  const int slot = (blockIdx.x % wgs) * slots_per_wg + w;
-  const int64_t b = unit / dm.Hkv;
-  const int g = unit % dm.Hkv;
-  if (vid && !vid[b]) return;
-  if (slot >= nslot) return;
-  const int G = dm.G;
-  const int64_t t = dm.q0, jt = t / SB;
-  int64_t wlo = t - dm.w + 1;
-  if (wlo < 0) wlo = 0;
-  const int64_t wb0 = wlo / SB;
-  const int32_t* sel = idx + (b * dm.Hkv + g) * dm.n;
-  bool in_sel = false, in_win = false;
-  const int64_t j = union_block(sel, dm.n, jt, wb0, slot, &in_sel, &in_win);
-  float* ps = part3 + (((int64_t)unit * nslot + slot) * 2) * G * (HD + 2);
-  if (j < 0) {  // unused slot: empty partials
-    for (int i = l; i < 2 * G; i += 64) ps[(i / G) * G * (HD + 2) + (i % G) * (HD + 2) + 1] = 0.f;
-    return;
-  }
-  const float c2 = dm.scale * LOG2E_F;
-  const bool hvalid = hn < G;
-  const int h = g * G + (hvalid ? hn : 0);
-  bf16x8 qf[4];
-  {
-    const bf16* qrow = q + (b * dm.Hq + h) * (int64_t)HD + 8 * grp;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = hvalid ? *(const bf16x8*)(qrow + 32 * ks) : zero8();
-  }
-  const int64_t stride = (int64_t)dm.Hkv * HD;
-  const bf16* kbase = k + (b * dm.T * dm.Hkv + g) * (int64_t)HD;
-  const bf16* vbase = v + (b * dm.T * dm.Hkv + g) * (int64_t)HD;
-  stage_tile64(vt[w], vbase, stride, j * SB, dm.T, 0, 1, l);
-  f32x4 sc[4];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    int64_t key = j * SB + 16 * kb + hn;
-    if (key >= dm.T) key = dm.T - 1;
-    const bf16* kr = kbase + key * stride + 8 * grp;
-    sc[kb] = f32x4{};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) sc[kb] = mfma16(*(const bf16x8*)(kr + 32 * ks), qf[ks], sc[kb]);
-  }
-  dwait();
-  __builtin_amdgcn_wave_barrier();
-  for (int br = 0; br < 2; ++br) {
-    const bool act = br == 0 ? in_sel : in_win;
-    float* pb_ = ps + br * G * (HD + 2);
-    if (!act) {
-      if (hvalid && grp == 0) pb_[hn * (HD + 2) + 1] = 0.f;
-      continue;
-    }
-    float x[16];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int64_t u = j * SB + 16 * kb + 4 * grp + jj;
-        const bool ok = br == 0 ? (u <= t) : (u <= t && u >= wlo);
-        x[4 * kb + jj] = ok ? sc[kb][jj] * c2 : -INFINITY;
-      }
-    float mx = x[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    float p[16], ls = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      p[e] = mx > -INFINITY ? fexp2(x[e] - mx) : 0.f;
-      ls += p[e];
-    }
-    ls += __shfl_xor(ls, 16, 64);
-    ls += __shfl_xor(ls, 32, 64);
-    f32x4 oacc[8];
-#pragma unroll
-    for (int db = 0; db < 8; ++db) oacc[db] = f32x4{};
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pb[e] = (bf16)p[4 * (2 * st) + e];
-        pb[4 + e] = (bf16)p[4 * (2 * st + 1) + e];
-      }
-      const int vr = 32 * st + 4 * grp + (hn >> 2);
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const int col = 16 * db + 4 * (hn & 3);
-        oacc[db] = mfma16(cat(lds_read_tr(vt[w] + swz128(vr, col >> 3) + (col & 7)),
-                              lds_read_tr(vt[w] + swz128(vr + 16, col >> 3) + (col & 7))),
-                          pb, oacc[db]);
-      }
-    }
-    if (hvalid) {
-      float* ph = pb_ + hn * (HD + 2);
-      if (grp == 0) {
-        ph[0] = mx;
-        ph[1] = ls;
-      }
-#pragma unroll
-      for (int db = 0; db < 8; ++db)
-        *(float4*)(ph + 2 + 16 * db + 4 * grp) = make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 4. merge the compression partials and the block partials, gated combine
-__global__ void __launch_bounds__(1024) dsparse_merge_kernel(const float* __restrict__ part,
-                                                            const float* __restrict__ part3,
-                                                            const uint8_t* __restrict__ vid,
-                                                            const float* __restrict__ gates, bf16* __restrict__ out,
-                                                            bf16* __restrict__ o_cmp, bf16* __restrict__ o_slc,
-                                                            bf16* __restrict__ o_swa, float* __restrict__ lse, Dims dm,
-                                                            int nsplit, int nslot) {
-  const int unit = blockIdx.x;
-  const int64_t b = unit / dm.Hkv;
-  const int g = unit % dm.Hkv;
-  if (vid && !vid[b]) return;
-  const int G = dm.G;
-  extern __shared__ float s_w[];  // [nslot][2][G] weights exp2(m - M) / L of the block partials
-  float* s_mx = s_w + nslot * 2 * G;
-  float* s_fac = s_mx + nslot * 2 * G;  // [G][nsplit] weights of the compression partials
   __shared__ float s_M[16], s_L[16];
+  __shared__ int32_t s_idx[32];
+  __shared__ TopkScratch s_tk;
+  __shared__ int s_last;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hn = l & 15, grp = l >> 4;
+  const int unit = blockIdx.x / wgs, sg = blockIdx.x % wgs;
+  const int64_t b = unit / dm.Hkv;
+  const int g = unit % dm.Hkv;
+  const bool text = vid && !vid[b];  // the same for the whole workgroup
+  const int64_t t = dm.q0, jt = t / SB;
   const float* pc = part + (int64_t)unit * nsplit * G * PSTRIDE;
-  const float* pu = part3 + (int64_t)unit * nslot * 2 * G * (HD + 2);
+
+  // ---- (video) importance of blocks 0 .. jt (heads summed in a fixed order) and the top-n
+  if (!text) {
   dsplit_stats(pc, G, nsplit, s_fac, s_M, s_L);
-  for (int i = threadIdx.x; i < nslot * 2 * G; i += blockDim.x) {
-    const float* ph = pu + i * (HD + 2);
-    s_w[i] = ph[1] > 0.f ? ph[1] : 0.f;  // sum for now
-    s_mx[i] = ph[1] > 0.f ? ph[0] : -INFINITY;
+  __syncthreads();
+  // 4 blocks a thread per pass, every load of a pass issued before the sums
+  for (int j0 = 0; j0 <= jt; j0 += 4 * blockDim.x) {
+    float a[4][8], c[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * blockDim.x + tid;
+      const int s = j / DBLK, jb = j % DBLK;
+#pragma unroll
+      for (int hh = 0; hh < 8; ++hh) {
+        a[u][hh] = (j <= jt && hh < G && s < nsplit) ? pc[(s * G + hh) * PSTRIDE + 2 + HD + jb] : 0.f;
+        c[u][hh] = (j <= jt && hh < G && jb == 0 && s > 0) ? pc[((s - 1) * G + hh) * PSTRIDE + 2 + HD + DBLK] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * blockDim.x + tid;
+      if (j > jt) continue;
+      const int s = j / DBLK, jb = j % DBLK;
+      float val = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < 8; ++hh) {
+        if (hh < G && s < nsplit) val += s_fac[hh * nsplit + s] * a[u][hh];
+        if (hh < G && jb == 0 && s > 0) val += s_fac[hh * nsplit + s - 1] * c[u][hh];
+      }
+      s_imp[j] = val;
+      if (imp_out && sg == 0) imp_out[(b * dm.Hkv + g) * dm.Ns + j] = val;
+    }
   }
   __syncthreads();
-  {  // one wave per (branch, head) pair
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (wv < 2 * G) {
-      const int br = wv / G, hh = wv % G;
-      float m = -INFINITY;
-      for (int s = lane; s < nslot; s += 64) m = fmaxf(m, s_mx[(s * 2 + br) * G + hh]);
-      const float M = wave_max(m);
-      float l = 0.f;
-      for (int s = lane; s < nslot; s += 64) {
-        const int i = (s * 2 + br) * G + hh;
-        if (s_mx[i] > -INFINITY) l += s_w[i] * fexp2(s_mx[i] - M);
+  if (w == 0) {
+    int lo, hi, nj;
+    const int kk = tk_bounds(t, dm.ls, dm.Ns, dm.n, dm.n_init, dm.n_local, &lo, &hi, &nj);
+    wave_select(s_imp, lo, hi, nj, kk, dm.n, &s_tk, s_idx, l);
+    if (sg == 0 && l < dm.n) idx[(b * dm.Hkv + g) * dm.n + l] = s_idx[l];
+  }
+  __syncthreads();
+  }
+
+  // ---- per wave: branch partials (max, sum, O) of its blocks, in registers until its V tile is
+  // free, then in LDS over it.  Video units: slot sg*4+w of the union, scored once, a selection
+  // and a window partial.  Text units: dense causal attention over blocks sg*4+w, +4*wgs, ...
+  // (one online softmax, branch 0).
+  constexpr int PO = 4;       // O offset within a partial (16-byte aligned rows)
+  constexpr int PW = HD + PO;  // partial of one (branch, head): max, sum, -, -, O[128]
+  const int slot = sg * 4 + w;
+  float* wp = (float*)vt[w];  // [2][G][PW] once the products are done
+  {
+    int64_t wlo = t - dm.w + 1;
+    if (wlo < 0) wlo = 0;
+    const int64_t wb0 = wlo / SB;
+    const bool hvalid = hn < G;
+    const float c2 = dm.scale * LOG2E_F;
+    float pm[2] = {-INFINITY, -INFINITY}, pl[2] = {0.f, 0.f};
+    f32x4 po[2][8];
+#pragma unroll
+    for (int br = 0; br < 2; ++br)
+#pragma unroll
+      for (int db = 0; db < 8; ++db) po[br][db] = f32x4{};
+    bf16x8 qf[4];
+    {
+      const int h = g * G + (hvalid ? hn : 0);
+      const bf16* qrow = q + (b * dm.Hq + h) * (int64_t)HD + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qf[ks] = hvalid ? *(const bf16x8*)(qrow + 32 * ks) : zero8();
+    }
+    const int64_t stride = (int64_t)dm.Hkv * HD;
+    const bf16* kbase = k + (b * dm.T * dm.Hkv + g) * (int64_t)HD;
+    const bf16* vbase = v + (b * dm.T * dm.Hkv + g) * (int64_t)HD;
+    // block j: stage V, scores S^T (keys on M, heads on N), returned per lane
+    auto block_scores = [&](int64_t j, f32x4* sc) {
+      stage_tile64(vt[w], vbase, stride, j * SB, dm.T, 0, 1, l);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        int64_t key = j * SB + 16 * kb + hn;
+        if (key >= dm.T) key = dm.T - 1;
+        const bf16* kr = kbase + key * stride + 8 * grp;
+        sc[kb] = f32x4{};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) sc[kb] = mfma16(*(const bf16x8*)(kr + 32 * ks), qf[ks], sc[kb]);
       }
-      const float L = wave_sum(l);
-      for (int s = lane; s < nslot; s += 64) {
-        const int i = (s * 2 + br) * G + hh;
-        s_mx[i] = (s_mx[i] > -INFINITY && L > 0.f) ? fexp2(s_mx[i] - M) / L : 0.f;
+      dwait();
+      __builtin_amdgcn_wave_barrier();
+    };
+    // one branch: masked scores x (log2 units) -> online update of (pm, pl, po)[br]
+    auto accumulate = [&](int br, const float* x) {
+      float mx = x[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = fmaxf(pm[br], mx);
+      if (mnew == -INFINITY) return;
+      const float sc_old = pm[br] > -INFINITY ? fexp2(pm[br] - mnew) : 0.f;
+      float p[16], ls = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        p[e] = fexp2(x[e] - mnew);
+        ls += p[e];
+      }
+      ls += __shfl_xor(ls, 16, 64);
+      ls += __shfl_xor(ls, 32, 64);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) po[br][db] *= sc_old;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pb[e] = (bf16)p[4 * (2 * st) + e];
+          pb[4 + e] = (bf16)p[4 * (2 * st + 1) + e];
+        }
+        const int vr = 32 * st + 4 * grp + (hn >> 2);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const int col = 16 * db + 4 * (hn & 3);
+          po[br][db] = mfma16(cat(lds_read_tr(vt[w] + swz128(vr, col >> 3) + (col & 7)),
+                                  lds_read_tr(vt[w] + swz128(vr + 16, col >> 3) + (col & 7))),
+                              pb, po[br][db]);
+        }
+      }
+      pl[br] = pl[br] * sc_old + ls;
+      pm[br] = mnew;
+    };
+    if (text) {
+      for (int64_t j = slot; j <= jt; j += 4 * wgs) {
+        f32x4 sc[4];
+        block_scores(j, sc);
+        float x[16];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int64_t u = j * SB + 16 * kb + 4 * grp + jj;
+            x[4 * kb + jj] = u <= t ? sc[kb][jj] * c2 : -INFINITY;
+          }
+        accumulate(0, x);
+        tk_wave_sync();  // the tile is read before the next block overwrites it
+      }
+    } else {
+      bool in_sel = false, in_win = false;
+      const int64_t j = slot < nslot ? union_block(s_idx, dm.n, jt, wb0, slot, &in_sel, &in_win) : -1;
+      if (j >= 0) {
+        f32x4 sc[4];
+        block_scores(j, sc);
+#pragma unroll
+        for (int br = 0; br < 2; ++br) {
+          if (!(br == 0 ? in_sel : in_win)) continue;
+          float x[16];
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int64_t u = j * SB + 16 * kb + 4 * grp + jj;
+              const bool ok = br == 0 ? (u <= t) : (u <= t && u >= wlo);
+              x[4 * kb + jj] = ok ? sc[kb][jj] * c2 : -INFINITY;
+            }
+          accumulate(br, x);
+        }
+      }
+    }
+    tk_wave_sync();  // every lane is done reading the V tile
+    if (hvalid) {
+#pragma unroll
+      for (int br = 0; br < 2; ++br) {
+        float* ph = wp + (br * G + hn) * PW;
+        if (grp == 0) {
+          ph[0] = pm[br];
+          ph[1] = pl[br];
+        }
+        if (pl[br] > 0.f) {
+#pragma unroll
+          for (int db = 0; db < 8; ++db)
+            *(float4*)(ph + PO + 16 * db + 4 * grp) = make_float4(po[br][db][0], po[br][db][1], po[br][db][2],
+                                                                  po[br][db][3]);
+        }
       }
     }
   }
   __syncthreads();
-  if (lse && threadIdx.x < G)
-    lse[b * dm.Hq + g * G + threadIdx.x] =
-        s_L[threadIdx.x] > 0.f ? (s_M[threadIdx.x] + flog2(s_L[threadIdx.x])) * LN2_F : -INFINITY;
-  for (int i = threadIdx.x; i < G * HD; i += blockDim.x) {
-    const int hh = i / HD, e = i % HD;
-    float oc = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < nsplit; ++s) oc += s_fac[hh * nsplit + s] * pc[(s * G + hh) * PSTRIDE + 2 + e];
-    float ob[2];
-    for (int br = 0; br < 2; ++br) {
-      float o = 0.f;
-#pragma unroll 5
-      for (int s = 0; s < nslot; ++s) {
-        const float f = s_mx[(s * 2 + br) * G + hh];
-        const float val = pu[((s * 2 + br) * G + hh) * (HD + 2) + 2 + e];  // unwritten for empty partials
-        o += (f != 0.f) ? f * val : 0.f;
+  // ---- this workgroup's share: its waves' partials merged per (branch, head), and (video) a
+  // slice of the compression output merged over the splits
+  float* pw = part3 + ((int64_t)unit * wgs + sg) * 2 * G * PW;
+  for (int i = tid; i < 2 * G * HD / 4; i += blockDim.x) {
+    const int bh = (4 * i) / HD, e = (4 * i) % HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float* ph = (const float*)vt[ww] + bh * PW;
+      if (ph[1] > 0.f) M = fmaxf(M, ph[0]);
+    }
+    float L = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float* ph = (const float*)vt[ww] + bh * PW;
+      if (ph[1] > 0.f) {
+        const float f = fexp2(ph[0] - M);
+        const float4 x = *(const float4*)(ph + PO + e);
+        L += f * ph[1];
+        O.x += f * x.x;
+        O.y += f * x.y;
+        O.z += f * x.z;
+        O.w += f * x.w;
       }
-      ob[br] = o;
+    }
+    *(float4*)(pw + bh * PW + PO + e) = O;
+    if (e == 0) {
+      pw[bh * PW] = M;
+      pw[bh * PW + 1] = L;
+    }
+  }
+  if (!text) {
+    const int per = (G * HD + wgs - 1) / wgs;
+    for (int i = sg * per + tid; i < (sg + 1) * per && i < G * HD; i += blockDim.x) {
+      const int hh = i / HD, e = i % HD;
+      float oc = 0.f;
+#pragma unroll 16
+      for (int s = 0; s < nsplit; ++s) oc += s_fac[hh * nsplit + s] * pc[(s * G + hh) * PSTRIDE + 2 + e];
+      ocmp32[(int64_t)unit * G * HD + i] = oc;
+    }
+  }
+
+  // ---- the unit's last workgroup merges.  Every wave's stores have landed in L2 before the
+  // barrier; one agent-scope release (L2 write-back) then publishes the workgroup's partials
+  // before it is counted, and the last workgroup's acquire (cache invalidation, CU- and
+  // XCD-wide) makes every other workgroup's partials visible to all its waves.
+  dwait();
+  __syncthreads();
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int last = atomicAdd(&cnt[unit], 1) == wgs - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  const float* pu = part3 + (int64_t)unit * wgs * 2 * G * PW;
+  float* s_wgt = (float*)vt[0];  // [wgs][2][G] weights 2^(m - M) / L of the workgroup partials
+  // statistics of the (branch, head) pairs: 16 lanes a pair, one load round for <= 16 partials
+  for (int pr0 = 0; pr0 < 2 * G; pr0 += 16) {
+    const int pr = pr0 + (tid >> 4), sl = tid & 15;
+    float m = -INFINITY, ls = 0.f;
+    if (pr < 2 * G)
+      for (int s = sl; s < wgs; s += 16) {
+        const float* ph = pu + (s * 2 * G + pr) * PW;
+        const float l1 = ph[1], m1 = ph[0];
+        if (l1 > 0.f) {
+          const float M1 = fmaxf(m, m1);
+          ls = ls * fexp2(m - M1) + l1 * fexp2(m1 - M1);
+          m = M1;
+        }
+      }
+    float M = m;
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    float L = m > -INFINITY ? ls * fexp2(m - M) : 0.f;
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+    if (pr < 2 * G)
+      for (int s = sl; s < wgs; s += 16) {
+        const float* ph = pu + (s * 2 * G + pr) * PW;
+        s_wgt[s * 2 * G + pr] = (ph[1] > 0.f && L > 0.f) ? fexp2(ph[0] - M) / L : 0.f;
+      }
+  }
+  __syncthreads();
+  if (!text && lse && tid < G)
+    lse[b * dm.Hq + g * G + tid] = s_L[tid] > 0.f ? (s_M[tid] + flog2(s_L[tid])) * LN2_F : -INFINITY;
+  for (int i = tid; i < G * HD / 4; i += blockDim.x) {
+    const int hh = (4 * i) / HD, e = (4 * i) % HD;
+    float ob[2][4];
+#pragma unroll
+    for (int br = 0; br < 2; ++br) {
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+      for (int s = 0; s < wgs; ++s) {
+        const float f = s_wgt[s * 2 * G + br * G + hh];
+        const float4 x = *(const float4*)(pu + (s * 2 * G + br * G + hh) * PW + PO + e);
+        if (f != 0.f) {  // the O of empty partials is never written
+          o.x += f * x.x;
+          o.y += f * x.y;
+          o.z += f * x.z;
+          o.w += f * x.w;
+        }
+      }
+      ob[br][0] = o.x;
+      ob[br][1] = o.y;
+      ob[br][2] = o.z;
+      ob[br][3] = o.w;
     }
     const int hq = g * G + hh;
     const int64_t off = (b * dm.Hq + hq) * (int64_t)HD + e;
-    if (o_cmp) o_cmp[off] = (bf16)oc;
-    if (o_slc) o_slc[off] = (bf16)ob[0];
-    if (o_swa) o_swa[off] = (bf16)ob[1];
-    if (out) {
-      const float* gg = gates + (b * dm.Hq + hq) * 3;
-      out[off] = (bf16)(gg[0] * oc + gg[1] * ob[0] + gg[2] * ob[1]);
+    if (text) {  // dense attention, ungated
+      bf16x4 v4;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v4[c] = (bf16)ob[0][c];
+      if (out) *(bf16x4*)(out + off) = v4;
+      continue;
     }
+    const float4 oc4 = *(const float4*)(ocmp32 + (int64_t)unit * G * HD + 4 * i);
+    const float oc[4] = {oc4.x, oc4.y, oc4.z, oc4.w};
+    const float* gg = gates + (b * dm.Hq + hq) * 3;
+    bf16x4 vc, vs, vw, vo;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      vc[c] = (bf16)oc[c];
+      vs[c] = (bf16)ob[0][c];
+      vw[c] = (bf16)ob[1][c];
+      vo[c] = (bf16)(gg[0] * oc[c] + gg[1] * ob[0][c] + gg[2] * ob[1][c]);
+    }
+    if (o_cmp) *(bf16x4*)(o_cmp + off) = vc;
+    if (o_slc) *(bf16x4*)(o_slc + off) = vs;
+    if (o_swa) *(bf16x4*)(o_swa + off) = vw;
+    if (out) *(bf16x4*)(out + off) = vo;
   }
+  if (tid == 0) cnt[unit] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -593,14 +612,18 @@ static size_t drup(size_t x) { return (x + 255) & ~(size_t)255; }
 static int dsplits(const Dims& dm) { return (int)((dm.Nc + DCH - 1) / DCH); }
 static int dslots(const Dims& dm) { return dm.n + (dm.w + SB - 1) / SB + 1; }
 
-bool decode_supported(const Dims& dm) { return dm.Tq == 1 && dm.Nc > 0; }
+// The selection kernel keeps the importance of all Ns blocks in LDS.
+bool decode_supported(const Dims& dm) { return dm.Tq == 1 && dm.Nc > 0 && dm.Ns <= 16384; }
 
 size_t decode_workspace(const Dims& dm) {
   const size_t units = (size_t)dm.B * dm.Hkv;
-  return drup(units * dsplits(dm) * dm.G * PSTRIDE * 4) + drup(units * dslots(dm) * 2 * dm.G * (HD + 2) * 4);
+  const size_t wgs = (dslots(dm) + 3) / 4;
+  return drup(units * dsplits(dm) * dm.G * PSTRIDE * 4) + drup(units * wgs * 2 * dm.G * (HD + 4) * 4) +
+         drup(units * dm.G * HD * 4) + drup(units * 4);
 }
 
-// kh/vh: compressed cache (bf16), kl/vl: low parts or NULL.  Text rows are not handled here.
+// kh/vh: compressed cache (bf16), kl/vl: low parts or NULL.  Text rows take dense causal
+// attention in the selection kernel (their compression split is skipped).
 hipError_t launch_decode_fast(const Dims& dm, const void* q, const void* kh, const void* kl, const void* vh,
                               const void* vl, const void* k, const void* v, const uint8_t* vid, const float* gates,
                               void* out, void* o_cmp, void* o_slc, void* o_swa, int32_t* idx, float* lse,
@@ -610,24 +633,27 @@ hipError_t launch_decode_fast(const Dims& dm, const void* q, const void* kh, con
   char* p = (char*)ws;
   float* part = (float*)p;
   p += drup((size_t)units * ns * dm.G * PSTRIDE * 4);
+  const int wgs = (nslot + 3) / 4;
   float* part3 = (float*)p;
+  p += drup((size_t)units * wgs * 2 * dm.G * (HD + 4) * 4);
+  float* ocmp32 = (float*)p;
+  p += drup((size_t)units * dm.G * HD * 4);
+  int* cnt = (int*)p;
   if (kl)
     dcmp_split_kernel<true><<<dim3(units * ns), dim3(256), 0, s>>>((const bf16*)q, (const bf16*)kh, (const bf16*)kl,
-                                                                   (const bf16*)vh, (const bf16*)vl, vid, part, dm, ns);
+                                                                   (const bf16*)vh, (const bf16*)vl, vid, part, cnt,
+                                                                   dm, ns);
   else
     dcmp_split_kernel<false><<<dim3(units * ns), dim3(256), 0, s>>>((const bf16*)q, (const bf16*)kh, nullptr,
-                                                                    (const bf16*)vh, nullptr, vid, part, dm, ns);
+                                                                    (const bf16*)vh, nullptr, vid, part, cnt, dm, ns);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dcmp_merge_kernel<<<dim3(units), dim3(1024), (size_t)(dm.Ns + dm.G * ns) * 4, s>>>(part, vid, imp, idx, dm, ns);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (mark) mark(s);
-  const int wgs = (nslot + 3) / 4;
-  dsparse_blocks_kernel<<<dim3(units * wgs), dim3(256), 0, s>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, idx,
-                                                                vid, part3, dm, nslot);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t shm4 = (size_t)(nslot * 4 * dm.G + dm.G * ns) * 4;
-  dsparse_merge_kernel<<<dim3(units), dim3(1024), shm4, s>>>(part, part3, vid, gates, (bf16*)out, (bf16*)o_cmp,
-                                                             (bf16*)o_slc, (bf16*)o_swa, lse, dm, ns, nslot);
+  const size_t shm = (size_t)(dm.Ns + dm.G * ns) * 4;
+  e = hipFuncSetAttribute((const void*)dsel_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  dsel_kernel<<<dim3(units * wgs), dim3(256), shm, s>>>(
+      (const bf16*)q, (const bf16*)k, (const bf16*)v, part, vid, gates, (bf16*)out, (bf16*)o_cmp, (bf16*)o_slc,
+      (bf16*)o_swa, lse, idx, imp, part3, ocmp32, cnt, dm, ns, nslot, wgs);
   return hipGetLastError();
 }

@@ -87,7 +87,7 @@ __device__ inline void wave_select(const float* __restrict__ x, int lo, int hi, 
           const int y = __shfl_up(incl, o, 64);
           if (lane >= o) incl += y;
         }
-        const int total = __shfl(incl, 63, 64);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
         if (total <= 64) {
           int pos = incl - cnt;
 #pragma unroll
@@ -113,7 +113,7 @@ __device__ inline void wave_select(const float* __restrict__ x, int lo, int hi, 
             int best = 0x7fffffff, bl = 0;
             for (uint64_t m = eq; m; m &= m - 1) {
               const int ln = (int)__builtin_ctzll(m);
-              const int jl = __shfl(cj, ln, 64);
+              const int jl = __builtin_amdgcn_readlane(cj, ln);
               if (jl < best) {
                 best = jl;
                 bl = ln;
@@ -168,7 +168,7 @@ __device__ inline void wave_select(const float* __restrict__ x, int lo, int hi, 
     }
   } else if (chosen) {
     int pos = lo;
-    for (uint64_t m = chosen; m; m &= m - 1) pos += __shfl(cj, (int)__builtin_ctzll(m), 64) < cj ? 1 : 0;
+    for (uint64_t m = chosen; m; m &= m - 1) pos += __builtin_amdgcn_readlane(cj, (int)__builtin_ctzll(m)) < cj ? 1 : 0;
     if ((chosen >> lane) & 1) out[pos] = cj;
   }
   if (lane < lo) out[lane] = lane;
