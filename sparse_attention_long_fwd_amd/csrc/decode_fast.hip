@@ -290,30 +290,35 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
   if (!text) {
   dsplit_stats(pc, G, nsplit, s_fac, s_M, s_L);
   __syncthreads();
-  // 4 blocks a thread per pass, every load of a pass issued before the sums
+  // 4 blocks a thread per pass; loads clamped to valid addresses and unconditional, so a pass
+  // has all of them in flight at once (invalid terms get weight 0)
   for (int j0 = 0; j0 <= jt; j0 += 4 * blockDim.x) {
-    float a[4][8], c[4][8];
+    float a[4][8], c[4][8], fa[4][8], fc[4][8];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int j = j0 + u * blockDim.x + tid;
       const int s = j / DBLK, jb = j % DBLK;
+      const int sa = s < nsplit ? s : nsplit - 1, scar = s > 0 ? s - 1 : 0;
+      const bool va = j <= jt && s < nsplit, vc = j <= jt && jb == 0 && s > 0;
 #pragma unroll
       for (int hh = 0; hh < 8; ++hh) {
-        a[u][hh] = (j <= jt && hh < G && s < nsplit) ? pc[(s * G + hh) * PSTRIDE + 2 + HD + jb] : 0.f;
-        c[u][hh] = (j <= jt && hh < G && jb == 0 && s > 0) ? pc[((s - 1) * G + hh) * PSTRIDE + 2 + HD + DBLK] : 0.f;
+        const int hc = hh < G ? hh : G - 1;
+        a[u][hh] = pc[(sa * G + hc) * PSTRIDE + 2 + HD + jb];
+        c[u][hh] = pc[(scar * G + hc) * PSTRIDE + 2 + HD + DBLK];
+        fa[u][hh] = (va && hh < G) ? s_fac[hc * nsplit + sa] : 0.f;
+        fc[u][hh] = (vc && hh < G) ? s_fac[hc * nsplit + scar] : 0.f;
       }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int j = j0 + u * blockDim.x + tid;
-      if (j > jt) continue;
-      const int s = j / DBLK, jb = j % DBLK;
       float val = 0.f;
 #pragma unroll
       for (int hh = 0; hh < 8; ++hh) {
-        if (hh < G && s < nsplit) val += s_fac[hh * nsplit + s] * a[u][hh];
-        if (hh < G && jb == 0 && s > 0) val += s_fac[hh * nsplit + s - 1] * c[u][hh];
+        val += fa[u][hh] * a[u][hh];
+        val += fc[u][hh] * c[u][hh];
       }
+      if (j > jt) continue;
       s_imp[j] = val;
       if (imp_out && sg == 0) imp_out[(b * dm.Hkv + g) * dm.Ns + j] = val;
     }
@@ -324,6 +329,16 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
     const int kk = tk_bounds(t, dm.ls, dm.Ns, dm.n, dm.n_init, dm.n_local, &lo, &hi, &nj);
     wave_select(s_imp, lo, hi, nj, kk, dm.n, &s_tk, s_idx, l);
     if (sg == 0 && l < dm.n) idx[(b * dm.Hkv + g) * dm.n + l] = s_idx[l];
+  } else {
+    // meanwhile the other waves merge this workgroup's slice of the compression output
+    const int per = (G * HD + wgs - 1) / wgs;
+    for (int i = sg * per + tid - 64; i < (sg + 1) * per && i < G * HD; i += blockDim.x - 64) {
+      const int hh = i / HD, e = i % HD;
+      float oc = 0.f;
+#pragma unroll 16
+      for (int s = 0; s < nsplit; ++s) oc += s_fac[hh * nsplit + s] * pc[(s * G + hh) * PSTRIDE + 2 + e];
+      ocmp32[(int64_t)unit * G * HD + i] = oc;
+    }
   }
   __syncthreads();
   }
@@ -499,16 +514,6 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
     if (e == 0) {
       pw[bh * PW] = M;
       pw[bh * PW + 1] = L;
-    }
-  }
-  if (!text) {
-    const int per = (G * HD + wgs - 1) / wgs;
-    for (int i = sg * per + tid; i < (sg + 1) * per && i < G * HD; i += blockDim.x) {
-      const int hh = i / HD, e = i % HD;
-      float oc = 0.f;
-#pragma unroll 16
-      for (int s = 0; s < nsplit; ++s) oc += s_fac[hh * nsplit + s] * pc[(s * G + hh) * PSTRIDE + 2 + e];
-      ocmp32[(int64_t)unit * G * HD + i] = oc;
     }
   }
 

@@ -71,10 +71,14 @@ __device__ inline void wave_select(const float* __restrict__ x, int lo, int hi, 
         float cv[TK_REG];
         float lm = -INFINITY;
 #pragma unroll
-        for (int c = 0; c < TK_REG; ++c) {
+        for (int c = 0; c < TK_REG; ++c) {  // unconditional (clamped) loads, all in flight at once
           const int j = lo + lane + 64 * c;
-          cv[c] = j < hi ? x[j] : -INFINITY;
-          if (j < hi) lm = fmaxf(lm, cv[c]);
+          cv[c] = x[j < hi ? j : hi - 1];
+        }
+#pragma unroll
+        for (int c = 0; c < TK_REG; ++c) {
+          if (lo + lane + 64 * c >= hi) cv[c] = -INFINITY;
+          else lm = fmaxf(lm, cv[c]);
         }
         // th: the kk-th largest lane maximum (lanes without a candidate take no part)
         const uint32_t thk = tk_kth_key(tk_key(lm), lane < nc, kk);
