@@ -1,0 +1,413 @@
+// Selection branch of the video rows, block-major, and the gated combine (gfx950).
+//
+// What it computes (top168.com digest of VideoNSA, section 一; csdn page
+// "VideoNSA：重新定义视频理解的稀疏注意力机制", section 2.2): for a video row t and
+// KV group g, the heads of g attend over the tokens u <= t of the blocks chosen
+// for (t, g); the output of the layer is g_cmp o_cmp + g_slc o_slc + g_swa o_swa
+// per head (section 3.1 of the csdn page: three gate values per head).
+//
+// The chosen blocks of different rows barely overlap (beyond the forced ones),
+// so a row-major kernel gathers 16 whole blocks (32 KB of K and V) per (row,
+// group).  Here the work is turned around: each chosen block is loaded once
+// per chunk of 32 rows that chose it, and each (row, slot, head) leaves a
+// partial softmax (max, sum, unnormalised value sum in fp16) that a merge
+// kernel combines.  Per (row, slot) pair that moves the row's query (1.8 KB for
+// 7 heads) and the partial (1.8 KB) instead of 32 KB of keys and values.
+//
+//  1. slc_count: per (batch, group, 2048-row range) an LDS histogram of the
+//     chosen blocks, added to the global per-block counts.
+//  2. slc_scan: per (batch, group) offsets of each block's pair list and of
+//     its chunks of 32 pairs; the chunk -> block map the attention grid uses.
+//  3. slc_scatter: the same histogram again, one global reservation per
+//     (workgroup, block), then each pair (row, slot) lands in its block's list.
+//  4. slc_chunk: per chunk, the block's K / V staged in LDS (swizzled rows), a
+//     wave per head: S^T = K Q^T (32x32x16 MFMA, the 32 rows on N), the causal
+//     mask on the row's own block, a local softmax, O^T = V^T P^T with
+//     transposing LDS reads; the partial goes to (row, group, slot, head).
+//  5. slc_merge: a wave per (row, group) merges the slots' partials per head
+//     and writes o_slc and the gated output.
+// The order of a block's pair list depends on atomics, but every partial has a
+// fixed home and the merge runs over the slots in order: results are
+// deterministic.
+#include "fast_common.hpp"
+
+namespace {
+constexpr int HD = 128;
+constexpr int SB = 64;       // tokens per selection block
+constexpr int RC = 32;       // rows per chunk
+constexpr int RROWS = 2048;  // rows per bucketing workgroup
+constexpr int REC = 8 + 2 * HD;  // bytes of one partial: max (log2 units), sum, O[128] fp16
+}  // namespace
+
+// Bucketing layout in the workspace (per bg = b * Hkv + g):
+//  count[bg][Ns], off[bg][Ns] (pair list of block j starts at pairs + bg*Tq*n + off),
+//  cfirst[bg][Ns] (first chunk of block j), cursor[bg][Ns], chunk_blk[bg][cap_c],
+//  pairs[bg][Tq * n] = (row << 5) | slot.
+struct SlcBuckets {
+  int* count;
+  int* off;
+  int* cfirst;
+  int* cursor;
+  int* chunk_blk;
+  int* pairs;
+  int cap_c;
+};
+
+static inline int slc_cap_chunks(const Dims& dm) { return (int)((dm.Tq * dm.n + RC - 1) / RC + dm.Ns); }
+
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) slc_zero_kernel(int* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+__global__ void __launch_bounds__(256) slc_count_kernel(const int32_t* __restrict__ idx,
+                                                        const uint8_t* __restrict__ vid, SlcBuckets bk, Dims dm,
+                                                        int wgs_per_bg) {
+  extern __shared__ int hist[];  // [Ns]
+  const int bg = blockIdx.x / wgs_per_bg, part = blockIdx.x % wgs_per_bg;
+  const int64_t b = bg / dm.Hkv;
+  const int g = bg % dm.Hkv;
+  for (int j = threadIdx.x; j < dm.Ns; j += blockDim.x) hist[j] = 0;
+  __syncthreads();
+  const int64_t r0 = (int64_t)part * RROWS;
+  const int64_t r1 = r0 + RROWS < dm.Tq ? r0 + RROWS : dm.Tq;
+  for (int64_t e = r0 * dm.n + threadIdx.x; e < r1 * dm.n; e += blockDim.x) {
+    const int64_t r = e / dm.n;
+    const int s = (int)(e % dm.n);
+    if (vid && !vid[b * dm.Tq + r]) continue;
+    const int j = idx[((b * dm.Tq + r) * dm.Hkv + g) * dm.n + s];
+    if (j >= 0) atomicAdd(&hist[j], 1);
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < dm.Ns; j += blockDim.x)
+    if (hist[j]) atomicAdd(&bk.count[(int64_t)bg * dm.Ns + j], hist[j]);
+}
+
+// Exclusive scan of x[0..n) in place with 1024 threads; returns the total.
+__device__ int block_excl_scan(int* x, int n, int* s_w) {
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wv = tid >> 6;
+  const int per = (n + nt - 1) / nt;
+  const int a = tid * per, e = a + per < n ? a + per : n;
+  int sum = 0;
+  for (int i = a; i < e; ++i) sum += x[i];
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) s_w[wv] = incl;
+  __syncthreads();
+  int wbase = 0, total = 0;
+  for (int i = 0; i < (nt >> 6); ++i) {
+    if (i < wv) wbase += s_w[i];
+    total += s_w[i];
+  }
+  int run = wbase + incl - sum;
+  for (int i = a; i < e; ++i) {
+    const int v = x[i];
+    x[i] = run;
+    run += v;
+  }
+  __syncthreads();
+  return total;
+}
+
+__global__ void __launch_bounds__(1024) slc_scan_kernel(SlcBuckets bk, Dims dm) {
+  extern __shared__ int sm[];  // [2][Ns]
+  __shared__ int s_w[16];
+  int* s_off = sm;
+  int* s_cf = sm + dm.Ns;
+  const int bg = blockIdx.x;
+  const int64_t base = (int64_t)bg * dm.Ns;
+  for (int j = threadIdx.x; j < dm.Ns; j += blockDim.x) {
+    const int c = bk.count[base + j];
+    s_off[j] = c;
+    s_cf[j] = (c + RC - 1) / RC;
+  }
+  __syncthreads();
+  block_excl_scan(s_off, (int)dm.Ns, s_w);
+  const int nch = block_excl_scan(s_cf, (int)dm.Ns, s_w);
+  int* cb = bk.chunk_blk + (int64_t)bg * bk.cap_c;
+  for (int j = threadIdx.x; j < dm.Ns; j += blockDim.x) {
+    bk.off[base + j] = s_off[j];
+    bk.cfirst[base + j] = s_cf[j];
+    bk.cursor[base + j] = 0;
+    const int c0 = s_cf[j], c1 = j + 1 < dm.Ns ? s_cf[j + 1] : nch;
+    for (int c = c0; c < c1; ++c) cb[c] = j;
+  }
+  for (int c = nch + threadIdx.x; c < bk.cap_c; c += blockDim.x) cb[c] = -1;
+}
+
+__global__ void __launch_bounds__(256) slc_scatter_kernel(const int32_t* __restrict__ idx,
+                                                          const uint8_t* __restrict__ vid, SlcBuckets bk, Dims dm,
+                                                          int wgs_per_bg) {
+  extern __shared__ int sm[];  // hist[Ns], base[Ns]
+  int* hist = sm;
+  int* pbase = sm + dm.Ns;
+  const int bg = blockIdx.x / wgs_per_bg, part = blockIdx.x % wgs_per_bg;
+  const int64_t b = bg / dm.Hkv;
+  const int g = bg % dm.Hkv;
+  for (int j = threadIdx.x; j < dm.Ns; j += blockDim.x) hist[j] = 0;
+  __syncthreads();
+  const int64_t r0 = (int64_t)part * RROWS;
+  const int64_t r1 = r0 + RROWS < dm.Tq ? r0 + RROWS : dm.Tq;
+  for (int64_t e = r0 * dm.n + threadIdx.x; e < r1 * dm.n; e += blockDim.x) {
+    const int64_t r = e / dm.n;
+    if (vid && !vid[b * dm.Tq + r]) continue;
+    const int j = idx[((b * dm.Tq + r) * dm.Hkv + g) * dm.n + e % dm.n];
+    if (j >= 0) atomicAdd(&hist[j], 1);
+  }
+  __syncthreads();
+  const int64_t base = (int64_t)bg * dm.Ns;
+  for (int j = threadIdx.x; j < dm.Ns; j += blockDim.x) {
+    const int c = hist[j];
+    pbase[j] = c ? bk.off[base + j] + atomicAdd(&bk.cursor[base + j], c) : 0;
+    hist[j] = 0;
+  }
+  __syncthreads();
+  int* pl = bk.pairs + (int64_t)bg * dm.Tq * dm.n;
+  for (int64_t e = r0 * dm.n + threadIdx.x; e < r1 * dm.n; e += blockDim.x) {
+    const int64_t r = e / dm.n;
+    const int s = (int)(e % dm.n);
+    if (vid && !vid[b * dm.Tq + r]) continue;
+    const int j = idx[((b * dm.Tq + r) * dm.Hkv + g) * dm.n + s];
+    if (j >= 0) pl[pbase[j] + atomicAdd(&hist[j], 1)] = (int)(r << 5) | s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One workgroup per chunk of up to 32 (row, slot) pairs of one block; wave w = head g*G + w.
+__global__ void __launch_bounds__(512) slc_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                        const bf16* __restrict__ v, SlcBuckets bk,
+                                                        unsigned char* __restrict__ part, Dims dm) {
+  __shared__ __attribute__((aligned(16))) bf16 kt[SB * HD];
+  __shared__ __attribute__((aligned(16))) bf16 vt[SB * HD];
+  __shared__ int s_pair[RC];
+  const int G = dm.G;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, n = l & 31;
+  const int bg = blockIdx.x / bk.cap_c, cc = blockIdx.x % bk.cap_c;
+  const int j = bk.chunk_blk[(int64_t)bg * bk.cap_c + cc];
+  if (j < 0) return;
+  const int64_t b = bg / dm.Hkv;
+  const int g = bg % dm.Hkv;
+  const int64_t bj = (int64_t)bg * dm.Ns + j;
+  const int kc = cc - bk.cfirst[bj];        // chunk within the block
+  const int cnt = bk.count[bj] - kc * RC;    // pairs in this chunk (may exceed RC)
+  const int* pl = bk.pairs + (int64_t)bg * dm.Tq * dm.n + bk.off[bj] + kc * RC;
+  if (tid < RC) s_pair[tid] = tid < cnt ? pl[tid] : -1;
+  const int64_t stride = (int64_t)dm.Hkv * HD;
+  const int64_t kvb = (b * dm.T * dm.Hkv + g) * (int64_t)HD;
+  stage_tile64(kt, k + kvb, stride, (int64_t)j * SB, dm.T, w, G, l);
+  stage_tile64(vt, v + kvb, stride, (int64_t)j * SB, dm.T, w, G, l);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  const int pr = s_pair[n];
+  const bool valid = pr >= 0;
+  const int64_t row = valid ? (pr >> 5) : 0;
+  const int slot = pr & 31;
+  const int h = g * G + w;
+  const int64_t t = dm.q0 + row;
+  bf16x8 qf[8];
+  {
+    const bf16* qrow = q + ((b * dm.Tq + row) * dm.Hq + h) * (int64_t)HD + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = valid ? *(const bf16x8*)(qrow + 16 * ks) : zero8();
+  }
+  // S^T: keys on M (two 32-key blocks), the chunk's rows on N
+  f32x16 s[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    s[kb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) s[kb] = mfma32(lds_read8(kt + swz128(kb * 32 + n, 2 * ks + hl)), qf[ks], s[kb]);
+  }
+  const float c2 = dm.scale * LOG2E_F;
+  const int64_t u0 = (int64_t)j * SB;
+  const bool need_mask = u0 + SB - 1 > t || u0 + SB > dm.T;  // the row's own block, or past the end
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      if (need_mask) {
+        const int64_t u = u0 + kb * 32 + 8 * (jj >> 2) + 4 * hl + (jj & 3);
+        if (u > t || u >= dm.T) s[kb][jj] = -INFINITY;
+      }
+      mx = fmaxf(mx, s[kb][jj]);
+    }
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(mx, __uint_as_float(hl ? r[0] : r[1]));
+  }
+  const float off = -mx * c2;
+  float ls = 0.f;
+  f32x16 oacc[4] = {};
+  const int g16 = l >> 4, i16 = l & 15;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    float p[16];
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      p[jj] = fexp2(fmaf(s[kb][jj], c2, off));
+      ls += p[jj];
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = (bf16)p[8 * st + e];
+      const int vr = kb * 32 + 16 * st + 4 * (g16 >> 1) + (i16 >> 2);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int col = 32 * db + (g16 & 1) * 16 + 4 * (i16 & 3);
+        oacc[db] = mfma32(cat(lds_read_tr(vt + swz128(vr, col >> 3) + (col & 7)),
+                              lds_read_tr(vt + swz128(vr + 8, col >> 3) + (col & 7))),
+                          pb, oacc[db]);
+      }
+    }
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ls), __float_as_uint(ls), false, false);
+    ls += __uint_as_float(hl ? r[0] : r[1]);
+  }
+  if (!valid) return;
+  unsigned char* rec = part + ((((b * dm.Tq + row) * dm.Hkv + g) * dm.n + slot) * G + w) * (int64_t)REC;
+  if (hl == 0) *(float2*)rec = make_float2(mx * c2, ls);
+  _Float16* o16 = (_Float16*)(rec + 8);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+      h4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (_Float16)oacc[db][4 * q4 + e];
+      *(h4*)(o16 + 32 * db + 8 * q4 + 4 * hl) = x;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One wave per (video row, group): merge the slots per head, gated combine.  Lane l owns
+// dims 2l, 2l+1.
+template <bool OCMP_F32>
+__global__ void __launch_bounds__(256) slc_merge_kernel(const unsigned char* __restrict__ part,
+                                                        const int32_t* __restrict__ idx,
+                                                        const uint8_t* __restrict__ vid, const void* __restrict__ ocmp,
+                                                        const float* __restrict__ swa32,
+                                                        const float* __restrict__ gates, bf16* __restrict__ out,
+                                                        bf16* __restrict__ o_slc, Dims dm) {
+  const int l = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= dm.B * dm.Tq * dm.Hkv) return;
+  const int g = (int)(item % dm.Hkv);
+  const int64_t br = item / dm.Hkv;  // b * Tq + r
+  if (vid && !vid[br]) return;
+  const int G = dm.G;
+  const int32_t* sel = idx + item * dm.n;
+  const bool lv = l < dm.n && sel[l < dm.n ? l : 0] >= 0;
+  const unsigned char* recs = part + item * dm.n * G * (int64_t)REC;
+  for (int w = 0; w < G; ++w) {
+    float m = -INFINITY, sm = 0.f;
+    if (lv) {
+      const float2 ml = *(const float2*)(recs + ((int64_t)l * G + w) * REC);
+      m = ml.x;
+      sm = ml.y;
+    }
+    float M = m;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float f = lv ? fexp2(m - M) : 0.f;
+    float L = f * sm;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+    const float wgt = L > 0.f ? f / L : 0.f;
+    float o0 = 0.f, o1 = 0.f;
+    for (int s = 0; s < dm.n; ++s) {
+      const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), s));
+      if (ws == 0.f) continue;  // uniform: unused slot
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      const h2 x = *(const h2*)(recs + ((int64_t)s * G + w) * REC + 8 + 4 * l);
+      o0 = fmaf(ws, (float)x[0], o0);
+      o1 = fmaf(ws, (float)x[1], o1);
+    }
+    const int hq = g * G + w;
+    const int64_t off = (br * dm.Hq + hq) * (int64_t)HD + 2 * l;
+    if (o_slc) {
+      o_slc[off] = (bf16)o0;
+      o_slc[off + 1] = (bf16)o1;
+    }
+    if (out) {
+      float c0, c1;
+      if constexpr (OCMP_F32) {
+        const float2 c = *(const float2*)((const float*)ocmp + off);
+        c0 = c.x;
+        c1 = c.y;
+      } else {
+        c0 = (float)((const bf16*)ocmp)[off];
+        c1 = (float)((const bf16*)ocmp)[off + 1];
+      }
+      const float2 sw = *(const float2*)(swa32 + off);
+      const float* gg = gates + (br * dm.Hq + hq) * 3;
+      const float g0 = gg[0], g1 = gg[1], g2 = gg[2];
+      out[off] = (bf16)(g0 * c0 + g1 * o0 + g2 * sw.x);
+      out[off + 1] = (bf16)(g0 * c1 + g1 * o1 + g2 * sw.y);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+static size_t srup(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t slc_block_workspace(const Dims& dm) {
+  const size_t bgs = (size_t)dm.B * dm.Hkv;
+  return 4 * srup(bgs * dm.Ns * 4) + srup(bgs * slc_cap_chunks(dm) * 4) + srup(bgs * dm.Tq * dm.n * 4) +
+         srup((size_t)dm.B * dm.Tq * dm.Hkv * dm.n * dm.G * REC);
+}
+
+hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
+                            const uint8_t* vid, const void* ocmp, bool ocmp_f32, const float* swa32,
+                            const float* gates, void* out, void* o_slc, void* ws, hipStream_t s) {
+  if (dm.B <= 0 || dm.Tq <= 0) return hipSuccess;
+  const int bgs = (int)(dm.B * dm.Hkv);
+  char* p = (char*)ws;
+  SlcBuckets bk;
+  const size_t nb = srup((size_t)bgs * dm.Ns * 4);
+  bk.count = (int*)p;
+  bk.off = (int*)(p + nb);
+  bk.cfirst = (int*)(p + 2 * nb);
+  bk.cursor = (int*)(p + 3 * nb);
+  p += 4 * nb;
+  bk.cap_c = slc_cap_chunks(dm);
+  bk.chunk_blk = (int*)p;
+  p += srup((size_t)bgs * bk.cap_c * 4);
+  bk.pairs = (int*)p;
+  p += srup((size_t)bgs * dm.Tq * dm.n * 4);
+  unsigned char* part = (unsigned char*)p;
+  const int wpb = (int)((dm.Tq + RROWS - 1) / RROWS);
+  const size_t hist = (size_t)dm.Ns * 4;
+  hipError_t e;
+  // counts start at zero (a kernel, not a memset: callers may capture the launch in a graph)
+  const int64_t ncount = (int64_t)bgs * dm.Ns;
+  slc_zero_kernel<<<dim3((unsigned)((ncount + 255) / 256)), dim3(256), 0, s>>>(bk.count, ncount);
+  for (const void* fn : {(const void*)slc_count_kernel, (const void*)slc_scatter_kernel, (const void*)slc_scan_kernel}) {
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * hist));
+    if (e != hipSuccess) return e;
+  }
+  slc_count_kernel<<<dim3(bgs * wpb), dim3(256), hist, s>>>(idx, vid, bk, dm, wpb);
+  slc_scan_kernel<<<dim3(bgs), dim3(1024), 2 * hist, s>>>(bk, dm);
+  slc_scatter_kernel<<<dim3(bgs * wpb), dim3(256), 2 * hist, s>>>(idx, vid, bk, dm, wpb);
+  slc_chunk_kernel<<<dim3((unsigned)bgs * bk.cap_c), dim3(dm.G * 64), 0, s>>>((const bf16*)q, (const bf16*)k,
+                                                                             (const bf16*)v, bk, part, dm);
+  const int64_t items = dm.B * dm.Tq * dm.Hkv;
+  const dim3 mg((unsigned)((items + 3) / 4));
+  if (ocmp_f32)
+    slc_merge_kernel<true><<<mg, dim3(256), 0, s>>>(part, idx, vid, ocmp, swa32, gates, (bf16*)out, (bf16*)o_slc,
+                                                    dm);
+  else
+    slc_merge_kernel<false><<<mg, dim3(256), 0, s>>>(part, idx, vid, ocmp, swa32, gates, (bf16*)out, (bf16*)o_slc,
+                                                     dm);
+  return hipGetLastError();
+}
