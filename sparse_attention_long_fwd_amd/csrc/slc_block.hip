@@ -184,7 +184,6 @@ __global__ void __launch_bounds__(512) slc_chunk_kernel(const bf16* __restrict__
                                                         unsigned char* __restrict__ part, Dims dm) {
   __shared__ __attribute__((aligned(16))) bf16 kt[SB * HD];
   __shared__ __attribute__((aligned(16))) bf16 vt[SB * HD];
-  __shared__ int s_pair[RC];
   const int G = dm.G;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, n = l & 31;
   const int bg = blockIdx.x / bk.cap_c, cc = blockIdx.x % bk.cap_c;
@@ -196,15 +195,12 @@ __global__ void __launch_bounds__(512) slc_chunk_kernel(const bf16* __restrict__
   const int kc = cc - bk.cfirst[bj];        // chunk within the block
   const int cnt = bk.count[bj] - kc * RC;    // pairs in this chunk (may exceed RC)
   const int* pl = bk.pairs + (int64_t)bg * dm.Tq * dm.n + bk.off[bj] + kc * RC;
-  if (tid < RC) s_pair[tid] = tid < cnt ? pl[tid] : -1;
   const int64_t stride = (int64_t)dm.Hkv * HD;
   const int64_t kvb = (b * dm.T * dm.Hkv + g) * (int64_t)HD;
   stage_tile64(kt, k + kvb, stride, (int64_t)j * SB, dm.T, w, G, l);
   stage_tile64(vt, v + kvb, stride, (int64_t)j * SB, dm.T, w, G, l);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  const int pr = s_pair[n];
+  // this lane's pair (row n of the chunk) and its query, loaded while the tile streams in
+  const int pr = n < cnt ? pl[n] : -1;
   const bool valid = pr >= 0;
   const int64_t row = valid ? (pr >> 5) : 0;
   const int slot = pr & 31;
@@ -214,8 +210,13 @@ __global__ void __launch_bounds__(512) slc_chunk_kernel(const bf16* __restrict__
   {
     const bf16* qrow = q + ((b * dm.Tq + row) * dm.Hq + h) * (int64_t)HD + 8 * hl;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = valid ? *(const bf16x8*)(qrow + 16 * ks) : zero8();
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(qrow + 16 * ks);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    if (!valid) qf[ks] = zero8();
   // S^T: keys on M (two 32-key blocks), the chunk's rows on N
   f32x16 s[2];
 #pragma unroll
@@ -324,14 +325,22 @@ __global__ void __launch_bounds__(256) slc_merge_kernel(const unsigned char* __r
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
     const float wgt = L > 0.f ? f / L : 0.f;
+    // every slot's values loaded at once (unused slots hold stale data: weight 0 selects them out)
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     float o0 = 0.f, o1 = 0.f;
-    for (int s = 0; s < dm.n; ++s) {
-      const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), s));
-      if (ws == 0.f) continue;  // uniform: unused slot
-      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-      const h2 x = *(const h2*)(recs + ((int64_t)s * G + w) * REC + 8 + 4 * l);
-      o0 = fmaf(ws, (float)x[0], o0);
-      o1 = fmaf(ws, (float)x[1], o1);
+    for (int s0 = 0; s0 < dm.n; s0 += 16) {
+      h2 x[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int s = s0 + u < dm.n ? s0 + u : dm.n - 1;
+        x[u] = *(const h2*)(recs + ((int64_t)s * G + w) * REC + 8 + 4 * l);
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float ws = s0 + u < dm.n ? __shfl(wgt, s0 + u, 64) : 0.f;
+        o0 += ws != 0.f ? ws * (float)x[u][0] : 0.f;
+        o1 += ws != 0.f ? ws * (float)x[u][1] : 0.f;
+      }
     }
     const int hq = g * G + w;
     const int64_t off = (br * dm.Hq + hq) * (int64_t)HD + 2 * l;
