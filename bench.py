@@ -18,12 +18,25 @@ Prints one JSON line.  Only N = 1 GPU is supported.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
+import os
 import sys
 import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# sources of each timed phase's main kernel (a counter record holds only while they are unchanged)
+PHASE_SOURCES = {
+    "cmp_attn_importance": ["sparse_attention_long_fwd_amd/csrc/cmp_fast.hip",
+                            "sparse_attention_long_fwd_amd/csrc/fast_common.hpp",
+                            "sparse_attention_long_fwd_amd/csrc/mfma.hpp",
+                            "sparse_attention_long_fwd_amd/csrc/common.hpp"],
+}
+PHASE_KERNELS = {"cmp_attn_importance": "cmp_fast_kernel"}
+COPY_PROBE_BYTES = 1 << 30
 PEAK_BF16_MFMA = 2.5e15   # FLOP/s, MI355X dense bf16
 PEAK_HBM = 8.0e12         # B/s, MI355X HBM3E
 METRIC = "NSA layer prefill tokens/s @128K (MFMA util %); decode GB/s @64K"
@@ -41,7 +54,72 @@ def parse():
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-phase timing pass")
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--cpu-sample-rows", type=int, default=0, help="oracle row sample (0: auto)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run one elementwise copy of 1 GiB (reference for counter runs)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc output directories "
+                         "(FETCH_SIZE, then WRITE_SIZE) of a --copy-probe run, and exit")
     return ap.parse_args()
+
+
+def sources_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def kernel_traffic(phase):
+    """HBM bytes per launch of the phase's kernel, from the committed counter record, or None when
+    there is none or the kernel's sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)[phase]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("sha256") != sources_sha(rec["sources"]):
+        return None
+    return rec["bytes_per_launch"]
+
+
+def record_traffic(fetch_dir, write_dir):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each phase kernel, scaled by what the same
+    counter reads for the 1 GiB elementwise copy of --copy-probe, into profiles/traffic.json."""
+    import csv
+    import glob
+
+    def read(d, counter):
+        path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        per = {}
+        for r in rows:  # sum over the counter's instances per dispatch
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        return per
+
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = read(d, counter)
+        copy = [v for (_, name), v in per.items() if "CUDAFunctor_add" in name or "AddFunctor" in name]
+        if not copy:
+            raise SystemExit("no copy-probe kernel in %s" % d)
+        factor = COPY_PROBE_BYTES / (copy[0] * 1024.0)
+        for phase, kname in PHASE_KERNELS.items():
+            vals = [v for (_, name), v in per.items() if kname in name]
+            if not vals:
+                continue
+            rec = out.setdefault(phase, {"kernel": kname, "sources": PHASE_SOURCES[phase],
+                                         "sha256": sources_sha(PHASE_SOURCES[phase])})
+            rec[counter.lower() + "_kib_per_launch"] = sum(vals) / len(vals)
+            rec[counter.lower() + "_copy_factor"] = factor
+    for rec in out.values():
+        rec["bytes_per_launch"] = (rec["fetch_size_kib_per_launch"] * rec["fetch_size_copy_factor"] +
+                                   rec["write_size_kib_per_launch"] * rec["write_size_copy_factor"]) * 1024.0
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(out))
 
 
 def log(msg):
@@ -92,8 +170,10 @@ def phase_rates(wl, ms):
             f = fl["swa"] + fl["text"]
             d.update(bound="mfma", algo_flops=f, tflops=f / (t * 1e-3) / 1e12)
         else:
-            d.update(bound="gather", algo_flops=fl["slc"], tflops=fl["slc"] / (t * 1e-3) / 1e12,
-                     gather_bytes=b_slc, gather_gbps=b_slc / (t * 1e-3) / 1e9)
+            # MFMA-bound by definition of the method; block-major, its memory traffic is about
+            # 1/5 of the row-major gather of the chosen blocks (reported for context)
+            d.update(bound="mfma", algo_flops=fl["slc"], tflops=fl["slc"] / (t * 1e-3) / 1e12,
+                     row_major_gather_bytes=b_slc)
         out[name] = d
     return out
 
@@ -265,6 +345,9 @@ def cpu_baseline(args, wl, inp):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the layer would shard by GQA group (up to 4 ways) and then by "
               "query rows, but no multi-GPU path is built; run with --gpus 1", file=sys.stderr)
@@ -274,6 +357,12 @@ def main():
 
     nsa.lib()
     torch.cuda.init()
+    if args.copy_probe:
+        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.add(src, 0.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     wl = synth.WORKLOADS[args.workload]
     if args.no_prefill:
         print(json.dumps({"decode": decode(args)}))
@@ -286,10 +375,11 @@ def main():
         dom = ker[dom_name]
         if dom["bound"] == "hbm":
             roofline = dict(kernel=dom_name, bound="hbm", achieved=dom["gbps"], peak=PEAK_HBM / 1e9, unit="GB/s",
-                            frac=dom["gbps"] * 1e9 / PEAK_HBM, traffic=None)
+                            frac=dom["gbps"] * 1e9 / PEAK_HBM, traffic=kernel_traffic(dom_name))
         else:
             roofline = dict(kernel=dom_name, bound="mfma", achieved=dom["tflops"], peak=PEAK_BF16_MFMA / 1e12,
-                            unit="TFLOP/s", frac=dom["tflops"] * 1e12 / PEAK_BF16_MFMA, traffic=None)
+                            unit="TFLOP/s", frac=dom["tflops"] * 1e12 / PEAK_BF16_MFMA,
+                            traffic=kernel_traffic(dom_name))
     cpu = None
     if not args.no_cpu_baseline:
         log("oracle timing")
