@@ -300,69 +300,87 @@ __global__ void __launch_bounds__(256) slc_merge_kernel(const unsigned char* __r
                                                         const float* __restrict__ swa32,
                                                         const float* __restrict__ gates, bf16* __restrict__ out,
                                                         bf16* __restrict__ o_slc, Dims dm) {
-  const int l = threadIdx.x & 63;
-  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ float s_wt[4][8][32];  // per wave: slot weights 2^(m - M) / L of each head
+  const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t item = (int64_t)blockIdx.x * 4 + wv;
   if (item >= dm.B * dm.Tq * dm.Hkv) return;
   const int g = (int)(item % dm.Hkv);
   const int64_t br = item / dm.Hkv;  // b * Tq + r
   if (vid && !vid[br]) return;
   const int G = dm.G;
   const int32_t* sel = idx + item * dm.n;
-  const bool lv = l < dm.n && sel[l < dm.n ? l : 0] >= 0;
   const unsigned char* recs = part + item * dm.n * G * (int64_t)REC;
-  for (int w = 0; w < G; ++w) {
-    float m = -INFINITY, sm = 0.f;
-    if (lv) {
-      const float2 ml = *(const float2*)(recs + ((int64_t)l * G + w) * REC);
-      m = ml.x;
-      sm = ml.y;
+  // weights: lane s (< n) holds slot s; one load round for the (max, sum) of every head
+  {
+    const bool lv = l < dm.n && sel[l < dm.n ? l : 0] >= 0;
+    float2 ml[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+      ml[w] = (lv && w < G) ? *(const float2*)(recs + ((int64_t)l * G + w) * REC) : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      if (w >= G) break;
+      float M = ml[w].x;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+      const float f = lv ? fexp2(ml[w].x - M) : 0.f;
+      float L = f * ml[w].y;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+      if (l < 32) s_wt[wv][w][l] = (L > 0.f && l < dm.n) ? f / L : 0.f;
     }
-    float M = m;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    const float f = lv ? fexp2(m - M) : 0.f;
-    float L = f * sm;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
-    const float wgt = L > 0.f ? f / L : 0.f;
-    // every slot's values loaded at once (unused slots hold stale data: weight 0 selects them out)
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    float o0 = 0.f, o1 = 0.f;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // values: lane l owns dims 2l, 2l+1; heads in pairs, 16 slots a pass, all loads of a pass in flight
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  for (int w0 = 0; w0 < G; w0 += 2) {
+    float o[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
     for (int s0 = 0; s0 < dm.n; s0 += 16) {
-      h2 x[16];
+      h2 x[2][16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int s = s0 + u < dm.n ? s0 + u : dm.n - 1;
-        x[u] = *(const h2*)(recs + ((int64_t)s * G + w) * REC + 8 + 4 * l);
-      }
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const float ws = s0 + u < dm.n ? __shfl(wgt, s0 + u, 64) : 0.f;
-        o0 += ws != 0.f ? ws * (float)x[u][0] : 0.f;
-        o1 += ws != 0.f ? ws * (float)x[u][1] : 0.f;
-      }
+        for (int u = 0; u < 16; ++u) {
+          const int s = s0 + u < dm.n ? s0 + u : dm.n - 1;
+          const int w = w0 + a < G ? w0 + a : G - 1;
+          x[a][u] = *(const h2*)(recs + ((int64_t)s * G + w) * REC + 8 + 4 * l);
+        }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const float ws = (s0 + u < dm.n && w0 + a < G) ? s_wt[wv][w0 + a][s0 + u] : 0.f;
+          o[a][0] += ws != 0.f ? ws * (float)x[a][u][0] : 0.f;  // unused slots: stale data, weight 0
+          o[a][1] += ws != 0.f ? ws * (float)x[a][u][1] : 0.f;
+        }
     }
-    const int hq = g * G + w;
-    const int64_t off = (br * dm.Hq + hq) * (int64_t)HD + 2 * l;
-    if (o_slc) {
-      o_slc[off] = (bf16)o0;
-      o_slc[off + 1] = (bf16)o1;
-    }
-    if (out) {
-      float c0, c1;
-      if constexpr (OCMP_F32) {
-        const float2 c = *(const float2*)((const float*)ocmp + off);
-        c0 = c.x;
-        c1 = c.y;
-      } else {
-        c0 = (float)((const bf16*)ocmp)[off];
-        c1 = (float)((const bf16*)ocmp)[off + 1];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int w = w0 + a;
+      if (w >= G) break;
+      const int hq = g * G + w;
+      const int64_t off = (br * dm.Hq + hq) * (int64_t)HD + 2 * l;
+      if (o_slc) {
+        o_slc[off] = (bf16)o[a][0];
+        o_slc[off + 1] = (bf16)o[a][1];
       }
-      const float2 sw = *(const float2*)(swa32 + off);
-      const float* gg = gates + (br * dm.Hq + hq) * 3;
-      const float g0 = gg[0], g1 = gg[1], g2 = gg[2];
-      out[off] = (bf16)(g0 * c0 + g1 * o0 + g2 * sw.x);
-      out[off + 1] = (bf16)(g0 * c1 + g1 * o1 + g2 * sw.y);
+      if (out) {
+        float c0, c1;
+        if constexpr (OCMP_F32) {
+          const float2 c = *(const float2*)((const float*)ocmp + off);
+          c0 = c.x;
+          c1 = c.y;
+        } else {
+          c0 = (float)((const bf16*)ocmp)[off];
+          c1 = (float)((const bf16*)ocmp)[off + 1];
+        }
+        const float2 sw = *(const float2*)(swa32 + off);
+        const float* gg = gates + (br * dm.Hq + hq) * 3;
+        out[off] = (bf16)(gg[0] * c0 + gg[1] * o[a][0] + gg[2] * sw.x);
+        out[off + 1] = (bf16)(gg[0] * c1 + gg[1] * o[a][1] + gg[2] * sw.y);
+      }
     }
   }
 }
