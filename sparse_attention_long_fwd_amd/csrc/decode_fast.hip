@@ -11,16 +11,16 @@
 //     scores for the G heads (16x16x32 MFMA, heads on N), a local softmax, the
 //     value sum, and the importance of the chunk's 32 selection blocks, all in
 //     the chunk's own frame (max, sum), written as a partial.
-//  2. dsel: one workgroup per (sequence, group, 4 blocks of the union of the
-//     chosen blocks and the window).  Each workgroup merges the importance
+//  2. dsel: a few workgroups per (sequence, group).  Each merges the importance
 //     partials (rescaled to the final normaliser, summed over the heads) and
-//     picks the top-n blocks itself; a wave per block scores it once and keeps
-//     a selection partial and a window partial with their own masks.  The last
-//     workgroup of a (sequence, group) to finish merges the compression,
-//     selection and window partials per head and applies the gated combine.
-//     Text rows (dense causal attention, ungated): their split workgroups exit
-//     at once; in this kernel each wave runs an online softmax over every
-//     (4 x workgroups)-th block, and the last workgroup merges those.
+//     picks the top-n blocks itself (wave 0) while its other waves already work
+//     on the window blocks, which need no selection; then every wave takes one
+//     chosen block below the window.  A block is scored once for both the
+//     selection and the window branch.  The last workgroup of a (sequence,
+//     group) to finish merges the compression, selection and window partials
+//     per head and applies the gated combine.  Text rows (dense causal
+//     attention, ungated): their split workgroups exit at once; here each wave
+//     runs an online softmax over a strided share of the blocks.
 #include "fast_common.hpp"
 #include "topk_wave.hpp"
 
@@ -232,34 +232,17 @@ __device__ __forceinline__ void dsplit_stats(const float* pu, int G, int nsplit,
   }
 }
 
-// Slot k of a unit: the k-th block of (chosen blocks below the window) ++ (window blocks).
-__device__ __forceinline__ int64_t union_block(const int32_t* sel, int n, int64_t jt, int64_t wb0, int k, bool* in_sel,
-                                               bool* in_win) {
-  int cnt_lt = 0;
-  for (int c = 0; c < n; ++c)
-    if (sel[c] >= 0 && sel[c] < wb0) {
-      if (cnt_lt == k) {
-        *in_sel = true;
-        *in_win = false;
-        return sel[c];
-      }
-      ++cnt_lt;
-    }
-  const int64_t j = wb0 + (k - cnt_lt);
-  if (j > jt) return -1;
-  bool s_ = false;
-  for (int c = 0; c < n; ++c) s_ |= (sel[c] == j);
-  *in_sel = s_;
-  *in_win = true;
-  return j;
-}
-
-// One workgroup per (unit, 4 slots of the union), a wave per slot.  Every workgroup of a unit
-// first merges the importance partials of the compression split and picks the unit's blocks
-// (the same deterministic result in each); then each wave scores its block once and keeps a
-// selection partial and a window partial (own masks, own local softmax).  The last workgroup
-// of the unit to finish (device-scope counter, zeroed by the split kernel) merges the
-// compression, selection and window partials per head and writes the gated outputs.
+// One workgroup per (unit, share): wgs workgroups per (sequence, KV group) with 4 waves each.
+// Every workgroup of a unit first merges the importance partials of the compression split and
+// picks the unit's blocks (the same deterministic result in each; wave 0 selects).  Meanwhile
+// waves 1-3 take the window blocks, which need no selection: window block wb0 + sg*3 + w-1
+// (scores once, a window partial, and after the selection a selection partial if the block
+// was chosen).  Then wave w takes chosen block sg*4 + w of those below the window.  A wave's
+// blocks accumulate online into one selection and one window partial (max, sum, O), which the
+// workgroup merges in LDS; the last workgroup of the unit to finish (device-scope counter,
+// zeroed by the split kernel) merges the compression, selection and window partials per head
+// and writes the gated outputs.  Text rows: dense causal attention, every wave an online
+// softmax over blocks sg*4+w, +4*wgs, ...
 __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                    const bf16* __restrict__ v, const float* __restrict__ part,
                                                    const uint8_t* __restrict__ vid, const float* __restrict__ gates,
@@ -268,7 +251,7 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
                                                    float* __restrict__ lse, int32_t* __restrict__ idx,
                                                    float* __restrict__ imp_out, float* __restrict__ part3,
                                                    float* __restrict__ ocmp32, int* __restrict__ cnt, Dims dm,
-                                                   int nsplit, int nslot, int wgs) {
+                                                   int nsplit, int wgs) {
   extern __shared__ float dsm[];
   const int G = dm.G;
   float* s_imp = dsm;                   // [Ns] importance of the unit's blocks
@@ -284,208 +267,224 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
   const int g = unit % dm.Hkv;
   const bool text = vid && !vid[b];  // the same for the whole workgroup
   const int64_t t = dm.q0, jt = t / SB;
+  int64_t wlo = t - dm.w + 1;
+  if (wlo < 0) wlo = 0;
+  const int64_t wb0 = wlo / SB;
   const float* pc = part + (int64_t)unit * nsplit * G * PSTRIDE;
-
-  // ---- (video) importance of blocks 0 .. jt (heads summed in a fixed order) and the top-n
-  if (!text) {
-  dsplit_stats(pc, G, nsplit, s_fac, s_M, s_L);
-  __syncthreads();
-  // 4 blocks a thread per pass; loads clamped to valid addresses and unconditional, so a pass
-  // has all of them in flight at once (invalid terms get weight 0)
-  for (int j0 = 0; j0 <= jt; j0 += 4 * blockDim.x) {
-    float a[4][8], c[4][8], fa[4][8], fc[4][8];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = j0 + u * blockDim.x + tid;
-      const int s = j / DBLK, jb = j % DBLK;
-      const int sa = s < nsplit ? s : nsplit - 1, scar = s > 0 ? s - 1 : 0;
-      const bool va = j <= jt && s < nsplit, vc = j <= jt && jb == 0 && s > 0;
-#pragma unroll
-      for (int hh = 0; hh < 8; ++hh) {
-        const int hc = hh < G ? hh : G - 1;
-        a[u][hh] = pc[(sa * G + hc) * PSTRIDE + 2 + HD + jb];
-        c[u][hh] = pc[(scar * G + hc) * PSTRIDE + 2 + HD + DBLK];
-        fa[u][hh] = (va && hh < G) ? s_fac[hc * nsplit + sa] : 0.f;
-        fc[u][hh] = (vc && hh < G) ? s_fac[hc * nsplit + scar] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = j0 + u * blockDim.x + tid;
-      float val = 0.f;
-#pragma unroll
-      for (int hh = 0; hh < 8; ++hh) {
-        val += fa[u][hh] * a[u][hh];
-        val += fc[u][hh] * c[u][hh];
-      }
-      if (j > jt) continue;
-      s_imp[j] = val;
-      if (imp_out && sg == 0) imp_out[(b * dm.Hkv + g) * dm.Ns + j] = val;
-    }
-  }
-  __syncthreads();
-  if (w == 0) {
-    int lo, hi, nj;
-    const int kk = tk_bounds(t, dm.ls, dm.Ns, dm.n, dm.n_init, dm.n_local, &lo, &hi, &nj);
-    wave_select(s_imp, lo, hi, nj, kk, dm.n, &s_tk, s_idx, l);
-    if (sg == 0 && l < dm.n) idx[(b * dm.Hkv + g) * dm.n + l] = s_idx[l];
-  } else {
-    // meanwhile the other waves merge this workgroup's slice of the compression output
-    const int per = (G * HD + wgs - 1) / wgs;
-    for (int i = sg * per + tid - 64; i < (sg + 1) * per && i < G * HD; i += blockDim.x - 64) {
-      const int hh = i / HD, e = i % HD;
-      float oc = 0.f;
-#pragma unroll 16
-      for (int s = 0; s < nsplit; ++s) oc += s_fac[hh * nsplit + s] * pc[(s * G + hh) * PSTRIDE + 2 + e];
-      ocmp32[(int64_t)unit * G * HD + i] = oc;
-    }
-  }
-  __syncthreads();
-  }
-
-  // ---- per wave: branch partials (max, sum, O) of its blocks, in registers until its V tile is
-  // free, then in LDS over it.  Video units: slot sg*4+w of the union, scored once, a selection
-  // and a window partial.  Text units: dense causal attention over blocks sg*4+w, +4*wgs, ...
-  // (one online softmax, branch 0).
-  constexpr int PO = 4;       // O offset within a partial (16-byte aligned rows)
+  constexpr int PO = 4;        // O offset within a partial (16-byte aligned rows)
   constexpr int PW = HD + PO;  // partial of one (branch, head): max, sum, -, -, O[128]
-  const int slot = sg * 4 + w;
-  float* wp = (float*)vt[w];  // [2][G][PW] once the products are done
+  const bool hvalid = hn < G;
+  const float c2 = dm.scale * LOG2E_F;
+
+  // ---- per-wave state: one selection (0) and one window (1) partial, online over its blocks
+  float pm[2] = {-INFINITY, -INFINITY}, pl[2] = {0.f, 0.f};
+  f32x4 po[2][8];
+#pragma unroll
+  for (int br = 0; br < 2; ++br)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) po[br][db] = f32x4{};
+  bf16x8 qf[4];
   {
-    int64_t wlo = t - dm.w + 1;
-    if (wlo < 0) wlo = 0;
-    const int64_t wb0 = wlo / SB;
-    const bool hvalid = hn < G;
-    const float c2 = dm.scale * LOG2E_F;
-    float pm[2] = {-INFINITY, -INFINITY}, pl[2] = {0.f, 0.f};
-    f32x4 po[2][8];
+    const int h = g * G + (hvalid ? hn : 0);
+    const bf16* qrow = q + (b * dm.Hq + h) * (int64_t)HD + 8 * grp;
 #pragma unroll
-    for (int br = 0; br < 2; ++br)
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = hvalid ? *(const bf16x8*)(qrow + 32 * ks) : zero8();
+  }
+  const int64_t stride = (int64_t)dm.Hkv * HD;
+  const bf16* kbase = k + (b * dm.T * dm.Hkv + g) * (int64_t)HD;
+  const bf16* vbase = v + (b * dm.T * dm.Hkv + g) * (int64_t)HD;
+  // block j: stage V into the wave's tile, scores S^T (keys on M, heads on N), per lane
+  auto block_scores = [&](int64_t j, f32x4* sc) {
+    stage_tile64(vt[w], vbase, stride, j * SB, dm.T, 0, 1, l);
 #pragma unroll
-      for (int db = 0; db < 8; ++db) po[br][db] = f32x4{};
-    bf16x8 qf[4];
-    {
-      const int h = g * G + (hvalid ? hn : 0);
-      const bf16* qrow = q + (b * dm.Hq + h) * (int64_t)HD + 8 * grp;
+    for (int kb = 0; kb < 4; ++kb) {
+      int64_t key = j * SB + 16 * kb + hn;
+      if (key >= dm.T) key = dm.T - 1;
+      const bf16* kr = kbase + key * stride + 8 * grp;
+      sc[kb] = f32x4{};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qf[ks] = hvalid ? *(const bf16x8*)(qrow + 32 * ks) : zero8();
+      for (int ks = 0; ks < 4; ++ks) sc[kb] = mfma16(*(const bf16x8*)(kr + 32 * ks), qf[ks], sc[kb]);
     }
-    const int64_t stride = (int64_t)dm.Hkv * HD;
-    const bf16* kbase = k + (b * dm.T * dm.Hkv + g) * (int64_t)HD;
-    const bf16* vbase = v + (b * dm.T * dm.Hkv + g) * (int64_t)HD;
-    // block j: stage V, scores S^T (keys on M, heads on N), returned per lane
-    auto block_scores = [&](int64_t j, f32x4* sc) {
-      stage_tile64(vt[w], vbase, stride, j * SB, dm.T, 0, 1, l);
+    dwait();
+    __builtin_amdgcn_wave_barrier();
+  };
+  // masked scores of block j for branch br (0: u <= t; 1: also u >= wlo), log2 units
+  auto masked = [&](int64_t j, const f32x4* sc, int br, float* x) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        int64_t key = j * SB + 16 * kb + hn;
-        if (key >= dm.T) key = dm.T - 1;
-        const bf16* kr = kbase + key * stride + 8 * grp;
-        sc[kb] = f32x4{};
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) sc[kb] = mfma16(*(const bf16x8*)(kr + 32 * ks), qf[ks], sc[kb]);
+      for (int jj = 0; jj < 4; ++jj) {
+        const int64_t u = j * SB + 16 * kb + 4 * grp + jj;
+        const bool ok = br == 0 ? (u <= t) : (u <= t && u >= wlo);
+        x[4 * kb + jj] = ok ? sc[kb][jj] * c2 : -INFINITY;
       }
-      dwait();
-      __builtin_amdgcn_wave_barrier();
-    };
-    // one branch: masked scores x (log2 units) -> online update of (pm, pl, po)[br]
-    auto accumulate = [&](int br, const float* x) {
-      float mx = x[0];
+  };
+  // online update of partial br with masked scores x of the block whose V tile is staged
+  auto accumulate = [&](int br, const float* x) {
+    float mx = x[0];
 #pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(pm[br], mx);
-      if (mnew == -INFINITY) return;
-      const float sc_old = pm[br] > -INFINITY ? fexp2(pm[br] - mnew) : 0.f;
-      float p[16], ls = 0.f;
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(pm[br], mx);
+    if (mnew == -INFINITY) return;
+    const float sc_old = pm[br] > -INFINITY ? fexp2(pm[br] - mnew) : 0.f;
+    float p[16], ls = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p[e] = fexp2(x[e] - mnew);
-        ls += p[e];
+    for (int e = 0; e < 16; ++e) {
+      p[e] = fexp2(x[e] - mnew);
+      ls += p[e];
+    }
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) po[br][db] *= sc_old;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pb[e] = (bf16)p[4 * (2 * st) + e];
+        pb[4 + e] = (bf16)p[4 * (2 * st + 1) + e];
       }
-      ls += __shfl_xor(ls, 16, 64);
-      ls += __shfl_xor(ls, 32, 64);
+      const int vr = 32 * st + 4 * grp + (hn >> 2);
 #pragma unroll
-      for (int db = 0; db < 8; ++db) po[br][db] *= sc_old;
+      for (int db = 0; db < 8; ++db) {
+        const int col = 16 * db + 4 * (hn & 3);
+        po[br][db] = mfma16(cat(lds_read_tr(vt[w] + swz128(vr, col >> 3) + (col & 7)),
+                                lds_read_tr(vt[w] + swz128(vr + 16, col >> 3) + (col & 7))),
+                            pb, po[br][db]);
+      }
+    }
+    pl[br] = pl[br] * sc_old + ls;
+    pm[br] = mnew;
+  };
+
+  if (!text) {
+    // ---- importance of blocks 0 .. jt (heads summed in a fixed order)
+    dsplit_stats(pc, G, nsplit, s_fac, s_M, s_L);
+    __syncthreads();
+    // 4 blocks a thread per pass; loads clamped to valid addresses and unconditional, so a
+    // pass has all of them in flight at once (invalid terms get weight 0)
+    for (int j0 = 0; j0 <= jt; j0 += 4 * blockDim.x) {
+      float a[4][8], c[4][8], fa[4][8], fc[4][8];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        bf16x8 pb;
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u * blockDim.x + tid;
+        const int s = j / DBLK, jb = j % DBLK;
+        const int sa = s < nsplit ? s : nsplit - 1, scar = s > 0 ? s - 1 : 0;
+        const bool va = j <= jt && s < nsplit, vc = j <= jt && jb == 0 && s > 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pb[e] = (bf16)p[4 * (2 * st) + e];
-          pb[4 + e] = (bf16)p[4 * (2 * st + 1) + e];
+        for (int hh = 0; hh < 8; ++hh) {
+          const int hc = hh < G ? hh : G - 1;
+          a[u][hh] = pc[(sa * G + hc) * PSTRIDE + 2 + HD + jb];
+          c[u][hh] = pc[(scar * G + hc) * PSTRIDE + 2 + HD + DBLK];
+          fa[u][hh] = (va && hh < G) ? s_fac[hc * nsplit + sa] : 0.f;
+          fc[u][hh] = (vc && hh < G) ? s_fac[hc * nsplit + scar] : 0.f;
         }
-        const int vr = 32 * st + 4 * grp + (hn >> 2);
+      }
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          const int col = 16 * db + 4 * (hn & 3);
-          po[br][db] = mfma16(cat(lds_read_tr(vt[w] + swz128(vr, col >> 3) + (col & 7)),
-                                  lds_read_tr(vt[w] + swz128(vr + 16, col >> 3) + (col & 7))),
-                              pb, po[br][db]);
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u * blockDim.x + tid;
+        float val = 0.f;
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) {
+          val += fa[u][hh] * a[u][hh];
+          val += fc[u][hh] * c[u][hh];
         }
+        if (j > jt) continue;
+        s_imp[j] = val;
+        if (imp_out && sg == 0) imp_out[(b * dm.Hkv + g) * dm.Ns + j] = val;
       }
-      pl[br] = pl[br] * sc_old + ls;
-      pm[br] = mnew;
-    };
-    if (text) {
-      for (int64_t j = slot; j <= jt; j += 4 * wgs) {
-        f32x4 sc[4];
-        block_scores(j, sc);
-        float x[16];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int64_t u = j * SB + 16 * kb + 4 * grp + jj;
-            x[4 * kb + jj] = u <= t ? sc[kb][jj] * c2 : -INFINITY;
-          }
-        accumulate(0, x);
-        tk_wave_sync();  // the tile is read before the next block overwrites it
-      }
+    }
+    __syncthreads();
+    // ---- wave 0 selects; waves 1-3 meanwhile score their window block
+    const int wslot = sg * 3 + w - 1;
+    const int64_t jw = wb0 + wslot;
+    const bool has_win = w > 0 && jw <= jt;
+    f32x4 scw[4];
+    if (w == 0) {
+      int lo, hi, nj;
+      const int kk = tk_bounds(t, dm.ls, dm.Ns, dm.n, dm.n_init, dm.n_local, &lo, &hi, &nj);
+      wave_select(s_imp, lo, hi, nj, kk, dm.n, &s_tk, s_idx, l);
+      if (sg == 0 && l < dm.n) idx[(b * dm.Hkv + g) * dm.n + l] = s_idx[l];
     } else {
-      bool in_sel = false, in_win = false;
-      const int64_t j = slot < nslot ? union_block(s_idx, dm.n, jt, wb0, slot, &in_sel, &in_win) : -1;
-      if (j >= 0) {
-        f32x4 sc[4];
-        block_scores(j, sc);
-#pragma unroll
-        for (int br = 0; br < 2; ++br) {
-          if (!(br == 0 ? in_sel : in_win)) continue;
-          float x[16];
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const int64_t u = j * SB + 16 * kb + 4 * grp + jj;
-              const bool ok = br == 0 ? (u <= t) : (u <= t && u >= wlo);
-              x[4 * kb + jj] = ok ? sc[kb][jj] * c2 : -INFINITY;
-            }
-          accumulate(br, x);
-        }
+      if (has_win) {
+        float x[16];
+        block_scores(jw, scw);
+        masked(jw, scw, 1, x);
+        accumulate(1, x);
+      }
+      // then this workgroup's slice of the compression output, merged over the splits
+      const int per = (G * HD + wgs - 1) / wgs;
+      for (int i = sg * per + tid - 64; i < (sg + 1) * per && i < G * HD; i += blockDim.x - 64) {
+        const int hh = i / HD, e = i % HD;
+        float oc = 0.f;
+#pragma unroll 16
+        for (int s = 0; s < nsplit; ++s) oc += s_fac[hh * nsplit + s] * pc[(s * G + hh) * PSTRIDE + 2 + e];
+        ocmp32[(int64_t)unit * G * HD + i] = oc;
       }
     }
-    tk_wave_sync();  // every lane is done reading the V tile
-    if (hvalid) {
-#pragma unroll
-      for (int br = 0; br < 2; ++br) {
-        float* ph = wp + (br * G + hn) * PW;
-        if (grp == 0) {
-          ph[0] = pm[br];
-          ph[1] = pl[br];
+    __syncthreads();
+    if (has_win) {  // the window block also counts for the selection branch if it was chosen
+      bool chosen = false;
+      for (int c = 0; c < dm.n; ++c) chosen |= s_idx[c] == jw;
+      if (chosen) {
+        float x[16];
+        masked(jw, scw, 0, x);
+        accumulate(0, x);
+      }
+    }
+    // ---- chosen block sg*4 + w among those below the window
+    {
+      const int want = sg * 4 + w;
+      int64_t js = -1;
+      int cnt_lt = 0;
+      for (int c = 0; c < dm.n; ++c)
+        if (s_idx[c] >= 0 && s_idx[c] < wb0) {
+          if (cnt_lt == want) js = s_idx[c];
+          ++cnt_lt;
         }
-        if (pl[br] > 0.f) {
+      if (js >= 0) {
+        tk_wave_sync();  // done reading the window block's tile
+        f32x4 sc[4];
+        float x[16];
+        block_scores(js, sc);
+        masked(js, sc, 0, x);
+        accumulate(0, x);
+      }
+    }
+  } else {
+    for (int64_t j = sg * 4 + w; j <= jt; j += 4 * wgs) {
+      f32x4 sc[4];
+      float x[16];
+      block_scores(j, sc);
+      masked(j, sc, 0, x);
+      accumulate(0, x);
+      tk_wave_sync();  // the tile is read before the next block overwrites it
+    }
+  }
+
+  // ---- the wave's partials into LDS over its V tile, merged per workgroup
+  float* wp = (float*)vt[w];  // [2][G][PW]
+  tk_wave_sync();
+  if (hvalid) {
 #pragma unroll
-          for (int db = 0; db < 8; ++db)
-            *(float4*)(ph + PO + 16 * db + 4 * grp) = make_float4(po[br][db][0], po[br][db][1], po[br][db][2],
-                                                                  po[br][db][3]);
-        }
+    for (int br = 0; br < 2; ++br) {
+      float* ph = wp + (br * G + hn) * PW;
+      if (grp == 0) {
+        ph[0] = pm[br];
+        ph[1] = pl[br];
+      }
+      if (pl[br] > 0.f) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+          *(float4*)(ph + PO + 16 * db + 4 * grp) = make_float4(po[br][db][0], po[br][db][1], po[br][db][2],
+                                                                po[br][db][3]);
       }
     }
   }
   __syncthreads();
-  // ---- this workgroup's share: its waves' partials merged per (branch, head), and (video) a
-  // slice of the compression output merged over the splits
   float* pw = part3 + ((int64_t)unit * wgs + sg) * 2 * G * PW;
   for (int i = tid; i < 2 * G * HD / 4; i += blockDim.x) {
     const int bh = (4 * i) / HD, e = (4 * i) % HD;
@@ -615,14 +614,18 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
 // ---------------------------------------------------------------------------
 static size_t drup(size_t x) { return (x + 255) & ~(size_t)255; }
 static int dsplits(const Dims& dm) { return (int)((dm.Nc + DCH - 1) / DCH); }
-static int dslots(const Dims& dm) { return dm.n + (dm.w + SB - 1) / SB + 1; }
+// workgroups per (sequence, group): window blocks 3 a workgroup, chosen blocks below the window 4
+static int dwgs(const Dims& dm) {
+  const int nwin = (dm.w + SB - 1) / SB + 1, a = (nwin + 2) / 3, c = (dm.n + 3) / 4;
+  return a > c ? a : c;
+}
 
 // The selection kernel keeps the importance of all Ns blocks in LDS.
 bool decode_supported(const Dims& dm) { return dm.Tq == 1 && dm.Nc > 0 && dm.Ns <= 16384; }
 
 size_t decode_workspace(const Dims& dm) {
   const size_t units = (size_t)dm.B * dm.Hkv;
-  const size_t wgs = (dslots(dm) + 3) / 4;
+  const size_t wgs = dwgs(dm);
   return drup(units * dsplits(dm) * dm.G * PSTRIDE * 4) + drup(units * wgs * 2 * dm.G * (HD + 4) * 4) +
          drup(units * dm.G * HD * 4) + drup(units * 4);
 }
@@ -634,11 +637,11 @@ hipError_t launch_decode_fast(const Dims& dm, const void* q, const void* kh, con
                               void* out, void* o_cmp, void* o_slc, void* o_swa, int32_t* idx, float* lse,
                               float* imp, void* ws, hipStream_t s, void (*mark)(hipStream_t)) {
   const int units = (int)(dm.B * dm.Hkv);
-  const int ns = dsplits(dm), nslot = dslots(dm);
+  const int ns = dsplits(dm);
   char* p = (char*)ws;
   float* part = (float*)p;
   p += drup((size_t)units * ns * dm.G * PSTRIDE * 4);
-  const int wgs = (nslot + 3) / 4;
+  const int wgs = dwgs(dm);
   float* part3 = (float*)p;
   p += drup((size_t)units * wgs * 2 * dm.G * (HD + 4) * 4);
   float* ocmp32 = (float*)p;
@@ -659,6 +662,6 @@ hipError_t launch_decode_fast(const Dims& dm, const void* q, const void* kh, con
   if (e != hipSuccess) return e;
   dsel_kernel<<<dim3(units * wgs), dim3(256), shm, s>>>(
       (const bf16*)q, (const bf16*)k, (const bf16*)v, part, vid, gates, (bf16*)out, (bf16*)o_cmp, (bf16*)o_slc,
-      (bf16*)o_swa, lse, idx, imp, part3, ocmp32, cnt, dm, ns, nslot, wgs);
+      (bf16*)o_swa, lse, idx, imp, part3, ocmp32, cnt, dm, ns, wgs);
   return hipGetLastError();
 }
