@@ -38,14 +38,18 @@ __device__ __forceinline__ uint32_t tk_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Largest key K with #{active lanes: key >= K} >= kk (the kk-th largest key); needs >= kk
-// active lanes.  Uniform result.
-__device__ __forceinline__ uint32_t tk_kth_key(uint32_t key, bool active, int kk) {
+// Largest key K with #{lanes: key >= K} >= kk (the kk-th largest key); lanes that take no part
+// pass key 0 (every real key has its top bit set).  Two bits a step, three independent ballots.
+// Uniform result.
+__device__ __forceinline__ uint32_t tk_kth_key(uint32_t key, int kk) {
   uint32_t res = 0;
 #pragma unroll
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = res | (1u << bit);
-    if ((int)__popcll(__ballot(active && key >= cand)) >= kk) res = cand;
+  for (int bit = 30; bit >= 0; bit -= 2) {
+    const uint32_t c1 = res | (1u << bit), c2 = res | (2u << bit), c3 = res | (3u << bit);
+    const int n1 = (int)__popcll(__ballot(key >= c1));
+    const int n2 = (int)__popcll(__ballot(key >= c2));
+    const int n3 = (int)__popcll(__ballot(key >= c3));
+    res = n3 >= kk ? c3 : n2 >= kk ? c2 : n1 >= kk ? c1 : res;
   }
   return res;
 }
@@ -81,51 +85,36 @@ __device__ inline void wave_select(const float* __restrict__ x, int lo, int hi, 
           else lm = fmaxf(lm, cv[c]);
         }
         // th: the kk-th largest lane maximum (lanes without a candidate take no part)
-        const uint32_t thk = tk_kth_key(tk_key(lm), lane < nc, kk);
-        int cnt = 0;
+        const uint32_t thk = tk_kth_key(lane < nc ? tk_key(lm) : 0u, kk);
+        // compact the candidates >= th into LDS, one ballot per register slot that has any
+        int total = 0;
 #pragma unroll
-        for (int c = 0; c < TK_REG; ++c) cnt += (lo + lane + 64 * c < hi && tk_key(cv[c]) >= thk) ? 1 : 0;
-        int incl = cnt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += y;
-        }
-        const int total = __builtin_amdgcn_readlane(incl, 63);
-        if (total <= 64) {
-          int pos = incl - cnt;
-#pragma unroll
-          for (int c = 0; c < TK_REG; ++c) {
-            const int j = lo + lane + 64 * c;
-            if (j < hi && tk_key(cv[c]) >= thk) {
-              sc->v[pos] = cv[c];
-              sc->j[pos] = j;
-              ++pos;
-            }
+        for (int c = 0; c < TK_REG; ++c) {
+          const int j = lo + lane + 64 * c;
+          const bool take = j < hi && tk_key(cv[c]) >= thk;
+          const uint64_t bal = __ballot(take);
+          if (bal == 0) continue;  // uniform
+          const int pos = total + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+          if (take && pos < 64) {
+            sc->v[pos] = cv[c];
+            sc->j[pos] = j;
           }
+          total += (int)__popcll(bal);
+        }
+        if (total <= 64) {
           tk_wave_sync();
+          // exact rank of each entry among the total (>= kk) ones: importance, then index
           const bool act = lane < total;
           const float v = act ? sc->v[lane] : -INFINITY;
           cj = act ? sc->j[lane] : 0x7fffffff;
-          // exact kk-th largest value among the total (>= kk) entries, then ties by index
-          const uint32_t k = tk_key(v);
-          const uint32_t kth = tk_kth_key(k, act, kk);
-          const uint64_t gt = __ballot(act && k > kth);
-          uint64_t eq = __ballot(act && k == kth);
-          chosen = gt;
-          for (int need = kk - (int)__popcll(gt); need > 0; --need) {  // lowest indices among the ties
-            int best = 0x7fffffff, bl = 0;
-            for (uint64_t m = eq; m; m &= m - 1) {
-              const int ln = (int)__builtin_ctzll(m);
-              const int jl = __builtin_amdgcn_readlane(cj, ln);
-              if (jl < best) {
-                best = jl;
-                bl = ln;
-              }
-            }
-            chosen |= 1ull << bl;
-            eq &= ~(1ull << bl);
+          int rk = 0;
+          for (int f = 0; f < total; ++f) {
+            const float vf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), f));
+            const int jf = __builtin_amdgcn_readlane(cj, f);
+            rk += tk_before(vf, jf, v, cj) ? 1 : 0;
           }
+          chosen = __ballot(act && rk < kk);
           nsel = kk;
           done = true;
         }
