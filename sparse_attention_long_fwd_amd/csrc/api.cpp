@@ -125,6 +125,8 @@ LayerWs layer_ws(const Dims& dm, int32_t dtype) {
   // parts on the MFMA path, fp32 on the generic path (4 bytes per element either way)
   w.kc = round_up((size_t)dm.B * dm.Nc * dm.Hkv * dm.D * 2) * 2;
   w.vc = w.kc;
+  // prefill split keys: bf16 high parts, then fp8 low parts and their scales
+  if (fast) w.kc += 512;
   w.lse = round_up((size_t)dm.B * dm.Tq * dm.Hq * 4);
   w.idx = round_up((size_t)dm.B * dm.Tq * dm.Hkv * dm.n * 4);
   if (fast && decode_supported(dm)) {
@@ -148,12 +150,12 @@ LayerWs layer_ws(const Dims& dm, int32_t dtype) {
 
 // kc/vc: compressed keys/values (bf16 high parts on the MFMA path, or cdtype on the generic path);
 // kl/vl: low parts on the MFMA path when the layer compressed them itself.
-int run_cmp(int32_t dtype, int32_t cdtype, const Dims& dm, const void* q, const void* kc, const void* kl,
-            const void* vc, const void* vl, const uint8_t* vid, void* o, float* o32, float* lse, float* imp,
-            hipStream_t s) {
+int run_cmp(int32_t dtype, int32_t cdtype, const Dims& dm, const void* q, const void* kc, const void* kl8,
+            const void* ksc, const void* vc, const void* vl, const uint8_t* vid, void* o, float* o32, float* lse,
+            float* imp, hipStream_t s) {
   // low parts come only from the layer's own compression, which writes V as V^T tiles
-  hipError_t e = use_fast(dtype, dm) ? launch_cmp_fast(dm, q, kc, kl, vc, vl, vid, o, o32, lse, imp,
-                                                       kl != nullptr, s)
+  hipError_t e = use_fast(dtype, dm) ? launch_cmp_fast(dm, q, kc, kl8, ksc, vc, vl, vid, o, o32, lse, imp,
+                                                       kl8 != nullptr, s)
                                      : launch_cmp_generic(dtype, cdtype, dm, q, kc, vc, vid, o, lse, imp, s);
   if (e != hipSuccess) return hip_fail(e, "compression-branch kernel");
   return NSA_OK;
@@ -265,7 +267,8 @@ int32_t nsa_cmp_attn_scores(const void* q, const void* k_cmp, const void* v_cmp,
     return fail(NSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
   if (!use_fast(dtype, dm) && dm.Ns > 16384)
     return fail(NSA_ERR_UNSUPPORTED, "generic kernel handles at most 16384 selection blocks");
-  return run_cmp(dtype, dtype, dm, q, k_cmp, nullptr, v_cmp, nullptr, is_video, o_cmp, nullptr, lse, importance,
+  return run_cmp(dtype, dtype, dm, q, k_cmp, nullptr, nullptr, v_cmp, nullptr, is_video, o_cmp, nullptr, lse,
+                 importance,
                  (hipStream_t)stream);
 }
 
@@ -366,18 +369,22 @@ int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const 
   const void* kc_use = k_cmp_in;
   const void* vc_use = v_cmp_in;
   const void* kl_use = nullptr;
+  const void* ksc_use = nullptr;
   const void* vl_use = nullptr;
   int32_t cdtype = dtype;
   if (!kc_use) {
     // Compressed inside the layer, carried at fp32 precision: the MFMA path as bf16 high + low
     // parts (both enter every product), the generic path as fp32.
-    // Prefill on the MFMA path takes the values as V^T tiles.
+    // Prefill on the MFMA path takes the values as V^T tiles and the keys' low parts in fp8
+    // with per-group scales (the scaled fp8 product of the compression branch).
     const bool fast = use_fast(dtype, dm);
     const bool vt = fast && !decode_supported(dm);
-    void* kl = fast ? (char*)kc + w.kc / 2 : nullptr;
+    void* kl = fast ? (char*)kc + round_up((size_t)dm.B * dm.Nc * dm.Hkv * dm.D * 2) : nullptr;
     void* vl = fast ? (char*)vc + w.vc / 2 : nullptr;
-    hipError_t e = launch_compress(dtype, fast ? 2 : 1, k, w_k, kc, kl, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d,
-                                   dm.Nc, s);
+    void* ksc = vt ? (char*)kl + round_up(k8_lo_bytes(dm)) : nullptr;
+    hipError_t e = vt ? launch_compress_k8(dm, k, w_k, kc, kl, ksc, s)
+                      : launch_compress(dtype, fast ? 2 : 1, k, w_k, kc, kl, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d,
+                                        dm.Nc, s);
     if (e == hipSuccess)
       e = vt ? launch_compress_vt(dm, v, w_v, vc, vl, s)
              : launch_compress(dtype, fast ? 2 : 1, v, w_v, vc, vl, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d, dm.Nc, s);
@@ -385,6 +392,7 @@ int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const 
     kc_use = kc;
     vc_use = vc;
     kl_use = kl;
+    ksc_use = ksc;
     vl_use = vl;
     cdtype = fast ? dtype : NSA_F32;
   }
@@ -404,7 +412,7 @@ int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const 
   void* ocmp = fast ? o_cmp : (o_cmp ? o_cmp : ocmp_ws);
   float* ocmp32 = fast ? (float*)ocmp_ws : nullptr;
   int32_t* idx = block_idx_out ? block_idx_out : idx_ws;
-  st = run_cmp(dtype, cdtype, dm, q, kc_use, kl_use, vc_use, vl_use, is_video, ocmp, ocmp32, lse, imp, s);
+  st = run_cmp(dtype, cdtype, dm, q, kc_use, kl_use, ksc_use, vc_use, vl_use, is_video, ocmp, ocmp32, lse, imp, s);
   if (st != NSA_OK) return st;
   prof_mark(s);
   hipError_t e = launch_topk(dm, imp, is_video, idx, s);

@@ -30,11 +30,17 @@
 // carry, the G heads are summed in a fixed order through LDS, so the result is
 // deterministic.
 //
-// Compressed K and V may come as bf16 high + low parts (compressed inside the
-// layer from an fp32 sum).  Both parts of K enter every score, so the scores
-// carry no bf16 rounding of the compression.  Both parts of V enter the value
-// sum for workgroups whose rows see fewer than kVloBelow compressed blocks;
-// longer rows use the high part alone (a sixth fewer products and staged bytes).
+// Compressed K and V may come split (compressed inside the layer from an fp32
+// sum).  K then comes as a bf16 high part plus the remainder in fp8 (e4m3) with
+// one power-of-two scale per 32 channels of a key (compress_k8_kernel); the
+// remainder enters every score through the scaled fp8 MFMA
+// (v_mfma_scale_f32_32x32x64_f8f6f4) against an fp8 copy of Q with per-lane
+// scales.  The remainder is below 2^-8 of the key and its product carries an
+// error near 2^-4 of itself, so the scores keep about 2^-12 relative precision
+// instead of the 2^-8 of bf16 keys, at a quarter of the matrix-core time of a
+// second bf16 product.  V comes as bf16 high + low parts; both enter the value
+// sum for workgroups whose rows see fewer than kVloBelow compressed blocks,
+// longer rows use the high part alone.
 #include "fast_common.hpp"
 
 namespace {
@@ -52,6 +58,11 @@ constexpr int64_t kVloBelow = 256;
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Instruction interleaving in the pipelined loop bodies: LLVM's AMDGPU scheduling groups (a
+// group of n instructions of one kind, in order).
+#define SG(kind, n) __builtin_amdgcn_sched_group_barrier(kind, n, 0)
+constexpr int SG_VALU = 0x2, SG_MFMA = 0x8, SG_DSR = 0x100;
+
 // Compressed values as V^T tiles (the layout compress_vt_kernel writes): per (b, KV head) a run
 // of ceil(Nc / 64) tiles of [128 dims][64 keys], keys zero-padded past Nc.  Inside a 16-key
 // group the key at offset o sits at slot 8*((o>>2)&1) + 4*(o>>3) + (o&3): the eight keys one
@@ -64,6 +75,20 @@ __device__ __forceinline__ int vt_slot(int dim, int key) {
   return dim * CK + ((((kidx >> 3) ^ (dim & 7))) << 3) + (kidx & 7);
 }
 
+// Split keys, low part (compress_k8_kernel, launch_compress_k8): [B, Nc, Hkv, 128] bytes of fp8
+// e4m3 plus [B, Nc, Hkv, 4] scale bytes (E8M0: 2^(byte - 127)).  Inside a key row channel d sits
+// at byte k8_pos(d): the 32 channels lane half hl of an MFMA step-pair feeds to scaled fp8 MFMA c
+// (the channels 16 ks + 8 hl + e, ks = 4c .. 4c + 3, e = 0 .. 7, which are the ones its bf16 Q
+// registers hold) are the 32 contiguous bytes [64 c + 32 hl, +32), and they share scale byte
+// 2 c + hl.
+__host__ __device__ __forceinline__ int k8_pos(int d) {
+  const int ks = d >> 4, hb = (d >> 3) & 1;
+  return (ks >> 2) * 64 + hb * 32 + (ks & 3) * 8 + (d & 7);
+}
+// Staged fp8 tile: 64 rows of 128 bytes, 16-byte chunk c of row r at chunk c ^ ((r >> 1) & 7), so
+// the 16 lanes reading one chunk of 16 consecutive rows hit distinct banks.
+__device__ __forceinline__ int swz8(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
+
 // Row stride (floats) of the per-head importance partials: 16 blocks + 1 pad, so 32 lanes
 // writing one block of 32 rows and 16 lanes reading the 16 blocks of a row hit distinct banks.
 constexpr int IPS = 17;
@@ -74,26 +99,39 @@ __device__ __forceinline__ float xchg32(float x, int hl) {
   return __uint_as_float(hl ? r[0] : r[1]);
 }
 
+// LDS image of one staging buffer (byte offsets): K high, [K low fp8, K scales,] V high[, V low]
+template <bool SPLIT>
+struct CmpLds {
+  static constexpr int KH = 0;
+  static constexpr int KL = TILE * 2;
+  static constexpr int KS = KL + CK * HD;
+  static constexpr int VH = SPLIT ? KS + CK * 4 : TILE * 2;
+  static constexpr int VL = VH + TILE * 2;
+  static constexpr int BUF = SPLIT ? VL + TILE * 2 : VH + TILE * 2;
+};
+
 // VT: values come as V^T tiles (high parts in vh, low parts in vl) instead of [B, Nc, Hkv, D].
+// SPLIT: keys as bf16 high parts (kh) + fp8 low parts (kl8) with scales (ksc).
 // ipart_bufs: 2 = importance partials double-buffered by tile parity, 1 = one buffer (one more
 // barrier a tile; used where two do not fit in LDS).
 template <bool SPLIT, bool VT>
 __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kh,
-                                                       const bf16* __restrict__ kl, const bf16* __restrict__ vh,
+                                                       const uint8_t* __restrict__ kl8,
+                                                       const uint8_t* __restrict__ ksc, const bf16* __restrict__ vh,
                                                        const bf16* __restrict__ vl, const uint8_t* __restrict__ vid,
                                                        bf16* __restrict__ o_bf, float* __restrict__ o_f32,
                                                        float* __restrict__ lse, float* __restrict__ imp, Dims dm,
                                                        int ntq, int ipart_bufs) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  constexpr int NARR = SPLIT ? 4 : 2;                    // staged arrays per buffer: K (hi, lo), V (hi, lo)
-  bf16* buf0 = (bf16*)smem;                               // buffer b, array a at buf0 + (b * NARR + a) * TILE
-  float* ipart0 = (float*)(smem + 2 * NARR * TILE * 2);  // [ipart_bufs][G][CQ][IPS]
+  using LY = CmpLds<SPLIT>;
+  float* ipart0 = (float*)(smem + 2 * LY::BUF);  // [ipart_bufs][G][CQ][IPS]
   __shared__ int s_any;
 
   const int G = dm.G;
   const int nthr = G * 64;
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, hl = l >> 5, n = l & 31;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index as a uniform value
   int unit, rank;
   if (!xcd_remap(blockIdx.x, (int)(dm.B * dm.Hkv), ntq, &unit, &rank)) return;
   const int64_t b = unit / dm.Hkv;
@@ -128,73 +166,162 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = rvalid ? *(const bf16x8*)(qrow + 16 * ks) : zero8();
   }
+  // fp8 copy of Q for the low parts of K: B operand of scaled MFMA c = the 32 values of
+  // qf[4c .. 4c+3] in order, scaled by 2^(8 - E) (E: the smallest power of two above their
+  // magnitudes, so every value stays below 256 in e4m3); scale byte 119 + E undoes it.
+  i32x8 q8[2] = {};
+  int q8s[2] = {127, 127};
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float mq = 0.f;
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mq = fmaxf(mq, fabsf((float)qf[4 * c + k4][e]));
+      int E = 0;
+      (void)frexpf(mq, &E);
+      const bool ok = mq > 0.f && 119 + E >= 1;
+      q8s[c] = ok ? 119 + E : 127;
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+          const bf16x8& v8 = qf[4 * c + k4];
+          const float f0 = ok ? ldexpf((float)v8[4 * e2 + 0], 8 - E) : 0.f;
+          const float f1 = ok ? ldexpf((float)v8[4 * e2 + 1], 8 - E) : 0.f;
+          const float f2 = ok ? ldexpf((float)v8[4 * e2 + 2], 8 - E) : 0.f;
+          const float f3 = ok ? ldexpf((float)v8[4 * e2 + 3], 8 - E) : 0.f;
+          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+          wd = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, wd, true);
+          q8[c][2 * k4 + e2] = wd;
+        }
+    }
+  }
 
   // VLO: the low parts of V enter the value sum (see kVloBelow); a uniform choice per workgroup
   auto body = [&](auto vlo_c) {
   constexpr bool VLO = decltype(vlo_c)::value;
   const int64_t stride = (int64_t)dm.Hkv * HD;
   const int64_t base = (b * dm.Nc * dm.Hkv + g) * (int64_t)HD;
-  auto arr = [&](int bufi, int a) { return buf0 + (bufi * NARR + a) * TILE; };
+  auto lds_at = [&](int bufi, int off) { return smem + bufi * LY::BUF + off; };
+  auto khs_of = [&](int bufi) { return (bf16*)lds_at(bufi, LY::KH); };
+  auto vhs_of = [&](int bufi) { return (bf16*)lds_at(bufi, LY::VH); };
+  auto vls_of = [&](int bufi) { return (bf16*)lds_at(bufi, LY::VL); };
+  // Direct global -> LDS staging of the 64 rows [tile CK, +CK) of a [*, 128] bf16 array into a
+  // swizzled tile (the swz128 layout): the tile takes 16 instructions of 64 lanes x 16 bytes,
+  // instruction ins covers LDS chunks [64 ins, +64) (rows 4 ins .. 4 ins + 3) and goes to wave
+  // ins mod G.  Rows at or past Nc repeat row Nc - 1 (finite data the masks never weight).
+  auto stage64 = [&](bf16* lds, const bf16* src, int tile) {
+    const bf16* st = src + (int64_t)tile * CK * stride;
+    const int64_t left64 = dm.Nc - (int64_t)tile * CK;
+    const int left = left64 < CK ? (int)left64 : CK;  // >= 0; 0 only for the flush tile past the end
+    for (int ins = wu; ins < 16; ins += G) {
+      const int row = ins * 4 + (l >> 4);
+      const int c = (l & 15) ^ (row & 15);
+      const int rr = row < left ? row : left - 1;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(st + (rr * (int)stride + c * 8)),
+                                       (__attribute__((address_space(3))) void*)(lds + ins * 512), 16, 0, 0);
+    }
+  };
+  // fp8 low parts: 8 instructions of 64 lanes x 16 bytes (rows 8 ins .. 8 ins + 7, the swz8
+  // layout), then the 64 keys' scale words (one 4-byte load a lane) from the last wave
   auto stage_k = [&](int tile, int bufi) {
-    stage_tile64(arr(bufi, 0), kh + base, stride, (int64_t)tile * CK, dm.Nc, w, G, l);
-    if constexpr (SPLIT) stage_tile64(arr(bufi, 1), kl + base, stride, (int64_t)tile * CK, dm.Nc, w, G, l);
+    stage64(khs_of(bufi), kh + base, tile);
+    if constexpr (SPLIT) {
+      const int64_t left64 = dm.Nc - (int64_t)tile * CK;
+      const int left = left64 < CK ? (int)left64 : CK;
+      const int64_t key0 = (b * dm.Nc + (int64_t)tile * CK) * dm.Hkv + g;  // (key, head) row index
+      unsigned char* lo = lds_at(bufi, LY::KL);
+      for (int ins = wu; ins < 8; ins += G) {
+        const int row = ins * 8 + (l >> 3);
+        const int c = (l & 7) ^ ((row >> 1) & 7);
+        const int rr = row < left ? row : left - 1;
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(kl8 + (key0 + (int64_t)rr * dm.Hkv) * HD + c * 16),
+            (__attribute__((address_space(3))) void*)(lo + ins * 1024), 16, 0, 0);
+      }
+      if (wu == G - 1) {
+        const int rr = l < left ? l : left - 1;
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(ksc + (key0 + (int64_t)rr * dm.Hkv) * 4),
+            (__attribute__((address_space(3))) void*)lds_at(bufi, LY::KS), 4, 0, 0);
+      }
+    }
   };
   const int ntv = (int)((dm.Nc + CK - 1) / CK);
   auto stage_v = [&](int tile, int bufi) {
     if constexpr (VT) {
       // past the last tile (only the importance carry is flushed there, every p is 0): restage it
       const int64_t t0 = ((b * dm.Hkv + g) * ntv + (tile < ntv ? tile : ntv - 1)) * (int64_t)TILE;
-      stage_lin16k(arr(bufi, SPLIT ? 2 : 1), vh + t0, w, G, l);
-      if constexpr (VLO) stage_lin16k(arr(bufi, 3), vl + t0, w, G, l);
+      stage_lin16k(vhs_of(bufi), vh + t0, wu, G, l);
+      if constexpr (VLO) stage_lin16k(vls_of(bufi), vl + t0, wu, G, l);
     } else {
-      stage_tile64(arr(bufi, SPLIT ? 2 : 1), vh + base, stride, (int64_t)tile * CK, dm.Nc, w, G, l);
-      if constexpr (VLO) stage_tile64(arr(bufi, 3), vl + base, stride, (int64_t)tile * CK, dm.Nc, w, G, l);
+      stage64(vhs_of(bufi), vh + base, tile);
+      if constexpr (VLO) stage64(vls_of(bufi), vl + base, tile);
     }
   };
-  // S^T block kb (32 keys) of the staged tile
-  auto scores = [&](int bufi, int kb) {
-    f32x16 s = {};
-    const int row = kb * 32 + n;
-    const bf16* khs = arr(bufi, 0);
+  // S^T blocks 0 and 1 (32 keys each) of the staged tile; the two accumulation chains alternate
+  auto scores2 = [&](int bufi, f32x16& s0, f32x16& s1) {
+    s0 = f32x16{};
+    s1 = f32x16{};
+    const bf16* khs = khs_of(bufi);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const int off = swz128(row, 2 * ks + hl);
-      s = mfma32(lds_read8(khs + off), qf[ks], s);
-      if constexpr (SPLIT) s = mfma32(lds_read8(arr(bufi, 1) + off), qf[ks], s);
+      const int off0 = swz128(n, 2 * ks + hl), off1 = swz128(32 + n, 2 * ks + hl);
+      s0 = mfma32(lds_read8(khs + off0), qf[ks], s0);
+      s1 = mfma32(lds_read8(khs + off1), qf[ks], s1);
     }
-    return s;
+    if constexpr (SPLIT) {
+      const unsigned char* lo = lds_at(bufi, LY::KL);
+      const int* sc = (const int*)lds_at(bufi, LY::KS);
+      // scale bytes 2c + hl of the lane's key row, moved so byte 2c belongs to this lane half
+      const int sa0 = sc[n] >> (8 * hl), sa1 = sc[32 + n] >> (8 * hl);
+      i32x8 a[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int row = kb * 32 + n;
+          const i32x4 x0 = *(const i32x4*)(lo + swz8(row, 4 * c + 2 * hl));
+          const i32x4 x1 = *(const i32x4*)(lo + swz8(row, 4 * c + 2 * hl + 1));
+          a[kb][c] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0][0], q8[0], s0, 0, 0, 0, sa0, 0, q8s[0]);
+      s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1][0], q8[0], s1, 0, 0, 0, sa1, 0, q8s[0]);
+      s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0][1], q8[1], s0, 0, 0, 2, sa0, 0, q8s[1]);
+      s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1][1], q8[1], s1, 0, 0, 2, sa1, 0, q8s[1]);
+    }
   };
-  // key of score register j of block kb in tile `tile`
-  auto key_of = [&](int tile, int kb, int j) { return tile * CK + kb * 32 + 8 * (j >> 2) + 4 * hl + (j & 3); };
+  // Score register j of block kb in tile `tile` holds key tile CK + kb 32 + 4 hl + koff(j); it is
+  // visible when koff(j) < lim(tile, kb)
+  auto koff = [](int j) { return 8 * (j >> 2) + (j & 3); };
+  auto lim = [&](int tile, int kb) { return nv - (tile * CK + kb * 32 + 4 * hl); };
   // tiles whose keys every row of the workgroup sees need no mask
   auto full = [&](int tile) { return (tile + 1) * CK <= nvmin; };
 
   // ---- sweep 1: log-sum-exp per (row, head) column.  mr: running maximum of the raw scores,
-  // lsum: sum of 2^((s - mr) c2)
+  // lsum: sum of 2^((s - mr) c2).  The scores of tile i are formed (MFMA) while the exponentials
+  // of tile i - 1 run (VALU).
   float mr = -INFINITY, lsum = 0.f;
-  auto lse_tile = [&](int bufi, int tile, auto mask_c) {
-    constexpr bool MASK = decltype(mask_c)::value;
+  auto lse_block = [&](f32x16 s, int tile, int kb, bool mask) {
+    if (mask) {  // uniform
+      const int lm = lim(tile, kb);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = scores(bufi, kb);
-      if constexpr (MASK) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (key_of(tile, kb, j) >= nv) s[j] = -INFINITY;
-      }
-      float mx = s[0];
-#pragma unroll
-      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[j]);
-      const float mnew = fmaxf(mr, mx);
-      if (mnew > -INFINITY) {
-        const float off = -mnew * c2;
-        float acc = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc += fexp2(fmaf(s[j], c2, off));
-        lsum = lsum * fexp2((mr - mnew) * c2) + acc;
-        mr = mnew;
-      }
+      for (int j = 0; j < 16; ++j)
+        if (koff(j) >= lm) s[j] = -INFINITY;
     }
+    float mx = s[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[j]);
+    const float mnew = fmaxf(mr, mx);
+    const float mu = mnew > -INFINITY ? mnew : 0.f;  // nothing visible yet: every term is 0
+    const float off = -mu * c2;
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc += fexp2(fmaf(s[j], c2, off));
+    lsum = lsum * fexp2((mr - mu) * c2) + acc;
+    mr = mnew;
   };
   const int nt1 = (nvmax + CK - 1) / CK;
   if (nt1 > 0) {
@@ -202,15 +329,53 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
     wait_loads();
   }
   __syncthreads();
-  for (int tile = 0; tile < nt1; ++tile) {
-    const int bufi = tile & 1;
-    if (tile + 1 < nt1) stage_k(tile + 1, bufi ^ 1);
-    if (full(tile))
-      lse_tile(bufi, tile, std::false_type{});
-    else
-      lse_tile(bufi, tile, std::true_type{});
-    wait_loads();
-    __syncthreads();
+  {
+    // Tiles [0, nfull) are seen whole by every row of the workgroup.  Their loop forms the scores
+    // of tile i (MFMA) while the exponentials of tile i - 1 run (VALU), interleaved by the
+    // scheduling groups; the remaining tiles go one by one with masks.
+    const int nfull = nvmin / CK;
+    f32x16 p0, p1;  // formed scores not yet summed: those of tile t - 1
+    int t = 0;
+    if (nt1 > 0) {
+      if (nt1 > 1) stage_k(1, 1);
+      scores2(0, p0, p1);
+      wait_loads();
+      __syncthreads();
+      t = 1;
+      for (; t < nt1 && t <= nfull; ++t) {
+        if (t + 1 < nt1) stage_k(t + 1, (t + 1) & 1);
+        f32x16 s0, s1;
+        scores2(t & 1, s0, s1);
+        lse_block(p0, t - 1, 0, false);
+        lse_block(p1, t - 1, 1, false);
+        SG(SG_DSR, 8);
+#pragma unroll
+        for (int i = 0; i < 24; ++i) {
+          SG(SG_MFMA, 1);
+          SG(SG_DSR, 1);
+          SG(SG_VALU, 4);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          SG(SG_MFMA, 1);
+          SG(SG_VALU, 5);
+        }
+        p0 = s0;
+        p1 = s1;
+        wait_loads();
+        __syncthreads();
+      }
+      lse_block(p0, t - 1, 0, !full(t - 1));
+      lse_block(p1, t - 1, 1, !full(t - 1));
+      for (; t < nt1; ++t) {
+        if (t + 1 < nt1) stage_k(t + 1, (t + 1) & 1);
+        scores2(t & 1, p0, p1);
+        lse_block(p0, t, 0, !full(t));
+        lse_block(p1, t, 1, !full(t));
+        wait_loads();
+        __syncthreads();
+      }
+    }
   }
   float L2;  // log2-domain normaliser: p = 2^(s c2 - L2)
   {
@@ -242,74 +407,75 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
   f32x16 oacc[4] = {};
   float carry = 0.f;  // half share of the previous run's last compressed block (hl == 0 lanes)
   const int g16 = l >> 4, i16 = l & 15;
-  auto pv_tile = [&](int bufi, int tile, float* ipb, bool mask) {
+  auto pv_block = [&](const f32x16& s, int bufi, int tile, int kb, float* ipb, bool mask) {
+    float p[16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const f32x16 s = scores(bufi, kb);
-      float p[16];
+    for (int j = 0; j < 16; ++j) p[j] = fexp2(fmaf(s[j], c2, -L2));
+    if (mask) {  // uniform: only tiles with keys past some row's last visible one
+      const int lm = lim(tile, kb);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) p[j] = fexp2(fmaf(s[j], c2, -L2));
-      if (mask) {  // uniform: only tiles with keys past some row's last visible one
+      for (int j = 0; j < 16; ++j) p[j] = koff(j) < lm ? p[j] : 0.f;
+    }
+    // importance of the four selection blocks this lane covers in this 32-key run
+    float a[4], oth[4];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) p[j] = key_of(tile, kb, j) < nv ? p[j] : 0.f;
-      }
-      // importance of the four selection blocks this lane covers in this 32-key run
-      float a[4], oth[4];
+    for (int qq = 0; qq < 4; ++qq) {
+      const float half = 0.5f * p[4 * qq + 3];
+      a[qq] = p[4 * qq] + p[4 * qq + 1] + p[4 * qq + 2] + half;
+      oth[qq] = xchg32(half, hl);
+    }
+    if (hl == 0) {
+      a[0] += carry;
+      a[1] += oth[0];
+      a[2] += oth[1];
+      a[3] += oth[2];
+      carry = oth[3];
+    } else {
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const float half = 0.5f * p[4 * qq + 3];
-        a[qq] = p[4 * qq] + p[4 * qq + 1] + p[4 * qq + 2] + half;
-        oth[qq] = xchg32(half, hl);
-      }
-      if (hl == 0) {
-        a[0] += carry;
-        a[1] += oth[0];
-        a[2] += oth[1];
-        a[3] += oth[2];
-        carry = oth[3];
-      } else {
+      for (int qq = 0; qq < 4; ++qq) a[qq] += oth[qq];
+    }
+    float* ip = ipb + (w * CQ + n) * IPS + kb * 8 + hl;
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) a[qq] += oth[qq];
-      }
-      float* ip = ipb + (w * CQ + n) * IPS + kb * 8 + hl;
+    for (int qq = 0; qq < 4; ++qq) ip[2 * qq] = a[qq];
+    // O^T += Vc^T P^T in two 16-key steps
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) ip[2 * qq] = a[qq];
-      // O^T += Vc^T P^T in two 16-key steps
+    for (int st = 0; st < 2; ++st) {
+      bf16x8 pb;
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        bf16x8 pb;
+      for (int e = 0; e < 8; ++e) pb[e] = (bf16)p[8 * st + e];
+      const int vr = kb * 32 + 16 * st + 4 * (g16 >> 1) + (i16 >> 2);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (bf16)p[8 * st + e];
-        const int vr = kb * 32 + 16 * st + 4 * (g16 >> 1) + (i16 >> 2);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          if constexpr (VT) {
-            // A operand: dims 32 db + n, the lane half's 8 keys of this 16-key step
-            const int off = (32 * db + n) * CK + (((2 * (2 * kb + st) + hl) ^ (n & 7)) << 3);
-            oacc[db] = mfma32(lds_read8(arr(bufi, SPLIT ? 2 : 1) + off), pb, oacc[db]);
-            if constexpr (VLO) oacc[db] = mfma32(lds_read8(arr(bufi, 3) + off), pb, oacc[db]);
-            continue;
-          }
-          const int col = 32 * db + (g16 & 1) * 16 + 4 * (i16 & 3);
-          const int o0 = swz128(vr, col >> 3) + (col & 7);
-          const int o1 = swz128(vr + 8, col >> 3) + (col & 7);
-          const bf16* vhs = arr(bufi, SPLIT ? 2 : 1);
-          oacc[db] = mfma32(cat(lds_read_tr(vhs + o0), lds_read_tr(vhs + o1)), pb, oacc[db]);
-          if constexpr (VLO) {
-            const bf16* vls = arr(bufi, 3);
-            oacc[db] = mfma32(cat(lds_read_tr(vls + o0), lds_read_tr(vls + o1)), pb, oacc[db]);
-          }
+      for (int db = 0; db < 4; ++db) {
+        if constexpr (VT) {
+          // A operand: dims 32 db + n, the lane half's 8 keys of this 16-key step
+          const int off = (32 * db + n) * CK + (((2 * (2 * kb + st) + hl) ^ (n & 7)) << 3);
+          oacc[db] = mfma32(lds_read8(vhs_of(bufi) + off), pb, oacc[db]);
+          if constexpr (VLO) oacc[db] = mfma32(lds_read8(vls_of(bufi) + off), pb, oacc[db]);
+          continue;
+        }
+        const int col = 32 * db + (g16 & 1) * 16 + 4 * (i16 & 3);
+        const int o0 = swz128(vr, col >> 3) + (col & 7);
+        const int o1 = swz128(vr + 8, col >> 3) + (col & 7);
+        const bf16* vhs = vhs_of(bufi);
+        oacc[db] = mfma32(cat(lds_read_tr(vhs + o0), lds_read_tr(vhs + o1)), pb, oacc[db]);
+        if constexpr (VLO) {
+          const bf16* vls = vls_of(bufi);
+          oacc[db] = mfma32(cat(lds_read_tr(vls + o0), lds_read_tr(vls + o1)), pb, oacc[db]);
         }
       }
     }
   };
+  // Each iteration: probabilities and value sums of tile i (its scores formed before), barrier,
+  // the scores of tile i + 1 (MFMA) while the group's heads are summed for tile i.
   const int nt2 = nvmax > 0 ? nvmax / CK + 1 : 0;
+  f32x16 s0, s1;
   if (nt2 > 0) {
     stage_k(0, 0);
     stage_v(0, 0);
     wait_loads();
   }
   __syncthreads();
+  if (nt2 > 0) scores2(0, s0, s1);
   for (int tile = 0; tile < nt2; ++tile) {
     const int bufi = tile & 1;
     if (tile + 1 < nt2) {
@@ -317,9 +483,12 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
       stage_v(tile + 1, bufi ^ 1);
     }
     float* ipb = ipart0 + (ipart_bufs == 2 ? bufi : 0) * G * CQ * IPS;
-    pv_tile(bufi, tile, ipb, !full(tile));
+    const bool m = !full(tile);
+    pv_block(s0, bufi, tile, 0, ipb, m);
+    pv_block(s1, bufi, tile, 1, ipb, m);
     wait_loads();
     __syncthreads();
+    if (tile + 1 < nt2) scores2(bufi ^ 1, s0, s1);
     // sum the group's heads in a fixed order; write the tile's 16 selection blocks
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
@@ -375,21 +544,22 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
 // Dynamic LDS: the staged K / V buffers, then 1 or 2 buffers of importance partials (2 when
 // they fit next to the static LDS of the kernel).
 static int cmp_ipart_bufs(const Dims& dm, bool split, size_t* bytes) {
-  const size_t stage = (size_t)2 * (split ? 4 : 2) * TILE * 2;
+  const size_t stage = (size_t)2 * (split ? CmpLds<true>::BUF : CmpLds<false>::BUF);
   const size_t ip = (size_t)dm.G * CQ * IPS * 4;
   const int bufs = stage + 2 * ip + 64 <= (size_t)160 * 1024 ? 2 : 1;
   *bytes = stage + bufs * ip;
   return bufs;
 }
 
-hipError_t launch_cmp_fast(const Dims& dm, const void* q, const void* kh, const void* kl, const void* vh,
-                           const void* vl, const uint8_t* vid, void* o, float* o32, float* lse, float* imp,
-                           bool vt, hipStream_t s) {
+hipError_t launch_cmp_fast(const Dims& dm, const void* q, const void* kh, const void* kl8, const void* ksc,
+                           const void* vh, const void* vl, const uint8_t* vid, void* o, float* o32, float* lse,
+                           float* imp, bool vt, hipStream_t s) {
   if (dm.Tq <= 0 || dm.B <= 0) return hipSuccess;
   const int ntq = (int)((dm.Tq + CQ - 1) / CQ);
   const int units = (int)(dm.B * dm.Hkv);
   dim3 grid(xcd_grid(units, ntq)), block(dm.G * 64);
-  const bool split = kl != nullptr;
+  const bool split = kl8 != nullptr;
+  if (split && !ksc) return hipErrorInvalidValue;
   size_t shm;
   const int bufs = cmp_ipart_bufs(dm, split, &shm);
   // the MFMA layer path always brings split parts with V^T tiles; standalone calls bring neither
@@ -398,11 +568,11 @@ hipError_t launch_cmp_fast(const Dims& dm, const void* q, const void* kh, const 
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   if (split)
-    cmp_fast_kernel<true, true><<<grid, block, shm, s>>>((const bf16*)q, (const bf16*)kh, (const bf16*)kl,
-                                                         (const bf16*)vh, (const bf16*)vl, vid, (bf16*)o, o32, lse,
-                                                         imp, dm, ntq, bufs);
+    cmp_fast_kernel<true, true><<<grid, block, shm, s>>>((const bf16*)q, (const bf16*)kh, (const uint8_t*)kl8,
+                                                         (const uint8_t*)ksc, (const bf16*)vh, (const bf16*)vl, vid,
+                                                         (bf16*)o, o32, lse, imp, dm, ntq, bufs);
   else
-    cmp_fast_kernel<false, false><<<grid, block, shm, s>>>((const bf16*)q, (const bf16*)kh, nullptr,
+    cmp_fast_kernel<false, false><<<grid, block, shm, s>>>((const bf16*)q, (const bf16*)kh, nullptr, nullptr,
                                                            (const bf16*)vh, nullptr, vid, (bf16*)o, o32, lse, imp,
                                                            dm, ntq, bufs);
   return hipGetLastError();
@@ -460,5 +630,76 @@ hipError_t launch_compress_vt(const Dims& dm, const void* v, const float* w_v, v
   const int ntv = (int)((dm.Nc + CK - 1) / CK);
   compress_vt_kernel<<<(unsigned)(dm.B * dm.Hkv * ntv), 256, 0, s>>>((const bf16*)v, w_v, (bf16*)hi, (bf16*)lo, dm.T,
                                                                     dm.Hkv, dm.l, dm.d, dm.Nc, ntv);
+  return hipGetLastError();
+}
+
+// Split keys for the compression branch: the fp32 sum x of each compressed key is stored as
+// its bf16 high part hi (row-major [B, Nc, Hkv, 128]) and the remainder x - hi in fp8 e4m3 at
+// the k8_pos layout, with one scale per group of 32 channels (the groups scaled fp8 MFMA c of
+// lane half hl reads).  Every |x| of a group lies below 2^E, so |x - hi| <= 2^(E - 9); the
+// remainder is stored times 2^(17 - E) (at most 256, inside e4m3's range) and scale byte
+// 110 + E (E8M0) undoes it.  Groups whose magnitudes are all below 2^-100 store zeros.
+// One thread per 8 channels of a compressed key; the 16 threads of a key row are 16
+// consecutive lanes, and the four of one group (channel chunks of equal parity inside one
+// half of the row) reduce their maximum with two lane exchanges.
+__global__ void __launch_bounds__(256) compress_k8_kernel(const bf16* __restrict__ x, const float* __restrict__ w,
+                                                          bf16* __restrict__ hi, uint8_t* __restrict__ lo8,
+                                                          uint8_t* __restrict__ sc, int64_t T_len, int H, int l,
+                                                          int d, int64_t Nc, int64_t total) {
+  __shared__ float ws[64];
+  for (int m = threadIdx.x; m < l; m += blockDim.x) ws[m] = w[m];
+  __syncthreads();
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool valid = gid < total;  // total is a multiple of 16: whole key rows
+  const int c8 = (int)(gid & 15);
+  const int64_t row = valid ? gid >> 4 : 0;  // (b, i, h)
+  const int h = (int)(row % H);
+  const int64_t i = (row / H) % Nc;
+  const int64_t b = row / H / Nc;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const bf16* src = x + ((b * T_len + i * d) * H + h) * (int64_t)HD + c8 * 8;
+  for (int m = 0; m < l; ++m) {
+    const bf16x8 u = *(const bf16x8*)(src + (int64_t)m * H * HD);
+    const float wm = ws[m];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(wm, (float)u[e], acc[e]);
+  }
+  float mx = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(acc[e]));
+  mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+  int E = 0;
+  (void)frexpf(mx, &E);
+  const bool keep = mx > 0.f && E >= -100;
+  bf16x8 vh;
+  float r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    vh[e] = (bf16)acc[e];
+    r[e] = keep ? ldexpf(acc[e] - (float)vh[e], 17 - E) : 0.f;
+  }
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[4], r[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[6], r[7], w1, true);
+  if (!valid) return;
+  *(bf16x8*)(hi + row * HD + c8 * 8) = vh;
+  *(int2*)(lo8 + row * HD + k8_pos(c8 * 8)) = make_int2(w0, w1);
+  // one thread of each group writes its scale byte 2 (group half of the row) + parity
+  if (((c8 >> 1) & 3) == 0) sc[row * 4 + 2 * (c8 >> 3) + (c8 & 1)] = (uint8_t)(keep ? 110 + E : 127);
+}
+
+size_t k8_lo_bytes(const Dims& dm) { return (size_t)dm.B * dm.Nc * dm.Hkv * HD; }
+size_t k8_sc_bytes(const Dims& dm) { return (size_t)dm.B * dm.Nc * dm.Hkv * 4; }
+
+hipError_t launch_compress_k8(const Dims& dm, const void* k, const float* w_k, void* hi, void* lo8, void* sc,
+                              hipStream_t s) {
+  if (dm.Nc <= 0 || dm.B <= 0) return hipSuccess;
+  if (dm.D != HD || dm.l > 64) return hipErrorInvalidValue;
+  const int64_t total = dm.B * dm.Nc * dm.Hkv * 16;
+  compress_k8_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>((const bf16*)k, w_k, (bf16*)hi, (uint8_t*)lo8,
+                                                                     (uint8_t*)sc, dm.T, dm.Hkv, dm.l, dm.d, dm.Nc,
+                                                                     total);
   return hipGetLastError();
 }

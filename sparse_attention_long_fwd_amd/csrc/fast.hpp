@@ -9,14 +9,22 @@ bool fast_supported(int32_t dtype, const Dims& dm);
 // Scratch bytes the MFMA selection/window path needs.
 size_t fast_sparse_workspace(const Dims& dm);
 
-// Compression branch + importance.  kh/vh: compressed keys/values (bf16); kl/vl:
-// their low parts when they come from an fp32 sum (both NULL otherwise).  vt: the
-// values come as V^T tiles from launch_compress_vt (required with low parts).
-// o (bf16) and o32 (fp32) are optional copies of the branch output; imp (optional)
-// the block importance.
-hipError_t launch_cmp_fast(const Dims& dm, const void* q, const void* kh, const void* kl, const void* vh,
-                           const void* vl, const uint8_t* vid, void* o, float* o32, float* lse, float* imp,
-                           bool vt, hipStream_t s);
+// Compression branch + importance.  kh/vh: compressed keys/values (bf16).  When
+// they come from an fp32 sum: kl8/ksc the fp8 low parts and scales of the keys
+// (launch_compress_k8) and vl the bf16 low parts of the values (all NULL otherwise).
+// vt: the values come as V^T tiles from launch_compress_vt (required with low
+// parts).  o (bf16) and o32 (fp32) are optional copies of the branch output; imp
+// (optional) the block importance.
+hipError_t launch_cmp_fast(const Dims& dm, const void* q, const void* kh, const void* kl8, const void* ksc,
+                           const void* vh, const void* vl, const uint8_t* vid, void* o, float* o32, float* lse,
+                           float* imp, bool vt, hipStream_t s);
+
+// Compressed keys split for launch_cmp_fast: bf16 high parts [B, Nc, Hkv, 128] in hi,
+// fp8 low parts (k8_lo_bytes) in lo8, their scales (k8_sc_bytes) in sc.
+size_t k8_lo_bytes(const Dims& dm);
+size_t k8_sc_bytes(const Dims& dm);
+hipError_t launch_compress_k8(const Dims& dm, const void* k, const float* w_k, void* hi, void* lo8, void* sc,
+                              hipStream_t s);
 
 // Compressed values (bf16 high + low parts of the fp32 sum) as the V^T tiles the
 // compression-branch kernel stages; each part takes vt_tiles_bytes(dm) bytes.
