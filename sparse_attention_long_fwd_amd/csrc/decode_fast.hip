@@ -196,6 +196,170 @@ __global__ void __launch_bounds__(256) dcmp_split_kernel(const bf16* __restrict_
   }
 }
 
+// Compression-branch partials from a bf16 cache, streamed: each wave owns one split of DCH keys
+// (the partial record above) and walks it in 4 steps of 32 keys; the K and V loads of step
+// i + 1 are in flight (into registers) while step i computes, with an online softmax over the
+// steps.  V goes through the wave's own LDS tile for the transposed reads; the waves of a
+// workgroup never synchronise.  Workgroup 0 zeroes the completion counters of dsel_kernel.
+__global__ void __launch_bounds__(256) dcmp_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kh,
+                                                        const bf16* __restrict__ vh, const uint8_t* __restrict__ vid,
+                                                        float* __restrict__ part, int* __restrict__ cnt, Dims dm,
+                                                        int nsplit) {
+  constexpr int NSTEP = DCH / 32;
+  __shared__ __attribute__((aligned(16))) bf16 s_v[4][32 * HD];
+  __shared__ float s_ea[4][16][DBLK + 1], s_ec[4][16][DBLK + 1];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, hn = l & 15, grp = l >> 4;
+  const int wpu = (nsplit + 3) / 4;  // workgroups per unit
+  const int unit = blockIdx.x / wpu;
+  const int s = (blockIdx.x % wpu) * 4 + w;
+  const int64_t b = unit / dm.Hkv;
+  const int g = unit % dm.Hkv;
+  if (blockIdx.x == 0)  // completion counters of the next kernel
+    for (int i = threadIdx.x; i < dm.B * dm.Hkv; i += blockDim.x) cnt[i] = 0;
+  if ((vid && !vid[b]) || s >= nsplit) return;
+  const int G = dm.G;
+  const int64_t nv = cmp_visible(dm.q0, dm.l, dm.d, dm.Nc);
+  const float c2 = dm.scale * LOG2E_F;
+  const bool hvalid = hn < G;
+  const int h = g * G + (hvalid ? hn : 0);
+  bf16x8 qf[4];
+  {
+    const bf16* qrow = q + (b * dm.Hq + h) * (int64_t)HD + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = hvalid ? *(const bf16x8*)(qrow + 32 * ks) : zero8();
+  }
+  const int64_t stride = (int64_t)dm.Hkv * HD;
+  const int64_t base = (b * dm.Nc * dm.Hkv + g) * (int64_t)HD;
+  const int64_t kbeg = (int64_t)s * DCH;
+  // step j: K fragments (rows kbeg + 32j + 16kb + hn, dims 32ks + 8grp) and V rows in the order
+  // of the wave's swizzled LDS tile (16-byte chunk ins*64 + l holds row p >> 4, chunk
+  // (p & 15) ^ (row & 15), p = ins*64 + l); rows past the cache repeat its last row (masked)
+  auto load_step = [&](int j, bf16x8* kf, bf16x8* vf) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      int64_t key = kbeg + 32 * j + 16 * kb + hn;
+      if (key >= dm.Nc) key = dm.Nc - 1;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kf[4 * kb + ks] = *(const bf16x8*)(kh + base + key * stride + 32 * ks + 8 * grp);
+    }
+#pragma unroll
+    for (int ins = 0; ins < 8; ++ins) {
+      const int p = ins * 64 + l, row = p >> 4, c = (p & 15) ^ (row & 15);
+      int64_t key = kbeg + 32 * j + row;
+      if (key >= dm.Nc) key = dm.Nc - 1;
+      vf[ins] = *(const bf16x8*)(vh + base + key * stride + c * 8);
+    }
+  };
+  bf16x8 kfa[8], vfa[8], kfb[8], vfb[8];
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 oacc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) oacc[db] = f32x4{};
+  float ea[NSTEP][2], ec[NSTEP][2], mus[NSTEP];
+  bool live[NSTEP];
+  bf16* vt = s_v[w];
+  const int vr = 4 * grp + (hn >> 2);
+  load_step(0, kfa, vfa);
+#pragma unroll
+  for (int j = 0; j < NSTEP; ++j) {
+    bf16x8* kf = (j & 1) ? kfb : kfa;
+    bf16x8* vf = (j & 1) ? vfb : vfa;
+    if (j + 1 < NSTEP) load_step(j + 1, (j & 1) ? kfa : kfb, (j & 1) ? vfa : vfb);
+    f32x4 sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sc[kb] = f32x4{};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) sc[kb] = mfma16(kf[4 * kb + ks], qf[ks], sc[kb]);
+    }
+    float x[8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int64_t key = kbeg + 32 * j + 16 * kb + 4 * grp + jj;
+        x[4 * kb + jj] = key < nv ? sc[kb][jj] * c2 : -INFINITY;
+      }
+    float mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(m_run, mx);
+    live[j] = mnew > -INFINITY;
+    const float mu = live[j] ? mnew : 0.f;  // nothing visible yet: every term below is 0
+    mus[j] = mu;
+    float p[8], ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = fexp2(x[e] - mu);
+      ls += p[e];
+    }
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    const float fac = fexp2(m_run - mu);  // 0 while m_run is -inf
+    l_run = l_run * fac + ls;
+    m_run = mnew;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) oacc[db][e] *= fac;
+    // importance pieces: this lane's 4 keys of sub-block kb are one selection block
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      ea[j][kb] = p[4 * kb] + p[4 * kb + 1] + p[4 * kb + 2] + 0.5f * p[4 * kb + 3];
+      ec[j][kb] = 0.5f * p[4 * kb + 3];
+    }
+    // V rows of this step into the wave's tile, then O^T += V^T P^T (LDS is in order per wave)
+#pragma unroll
+    for (int ins = 0; ins < 8; ++ins) *(bf16x8*)(vt + (ins * 64 + l) * 8) = vf[ins];
+    bf16x8 pb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pb[e] = (bf16)p[e];
+      pb[4 + e] = (bf16)p[4 + e];
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int col = 16 * db + 4 * (hn & 3);
+      oacc[db] = mfma16(cat(lds_read_tr(vt + swz128(vr, col >> 3) + (col & 7)),
+                            lds_read_tr(vt + swz128(vr + 16, col >> 3) + (col & 7))),
+                        pb, oacc[db]);
+    }
+  }
+  // the split's partial: per head max, sum, O and the importance of its DBLK blocks + carry,
+  // every piece rescaled to the final maximum
+  const float M = m_run;
+#pragma unroll
+  for (int j = 0; j < NSTEP; ++j) {
+    const float f = live[j] ? fexp2(mus[j] - M) : 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int jb = 8 * j + 4 * kb + grp;
+      s_ea[w][hn][jb] = ea[j][kb] * f;
+      s_ec[w][hn][jb + 1] = ec[j][kb] * f;
+    }
+  }
+  if (grp == 0) s_ec[w][hn][0] = 0.f;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float* pp = part + ((int64_t)unit * nsplit + s) * G * PSTRIDE;
+  if (hvalid) {
+    float* ph = pp + hn * PSTRIDE;
+    if (grp == 0) {
+      ph[0] = M;
+      ph[1] = l_run;
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ph[2 + 16 * db + 4 * grp + e] = oacc[db][e];
+    for (int jb = grp; jb <= DBLK; jb += 4)
+      ph[2 + HD + jb] = (jb < DBLK ? s_ea[w][hn][jb] : 0.f) + s_ec[w][hn][jb];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 2. selection, window and the final merge
 
@@ -652,8 +816,8 @@ hipError_t launch_decode_fast(const Dims& dm, const void* q, const void* kh, con
                                                                    (const bf16*)vh, (const bf16*)vl, vid, part, cnt,
                                                                    dm, ns);
   else
-    dcmp_split_kernel<false><<<dim3(units * ns), dim3(256), 0, s>>>((const bf16*)q, (const bf16*)kh, nullptr,
-                                                                    (const bf16*)vh, nullptr, vid, part, cnt, dm, ns);
+    dcmp_pipe_kernel<<<dim3(units * ((ns + 3) / 4)), dim3(256), 0, s>>>((const bf16*)q, (const bf16*)kh,
+                                                                        (const bf16*)vh, vid, part, cnt, dm, ns);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (mark) mark(s);
