@@ -10,14 +10,15 @@
 // so a row-major kernel gathers 16 whole blocks (32 KB of K and V) per (row,
 // group).  Here the work is turned around: each chosen block is loaded once
 // per chunk of 32 rows that chose it, and each (row, slot, head) leaves a
-// partial softmax (max, sum, unnormalised value sum in fp16) that a merge
-// kernel combines.  Per (row, slot) pair that moves the row's query (1.8 KB for
+// partial softmax (max and sum in one array, the unnormalised value sum in fp16
+// in another, 256-byte aligned) that a merge kernel combines.  Per (row, slot) pair that moves the row's query (1.8 KB for
 // 7 heads) and the partial (1.8 KB) instead of 32 KB of keys and values.
 //
 //  1. slc_count: per (batch, group, 2048-row range) an LDS histogram of the
 //     chosen blocks, added to the global per-block counts.
-//  2. slc_scan: per (batch, group) offsets of each block's pair list and of
-//     its chunks of 32 pairs; the chunk -> block map the attention grid uses.
+//  2. slc_scan: per (batch, group) the first chunk of each block's pair list
+//     (lists are padded to whole chunks of 32 pairs, -1 filled, so a chunk's
+//     pairs sit at chunk * 32); the chunk -> block map the attention grid uses.
 //  3. slc_scatter: the same histogram again, one global reservation per
 //     (workgroup, block), then each pair (row, slot) lands in its block's list.
 //  4. slc_chunk: per chunk, the block's K / V staged in LDS (swizzled rows), a
@@ -36,13 +37,14 @@ constexpr int HD = 128;
 constexpr int SB = 64;       // tokens per selection block
 constexpr int RC = 32;       // rows per chunk
 constexpr int RROWS = 2048;  // rows per bucketing workgroup
-constexpr int REC = 8 + 2 * HD;  // bytes of one partial: max (log2 units), sum, O[128] fp16
 }  // namespace
 
 // Bucketing layout in the workspace (per bg = b * Hkv + g):
-//  count[bg][Ns], off[bg][Ns] (pair list of block j starts at pairs + bg*Tq*n + off),
-//  cfirst[bg][Ns] (first chunk of block j), cursor[bg][Ns], chunk_blk[bg][cap_c],
-//  pairs[bg][Tq * n] = (row << 5) | slot.
+//  count[bg][Ns], off[bg][Ns] (pair list of block j starts at pairs + bg*cap_c*RC + off,
+//  off = 32 * its first chunk), cfirst[bg][Ns] (first chunk of block j), cursor[bg][Ns],
+//  chunk_blk[bg][cap_c], pairs[bg][cap_c * RC] = (row << 5) | slot, or -1 past a list's end.
+// Partials: ml[(b*Tq + row)*Hkv + g][slot][head] = (max in log2 units, sum) and
+// po[same index][128] fp16 (one 256-byte record).
 struct SlcBuckets {
   int* count;
   int* off;
@@ -127,15 +129,16 @@ __global__ void __launch_bounds__(1024) slc_scan_kernel(SlcBuckets bk, Dims dm) 
     s_cf[j] = (c + RC - 1) / RC;
   }
   __syncthreads();
-  block_excl_scan(s_off, (int)dm.Ns, s_w);
   const int nch = block_excl_scan(s_cf, (int)dm.Ns, s_w);
   int* cb = bk.chunk_blk + (int64_t)bg * bk.cap_c;
+  int* pl = bk.pairs + (int64_t)bg * bk.cap_c * RC;
   for (int j = threadIdx.x; j < dm.Ns; j += blockDim.x) {
-    bk.off[base + j] = s_off[j];
-    bk.cfirst[base + j] = s_cf[j];
-    bk.cursor[base + j] = 0;
     const int c0 = s_cf[j], c1 = j + 1 < dm.Ns ? s_cf[j + 1] : nch;
+    bk.off[base + j] = c0 * RC;
+    bk.cfirst[base + j] = c0;
+    bk.cursor[base + j] = 0;
     for (int c = c0; c < c1; ++c) cb[c] = j;
+    for (int e = c0 * RC + s_off[j]; e < c1 * RC; ++e) pl[e] = -1;  // the last chunk's unused places
   }
   for (int c = nch + threadIdx.x; c < bk.cap_c; c += blockDim.x) cb[c] = -1;
 }
@@ -167,7 +170,7 @@ __global__ void __launch_bounds__(256) slc_scatter_kernel(const int32_t* __restr
     hist[j] = 0;
   }
   __syncthreads();
-  int* pl = bk.pairs + (int64_t)bg * dm.Tq * dm.n;
+  int* pl = bk.pairs + (int64_t)bg * bk.cap_c * RC;
   for (int64_t e = r0 * dm.n + threadIdx.x; e < r1 * dm.n; e += blockDim.x) {
     const int64_t r = e / dm.n;
     const int s = (int)(e % dm.n);
@@ -181,26 +184,24 @@ __global__ void __launch_bounds__(256) slc_scatter_kernel(const int32_t* __restr
 // One workgroup per chunk of up to 32 (row, slot) pairs of one block; wave w = head g*G + w.
 __global__ void __launch_bounds__(512) slc_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                         const bf16* __restrict__ v, SlcBuckets bk,
-                                                        unsigned char* __restrict__ part, Dims dm) {
+                                                        float2* __restrict__ pml, _Float16* __restrict__ po, Dims dm) {
   __shared__ __attribute__((aligned(16))) bf16 kt[SB * HD];
   __shared__ __attribute__((aligned(16))) bf16 vt[SB * HD];
   const int G = dm.G;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, n = l & 31;
   const int bg = blockIdx.x / bk.cap_c, cc = blockIdx.x % bk.cap_c;
-  const int j = bk.chunk_blk[(int64_t)bg * bk.cap_c + cc];
+  // the chunk's block and this lane's pair (row n of the chunk): two independent loads
+  const int64_t ci = (int64_t)bg * bk.cap_c + cc;
+  const int j = bk.chunk_blk[ci];
+  const int pr = bk.pairs[ci * RC + n];
   if (j < 0) return;
   const int64_t b = bg / dm.Hkv;
   const int g = bg % dm.Hkv;
-  const int64_t bj = (int64_t)bg * dm.Ns + j;
-  const int kc = cc - bk.cfirst[bj];        // chunk within the block
-  const int cnt = bk.count[bj] - kc * RC;    // pairs in this chunk (may exceed RC)
-  const int* pl = bk.pairs + (int64_t)bg * dm.Tq * dm.n + bk.off[bj] + kc * RC;
   const int64_t stride = (int64_t)dm.Hkv * HD;
   const int64_t kvb = (b * dm.T * dm.Hkv + g) * (int64_t)HD;
   stage_tile64(kt, k + kvb, stride, (int64_t)j * SB, dm.T, w, G, l);
   stage_tile64(vt, v + kvb, stride, (int64_t)j * SB, dm.T, w, G, l);
-  // this lane's pair (row n of the chunk) and its query, loaded while the tile streams in
-  const int pr = n < cnt ? pl[n] : -1;
+  // the lane's query, loaded while the tile streams in
   const bool valid = pr >= 0;
   const int64_t row = valid ? (pr >> 5) : 0;
   const int slot = pr & 31;
@@ -274,27 +275,48 @@ __global__ void __launch_bounds__(512) slc_chunk_kernel(const bf16* __restrict__
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ls), __float_as_uint(ls), false, false);
     ls += __uint_as_float(hl ? r[0] : r[1]);
   }
-  if (!valid) return;
-  unsigned char* rec = part + ((((b * dm.Tq + row) * dm.Hkv + g) * dm.n + slot) * G + w) * (int64_t)REC;
-  if (hl == 0) *(float2*)rec = make_float2(mx * c2, ls);
-  _Float16* o16 = (_Float16*)(rec + 8);
+  // O^T register j of dims block db holds dim 32 db + 8 (j >> 2) + 4 hl + (j & 3) of row n.
+  // Lanes n and n + 32 swap halves so that each stores 16 contiguous bytes: lane half hl
+  // writes dims 32 db + 8 (2 qp + hl) .. +8.
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  uint4 st[4][2];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-      h4 x;
+    for (int qp = 0; qp < 2; ++qp) {
+      h4 x0, x1;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = (_Float16)oacc[db][4 * q4 + e];
-      *(h4*)(o16 + 32 * db + 8 * q4 + 4 * hl) = x;
+      for (int e = 0; e < 4; ++e) {
+        x0[e] = (_Float16)oacc[db][8 * qp + e];      // dim 8 (2 qp) + 4 hl + e
+        x1[e] = (_Float16)oacc[db][8 * qp + 4 + e];  // dim 8 (2 qp + 1) + 4 hl + e
+      }
+      const uint2 own0 = __builtin_bit_cast(uint2, x0), own1 = __builtin_bit_cast(uint2, x1);
+      const uint2 send = hl ? own0 : own1, keep = hl ? own1 : own0;
+      uint2 recv;
+      {
+        const auto r0 = __builtin_amdgcn_permlane32_swap(send.x, send.x, false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(send.y, send.y, false, false);
+        recv.x = hl ? r0[0] : r0[1];
+        recv.y = hl ? r1[0] : r1[1];
+      }
+      st[db][qp] = hl ? make_uint4(recv.x, recv.y, keep.x, keep.y) : make_uint4(keep.x, keep.y, recv.x, recv.y);
     }
+  if (!valid) return;
+  const int64_t ri = (((b * dm.Tq + row) * dm.Hkv + g) * dm.n + slot) * G + w;
+  if (hl == 0) pml[ri] = make_float2(mx * c2, ls);
+  _Float16* o16 = po + ri * HD;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int qp = 0; qp < 2; ++qp) *(uint4*)(o16 + 32 * db + 8 * (2 * qp + hl)) = st[db][qp];
 }
 
 // ---------------------------------------------------------------------------
 // One wave per (video row, group): merge the slots per head, gated combine.  Lane l owns
 // dims 2l, 2l+1.
 template <bool OCMP_F32>
-__global__ void __launch_bounds__(256) slc_merge_kernel(const unsigned char* __restrict__ part,
+__global__ void __launch_bounds__(256) slc_merge_kernel(const float2* __restrict__ pml,
+                                                        const _Float16* __restrict__ po,
                                                         const int32_t* __restrict__ idx,
                                                         const uint8_t* __restrict__ vid, const void* __restrict__ ocmp,
                                                         const float* __restrict__ swa32,
@@ -309,14 +331,15 @@ __global__ void __launch_bounds__(256) slc_merge_kernel(const unsigned char* __r
   if (vid && !vid[br]) return;
   const int G = dm.G;
   const int32_t* sel = idx + item * dm.n;
-  const unsigned char* recs = part + item * dm.n * G * (int64_t)REC;
+  const float2* mls = pml + item * dm.n * G;
+  const _Float16* ors = po + item * dm.n * G * (int64_t)HD;
   // weights: lane s (< n) holds slot s; one load round for the (max, sum) of every head
   {
     const bool lv = l < dm.n && sel[l < dm.n ? l : 0] >= 0;
     float2 ml[8];
 #pragma unroll
     for (int w = 0; w < 8; ++w)
-      ml[w] = (lv && w < G) ? *(const float2*)(recs + ((int64_t)l * G + w) * REC) : make_float2(-INFINITY, 0.f);
+      ml[w] = (lv && w < G) ? mls[l * G + w] : make_float2(-INFINITY, 0.f);
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       if (w >= G) break;
@@ -345,7 +368,7 @@ __global__ void __launch_bounds__(256) slc_merge_kernel(const unsigned char* __r
         for (int u = 0; u < 16; ++u) {
           const int s = s0 + u < dm.n ? s0 + u : dm.n - 1;
           const int w = w0 + a < G ? w0 + a : G - 1;
-          x[a][u] = *(const h2*)(recs + ((int64_t)s * G + w) * REC + 8 + 4 * l);
+          x[a][u] = *(const h2*)(ors + ((int64_t)s * G + w) * HD + 2 * l);
         }
 #pragma unroll
       for (int a = 0; a < 2; ++a)
@@ -390,8 +413,9 @@ static size_t srup(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t slc_block_workspace(const Dims& dm) {
   const size_t bgs = (size_t)dm.B * dm.Hkv;
-  return 4 * srup(bgs * dm.Ns * 4) + srup(bgs * slc_cap_chunks(dm) * 4) + srup(bgs * dm.Tq * dm.n * 4) +
-         srup((size_t)dm.B * dm.Tq * dm.Hkv * dm.n * dm.G * REC);
+  const size_t recs = (size_t)dm.B * dm.Tq * dm.Hkv * dm.n * dm.G;
+  return 4 * srup(bgs * dm.Ns * 4) + srup(bgs * slc_cap_chunks(dm) * 4) + srup(bgs * slc_cap_chunks(dm) * RC * 4) +
+         srup(recs * 8) + srup(recs * HD * 2);
 }
 
 hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
@@ -411,8 +435,11 @@ hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const 
   bk.chunk_blk = (int*)p;
   p += srup((size_t)bgs * bk.cap_c * 4);
   bk.pairs = (int*)p;
-  p += srup((size_t)bgs * dm.Tq * dm.n * 4);
-  unsigned char* part = (unsigned char*)p;
+  p += srup((size_t)bgs * bk.cap_c * RC * 4);
+  const size_t recs = (size_t)dm.B * dm.Tq * dm.Hkv * dm.n * dm.G;
+  float2* pml = (float2*)p;
+  p += srup(recs * 8);
+  _Float16* po = (_Float16*)p;
   const int wpb = (int)((dm.Tq + RROWS - 1) / RROWS);
   const size_t hist = (size_t)dm.Ns * 4;
   hipError_t e;
@@ -427,14 +454,14 @@ hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const 
   slc_scan_kernel<<<dim3(bgs), dim3(1024), 2 * hist, s>>>(bk, dm);
   slc_scatter_kernel<<<dim3(bgs * wpb), dim3(256), 2 * hist, s>>>(idx, vid, bk, dm, wpb);
   slc_chunk_kernel<<<dim3((unsigned)bgs * bk.cap_c), dim3(dm.G * 64), 0, s>>>((const bf16*)q, (const bf16*)k,
-                                                                             (const bf16*)v, bk, part, dm);
+                                                                             (const bf16*)v, bk, pml, po, dm);
   const int64_t items = dm.B * dm.Tq * dm.Hkv;
   const dim3 mg((unsigned)((items + 3) / 4));
   if (ocmp_f32)
-    slc_merge_kernel<true><<<mg, dim3(256), 0, s>>>(part, idx, vid, ocmp, swa32, gates, (bf16*)out, (bf16*)o_slc,
-                                                    dm);
+    slc_merge_kernel<true><<<mg, dim3(256), 0, s>>>(pml, po, idx, vid, ocmp, swa32, gates, (bf16*)out,
+                                                    (bf16*)o_slc, dm);
   else
-    slc_merge_kernel<false><<<mg, dim3(256), 0, s>>>(part, idx, vid, ocmp, swa32, gates, (bf16*)out, (bf16*)o_slc,
-                                                     dm);
+    slc_merge_kernel<false><<<mg, dim3(256), 0, s>>>(pml, po, idx, vid, ocmp, swa32, gates, (bf16*)out,
+                                                     (bf16*)o_slc, dm);
   return hipGetLastError();
 }
