@@ -200,7 +200,11 @@ __global__ void __launch_bounds__(256) dcmp_split_kernel(const bf16* __restrict_
 // (the partial record above) and walks it in 4 steps of 32 keys; the K and V loads of step
 // i + 1 are in flight (into registers) while step i computes, with an online softmax over the
 // steps.  V goes through the wave's own LDS tile for the transposed reads; the waves of a
-// workgroup never synchronise.  Workgroup 0 zeroes the completion counters of dsel_kernel.
+// workgroup never synchronise.  When Hkv divides 4, the 4 waves of a workgroup take the same
+// split of all KV heads of a sequence (4 / Hkv splits), so together they read whole token rows
+// of the cache ([Nc, Hkv, D]: Hkv x 256 contiguous bytes a key) at the same time; otherwise
+// the 4 waves take 4 splits of one (sequence, KV head).  Workgroup 0 zeroes the completion
+// counters of dsel_kernel.
 __global__ void __launch_bounds__(256) dcmp_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kh,
                                                         const bf16* __restrict__ vh, const uint8_t* __restrict__ vid,
                                                         float* __restrict__ part, int* __restrict__ cnt, Dims dm,
@@ -209,11 +213,21 @@ __global__ void __launch_bounds__(256) dcmp_pipe_kernel(const bf16* __restrict__
   __shared__ __attribute__((aligned(16))) bf16 s_v[4][32 * HD];
   __shared__ float s_ea[4][16][DBLK + 1], s_ec[4][16][DBLK + 1];
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, hn = l & 15, grp = l >> 4;
-  const int wpu = (nsplit + 3) / 4;  // workgroups per unit
-  const int unit = blockIdx.x / wpu;
-  const int s = (blockIdx.x % wpu) * 4 + w;
-  const int64_t b = unit / dm.Hkv;
-  const int g = unit % dm.Hkv;
+  int64_t b;
+  int g, s;
+  if (4 % dm.Hkv == 0) {
+    const int spw = 4 / dm.Hkv;                   // splits per workgroup
+    const int wps = (nsplit + spw - 1) / spw;      // workgroups per sequence
+    b = blockIdx.x / wps;
+    g = w % dm.Hkv;
+    s = (blockIdx.x % wps) * spw + w / dm.Hkv;
+  } else {
+    const int wpu = (nsplit + 3) / 4;  // workgroups per unit
+    b = (blockIdx.x / wpu) / dm.Hkv;
+    g = (blockIdx.x / wpu) % dm.Hkv;
+    s = (blockIdx.x % wpu) * 4 + w;
+  }
+  const int unit = (int)(b * dm.Hkv + g);
   if (blockIdx.x == 0)  // completion counters of the next kernel
     for (int i = threadIdx.x; i < dm.B * dm.Hkv; i += blockDim.x) cnt[i] = 0;
   if ((vid && !vid[b]) || s >= nsplit) return;
@@ -776,6 +790,13 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
 }
 
 // ---------------------------------------------------------------------------
+static unsigned dcmp_pipe_grid(const Dims& dm, int ns) {
+  if (4 % dm.Hkv == 0) {
+    const int spw = 4 / (int)dm.Hkv;
+    return (unsigned)(dm.B * ((ns + spw - 1) / spw));
+  }
+  return (unsigned)(dm.B * dm.Hkv * ((ns + 3) / 4));
+}
 static size_t drup(size_t x) { return (x + 255) & ~(size_t)255; }
 static int dsplits(const Dims& dm) { return (int)((dm.Nc + DCH - 1) / DCH); }
 // workgroups per (sequence, group): window blocks 3 a workgroup, chosen blocks below the window 4
@@ -816,7 +837,7 @@ hipError_t launch_decode_fast(const Dims& dm, const void* q, const void* kh, con
                                                                    (const bf16*)vh, (const bf16*)vl, vid, part, cnt,
                                                                    dm, ns);
   else
-    dcmp_pipe_kernel<<<dim3(units * ((ns + 3) / 4)), dim3(256), 0, s>>>((const bf16*)q, (const bf16*)kh,
+    dcmp_pipe_kernel<<<dim3(dcmp_pipe_grid(dm, ns)), dim3(256), 0, s>>>((const bf16*)q, (const bf16*)kh,
                                                                         (const bf16*)vh, vid, part, cnt, dm, ns);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
