@@ -36,6 +36,22 @@ PHASE_SOURCES = {
                             "sparse_attention_long_fwd_amd/csrc/common.hpp"],
 }
 PHASE_KERNELS = {"cmp_attn_importance": "cmp_fast_kernel"}
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+# kernels whose counters the bench line carries: name fragment -> sources
+COUNTER_KERNELS = {
+    "cmp_fast_kernel": PHASE_SOURCES["cmp_attn_importance"],
+    "flash_fast_kernel": ["sparse_attention_long_fwd_amd/csrc/flash_fast.hip",
+                          "sparse_attention_long_fwd_amd/csrc/fast_common.hpp",
+                          "sparse_attention_long_fwd_amd/csrc/mfma.hpp"],
+    "slc_chunk_kernel": ["sparse_attention_long_fwd_amd/csrc/slc_block.hip",
+                         "sparse_attention_long_fwd_amd/csrc/fast_common.hpp"],
+    "slc_merge_kernel": ["sparse_attention_long_fwd_amd/csrc/slc_block.hip"],
+    "dcmp_pipe_kernel": ["sparse_attention_long_fwd_amd/csrc/decode_fast.hip",
+                         "sparse_attention_long_fwd_amd/csrc/topk_wave.hpp"],
+    "dsel_kernel": ["sparse_attention_long_fwd_amd/csrc/decode_fast.hip",
+                    "sparse_attention_long_fwd_amd/csrc/topk_wave.hpp"],
+}
+SIMDS_PER_XCD = 32 * 4  # GRBM_GUI_ACTIVE sums core cycles over the 8 XCDs
 COPY_PROBE_BYTES = 1 << 30
 PEAK_BF16_MFMA = 2.5e15   # FLOP/s, MI355X dense bf16
 PEAK_HBM = 8.0e12         # B/s, MI355X HBM3E
@@ -59,6 +75,10 @@ def parse():
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc output directories "
                          "(FETCH_SIZE, then WRITE_SIZE) of a --copy-probe run, and exit")
+    ap.add_argument("--record-counters", nargs=3, metavar=("MFMA_DIR", "EA_READ_DIR", "EA_WRITE_DIR"),
+                    help="write profiles/counters.json from three rocprofv3 --pmc output directories "
+                         "(SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA GRBM_GUI_ACTIVE; TCC_EA0_RDREQ_*; "
+                         "TCC_EA0_WRREQ_*), and exit")
     return ap.parse_args()
 
 
@@ -122,21 +142,85 @@ def record_traffic(fetch_dir, write_dir):
     print(json.dumps(out))
 
 
+def record_counters(mfma_dir, ea_r_dir, ea_w_dir):
+    """Per-dispatch averages of the matrix-core busy cycles against GPU-active cycles and of the
+    L2-to-memory requests (bytes by request size) of the kernels in COUNTER_KERNELS, into
+    profiles/counters.json."""
+    import csv
+    import glob
+
+    def read(d):
+        path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        per = {}
+        for r in csv.DictReader(open(path)):
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            c = per.setdefault(key, {})
+            c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        return per
+
+    out = {}
+    for frag, srcs in COUNTER_KERNELS.items():
+        rec = {"sources": srcs, "sha256": sources_sha(srcs)}
+        for d, kind in ((mfma_dir, "mfma"), (ea_r_dir, "read"), (ea_w_dir, "write")):
+            vals = [c for (_, name), c in read(d).items() if frag in name]
+            if not vals:
+                continue
+            n = len(vals)
+            tot = {k: sum(v.get(k, 0.0) for v in vals) / n for k in vals[0]}
+            if kind == "mfma":
+                rec["mfma_busy_frac"] = tot["SQ_VALU_MFMA_BUSY_CYCLES"] / (tot["GRBM_GUI_ACTIVE"] * SIMDS_PER_XCD)
+                rec["mfma_insts"] = tot["SQ_INSTS_MFMA"]
+                rec["grbm_gui_active"] = tot["GRBM_GUI_ACTIVE"]
+            elif kind == "read":
+                rec["mem_read_bytes"] = (32 * tot["TCC_EA0_RDREQ_32B_sum"] + 64 * tot["TCC_EA0_RDREQ_64B_sum"] +
+                                         128 * tot["TCC_EA0_RDREQ_128B_sum"])
+            else:
+                w64 = tot["TCC_EA0_WRREQ_64B_sum"]
+                rec["mem_write_bytes"] = 64 * w64 + 32 * (tot["TCC_EA0_WRREQ_sum"] - w64)
+            rec["dispatches_" + kind] = n
+        out[frag] = rec
+    with open(COUNTERS_FILE, "w") as fh:
+        json.dump(out, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(out))
+
+
+def kernel_counters():
+    """Counter record of each kernel whose sources are unchanged since it was taken."""
+    try:
+        with open(COUNTERS_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    out = {}
+    for name, r in rec.items():
+        if r.get("sha256") == sources_sha(r["sources"]):
+            out[name] = {k: v for k, v in r.items() if k not in ("sources", "sha256")}
+    return out or None
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def time_calls(fn, reps, stream):
-    """Average milliseconds per call of fn() over reps calls, HIP events on `stream`."""
+def time_calls(fn, reps, stream, per_call=None):
+    """Average milliseconds per call of fn() over reps calls, HIP events on `stream`; per_call (a
+    list) receives each call's milliseconds from events between the calls."""
     import torch
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps - 1)] if per_call is not None else []
     torch.cuda.synchronize()
     start.record(stream)
-    for _ in range(reps):
+    for i in range(reps):
         fn()
+        if i < len(marks):
+            marks[i].record(stream)
     end.record(stream)
     end.synchronize()
+    if per_call is not None:
+        ev = [start] + marks + [end]
+        per_call.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
     return start.elapsed_time(end) / reps
 
 
@@ -149,8 +233,9 @@ def phase_rates(wl, ms):
     Nc = nsa.num_cmp_blocks(T, wl.cmp_block, wl.cmp_stride)
     pos = np.arange(wl.q_start, wl.q_start + Tq)
     vid = (pos >= wl.text_lead) & (pos < T - wl.text_tail)
-    # compress: read K and V once, write compressed keys and values (bf16 high + low parts)
-    b_cmpr = B * (2 * T * Hkv * D * 2 + 2 * 2 * Nc * Hkv * D * 2)
+    # compress: read K and V once; write compressed keys (bf16 high part, fp8 low part, a scale byte
+    # per 32 channels) and values (bf16 high + low parts)
+    b_cmpr = B * (2 * T * Hkv * D * 2 + Nc * Hkv * (D * 3 + D // 32) + 2 * Nc * Hkv * D * 2)
     # top-n: read each video row's candidate importances (blocks 0 .. t / 64), write the chosen blocks
     b_topk = B * Hkv * (int((pos[vid] // wl.sel_block + 1).sum()) * 4 + int(vid.sum()) * wl.top_n * 4)
     # selection: the chosen blocks' K and V, per (video row, group)
@@ -205,10 +290,12 @@ def prefill(args, wl):
     torch.cuda.synchronize()
     log("timing %d steps" % args.steps)
     t0 = time.perf_counter()
-    ms = time_calls(step, args.steps, stream)
+    each = []
+    ms = time_calls(step, args.steps, stream, each)
     wall = time.perf_counter() - t0
     fl = accounting.flops(wl)
-    res = dict(ms_per_step=ms, wall_s=wall, tokens_per_s=wl.q_len * wl.batch / (ms * 1e-3),
+    res = dict(ms_per_step=ms, ms_median=float(np.median(each)), ms_min=float(np.min(each)), wall_s=wall,
+               tokens_per_s=wl.q_len * wl.batch / (ms * 1e-3),
                algo_flops=fl, mfma_util=fl["total"] / (ms * 1e-3) / PEAK_BF16_MFMA)
     if not args.no_kernels:
         log("per-phase timing (%d steps)" % args.steps)
@@ -348,6 +435,9 @@ def main():
     if args.record_traffic:
         record_traffic(*args.record_traffic)
         return
+    if args.record_counters:
+        record_counters(*args.record_counters)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the layer would shard by GQA group (up to 4 ways) and then by "
               "query rows, but no multi-GPU path is built; run with --gpus 1", file=sys.stderr)
@@ -398,6 +488,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": res["ms_per_step"],
+        "ms_median": res["ms_median"],
+        "ms_min": res["ms_min"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -413,6 +505,7 @@ def main():
         "roofline": roofline,
         "decode": dec,
         "cpu_baseline": cpu,
+        "counters": kernel_counters(),
     }
     print(json.dumps(line))
 
