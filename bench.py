@@ -69,6 +69,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-phase timing pass")
     ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the variable-length paged decode measurement")
     ap.add_argument("--cpu-sample-rows", type=int, default=0, help="oracle row sample (0: auto)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run one elementwise copy of 1 GiB (reference for counter runs)")
@@ -399,6 +401,86 @@ def decode(args):
                 roofline=dict(bound="hbm", achieved=bw / 1e9, peak=PEAK_HBM / 1e9, unit="GB/s", frac=bw / PEAK_HBM))
 
 
+def decode_varlen(args):
+    """Variable-length decode over a paged cache: 16 sequences of 4K..64K tokens (seeded), pages of 64
+    tokens at shuffled pool positions; a step is the compressed-cache update for one appended token
+    plus the decode row of every sequence.  Rotates over 4 independent pools."""
+    import torch
+    from sparse_attention_long_fwd_amd import nsa, synth
+
+    wl = synth.WORKLOADS["decode_varlen"]
+    lens = synth.decode_lengths(wl)
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    B, T, Hkv, D = wl.batch, wl.kv_len, wl.num_kv_heads, wl.head_dim
+    mp = T // nsa.PAGE_ROWS
+    lens_t = torch.tensor(lens, dtype=torch.int32, device=dev)
+    sets = []
+    n_rot = 4
+    for r in range(n_rot):
+        log("decode_varlen pool %d" % r)
+        inp = synth.make_inputs(wl, dev, batch_offset=wl.batch * r)
+        gen = torch.Generator().manual_seed(1000 * wl.index + r)
+        perm = torch.randperm(B * mp, generator=gen).to(dev)
+        s = dict(q=inp["q"], gates=inp["gates"], is_video=inp["is_video"], table=perm.view(B, mp).to(torch.int32))
+        for name in ("k", "v"):
+            pool = torch.empty(B * mp, nsa.PAGE_ROWS, Hkv, D, dtype=inp[name].dtype, device=dev)
+            pool[perm] = inp[name].view(B * mp, nsa.PAGE_ROWS, Hkv, D)
+            s[name] = pool
+            del inp[name]
+        Nc = nsa.num_cmp_blocks(T, wl.cmp_block, wl.cmp_stride)
+        s["kc"] = torch.zeros(B, Nc, Hkv, D, dtype=torch.bfloat16, device=dev)
+        s["vc"] = torch.zeros_like(s["kc"])
+        nsa.nsa_compress_append(s["k"], s["v"], inp["w_k"], inp["w_v"], s["kc"], s["vc"], T, T, kv_lens=lens_t,
+                                page_table=s["table"])
+        s["w_k"], s["w_v"] = inp["w_k"], inp["w_v"]
+        sets.append(s)
+    Hq = sets[0]["q"].shape[2]
+    sh = nsa.make_shape(B, 1, T, 0, Hq, Hkv, D)
+    pr = nsa.make_params(**wl.params())
+    ws = torch.empty(nsa.nsa_decode_workspace_size(sh, pr, nsa.NSA_BF16), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(s["q"]) for s in sets]
+    idxs = [torch.full((B, 1, Hkv, wl.top_n), -1, dtype=torch.int32, device=dev) for _ in sets]
+    state = {"i": 0}
+
+    def step():
+        i = state["i"] % n_rot
+        s = sets[i]
+        nsa.nsa_compress_append(s["k"], s["v"], s["w_k"], s["w_v"], s["kc"], s["vc"], T, 1, kv_lens=lens_t,
+                                page_table=s["table"], stream=stream)
+        nsa.nsa_decode_fwd(s["q"], s["k"], s["v"], s["kc"], s["vc"], s["gates"], sh, pr, kv_lens=lens_t,
+                           page_table=s["table"], is_video=s["is_video"], out=outs[i], block_idx_out=idxs[i],
+                           workspace=ws, stream=stream)
+        state["i"] += 1
+
+    for _ in range(2 * n_rot):
+        step()
+    ms = time_calls(step, args.decode_steps, stream)
+    # algorithmic bytes per sequence: its visible compressed blocks, the union of its selected-block and
+    # window tokens, each once, the appended block's l tokens when the new token completes one; plus q,
+    # out and gates
+    total = 0
+    for i in range(n_rot):
+        idx = idxs[i].cpu().numpy()
+        for b, L in enumerate(lens):
+            t = L - 1
+            nc = nsa.num_cmp_blocks(L, wl.cmp_block, wl.cmp_stride)
+            app = (L - wl.cmp_block) >= 0 and (L - wl.cmp_block) % wl.cmp_stride == 0
+            for g in range(Hkv):
+                toks = set(range(max(0, t - wl.window + 1), t + 1))
+                for j in idx[b, 0, g]:
+                    if j >= 0:
+                        toks |= set(range(j * wl.sel_block, min((j + 1) * wl.sel_block, t + 1)))
+                total += (2 * nc + 2 * len(toks)) * D * 2
+                if app:
+                    total += (2 * wl.cmp_block * D * 2 + 2 * D * 2)
+    total = total / n_rot + B * Hq * D * 2 * 2 + B * Hq * 3 * 4
+    bw = total / (ms * 1e-3)
+    return dict(workload=wl.name, lens_min=min(lens), lens_max=max(lens), lens_mean=float(np.mean(lens)),
+                page_rows=nsa.PAGE_ROWS, ms_per_step=ms, algo_bytes=total, gbps=bw / 1e9, hbm_frac=bw / PEAK_HBM,
+                rotating_pools=n_rot, steps=args.decode_steps)
+
+
 def cpu_baseline(args, wl, inp):
     """The fp64 oracle on a bounded row sample of the same prefill (rank 0)."""
     import torch
@@ -455,7 +537,10 @@ def main():
         del src, dst
     wl = synth.WORKLOADS[args.workload]
     if args.no_prefill:
-        print(json.dumps({"decode": decode(args)}))
+        res = {"decode": decode(args)}
+        if not args.no_varlen:
+            res["decode_varlen"] = decode_varlen(args)
+        print(json.dumps(res))
         return
     res, inp = prefill(args, wl)
     ker = res.get("kernels", {})
@@ -480,6 +565,9 @@ def main():
     if not args.no_decode:
         log("decode")
         dec = decode(args)
+        if not args.no_varlen:
+            log("decode_varlen")
+            dec["varlen_paged"] = decode_varlen(args)
     line = {
         "metric": METRIC,
         "value": res["tokens_per_s"],

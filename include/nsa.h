@@ -183,6 +183,55 @@ int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const 
                              const nsa_params* params, void* out, void* o_cmp, void* o_slc, void* o_swa,
                              int32_t* block_idx_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode over a batch of sequences of different lengths, with an optional
+ * paged K / V cache.  The same layer as nsa_hybrid_layer_fwd ([A] abstract,
+ * [B] section 一, [C] sections 2.2 and 3.1), one query row per sequence:
+ * sequence b holds L_b tokens and its query sits at position t = L_b - 1;
+ * every definition above applies with kv_len replaced by L_b (C(t), the
+ * candidate blocks 0 .. t / sel_block, the window, the dense text rows).
+ *  shape      q_len = 1; kv_len = the per-sequence capacity Lmax (q_start is
+ *             ignored); k_cmp / v_cmp hold Nc(Lmax) blocks per sequence.
+ *  kv_lens    device int32 [B]: L_b (clamped to [1, kv_len]); NULL means
+ *             every sequence holds kv_len tokens.
+ *  page_table device int32 [B, max_pages] or NULL.  NULL: k, v are
+ *             [B, kv_len, Hkv, D].  Otherwise k, v are a page pool
+ *             [num_pages, 64, Hkv, D]; token u of sequence b is row u % 64 of
+ *             page page_table[b, u / 64] (ids clamped into [0, num_pages)).
+ *             max_pages * 64 must cover kv_len.
+ *  k_cmp, v_cmp [B, Nc(kv_len), Hkv, D]: blocks i < Nc(L_b) must be current
+ *             (nsa_compress_kv, or nsa_compress_append after each step).
+ *  q, gates, out, o_* are [B, 1, Hq, ...]; is_video [B] (NULL: all video);
+ *  block_idx_out [B, 1, Hkv, top_n] or NULL.  lse and importance are not
+ *  produced.  Covers bf16, head_dim 128, cmp_block 32, cmp_stride 16,
+ *  sel_block 64, 4..8 query heads per KV head, kv_len >= 32; anything else is
+ *  NSA_ERR_UNSUPPORTED.  workspace: nsa_decode_workspace_size() bytes.
+ */
+size_t nsa_decode_workspace_size(const nsa_shape* shape, const nsa_params* params, int32_t dtype);
+int32_t nsa_decode_fwd(const void* q, const void* k, const void* v, const void* k_cmp, const void* v_cmp,
+                       const float* gates, const uint8_t* is_video, int32_t dtype, const nsa_shape* shape,
+                       const nsa_params* params, const int32_t* kv_lens, const int32_t* page_table,
+                       int32_t max_pages, int64_t num_pages, void* out, void* o_cmp, void* o_slc, void* o_swa,
+                       int32_t* block_idx_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * nsa_compress_append -- incremental update of a compressed cache ([B]
+ * section 一, [C] section 2.2; the weighted block sum of nsa_compress_kv).
+ * After n_new tokens were appended to every sequence (kv_lens[b] = L_b
+ * counts them; NULL means kv_len), writes every compressed block i whose last
+ * token i*cmp_stride + cmp_block - 1 lies in [L_b - n_new, L_b - 1], with the
+ * same fp32 sums and rounding as nsa_compress_kv, so the cache equals a full
+ * recompression of the first L_b tokens.  Other blocks are left untouched.
+ * k, v, kv_lens, page_table, max_pages, num_pages are as for nsa_decode_fwd;
+ * k_cmp, v_cmp are [B, Nc(kv_len), Hkv, D].  n_new = 0 launches nothing.
+ * Covers bf16 with head_dim 128 (else NSA_ERR_UNSUPPORTED).
+ */
+int32_t nsa_compress_append(const void* k, const void* v, int32_t dtype, int64_t batch, int64_t kv_len,
+                            int32_t num_kv_heads, int32_t head_dim, const float* w_k, const float* w_v,
+                            int32_t cmp_block, int32_t cmp_stride, const int32_t* kv_lens, const int32_t* page_table,
+                            int32_t max_pages, int64_t num_pages, int32_t n_new, void* k_cmp, void* v_cmp,
+                            void* stream);
+
 /* Debug / test switch: 1 forces the generic (non-MFMA) kernels, 0 restores the
  * default dispatch.  Returns the previous value.  Process-wide. */
 int32_t nsa_set_force_generic(int32_t on);

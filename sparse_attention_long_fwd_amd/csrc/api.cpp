@@ -400,7 +400,7 @@ int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const 
     // one row per sequence: phases = compress | compression branch + top-n | selection, window, combine
     int32_t* didx = block_idx_out ? block_idx_out : idx_ws;
     prof_mark(s);
-    hipError_t e = launch_decode_fast(dm, q, kc_use, kl_use, vc_use, vl_use, k, v, is_video, gates, out, o_cmp,
+    hipError_t e = launch_decode_fast(dm, DecVar{}, q, kc_use, kl_use, vc_use, vl_use, k, v, is_video, gates, out, o_cmp,
                                       o_slc, o_swa, didx, lse, nullptr, sparse_ws_ptr, s, prof_mark);
     if (e != hipSuccess) return hip_fail(e, "decode kernels");
     prof_mark(s);
@@ -425,6 +425,114 @@ int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const 
   }
   void* oswa = o_swa ? o_swa : oswa_ws;
   return run_sparse(dtype, dm, q, k, v, idx, is_video, ocmp, false, gates, out, o_slc, oswa, sparse_ws_ptr, s);
+}
+
+// Shape of a decode batch: one query row per sequence at its own length.
+static int decode_dims(const nsa_shape* shape, const nsa_params* params, int32_t dtype, const int32_t* page_table,
+                       int32_t max_pages, int64_t num_pages, Dims* dm) {
+  if (!shape) return fail(NSA_ERR_INVALID_ARG, "shape must not be NULL");
+  if (shape->q_len != 1) return fail(NSA_ERR_INVALID_ARG, "q_len must be 1 (one query row per sequence)");
+  if (shape->kv_len < 1) return fail(NSA_ERR_INVALID_ARG, "kv_len (the per-sequence capacity) must be >= 1");
+  nsa_shape sh = *shape;
+  sh.q_start = sh.kv_len - 1;
+  int st = check_dims(&sh, params, dtype, dm, true);
+  if (st != NSA_OK) return st;
+  if (page_table) {
+    if (max_pages < 1 || (int64_t)max_pages * kPageRows < dm->T)
+      return fail(NSA_ERR_INVALID_ARG, "max_pages (%d) x %d rows must cover kv_len (%lld)", max_pages, kPageRows,
+                  (long long)dm->T);
+    if (num_pages < 1) return fail(NSA_ERR_INVALID_ARG, "num_pages must be >= 1");
+  }
+  if (!use_decode(dtype, *dm))
+    return fail(NSA_ERR_UNSUPPORTED,
+                "decode kernels cover bf16, head_dim 128, cmp_block 32, cmp_stride 16, sel_block 64, 4..8 query "
+                "heads per KV head and kv_len >= cmp_block (generic kernels not forced)");
+  return NSA_OK;
+}
+
+static size_t decode_ws_bytes(const Dims& dm) {
+  return round_up(decode_workspace(dm)) + round_up((size_t)dm.B * dm.Hkv * dm.n * 4);
+}
+
+size_t nsa_decode_workspace_size(const nsa_shape* shape, const nsa_params* params, int32_t dtype) {
+  Dims dm;
+  if (decode_dims(shape, params, dtype, nullptr, 0, 0, &dm) != NSA_OK) return 0;
+  return decode_ws_bytes(dm);
+}
+
+int32_t nsa_decode_fwd(const void* q, const void* k, const void* v, const void* k_cmp, const void* v_cmp,
+                       const float* gates, const uint8_t* is_video, int32_t dtype, const nsa_shape* shape,
+                       const nsa_params* params, const int32_t* kv_lens, const int32_t* page_table,
+                       int32_t max_pages, int64_t num_pages, void* out, void* o_cmp, void* o_slc, void* o_swa,
+                       int32_t* block_idx_out, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  Dims dm;
+  int st = decode_dims(shape, params, dtype, page_table, max_pages, num_pages, &dm);
+  if (st != NSA_OK) return st;
+  if (!out) return fail(NSA_ERR_INVALID_ARG, "out must not be NULL");
+  if (dm.B == 0) return NSA_OK;
+  if (!q || !k || !v || !k_cmp || !v_cmp || !gates) return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_cmp) || !aligned16(v_cmp) ||
+      !aligned16(out) || !aligned16(o_cmp) || !aligned16(o_slc) || !aligned16(o_swa) || !aligned16(workspace))
+    return fail(NSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  const size_t need = decode_ws_bytes(dm);
+  if (workspace_bytes < need)
+    return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  if (!workspace) return fail(NSA_ERR_INVALID_ARG, "NULL workspace");
+  DecVar dv;
+  dv.lens = kv_lens;
+  dv.pages = page_table;
+  dv.max_pages = page_table ? max_pages : 0;
+  dv.num_pages = page_table ? num_pages : 0;
+  char* p = (char*)workspace;
+  int32_t* idx = block_idx_out ? block_idx_out : (int32_t*)p;
+  p += round_up((size_t)dm.B * dm.Hkv * dm.n * 4);
+  hipError_t e = launch_decode_fast(dm, dv, q, k_cmp, nullptr, v_cmp, nullptr, k, v, is_video, gates, out, o_cmp,
+                                    o_slc, o_swa, idx, nullptr, nullptr, p, (hipStream_t)stream, nullptr);
+  if (e != hipSuccess) return hip_fail(e, "decode kernels");
+  return NSA_OK;
+}
+
+int32_t nsa_compress_append(const void* k, const void* v, int32_t dtype, int64_t batch, int64_t kv_len,
+                            int32_t num_kv_heads, int32_t head_dim, const float* w_k, const float* w_v,
+                            int32_t cmp_block, int32_t cmp_stride, const int32_t* kv_lens, const int32_t* page_table,
+                            int32_t max_pages, int64_t num_pages, int32_t n_new, void* k_cmp, void* v_cmp,
+                            void* stream) {
+  g_err[0] = 0;
+  if (dtype != NSA_F32 && dtype != NSA_BF16) return fail(NSA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (batch < 0 || kv_len < 1 || num_kv_heads <= 0 || head_dim <= 0 || cmp_block <= 0 || cmp_stride <= 0)
+    return fail(NSA_ERR_INVALID_ARG, "sizes must be positive (batch >= 0)");
+  if (n_new < 0) return fail(NSA_ERR_INVALID_ARG, "n_new must be >= 0");
+  if (kv_len > ((int64_t)1 << 31)) return fail(NSA_ERR_UNSUPPORTED, "kv_len above 2^31");
+  if (dtype != NSA_BF16 || head_dim != 128)
+    return fail(NSA_ERR_UNSUPPORTED, "compressed-cache append covers bf16 with head_dim 128");
+  if (page_table && (max_pages < 1 || (int64_t)max_pages * kPageRows < kv_len || num_pages < 1))
+    return fail(NSA_ERR_INVALID_ARG, "page table: max_pages x %d rows must cover kv_len and num_pages >= 1",
+                kPageRows);
+  Dims dm{};
+  dm.B = batch;
+  dm.T = kv_len;
+  dm.Tq = 1;
+  dm.q0 = kv_len - 1;
+  dm.Hkv = num_kv_heads;
+  dm.Hq = num_kv_heads;
+  dm.G = 1;
+  dm.D = head_dim;
+  dm.l = cmp_block;
+  dm.d = cmp_stride;
+  dm.Nc = ncmp(kv_len, cmp_block, cmp_stride);
+  if (dm.Nc == 0 || batch == 0 || n_new == 0) return NSA_OK;
+  if (!k || !v || !w_k || !w_v || !k_cmp || !v_cmp) return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cmp) || !aligned16(v_cmp))
+    return fail(NSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  DecVar dv;
+  dv.lens = kv_lens;
+  dv.pages = page_table;
+  dv.max_pages = page_table ? max_pages : 0;
+  dv.num_pages = page_table ? num_pages : 0;
+  hipError_t e = launch_compress_append(dm, dv, k, v, w_k, w_v, k_cmp, v_cmp, n_new, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "compressed-cache append kernel");
+  return NSA_OK;
 }
 
 }  // extern "C"

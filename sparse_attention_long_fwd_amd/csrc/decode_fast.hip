@@ -30,9 +30,28 @@ constexpr int DCH = 128;           // compressed keys per split
 constexpr int DBLK = DCH / 4;      // selection blocks per split (4 compressed keys per 64-token block)
 constexpr int PSTRIDE = 2 + HD + DBLK + 1;  // per head: max, sum, O[128], E[32] + carry
 constexpr int SB = 64;
+static_assert(kPageRows == SB, "a page holds one selection block");
 }  // namespace
 
 __device__ __forceinline__ void dwait() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
+
+// Tokens in sequence b (clamped to [1, capacity]).
+__device__ __forceinline__ int64_t dv_len(const DecVar& dv, const Dims& dm, int64_t b) {
+  if (!dv.lens) return dm.T;
+  const int64_t n = dv.lens[b];
+  return n < 1 ? 1 : (n > dm.T ? dm.T : n);
+}
+// Row u (of KV head g) of sequence b in a K or V cache, contiguous [B, T, Hkv, D] or paged
+// [num_pages, 64, Hkv, D] (page ids clamped into the pool).
+__device__ __forceinline__ const bf16* dv_row(const DecVar& dv, const Dims& dm, const bf16* base, int64_t b, int g,
+                                              int64_t u) {
+  if (dv.pages) {
+    int64_t pg = dv.pages[b * dv.max_pages + u / kPageRows];
+    pg = pg < 0 ? 0 : (pg >= dv.num_pages ? dv.num_pages - 1 : pg);
+    return base + ((pg * kPageRows + u % kPageRows) * dm.Hkv + g) * (int64_t)HD;
+  }
+  return base + ((b * dm.T + u) * dm.Hkv + g) * (int64_t)HD;
+}
 
 // ---------------------------------------------------------------------------
 // 1. compression-branch partials
@@ -208,7 +227,7 @@ __global__ void __launch_bounds__(256) dcmp_split_kernel(const bf16* __restrict_
 __global__ void __launch_bounds__(256) dcmp_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kh,
                                                         const bf16* __restrict__ vh, const uint8_t* __restrict__ vid,
                                                         float* __restrict__ part, int* __restrict__ cnt, Dims dm,
-                                                        int nsplit) {
+                                                        DecVar dv, int nsplit) {
   constexpr int NSTEP = DCH / 32;
   __shared__ __attribute__((aligned(16))) bf16 s_v[4][32 * HD];
   __shared__ float s_ea[4][16][DBLK + 1], s_ec[4][16][DBLK + 1];
@@ -232,7 +251,13 @@ __global__ void __launch_bounds__(256) dcmp_pipe_kernel(const bf16* __restrict__
     for (int i = threadIdx.x; i < dm.B * dm.Hkv; i += blockDim.x) cnt[i] = 0;
   if ((vid && !vid[b]) || s >= nsplit) return;
   const int G = dm.G;
-  const int64_t nv = cmp_visible(dm.q0, dm.l, dm.d, dm.Nc);
+  // compressed blocks of this sequence seen by its query (every block of a full cache)
+  const int64_t nv = cmp_visible(dv.lens ? dv_len(dv, dm, b) - 1 : dm.q0, dm.l, dm.d, dm.Nc);
+  if ((int64_t)s * DCH >= nv) {  // a split past the sequence's blocks: an empty partial
+    float* ph = part + ((int64_t)unit * nsplit + s) * G * PSTRIDE;
+    for (int i = l; i < G * PSTRIDE; i += 64) ph[i] = (i % PSTRIDE) == 0 ? -INFINITY : 0.f;
+    return;
+  }
   const float c2 = dm.scale * LOG2E_F;
   const bool hvalid = hn < G;
   const int h = g * G + (hvalid ? hn : 0);
@@ -252,7 +277,7 @@ __global__ void __launch_bounds__(256) dcmp_pipe_kernel(const bf16* __restrict__
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       int64_t key = kbeg + 32 * j + 16 * kb + hn;
-      if (key >= dm.Nc) key = dm.Nc - 1;
+      if (key >= nv) key = nv - 1;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) kf[4 * kb + ks] = *(const bf16x8*)(kh + base + key * stride + 32 * ks + 8 * grp);
     }
@@ -260,7 +285,7 @@ __global__ void __launch_bounds__(256) dcmp_pipe_kernel(const bf16* __restrict__
     for (int ins = 0; ins < 8; ++ins) {
       const int p = ins * 64 + l, row = p >> 4, c = (p & 15) ^ (row & 15);
       int64_t key = kbeg + 32 * j + row;
-      if (key >= dm.Nc) key = dm.Nc - 1;
+      if (key >= nv) key = nv - 1;
       vf[ins] = *(const bf16x8*)(vh + base + key * stride + c * 8);
     }
   };
@@ -429,7 +454,7 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
                                                    float* __restrict__ lse, int32_t* __restrict__ idx,
                                                    float* __restrict__ imp_out, float* __restrict__ part3,
                                                    float* __restrict__ ocmp32, int* __restrict__ cnt, Dims dm,
-                                                   int nsplit, int wgs) {
+                                                   DecVar dv, int nsplit, int wgs) {
   extern __shared__ float dsm[];
   const int G = dm.G;
   float* s_imp = dsm;                   // [Ns] importance of the unit's blocks
@@ -444,7 +469,8 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
   const int64_t b = unit / dm.Hkv;
   const int g = unit % dm.Hkv;
   const bool text = vid && !vid[b];  // the same for the whole workgroup
-  const int64_t t = dm.q0, jt = t / SB;
+  const int64_t len = dv_len(dv, dm, b);  // tokens of this sequence; the query sits at len - 1
+  const int64_t t = dv.lens ? len - 1 : dm.q0, jt = t / SB;
   int64_t wlo = t - dm.w + 1;
   if (wlo < 0) wlo = 0;
   const int64_t wb0 = wlo / SB;
@@ -469,16 +495,21 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
     for (int ks = 0; ks < 4; ++ks) qf[ks] = hvalid ? *(const bf16x8*)(qrow + 32 * ks) : zero8();
   }
   const int64_t stride = (int64_t)dm.Hkv * HD;
-  const bf16* kbase = k + (b * dm.T * dm.Hkv + g) * (int64_t)HD;
-  const bf16* vbase = v + (b * dm.T * dm.Hkv + g) * (int64_t)HD;
+  // block j's rows: 64 consecutive rows of stride Hkv*D from its first row (contiguous cache) or
+  // from its page (paged cache); rows past the sequence repeat its last row (masked)
+  auto krow0 = [&](int64_t j) { return dv_row(dv, dm, k, b, g, j * SB); };
+  auto vrow0 = [&](int64_t j) { return dv_row(dv, dm, v, b, g, j * SB); };
+  auto rows_in = [&](int64_t j) { return len - j * SB < SB ? len - j * SB : (int64_t)SB; };
   // block j: stage V into the wave's tile, scores S^T (keys on M, heads on N), per lane
   auto block_scores = [&](int64_t j, f32x4* sc) {
-    stage_tile64(vt[w], vbase, stride, j * SB, dm.T, 0, 1, l);
+    const int64_t nr = rows_in(j);
+    stage_tile64(vt[w], vrow0(j), stride, 0, nr, 0, 1, l);
+    const bf16* kb0 = krow0(j);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      int64_t key = j * SB + 16 * kb + hn;
-      if (key >= dm.T) key = dm.T - 1;
-      const bf16* kr = kbase + key * stride + 8 * grp;
+      int64_t r = 16 * kb + hn;
+      if (r >= nr) r = nr - 1;
+      const bf16* kr = kb0 + r * stride + 8 * grp;
       sc[kb] = f32x4{};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) sc[kb] = mfma16(*(const bf16x8*)(kr + 32 * ks), qf[ks], sc[kb]);
@@ -817,10 +848,11 @@ size_t decode_workspace(const Dims& dm) {
 
 // kh/vh: compressed cache (bf16), kl/vl: low parts or NULL.  Text rows take dense causal
 // attention in the selection kernel (their compression split is skipped).
-hipError_t launch_decode_fast(const Dims& dm, const void* q, const void* kh, const void* kl, const void* vh,
-                              const void* vl, const void* k, const void* v, const uint8_t* vid, const float* gates,
-                              void* out, void* o_cmp, void* o_slc, void* o_swa, int32_t* idx, float* lse,
-                              float* imp, void* ws, hipStream_t s, void (*mark)(hipStream_t)) {
+hipError_t launch_decode_fast(const Dims& dm, const DecVar& dv, const void* q, const void* kh, const void* kl,
+                              const void* vh, const void* vl, const void* k, const void* v, const uint8_t* vid,
+                              const float* gates, void* out, void* o_cmp, void* o_slc, void* o_swa, int32_t* idx,
+                              float* lse, float* imp, void* ws, hipStream_t s, void (*mark)(hipStream_t)) {
+  if (kl && (dv.lens || dv.pages)) return hipErrorInvalidValue;  // split parts: full contiguous caches only
   const int units = (int)(dm.B * dm.Hkv);
   const int ns = dsplits(dm);
   char* p = (char*)ws;
@@ -838,7 +870,7 @@ hipError_t launch_decode_fast(const Dims& dm, const void* q, const void* kh, con
                                                                    dm, ns);
   else
     dcmp_pipe_kernel<<<dim3(dcmp_pipe_grid(dm, ns)), dim3(256), 0, s>>>((const bf16*)q, (const bf16*)kh,
-                                                                        (const bf16*)vh, vid, part, cnt, dm, ns);
+                                                                        (const bf16*)vh, vid, part, cnt, dm, dv, ns);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (mark) mark(s);
@@ -847,6 +879,66 @@ hipError_t launch_decode_fast(const Dims& dm, const void* q, const void* kh, con
   if (e != hipSuccess) return e;
   dsel_kernel<<<dim3(units * wgs), dim3(256), shm, s>>>(
       (const bf16*)q, (const bf16*)k, (const bf16*)v, part, vid, gates, (bf16*)out, (bf16*)o_cmp, (bf16*)o_slc,
-      (bf16*)o_swa, lse, idx, imp, part3, ocmp32, cnt, dm, ns, wgs);
+      (bf16*)o_swa, lse, idx, imp, part3, ocmp32, cnt, dm, dv, ns, wgs);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 3. compressed-cache update for a decode stream
+// Compressed block i covers tokens [i d, i d + l) and is complete once token i d + l - 1 is in
+// the cache.  After n_new tokens were appended to every sequence, the blocks whose last token
+// is among them are computed from the sequence's K / V rows (contiguous or paged), with the same
+// weights, order of summation and rounding as the full compression.  One thread per 8 channels
+// of one (sequence, new-block slot, KV head).
+__global__ void __launch_bounds__(256) compress_append_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
+                                                              const float* __restrict__ w_k,
+                                                              const float* __restrict__ w_v, bf16* __restrict__ kc,
+                                                              bf16* __restrict__ vc, Dims dm, DecVar dv, int n_new,
+                                                              int slots) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int c8 = (int)(gid % (HD / 8));
+  int64_t rest = gid / (HD / 8);
+  const int h = (int)(rest % dm.Hkv);
+  rest /= dm.Hkv;
+  const int slot = (int)(rest % slots);
+  const int64_t b = rest / slots;
+  if (b >= dm.B) return;
+  const int64_t len = dv_len(dv, dm, b);
+  if (len < dm.l) return;
+  const int64_t hi = (len - dm.l) / dm.d;  // last complete block
+  const int64_t lo_num = len - n_new - dm.l + 1;
+  const int64_t i = (lo_num <= 0 ? 0 : (lo_num + dm.d - 1) / dm.d) + slot;
+  if (i > hi || i >= dm.Nc) return;
+  float ak[8] = {0, 0, 0, 0, 0, 0, 0, 0}, av[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int m = 0; m < dm.l; ++m) {
+    const int64_t u = i * dm.d + m;
+    const bf16x8 xk = *(const bf16x8*)(dv_row(dv, dm, k, b, h, u) + c8 * 8);
+    const bf16x8 xv = *(const bf16x8*)(dv_row(dv, dm, v, b, h, u) + c8 * 8);
+    const float wk = w_k[m], wv = w_v[m];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ak[e] = fmaf(wk, (float)xk[e], ak[e]);
+      av[e] = fmaf(wv, (float)xv[e], av[e]);
+    }
+  }
+  bf16x8 ok, ov;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ok[e] = (bf16)ak[e];
+    ov[e] = (bf16)av[e];
+  }
+  const int64_t o = ((b * dm.Nc + i) * dm.Hkv + h) * (int64_t)HD + c8 * 8;
+  *(bf16x8*)(kc + o) = ok;
+  *(bf16x8*)(vc + o) = ov;
+}
+
+hipError_t launch_compress_append(const Dims& dm, const DecVar& dv, const void* k, const void* v, const float* w_k,
+                                  const float* w_v, void* kc, void* vc, int n_new, hipStream_t s) {
+  if (dm.B <= 0 || dm.Nc <= 0 || n_new <= 0) return hipSuccess;
+  if (dm.D != HD) return hipErrorInvalidValue;
+  const int slots = (n_new + dm.d - 1) / dm.d + 1;
+  const int64_t total = dm.B * slots * dm.Hkv * (HD / 8);
+  compress_append_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(
+      (const bf16*)k, (const bf16*)v, w_k, w_v, (bf16*)kc, (bf16*)vc, dm, dv, n_new, slots);
   return hipGetLastError();
 }

@@ -45,9 +45,25 @@ hipError_t launch_flash_fast(const Dims& dm, const void* q, const void* k, const
 size_t flash_workspace(const Dims& dm);
 
 // Decode path (one query row per sequence, split over the compressed keys).
+// Variable-length batches: lens[b] tokens in sequence b (the query at lens[b] - 1), dm.T the
+// capacity; pages (optional) maps 64-token page i of sequence b to pool page pages[b * max_pages
+// + i] of a [num_pages, 64, Hkv, D] cache.  All null: every sequence holds dm.T tokens of a
+// contiguous [B, T, Hkv, D] cache, the query at dm.q0.
+// Rows of one page of a paged K / V cache ([num_pages, kPageRows, Hkv, D]): one selection block.
+constexpr int kPageRows = 64;
+struct DecVar {
+  const int32_t* lens = nullptr;
+  const int32_t* pages = nullptr;
+  int max_pages = 0;
+  int64_t num_pages = 0;
+};
 bool decode_supported(const Dims& dm);
 size_t decode_workspace(const Dims& dm);
-hipError_t launch_decode_fast(const Dims& dm, const void* q, const void* kh, const void* kl, const void* vh,
-                              const void* vl, const void* k, const void* v, const uint8_t* vid, const float* gates,
-                              void* out, void* o_cmp, void* o_slc, void* o_swa, int32_t* idx, float* lse,
-                              float* imp, void* ws, hipStream_t s, void (*mark)(hipStream_t));
+hipError_t launch_decode_fast(const Dims& dm, const DecVar& dv, const void* q, const void* kh, const void* kl,
+                              const void* vh, const void* vl, const void* k, const void* v, const uint8_t* vid,
+                              const float* gates, void* out, void* o_cmp, void* o_slc, void* o_swa, int32_t* idx,
+                              float* lse, float* imp, void* ws, hipStream_t s, void (*mark)(hipStream_t));
+// Compressed cache update after n_new tokens were appended to every sequence: the blocks whose
+// last token is among them (per sequence), from the (possibly paged) K / V cache.
+hipError_t launch_compress_append(const Dims& dm, const DecVar& dv, const void* k, const void* v, const float* w_k,
+                                  const float* w_v, void* kc, void* vc, int n_new, hipStream_t s);

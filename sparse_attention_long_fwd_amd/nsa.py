@@ -56,6 +56,11 @@ EXPORTS = {
     "nsa_hybrid_layer_workspace_size": (_SZ, [_SH, _PR, _I32]),
     "nsa_hybrid_layer_fwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _SH, _PR, _P, _P, _P, _P, _P, _P,
                                     _SZ, _P]),
+    "nsa_decode_workspace_size": (_SZ, [_SH, _PR, _I32]),
+    "nsa_decode_fwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _SH, _PR, _P, _P, _I32, _I64, _P, _P, _P, _P, _P,
+                              _P, _SZ, _P]),
+    "nsa_compress_append": (_I32, [_P, _P, _I32, _I64, _I64, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _I32, _I64,
+                                   _I32, _P, _P, _P]),
     "nsa_set_force_generic": (_I32, [_I32]),
     "nsa_profile_enable": (_I32, [_I32]),
     "nsa_profile_read": (_I32, [ctypes.POINTER(ctypes.c_float), _I32]),
@@ -225,3 +230,42 @@ def nsa_hybrid_layer_fwd(q, k, v, gates, shape: NsaShape, params: NsaParams, w_k
                                       ctypes.byref(params), _ptr(out), _ptr(o_cmp), _ptr(o_slc), _ptr(o_swa),
                                       _ptr(block_idx_out), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+PAGE_ROWS = 64  # tokens per page of a paged K / V cache
+
+
+def nsa_decode_workspace_size(shape: NsaShape, params: NsaParams, dtype_code: int) -> int:
+    return int(lib().nsa_decode_workspace_size(ctypes.byref(shape), ctypes.byref(params), dtype_code))
+
+
+def nsa_decode_fwd(q, k, v, k_cmp, v_cmp, gates, shape: NsaShape, params: NsaParams, kv_lens=None,
+                   page_table=None, num_pages=0, is_video=None, out=None, o_cmp=None, o_slc=None, o_swa=None,
+                   block_idx_out=None, workspace=None, stream=None):
+    """One decode row per sequence; kv_lens [B] int32, page_table [B, max_pages] int32 (k, v then a page pool)."""
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = torch.empty(nsa_decode_workspace_size(shape, params, dt), dtype=torch.uint8, device=q.device)
+    max_pages = 0 if page_table is None else page_table.shape[1]
+    if page_table is not None and not num_pages:
+        num_pages = k.shape[0]
+    _check(lib().nsa_decode_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cmp), _ptr(v_cmp), _ptr(gates), _ptr(is_video),
+                                dt, ctypes.byref(shape), ctypes.byref(params), _ptr(kv_lens), _ptr(page_table),
+                                max_pages, num_pages, _ptr(out), _ptr(o_cmp), _ptr(o_slc), _ptr(o_swa),
+                                _ptr(block_idx_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def nsa_compress_append(k, v, w_k, w_v, k_cmp, v_cmp, kv_len, n_new, kv_lens=None, page_table=None, num_pages=0,
+                        cmp_block=32, cmp_stride=16, stream=None):
+    """Writes the compressed blocks completed by the last n_new tokens of every sequence."""
+    B, _, H, D = k_cmp.shape
+    max_pages = 0 if page_table is None else page_table.shape[1]
+    if page_table is not None and not num_pages:
+        num_pages = k.shape[0]
+    _check(lib().nsa_compress_append(_ptr(k), _ptr(v), _dtype_code(k), B, kv_len, H, D, _ptr(w_k), _ptr(w_v),
+                                     cmp_block, cmp_stride, _ptr(kv_lens), _ptr(page_table), max_pages, num_pages,
+                                     n_new, _ptr(k_cmp), _ptr(v_cmp), _stream(stream)))
+    return k_cmp, v_cmp

@@ -104,6 +104,7 @@ def normal(seed: int, shape, device="cpu", dtype=torch.float64, scale: float = 1
 # Workloads
 # ----------------------------------------------------------------------------
 STREAM_Q, STREAM_LATENT, STREAM_KNOISE, STREAM_V, STREAM_GATES, STREAM_PHI = 1, 2, 3, 4, 5, 6
+STREAM_LENS = 7
 
 
 @dataclasses.dataclass(frozen=True)
@@ -166,7 +167,17 @@ WORKLOADS: Dict[str, Workload] = {
                        q_start=65535, num_q_heads=28, num_kv_heads=4, head_dim=128, top_n=16,
                        window=512, frame_corr=True),
     "sweep": _prefill("sweep-128k-1pct-text", 5, "bf16", 131072, 28, 4, 128, 16, 512, 640, 640, True),
+    # 16 sequences of mixed lengths (decode_lengths) in a paged cache of 64K-token capacity
+    "decode_varlen": Workload(name="decode-varlen-paged-16x(4K..64K)", index=6, dtype="bf16", batch=16,
+                              kv_len=65536, q_len=1, q_start=65535, num_q_heads=28, num_kv_heads=4,
+                              head_dim=128, top_n=16, window=512, frame_corr=True),
 }
+
+
+def decode_lengths(wl: Workload, lo: int = 4096) -> List[int]:
+    """Per-sequence token counts of a variable-length decode batch: seeded, uniform in [lo, kv_len]."""
+    u = uniform(1000 * wl.index + STREAM_LENS, 0, wl.batch)
+    return [int(lo + math.floor(x * (wl.kv_len - lo + 1))) for x in u.tolist()]
 
 SWEEP_VARIANTS = [(n, w, g) for (n, w) in ((16, 512), (8, 256)) for g in ("sigmoid", "cmp", "slc")]
 

@@ -113,3 +113,50 @@ def test_other_entry_points_validate_first():
     # empty problems launch nothing and succeed
     e = _shape(q_len=0)
     assert L.nsa_topk_blocks(None, ctypes.byref(e), ctypes.byref(pr), None, None, None) == 0
+
+
+def _dshape(**kw):
+    d = dict(batch=2, q_len=1, kv_len=4096, q_start=0, num_q_heads=28, num_kv_heads=4, head_dim=128)
+    d.update(kw)
+    return nsa.make_shape(**d)
+
+
+def _decode(shape, params=None, dtype=nsa.NSA_BF16, ws=1 << 40, kc=FAKE, table=None, max_pages=0, num_pages=0):
+    L = nsa.lib()
+    pr = params or _params(top_n=16, window=512)
+    return L.nsa_decode_fwd(FAKE, FAKE, FAKE, kc, FAKE, FAKE, None, dtype, ctypes.byref(shape), ctypes.byref(pr),
+                            FAKE, table, max_pages, num_pages, FAKE, None, None, None, None, FAKE, ws, None)
+
+
+def test_decode_varlen_validates_first():
+    pr = _params(top_n=16, window=512)
+    need = nsa.nsa_decode_workspace_size(_dshape(), pr, nsa.NSA_BF16)
+    assert need > 0
+    assert nsa.nsa_decode_workspace_size(_dshape(), pr, nsa.NSA_F32) == 0
+    assert _decode(_dshape(q_len=2)) == nsa.NSA_ERR_INVALID_ARG
+    assert _decode(_dshape(), dtype=nsa.NSA_F32) == nsa.NSA_ERR_UNSUPPORTED
+    assert _decode(_dshape(head_dim=64)) == nsa.NSA_ERR_UNSUPPORTED
+    assert _decode(_dshape(kv_len=31)) == nsa.NSA_ERR_UNSUPPORTED          # no compressed block at capacity
+    assert _decode(_dshape(), kc=None) == nsa.NSA_ERR_INVALID_ARG
+    assert _decode(_dshape(), ws=need - 1) == nsa.NSA_ERR_WORKSPACE_TOO_SMALL
+    # a page table must cover the capacity and name a non-empty pool
+    assert _decode(_dshape(), table=FAKE, max_pages=63, num_pages=100) == nsa.NSA_ERR_INVALID_ARG
+    assert _decode(_dshape(), table=FAKE, max_pages=64, num_pages=0) == nsa.NSA_ERR_INVALID_ARG
+    assert "page" in nsa.last_error() or "num_pages" in nsa.last_error()
+    assert _decode(_dshape(batch=0)) == nsa.NSA_OK                       # empty batch launches nothing
+
+
+def test_compress_append_validates_first():
+    L = nsa.lib()
+
+    def call(dtype=nsa.NSA_BF16, D=128, n_new=1, table=None, max_pages=0, num_pages=0, k=FAKE):
+        return L.nsa_compress_append(k, FAKE, dtype, 2, 4096, 4, D, FAKE, FAKE, 32, 16, None, table, max_pages,
+                                     num_pages, n_new, FAKE, FAKE, None)
+
+    assert call(dtype=nsa.NSA_F32) == nsa.NSA_ERR_UNSUPPORTED
+    assert call(dtype=5) == nsa.NSA_ERR_INVALID_ARG
+    assert call(D=64) == nsa.NSA_ERR_UNSUPPORTED
+    assert call(n_new=-1) == nsa.NSA_ERR_INVALID_ARG
+    assert call(k=None) == nsa.NSA_ERR_INVALID_ARG
+    assert call(table=FAKE, max_pages=10, num_pages=8) == nsa.NSA_ERR_INVALID_ARG
+    assert call(n_new=0, k=None) == nsa.NSA_OK                            # nothing appended
