@@ -68,6 +68,7 @@ def lib():
         L.oracle_sparse_rows.argtypes = [_p, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _i64,
                                          _i64, _dbl, _p, _p]
         L.oracle_dense_rows.argtypes = [_p, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _dbl, _p, _p]
+        L.oracle_gate_proj.argtypes = [_p, _i64, _i64, _p, _i64, _p, _p]
         _lib = L
     return _lib
 
@@ -163,6 +164,19 @@ def dense_rows(q_rows, pos, k, v, scale: float):
     lse = np.zeros((R, Hq), dtype=np.float64)
     lib().oracle_dense_rows(_ptr(q_rows), _ptr(pos), R, _ptr(k), _ptr(v), T, Hq, Hkv, D, scale, _ptr(o), _ptr(lse))
     return o, lse
+
+
+def gate_proj(x, w, b=None) -> np.ndarray:
+    """Gate values g = 1 / (1 + exp(-(x w^T + b))) for x [R, K], w [N, K], b [N] -> [R, N] fp64
+    (column f = 3 h + c: head h, branch c in cmp, slc, swa order)."""
+    x = _f32(x)
+    w = _f32(w)
+    b = None if b is None else _f32(b)
+    R, K = x.shape
+    N = w.shape[0]
+    g = np.zeros((R, N), dtype=np.float64)
+    lib().oracle_gate_proj(_ptr(x), R, K, _ptr(w), N, _ptr(b), _ptr(g))
+    return g
 
 
 def layer(q, k, v, w_k, w_v, gates, is_video, params: Dict, q_start: int = 0,

@@ -335,3 +335,26 @@ void oracle_dense_rows(const float* q, const int64_t* pos, int64_t R, const floa
     free(z);
   }
 }
+
+/*
+ * Gate values of the three branches from a token's hidden state (top168.com
+ * digest, section 一: a learned weighting mixes the branches per head;
+ * "VideoNSA：重新定义视频理解的稀疏注意力机制", section 3.1: three gate values
+ * per head come from the token's features).  Plain per-token reading: a
+ * linear map of the hidden state followed by the logistic function,
+ *   z[t][f] = b[f] + sum_k x[t][k] * w[f][k],   g[t][f] = 1 / (1 + exp(-z)),
+ * for f = 3 h + c (head h, branch c in cmp, slc, swa order).  The pages'
+ * pooled, softmax-normalised gate network is not followed.
+ *   x [R, K], w [N, K], b [N] or NULL, g [R, N] (fp64).
+ */
+void oracle_gate_proj(const float* x, int64_t R, int64_t K, const float* w, int64_t N, const float* b,
+                      double* g) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < R; ++r) {
+    for (int64_t f = 0; f < N; ++f) {
+      double z = b ? (double)b[f] : 0.0;
+      for (int64_t k = 0; k < K; ++k) z += (double)x[r * K + k] * (double)w[f * K + k];
+      g[r * N + f] = 1.0 / (1.0 + exp(-z));
+    }
+  }
+}

@@ -345,3 +345,45 @@ def test_pair_counts_against_key_lists_and_page_identity():
         sel = set(idx[t, 0][idx[t, 0] >= 0].tolist())
         nslc += sum(1 for x in range(t + 1) if x // 16 in sel)
     assert c["slc"] == 2 * nslc
+
+
+def _logit(g):
+    return np.log(g) - np.log1p(-g)
+
+
+def test_gate_proj_closed_forms():
+    """Gate projection: x = 0 gives the logistic of the bias at exactly known points; a permutation
+    (one-hot) weight reads one hidden channel per gate; a rank-1 weight gives u_f (x . v); the
+    logistic is odd about 1/2; the logit is linear in x."""
+    rng = np.random.default_rng(7)
+    R, K, N = 5, 67, 12
+    b = np.array([0.0, math.log(3), -math.log(3), math.log(9)] * 3, dtype=np.float32)
+    g0 = oracle.gate_proj(np.zeros((R, K), np.float32), rng.standard_normal((N, K)).astype(np.float32), b)
+    want = np.array([0.5, 0.75, 0.25, 0.9] * 3)
+    assert np.allclose(g0, want[None, :], atol=1e-6, rtol=0)   # b rounded to float: ~1e-8
+    x = rng.standard_normal((R, K)).astype(np.float32)
+    perm = rng.permutation(K)[:N]
+    w1 = np.zeros((N, K), np.float32)
+    w1[np.arange(N), perm] = 1.0
+    bb = rng.standard_normal(N).astype(np.float32)
+    g1 = oracle.gate_proj(x, w1, bb)
+    assert np.allclose(_logit(g1), x[:, perm].astype(np.float64) + bb, atol=1e-9)
+    assert g1.shape == (R, N)
+    u = rng.standard_normal(N).astype(np.float32)
+    v = rng.standard_normal(K).astype(np.float32)
+    w2 = (u[:, None].astype(np.float64) * v[None, :]).astype(np.float32)
+    g2 = oracle.gate_proj(x, w2)
+    xv = x.astype(np.float64) @ v.astype(np.float64)
+    assert np.allclose(_logit(g2), xv[:, None] * u[None, :], atol=1e-4)   # w2 rounded to float
+    w = (rng.standard_normal((N, K)) / math.sqrt(K)).astype(np.float32)
+    gp, gm = oracle.gate_proj(x, w), oracle.gate_proj(-x, w)
+    assert np.allclose(gp + gm, 1.0, atol=1e-12)
+    # multiples of 2^-10 below 8 in magnitude: their float sums are exact
+    xa = (np.round(rng.standard_normal((R, K)) * 1024) / 1024).astype(np.float32)
+    xb = (np.round(rng.standard_normal((R, K)) * 1024) / 1024).astype(np.float32)
+    s = xa + xb
+    assert np.array_equal(s.astype(np.float64), xa.astype(np.float64) + xb)
+    lin = _logit(oracle.gate_proj(s, w, bb)) - _logit(oracle.gate_proj(xa, w, bb)) - _logit(
+        oracle.gate_proj(xb, w, bb)) + bb
+    assert np.allclose(lin, 0.0, atol=1e-9)
+    assert np.all((g1 > 0) & (g1 < 1))
