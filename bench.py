@@ -69,6 +69,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-phase timing pass")
     ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--no-gate-proj", action="store_true", help="skip the gate projection measurement")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the variable-length paged decode measurement")
     ap.add_argument("--cpu-sample-rows", type=int, default=0, help="oracle row sample (0: auto)")
@@ -481,6 +482,31 @@ def decode_varlen(args):
                 rotating_pools=n_rot, steps=args.decode_steps)
 
 
+def gate_proj(args, wl):
+    """Gate projection in front of the layer: sigmoid(x w_g^T + b) for every token of the workload,
+    x [1, T, 3584] bf16 hidden states (Qwen2.5-VL-7B), w_g [3 Hq, 3584]; HBM-bound on x."""
+    import torch
+    from sparse_attention_long_fwd_amd import nsa, synth
+
+    gi = synth.make_gate_inputs(wl, "cuda")
+    g = torch.empty(wl.batch, wl.q_len, wl.num_q_heads, 3, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        nsa.nsa_gate_proj(gi["x"], gi["w_g"], gi["b_g"], gates=g, stream=stream)
+
+    for _ in range(3):
+        step()
+    ms = time_calls(step, max(20, args.steps), stream)
+    byts = gi["x"].numel() * 2 + gi["w_g"].numel() * 2 + gi["b_g"].numel() * 4 + g.numel() * 4
+    flops = 2.0 * gi["x"].numel() * gi["w_g"].shape[0]
+    bw = byts / (ms * 1e-3)
+    del gi, g
+    return dict(workload="%s hidden=%d" % (wl.name, synth.HIDDEN), ms_per_call=ms, algo_bytes=byts,
+                gbps=bw / 1e9, hbm_frac=bw / PEAK_HBM, tflops=flops / (ms * 1e-3) / 1e12,
+                roofline=dict(bound="hbm", achieved=bw / 1e9, peak=PEAK_HBM / 1e9, unit="GB/s", frac=bw / PEAK_HBM))
+
+
 def cpu_baseline(args, wl, inp):
     """The fp64 oracle on a bounded row sample of the same prefill (rank 0)."""
     import torch
@@ -561,6 +587,11 @@ def main():
         cpu = cpu_baseline(args, wl, inp)
     del inp
     torch.cuda.empty_cache()
+    gp = None
+    if not args.no_gate_proj:
+        log("gate projection")
+        gp = gate_proj(args, wl)
+        torch.cuda.empty_cache()
     dec = None
     if not args.no_decode:
         log("decode")
@@ -592,6 +623,7 @@ def main():
         "kernels": ker,
         "roofline": roofline,
         "decode": dec,
+        "gate_proj": gp,
         "cpu_baseline": cpu,
         "counters": kernel_counters(),
     }

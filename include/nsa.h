@@ -232,6 +232,23 @@ int32_t nsa_compress_append(const void* k, const void* v, int32_t dtype, int64_t
                             int32_t max_pages, int64_t num_pages, int32_t n_new, void* k_cmp, void* v_cmp,
                             void* stream);
 
+/*
+ * nsa_gate_proj -- the per-head branch gates from each token's hidden state,
+ * computed in front of the layer ([B] section 一: a learned weighting mixes
+ * the three branches per head; [C] section 3.1: three gate values per head
+ * from the token's features).  Plain per-token reading, a linear map followed
+ * by the logistic function:
+ *   gates[b, t, h, c] = 1 / (1 + exp(-(b_g[f] + sum_k x[b, t, k] * w_g[f, k]))),
+ *   f = 3 h + c, c = 0 (cmp), 1 (slc), 2 (swa)
+ * x [B, seq_len, hidden] (dtype), w_g [3 * num_q_heads, hidden] (dtype, the
+ * weight of a linear layer), b_g [3 * num_q_heads] fp32 or NULL (no bias),
+ * gates [B, seq_len, num_q_heads, 3] fp32 -- the gates argument of the layer.
+ * Products are accumulated in fp32.  Covers bf16 with hidden a multiple of 64
+ * and num_q_heads <= 32 (else NSA_ERR_UNSUPPORTED).
+ */
+int32_t nsa_gate_proj(const void* x, const void* w_g, const float* b_g, int32_t dtype, int64_t batch,
+                      int64_t seq_len, int32_t hidden, int32_t num_q_heads, float* gates, void* stream);
+
 /* Debug / test switch: 1 forces the generic (non-MFMA) kernels, 0 restores the
  * default dispatch.  Returns the previous value.  Process-wide. */
 int32_t nsa_set_force_generic(int32_t on);

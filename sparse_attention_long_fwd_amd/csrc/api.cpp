@@ -535,4 +535,23 @@ int32_t nsa_compress_append(const void* k, const void* v, int32_t dtype, int64_t
   return NSA_OK;
 }
 
+int32_t nsa_gate_proj(const void* x, const void* w_g, const float* b_g, int32_t dtype, int64_t batch,
+                      int64_t seq_len, int32_t hidden, int32_t num_q_heads, float* gates, void* stream) {
+  g_err[0] = 0;
+  if (dtype != NSA_F32 && dtype != NSA_BF16) return fail(NSA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (batch < 0 || seq_len < 0 || hidden <= 0 || num_q_heads <= 0)
+    return fail(NSA_ERR_INVALID_ARG, "sizes must be positive (batch, seq_len >= 0)");
+  const int N = 3 * num_q_heads;
+  if (dtype != NSA_BF16 || !gate_proj_supported(hidden, N))
+    return fail(NSA_ERR_UNSUPPORTED, "gate projection covers bf16, hidden a multiple of 64, num_q_heads <= 32");
+  const int64_t R = batch * seq_len;
+  if (R == 0) return NSA_OK;
+  if (!x || !w_g || !gates) return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(x) || !aligned16(w_g) || !aligned16(gates))
+    return fail(NSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  hipError_t e = launch_gate_proj(x, w_g, b_g, gates, R, hidden, N, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "gate projection kernel");
+  return NSA_OK;
+}
+
 }  // extern "C"

@@ -44,6 +44,11 @@ hipError_t launch_flash_fast(const Dims& dm, const void* q, const void* k, const
                              float* swa32, void* swa_bf, void* text, void* ws, hipStream_t s);
 size_t flash_workspace(const Dims& dm);
 
+// Gate values g = sigmoid(x w^T + b): x [R, K] bf16, w [N, K] bf16, b [N] fp32 or null, g [R, N] fp32.
+bool gate_proj_supported(int64_t K, int N);
+hipError_t launch_gate_proj(const void* x, const void* w, const float* bias, float* g, int64_t R, int64_t K, int N,
+                            hipStream_t s);
+
 // Decode path (one query row per sequence, split over the compressed keys).
 // Variable-length batches: lens[b] tokens in sequence b (the query at lens[b] - 1), dm.T the
 // capacity; pages (optional) maps 64-token page i of sequence b to pool page pages[b * max_pages

@@ -61,6 +61,7 @@ EXPORTS = {
                               _P, _SZ, _P]),
     "nsa_compress_append": (_I32, [_P, _P, _I32, _I64, _I64, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _I32, _I64,
                                    _I32, _P, _P, _P]),
+    "nsa_gate_proj": (_I32, [_P, _P, _P, _I32, _I64, _I64, _I32, _I32, _P, _P]),
     "nsa_set_force_generic": (_I32, [_I32]),
     "nsa_profile_enable": (_I32, [_I32]),
     "nsa_profile_read": (_I32, [ctypes.POINTER(ctypes.c_float), _I32]),
@@ -269,3 +270,14 @@ def nsa_compress_append(k, v, w_k, w_v, k_cmp, v_cmp, kv_len, n_new, kv_lens=Non
                                      cmp_block, cmp_stride, _ptr(kv_lens), _ptr(page_table), max_pages, num_pages,
                                      n_new, _ptr(k_cmp), _ptr(v_cmp), _stream(stream)))
     return k_cmp, v_cmp
+
+
+def nsa_gate_proj(x, w_g, b_g=None, gates=None, stream=None):
+    """Branch gates [B, T, Hq, 3] (fp32) from hidden states x [B, T, hidden] and w_g [3 Hq, hidden]."""
+    B, T, K = x.shape
+    Hq = w_g.shape[0] // 3
+    if gates is None:
+        gates = torch.empty(B, T, Hq, 3, dtype=torch.float32, device=x.device)
+    _check(lib().nsa_gate_proj(_ptr(x), _ptr(w_g), _ptr(b_g), _dtype_code(x), B, T, K, Hq, _ptr(gates),
+                               _stream(stream)))
+    return gates

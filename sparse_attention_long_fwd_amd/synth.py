@@ -105,6 +105,8 @@ def normal(seed: int, shape, device="cpu", dtype=torch.float64, scale: float = 1
 # ----------------------------------------------------------------------------
 STREAM_Q, STREAM_LATENT, STREAM_KNOISE, STREAM_V, STREAM_GATES, STREAM_PHI = 1, 2, 3, 4, 5, 6
 STREAM_LENS = 7
+STREAM_HIDDEN, STREAM_WG, STREAM_BG = 8, 9, 10
+HIDDEN = 3584  # hidden size of the Qwen2.5-VL-7B language model
 
 
 @dataclasses.dataclass(frozen=True)
@@ -228,6 +230,22 @@ def make_inputs(wl: Workload, device="cpu", batch_offset: int = 0) -> Dict[str, 
     w = normal(base + STREAM_PHI, (wl.cmp_block,), device, scale=1.0 / math.sqrt(wl.cmp_block))
     w = w.to(torch.float32)
     return dict(q=q, k=k, v=v, gates=g, w_k=w, w_v=w.clone(), is_video=video_mask(wl, device))
+
+
+def make_gate_inputs(wl: Workload, device="cpu", hidden: int = HIDDEN, batch_offset: int = 0
+                     ) -> Dict[str, torch.Tensor]:
+    """Inputs of the gate projection for the query rows of a workload: hidden states x [B, q_len,
+    hidden] ~ N(0, 1), weight w_g [3 Hq, hidden] ~ N(0, 1/hidden) (both rounded to the workload's
+    dtype) and bias b_g [3 Hq] ~ N(0, 1/4) in fp32, so that the gate logits are about N(0, 1.25)."""
+    dt = wl.torch_dtype
+    B, Tq, N = wl.batch, wl.q_len, 3 * wl.num_q_heads
+    base = 1000 * wl.index
+    x = torch.empty(B, Tq, hidden, dtype=dt, device=device)
+    for b in range(B):
+        normal(base + 100 * (b + batch_offset) + STREAM_HIDDEN, (Tq, hidden), device, out=x[b])
+    w = normal(base + STREAM_WG, (N, hidden), device, scale=1.0 / math.sqrt(hidden)).to(dt)
+    bias = normal(base + STREAM_BG, (N,), device, scale=0.5).to(torch.float32)
+    return dict(x=x, w_g=w, b_g=bias)
 
 
 def small(wl: Workload, **kw) -> Workload:

@@ -160,3 +160,19 @@ def test_compress_append_validates_first():
     assert call(k=None) == nsa.NSA_ERR_INVALID_ARG
     assert call(table=FAKE, max_pages=10, num_pages=8) == nsa.NSA_ERR_INVALID_ARG
     assert call(n_new=0, k=None) == nsa.NSA_OK                            # nothing appended
+
+
+def test_gate_proj_validates_first():
+    L = nsa.lib()
+
+    def call(dtype=nsa.NSA_BF16, hidden=3584, hq=28, x=FAKE, batch=1, seq=100):
+        return L.nsa_gate_proj(x, FAKE, None, dtype, batch, seq, hidden, hq, FAKE, None)
+
+    assert call(dtype=nsa.NSA_F32) == nsa.NSA_ERR_UNSUPPORTED
+    assert call(dtype=3) == nsa.NSA_ERR_INVALID_ARG
+    assert call(hidden=100) == nsa.NSA_ERR_UNSUPPORTED     # not a multiple of 64
+    assert call(hq=33) == nsa.NSA_ERR_UNSUPPORTED          # more than 96 gate outputs
+    assert call(hq=0) == nsa.NSA_ERR_INVALID_ARG
+    assert call(x=None) == nsa.NSA_ERR_INVALID_ARG
+    assert call(x=FAKE + 8) == nsa.NSA_ERR_INVALID_ARG     # misaligned
+    assert call(x=None, seq=0) == nsa.NSA_OK               # no tokens: nothing launched
