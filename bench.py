@@ -50,6 +50,8 @@ COUNTER_KERNELS = {
                          "sparse_attention_long_fwd_amd/csrc/topk_wave.hpp"],
     "dsel_kernel": ["sparse_attention_long_fwd_amd/csrc/decode_fast.hip",
                     "sparse_attention_long_fwd_amd/csrc/topk_wave.hpp"],
+    "gate_proj_kernel": ["sparse_attention_long_fwd_amd/csrc/gate_proj.hip",
+                         "sparse_attention_long_fwd_amd/csrc/mfma.hpp"],
 }
 SIMDS_PER_XCD = 32 * 4  # GRBM_GUI_ACTIVE sums core cycles over the 8 XCDs
 COPY_PROBE_BYTES = 1 << 30
