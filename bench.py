@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-phase timing pass")
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-gate-proj", action="store_true", help="skip the gate projection measurement")
+    ap.add_argument("--no-budget-sweep", action="store_true",
+                    help="skip the fixed-budget (top-n, window) performance surface")
+    ap.add_argument("--sweep-steps", type=int, default=5, help="timed steps per budget point")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the variable-length paged decode measurement")
     ap.add_argument("--cpu-sample-rows", type=int, default=0, help="oracle row sample (0: auto)")
@@ -80,8 +83,8 @@ def parse():
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc output directories "
                          "(FETCH_SIZE, then WRITE_SIZE) of a --copy-probe run, and exit")
-    ap.add_argument("--record-counters", nargs=3, metavar=("MFMA_DIR", "EA_READ_DIR", "EA_WRITE_DIR"),
-                    help="write profiles/counters.json from three rocprofv3 --pmc output directories "
+    ap.add_argument("--record-counters", nargs=3, metavar=("MFMA_DIRS", "EA_READ_DIRS", "EA_WRITE_DIRS"),
+                    help="write profiles/counters.json from rocprofv3 --pmc output directories (comma-separated runs) "
                          "(SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA GRBM_GUI_ACTIVE; TCC_EA0_RDREQ_*; "
                          "TCC_EA0_WRREQ_*), and exit")
     return ap.parse_args()
@@ -154,20 +157,21 @@ def record_counters(mfma_dir, ea_r_dir, ea_w_dir):
     import csv
     import glob
 
-    def read(d):
-        path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+    def read(dirs):  # comma-separated output directories of separate runs
         per = {}
-        for r in csv.DictReader(open(path)):
-            key = (r["Dispatch_Id"], r["Kernel_Name"])
-            c = per.setdefault(key, {})
-            c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        for i, d in enumerate(dirs.split(",")):
+            path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+            for r in csv.DictReader(open(path)):
+                key = (i, r["Dispatch_Id"], r["Kernel_Name"])
+                c = per.setdefault(key, {})
+                c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
         return per
 
     out = {}
     for frag, srcs in COUNTER_KERNELS.items():
         rec = {"sources": srcs, "sha256": sources_sha(srcs)}
         for d, kind in ((mfma_dir, "mfma"), (ea_r_dir, "read"), (ea_w_dir, "write")):
-            vals = [c for (_, name), c in read(d).items() if frag in name]
+            vals = [c for (_, _, name), c in read(d).items() if frag in name]
             if not vals:
                 continue
             n = len(vals)
@@ -183,7 +187,8 @@ def record_counters(mfma_dir, ea_r_dir, ea_w_dir):
                 w64 = tot["TCC_EA0_WRREQ_64B_sum"]
                 rec["mem_write_bytes"] = 64 * w64 + 32 * (tot["TCC_EA0_WRREQ_sum"] - w64)
             rec["dispatches_" + kind] = n
-        out[frag] = rec
+        if len(rec) > 2:  # counters were found for it
+            out[frag] = rec
     with open(COUNTERS_FILE, "w") as fh:
         json.dump(out, fh, indent=1, sort_keys=True)
         fh.write("\n")
@@ -314,6 +319,53 @@ def prefill(args, wl):
         res["kernels"] = phase_rates(wl, list(acc / args.steps))
     del ws
     return res, inp
+
+
+BUDGET = 16 * 64 + 512   # tokens each video row attends in the selection + window branches
+BUDGET_POINTS = [(8, 1024), (12, 768), (16, 512), (20, 256), (22, 128), (23, 64)]
+
+
+def budget_sweep(args, wl, inp):
+    """Performance surface of the selection / window split at a fixed budget: top-n blocks of 64
+    tokens plus a window of w tokens with 64 n + w = 1536, on the same 128K inputs; per point the
+    step time, tokens/s, algorithmic FLOP rate and the library's phase times."""
+    import torch
+    from sparse_attention_long_fwd_amd import accounting, nsa
+
+    stream = torch.cuda.current_stream()
+    q, k, v, g, vid = inp["q"], inp["k"], inp["v"], inp["gates"], inp["is_video"]
+    B, Tq, Hq, D = q.shape
+    sh = nsa.make_shape(B, Tq, wl.kv_len, wl.q_start, Hq, k.shape[2], D)
+    out = torch.empty_like(q)
+    pts = []
+    for n, w in BUDGET_POINTS:
+        assert 64 * n + w == BUDGET
+        wv = wl.with_(top_n=n, window=w)
+        pr = nsa.make_params(**wv.params())
+        ws = torch.empty(nsa.nsa_hybrid_layer_workspace_size(sh, pr, nsa.NSA_BF16), dtype=torch.uint8,
+                         device="cuda")
+
+        def step():
+            nsa.nsa_hybrid_layer_fwd(q, k, v, g, sh, pr, w_k=inp["w_k"], w_v=inp["w_v"], is_video=vid, out=out,
+                                     workspace=ws, stream=stream)
+
+        for _ in range(2):
+            step()
+        ms = time_calls(step, args.sweep_steps, stream)
+        nsa.profile_enable(True)
+        acc = None
+        for _ in range(args.sweep_steps):
+            step()
+            ph = np.array(nsa.profile_read())
+            acc = ph if acc is None else acc + ph
+        nsa.profile_enable(False)
+        fl = accounting.flops(wv)["total"]
+        pts.append(dict(top_n=n, window=w, ms_per_step=ms, tokens_per_s=Tq * B / (ms * 1e-3),
+                        algo_tflops=fl / (ms * 1e-3) / 1e12,
+                        phase_ms={name: round(float(x), 4) for name, x in zip(nsa.PHASES, acc / args.sweep_steps)}))
+        log("budget point n=%d w=%d: %.2f ms" % (n, w, ms))
+        del ws
+    return dict(workload=wl.name, budget_tokens=BUDGET, sel_block=64, points=pts)
 
 
 def decode(args):
@@ -583,6 +635,10 @@ def main():
             roofline = dict(kernel=dom_name, bound="mfma", achieved=dom["tflops"], peak=PEAK_BF16_MFMA / 1e12,
                             unit="TFLOP/s", frac=dom["tflops"] * 1e12 / PEAK_BF16_MFMA,
                             traffic=kernel_traffic(dom_name))
+    sweep = None
+    if not args.no_budget_sweep and wl.name == synth.WORKLOADS["128k"].name:
+        log("budget sweep")
+        sweep = budget_sweep(args, wl, inp)
     cpu = None
     if not args.no_cpu_baseline:
         log("oracle timing")
@@ -626,6 +682,7 @@ def main():
         "roofline": roofline,
         "decode": dec,
         "gate_proj": gp,
+        "budget_sweep": sweep,
         "cpu_baseline": cpu,
         "counters": kernel_counters(),
     }

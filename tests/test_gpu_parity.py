@@ -323,6 +323,17 @@ def test_layer_sweep_sampled(variant):
     compare_layer(wl, inp, got, rows)
 
 
+@pytest.mark.parametrize("n,w", [(8, 1024), (23, 64)])
+def test_layer_budget_points_sampled(n, w):
+    """The ends of the fixed-budget (64 n + w = 1536) performance surface at 128K."""
+    wl = synth.WORKLOADS["128k"].with_(top_n=n, window=w)
+    flush("budget point n=%d w=%d" % (n, w))
+    inp = synth.make_inputs(wl, DEV)
+    got = run_layer(wl, inp)
+    rows = _sample_rows(wl, seed=n, text=4, edge=16)[::3]
+    compare_layer(wl, inp, got, rows)
+
+
 def test_decode_with_compressed_cache():
     wl = synth.WORKLOADS["decode"]
     flush("decode B=%d L=%d" % (wl.batch, wl.kv_len))
