@@ -75,6 +75,7 @@ def parse():
     ap.add_argument("--no-budget-sweep", action="store_true",
                     help="skip the fixed-budget (top-n, window) performance surface")
     ap.add_argument("--sweep-steps", type=int, default=5, help="timed steps per budget point")
+    ap.add_argument("--no-branch-kv", action="store_true", help="skip the per-branch K/V prefill measurement")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the variable-length paged decode measurement")
     ap.add_argument("--cpu-sample-rows", type=int, default=0, help="oracle row sample (0: auto)")
@@ -368,6 +369,37 @@ def budget_sweep(args, wl, inp):
     return dict(workload=wl.name, budget_tokens=BUDGET, sel_block=64, points=pts)
 
 
+def branch_kv(args, wl, inp):
+    """The same 128K prefill with independent keys / values per branch (compression, selection,
+    window + text rows): three K/V pairs in HBM, the same kernels."""
+    import torch
+    from sparse_attention_long_fwd_amd import nsa, synth
+
+    stream = torch.cuda.current_stream()
+    kv = {}
+    for tag, off in (("s", 40), ("w", 80)):
+        other = synth.make_inputs(wl, "cuda", batch_offset=off)
+        kv[tag] = (other["k"], other["v"])
+        del other
+    q = inp["q"]
+    B, Tq, Hq, D = q.shape
+    sh = nsa.make_shape(B, Tq, wl.kv_len, wl.q_start, Hq, inp["k"].shape[2], D)
+    pr = nsa.make_params(**wl.params())
+    ws = torch.empty(nsa.nsa_hybrid_layer_workspace_size(sh, pr, nsa.NSA_BF16), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+
+    def step():
+        nsa.nsa_hybrid_layer_fwd_branch_kv(q, (inp["k"], inp["v"]), kv["s"], kv["w"], inp["gates"], sh, pr,
+                                           w_k=inp["w_k"], w_v=inp["w_v"], is_video=inp["is_video"], out=out,
+                                           workspace=ws, stream=stream)
+
+    for _ in range(2):
+        step()
+    ms = time_calls(step, args.sweep_steps, stream)
+    del ws, kv
+    return dict(workload=wl.name, ms_per_step=ms, tokens_per_s=Tq * B / (ms * 1e-3), steps=args.sweep_steps)
+
+
 def decode(args):
     """16 x 64K decode step, rotating over 4 independent caches."""
     import torch
@@ -639,6 +671,10 @@ def main():
     if not args.no_budget_sweep and wl.name == synth.WORKLOADS["128k"].name:
         log("budget sweep")
         sweep = budget_sweep(args, wl, inp)
+    bkv = None
+    if not args.no_branch_kv:
+        log("keys / values per branch")
+        bkv = branch_kv(args, wl, inp)
     cpu = None
     if not args.no_cpu_baseline:
         log("oracle timing")
@@ -683,6 +719,7 @@ def main():
         "decode": dec,
         "gate_proj": gp,
         "budget_sweep": sweep,
+        "branch_kv": bkv,
         "cpu_baseline": cpu,
         "counters": kernel_counters(),
     }

@@ -249,6 +249,27 @@ int32_t nsa_compress_append(const void* k, const void* v, int32_t dtype, int64_t
 int32_t nsa_gate_proj(const void* x, const void* w_g, const float* b_g, int32_t dtype, int64_t batch,
                       int64_t seq_len, int32_t hidden, int32_t num_q_heads, float* gates, void* stream);
 
+/*
+ * nsa_hybrid_layer_fwd_branch_kv -- the same layer with independent keys and
+ * values per branch, as in Native Sparse Attention, where each branch has its
+ * own key/value projections ([B] section 一 names three separate branches;
+ * [C] section 2.2).  k_c / v_c feed the compression (ignored when k_cmp_in /
+ * v_cmp_in are given), k_s / v_s the selection branch, k_w / v_w the
+ * sliding-window branch and the dense attention of text rows; the block
+ * importance still comes from the compression branch.  All six are
+ * [B, kv_len, Hkv, D]; they may alias each other (all equal gives
+ * nsa_hybrid_layer_fwd).  Workspace as nsa_hybrid_layer_workspace_size().
+ * One query row per sequence (decode shapes on the MFMA path) needs
+ * k_s == k_w and v_s == v_w (else NSA_ERR_UNSUPPORTED).
+ */
+int32_t nsa_hybrid_layer_fwd_branch_kv(const void* q, const void* k_c, const void* v_c, const void* k_s,
+                                       const void* v_s, const void* k_w, const void* v_w, const void* k_cmp_in,
+                                       const void* v_cmp_in, const float* w_k, const float* w_v,
+                                       const float* gates, const uint8_t* is_video, int32_t dtype,
+                                       const nsa_shape* shape, const nsa_params* params, void* out, void* o_cmp,
+                                       void* o_slc, void* o_swa, int32_t* block_idx_out, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
 /* Debug / test switch: 1 forces the generic (non-MFMA) kernels, 0 restores the
  * default dispatch.  Returns the previous value.  Process-wide. */
 int32_t nsa_set_force_generic(int32_t on);

@@ -180,13 +180,16 @@ def gate_proj(x, w, b=None) -> np.ndarray:
 
 
 def layer(q, k, v, w_k, w_v, gates, is_video, params: Dict, q_start: int = 0,
-          rows: Optional[np.ndarray] = None, kc=None, vc=None) -> Dict[str, np.ndarray]:
+          rows: Optional[np.ndarray] = None, kc=None, vc=None, kv_slc=None, kv_swa=None) -> Dict[str, np.ndarray]:
     """The hybrid layer for one batch element.
 
     q [Tq, Hq, D], k/v [T, Hkv, D], gates [Tq, Hq, 3], is_video [Tq]; row r of q
     sits at absolute position q_start + r.  ``rows`` picks a subset of q's rows
     (default: all).  ``kc``/``vc`` replace the compression of k/v when given (a
-    precomputed compressed cache).  Returns fp64 arrays over the chosen rows:
+    precomputed compressed cache).  ``kv_slc`` / ``kv_swa`` give the selection
+    branch, and the window branch with the text rows, keys and values of their
+    own (Native Sparse Attention's per-branch projections); by default all
+    branches share k/v.  Returns fp64 arrays over the chosen rows:
     o_cmp, lse_cmp, imp, idx, gap, o_slc, o_swa (video rows; zero for text rows)
     and out (gated sum for video rows, dense causal attention for text rows).
     """
@@ -215,13 +218,17 @@ def layer(q, k, v, w_k, w_v, gates, is_video, params: Dict, q_start: int = 0,
     if vr.size:
         o_cmp, lse, imp = cmp_rows(q_rows[vr], pos[vr], kc, vc, Hq, l, d, ls, T, scale)
         idx, gap = topk_rows(imp, pos[vr], ls, n, n_init, n_local)
-        o_slc, o_swa = sparse_rows(q_rows[vr], pos[vr], k, v, idx, ls, w, scale)
+        ks, vs = kv_slc if kv_slc is not None else (k, v)
+        kw, vw = kv_swa if kv_swa is not None else (k, v)
+        o_slc, _ = sparse_rows(q_rows[vr], pos[vr], ks, vs, idx, ls, w, scale, swa=False)
+        _, o_swa = sparse_rows(q_rows[vr], pos[vr], kw, vw, idx, ls, w, scale, slc=False)
         g = np.asarray(gates, dtype=np.float64)[rows[vr]]
         res["o_cmp"][vr], res["lse_cmp"][vr], res["imp"][vr] = o_cmp, lse, imp
         res["idx"][vr], res["gap"][vr] = idx, gap
         res["o_slc"][vr], res["o_swa"][vr] = o_slc, o_swa
         res["out"][vr] = g[..., 0:1] * o_cmp + g[..., 1:2] * o_slc + g[..., 2:3] * o_swa
     if tr.size:
-        res["out"][tr], _ = dense_rows(q_rows[tr], pos[tr], k, v, scale)
+        kw, vw = kv_swa if kv_swa is not None else (k, v)
+        res["out"][tr], _ = dense_rows(q_rows[tr], pos[tr], kw, vw, scale)
     res["kc"], res["vc"] = kc, vc
     return res

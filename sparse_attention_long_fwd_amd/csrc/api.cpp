@@ -161,13 +161,21 @@ int run_cmp(int32_t dtype, int32_t cdtype, const Dims& dm, const void* q, const 
   return NSA_OK;
 }
 
-int run_sparse(int32_t dtype, const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
+// Keys and values of each branch: the compression branch compresses (kc, vc); the selection
+// branch reads (ks, vs); the window branch and the text rows read (kw, vw).
+struct BranchKV {
+  const void *kc, *vc, *ks, *vs, *kw, *vw;
+  bool shared() const { return kc == ks && ks == kw && vc == vs && vs == vw; }
+};
+
+int run_sparse(int32_t dtype, const Dims& dm, const void* q, const BranchKV& kv, const int32_t* idx,
                const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out, void* o_slc,
                void* o_swa, void* ws, hipStream_t s) {
   hipError_t e = use_fast(dtype, dm)
-                     ? launch_sparse_fast(dm, q, k, v, idx, vid, o_cmp, ocmp_f32, gates, out, o_slc, o_swa, ws, s,
-                                          prof_mark)
-                     : launch_sparse_generic(dtype, dm, q, k, v, idx, vid, o_cmp, gates, out, o_slc, o_swa, s);
+                     ? launch_sparse_fast(dm, q, kv.ks, kv.vs, kv.kw, kv.vw, idx, vid, o_cmp, ocmp_f32, gates, out,
+                                          o_slc, o_swa, ws, s, prof_mark)
+                     : launch_sparse_generic(dtype, dm, q, kv.ks, kv.vs, kv.kw, kv.vw, idx, vid, o_cmp, gates, out,
+                                             o_slc, o_swa, s);
   if (e != hipSuccess) return hip_fail(e, "selection/window kernel");
   return NSA_OK;
 }
@@ -311,7 +319,8 @@ int32_t nsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t
   if (fast && workspace_bytes < w.total)
     return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, w.total);
   if (fast && w.total > 0 && !workspace) return fail(NSA_ERR_INVALID_ARG, "NULL workspace");
-  return run_sparse(dtype, dm, q, k, v, block_idx, is_video, o_cmp, false, gates, out, o_slc, o_swa, workspace,
+  return run_sparse(dtype, dm, q, BranchKV{k, v, k, v, k, v}, block_idx, is_video, o_cmp, false, gates, out, o_slc,
+                    o_swa, workspace,
                     (hipStream_t)stream);
 }
 
@@ -321,11 +330,15 @@ size_t nsa_hybrid_layer_workspace_size(const nsa_shape* shape, const nsa_params*
   return layer_ws(dm, dtype).total;
 }
 
-int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const void* k_cmp_in,
-                             const void* v_cmp_in, const float* w_k, const float* w_v, const float* gates,
-                             const uint8_t* is_video, int32_t dtype, const nsa_shape* shape,
-                             const nsa_params* params, void* out, void* o_cmp, void* o_slc, void* o_swa,
-                             int32_t* block_idx_out, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The whole layer (nsa_hybrid_layer_fwd and its per-branch K/V form).
+int32_t layer_fwd(const void* q, const BranchKV& kv, const void* k_cmp_in, const void* v_cmp_in,
+                  const float* w_k, const float* w_v, const float* gates, const uint8_t* is_video, int32_t dtype,
+                  const nsa_shape* shape, const nsa_params* params, void* out, void* o_cmp, void* o_slc,
+                  void* o_swa, int32_t* block_idx_out, void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   Dims dm;
   int st = check_dims(shape, params, dtype, &dm, true);
@@ -334,12 +347,16 @@ int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const 
   if ((k_cmp_in == nullptr) != (v_cmp_in == nullptr))
     return fail(NSA_ERR_INVALID_ARG, "give both k_cmp_in and v_cmp_in, or neither");
   if (dm.B == 0 || dm.Tq == 0) return NSA_OK;
-  if (!q || !k || !v || !gates) return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!q || !kv.kc || !kv.vc || !kv.ks || !kv.vs || !kv.kw || !kv.vw || !gates)
+    return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (!k_cmp_in && dm.Nc > 0 && (!w_k || !w_v)) return fail(NSA_ERR_INVALID_ARG, "NULL compression weights");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(o_cmp) ||
-      !aligned16(o_slc) || !aligned16(o_swa) || !aligned16(k_cmp_in) || !aligned16(v_cmp_in) ||
-      !aligned16(workspace))
+  if (!aligned16(q) || !aligned16(kv.kc) || !aligned16(kv.vc) || !aligned16(kv.ks) || !aligned16(kv.vs) ||
+      !aligned16(kv.kw) || !aligned16(kv.vw) || !aligned16(out) || !aligned16(o_cmp) || !aligned16(o_slc) ||
+      !aligned16(o_swa) || !aligned16(k_cmp_in) || !aligned16(v_cmp_in) || !aligned16(workspace))
     return fail(NSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  // the decode kernels score a block once for the selection and the window branch
+  if (use_decode(dtype, dm) && !(kv.ks == kv.kw && kv.vs == kv.vw))
+    return fail(NSA_ERR_UNSUPPORTED, "one query row per sequence needs one K/V for selection and window");
   if (!use_fast(dtype, dm) && dm.Ns > 16384)
     return fail(NSA_ERR_UNSUPPORTED, "generic kernels handle at most 16384 selection blocks");
   const LayerWs w = layer_ws(dm, dtype);
@@ -382,12 +399,13 @@ int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const 
     void* kl = fast ? (char*)kc + round_up((size_t)dm.B * dm.Nc * dm.Hkv * dm.D * 2) : nullptr;
     void* vl = fast ? (char*)vc + w.vc / 2 : nullptr;
     void* ksc = vt ? (char*)kl + round_up(k8_lo_bytes(dm)) : nullptr;
-    hipError_t e = vt ? launch_compress_k8(dm, k, w_k, kc, kl, ksc, s)
-                      : launch_compress(dtype, fast ? 2 : 1, k, w_k, kc, kl, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d,
+    hipError_t e = vt ? launch_compress_k8(dm, kv.kc, w_k, kc, kl, ksc, s)
+                      : launch_compress(dtype, fast ? 2 : 1, kv.kc, w_k, kc, kl, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d,
                                         dm.Nc, s);
     if (e == hipSuccess)
-      e = vt ? launch_compress_vt(dm, v, w_v, vc, vl, s)
-             : launch_compress(dtype, fast ? 2 : 1, v, w_v, vc, vl, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d, dm.Nc, s);
+      e = vt ? launch_compress_vt(dm, kv.vc, w_v, vc, vl, s)
+             : launch_compress(dtype, fast ? 2 : 1, kv.vc, w_v, vc, vl, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d, dm.Nc,
+                               s);
     if (e != hipSuccess) return hip_fail(e, "compress kernel");
     kc_use = kc;
     vc_use = vc;
@@ -400,7 +418,8 @@ int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const 
     // one row per sequence: phases = compress | compression branch + top-n | selection, window, combine
     int32_t* didx = block_idx_out ? block_idx_out : idx_ws;
     prof_mark(s);
-    hipError_t e = launch_decode_fast(dm, DecVar{}, q, kc_use, kl_use, vc_use, vl_use, k, v, is_video, gates, out, o_cmp,
+    hipError_t e = launch_decode_fast(dm, DecVar{}, q, kc_use, kl_use, vc_use, vl_use, kv.ks, kv.vs, is_video, gates,
+                                      out, o_cmp,
                                       o_slc, o_swa, didx, lse, nullptr, sparse_ws_ptr, s, prof_mark);
     if (e != hipSuccess) return hip_fail(e, "decode kernels");
     prof_mark(s);
@@ -419,12 +438,37 @@ int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const 
   if (e != hipSuccess) return hip_fail(e, "top-n kernel");
   prof_mark(s);
   if (fast) {
-    st = run_sparse(dtype, dm, q, k, v, idx, is_video, ocmp32, true, gates, out, o_slc, o_swa, sparse_ws_ptr, s);
+    st = run_sparse(dtype, dm, q, kv, idx, is_video, ocmp32, true, gates, out, o_slc, o_swa, sparse_ws_ptr, s);
     prof_mark(s);
     return st;
   }
   void* oswa = o_swa ? o_swa : oswa_ws;
-  return run_sparse(dtype, dm, q, k, v, idx, is_video, ocmp, false, gates, out, o_slc, oswa, sparse_ws_ptr, s);
+  return run_sparse(dtype, dm, q, kv, idx, is_video, ocmp, false, gates, out, o_slc, oswa, sparse_ws_ptr, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const void* k_cmp_in,
+                             const void* v_cmp_in, const float* w_k, const float* w_v, const float* gates,
+                             const uint8_t* is_video, int32_t dtype, const nsa_shape* shape,
+                             const nsa_params* params, void* out, void* o_cmp, void* o_slc, void* o_swa,
+                             int32_t* block_idx_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return layer_fwd(q, BranchKV{k, v, k, v, k, v}, k_cmp_in, v_cmp_in, w_k, w_v, gates, is_video, dtype, shape,
+                   params, out, o_cmp, o_slc, o_swa, block_idx_out, workspace, workspace_bytes, stream);
+}
+
+int32_t nsa_hybrid_layer_fwd_branch_kv(const void* q, const void* k_c, const void* v_c, const void* k_s,
+                                       const void* v_s, const void* k_w, const void* v_w, const void* k_cmp_in,
+                                       const void* v_cmp_in, const float* w_k, const float* w_v,
+                                       const float* gates, const uint8_t* is_video, int32_t dtype,
+                                       const nsa_shape* shape, const nsa_params* params, void* out, void* o_cmp,
+                                       void* o_slc, void* o_swa, int32_t* block_idx_out, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  return layer_fwd(q, BranchKV{k_c, v_c, k_s, v_s, k_w, v_w}, k_cmp_in, v_cmp_in, w_k, w_v, gates, is_video,
+                   dtype, shape, params, out, o_cmp, o_slc, o_swa, block_idx_out, workspace, workspace_bytes,
+                   stream);
 }
 
 // Shape of a decode batch: one query row per sequence at its own length.

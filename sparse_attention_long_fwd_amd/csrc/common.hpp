@@ -77,6 +77,7 @@ hipError_t launch_cmp_generic(int dtype, int cdtype, const Dims& dm, const void*
 hipError_t launch_topk(const Dims& dm, const float* imp, const uint8_t* vid, int32_t* idx, hipStream_t s);
 
 // Generic selection / window / text-row kernel.  Writes whichever outputs are non-null.
-hipError_t launch_sparse_generic(int dtype, const Dims& dm, const void* q, const void* k, const void* v,
-                                 const int32_t* idx, const uint8_t* vid, const void* o_cmp, const float* gates,
+// ks / vs: keys and values of the selection branch; kw / vw: of the window branch and text rows.
+hipError_t launch_sparse_generic(int dtype, const Dims& dm, const void* q, const void* ks, const void* vs,
+                                 const void* kw, const void* vw, const int32_t* idx, const uint8_t* vid, const void* o_cmp, const float* gates,
                                  void* out, void* o_slc, void* o_swa, hipStream_t s);

@@ -32,8 +32,10 @@ size_t vt_tiles_bytes(const Dims& dm);
 hipError_t launch_compress_vt(const Dims& dm, const void* v, const float* w_v, void* hi, void* lo, hipStream_t s);
 
 // Window branch, text rows, selection branch and the gated combine.  o_cmp is
-// fp32 when ocmp_f32, else bf16.  ws: fast_sparse_workspace(dm) bytes.
-hipError_t launch_sparse_fast(const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
+// fp32 when ocmp_f32, else bf16.  ws: fast_sparse_workspace(dm) bytes.  ks / vs: keys and values
+// of the selection branch; kw / vw: of the window branch and text rows.
+hipError_t launch_sparse_fast(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
+                              const void* vw, const int32_t* idx,
                               const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out,
                               void* o_slc, void* o_swa, void* ws, hipStream_t s,
                               void (*mark)(hipStream_t) = nullptr);

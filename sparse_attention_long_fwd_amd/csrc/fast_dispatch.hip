@@ -22,16 +22,17 @@ size_t fast_sparse_workspace(const Dims& dm) {
   return rup((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 4) + rup(flash_workspace(dm)) + rup(slc_block_workspace(dm));
 }
 
-hipError_t launch_sparse_fast(const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
+hipError_t launch_sparse_fast(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
+                              const void* vw, const int32_t* idx,
                               const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out,
                               void* o_slc, void* o_swa, void* ws, hipStream_t s, void (*mark)(hipStream_t)) {
   float* swa32 = (float*)ws;
   char* fws = (char*)ws + rup((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 4);
   // window branch (fp32 for the combine, bf16 copy if asked) and dense text rows
-  hipError_t e = launch_flash_fast(dm, q, k, v, vid, swa32, o_swa, out, fws, s);
+  hipError_t e = launch_flash_fast(dm, q, kw, vw, vid, swa32, o_swa, out, fws, s);
   if (e != hipSuccess) return e;
   if (mark) mark(s);
   // selection branch and the gated combine of video rows
-  return launch_slc_block(dm, q, k, v, idx, vid, o_cmp, ocmp_f32, swa32, gates, out, o_slc,
+  return launch_slc_block(dm, q, ks, vs, idx, vid, o_cmp, ocmp_f32, swa32, gates, out, o_slc,
                           fws + rup(flash_workspace(dm)), s);
 }

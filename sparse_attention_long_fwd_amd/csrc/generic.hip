@@ -173,8 +173,8 @@ __device__ float attend_list(const float* qs, const T* kb, const T* vb, int64_t 
 
 template <typename T>
 __global__ void __launch_bounds__(GEN_THREADS)
-    sparse_generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                          const int32_t* __restrict__ idx, const uint8_t* __restrict__ vid,
+    sparse_generic_kernel(const T* __restrict__ q, const T* __restrict__ ks, const T* __restrict__ vs,
+                          const T* __restrict__ kw, const T* __restrict__ vw, const int32_t* __restrict__ idx, const uint8_t* __restrict__ vid,
                           const T* __restrict__ o_cmp, const float* __restrict__ gates, T* __restrict__ out,
                           T* __restrict__ o_slc, T* __restrict__ o_swa, Dims dm) {
   __shared__ float qs[256];
@@ -189,8 +189,11 @@ __global__ void __launch_bounds__(GEN_THREADS)
   const int64_t t = dm.q0 + r;
   const bool is_vid = vid ? (vid[b * dm.Tq + r] != 0) : true;
   const int64_t kstride = (int64_t)dm.Hkv * D;
-  const T* kb = k + (b * dm.T * dm.Hkv + g) * (int64_t)D;
-  const T* vb = v + (b * dm.T * dm.Hkv + g) * (int64_t)D;
+  // selection keys / values, and those of the window branch and text rows
+  const T* ksb = ks + (b * dm.T * dm.Hkv + g) * (int64_t)D;
+  const T* vsb = vs + (b * dm.T * dm.Hkv + g) * (int64_t)D;
+  const T* kb = kw + (b * dm.T * dm.Hkv + g) * (int64_t)D;
+  const T* vb = vw + (b * dm.T * dm.Hkv + g) * (int64_t)D;
   const int32_t* sel = idx ? idx + ((b * dm.Tq + r) * dm.Hkv + g) * dm.n : nullptr;
   const int ls = dm.ls;
   for (int hh = 0; hh < dm.G; ++hh) {
@@ -214,7 +217,7 @@ __global__ void __launch_bounds__(GEN_THREADS)
         const int64_t u = (int64_t)j * ls + (a % ls);
         return (u <= t && u < dm.T) ? u : -1;
       };
-      os = attend_list(qs, kb, vb, kstride, D, (int64_t)dm.n * ls, slc_key, dm.scale, ps, us, red);
+      os = attend_list(qs, ksb, vsb, kstride, D, (int64_t)dm.n * ls, slc_key, dm.scale, ps, us, red);
       if (o_slc && tid < D) o_slc[row * D + tid] = from_f32<T>(os);
     }
     if (o_swa || out) {
@@ -230,18 +233,18 @@ __global__ void __launch_bounds__(GEN_THREADS)
   }
 }
 
-hipError_t launch_sparse_generic(int dtype, const Dims& dm, const void* q, const void* k, const void* v,
-                                 const int32_t* idx, const uint8_t* vid, const void* o_cmp, const float* gates,
+hipError_t launch_sparse_generic(int dtype, const Dims& dm, const void* q, const void* ks, const void* vs,
+                                 const void* kw, const void* vw, const int32_t* idx, const uint8_t* vid, const void* o_cmp, const float* gates,
                                  void* out, void* o_slc, void* o_swa, hipStream_t s) {
   if (dm.Tq <= 0 || dm.B <= 0) return hipSuccess;
   dim3 grid((unsigned)dm.Tq, (unsigned)dm.Hkv, (unsigned)dm.B);
   if (dtype == 1)
     sparse_generic_kernel<bf16><<<grid, GEN_THREADS, 0, s>>>(
-        (const bf16*)q, (const bf16*)k, (const bf16*)v, idx, vid, (const bf16*)o_cmp, gates, (bf16*)out,
+        (const bf16*)q, (const bf16*)ks, (const bf16*)vs, (const bf16*)kw, (const bf16*)vw, idx, vid, (const bf16*)o_cmp, gates, (bf16*)out,
         (bf16*)o_slc, (bf16*)o_swa, dm);
   else
     sparse_generic_kernel<float><<<grid, GEN_THREADS, 0, s>>>(
-        (const float*)q, (const float*)k, (const float*)v, idx, vid, (const float*)o_cmp, gates, (float*)out,
+        (const float*)q, (const float*)ks, (const float*)vs, (const float*)kw, (const float*)vw, idx, vid, (const float*)o_cmp, gates, (float*)out,
         (float*)o_slc, (float*)o_swa, dm);
   return hipGetLastError();
 }

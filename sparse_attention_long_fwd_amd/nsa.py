@@ -62,6 +62,8 @@ EXPORTS = {
     "nsa_compress_append": (_I32, [_P, _P, _I32, _I64, _I64, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _I32, _I64,
                                    _I32, _P, _P, _P]),
     "nsa_gate_proj": (_I32, [_P, _P, _P, _I32, _I64, _I64, _I32, _I32, _P, _P]),
+    "nsa_hybrid_layer_fwd_branch_kv": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _SH, _PR,
+                                              _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "nsa_set_force_generic": (_I32, [_I32]),
     "nsa_profile_enable": (_I32, [_I32]),
     "nsa_profile_read": (_I32, [ctypes.POINTER(ctypes.c_float), _I32]),
@@ -281,3 +283,22 @@ def nsa_gate_proj(x, w_g, b_g=None, gates=None, stream=None):
     _check(lib().nsa_gate_proj(_ptr(x), _ptr(w_g), _ptr(b_g), _dtype_code(x), B, T, K, Hq, _ptr(gates),
                                _stream(stream)))
     return gates
+
+
+def nsa_hybrid_layer_fwd_branch_kv(q, kv_c, kv_s, kv_w, gates, shape: NsaShape, params: NsaParams, w_k=None,
+                                   w_v=None, k_cmp_in=None, v_cmp_in=None, is_video=None, out=None, o_cmp=None,
+                                   o_slc=None, o_swa=None, block_idx_out=None, workspace=None, stream=None):
+    """The layer with keys / values per branch: kv_c (compression), kv_s (selection), kv_w (window and
+    text rows), each a (k, v) pair."""
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = torch.empty(nsa_hybrid_layer_workspace_size(shape, params, dt), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib().nsa_hybrid_layer_fwd_branch_kv(
+        _ptr(q), _ptr(kv_c[0]), _ptr(kv_c[1]), _ptr(kv_s[0]), _ptr(kv_s[1]), _ptr(kv_w[0]), _ptr(kv_w[1]),
+        _ptr(k_cmp_in), _ptr(v_cmp_in), _ptr(w_k), _ptr(w_v), _ptr(gates), _ptr(is_video), dt, ctypes.byref(shape),
+        ctypes.byref(params), _ptr(out), _ptr(o_cmp), _ptr(o_slc), _ptr(o_swa), _ptr(block_idx_out),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out

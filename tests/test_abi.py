@@ -176,3 +176,22 @@ def test_gate_proj_validates_first():
     assert call(x=None) == nsa.NSA_ERR_INVALID_ARG
     assert call(x=FAKE + 8) == nsa.NSA_ERR_INVALID_ARG     # misaligned
     assert call(x=None, seq=0) == nsa.NSA_OK               # no tokens: nothing launched
+
+
+def test_branch_kv_decode_needs_one_selection_window_kv():
+    L = nsa.lib()
+    sh = _dshape(batch=2, q_len=1, kv_len=4096, q_start=4095)
+    pr = _params(top_n=16, window=512)
+    need = nsa.nsa_hybrid_layer_workspace_size(sh, pr, nsa.NSA_BF16)
+
+    def call(kw):
+        return L.nsa_hybrid_layer_fwd_branch_kv(FAKE, FAKE, FAKE, FAKE, FAKE, kw, FAKE, FAKE, FAKE, None, None, FAKE,
+                                                None, nsa.NSA_BF16, ctypes.byref(sh), ctypes.byref(pr), FAKE, None,
+                                                None, None, None, FAKE, need, None)
+
+    assert call(FAKE + 4096) == nsa.NSA_ERR_UNSUPPORTED     # window keys differ from selection keys
+    assert "selection and window" in nsa.last_error()
+    sh2 = _dshape(batch=2, q_len=4096, kv_len=4096)
+    assert L.nsa_hybrid_layer_fwd_branch_kv(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE,
+                                            None, nsa.NSA_BF16, ctypes.byref(sh2), ctypes.byref(pr), FAKE, None, None,
+                                            None, None, FAKE, 1 << 40, None) == nsa.NSA_ERR_INVALID_ARG

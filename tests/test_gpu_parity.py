@@ -232,12 +232,16 @@ def run_layer(wl, inp, **kw):
 
 
 def compare_layer(wl, inp, got, rows, b=0, kc=None, vc=None):
-    """Oracle on the chosen rows of batch element b; assert the parity rules."""
+    """Oracle on the chosen rows of batch element b; assert the parity rules.  inp may hold
+    per-branch keys / values (k_s, v_s: selection; k_w, v_w: window and text rows)."""
     dtype = wl.dtype
     q = host(inp["q"][b])
     k, v = host(inp["k"][b]), host(inp["v"][b])
+    okw = {}
+    if "k_s" in inp:
+        okw = dict(kv_slc=(host(inp["k_s"][b]), host(inp["v_s"][b])), kv_swa=(host(inp["k_w"][b]), host(inp["v_w"][b])))
     res = oracle.layer(q, k, v, host(inp["w_k"]), host(inp["w_v"]), host(inp["gates"][b]),
-                       host(inp["is_video"][b]), wl.params(), q_start=wl.q_start, rows=rows, kc=kc, vc=vc)
+                       host(inp["is_video"][b]), wl.params(), q_start=wl.q_start, rows=rows, kc=kc, vc=vc, **okw)
     V = host(inp["is_video"][b])[rows].astype(bool)
     pos = rows + wl.q_start
     tol = TOL[dtype]
@@ -413,3 +417,59 @@ def test_decode_single_row(case, path):
     got = run_layer(wl, inp)
     for b in range(B):
         compare_layer(wl, inp, got, np.arange(1), b)
+
+
+# --------------------------------------------------------------------------- keys / values per branch
+def run_layer_branch_kv(wl, inp, **kw):
+    q = inp["q"]
+    B, Tq, Hq, D = q.shape
+    Hkv = inp["k"].shape[2]
+    sh = nsa.make_shape(B, Tq, wl.kv_len, wl.q_start, Hq, Hkv, D)
+    pr = nsa.make_params(**wl.params())
+    o_cmp, o_slc, o_swa = torch.zeros_like(q), torch.zeros_like(q), torch.zeros_like(q)
+    idx = torch.full((B, Tq, Hkv, wl.top_n), -1, dtype=torch.int32, device=DEV)
+    out = nsa.nsa_hybrid_layer_fwd_branch_kv(q, (inp["k"], inp["v"]), (inp["k_s"], inp["v_s"]),
+                                             (inp["k_w"], inp["v_w"]), inp["gates"], sh, pr, w_k=inp["w_k"],
+                                             w_v=inp["w_v"], is_video=inp["is_video"], o_cmp=o_cmp, o_slc=o_slc,
+                                             o_swa=o_swa, block_idx_out=idx, **kw)
+    torch.cuda.synchronize()
+    return dict(out=out, o_cmp=o_cmp, o_slc=o_slc, o_swa=o_swa, idx=idx)
+
+
+def _branch_inputs(wl):
+    inp = synth.make_inputs(wl, DEV)
+    for tag, off in (("s", 40), ("w", 80)):
+        other = synth.make_inputs(wl, DEV, batch_offset=off)
+        inp["k_" + tag], inp["v_" + tag] = other["k"], other["v"]
+    return inp
+
+
+@pytest.mark.parametrize("case", ["bf16-4k", "bf16-ragged-batch2"])
+def test_layer_branch_kv(case, path):
+    if case == "bf16-4k":
+        wl = _wl(T=4096, lead=256, tail=256)
+    else:
+        wl = _wl(T=1000 + 37, B=2, Hq=14, Hkv=2, lead=64, tail=13, n=6, w=100)
+    flush("branch kv %s path=%s" % (case, path))
+    inp = _branch_inputs(wl)
+    got = run_layer_branch_kv(wl, inp)
+    for b in range(wl.batch):
+        compare_layer(wl, inp, got, np.arange(wl.q_len), b)
+
+
+def test_layer_branch_kv_full_size_sampled():
+    wl = synth.WORKLOADS["36k"]
+    flush("branch kv 36k")
+    inp = _branch_inputs(wl)
+    got = run_layer_branch_kv(wl, inp)
+    compare_layer(wl, inp, got, _sample_rows(wl, seed=7, text=8, edge=32)[::2])
+
+
+def test_layer_branch_kv_shared_equals_layer():
+    wl = _wl(T=3000, lead=128, tail=128)
+    inp = synth.make_inputs(wl, DEV)
+    inp["k_s"], inp["v_s"], inp["k_w"], inp["v_w"] = inp["k"], inp["v"], inp["k"], inp["v"]
+    a = run_layer(wl, inp)
+    b = run_layer_branch_kv(wl, inp)
+    for key in ("out", "o_cmp", "o_slc", "o_swa", "idx"):
+        assert torch.equal(a[key], b[key]), key

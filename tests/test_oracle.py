@@ -387,3 +387,45 @@ def test_gate_proj_closed_forms():
         oracle.gate_proj(xb, w, bb)) + bb
     assert np.allclose(lin, 0.0, atol=1e-9)
     assert np.all((g1 > 0) & (g1 < 1))
+
+
+def test_layer_branch_kv_independence_and_reductions():
+    """Per-branch keys / values: each branch output depends on its own K/V only; with every
+    block chosen and a window spanning the sequence, the selection and window outputs are dense
+    causal attention over their own K/V (the independent dense path); text rows read the window's
+    K/V; all three equal gives the shared-K/V layer."""
+    T, Hq, Hkv, D = 200, 4, 2, 16
+    q = rnd(61, T, Hq, D)
+    k, v = rnd(62, T, Hkv, D), rnd(63, T, Hkv, D)
+    k2, v2 = rnd(64, T, Hkv, D), rnd(65, T, Hkv, D)
+    k3, v3 = rnd(66, T, Hkv, D), rnd(67, T, Hkv, D)
+    w = (rnd(68, 8) / 3).astype(np.float32)
+    g = (1 / (1 + np.exp(-rnd(69, T, Hq, 3)))).astype(np.float32)
+    vid = np.ones(T, np.uint8)
+    vid[:20] = 0
+    p = small_params()
+    base = oracle.layer(q, k, v, w, w, g, vid, p)
+    same = oracle.layer(q, k, v, w, w, g, vid, p, kv_slc=(k, v), kv_swa=(k, v))
+    for key in ("o_cmp", "o_slc", "o_swa", "out", "imp"):
+        assert np.array_equal(base[key], same[key]), key
+    r = oracle.layer(q, k, v, w, w, g, vid, p, kv_slc=(k2, v2), kv_swa=(k3, v3))
+    V = vid.astype(bool)
+    assert np.array_equal(r["o_cmp"], base["o_cmp"]) and np.array_equal(r["imp"], base["imp"])
+    assert np.array_equal(r["idx"], base["idx"])
+    assert not np.allclose(r["o_slc"][V], base["o_slc"][V]) and not np.allclose(r["o_swa"][V], base["o_swa"][V])
+    # text rows: dense causal attention over the window branch's K/V
+    s = 1 / math.sqrt(D)
+    tr = np.nonzero(~V)[0]
+    dw, _ = oracle.dense_rows(q[tr], tr, k3, v3, s)
+    assert np.allclose(r["out"][tr], dw, atol=1e-12)
+    # every block chosen (top-n covers all 13 blocks) and a window over the whole sequence
+    pall = small_params(top_n=13, window=4096)
+    ra = oracle.layer(q, k, v, w, w, g, vid, pall, kv_slc=(k2, v2), kv_swa=(k3, v3))
+    vr = np.nonzero(V)[0]
+    ds, _ = oracle.dense_rows(q[vr], vr, k2, v2, s)
+    dw2, _ = oracle.dense_rows(q[vr], vr, k3, v3, s)
+    assert np.allclose(ra["o_slc"][vr], ds, atol=1e-12)
+    assert np.allclose(ra["o_swa"][vr], dw2, atol=1e-12)
+    gg = g.astype(np.float64)
+    assert np.allclose(ra["out"][vr], gg[vr, :, 0:1] * ra["o_cmp"][vr] + gg[vr, :, 1:2] * ds + gg[vr, :, 2:3] * dw2,
+                       atol=1e-12)
