@@ -69,6 +69,8 @@ def lib():
                                          _i64, _dbl, _p, _p]
         L.oracle_dense_rows.argtypes = [_p, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _dbl, _p, _p]
         L.oracle_gate_proj.argtypes = [_p, _i64, _i64, _p, _i64, _p, _p]
+        L.oracle_layer_bwd.argtypes = [_p, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _i64, _p, _p, _i64,
+                                       _i64, _i64, _p, _i64, _i64, _dbl, _p, _p, _p, _p, _p, _p, _p, _p, _p]
         _lib = L
     return _lib
 
@@ -232,3 +234,38 @@ def layer(q, k, v, w_k, w_v, gates, is_video, params: Dict, q_start: int = 0,
         res["out"][tr], _ = dense_rows(q_rows[tr], pos[tr], kw, vw, scale)
     res["kc"], res["vc"] = kc, vc
     return res
+
+
+def layer_bwd(q, k, v, w_k, w_v, gates, is_video, params: Dict, dout, q_start: int = 0,
+              idx: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Gradients of sum(dout * out) for the hybrid layer of one batch element (all of q's rows).
+
+    q, dout [Tq, Hq, D], k/v [T, Hkv, D], gates [Tq, Hq, 3], is_video [Tq], w_k / w_v [l].  The
+    chosen blocks are held fixed (no gradient through top-n): ``idx`` [Tq, Hkv, n] when given, else
+    the forward's own choice.  Returns fp64 dq, dk, dv, dgates, dw_k, dw_v and the idx used.
+    """
+    q = _f32(q)
+    k = _f32(k)
+    v = _f32(v)
+    Tq, Hq, D = q.shape
+    T, Hkv, _ = k.shape
+    l, d, ls = params["cmp_block"], params["cmp_stride"], params["sel_block"]
+    n, w = params["top_n"], params["window"]
+    scale = default_scale(D, params.get("scale", 0.0))
+    if idx is None:
+        idx = layer(q, k, v, w_k, w_v, gates, is_video, params, q_start=q_start)["idx"]
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    kc = compress(k, w_k, l, d)
+    vc = compress(v, w_v, l, d)
+    Nc = kc.shape[0]
+    pos = np.arange(q_start, q_start + Tq, dtype=np.int64)
+    vid = np.ascontiguousarray(is_video, dtype=np.uint8)
+    out = dict(dq=np.zeros((Tq, Hq, D)), dk=np.zeros((T, Hkv, D)), dv=np.zeros((T, Hkv, D)),
+               dgates=np.zeros((Tq, Hq, 3)), dw_k=np.zeros(l), dw_v=np.zeros(l))
+    wk, wv, gg, do = _f32(w_k), _f32(w_v), _f32(gates), _f32(dout)  # kept alive through the call
+    lib().oracle_layer_bwd(_ptr(q), _ptr(pos), Tq, _ptr(k), _ptr(v), T, Hq, Hkv, D, _ptr(kc), _ptr(vc), Nc,
+                           _ptr(wk), _ptr(wv), l, d, ls, _ptr(idx), n, w, scale, _ptr(gg), _ptr(vid), _ptr(do),
+                           _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dgates"]),
+                           _ptr(out["dw_k"]), _ptr(out["dw_v"]))
+    out["idx"] = idx
+    return out

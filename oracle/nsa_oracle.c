@@ -358,3 +358,147 @@ void oracle_gate_proj(const float* x, int64_t R, int64_t K, const float* w, int6
     }
   }
 }
+
+/*
+ * Backward pass of one attention branch for one (row, head): softmax attention
+ * of query qh over the listed keys of K / V (fp64, [N, Hkv, D], KV head g),
+ * whose output enters the loss scaled by `gate` against the upstream gradient
+ * dout.  With P the probabilities and E = sum_a P_a <dout, v_a>:
+ *   d gate = E,   ds_a = gate * P_a * (<dout, v_a> - E),
+ *   dq += scale * sum_a ds_a k_a,  dK[a] += scale * ds_a q,  dV[a] += gate * P_a dout.
+ * Returns E (0 for an empty list: the branch output is 0).
+ */
+static double branch_bwd(const double* qh, const double* K, const double* V, int64_t Hkv, int64_t g, int64_t D,
+                         const int64_t* keys, int64_t nk, double scale, double gate, const double* dout,
+                         double* z, double* dpv, double* dq, double* dK, double* dV) {
+  if (nk == 0) return 0.0;
+  double m = -INFINITY;
+  for (int64_t a = 0; a < nk; ++a) {
+    const double* ka = K + (keys[a] * Hkv + g) * D;
+    double s = 0.0;
+    for (int64_t e = 0; e < D; ++e) s += qh[e] * ka[e];
+    z[a] = scale * s;
+    if (z[a] > m) m = z[a];
+  }
+  double sum = 0.0;
+  for (int64_t a = 0; a < nk; ++a) sum += exp(z[a] - m);
+  const double L = m + log(sum);
+  double E = 0.0;
+  for (int64_t a = 0; a < nk; ++a) {
+    const double* va = V + (keys[a] * Hkv + g) * D;
+    double s = 0.0;
+    for (int64_t e = 0; e < D; ++e) s += dout[e] * va[e];
+    dpv[a] = s;
+    z[a] = exp(z[a] - L);  /* now the probability */
+    E += z[a] * s;
+  }
+  for (int64_t a = 0; a < nk; ++a) {
+    const double p = z[a], ds = gate * p * (dpv[a] - E);
+    const double* ka = K + (keys[a] * Hkv + g) * D;
+    double* dka = dK + (keys[a] * Hkv + g) * D;
+    double* dva = dV + (keys[a] * Hkv + g) * D;
+    for (int64_t e = 0; e < D; ++e) {
+      dq[e] += scale * ds * ka[e];
+      dka[e] += scale * ds * qh[e];
+      dva[e] += gate * p * dout[e];
+    }
+  }
+  return E;
+}
+
+/*
+ * Backward pass of the hybrid layer for one batch element, the loss being
+ * sum(dout * out) for the layer output out of R query rows (row r at position
+ * pos[r]).  The forward is the one above: for video rows out = g_cmp o_cmp +
+ * g_slc o_slc + g_swa o_swa over the branches' key sets, for text rows dense
+ * causal attention (ungated).  The chosen blocks idx [R, Hkv, n] are held
+ * fixed: top-n selection passes no gradient (the importance only picks
+ * indices).  Compressed keys and values kc, vc [Nc, Hkv, D] are the forward's
+ * positional weighted sums, so their gradients flow back to k, v and to the
+ * weights w_k, w_v [l]:
+ *   dk[i d + m] += w_k[m] dkc[i],   dw_k[m] = sum_i <dkc[i], k[i d + m]>   (likewise v).
+ * Outputs (fp64): dq [R, Hq, D], dk, dv [T, Hkv, D], dgates [R, Hq, 3]
+ * (zero for text rows), dw_k, dw_v [l].  Serial: test sizes only.
+ */
+void oracle_layer_bwd(const float* q, const int64_t* pos, int64_t R, const float* k, const float* v, int64_t T,
+                      int64_t Hq, int64_t Hkv, int64_t D, const double* kc, const double* vc, int64_t Nc,
+                      const float* w_k, const float* w_v, int64_t l, int64_t d, int64_t ls, const int32_t* idx,
+                      int64_t n, int64_t w, double scale, const float* gates, const unsigned char* is_video,
+                      const float* dout, double* dq, double* dk, double* dv, double* dgates, double* dw_k,
+                      double* dw_v) {
+  const int64_t G = Hq / Hkv;
+  double* kd = (double*)malloc(sizeof(double) * (size_t)(T * Hkv * D + 1));
+  double* vd = (double*)malloc(sizeof(double) * (size_t)(T * Hkv * D + 1));
+  double* dkc = (double*)calloc((size_t)(Nc * Hkv * D + 1), sizeof(double));
+  double* dvc = (double*)calloc((size_t)(Nc * Hkv * D + 1), sizeof(double));
+  const int64_t cap = (T > Nc ? T : Nc) + 1;
+  int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
+  double* z = (double*)malloc(sizeof(double) * (size_t)cap);
+  double* dpv = (double*)malloc(sizeof(double) * (size_t)cap);
+  double qh[1024], dh[1024];
+  for (int64_t x = 0; x < T * Hkv * D; ++x) {
+    kd[x] = k[x];
+    vd[x] = v[x];
+    dk[x] = 0.0;
+    dv[x] = 0.0;
+  }
+  for (int64_t m = 0; m < l; ++m) dw_k[m] = dw_v[m] = 0.0;
+  for (int64_t r = 0; r < R; ++r) {
+    const int64_t t = pos[r];
+    for (int64_t h = 0; h < Hq; ++h) {
+      const int64_t g = h / G, row = r * Hq + h;
+      for (int64_t e = 0; e < D; ++e) {
+        qh[e] = q[row * D + e];
+        dh[e] = dout[row * D + e];
+        dq[row * D + e] = 0.0;
+      }
+      double* dqh = dq + row * D;
+      double* dg = dgates + row * 3;
+      dg[0] = dg[1] = dg[2] = 0.0;
+      if (!is_video[r]) {
+        int64_t nk = 0;
+        for (int64_t u = 0; u <= t && u < T; ++u) keys[nk++] = u;
+        branch_bwd(qh, kd, vd, Hkv, g, D, keys, nk, scale, 1.0, dh, z, dpv, dqh, dk, dv);
+        continue;
+      }
+      const float* gg = gates + row * 3;
+      /* compression branch: the visible compressed blocks */
+      int64_t nvis = (t + 1 >= l) ? (t + 1 - l) / d + 1 : 0;
+      if (nvis > Nc) nvis = Nc;
+      for (int64_t i = 0; i < nvis; ++i) keys[i] = i;
+      dg[0] = branch_bwd(qh, kc, vc, Hkv, g, D, keys, nvis, scale, gg[0], dh, z, dpv, dqh, dkc, dvc);
+      /* selection branch: tokens u <= t of the chosen blocks */
+      int64_t nk = 0;
+      const int32_t* sel = idx + (r * Hkv + g) * n;
+      for (int64_t c = 0; c < n; ++c) {
+        if (sel[c] < 0) continue;
+        for (int64_t u = (int64_t)sel[c] * ls; u < ((int64_t)sel[c] + 1) * ls && u <= t && u < T; ++u)
+          keys[nk++] = u;
+      }
+      dg[1] = branch_bwd(qh, kd, vd, Hkv, g, D, keys, nk, scale, gg[1], dh, z, dpv, dqh, dk, dv);
+      /* sliding window: the w most recent tokens including t */
+      nk = 0;
+      for (int64_t u = (t - w + 1 > 0 ? t - w + 1 : 0); u <= t && u < T; ++u) keys[nk++] = u;
+      dg[2] = branch_bwd(qh, kd, vd, Hkv, g, D, keys, nk, scale, gg[2], dh, z, dpv, dqh, dk, dv);
+    }
+  }
+  /* back through the compression */
+  for (int64_t i = 0; i < Nc; ++i)
+    for (int64_t m = 0; m < l; ++m) {
+      const int64_t u = i * d + m;
+      for (int64_t x = 0; x < Hkv * D; ++x) {
+        const double gk = dkc[i * Hkv * D + x], gv = dvc[i * Hkv * D + x];
+        dk[u * Hkv * D + x] += (double)w_k[m] * gk;
+        dv[u * Hkv * D + x] += (double)w_v[m] * gv;
+        dw_k[m] += gk * kd[u * Hkv * D + x];
+        dw_v[m] += gv * vd[u * Hkv * D + x];
+      }
+    }
+  free(kd);
+  free(vd);
+  free(dkc);
+  free(dvc);
+  free(keys);
+  free(z);
+  free(dpv);
+}

@@ -429,3 +429,59 @@ def test_layer_branch_kv_independence_and_reductions():
     gg = g.astype(np.float64)
     assert np.allclose(ra["out"][vr], gg[vr, :, 0:1] * ra["o_cmp"][vr] + gg[vr, :, 1:2] * ds + gg[vr, :, 2:3] * dw2,
                        atol=1e-12)
+
+
+def _grid(seed, *shape, step=2.0 ** -6, lim=3.0):
+    """Seeded values on a 2^-6 grid in [-lim, lim]: x +- 2^-12 stays exact in float32."""
+    x = np.clip(np.round(synth.normal(seed, shape).numpy() / step) * step, -lim, lim)
+    return x.astype(np.float32)
+
+
+def test_layer_backward_matches_finite_differences():
+    """Backward of sum(dout * out) against central differences of the forward oracle (fp64
+    arithmetic on exactly perturbed float inputs, chosen blocks held fixed), over q, k, v, the
+    gates and both compression weight vectors, with text and video rows."""
+    T, Hq, Hkv, D = 96, 4, 2, 8
+    p = small_params(window=20)
+    q, k, v = _grid(71, T, Hq, D), _grid(72, T, Hkv, D), _grid(73, T, Hkv, D)
+    w_k = (_grid(74, 8) / 4).astype(np.float32)
+    w_v = (_grid(75, 8) / 4).astype(np.float32)
+    g = (0.25 + 0.5 * (_grid(76, T, Hq, 3) > 0)).astype(np.float32) + _grid(77, T, Hq, 3) / 64
+    g = g.astype(np.float32)
+    vid = np.ones(T, np.uint8)
+    vid[:10] = 0
+    vid[-6:] = 0
+    dout = _grid(78, T, Hq, D)
+    base = oracle.layer(q, k, v, w_k, w_v, g, vid, p)
+    idx = base["idx"]
+    grad = oracle.layer_bwd(q, k, v, w_k, w_v, g, vid, p, dout, idx=idx)
+    eps = 2.0 ** -12
+    rng = np.random.default_rng(5)
+
+    def loss(**kw):
+        a = dict(q=q, k=k, v=v, w_k=w_k, w_v=w_v, gates=g)
+        a.update(kw)
+        r = oracle.layer(a["q"], a["k"], a["v"], a["w_k"], a["w_v"], a["gates"], vid, p)
+        return float(np.sum(r["out"] * dout)), r["idx"]
+
+    checked = 0
+    for name, arr, key in (("q", q, "dq"), ("k", k, "dk"), ("v", v, "dv"), ("gates", g, "dgates"),
+                           ("w_k", w_k, "dw_k"), ("w_v", w_v, "dw_v")):
+        flat = [tuple(rng.integers(0, s) for s in arr.shape) for _ in range(8)]
+        for ix in flat:
+            xp, xm = arr.copy(), arr.copy()
+            xp[ix] += eps
+            xm[ix] -= eps
+            lp, ip = loss(**{name: xp})
+            lm, im = loss(**{name: xm})
+            if not (np.array_equal(ip, idx) and np.array_equal(im, idx)):
+                continue  # the perturbation moved a top-n choice: no derivative there
+            fd = (lp - lm) / (2 * eps)
+            an = grad[key][ix]
+            assert abs(fd - an) <= 1e-6 + 1e-5 * abs(an), (name, ix, fd, an)
+            checked += 1
+    assert checked >= 40
+    # text rows have no gate gradient; a zero upstream gradient gives zero gradients
+    assert not grad["dgates"][:10].any()
+    z = oracle.layer_bwd(q, k, v, w_k, w_v, g, vid, p, np.zeros_like(dout), idx=idx)
+    assert all(not z[key].any() for key in ("dq", "dk", "dv", "dgates", "dw_k", "dw_v"))
