@@ -270,6 +270,34 @@ int32_t nsa_hybrid_layer_fwd_branch_kv(const void* q, const void* k_c, const voi
                                        void* o_slc, void* o_swa, int32_t* block_idx_out, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/*
+ * nsa_hybrid_layer_bwd -- backward pass of nsa_hybrid_layer_fwd: gradients of
+ * the loss sum(d_out * out) ([B] section 一 and [C] sections 2.2 / 3.1 define
+ * the forward; the selection is non-differentiable, so the chosen blocks are
+ * an input and pass no gradient).  Per branch of a video row (and the single
+ * dense branch of a text row, gate 1), with P the probabilities over the
+ * branch's keys and E = sum_u P_u <d_out, v_u>:
+ *   d_gates = E,  ds_u = gate P_u (<d_out, v_u> - E),  dq += scale sum ds_u k_u,
+ *   dk_u += scale ds_u q,  dv_u += gate P_u d_out;
+ * compressed keys / values pass their gradients back through the weighted block
+ * sum: dk[i*d + m] += w_k[m] dk_cmp[i], dw_k[m] = sum_i <dk_cmp[i], k[i*d + m]>
+ * (likewise v).  Compression is recomputed from k, v in fp32.
+ *  q, d_out [B, q_len, Hq, D] (dtype); k, v [B, kv_len, Hkv, D] (dtype);
+ *  w_k, w_v [cmp_block] fp32; gates [B, q_len, Hq, 3] fp32; is_video as for
+ *  the forward; block_idx [B, q_len, Hkv, top_n] int32 (the forward's choice).
+ *  Outputs, all fp32 and required: dq [B, q_len, Hq, D], dk, dv
+ *  [B, kv_len, Hkv, D], d_gates [B, q_len, Hq, 3] (0 for text rows), dw_k,
+ *  dw_v [cmp_block] (summed over the batch).  Generic kernels: head_dim <= 256
+ *  and a multiple of 8, fp32 or bf16.  workspace:
+ *  nsa_hybrid_layer_bwd_workspace_size() bytes.
+ */
+size_t nsa_hybrid_layer_bwd_workspace_size(const nsa_shape* shape, const nsa_params* params, int32_t dtype);
+int32_t nsa_hybrid_layer_bwd(const void* q, const void* k, const void* v, const float* w_k, const float* w_v,
+                             const float* gates, const uint8_t* is_video, const int32_t* block_idx,
+                             const void* d_out, int32_t dtype, const nsa_shape* shape, const nsa_params* params,
+                             float* dq, float* dk, float* dv, float* d_gates, float* dw_k, float* dw_v,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Debug / test switch: 1 forces the generic (non-MFMA) kernels, 0 restores the
  * default dispatch.  Returns the previous value.  Process-wide. */
 int32_t nsa_set_force_generic(int32_t on);

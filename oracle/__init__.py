@@ -237,13 +237,26 @@ def layer(q, k, v, w_k, w_v, gates, is_video, params: Dict, q_start: int = 0,
 
 
 def layer_bwd(q, k, v, w_k, w_v, gates, is_video, params: Dict, dout, q_start: int = 0,
-              idx: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
-    """Gradients of sum(dout * out) for the hybrid layer of one batch element (all of q's rows).
+              idx: Optional[np.ndarray] = None, rows: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Gradients of sum(dout * out) for the hybrid layer of one batch element.
 
     q, dout [Tq, Hq, D], k/v [T, Hkv, D], gates [Tq, Hq, 3], is_video [Tq], w_k / w_v [l].  The
     chosen blocks are held fixed (no gradient through top-n): ``idx`` [Tq, Hkv, n] when given, else
-    the forward's own choice.  Returns fp64 dq, dk, dv, dgates, dw_k, dw_v and the idx used.
+    the forward's own choice.  ``rows`` restricts the loss to those rows of q (dq and dgates are
+    then those rows' own; dk, dv, dw_k, dw_v hold only their contributions).  Returns fp64 dq, dk,
+    dv, dgates, dw_k, dw_v and the idx used.
     """
+    if rows is not None:
+        rows = np.asarray(rows, dtype=np.int64)
+        if idx is None:
+            idx = layer(q, k, v, w_k, w_v, gates, is_video, params, q_start=q_start, rows=rows)["idx"]
+        else:
+            idx = np.asarray(idx)[rows]
+        q, gates, dout = np.asarray(q)[rows], np.asarray(gates)[rows], np.asarray(dout)[rows]
+        is_video = np.asarray(is_video)[rows]
+        pos = (rows + q_start).astype(np.int64)
+    else:
+        pos = None
     q = _f32(q)
     k = _f32(k)
     v = _f32(v)
@@ -258,7 +271,8 @@ def layer_bwd(q, k, v, w_k, w_v, gates, is_video, params: Dict, dout, q_start: i
     kc = compress(k, w_k, l, d)
     vc = compress(v, w_v, l, d)
     Nc = kc.shape[0]
-    pos = np.arange(q_start, q_start + Tq, dtype=np.int64)
+    if pos is None:
+        pos = np.arange(q_start, q_start + Tq, dtype=np.int64)
     vid = np.ascontiguousarray(is_video, dtype=np.uint8)
     out = dict(dq=np.zeros((Tq, Hq, D)), dk=np.zeros((T, Hkv, D)), dv=np.zeros((T, Hkv, D)),
                dgates=np.zeros((Tq, Hq, 3)), dw_k=np.zeros(l), dw_v=np.zeros(l))

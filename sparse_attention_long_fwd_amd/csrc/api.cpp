@@ -598,4 +598,33 @@ int32_t nsa_gate_proj(const void* x, const void* w_g, const float* b_g, int32_t 
   return NSA_OK;
 }
 
+size_t nsa_hybrid_layer_bwd_workspace_size(const nsa_shape* shape, const nsa_params* params, int32_t dtype) {
+  Dims dm;
+  if (check_dims(shape, params, dtype, &dm, true) != NSA_OK) return 0;
+  return bwd_workspace(dm);
+}
+
+int32_t nsa_hybrid_layer_bwd(const void* q, const void* k, const void* v, const float* w_k, const float* w_v,
+                             const float* gates, const uint8_t* is_video, const int32_t* block_idx,
+                             const void* d_out, int32_t dtype, const nsa_shape* shape, const nsa_params* params,
+                             float* dq, float* dk, float* dv, float* d_gates, float* dw_k, float* dw_v,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  Dims dm;
+  int st = check_dims(shape, params, dtype, &dm, true);
+  if (st != NSA_OK) return st;
+  if (dm.B == 0 || dm.Tq == 0) return NSA_OK;
+  if (!q || !k || !v || !gates || !block_idx || !d_out || !dq || !dk || !dv || !d_gates || !dw_k || !dw_v)
+    return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (dm.Nc > 0 && (!w_k || !w_v)) return fail(NSA_ERR_INVALID_ARG, "NULL compression weights");
+  const size_t need = bwd_workspace(dm);
+  if (workspace_bytes < need)
+    return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  if (need > 0 && !workspace) return fail(NSA_ERR_INVALID_ARG, "NULL workspace");
+  hipError_t e = launch_layer_bwd(dtype, dm, q, k, v, w_k, w_v, gates, is_video, block_idx, d_out, dq, dk, dv,
+                                  d_gates, dw_k, dw_v, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "backward kernels");
+  return NSA_OK;
+}
+
 }  // extern "C"

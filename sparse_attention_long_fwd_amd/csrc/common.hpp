@@ -70,6 +70,13 @@ __device__ __forceinline__ float block_sum(float x, float* scratch) {
 hipError_t launch_compress(int dtype, int out_mode, const void* x, const float* w, void* out, void* out_lo,
                            int64_t B, int64_t T, int H, int D, int l, int d, int64_t Nc, hipStream_t s);
 
+// Backward pass of the layer (generic kernels): gradients of sum(dout * out); outputs fp32.
+size_t bwd_workspace(const Dims& dm);
+hipError_t launch_layer_bwd(int dtype, const Dims& dm, const void* q, const void* k, const void* v, const float* w_k,
+                            const float* w_v, const float* gates, const uint8_t* vid, const int32_t* idx,
+                            const void* dout, float* dq, float* dk, float* dv, float* dgates, float* dw_k,
+                            float* dw_v, void* ws, hipStream_t s);
+
 // cdtype: element type of the compressed keys / values (dtype or fp32).
 hipError_t launch_cmp_generic(int dtype, int cdtype, const Dims& dm, const void* q, const void* kc, const void* vc,
                               const uint8_t* vid, void* o, float* lse, float* imp, hipStream_t s);

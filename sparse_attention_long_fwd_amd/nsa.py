@@ -64,6 +64,9 @@ EXPORTS = {
     "nsa_gate_proj": (_I32, [_P, _P, _P, _I32, _I64, _I64, _I32, _I32, _P, _P]),
     "nsa_hybrid_layer_fwd_branch_kv": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _SH, _PR,
                                               _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "nsa_hybrid_layer_bwd_workspace_size": (_SZ, [_SH, _PR, _I32]),
+    "nsa_hybrid_layer_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _SH, _PR, _P, _P, _P, _P, _P, _P, _P,
+                                    _SZ, _P]),
     "nsa_set_force_generic": (_I32, [_I32]),
     "nsa_profile_enable": (_I32, [_I32]),
     "nsa_profile_read": (_I32, [ctypes.POINTER(ctypes.c_float), _I32]),
@@ -302,3 +305,28 @@ def nsa_hybrid_layer_fwd_branch_kv(q, kv_c, kv_s, kv_w, gates, shape: NsaShape, 
         ctypes.byref(params), _ptr(out), _ptr(o_cmp), _ptr(o_slc), _ptr(o_swa), _ptr(block_idx_out),
         _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+def nsa_hybrid_layer_bwd_workspace_size(shape: NsaShape, params: NsaParams, dtype_code: int) -> int:
+    return int(lib().nsa_hybrid_layer_bwd_workspace_size(ctypes.byref(shape), ctypes.byref(params), dtype_code))
+
+
+def nsa_hybrid_layer_bwd(q, k, v, gates, block_idx, d_out, shape: NsaShape, params: NsaParams, w_k=None, w_v=None,
+                         is_video=None, workspace=None, stream=None):
+    """Gradients of sum(d_out * out): returns dict dq, dk, dv, d_gates, dw_k, dw_v (fp32)."""
+    dt = _dtype_code(q)
+    dev = q.device
+    f32 = torch.float32
+    g = dict(dq=torch.empty(q.shape, dtype=f32, device=dev), dk=torch.empty(k.shape, dtype=f32, device=dev),
+             dv=torch.empty(v.shape, dtype=f32, device=dev), d_gates=torch.empty(gates.shape, dtype=f32, device=dev),
+             dw_k=torch.empty(params.cmp_block, dtype=f32, device=dev),
+             dw_v=torch.empty(params.cmp_block, dtype=f32, device=dev))
+    if workspace is None:
+        workspace = torch.empty(max(1, nsa_hybrid_layer_bwd_workspace_size(shape, params, dt)), dtype=torch.uint8,
+                                device=dev)
+    _check(lib().nsa_hybrid_layer_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(w_k), _ptr(w_v), _ptr(gates), _ptr(is_video),
+                                      _ptr(block_idx), _ptr(d_out), dt, ctypes.byref(shape), ctypes.byref(params),
+                                      _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["d_gates"]),
+                                      _ptr(g["dw_k"]), _ptr(g["dw_v"]), _ptr(workspace), workspace.numel(),
+                                      _stream(stream)))
+    return g
