@@ -72,6 +72,7 @@ def parse():
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-phase timing pass")
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-gate-proj", action="store_true", help="skip the gate projection measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement (36K)")
     ap.add_argument("--no-budget-sweep", action="store_true",
                     help="skip the fixed-budget (top-n, window) performance surface")
     ap.add_argument("--sweep-steps", type=int, default=5, help="timed steps per budget point")
@@ -400,6 +401,37 @@ def branch_kv(args, wl, inp):
     return dict(workload=wl.name, ms_per_step=ms, tokens_per_s=Tq * B / (ms * 1e-3), steps=args.sweep_steps)
 
 
+def backward(args):
+    """Backward pass (generic kernels) of the 36K layer: gradients of sum(d_out * out) for q, k,
+    v, the gates and the compression weights, the forward's chosen blocks held fixed."""
+    import torch
+    from sparse_attention_long_fwd_amd import accounting, nsa, synth
+
+    wl = synth.WORKLOADS["36k"]
+    stream = torch.cuda.current_stream()
+    inp = synth.make_inputs(wl, "cuda")
+    B, Tq, Hq, D = inp["q"].shape
+    sh = nsa.make_shape(B, Tq, wl.kv_len, wl.q_start, Hq, wl.num_kv_heads, D)
+    pr = nsa.make_params(**wl.params())
+    idx = torch.full((B, Tq, wl.num_kv_heads, wl.top_n), -1, dtype=torch.int32, device="cuda")
+    nsa.nsa_hybrid_layer_fwd(inp["q"], inp["k"], inp["v"], inp["gates"], sh, pr, w_k=inp["w_k"], w_v=inp["w_v"],
+                             is_video=inp["is_video"], block_idx_out=idx, stream=stream)
+    dout = synth.normal(1000 * wl.index + 900, (B, Tq, Hq, D), "cuda").to(torch.bfloat16)
+    ws = torch.empty(nsa.nsa_hybrid_layer_bwd_workspace_size(sh, pr, nsa.NSA_BF16), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        nsa.nsa_hybrid_layer_bwd(inp["q"], inp["k"], inp["v"], inp["gates"], idx, dout, sh, pr, w_k=inp["w_k"],
+                                 w_v=inp["w_v"], is_video=inp["is_video"], workspace=ws, stream=stream)
+
+    step()
+    ms = time_calls(step, 1, stream)
+    fl = accounting.backward_flops(wl)["total"]
+    del inp, ws
+    return dict(workload=wl.name, kernels="generic (VALU)", ms_per_step=ms, algo_flops=fl,
+                tflops=fl / (ms * 1e-3) / 1e12, mfma_frac=fl / (ms * 1e-3) / PEAK_BF16_MFMA, steps=1)
+
+
 def decode(args):
     """16 x 64K decode step, rotating over 4 independent caches."""
     import torch
@@ -686,6 +718,11 @@ def main():
         log("gate projection")
         gp = gate_proj(args, wl)
         torch.cuda.empty_cache()
+    bwd = None
+    if not args.no_backward:
+        log("backward (36K)")
+        bwd = backward(args)
+        torch.cuda.empty_cache()
     dec = None
     if not args.no_decode:
         log("decode")
@@ -718,6 +755,7 @@ def main():
         "roofline": roofline,
         "decode": dec,
         "gate_proj": gp,
+        "backward": bwd,
         "budget_sweep": sweep,
         "branch_kv": bkv,
         "cpu_baseline": cpu,

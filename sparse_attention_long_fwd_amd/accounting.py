@@ -58,6 +58,16 @@ def flops(wl) -> Dict[str, float]:
     return f
 
 
+def backward_flops(wl) -> Dict[str, float]:
+    """Algorithmic FLOPs of the backward pass: per attended (query head, key) pair the score
+    and the upstream product <d_out, v> (recomputed), and the three gradient products dq, dk, dv,
+    each 2 D: 10 D per pair (2.5x the forward's 4 D)."""
+    c = pair_counts(wl)
+    f = {k: 10.0 * wl.head_dim * v for k, v in c.items()}
+    f["total"] = sum(f.values())
+    return f
+
+
 def dense_causal_pairs(T: int) -> int:
     """Causal (query, key) pairs of one head over T tokens."""
     return T * (T + 1) // 2
