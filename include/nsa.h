@@ -287,8 +287,8 @@ int32_t nsa_hybrid_layer_fwd_branch_kv(const void* q, const void* k_c, const voi
  *  the forward; block_idx [B, q_len, Hkv, top_n] int32 (the forward's choice).
  *  Outputs, all fp32 and required: dq [B, q_len, Hq, D], dk, dv
  *  [B, kv_len, Hkv, D], d_gates [B, q_len, Hq, 3] (0 for text rows), dw_k,
- *  dw_v [cmp_block] (summed over the batch).  Generic kernels: head_dim <= 256
- *  and a multiple of 8, fp32 or bf16.  workspace:
+ *  dw_v [cmp_block] (summed over the batch).  Generic kernels: head_dim a
+ *  multiple of 64 up to 256 (else NSA_ERR_UNSUPPORTED), fp32 or bf16.  workspace:
  *  nsa_hybrid_layer_bwd_workspace_size() bytes.
  */
 size_t nsa_hybrid_layer_bwd_workspace_size(const nsa_shape* shape, const nsa_params* params, int32_t dtype);

@@ -617,6 +617,7 @@ int32_t nsa_hybrid_layer_bwd(const void* q, const void* k, const void* v, const 
   if (!q || !k || !v || !gates || !block_idx || !d_out || !dq || !dk || !dv || !d_gates || !dw_k || !dw_v)
     return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (dm.Nc > 0 && (!w_k || !w_v)) return fail(NSA_ERR_INVALID_ARG, "NULL compression weights");
+  if (!bwd_supported(dm)) return fail(NSA_ERR_UNSUPPORTED, "backward kernels cover head_dim 64, 128, 192, 256");
   const size_t need = bwd_workspace(dm);
   if (workspace_bytes < need)
     return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, need);

@@ -31,10 +31,34 @@
 namespace {
 constexpr int KB = 32;        // keys per workgroup of the key kernels
 constexpr int LPK = 8;        // lanes per key
-constexpr int MAXC = 256 / LPK;  // channels per lane (head_dim <= 256)
 }  // namespace
 
 __device__ __forceinline__ float bwd_block_sum(float x, float* red) { return block_sum(x, red); }
+
+// 8 consecutive elements (16-byte aligned for bf16, 32-byte for fp32) widened to float
+__device__ __forceinline__ void ld8(const bf16* p, float* f) {
+  typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 v8;
+  const v8 u = *(const v8*)p;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = (float)u[i];
+}
+__device__ __forceinline__ void ld8(const float* p, float* f) {
+  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+// <x, y> over D channels, x in LDS (fp32), y in global memory (8 at a time)
+template <typename TK>
+__device__ __forceinline__ float dot_lds(const float* x, const TK* y, int D) {
+  float acc = 0.f;
+  for (int e = 0; e < D; e += 8) {
+    float f[8];
+    ld8(y + e, f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf(x[e + i], f[i], acc);
+  }
+  return acc;
+}
 
 // ---------------------------------------------------------------------------
 // Stage 1.  For one query vector qs (LDS) and upstream gradient ds_ (LDS) over a key list:
@@ -50,12 +74,7 @@ __device__ float2 bwd_branch_rows(const float* qs, const float* dos, const TK* k
     const int64_t a = a0 + tid;
     const int64_t u = a < nslots ? key_of(a) : -1;
     float z = -INFINITY;
-    if (u >= 0) {
-      const TK* kr = kb + u * kstride;
-      float acc = 0.f;
-      for (int e = 0; e < D; ++e) acc = fmaf(qs[e], to_f32(kr[e]), acc);
-      z = acc * scale;
-    }
+    if (u >= 0) z = dot_lds(qs, kb + u * kstride, D) * scale;
     const float mc = block_max(z, red);
     const float m_new = fmaxf(m_run, mc);
     const float p = (u >= 0 && m_new > -INFINITY) ? expf(z - m_new) : 0.f;
@@ -73,15 +92,8 @@ __device__ float2 bwd_branch_rows(const float* qs, const float* dos, const TK* k
     const int64_t u = a < nslots ? key_of(a) : -1;
     float p = 0.f, dpv = 0.f;
     if (u >= 0) {
-      const TK* kr = kb + u * kstride;
-      const TK* vr = vb + u * kstride;
-      float acc = 0.f, accv = 0.f;
-      for (int e = 0; e < D; ++e) {
-        acc = fmaf(qs[e], to_f32(kr[e]), acc);
-        accv = fmaf(dos[e], to_f32(vr[e]), accv);
-      }
-      p = expf(acc * scale - L);
-      dpv = accv;
+      p = expf(dot_lds(qs, kb + u * kstride, D) * scale - L);
+      dpv = dot_lds(dos, vb + u * kstride, D);
     }
     E += bwd_block_sum(p * dpv, red);
     __syncthreads();
@@ -179,16 +191,23 @@ __global__ void __launch_bounds__(BWD_THREADS)
 // Stage 2.  Lane c8 = tid % 8 of key kk = tid / 8 owns channels [c8 nc, c8 nc + nc), nc = D / 8.
 // One (row, head, branch) term: P = exp(scale <q, k> - L), ds = g P (<d_out, v> - E);
 // dk += scale ds q, dv += g P d_out on the lane's channels.  `on` masks the key.
-template <typename TK, typename TQ>
-__device__ __forceinline__ void bwd_key_term(const TK* kr, const TK* vr, const TQ* qr, const TQ* dr, int nc,
+template <int MAXC, typename TQ>
+__device__ __forceinline__ void bwd_key_term(const float* kf, const float* vf, const TQ* qr, const TQ* dr, int nc,
                                              float scale, float L, float E, float gate, bool on, float* ak,
                                              float* av) {
+  float qf[MAXC], df[MAXC];
+#pragma unroll
+  for (int c = 0; c < MAXC; c += 8)
+    if (c < nc) {
+      ld8(qr + c, qf + c);
+      ld8(dr + c, df + c);
+    }
   float zq = 0.f, zd = 0.f;
 #pragma unroll
   for (int c = 0; c < MAXC; ++c)
     if (c < nc) {
-      zq = fmaf(to_f32(qr[c]), to_f32(kr[c]), zq);
-      zd = fmaf(to_f32(dr[c]), to_f32(vr[c]), zd);
+      zq = fmaf(qf[c], kf[c], zq);
+      zd = fmaf(df[c], vf[c], zd);
     }
 #pragma unroll
   for (int o = LPK / 2; o >= 1; o >>= 1) {
@@ -201,14 +220,25 @@ __device__ __forceinline__ void bwd_key_term(const TK* kr, const TK* vr, const T
 #pragma unroll
   for (int c = 0; c < MAXC; ++c)
     if (c < nc) {
-      ak[c] = fmaf(scale * ds, to_f32(qr[c]), ak[c]);
-      av[c] = fmaf(gate * p, to_f32(dr[c]), av[c]);
+      ak[c] = fmaf(scale * ds, qf[c], ak[c]);
+      av[c] = fmaf(gate * p, df[c], av[c]);
+    }
+}
+
+// The lane's nc channels of one key row, widened once.
+template <int MAXC, typename TK>
+__device__ __forceinline__ void load_key(const TK* kr, const TK* vr, int nc, float* kf, float* vf) {
+#pragma unroll
+  for (int c = 0; c < MAXC; c += 8)
+    if (c < nc) {
+      ld8(kr + c, kf + c);
+      ld8(vr + c, vf + c);
     }
 }
 
 // Full-resolution keys [u0, u0 + 32) of KV head g: window and selection terms of video rows,
 // dense terms of text rows.
-template <typename T>
+template <typename T, int MAXC>
 __global__ void __launch_bounds__(BWD_THREADS)
     bwd_key_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                    const int32_t* __restrict__ idx, const uint8_t* __restrict__ vid, const float* __restrict__ gates,
@@ -224,9 +254,10 @@ __global__ void __launch_bounds__(BWD_THREADS)
   const int64_t kstride = (int64_t)dm.Hkv * D;
   const T* kr = k + (b * dm.T + ur) * kstride + (int64_t)g * D + c8 * nc;
   const T* vr = v + (b * dm.T + ur) * kstride + (int64_t)g * D + c8 * nc;
-  float ak[MAXC], av[MAXC];
+  float ak[MAXC], av[MAXC], kf[MAXC], vf[MAXC];
 #pragma unroll
-  for (int c = 0; c < MAXC; ++c) ak[c] = av[c] = 0.f;
+  for (int c = 0; c < MAXC; ++c) ak[c] = av[c] = kf[c] = vf[c] = 0.f;
+  load_key<MAXC>(kr, vr, nc, kf, vf);
   const int64_t ulast = (u0 + KB - 1 < dm.T - 1) ? u0 + KB - 1 : dm.T - 1;
   // rows that can see a key of the block: t >= u0 (causal), among the query rows
   int64_t r0 = u0 - dm.q0;
@@ -260,11 +291,11 @@ __global__ void __launch_bounds__(BWD_THREADS)
       const T* qr = q + row * D + c8 * nc;
       const T* dr = dout + row * D + c8 * nc;
       if (!is_vid) {
-        bwd_key_term(kr, vr, qr, dr, nc, dm.scale, st_l[row * 3], st_e[row * 3], 1.f, in_txt, ak, av);
+        bwd_key_term<MAXC>(kf, vf, qr, dr, nc, dm.scale, st_l[row * 3], st_e[row * 3], 1.f, in_txt, ak, av);
       } else {
         const float* gg = gates + row * 3;
-        bwd_key_term(kr, vr, qr, dr, nc, dm.scale, st_l[row * 3 + 1], st_e[row * 3 + 1], gg[1], in_slc, ak, av);
-        bwd_key_term(kr, vr, qr, dr, nc, dm.scale, st_l[row * 3 + 2], st_e[row * 3 + 2], gg[2], in_swa, ak, av);
+        bwd_key_term<MAXC>(kf, vf, qr, dr, nc, dm.scale, st_l[row * 3 + 1], st_e[row * 3 + 1], gg[1], in_slc, ak, av);
+        bwd_key_term<MAXC>(kf, vf, qr, dr, nc, dm.scale, st_l[row * 3 + 2], st_e[row * 3 + 2], gg[2], in_swa, ak, av);
       }
     }
   }
@@ -280,7 +311,7 @@ __global__ void __launch_bounds__(BWD_THREADS)
 }
 
 // Compressed keys [i0, i0 + 32) of KV head g: compression-branch terms of video rows.
-template <typename T>
+template <typename T, int MAXC>
 __global__ void __launch_bounds__(BWD_THREADS)
     bwd_ckey_kernel(const T* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
                     const uint8_t* __restrict__ vid, const float* __restrict__ gates, const T* __restrict__ dout,
@@ -296,9 +327,10 @@ __global__ void __launch_bounds__(BWD_THREADS)
   const int64_t kstride = (int64_t)dm.Hkv * D;
   const float* kr = kc + (b * dm.Nc + ir) * kstride + (int64_t)g * D + c8 * nc;
   const float* vr = vc + (b * dm.Nc + ir) * kstride + (int64_t)g * D + c8 * nc;
-  float ak[MAXC], av[MAXC];
+  float ak[MAXC], av[MAXC], kf[MAXC], vf[MAXC];
 #pragma unroll
-  for (int c = 0; c < MAXC; ++c) ak[c] = av[c] = 0.f;
+  for (int c = 0; c < MAXC; ++c) ak[c] = av[c] = kf[c] = vf[c] = 0.f;
+  load_key<MAXC>(kr, vr, nc, kf, vf);
   const int64_t end_i = i * dm.d + dm.l - 1;  // the key is visible from this position on
   int64_t r0 = i0 * dm.d + dm.l - 1 - dm.q0;
   if (r0 < 0) r0 = 0;
@@ -309,7 +341,7 @@ __global__ void __launch_bounds__(BWD_THREADS)
     for (int hh = 0; hh < dm.G; ++hh) {
       const int h = g * dm.G + hh;
       const int64_t row = (b * dm.Tq + r) * dm.Hq + h;
-      bwd_key_term(kr, vr, q + row * D + c8 * nc, dout + row * D + c8 * nc, nc, dm.scale, st_l[row * 3],
+      bwd_key_term<MAXC>(kf, vf, q + row * D + c8 * nc, dout + row * D + c8 * nc, nc, dm.scale, st_l[row * 3],
                    st_e[row * 3], gates[row * 3], on, ak, av);
     }
   }
@@ -384,6 +416,9 @@ __global__ void bwd_fill_kernel(float* __restrict__ p, int64_t n) {
   if (x < n) p[x] = 0.f;
 }
 
+// Each lane of a key takes D / 8 channels in runs of 8: head_dim a multiple of 64, at most 256.
+bool bwd_supported(const Dims& dm) { return dm.D <= 256 && dm.D % (8 * LPK) == 0; }
+
 static size_t brup(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t bwd_workspace(const Dims& dm) {
@@ -415,13 +450,22 @@ static hipError_t launch_bwd_t(const Dims& dm, const void* q, const void* k, con
   bwd_fill_kernel<<<dim3((unsigned)((dm.l + 255) / 256)), dim3(256), 0, s>>>(dw_v, dm.l);
   bwd_row_kernel<T><<<dim3((unsigned)dm.Tq, (unsigned)dm.Hkv, (unsigned)dm.B), dim3(BWD_THREADS), 0, s>>>(
       (const T*)q, (const T*)k, (const T*)v, kc, vc, idx, vid, gates, (const T*)dout, dq, dgates, st_l, st_e, dm);
-  bwd_key_kernel<T><<<dim3((unsigned)((dm.T + KB - 1) / KB), (unsigned)dm.Hkv, (unsigned)dm.B), dim3(BWD_THREADS), 0,
-                      s>>>((const T*)q, (const T*)k, (const T*)v, idx, vid, gates, (const T*)dout, st_l, st_e, dk, dv,
-                           dm);
+  // channels per lane: 16 (head_dim <= 128) or 32 (<= 256)
+  const dim3 gk((unsigned)((dm.T + KB - 1) / KB), (unsigned)dm.Hkv, (unsigned)dm.B);
+  if (dm.D <= 128)
+    bwd_key_kernel<T, 16><<<gk, dim3(BWD_THREADS), 0, s>>>((const T*)q, (const T*)k, (const T*)v, idx, vid, gates,
+                                                          (const T*)dout, st_l, st_e, dk, dv, dm);
+  else
+    bwd_key_kernel<T, 32><<<gk, dim3(BWD_THREADS), 0, s>>>((const T*)q, (const T*)k, (const T*)v, idx, vid, gates,
+                                                          (const T*)dout, st_l, st_e, dk, dv, dm);
   if (dm.Nc > 0) {
-    bwd_ckey_kernel<T><<<dim3((unsigned)((dm.Nc + KB - 1) / KB), (unsigned)dm.Hkv, (unsigned)dm.B),
-                         dim3(BWD_THREADS), 0, s>>>((const T*)q, kc, vc, vid, gates, (const T*)dout, st_l, st_e, dkc,
-                                                    dvc, dm);
+    const dim3 gc((unsigned)((dm.Nc + KB - 1) / KB), (unsigned)dm.Hkv, (unsigned)dm.B);
+    if (dm.D <= 128)
+      bwd_ckey_kernel<T, 16><<<gc, dim3(BWD_THREADS), 0, s>>>((const T*)q, kc, vc, vid, gates, (const T*)dout, st_l,
+                                                             st_e, dkc, dvc, dm);
+    else
+      bwd_ckey_kernel<T, 32><<<gc, dim3(BWD_THREADS), 0, s>>>((const T*)q, kc, vc, vid, gates, (const T*)dout, st_l,
+                                                             st_e, dkc, dvc, dm);
     const int64_t tot = dm.B * dm.T * dm.Hkv * dm.D;
     bwd_compress_kernel<<<dim3((unsigned)((tot + BWD_THREADS - 1) / BWD_THREADS)), dim3(BWD_THREADS), 0, s>>>(
         dkc, dvc, w_k, w_v, dk, dv, dm);
@@ -436,7 +480,7 @@ hipError_t launch_layer_bwd(int dtype, const Dims& dm, const void* q, const void
                             const void* dout, float* dq, float* dk, float* dv, float* dgates, float* dw_k,
                             float* dw_v, void* ws, hipStream_t s) {
   if (dm.B <= 0 || dm.Tq <= 0) return hipSuccess;
-  if (dm.D > 256 || dm.D % LPK != 0) return hipErrorInvalidValue;
+  if (!bwd_supported(dm)) return hipErrorInvalidValue;
   return dtype == 1 ? launch_bwd_t<bf16>(dm, q, k, v, w_k, w_v, gates, vid, idx, dout, dq, dk, dv, dgates, dw_k,
                                          dw_v, ws, s)
                     : launch_bwd_t<float>(dm, q, k, v, w_k, w_v, gates, vid, idx, dout, dq, dk, dv, dgates, dw_k,

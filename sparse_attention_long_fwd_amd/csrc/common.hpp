@@ -72,6 +72,7 @@ hipError_t launch_compress(int dtype, int out_mode, const void* x, const float* 
 
 // Backward pass of the layer (generic kernels): gradients of sum(dout * out); outputs fp32.
 size_t bwd_workspace(const Dims& dm);
+bool bwd_supported(const Dims& dm);
 hipError_t launch_layer_bwd(int dtype, const Dims& dm, const void* q, const void* k, const void* v, const float* w_k,
                             const float* w_v, const float* gates, const uint8_t* vid, const int32_t* idx,
                             const void* dout, float* dq, float* dk, float* dv, float* dgates, float* dw_k,

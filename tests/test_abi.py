@@ -195,3 +195,20 @@ def test_branch_kv_decode_needs_one_selection_window_kv():
     assert L.nsa_hybrid_layer_fwd_branch_kv(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE,
                                             None, nsa.NSA_BF16, ctypes.byref(sh2), ctypes.byref(pr), FAKE, None, None,
                                             None, None, FAKE, 1 << 40, None) == nsa.NSA_ERR_INVALID_ARG
+
+
+def test_backward_validates_first():
+    L = nsa.lib()
+    pr = _params()
+
+    def call(sh, idx=FAKE, ws=1 << 40, dq=FAKE):
+        return L.nsa_hybrid_layer_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, idx, FAKE, nsa.NSA_BF16,
+                                      ctypes.byref(sh), ctypes.byref(pr), dq, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+                                      None)
+
+    assert call(_shape(head_dim=72)) == nsa.NSA_ERR_UNSUPPORTED      # not a multiple of 64
+    assert call(_shape(), idx=None) == nsa.NSA_ERR_INVALID_ARG        # the forward's chosen blocks are required
+    assert call(_shape(), dq=None) == nsa.NSA_ERR_INVALID_ARG
+    need = nsa.nsa_hybrid_layer_bwd_workspace_size(_shape(), pr, nsa.NSA_BF16)
+    assert need > 0 and call(_shape(), ws=need - 1) == nsa.NSA_ERR_WORKSPACE_TOO_SMALL
+    assert call(_shape(q_len=0)) == nsa.NSA_OK                        # no rows: nothing launched
