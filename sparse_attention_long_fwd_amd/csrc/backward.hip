@@ -61,58 +61,156 @@ __device__ __forceinline__ float dot_lds(const float* x, const TK* y, int D) {
 }
 
 // ---------------------------------------------------------------------------
-// Stage 1.  For one query vector qs (LDS) and upstream gradient ds_ (LDS) over a key list:
-// returns (L, E) and adds g * scale * (sum P dpv k - E sum P k) to dq (thread e < D owns channel e).
+// Stage 1.  Up to HB heads of one KV group at once over one key list, so each key row is read
+// once for all of them.  qs, dos: [HB][D] query and upstream gradient (LDS); thread e < D owns
+// channel e of dqs [HB][D] (LDS), to which g_h scale (sum P dpv k - E sum P k) is added.  On
+// return L[h], E[h] (uniform) are each head's log-sum-exp (-inf for an empty list) and E.
+constexpr int HB = 8;
+
 template <typename TK, typename KeyFn>
-__device__ float2 bwd_branch_rows(const float* qs, const float* dos, const TK* kb, const TK* vb, int64_t kstride,
-                                  int D, int64_t nslots, KeyFn key_of, float scale, float gate, float* dq,
-                                  float* ps, float* pds, int64_t* us, float* red) {
-  const int tid = threadIdx.x;
-  // pass A: log-sum-exp (online over chunks of 256 slots)
-  float m_run = -INFINITY, l_run = 0.f;
-  for (int64_t a0 = 0; a0 < nslots; a0 += BWD_THREADS) {
-    const int64_t a = a0 + tid;
-    const int64_t u = a < nslots ? key_of(a) : -1;
-    float z = -INFINITY;
-    if (u >= 0) z = dot_lds(qs, kb + u * kstride, D) * scale;
-    const float mc = block_max(z, red);
-    const float m_new = fmaxf(m_run, mc);
-    const float p = (u >= 0 && m_new > -INFINITY) ? expf(z - m_new) : 0.f;
-    const float lc = bwd_block_sum(p, red);
-    if (m_new == -INFINITY) continue;
-    l_run = (m_run == -INFINITY ? 0.f : l_run * expf(m_run - m_new)) + lc;
-    m_run = m_new;
+__device__ void bwd_branch_rows(const float* qs, const float* dos, const TK* kb, const TK* vb, int64_t kstride,
+                                int D, int64_t nslots, KeyFn key_of, float scale, const float* gate, int nh,
+                                float* dqs, float* ps, float* pds, int64_t* us, float* wred, float* L, float* E) {
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  float m_run[HB], l_run[HB];
+#pragma unroll
+  for (int h = 0; h < HB; ++h) {
+    m_run[h] = -INFINITY;
+    l_run[h] = 0.f;
   }
-  if (!(l_run > 0.f)) return make_float2(-INFINITY, 0.f);  // no key: the branch output is 0
-  const float L = m_run + logf(l_run);
-  // pass B: E = sum P dpv, and per channel A1 = sum P dpv k, A2 = sum P k
-  float E = 0.f, a1 = 0.f, a2 = 0.f;
+  // reduce x[h] over the workgroup (op: 0 max, 1 sum); uniform result in x
+  auto reduce = [&](float* x, int op) {
+#pragma unroll
+    for (int h = 0; h < HB; ++h) x[h] = op ? wave_sum(x[h]) : wave_max(x[h]);
+    __syncthreads();  // earlier readers of wred are done
+    if (lane == 0)
+#pragma unroll
+      for (int h = 0; h < HB; ++h) wred[wv * HB + h] = x[h];
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+      float r = wred[h];
+      for (int w2 = 1; w2 < BWD_THREADS / 64; ++w2) r = op ? r + wred[w2 * HB + h] : fmaxf(r, wred[w2 * HB + h]);
+      x[h] = r;
+    }
+  };
+  // pass A: log-sum-exp per head (online over chunks of 256 slots)
   for (int64_t a0 = 0; a0 < nslots; a0 += BWD_THREADS) {
     const int64_t a = a0 + tid;
     const int64_t u = a < nslots ? key_of(a) : -1;
-    float p = 0.f, dpv = 0.f;
+    float z[HB];
+#pragma unroll
+    for (int h = 0; h < HB; ++h) z[h] = -INFINITY;
     if (u >= 0) {
-      p = expf(dot_lds(qs, kb + u * kstride, D) * scale - L);
-      dpv = dot_lds(dos, vb + u * kstride, D);
+      const TK* kr = kb + u * kstride;
+      float acc[HB];
+#pragma unroll
+      for (int h = 0; h < HB; ++h) acc[h] = 0.f;
+      for (int e = 0; e < D; e += 8) {
+        float f[8];
+        ld8(kr + e, f);
+#pragma unroll
+        for (int h = 0; h < HB; ++h)
+          if (h < nh)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[h] = fmaf(qs[h * D + e + i], f[i], acc[h]);
+      }
+#pragma unroll
+      for (int h = 0; h < HB; ++h)
+        if (h < nh) z[h] = acc[h] * scale;
     }
-    E += bwd_block_sum(p * dpv, red);
-    __syncthreads();
-    ps[tid] = p;
-    pds[tid] = p * dpv;
+    float mx[HB], p[HB];
+#pragma unroll
+    for (int h = 0; h < HB; ++h) mx[h] = z[h];
+    reduce(mx, 0);
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+      mx[h] = fmaxf(m_run[h], mx[h]);
+      p[h] = (u >= 0 && mx[h] > -INFINITY) ? expf(z[h] - mx[h]) : 0.f;
+    }
+    reduce(p, 1);
+#pragma unroll
+    for (int h = 0; h < HB; ++h)
+      if (mx[h] > -INFINITY) {
+        l_run[h] = (m_run[h] == -INFINITY ? 0.f : l_run[h] * expf(m_run[h] - mx[h])) + p[h];
+        m_run[h] = mx[h];
+      }
+  }
+#pragma unroll
+  for (int h = 0; h < HB; ++h) {
+    L[h] = l_run[h] > 0.f ? m_run[h] + logf(l_run[h]) : -INFINITY;
+    E[h] = 0.f;
+  }
+  // pass B: E = sum P dpv, and per channel A1 = sum P dpv k, A2 = sum P k
+  float a1[HB], a2[HB];
+#pragma unroll
+  for (int h = 0; h < HB; ++h) a1[h] = a2[h] = 0.f;
+  for (int64_t a0 = 0; a0 < nslots; a0 += BWD_THREADS) {
+    const int64_t a = a0 + tid;
+    const int64_t u = a < nslots ? key_of(a) : -1;
+    float p[HB], pd[HB];
+#pragma unroll
+    for (int h = 0; h < HB; ++h) p[h] = pd[h] = 0.f;
+    if (u >= 0) {
+      const TK* kr = kb + u * kstride;
+      const TK* vr = vb + u * kstride;
+      float aq[HB], ad[HB];
+#pragma unroll
+      for (int h = 0; h < HB; ++h) aq[h] = ad[h] = 0.f;
+      for (int e = 0; e < D; e += 8) {
+        float fk[8], fv[8];
+        ld8(kr + e, fk);
+        ld8(vr + e, fv);
+#pragma unroll
+        for (int h = 0; h < HB; ++h)
+          if (h < nh)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              aq[h] = fmaf(qs[h * D + e + i], fk[i], aq[h]);
+              ad[h] = fmaf(dos[h * D + e + i], fv[i], ad[h]);
+            }
+      }
+#pragma unroll
+      for (int h = 0; h < HB; ++h)
+        if (h < nh && L[h] > -INFINITY) {
+          p[h] = expf(aq[h] * scale - L[h]);
+          pd[h] = p[h] * ad[h];
+        }
+    }
+    float es[HB];
+#pragma unroll
+    for (int h = 0; h < HB; ++h) es[h] = wave_sum(pd[h]);
+    __syncthreads();  // the previous chunk's readers of ps, pds, us and wred are done
+    if (lane == 0)
+#pragma unroll
+      for (int h = 0; h < HB; ++h) wred[wv * HB + h] = es[h];
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+      ps[h * BWD_THREADS + tid] = p[h];
+      pds[h * BWD_THREADS + tid] = pd[h];
+    }
     us[tid] = u;
     __syncthreads();
+#pragma unroll
+    for (int h = 0; h < HB; ++h)
+      for (int w2 = 0; w2 < BWD_THREADS / 64; ++w2) E[h] += wred[w2 * HB + h];
     if (tid < D) {
       const int64_t cnt = (nslots - a0 < BWD_THREADS) ? nslots - a0 : BWD_THREADS;
       for (int c = 0; c < cnt; ++c)
         if (us[c] >= 0) {
           const float kv = to_f32(kb[us[c] * kstride + tid]);
-          a1 = fmaf(pds[c], kv, a1);
-          a2 = fmaf(ps[c], kv, a2);
+#pragma unroll
+          for (int h = 0; h < HB; ++h) {
+            a1[h] = fmaf(pds[h * BWD_THREADS + c], kv, a1[h]);
+            a2[h] = fmaf(ps[h * BWD_THREADS + c], kv, a2[h]);
+          }
         }
     }
   }
-  if (tid < D) dq[tid] += gate * scale * (a1 - E * a2);
-  return make_float2(L, E);
+  if (tid < D)
+#pragma unroll
+    for (int h = 0; h < HB; ++h)
+      if (h < nh) dqs[h * D + tid] += gate[h] * scale * (a1[h] - E[h] * a2[h]);
 }
 
 template <typename T>
@@ -122,10 +220,10 @@ __global__ void __launch_bounds__(BWD_THREADS)
                    const uint8_t* __restrict__ vid, const float* __restrict__ gates, const T* __restrict__ dout,
                    float* __restrict__ dq, float* __restrict__ dgates, float* __restrict__ st_l,
                    float* __restrict__ st_e, Dims dm) {
-  __shared__ float qs[256], dos[256], dqs[256];
-  __shared__ float ps[BWD_THREADS], pds[BWD_THREADS];
+  __shared__ float qs[HB * 256], dos[HB * 256], dqs[HB * 256];
+  __shared__ float ps[HB * BWD_THREADS], pds[HB * BWD_THREADS];
   __shared__ int64_t us[BWD_THREADS];
-  __shared__ float red[16];
+  __shared__ float wred[(BWD_THREADS / 64) * HB];
   const int64_t r = blockIdx.x;
   const int g = blockIdx.y;
   const int64_t b = blockIdx.z;
@@ -140,50 +238,67 @@ __global__ void __launch_bounds__(BWD_THREADS)
   const float* vcb = vc + (b * dm.Nc * dm.Hkv + g) * (int64_t)D;
   const int32_t* sel = idx ? idx + ((b * dm.Tq + r) * dm.Hkv + g) * dm.n : nullptr;
   const int ls = dm.ls;
-  for (int hh = 0; hh < dm.G; ++hh) {
-    const int h = g * dm.G + hh;
-    const int64_t row = (b * dm.Tq + r) * dm.Hq + h;
+  const int64_t row0 = (b * dm.Tq + r) * dm.Hq + (int64_t)g * dm.G;  // the group's first head's row
+  for (int hb = 0; hb < dm.G; hb += HB) {
+    const int nh = dm.G - hb < HB ? dm.G - hb : HB;
     __syncthreads();
-    for (int e = tid; e < D; e += BWD_THREADS) {
-      qs[e] = to_f32(q[row * D + e]);
-      dos[e] = to_f32(dout[row * D + e]);
-      dqs[e] = 0.f;
+    for (int x = tid; x < nh * D; x += BWD_THREADS) {
+      const int64_t o = (row0 + hb) * D + x;
+      qs[x] = to_f32(q[o]);
+      dos[x] = to_f32(dout[o]);
+      dqs[x] = 0.f;
     }
     __syncthreads();
-    float2 s0, s1 = make_float2(-INFINITY, 0.f), s2 = make_float2(-INFINITY, 0.f);
+    float L0[HB], E0[HB], L1[HB], E1[HB], L2[HB], E2[HB], gt[HB];
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+      L1[h] = L2[h] = -INFINITY;
+      E1[h] = E2[h] = 0.f;
+    }
     if (!is_vid) {
-      s0 = bwd_branch_rows(qs, dos, kb, vb, kstride, D, t + 1, [=](int64_t a) { return a; }, dm.scale, 1.f, dqs,
-                           ps, pds, us, red);
+#pragma unroll
+      for (int h = 0; h < HB; ++h) gt[h] = 1.f;
+      bwd_branch_rows(qs, dos, kb, vb, kstride, D, t + 1, [=](int64_t a) { return a; }, dm.scale, gt, nh, dqs, ps,
+                      pds, us, wred, L0, E0);
     } else {
-      const float* gg = gates + row * 3;
+      const float* gg = gates + (row0 + hb) * 3;
+#pragma unroll
+      for (int h = 0; h < HB; ++h) gt[h] = h < nh ? gg[3 * h] : 0.f;
       const int64_t nvis = cmp_visible(t, dm.l, dm.d, dm.Nc);
-      s0 = bwd_branch_rows(qs, dos, kcb, vcb, kstride, D, nvis, [=](int64_t a) { return a; }, dm.scale, gg[0],
-                           dqs, ps, pds, us, red);
+      bwd_branch_rows(qs, dos, kcb, vcb, kstride, D, nvis, [=](int64_t a) { return a; }, dm.scale, gt, nh, dqs, ps,
+                      pds, us, wred, L0, E0);
       auto slc_key = [=](int64_t a) -> int64_t {
         const int32_t j = sel[a / ls];
         if (j < 0) return -1;
         const int64_t u = (int64_t)j * ls + (a % ls);
         return (u <= t && u < dm.T) ? u : -1;
       };
-      s1 = bwd_branch_rows(qs, dos, kb, vb, kstride, D, (int64_t)dm.n * ls, slc_key, dm.scale, gg[1], dqs, ps, pds,
-                           us, red);
+#pragma unroll
+      for (int h = 0; h < HB; ++h) gt[h] = h < nh ? gg[3 * h + 1] : 0.f;
+      bwd_branch_rows(qs, dos, kb, vb, kstride, D, (int64_t)dm.n * ls, slc_key, dm.scale, gt, nh, dqs, ps, pds, us,
+                      wred, L1, E1);
       const int64_t lo = t - dm.w + 1 > 0 ? t - dm.w + 1 : 0;
-      s2 = bwd_branch_rows(qs, dos, kb, vb, kstride, D, t - lo + 1, [=](int64_t a) { return lo + a; }, dm.scale,
-                           gg[2], dqs, ps, pds, us, red);
+#pragma unroll
+      for (int h = 0; h < HB; ++h) gt[h] = h < nh ? gg[3 * h + 2] : 0.f;
+      bwd_branch_rows(qs, dos, kb, vb, kstride, D, t - lo + 1, [=](int64_t a) { return lo + a; }, dm.scale, gt, nh,
+                      dqs, ps, pds, us, wred, L2, E2);
     }
     __syncthreads();
-    for (int e = tid; e < D; e += BWD_THREADS) dq[row * D + e] = dqs[e];
-    if (tid == 0) {
-      st_l[row * 3 + 0] = s0.x;
-      st_l[row * 3 + 1] = s1.x;
-      st_l[row * 3 + 2] = s2.x;
-      st_e[row * 3 + 0] = s0.y;
-      st_e[row * 3 + 1] = s1.y;
-      st_e[row * 3 + 2] = s2.y;
-      dgates[row * 3 + 0] = is_vid ? s0.y : 0.f;
-      dgates[row * 3 + 1] = is_vid ? s1.y : 0.f;
-      dgates[row * 3 + 2] = is_vid ? s2.y : 0.f;
-    }
+    for (int x = tid; x < nh * D; x += BWD_THREADS) dq[(row0 + hb) * D + x] = dqs[x];
+#pragma unroll
+    for (int h = 0; h < HB; ++h)
+      if (tid == h && h < nh) {
+        const int64_t row = row0 + hb + h;
+        st_l[row * 3 + 0] = L0[h];
+        st_l[row * 3 + 1] = L1[h];
+        st_l[row * 3 + 2] = L2[h];
+        st_e[row * 3 + 0] = E0[h];
+        st_e[row * 3 + 1] = E1[h];
+        st_e[row * 3 + 2] = E2[h];
+        dgates[row * 3 + 0] = is_vid ? E0[h] : 0.f;
+        dgates[row * 3 + 1] = is_vid ? E1[h] : 0.f;
+        dgates[row * 3 + 2] = is_vid ? E2[h] : 0.f;
+      }
   }
 }
 
