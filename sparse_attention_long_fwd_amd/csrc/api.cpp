@@ -347,7 +347,8 @@ int32_t layer_fwd(const void* q, const BranchKV& kv, const void* k_cmp_in, const
   if ((k_cmp_in == nullptr) != (v_cmp_in == nullptr))
     return fail(NSA_ERR_INVALID_ARG, "give both k_cmp_in and v_cmp_in, or neither");
   if (dm.B == 0 || dm.Tq == 0) return NSA_OK;
-  if (!q || !kv.kc || !kv.vc || !kv.ks || !kv.vs || !kv.kw || !kv.vw || !gates)
+  // the compression's keys / values are not read when the compressed cache is given
+  if (!q || (!k_cmp_in && (!kv.kc || !kv.vc)) || !kv.ks || !kv.vs || !kv.kw || !kv.vw || !gates)
     return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (!k_cmp_in && dm.Nc > 0 && (!w_k || !w_v)) return fail(NSA_ERR_INVALID_ARG, "NULL compression weights");
   if (!aligned16(q) || !aligned16(kv.kc) || !aligned16(kv.vc) || !aligned16(kv.ks) || !aligned16(kv.vs) ||
