@@ -77,6 +77,8 @@ def parse():
                     help="skip the fixed-budget (top-n, window) performance surface")
     ap.add_argument("--sweep-steps", type=int, default=5, help="timed steps per budget point")
     ap.add_argument("--no-branch-kv", action="store_true", help="skip the per-branch K/V prefill measurement")
+    ap.add_argument("--varlen-only", action="store_true",
+                    help="with --no-prefill: only the variable-length paged decode (for profiling)")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the variable-length paged decode measurement")
     ap.add_argument("--cpu-sample-rows", type=int, default=0, help="oracle row sample (0: auto)")
@@ -681,7 +683,7 @@ def main():
         del src, dst
     wl = synth.WORKLOADS[args.workload]
     if args.no_prefill:
-        res = {"decode": decode(args)}
+        res = {} if args.varlen_only else {"decode": decode(args)}
         if not args.no_varlen:
             res["decode_varlen"] = decode_varlen(args)
         print(json.dumps(res))
