@@ -16,9 +16,10 @@
 //     picks the top-n blocks itself (wave 0) while its other waves already work
 //     on the window blocks, which need no selection; then every wave takes one
 //     chosen block below the window.  A block is scored once for both the
-//     selection and the window branch.  The last workgroup of a (sequence,
-//     group) to finish merges the compression, selection and window partials
-//     per head and applies the gated combine.  Text rows (dense causal
+//     selection and the window branch; each workgroup leaves one partial per
+//     (branch, head).
+//  3. dmerge: one workgroup per (sequence, group) merges those partials per
+//     head and applies the gated combine with the compression output.  Text rows (dense causal
 //     attention, ungated): their split workgroups exit at once; here each wave
 //     runs an online softmax over a strided share of the blocks.
 #include "fast_common.hpp"
@@ -59,7 +60,7 @@ template <bool SPLIT>
 __global__ void __launch_bounds__(256) dcmp_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kh,
                                                          const bf16* __restrict__ kl, const bf16* __restrict__ vh,
                                                          const bf16* __restrict__ vl, const uint8_t* __restrict__ vid,
-                                                         float* __restrict__ part, int* __restrict__ cnt, Dims dm,
+                                                         float* __restrict__ part, Dims dm,
                                                          int nsplit) {
   constexpr int NA = SPLIT ? 2 : 1;  // staged V arrays (hi, lo)
   // per wave: V rows; after the value products the same bytes hold the waves' outputs [4][16][HD] fp32
@@ -73,8 +74,6 @@ __global__ void __launch_bounds__(256) dcmp_split_kernel(const bf16* __restrict_
   const int unit = blockIdx.x / nsplit;
   const int64_t b = unit / dm.Hkv;
   const int g = unit % dm.Hkv;
-  if (blockIdx.x == 0)  // completion counters of the next kernel
-    for (int i = threadIdx.x; i < dm.B * dm.Hkv; i += blockDim.x) cnt[i] = 0;
   if (vid && !vid[b]) return;
   const int G = dm.G;
   const int64_t t = dm.q0;
@@ -226,7 +225,7 @@ __global__ void __launch_bounds__(256) dcmp_split_kernel(const bf16* __restrict_
 // counters of dsel_kernel.
 __global__ void __launch_bounds__(256) dcmp_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kh,
                                                         const bf16* __restrict__ vh, const uint8_t* __restrict__ vid,
-                                                        float* __restrict__ part, int* __restrict__ cnt, Dims dm,
+                                                        float* __restrict__ part, Dims dm,
                                                         DecVar dv, int nsplit) {
   constexpr int NSTEP = DCH / 32;
   __shared__ __attribute__((aligned(16))) bf16 s_v[4][32 * HD];
@@ -247,8 +246,6 @@ __global__ void __launch_bounds__(256) dcmp_pipe_kernel(const bf16* __restrict__
     s = (blockIdx.x % wpu) * 4 + w;
   }
   const int unit = (int)(b * dm.Hkv + g);
-  if (blockIdx.x == 0)  // completion counters of the next kernel
-    for (int i = threadIdx.x; i < dm.B * dm.Hkv; i += blockDim.x) cnt[i] = 0;
   if ((vid && !vid[b]) || s >= nsplit) return;
   const int G = dm.G;
   // compressed blocks of this sequence seen by its query (every block of a full cache)
@@ -453,7 +450,7 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
                                                    bf16* __restrict__ o_slc, bf16* __restrict__ o_swa,
                                                    float* __restrict__ lse, int32_t* __restrict__ idx,
                                                    float* __restrict__ imp_out, float* __restrict__ part3,
-                                                   float* __restrict__ ocmp32, int* __restrict__ cnt, Dims dm,
+                                                   float* __restrict__ ocmp32, Dims dm,
                                                    DecVar dv, int nsplit, int wgs) {
   extern __shared__ float dsm[];
   const int G = dm.G;
@@ -463,7 +460,6 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
   __shared__ float s_M[16], s_L[16];
   __shared__ int32_t s_idx[32];
   __shared__ TopkScratch s_tk;
-  __shared__ int s_last;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hn = l & 15, grp = l >> 4;
   const int unit = blockIdx.x / wgs, sg = blockIdx.x % wgs;
   const int64_t b = unit / dm.Hkv;
@@ -573,6 +569,8 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
     // ---- importance of blocks 0 .. jt (heads summed in a fixed order)
     dsplit_stats(pc, G, nsplit, s_fac, s_M, s_L);
     __syncthreads();
+    if (sg == 0 && lse && tid < G)
+      lse[b * dm.Hq + g * G + tid] = s_L[tid] > 0.f ? (s_M[tid] + flog2(s_L[tid])) * LN2_F : -INFINITY;
     // 4 blocks a thread per pass; loads clamped to valid addresses and unconditional, so a
     // pass has all of them in flight at once (invalid terms get weight 0)
     for (int j0 = 0; j0 <= jt; j0 += 4 * blockDim.x) {
@@ -725,22 +723,29 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
     }
   }
 
-  // ---- the unit's last workgroup merges.  Every wave's stores have landed in L2 before the
-  // barrier; one agent-scope release (L2 write-back) then publishes the workgroup's partials
-  // before it is counted, and the last workgroup's acquire (cache invalidation, CU- and
-  // XCD-wide) makes every other workgroup's partials visible to all its waves.
-  dwait();
-  __syncthreads();
-  if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const int last = atomicAdd(&cnt[unit], 1) == wgs - 1;
-    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    s_last = last;
-  }
-  __syncthreads();
-  if (!s_last) return;
+  // the workgroup partials are merged by dmerge_kernel (the kernel boundary orders the stores)
+}
+
+
+// ---------------------------------------------------------------------------
+// One workgroup per (sequence, KV group): merges the selection kernel's workgroup partials of the
+// selection and window branches (text rows: the dense partials) per head and writes the outputs,
+// gated for video rows with the compression output.
+__global__ void __launch_bounds__(256) dmerge_kernel(const float* __restrict__ part3,
+                                                     const float* __restrict__ ocmp32,
+                                                     const uint8_t* __restrict__ vid, const float* __restrict__ gates,
+                                                     bf16* __restrict__ out, bf16* __restrict__ o_cmp,
+                                                     bf16* __restrict__ o_slc, bf16* __restrict__ o_swa, Dims dm,
+                                                     int wgs) {
+  constexpr int PO = 4;        // O offset within a partial (16-byte aligned rows)
+  constexpr int PW = HD + PO;  // partial of one (branch, head): max, sum, -, -, O[128]
+  extern __shared__ float s_wgt[];  // [wgs][2][G] weights 2^(m - M) / L of the workgroup partials
+  const int G = dm.G, tid = threadIdx.x;
+  const int unit = blockIdx.x;
+  const int64_t b = unit / dm.Hkv;
+  const int g = unit % dm.Hkv;
+  const bool text = vid && !vid[b];
   const float* pu = part3 + (int64_t)unit * wgs * 2 * G * PW;
-  float* s_wgt = (float*)vt[0];  // [wgs][2][G] weights 2^(m - M) / L of the workgroup partials
   // statistics of the (branch, head) pairs: 16 lanes a pair, one load round for <= 16 partials
   for (int pr0 = 0; pr0 < 2 * G; pr0 += 16) {
     const int pr = pr0 + (tid >> 4), sl = tid & 15;
@@ -768,8 +773,6 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
       }
   }
   __syncthreads();
-  if (!text && lse && tid < G)
-    lse[b * dm.Hq + g * G + tid] = s_L[tid] > 0.f ? (s_M[tid] + flog2(s_L[tid])) * LN2_F : -INFINITY;
   for (int i = tid; i < G * HD / 4; i += blockDim.x) {
     const int hh = (4 * i) / HD, e = (4 * i) % HD;
     float ob[2][4];
@@ -817,7 +820,6 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
     if (o_swa) *(bf16x4*)(o_swa + off) = vw;
     if (out) *(bf16x4*)(out + off) = vo;
   }
-  if (tid == 0) cnt[unit] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -843,7 +845,7 @@ size_t decode_workspace(const Dims& dm) {
   const size_t units = (size_t)dm.B * dm.Hkv;
   const size_t wgs = dwgs(dm);
   return drup(units * dsplits(dm) * dm.G * PSTRIDE * 4) + drup(units * wgs * 2 * dm.G * (HD + 4) * 4) +
-         drup(units * dm.G * HD * 4) + drup(units * 4);
+         drup(units * dm.G * HD * 4);
 }
 
 // kh/vh: compressed cache (bf16), kl/vl: low parts or NULL.  Text rows take dense causal
@@ -862,15 +864,13 @@ hipError_t launch_decode_fast(const Dims& dm, const DecVar& dv, const void* q, c
   float* part3 = (float*)p;
   p += drup((size_t)units * wgs * 2 * dm.G * (HD + 4) * 4);
   float* ocmp32 = (float*)p;
-  p += drup((size_t)units * dm.G * HD * 4);
-  int* cnt = (int*)p;
   if (kl)
     dcmp_split_kernel<true><<<dim3(units * ns), dim3(256), 0, s>>>((const bf16*)q, (const bf16*)kh, (const bf16*)kl,
-                                                                   (const bf16*)vh, (const bf16*)vl, vid, part, cnt,
+                                                                   (const bf16*)vh, (const bf16*)vl, vid, part,
                                                                    dm, ns);
   else
     dcmp_pipe_kernel<<<dim3(dcmp_pipe_grid(dm, ns)), dim3(256), 0, s>>>((const bf16*)q, (const bf16*)kh,
-                                                                        (const bf16*)vh, vid, part, cnt, dm, dv, ns);
+                                                                        (const bf16*)vh, vid, part, dm, dv, ns);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (mark) mark(s);
@@ -879,7 +879,11 @@ hipError_t launch_decode_fast(const Dims& dm, const DecVar& dv, const void* q, c
   if (e != hipSuccess) return e;
   dsel_kernel<<<dim3(units * wgs), dim3(256), shm, s>>>(
       (const bf16*)q, (const bf16*)k, (const bf16*)v, part, vid, gates, (bf16*)out, (bf16*)o_cmp, (bf16*)o_slc,
-      (bf16*)o_swa, lse, idx, imp, part3, ocmp32, cnt, dm, dv, ns, wgs);
+      (bf16*)o_swa, lse, idx, imp, part3, ocmp32, dm, dv, ns, wgs);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dmerge_kernel<<<dim3(units), dim3(256), (size_t)wgs * 2 * dm.G * 4, s>>>(
+      part3, ocmp32, vid, gates, (bf16*)out, (bf16*)o_cmp, (bf16*)o_slc, (bf16*)o_swa, dm, wgs);
   return hipGetLastError();
 }
 
