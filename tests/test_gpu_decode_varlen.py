@@ -80,31 +80,64 @@ def _compare_each(wl, inp, got, kc, vc, lens):
                       vc=host(vc[b, :nc]).astype(np.float64))
 
 
+def _oracle_cache(inp, lens, cap):
+    """The compressed cache of each sequence's own tokens, from the oracle, rounded to bf16
+    (blocks past a sequence's length stay 0); it feeds both sides."""
+    B = len(lens)
+    nc = _ncmp(cap)
+    kc = np.zeros((B, nc, 4, 128), np.float32)
+    vc = np.zeros_like(kc)
+    for b, L in enumerate(lens):
+        m = _ncmp(L)
+        if m:
+            kc[b, :m] = oracle.compress(host(inp["k"][b, :L]), host(inp["w_k"]), 32, 16)
+            vc[b, :m] = oracle.compress(host(inp["v"][b, :L]), host(inp["w_v"]), 32, 16)
+    return (torch.from_numpy(kc).to(DEV).to(torch.bfloat16), torch.from_numpy(vc).to(DEV).to(torch.bfloat16))
+
+
 @pytest.mark.parametrize("layout", ["contiguous", "paged"])
 def test_decode_varlen(layout):
     flush("decode varlen %s lens=%s" % (layout, LENS))
     wl, inp = _inputs(LENS)
-    nc = _ncmp(CAP)
-    kc = torch.zeros(len(LENS), nc, 4, 128, dtype=torch.bfloat16, device=DEV)
-    vc = torch.zeros_like(kc)
-    lens_t = torch.tensor(LENS, dtype=torch.int32, device=DEV)
+    kc, vc = _oracle_cache(inp, LENS, CAP)
     if layout == "contiguous":
-        nsa.nsa_compress_kv(inp["k"], inp["v"], inp["w_k"], inp["w_v"], k_cmp=kc, v_cmp=vc)
         got = _decode(wl, inp, kc, vc, LENS)
     else:
         kp, table = _paged(inp["k"], LENS, seed=1)
         vp, _ = _paged(inp["v"], LENS, seed=1)
-        # the whole cache through the incremental update: every block complete within L_b
-        nsa.nsa_compress_append(kp, vp, inp["w_k"], inp["w_v"], kc, vc, CAP, CAP, kv_lens=lens_t, page_table=table)
         got = _decode(wl, inp, kc, vc, LENS, k=kp, v=vp, table=table)
     _compare_each(wl, inp, got, kc, vc, LENS)
+
+
+def test_decode_varlen_full_size():
+    """The bench's batch: 16 sequences of seeded lengths in [4096, 65536], 64K capacity, pages at
+    shuffled pool positions; every sequence's row checked."""
+    wlv = synth.WORKLOADS["decode_varlen"]
+    lens = synth.decode_lengths(wlv)
+    flush("decode varlen full size lens=%s" % lens)
+    inp = synth.make_inputs(wlv, DEV)
+    kc, vc = _oracle_cache(inp, lens, wlv.kv_len)
+    kp, table = _paged(inp["k"], lens, seed=6)
+    vp, _ = _paged(inp["v"], lens, seed=6)
+    q = inp["q"]
+    B, _, Hq, D = q.shape
+    sh = nsa.make_shape(B, 1, wlv.kv_len, 0, Hq, 4, D)
+    pr = nsa.make_params(**wlv.params())
+    o_cmp, o_slc, o_swa = torch.zeros_like(q), torch.zeros_like(q), torch.zeros_like(q)
+    idx = torch.full((B, 1, 4, wlv.top_n), -1, dtype=torch.int32, device=DEV)
+    out = nsa.nsa_decode_fwd(q, kp, vp, kc, vc, inp["gates"], sh, pr,
+                             kv_lens=torch.tensor(lens, dtype=torch.int32, device=DEV), page_table=table,
+                             is_video=inp["is_video"], o_cmp=o_cmp, o_slc=o_slc, o_swa=o_swa, block_idx_out=idx)
+    torch.cuda.synchronize()
+    got = dict(out=out, o_cmp=o_cmp, o_slc=o_slc, o_swa=o_swa, idx=idx)
+    _compare_each(wlv, inp, got, kc, vc, lens)
 
 
 def test_decode_varlen_full_lengths_match_uniform_decode():
     """Every sequence at the capacity: the same kernels and the same bits as the layer's decode."""
     lens = [CAP] * 3
     wl, inp = _inputs(lens, text=(1,))
-    kc, vc = nsa.nsa_compress_kv(inp["k"], inp["v"], inp["w_k"], inp["w_v"])
+    kc, vc = _oracle_cache(inp, lens, CAP)
     a = _decode(wl, inp, kc, vc, lens)
     b = _decode(wl, inp, kc, vc, None)
     q = inp["q"]
