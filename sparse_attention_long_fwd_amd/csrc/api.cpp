@@ -168,12 +168,13 @@ struct BranchKV {
   bool shared() const { return kc == ks && ks == kw && vc == vs && vs == vw; }
 };
 
+// forced_local: idx is the layer's own top-n (its forced blocks present), not a caller's set.
 int run_sparse(int32_t dtype, const Dims& dm, const void* q, const BranchKV& kv, const int32_t* idx,
                const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out, void* o_slc,
-               void* o_swa, void* ws, hipStream_t s) {
+               void* o_swa, void* ws, hipStream_t s, bool forced_local = false) {
   hipError_t e = use_fast(dtype, dm)
                      ? launch_sparse_fast(dm, q, kv.ks, kv.vs, kv.kw, kv.vw, idx, vid, o_cmp, ocmp_f32, gates, out,
-                                          o_slc, o_swa, ws, s, prof_mark)
+                                          o_slc, o_swa, ws, s, prof_mark, forced_local)
                      : launch_sparse_generic(dtype, dm, q, kv.ks, kv.vs, kv.kw, kv.vw, idx, vid, o_cmp, gates, out,
                                              o_slc, o_swa, s);
   if (e != hipSuccess) return hip_fail(e, "selection/window kernel");
@@ -439,7 +440,8 @@ int32_t layer_fwd(const void* q, const BranchKV& kv, const void* k_cmp_in, const
   if (e != hipSuccess) return hip_fail(e, "top-n kernel");
   prof_mark(s);
   if (fast) {
-    st = run_sparse(dtype, dm, q, kv, idx, is_video, ocmp32, true, gates, out, o_slc, o_swa, sparse_ws_ptr, s);
+    st = run_sparse(dtype, dm, q, kv, idx, is_video, ocmp32, true, gates, out, o_slc, o_swa, sparse_ws_ptr, s,
+                    true);
     prof_mark(s);
     return st;
   }

@@ -33,17 +33,27 @@ hipError_t launch_compress_vt(const Dims& dm, const void* v, const float* w_v, v
 
 // Window branch, text rows, selection branch and the gated combine.  o_cmp is
 // fp32 when ocmp_f32, else bf16.  ws: fast_sparse_workspace(dm) bytes.  ks / vs: keys and values
-// of the selection branch; kw / vw: of the window branch and text rows.
+// of the selection branch; kw / vw: of the window branch and text rows.  forced_local: idx comes
+// from the layer's own top-n, so each video row's last min(n_local, jt + 1) entries are its forced
+// local blocks jt - n_local + 1 .. jt (the window pass may then take them over).
 hipError_t launch_sparse_fast(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
                               const void* vw, const int32_t* idx,
                               const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out,
                               void* o_slc, void* o_swa, void* ws, hipStream_t s,
-                              void (*mark)(hipStream_t) = nullptr);
+                              void (*mark)(hipStream_t) = nullptr, bool forced_local = false);
 
 // Window / text-row flash kernel: swa32 / swa_bf window outputs (either may be
 // NULL), text: output of text rows (NULL: skip them); ws: flash_workspace(dm).
+// local_ml / local_o (both or neither): the selection partial arrays of the selection kernels;
+// when given, the window pass also forms each video row's selection partial over its forced local
+// blocks (local_fusable(dm) must hold) and stores it in the row's first local slot (the others
+// are marked empty).
 hipError_t launch_flash_fast(const Dims& dm, const void* q, const void* k, const void* v, const uint8_t* vid,
-                             float* swa32, void* swa_bf, void* text, void* ws, hipStream_t s);
+                             float* swa32, void* swa_bf, void* text, void* ws, hipStream_t s,
+                             void* local_ml = nullptr, void* local_o = nullptr);
+// The forced local blocks of every video row lie inside its window and the query tiles of 32 rows
+// never straddle a 64-token block.
+bool local_fusable(const Dims& dm);
 size_t flash_workspace(const Dims& dm);
 
 // Gate values g = sigmoid(x w^T + b): x [R, K] bf16, w [N, K] bf16, b [N] fp32 or null, g [R, N] fp32.

@@ -1,13 +1,12 @@
 // Dispatch of the MFMA path: coverage test, workspace sizes, launch order.
 #include "fast_common.hpp"
 
-hipError_t launch_flash_fast(const Dims& dm, const void* q, const void* k, const void* v, const uint8_t* vid,
-                             float* swa32, void* swa_bf, void* text, void* ws, hipStream_t s);
-size_t flash_workspace(const Dims& dm);
 size_t slc_block_workspace(const Dims& dm);
+void slc_partial_arrays(const Dims& dm, void* ws, void** ml, void** o);
 hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
                             const uint8_t* vid, const void* ocmp, bool ocmp_f32, const float* swa32,
-                            const float* gates, void* out, void* o_slc, void* ws, hipStream_t s);
+                            const float* gates, void* out, void* o_slc, void* ws, hipStream_t s,
+                            bool local_fused);
 
 // Block-major selection packs (row, slot) into 32 bits: rows below 2^26.
 bool fast_supported(int32_t dtype, const Dims& dm) {
@@ -25,14 +24,20 @@ size_t fast_sparse_workspace(const Dims& dm) {
 hipError_t launch_sparse_fast(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
                               const void* vw, const int32_t* idx,
                               const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out,
-                              void* o_slc, void* o_swa, void* ws, hipStream_t s, void (*mark)(hipStream_t)) {
+                              void* o_slc, void* o_swa, void* ws, hipStream_t s, void (*mark)(hipStream_t),
+                              bool forced_local) {
   float* swa32 = (float*)ws;
   char* fws = (char*)ws + rup((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 4);
+  char* sws = fws + rup(flash_workspace(dm));
+  // The window pass takes over the forced local blocks of the selection (they lie inside the
+  // window and are scored there anyway) when the layer chose the blocks and the keys are shared.
+  const bool fuse = forced_local && ks == kw && vs == vw && local_fusable(dm);
+  void *lml = nullptr, *lo = nullptr;
+  if (fuse) slc_partial_arrays(dm, sws, &lml, &lo);
   // window branch (fp32 for the combine, bf16 copy if asked) and dense text rows
-  hipError_t e = launch_flash_fast(dm, q, kw, vw, vid, swa32, o_swa, out, fws, s);
+  hipError_t e = launch_flash_fast(dm, q, kw, vw, vid, swa32, o_swa, out, fws, s, lml, lo);
   if (e != hipSuccess) return e;
   if (mark) mark(s);
   // selection branch and the gated combine of video rows
-  return launch_slc_block(dm, q, ks, vs, idx, vid, o_cmp, ocmp_f32, swa32, gates, out, o_slc,
-                          fws + rup(flash_workspace(dm)), s);
+  return launch_slc_block(dm, q, ks, vs, idx, vid, o_cmp, ocmp_f32, swa32, gates, out, o_slc, sws, s, fuse);
 }

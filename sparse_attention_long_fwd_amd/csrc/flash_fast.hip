@@ -33,6 +33,8 @@ constexpr float RESCALE_SLACK = 8.f;
 __device__ __forceinline__ void fwait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 struct FlashOut {
+  float2* lml;    // selection partials (max, sum) per (row, group, slot, head), or NULL (no local pass)
+  _Float16* lo;   // their value records [.. , D] fp16
   float* swa32;   // [B, Tq, Hq, D] fp32 window output (may be NULL)
   bf16* swa_bf;   // bf16 window output (may be NULL)
   bf16* text;     // dense output of text rows (the layer's out)
@@ -44,17 +46,20 @@ struct FlashOut {
 // One pass of online-softmax attention over key tiles [kt0, kt1) for the
 // lanes whose column is active; the key of each column is limited to
 // [klo, khi] (inclusive).  Returns (in the references) the running maximum,
-// the lane's partial sum and the accumulator (unnormalised).
-template <int DUMMY = 0>
+// the lane's partial sum and the accumulator (unnormalised).  RESUME: continue
+// from the state in the references instead of starting empty.
+template <bool RESUME = false>
 __device__ __forceinline__ void flash_pass(const bf16* __restrict__ kbase, const bf16* __restrict__ vbase,
                                            int64_t stride, int64_t T, int kt0, int kt1, const bf16x8 (&qf)[8],
                                            int64_t klo, int64_t khi, bool active, float c2, bf16* buf0, int w,
                                            int G, int l, float& m_run, float& l_run, f32x16 (&oacc)[4]) {
   const int hl = l >> 5, n = l & 31, g16 = l >> 4, i16 = l & 15;
-  m_run = -INFINITY;
-  l_run = 0.f;
+  if (!RESUME) {
+    m_run = -INFINITY;
+    l_run = 0.f;
 #pragma unroll
-  for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+    for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+  }
   if (kt1 <= kt0) return;
   auto arr = [&](int bufi, int a) { return buf0 + (bufi * 2 + a) * TILE; };
   auto stage = [&](int kt, int bufi) {
@@ -192,7 +197,40 @@ __global__ void __launch_bounds__(512) flash_fast_kernel(const bf16* __restrict_
     const int kt0 = (int)(lo0 / FK), kt1 = (int)(tlast / FK) + 1;
     int64_t klo = t - dm.w + 1;
     if (klo < 0) klo = 0;
-    flash_pass(kbase, vbase, stride, dm.T, kt0, kt1, qf, klo, t, isv, c2, buf0, w, G, l, m_run, l_run, oacc);
+    if (fo.lml) {
+      // The row tile's forced local selection blocks (jt - n_local + 1 .. jt, inside every row's
+      // window) go first; the state after them is the selection partial of those blocks (the
+      // window and selection masks agree there), stored in the row's first local slot.
+      const int jt = kt1 - 1;
+      const int nle = dm.n_local < jt + 1 ? dm.n_local : jt + 1;
+      const int ktl = jt - nle + 1 > kt0 ? jt - nle + 1 : kt0;
+      flash_pass(kbase, vbase, stride, dm.T, ktl, kt1, qf, klo, t, isv, c2, buf0, w, G, l, m_run, l_run, oacc);
+      const float lt = l_run + __shfl_xor(l_run, 32, 64);
+      if (isv) {
+        const int nvalid = dm.n < jt + 1 ? dm.n : jt + 1;
+        const int64_t rec0 = (((b * dm.Tq + r) * dm.Hkv + g) * dm.n + (nvalid - nle)) * G + w;
+        // normalised to sum 1 (the maximum is kept lazily and the fp16 record needs bounded values)
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int j4 = 0; j4 < 4; ++j4) {
+            h4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (_Float16)(oacc[db][4 * j4 + e] * inv);
+            *(h4*)(fo.lo + rec0 * HD + 32 * db + 8 * j4 + 4 * hl) = x;
+          }
+        if (hl == 0) {
+          fo.lml[rec0] = lt > 0.f ? make_float2(m_run + flog2(lt), 1.f) : make_float2(-INFINITY, 0.f);
+          for (int e = 1; e < nle; ++e) fo.lml[rec0 + (int64_t)e * G] = make_float2(-INFINITY, 0.f);
+        }
+      }
+      flash_pass<true>(kbase, vbase, stride, dm.T, kt0, ktl, qf, klo, t, isv, c2, buf0, w, G, l, m_run, l_run,
+                       oacc);
+    } else {
+      flash_pass(kbase, vbase, stride, dm.T, kt0, kt1, qf, klo, t, isv, c2, buf0, w, G, l, m_run, l_run, oacc);
+    }
     const float lt = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (isv) {
@@ -330,12 +368,20 @@ size_t flash_workspace(const Dims& dm) {
 }
 
 // swa32 / swa_bf: window outputs (either may be NULL); text: output of text rows (NULL: skip them).
+bool local_fusable(const Dims& dm) {
+  return dm.ls == FK && dm.n_local >= 1 && dm.w >= FK * dm.n_local && dm.q0 % FQ == 0;
+}
+
 hipError_t launch_flash_fast(const Dims& dm, const void* q, const void* k, const void* v, const uint8_t* vid,
-                             float* swa32, void* swa_bf, void* text, void* ws, hipStream_t s) {
+                             float* swa32, void* swa_bf, void* text, void* ws, hipStream_t s, void* local_ml,
+                             void* local_o) {
   if (dm.Tq <= 0 || dm.B <= 0) return hipSuccess;
   const int ntq = (int)((dm.Tq + FQ - 1) / FQ);
   const int units = (int)(dm.B * dm.Hkv);
   FlashOut fo;
+  if ((local_ml != nullptr) != (local_o != nullptr) || (local_ml && !local_fusable(dm))) return hipErrorInvalidValue;
+  fo.lml = (float2*)local_ml;
+  fo.lo = (_Float16*)local_o;
   fo.swa32 = swa32;
   fo.swa_bf = (bf16*)swa_bf;
   fo.text = (bf16*)text;
@@ -343,7 +389,7 @@ hipError_t launch_flash_fast(const Dims& dm, const void* q, const void* k, const
   fo.max_split = fo.nsplit > 1 ? (ntq < MAX_SPLIT_TILES ? ntq : MAX_SPLIT_TILES) : 0;
   fo.part = (float*)ws;
   if (fo.nsplit > 1 && !ws) fo.nsplit = 1, fo.max_split = 0;
-  const int do_swa = (swa32 || swa_bf) ? 1 : 0;
+  const int do_swa = (swa32 || swa_bf || local_ml) ? 1 : 0;
   const int do_text = text ? 1 : 0;
   if (!do_swa && !do_text) return hipSuccess;
   dim3 grid(xcd_grid(units, fo.max_split * fo.nsplit + ntq - fo.max_split)), block(dm.G * 64);

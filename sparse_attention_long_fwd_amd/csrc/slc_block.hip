@@ -63,9 +63,15 @@ __global__ void __launch_bounds__(256) slc_zero_kernel(int* __restrict__ p, int6
   if (i < n) p[i] = 0;
 }
 
+// A pair (row, slot) is left to the window pass when that pass forms the row's forced local
+// blocks (local_fused): blocks jt - n_local + 1 .. jt of the row's own block jt.
+__device__ __forceinline__ bool slc_pair_kept(int j, int64_t r, const Dims& dm, int local_fused) {
+  return j >= 0 && !(local_fused && (int64_t)j > (dm.q0 + r) / dm.ls - dm.n_local);
+}
+
 __global__ void __launch_bounds__(256) slc_count_kernel(const int32_t* __restrict__ idx,
                                                         const uint8_t* __restrict__ vid, SlcBuckets bk, Dims dm,
-                                                        int wgs_per_bg) {
+                                                        int wgs_per_bg, int local_fused) {
   extern __shared__ int hist[];  // [Ns]
   const int bg = blockIdx.x / wgs_per_bg, part = blockIdx.x % wgs_per_bg;
   const int64_t b = bg / dm.Hkv;
@@ -79,7 +85,7 @@ __global__ void __launch_bounds__(256) slc_count_kernel(const int32_t* __restric
     const int s = (int)(e % dm.n);
     if (vid && !vid[b * dm.Tq + r]) continue;
     const int j = idx[((b * dm.Tq + r) * dm.Hkv + g) * dm.n + s];
-    if (j >= 0) atomicAdd(&hist[j], 1);
+    if (slc_pair_kept(j, r, dm, local_fused)) atomicAdd(&hist[j], 1);
   }
   __syncthreads();
   for (int j = threadIdx.x; j < dm.Ns; j += blockDim.x)
@@ -145,7 +151,7 @@ __global__ void __launch_bounds__(1024) slc_scan_kernel(SlcBuckets bk, Dims dm) 
 
 __global__ void __launch_bounds__(256) slc_scatter_kernel(const int32_t* __restrict__ idx,
                                                           const uint8_t* __restrict__ vid, SlcBuckets bk, Dims dm,
-                                                          int wgs_per_bg) {
+                                                          int wgs_per_bg, int local_fused) {
   extern __shared__ int sm[];  // hist[Ns], base[Ns]
   int* hist = sm;
   int* pbase = sm + dm.Ns;
@@ -160,7 +166,7 @@ __global__ void __launch_bounds__(256) slc_scatter_kernel(const int32_t* __restr
     const int64_t r = e / dm.n;
     if (vid && !vid[b * dm.Tq + r]) continue;
     const int j = idx[((b * dm.Tq + r) * dm.Hkv + g) * dm.n + e % dm.n];
-    if (j >= 0) atomicAdd(&hist[j], 1);
+    if (slc_pair_kept(j, r, dm, local_fused)) atomicAdd(&hist[j], 1);
   }
   __syncthreads();
   const int64_t base = (int64_t)bg * dm.Ns;
@@ -176,7 +182,7 @@ __global__ void __launch_bounds__(256) slc_scatter_kernel(const int32_t* __restr
     const int s = (int)(e % dm.n);
     if (vid && !vid[b * dm.Tq + r]) continue;
     const int j = idx[((b * dm.Tq + r) * dm.Hkv + g) * dm.n + s];
-    if (j >= 0) pl[pbase[j] + atomicAdd(&hist[j], 1)] = (int)(r << 5) | s;
+    if (slc_pair_kept(j, r, dm, local_fused)) pl[pbase[j] + atomicAdd(&hist[j], 1)] = (int)(r << 5) | s;
   }
 }
 
@@ -418,9 +424,19 @@ size_t slc_block_workspace(const Dims& dm) {
          srup(recs * 8) + srup(recs * HD * 2);
 }
 
+// The (max, sum) and value-record arrays of the selection partials inside the workspace.
+void slc_partial_arrays(const Dims& dm, void* ws, void** ml, void** o) {
+  const size_t bgs = (size_t)dm.B * dm.Hkv;
+  const size_t recs = (size_t)dm.B * dm.Tq * dm.Hkv * dm.n * dm.G;
+  char* p = (char*)ws + 4 * srup(bgs * dm.Ns * 4) + srup(bgs * slc_cap_chunks(dm) * 4) +
+            srup(bgs * slc_cap_chunks(dm) * RC * 4);
+  *ml = p;
+  *o = p + srup(recs * 8);
+}
+
 hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
                             const uint8_t* vid, const void* ocmp, bool ocmp_f32, const float* swa32,
-                            const float* gates, void* out, void* o_slc, void* ws, hipStream_t s) {
+                            const float* gates, void* out, void* o_slc, void* ws, hipStream_t s, bool local_fused) {
   if (dm.B <= 0 || dm.Tq <= 0) return hipSuccess;
   const int bgs = (int)(dm.B * dm.Hkv);
   char* p = (char*)ws;
@@ -450,9 +466,10 @@ hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const 
     e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * hist));
     if (e != hipSuccess) return e;
   }
-  slc_count_kernel<<<dim3(bgs * wpb), dim3(256), hist, s>>>(idx, vid, bk, dm, wpb);
+  slc_count_kernel<<<dim3(bgs * wpb), dim3(256), hist, s>>>(idx, vid, bk, dm, wpb, local_fused ? 1 : 0);
   slc_scan_kernel<<<dim3(bgs), dim3(1024), 2 * hist, s>>>(bk, dm);
-  slc_scatter_kernel<<<dim3(bgs * wpb), dim3(256), 2 * hist, s>>>(idx, vid, bk, dm, wpb);
+  slc_scatter_kernel<<<dim3(bgs * wpb), dim3(256), 2 * hist, s>>>(idx, vid, bk, dm, wpb,
+                                                                   local_fused ? 1 : 0);
   slc_chunk_kernel<<<dim3((unsigned)bgs * bk.cap_c), dim3(dm.G * 64), 0, s>>>((const bf16*)q, (const bf16*)k,
                                                                              (const bf16*)v, bk, pml, po, dm);
   const int64_t items = dm.B * dm.Tq * dm.Hkv;
