@@ -445,10 +445,8 @@ __device__ __forceinline__ void dsplit_stats(const float* pu, int G, int nsplit,
 // softmax over blocks sg*4+w, +4*wgs, ...
 __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                    const bf16* __restrict__ v, const float* __restrict__ part,
-                                                   const uint8_t* __restrict__ vid, const float* __restrict__ gates,
-                                                   bf16* __restrict__ out, bf16* __restrict__ o_cmp,
-                                                   bf16* __restrict__ o_slc, bf16* __restrict__ o_swa,
-                                                   float* __restrict__ lse, int32_t* __restrict__ idx,
+                                                   const uint8_t* __restrict__ vid, float* __restrict__ lse,
+                                                   int32_t* __restrict__ idx,
                                                    float* __restrict__ imp_out, float* __restrict__ part3,
                                                    float* __restrict__ ocmp32, Dims dm,
                                                    DecVar dv, int nsplit, int wgs) {
@@ -878,8 +876,7 @@ hipError_t launch_decode_fast(const Dims& dm, const DecVar& dv, const void* q, c
   e = hipFuncSetAttribute((const void*)dsel_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   dsel_kernel<<<dim3(units * wgs), dim3(256), shm, s>>>(
-      (const bf16*)q, (const bf16*)k, (const bf16*)v, part, vid, gates, (bf16*)out, (bf16*)o_cmp, (bf16*)o_slc,
-      (bf16*)o_swa, lse, idx, imp, part3, ocmp32, dm, dv, ns, wgs);
+      (const bf16*)q, (const bf16*)k, (const bf16*)v, part, vid, lse, idx, imp, part3, ocmp32, dm, dv, ns, wgs);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   dmerge_kernel<<<dim3(units), dim3(256), (size_t)wgs * 2 * dm.G * 4, s>>>(
