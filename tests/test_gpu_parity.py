@@ -389,6 +389,17 @@ def test_layer_selection_params(n, n_init, n_local, path):
     compare_layer(wl, inp, got, rows)
 
 
+@pytest.mark.parametrize("q_start", [1024, 1000])
+def test_layer_query_block(q_start, path):
+    """A block of query rows at the end of the sequence (chunked prefill): rows start at position
+    q_start, aligned to 32 (the window pass then takes over the forced local blocks) or not."""
+    wl = _wl(T=3000, Hq=14, Hkv=2, lead=40, tail=60, n=8, w=256, q_start=q_start)
+    flush("query block q_start=%d path=%s" % (q_start, path))
+    inp = synth.make_inputs(wl, DEV)
+    got = run_layer(wl, inp)
+    compare_layer(wl, inp, got, np.arange(wl.q_len))
+
+
 def test_layer_deterministic():
     wl = _wl(T=3000, lead=128, tail=128)
     inp = synth.make_inputs(wl, DEV)
