@@ -195,16 +195,24 @@ __device__ void bwd_branch_rows(const float* qs, const float* dos, const TK* kb,
     for (int h = 0; h < HB; ++h)
       for (int w2 = 0; w2 < BWD_THREADS / 64; ++w2) E[h] += wred[w2 * HB + h];
     if (tid < D) {
+      // 8 keys at a time, their loads issued together (a slot without a key has P = 0)
       const int64_t cnt = (nslots - a0 < BWD_THREADS) ? nslots - a0 : BWD_THREADS;
-      for (int c = 0; c < cnt; ++c)
-        if (us[c] >= 0) {
-          const float kv = to_f32(kb[us[c] * kstride + tid]);
+      for (int c0 = 0; c0 < cnt; c0 += 8) {
+        float kv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int64_t uu = c0 + i < cnt ? us[c0 + i] : -1;
+          const float x = to_f32(kb[(uu >= 0 ? uu : 0) * kstride + tid]);
+          kv[i] = uu >= 0 ? x : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
           for (int h = 0; h < HB; ++h) {
-            a1[h] = fmaf(pds[h * BWD_THREADS + c], kv, a1[h]);
-            a2[h] = fmaf(ps[h * BWD_THREADS + c], kv, a2[h]);
+            a1[h] = fmaf(pds[h * BWD_THREADS + c0 + i], kv[i], a1[h]);
+            a2[h] = fmaf(ps[h * BWD_THREADS + c0 + i], kv[i], a2[h]);
           }
-        }
+      }
     }
   }
   if (tid < D)
@@ -214,7 +222,7 @@ __device__ void bwd_branch_rows(const float* qs, const float* dos, const TK* kb,
 }
 
 template <typename T>
-__global__ void __launch_bounds__(BWD_THREADS)
+__global__ void __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
     bwd_row_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                    const float* __restrict__ kc, const float* __restrict__ vc, const int32_t* __restrict__ idx,
                    const uint8_t* __restrict__ vid, const float* __restrict__ gates, const T* __restrict__ dout,
@@ -304,41 +312,6 @@ __global__ void __launch_bounds__(BWD_THREADS)
 
 // ---------------------------------------------------------------------------
 // Stage 2.  Lane c8 = tid % 8 of key kk = tid / 8 owns channels [c8 nc, c8 nc + nc), nc = D / 8.
-// One (row, head, branch) term: P = exp(scale <q, k> - L), ds = g P (<d_out, v> - E);
-// dk += scale ds q, dv += g P d_out on the lane's channels.  `on` masks the key.
-template <int MAXC, typename TQ>
-__device__ __forceinline__ void bwd_key_term(const float* kf, const float* vf, const TQ* qr, const TQ* dr, int nc,
-                                             float scale, float L, float E, float gate, bool on, float* ak,
-                                             float* av) {
-  float qf[MAXC], df[MAXC];
-#pragma unroll
-  for (int c = 0; c < MAXC; c += 8)
-    if (c < nc) {
-      ld8(qr + c, qf + c);
-      ld8(dr + c, df + c);
-    }
-  float zq = 0.f, zd = 0.f;
-#pragma unroll
-  for (int c = 0; c < MAXC; ++c)
-    if (c < nc) {
-      zq = fmaf(qf[c], kf[c], zq);
-      zd = fmaf(df[c], vf[c], zd);
-    }
-#pragma unroll
-  for (int o = LPK / 2; o >= 1; o >>= 1) {
-    zq += __shfl_xor(zq, o, 64);
-    zd += __shfl_xor(zd, o, 64);
-  }
-  if (!on) return;
-  const float p = expf(zq * scale - L);
-  const float ds = gate * p * (zd - E);
-#pragma unroll
-  for (int c = 0; c < MAXC; ++c)
-    if (c < nc) {
-      ak[c] = fmaf(scale * ds, qf[c], ak[c]);
-      av[c] = fmaf(gate * p, df[c], av[c]);
-    }
-}
 
 // The lane's nc channels of one key row, widened once.
 template <int MAXC, typename TK>
@@ -351,124 +324,279 @@ __device__ __forceinline__ void load_key(const TK* kr, const TK* vr, int nc, flo
     }
 }
 
-// Full-resolution keys [u0, u0 + 32) of KV head g: window and selection terms of video rows,
-// dense terms of text rows.
+// Rows are split into chunks of rc rows (a multiple of 32), so that keys seen by nearly every row
+// (the forced first selection block, the first compressed blocks) are shared by several
+// workgroups.  Chunk c < n - 1 holds the keys [0, keys[c]) its rows can see in a slab
+// [B, keys[c], Hkv, D] of its own at off[c] (the dv slabs follow at `half`); the last chunk writes
+// the gradients themselves, and bwd_chunk_sum_kernel adds the slabs to them in chunk order, so
+// the sums do not depend on scheduling.
+constexpr int MAXCH = 32;
+struct RowChunks {
+  int64_t rc, half;
+  int n;
+  int64_t keys[MAXCH], off[MAXCH];
+};
+
+// At most max_chunks chunks of at least min_rows rows; compressed: the keys are compressed blocks.
+static RowChunks make_chunks(const Dims& dm, int max_chunks, int64_t min_rows, bool compressed) {
+  RowChunks ch{};
+  int64_t r = (dm.Tq + max_chunks - 1) / max_chunks;
+  if (r < min_rows) r = min_rows;
+  r = (r + 31) / 32 * 32;
+  ch.rc = r;
+  ch.n = (int)((dm.Tq + r - 1) / r);
+  const int64_t N = compressed ? dm.Nc : dm.T;
+  int64_t o = 0;
+  for (int c = 0; c < ch.n; ++c) {
+    int64_t kc = N;
+    if (c < ch.n - 1) {
+      const int64_t t = dm.q0 + (c + 1) * r - 1;  // the chunk's last position
+      kc = compressed ? (t + 1 >= dm.l ? (t + 1 - dm.l) / dm.d + 1 : 0) : t + 1;
+      if (kc > N) kc = N;
+    }
+    ch.keys[c] = kc;
+    ch.off[c] = o;
+    if (c < ch.n - 1) o += kc * dm.B * dm.Hkv * dm.D;
+  }
+  ch.half = o;
+  return ch;
+}
+
+// One query row's terms for the lane's key over the G heads of the group, HG heads at a time with
+// their q and d_out loaded together.  Branch 1 takes statistics slot s1 and gate slot gs1 (gate 1
+// when gs1 < 0); branch 2, when TWO, the window's slot 2.  Per head and branch b:
+//   P_b = exp(scale <q, k> - L_b),  ds = sum_b g_b P_b (<d_out, v> - E_b),
+//   dk += scale ds q,  dv += (sum_b g_b P_b) d_out,
+// the branches sharing the loads and the dot products.
+template <typename T, int MAXC, bool TWO>
+__device__ __forceinline__ void bwd_row_terms(const T* __restrict__ q, const T* __restrict__ dout,
+                                              const float* __restrict__ st_l, const float* __restrict__ st_e,
+                                              const float* __restrict__ gates, int64_t row0, const Dims& dm,
+                                              int c8, int s1, int gs1, bool on1, bool on2, const float* kf,
+                                              const float* vf, float* ak, float* av) {
+  constexpr int E = 16 / (int)sizeof(T);  // elements per 16-byte load
+  constexpr int NV = MAXC / E;
+  constexpr int HG = 128 / (MAXC * (int)sizeof(T)) > 1 ? 128 / (MAXC * (int)sizeof(T)) : 1;
+  typedef T rawv __attribute__((ext_vector_type(E)));
+  const int D = dm.D, nc = D / LPK;
+  for (int h0 = 0; h0 < dm.G; h0 += HG) {
+    rawv qv[HG][NV], dw[HG][NV];
+    float L1[HG], E1[HG], G1[HG], L2[HG], E2[HG], G2[HG];
+#pragma unroll
+    for (int i = 0; i < HG; ++i) {
+      const int hh = h0 + i < dm.G ? h0 + i : dm.G - 1;
+      const int64_t row = row0 + hh;
+      const T* qr = q + row * D + c8 * nc;
+      const T* dr = dout + row * D + c8 * nc;
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+        if (j * E < nc) {
+          qv[i][j] = *(const rawv*)(qr + j * E);
+          dw[i][j] = *(const rawv*)(dr + j * E);
+        }
+      L1[i] = st_l[row * 3 + s1];
+      E1[i] = st_e[row * 3 + s1];
+      G1[i] = gs1 >= 0 ? gates[row * 3 + gs1] : 1.f;
+      if (TWO) {
+        L2[i] = st_l[row * 3 + 2];
+        E2[i] = st_e[row * 3 + 2];
+        G2[i] = gates[row * 3 + 2];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < HG; ++i) {
+      float zq = 0.f, zd = 0.f;
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (j * E + e < nc) {
+            zq = fmaf(to_f32(qv[i][j][e]), kf[j * E + e], zq);
+            zd = fmaf(to_f32(dw[i][j][e]), vf[j * E + e], zd);
+          }
+#pragma unroll
+      for (int o = LPK / 2; o >= 1; o >>= 1) {
+        zq += __shfl_xor(zq, o, 64);
+        zd += __shfl_xor(zd, o, 64);
+      }
+      const bool hv = h0 + i < dm.G;
+      const float a1 = hv && on1 ? G1[i] * expf(zq * dm.scale - L1[i]) : 0.f;
+      float sds = a1 * (zd - E1[i]), pa = a1;
+      if (TWO) {
+        const float a2 = hv && on2 ? G2[i] * expf(zq * dm.scale - L2[i]) : 0.f;
+        sds += a2 * (zd - E2[i]);
+        pa += a2;
+      }
+      sds *= dm.scale;
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (j * E + e < nc) {
+            ak[j * E + e] = fmaf(sds, to_f32(qv[i][j][e]), ak[j * E + e]);
+            av[j * E + e] = fmaf(pa, to_f32(dw[i][j][e]), av[j * E + e]);
+          }
+    }
+  }
+}
+
+// Bits [lo, hi) of 32-row word `base` (lo, hi relative to the chunk's rows [ra, rb)).
+__device__ __forceinline__ uint32_t word_range(int64_t base, int64_t ra, int64_t rb, uint32_t m) {
+  if (base < ra) m &= ~((1u << (ra - base)) - 1u);
+  if (base + 32 > rb) m &= (1u << (rb - base)) - 1u;
+  return m;
+}
+
+// The lane's accumulated gradients: the gradient rows themselves for the last chunk, else the
+// chunk's slab.
+template <int MAXC>
+__device__ __forceinline__ void store_key_grads(const float* ak, const float* av, float* gk, float* gv,
+                                                float* part, const RowChunks& ch, int c, int64_t b, int64_t u,
+                                                int64_t N, int g, const Dims& dm, int c8) {
+  const int nc = dm.D / LPK;
+  const int64_t kstride = (int64_t)dm.Hkv * dm.D;
+  float *dko, *dvo;
+  if (c == ch.n - 1) {
+    dko = gk + (b * N + u) * kstride + (int64_t)g * dm.D + c8 * nc;
+    dvo = gv + (b * N + u) * kstride + (int64_t)g * dm.D + c8 * nc;
+  } else {
+    const int64_t o = ch.off[c] + (b * ch.keys[c] + u) * kstride + (int64_t)g * dm.D + c8 * nc;
+    dko = part + o;
+    dvo = part + ch.half + o;
+  }
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i)
+    if (i < nc) {
+      dko[i] = ak[i];
+      dvo[i] = av[i];
+    }
+}
+
+// Full-resolution keys [u0, u0 + 32) of KV head g, the rows of chunk c: window and selection
+// terms of video rows, dense terms of text rows.
 template <typename T, int MAXC>
 __global__ void __launch_bounds__(BWD_THREADS)
     bwd_key_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                    const int32_t* __restrict__ idx, const uint8_t* __restrict__ vid, const float* __restrict__ gates,
                    const T* __restrict__ dout, const float* __restrict__ st_l, const float* __restrict__ st_e,
-                   float* __restrict__ dk, float* __restrict__ dv, Dims dm) {
-  const int tid = threadIdx.x, kk = tid / LPK, c8 = tid % LPK;
+                   const uint32_t* __restrict__ sbits, const uint32_t* __restrict__ tbits, float* __restrict__ dk,
+                   float* __restrict__ dv, float* __restrict__ part, Dims dm, RowChunks ch) {
+  const int tid = threadIdx.x, kk = tid / LPK, c8 = tid % LPK, lane = tid & 63;
   const int g = blockIdx.y;
-  const int64_t b = blockIdx.z;
+  const int64_t b = blockIdx.z / ch.n;
+  const int c = (int)(blockIdx.z % ch.n);
   const int64_t u0 = (int64_t)blockIdx.x * KB, u = u0 + kk;
+  if (u0 >= ch.keys[c]) return;  // no row of the chunk sees these keys, and the chunk stores none of them
   const int D = dm.D, nc = D / LPK;
   const bool kvalid = u < dm.T;
   const int64_t ur = kvalid ? u : dm.T - 1;
   const int64_t kstride = (int64_t)dm.Hkv * D;
-  const T* kr = k + (b * dm.T + ur) * kstride + (int64_t)g * D + c8 * nc;
-  const T* vr = v + (b * dm.T + ur) * kstride + (int64_t)g * D + c8 * nc;
   float ak[MAXC], av[MAXC], kf[MAXC], vf[MAXC];
 #pragma unroll
-  for (int c = 0; c < MAXC; ++c) ak[c] = av[c] = kf[c] = vf[c] = 0.f;
-  load_key<MAXC>(kr, vr, nc, kf, vf);
+  for (int i = 0; i < MAXC; ++i) ak[i] = av[i] = kf[i] = vf[i] = 0.f;
+  load_key<MAXC>(k + (b * dm.T + ur) * kstride + (int64_t)g * D + c8 * nc,
+                 v + (b * dm.T + ur) * kstride + (int64_t)g * D + c8 * nc, nc, kf, vf);
   const int64_t ulast = (u0 + KB - 1 < dm.T - 1) ? u0 + KB - 1 : dm.T - 1;
-  // rows that can see a key of the block: t >= u0 (causal), among the query rows
-  int64_t r0 = u0 - dm.q0;
-  if (r0 < 0) r0 = 0;
-  for (int64_t r = r0; r < dm.Tq; ++r) {
-    const int64_t t = dm.q0 + r;
-    const bool is_vid = vid ? (vid[b * dm.Tq + r] != 0) : true;
-    const int32_t* sel = idx ? idx + ((b * dm.Tq + r) * dm.Hkv + g) * dm.n : nullptr;
-    // branch membership of this key for this row (uniform checks first)
-    bool in_swa = false, in_slc = false, in_txt = false;
-    if (!is_vid) {
-      in_txt = kvalid && u <= t;
-    } else {
-      const int64_t lo = t - dm.w + 1;
-      if (ulast >= (lo > 0 ? lo : 0) && u0 <= t) in_swa = kvalid && u <= t && u >= lo;
-      bool any = false;
-      for (int c = 0; c < dm.n; ++c) {
-        const int32_t j = sel[c];
-        if (j >= 0 && (int64_t)j * dm.ls <= ulast && ((int64_t)j + 1) * dm.ls > u0) any = true;
-      }
-      if (any && kvalid && u <= t) {
-        const int64_t ju = u / dm.ls;
-        for (int c = 0; c < dm.n; ++c) in_slc |= sel[c] == ju;
-      }
-      // skip rows where no key of the block takes part (uniform over the workgroup)
-      if (!any && !(ulast >= (lo > 0 ? lo : 0) && u0 <= t)) continue;
+  // Rows that can see a key of the block (t >= u0) among the chunk's rows [ra, rb).  Only rows
+  // that can take part are visited, 32 at a time from bit masks: text rows, the window range of
+  // the block's keys, and the rows that chose a selection block overlapping the keys.
+  int64_t ra = u0 - dm.q0;
+  if (ra < c * ch.rc) ra = c * ch.rc;
+  if (ra < 0) ra = 0;
+  const int64_t rb = (c + 1) * ch.rc < dm.Tq ? (c + 1) * ch.rc : dm.Tq;
+  const int64_t nw = (dm.Tq + 31) / 32;
+  const int64_t rw1 = ulast + dm.w - 1 - dm.q0;  // last row whose window reaches a key of the block
+  const int64_t j0 = u0 / dm.ls, j1 = ulast / dm.ls, ju = ur / dm.ls;
+  const uint32_t* sb = sbits + ((b * dm.Hkv + g) * dm.Ns) * nw;
+  for (int64_t wi = ra / 32; wi * 32 < rb; ++wi) {
+    const int64_t base = wi * 32;
+    uint32_t m = tbits[b * nw + wi];
+    for (int64_t j = j0; j <= j1; ++j) m |= sb[j * nw + wi];
+    const int64_t wa = base > ra ? base : ra, wb = base + 31 < rw1 ? base + 31 : rw1;
+    if (wa <= wb) {  // rows wa .. wb of the window range
+      const uint32_t hi = (wb - base) == 31 ? 0xffffffffu : ((1u << (wb - base + 1)) - 1u);
+      m |= hi & ~((1u << (wa - base)) - 1u);
     }
-    for (int hh = 0; hh < dm.G; ++hh) {
-      const int h = g * dm.G + hh;
-      const int64_t row = (b * dm.Tq + r) * dm.Hq + h;
-      const T* qr = q + row * D + c8 * nc;
-      const T* dr = dout + row * D + c8 * nc;
+    for (m = word_range(base, ra, rb, m); m; m &= m - 1) {
+      const int64_t r = base + __builtin_ctz(m);
+      const int64_t t = dm.q0 + r;
+      // the row's top-n list, one entry per lane (n <= 32), loaded beside the row's video flag
+      const int32_t sj = lane < dm.n ? idx[((b * dm.Tq + r) * dm.Hkv + g) * dm.n + lane] : -1;
+      const bool is_vid = vid ? (vid[b * dm.Tq + r] != 0) : true;
+      // branch membership of this key for this row: on1 (text, or selection) and on2 (window)
+      bool on1 = false, on2 = false;
       if (!is_vid) {
-        bwd_key_term<MAXC>(kf, vf, qr, dr, nc, dm.scale, st_l[row * 3], st_e[row * 3], 1.f, in_txt, ak, av);
+        on1 = kvalid && u <= t;
       } else {
-        const float* gg = gates + row * 3;
-        bwd_key_term<MAXC>(kf, vf, qr, dr, nc, dm.scale, st_l[row * 3 + 1], st_e[row * 3 + 1], gg[1], in_slc, ak, av);
-        bwd_key_term<MAXC>(kf, vf, qr, dr, nc, dm.scale, st_l[row * 3 + 2], st_e[row * 3 + 2], gg[2], in_swa, ak, av);
+        on2 = kvalid && u <= t && u >= t - dm.w + 1;
+        for (int64_t j = j0; j <= j1; ++j)
+          if (__any(sj == (int32_t)j) && j == ju) on1 = kvalid && u <= t;
       }
+      if (!__any(on1 || on2)) continue;  // no key of this wave takes part
+      bwd_row_terms<T, MAXC, true>(q, dout, st_l, st_e, gates, (b * dm.Tq + r) * dm.Hq + (int64_t)g * dm.G, dm,
+                                   c8, is_vid ? 1 : 0, is_vid ? 1 : -1, on1, on2, kf, vf, ak, av);
     }
   }
-  if (!kvalid) return;
-  float* dko = dk + (b * dm.T + u) * kstride + (int64_t)g * D + c8 * nc;
-  float* dvo = dv + (b * dm.T + u) * kstride + (int64_t)g * D + c8 * nc;
-#pragma unroll
-  for (int c = 0; c < MAXC; ++c)
-    if (c < nc) {
-      dko[c] = ak[c];
-      dvo[c] = av[c];
-    }
+  if (kvalid && u < ch.keys[c]) store_key_grads<MAXC>(ak, av, dk, dv, part, ch, c, b, u, dm.T, g, dm, c8);
 }
 
-// Compressed keys [i0, i0 + 32) of KV head g: compression-branch terms of video rows.
+// Compressed keys [i0, i0 + 32) of KV head g, the video rows of chunk c: compression-branch terms.
 template <typename T, int MAXC>
 __global__ void __launch_bounds__(BWD_THREADS)
     bwd_ckey_kernel(const T* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
-                    const uint8_t* __restrict__ vid, const float* __restrict__ gates, const T* __restrict__ dout,
-                    const float* __restrict__ st_l, const float* __restrict__ st_e, float* __restrict__ dkc,
-                    float* __restrict__ dvc, Dims dm) {
+                    const float* __restrict__ gates, const T* __restrict__ dout, const float* __restrict__ st_l,
+                    const float* __restrict__ st_e, const uint32_t* __restrict__ tbits, float* __restrict__ dkc,
+                    float* __restrict__ dvc, float* __restrict__ part, Dims dm, RowChunks ch) {
   const int tid = threadIdx.x, kk = tid / LPK, c8 = tid % LPK;
   const int g = blockIdx.y;
-  const int64_t b = blockIdx.z;
+  const int64_t b = blockIdx.z / ch.n;
+  const int c = (int)(blockIdx.z % ch.n);
   const int64_t i0 = (int64_t)blockIdx.x * KB, i = i0 + kk;
+  if (i0 >= ch.keys[c]) return;
   const int D = dm.D, nc = D / LPK;
   const bool kvalid = i < dm.Nc;
   const int64_t ir = kvalid ? i : dm.Nc - 1;
   const int64_t kstride = (int64_t)dm.Hkv * D;
-  const float* kr = kc + (b * dm.Nc + ir) * kstride + (int64_t)g * D + c8 * nc;
-  const float* vr = vc + (b * dm.Nc + ir) * kstride + (int64_t)g * D + c8 * nc;
   float ak[MAXC], av[MAXC], kf[MAXC], vf[MAXC];
 #pragma unroll
-  for (int c = 0; c < MAXC; ++c) ak[c] = av[c] = kf[c] = vf[c] = 0.f;
-  load_key<MAXC>(kr, vr, nc, kf, vf);
+  for (int x = 0; x < MAXC; ++x) ak[x] = av[x] = kf[x] = vf[x] = 0.f;
+  load_key<MAXC>(kc + (b * dm.Nc + ir) * kstride + (int64_t)g * D + c8 * nc,
+                 vc + (b * dm.Nc + ir) * kstride + (int64_t)g * D + c8 * nc, nc, kf, vf);
   const int64_t end_i = i * dm.d + dm.l - 1;  // the key is visible from this position on
-  int64_t r0 = i0 * dm.d + dm.l - 1 - dm.q0;
-  if (r0 < 0) r0 = 0;
-  for (int64_t r = r0; r < dm.Tq; ++r) {
-    const int64_t t = dm.q0 + r;
-    if (vid && !vid[b * dm.Tq + r]) continue;
-    const bool on = kvalid && end_i <= t;
-    for (int hh = 0; hh < dm.G; ++hh) {
-      const int h = g * dm.G + hh;
-      const int64_t row = (b * dm.Tq + r) * dm.Hq + h;
-      bwd_key_term<MAXC>(kf, vf, q + row * D + c8 * nc, dout + row * D + c8 * nc, nc, dm.scale, st_l[row * 3],
-                   st_e[row * 3], gates[row * 3], on, ak, av);
+  int64_t ra = i0 * dm.d + dm.l - 1 - dm.q0;
+  if (ra < c * ch.rc) ra = c * ch.rc;
+  if (ra < 0) ra = 0;
+  const int64_t rb = (c + 1) * ch.rc < dm.Tq ? (c + 1) * ch.rc : dm.Tq;
+  const int64_t nw = (dm.Tq + 31) / 32;
+  for (int64_t wi = ra / 32; wi * 32 < rb; ++wi) {
+    const int64_t base = wi * 32;
+    for (uint32_t m = word_range(base, ra, rb, ~tbits[b * nw + wi]); m; m &= m - 1) {  // video rows
+      const int64_t r = base + __builtin_ctz(m);
+      const bool on = kvalid && end_i <= dm.q0 + r;
+      if (!__any(on)) continue;
+      bwd_row_terms<T, MAXC, false>(q, dout, st_l, st_e, gates, (b * dm.Tq + r) * dm.Hq + (int64_t)g * dm.G, dm,
+                                    c8, 0, 0, on, false, kf, vf, ak, av);
     }
   }
-  if (!kvalid) return;
-  float* dko = dkc + (b * dm.Nc + i) * kstride + (int64_t)g * D + c8 * nc;
-  float* dvo = dvc + (b * dm.Nc + i) * kstride + (int64_t)g * D + c8 * nc;
-#pragma unroll
-  for (int c = 0; c < MAXC; ++c)
-    if (c < nc) {
-      dko[c] = ak[c];
-      dvo[c] = av[c];
+  if (kvalid && i < ch.keys[c]) store_key_grads<MAXC>(ak, av, dkc, dvc, part, ch, c, b, i, dm.Nc, g, dm, c8);
+}
+
+// gk, gv [B, N, Hkv, D] (the last chunk's sums) += the slabs of the other chunks, in chunk order.
+__global__ void bwd_chunk_sum_kernel(const float* __restrict__ part, float* __restrict__ gk, float* __restrict__ gv,
+                                     int64_t N, Dims dm, RowChunks ch) {
+  const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t hd = (int64_t)dm.Hkv * dm.D;
+  if (x >= dm.B * N * hd) return;
+  const int64_t b = x / (N * hd), u = (x / hd) % N, e = x % hd;
+  float sk = 0.f, sv = 0.f;
+  for (int c = 0; c < ch.n - 1; ++c)
+    if (u < ch.keys[c]) {
+      const int64_t o = ch.off[c] + (b * ch.keys[c] + u) * hd + e;
+      sk += part[o];
+      sv += part[ch.half + o];
     }
+  gk[x] += sk;
+  gv[x] += sv;
 }
 
 // ---------------------------------------------------------------------------
@@ -531,14 +659,49 @@ __global__ void bwd_fill_kernel(float* __restrict__ p, int64_t n) {
   if (x < n) p[x] = 0.f;
 }
 
+// Row bit masks for the key kernel: sbits [B, Hkv, Ns, nw] marks the video rows that chose each
+// block, tbits [B, nw] the text rows (nw = 32-row words).  One thread per (batch, row, group, slot);
+// the masks start at zero.  OR is order-free, so the masks are deterministic.
+__global__ void bwd_bits_kernel(const int32_t* __restrict__ idx, const uint8_t* __restrict__ vid,
+                                uint32_t* __restrict__ sbits, uint32_t* __restrict__ tbits, Dims dm) {
+  const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (x >= dm.B * dm.Tq * dm.Hkv * dm.n) return;
+  const int s = (int)(x % dm.n);
+  const int g = (int)((x / dm.n) % dm.Hkv);
+  const int64_t br = x / ((int64_t)dm.n * dm.Hkv);  // b * Tq + r
+  const int64_t b = br / dm.Tq, r = br % dm.Tq;
+  const int64_t nw = (dm.Tq + 31) / 32;
+  const uint32_t bit = 1u << (r % 32);
+  if (vid && !vid[br]) {
+    if (g == 0 && s == 0) atomicOr(tbits + b * nw + r / 32, bit);
+    return;
+  }
+  const int j = idx[x];
+  if (j >= 0 && j < dm.Ns) atomicOr(sbits + ((b * dm.Hkv + g) * dm.Ns + j) * nw + r / 32, bit);
+}
+
 // Each lane of a key takes D / 8 channels in runs of 8: head_dim a multiple of 64, at most 256.
 bool bwd_supported(const Dims& dm) { return dm.D <= 256 && dm.D % (8 * LPK) == 0; }
 
 static size_t brup(size_t x) { return (x + 255) & ~(size_t)255; }
 
+static size_t bits_bytes(const Dims& dm) {
+  const size_t nw = (size_t)(dm.Tq + 31) / 32;
+  return brup((size_t)dm.B * dm.Hkv * dm.Ns * nw * 4) + brup((size_t)dm.B * nw * 4);
+}
+
+// chunking of the key kernel's rows (at most 4 chunks) and of the compressed-key kernel's (at most 32)
+static RowChunks key_rows(const Dims& dm) { return make_chunks(dm, 4, 2048, false); }
+static RowChunks ckey_rows(const Dims& dm) { return make_chunks(dm, MAXCH, 1024, true); }
+
+static size_t part_bytes(const Dims& dm) {
+  const size_t a = (size_t)key_rows(dm).half, c = dm.Nc > 0 ? (size_t)ckey_rows(dm).half : 0;
+  return brup((a > c ? a : c) * 2 * 4);
+}
+
 size_t bwd_workspace(const Dims& dm) {
   const size_t ckv = brup((size_t)dm.B * dm.Nc * dm.Hkv * dm.D * 4);
-  return 4 * ckv + 2 * brup((size_t)dm.B * dm.Tq * dm.Hq * 3 * 4);
+  return 4 * ckv + 2 * brup((size_t)dm.B * dm.Tq * dm.Hq * 3 * 4) + bits_bytes(dm) + part_bytes(dm);
 }
 
 template <typename T>
@@ -554,6 +717,11 @@ static hipError_t launch_bwd_t(const Dims& dm, const void* q, const void* k, con
   float* dvc = (float*)(p + 3 * ckv);
   float* st_l = (float*)(p + 4 * ckv);
   float* st_e = (float*)(p + 4 * ckv + brup((size_t)dm.B * dm.Tq * dm.Hq * 3 * 4));
+  uint32_t* sbits = (uint32_t*)(p + 4 * ckv + 2 * brup((size_t)dm.B * dm.Tq * dm.Hq * 3 * 4));
+  const size_t nw = (size_t)(dm.Tq + 31) / 32;
+  uint32_t* tbits = sbits + brup((size_t)dm.B * dm.Hkv * dm.Ns * nw * 4) / 4;
+  float* part = (float*)((char*)sbits + bits_bytes(dm));
+  const RowChunks kch = key_rows(dm);
   const int dt = sizeof(T) == 2 ? 1 : 0;
   hipError_t e = hipSuccess;
   if (dm.Nc > 0) {
@@ -561,27 +729,41 @@ static hipError_t launch_bwd_t(const Dims& dm, const void* q, const void* k, con
     if (e == hipSuccess) e = launch_compress(dt, 1, v, w_v, vc, nullptr, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d, dm.Nc, s);
     if (e != hipSuccess) return e;
   }
+  const int64_t nbits = (int64_t)(bits_bytes(dm) / 4);
+  bwd_fill_kernel<<<dim3((unsigned)((nbits + 255) / 256)), dim3(256), 0, s>>>((float*)sbits, nbits);
+  const int64_t npairs = dm.B * dm.Tq * dm.Hkv * dm.n;
+  bwd_bits_kernel<<<dim3((unsigned)((npairs + 255) / 256)), dim3(256), 0, s>>>(idx, vid, sbits, tbits, dm);
   bwd_fill_kernel<<<dim3((unsigned)((dm.l + 255) / 256)), dim3(256), 0, s>>>(dw_k, dm.l);
   bwd_fill_kernel<<<dim3((unsigned)((dm.l + 255) / 256)), dim3(256), 0, s>>>(dw_v, dm.l);
   bwd_row_kernel<T><<<dim3((unsigned)dm.Tq, (unsigned)dm.Hkv, (unsigned)dm.B), dim3(BWD_THREADS), 0, s>>>(
       (const T*)q, (const T*)k, (const T*)v, kc, vc, idx, vid, gates, (const T*)dout, dq, dgates, st_l, st_e, dm);
   // channels per lane: 16 (head_dim <= 128) or 32 (<= 256)
-  const dim3 gk((unsigned)((dm.T + KB - 1) / KB), (unsigned)dm.Hkv, (unsigned)dm.B);
+  const dim3 gk((unsigned)((dm.T + KB - 1) / KB), (unsigned)dm.Hkv, (unsigned)(dm.B * kch.n));
   if (dm.D <= 128)
     bwd_key_kernel<T, 16><<<gk, dim3(BWD_THREADS), 0, s>>>((const T*)q, (const T*)k, (const T*)v, idx, vid, gates,
-                                                          (const T*)dout, st_l, st_e, dk, dv, dm);
+                                                          (const T*)dout, st_l, st_e, sbits, tbits, dk, dv, part,
+                                                          dm, kch);
   else
     bwd_key_kernel<T, 32><<<gk, dim3(BWD_THREADS), 0, s>>>((const T*)q, (const T*)k, (const T*)v, idx, vid, gates,
-                                                          (const T*)dout, st_l, st_e, dk, dv, dm);
+                                                          (const T*)dout, st_l, st_e, sbits, tbits, dk, dv, part,
+                                                          dm, kch);
+  const int64_t tot = dm.B * dm.T * dm.Hkv * dm.D;
+  if (kch.n > 1)
+    bwd_chunk_sum_kernel<<<dim3((unsigned)((tot + BWD_THREADS - 1) / BWD_THREADS)), dim3(BWD_THREADS), 0, s>>>(
+        part, dk, dv, dm.T, dm, kch);
   if (dm.Nc > 0) {
-    const dim3 gc((unsigned)((dm.Nc + KB - 1) / KB), (unsigned)dm.Hkv, (unsigned)dm.B);
+    const RowChunks cch = ckey_rows(dm);
+    const dim3 gc((unsigned)((dm.Nc + KB - 1) / KB), (unsigned)dm.Hkv, (unsigned)(dm.B * cch.n));
     if (dm.D <= 128)
-      bwd_ckey_kernel<T, 16><<<gc, dim3(BWD_THREADS), 0, s>>>((const T*)q, kc, vc, vid, gates, (const T*)dout, st_l,
-                                                             st_e, dkc, dvc, dm);
+      bwd_ckey_kernel<T, 16><<<gc, dim3(BWD_THREADS), 0, s>>>((const T*)q, kc, vc, gates, (const T*)dout, st_l,
+                                                             st_e, tbits, dkc, dvc, part, dm, cch);
     else
-      bwd_ckey_kernel<T, 32><<<gc, dim3(BWD_THREADS), 0, s>>>((const T*)q, kc, vc, vid, gates, (const T*)dout, st_l,
-                                                             st_e, dkc, dvc, dm);
-    const int64_t tot = dm.B * dm.T * dm.Hkv * dm.D;
+      bwd_ckey_kernel<T, 32><<<gc, dim3(BWD_THREADS), 0, s>>>((const T*)q, kc, vc, gates, (const T*)dout, st_l,
+                                                             st_e, tbits, dkc, dvc, part, dm, cch);
+    const int64_t ctot = dm.B * dm.Nc * dm.Hkv * dm.D;
+    if (cch.n > 1)
+      bwd_chunk_sum_kernel<<<dim3((unsigned)((ctot + BWD_THREADS - 1) / BWD_THREADS)), dim3(BWD_THREADS), 0, s>>>(
+          part, dkc, dvc, dm.Nc, dm, cch);
     bwd_compress_kernel<<<dim3((unsigned)((tot + BWD_THREADS - 1) / BWD_THREADS)), dim3(BWD_THREADS), 0, s>>>(
         dkc, dvc, w_k, w_v, dk, dv, dm);
     bwd_dw_kernel<T><<<dim3((unsigned)((dm.Nc + 15) / 16), (unsigned)dm.B), dim3(BWD_THREADS), 0, s>>>(

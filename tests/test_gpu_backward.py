@@ -46,7 +46,7 @@ def _run(wl, inp, dout, idx):
 
 
 @pytest.mark.parametrize("case", ["f32-tiny", "bf16-ragged", "bf16-batch2", "bf16-short", "bf16-no-cmp-block",
-                                  "bf16-all-text", "bf16-q-start"])
+                                  "bf16-all-text", "bf16-q-start", "bf16-row-chunks"])
 def test_layer_backward(case):
     if case == "f32-tiny":
         wl = _wl(dtype="f32", T=300, Hq=4, Hkv=1, D=64, n=4, w=128, lead=16, corr=False)
@@ -60,8 +60,10 @@ def test_layer_backward(case):
         wl = _wl(T=31, Hq=8, Hkv=2, n=4, w=16)
     elif case == "bf16-all-text":
         wl = _wl(T=200, Hq=8, Hkv=2, lead=200, n=4, w=64)
-    else:  # a block of query rows at the end of the sequence
+    elif case == "bf16-q-start":  # a block of query rows at the end of the sequence
         wl = _wl(T=900, Hq=14, Hkv=2, q_start=600, q_len=300, lead=0, tail=20, n=6, w=128)
+    else:  # enough rows that the key kernels split them into several chunks (3 and 5)
+        wl = _wl(T=4500, Hq=8, Hkv=2, lead=32, tail=40, n=6, w=200)
     flush("backward %s" % case)
     inp, dout, idx = _setup(wl)
     got = _run(wl, inp, dout, idx)
