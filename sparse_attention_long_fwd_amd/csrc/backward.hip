@@ -60,6 +60,21 @@ __device__ __forceinline__ float dot_lds(const float* x, const TK* y, int D) {
   return acc;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+// acc + <x, y> over 8 bf16 channels: v_dot2_f32_bf16 takes two exact products per instruction
+// into an fp32 sum.
+__device__ __forceinline__ float dot8_bf16(bf16x8 x, bf16x8 y, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), __builtin_shufflevector(y, y, 0, 1),
+                                        acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), __builtin_shufflevector(y, y, 2, 3),
+                                        acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), __builtin_shufflevector(y, y, 4, 5),
+                                        acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), __builtin_shufflevector(y, y, 6, 7),
+                                         acc, false);
+}
+
 // ---------------------------------------------------------------------------
 // Stage 1.  Up to HB heads of one KV group at once over one key list, so each key row is read
 // once for all of them.  qs, dos: [HB][D] query and upstream gradient (LDS); thread e < D owns
@@ -68,7 +83,8 @@ __device__ __forceinline__ float dot_lds(const float* x, const TK* y, int D) {
 constexpr int HB = 8;
 
 template <typename TK, typename KeyFn>
-__device__ void bwd_branch_rows(const float* qs, const float* dos, const TK* kb, const TK* vb, int64_t kstride,
+__device__ void bwd_branch_rows(const float* qs, const float* dos, const bf16* qh, const bf16* dh, const TK* kb,
+                                const TK* vb, int64_t kstride,
                                 int D, int64_t nslots, KeyFn key_of, float scale, const float* gate, int nh,
                                 float* dqs, float* ps, float* pds, int64_t* us, float* wred, float* L, float* E) {
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
@@ -106,14 +122,23 @@ __device__ void bwd_branch_rows(const float* qs, const float* dos, const TK* kb,
       float acc[HB];
 #pragma unroll
       for (int h = 0; h < HB; ++h) acc[h] = 0.f;
-      for (int e = 0; e < D; e += 8) {
-        float f[8];
-        ld8(kr + e, f);
+      if constexpr (sizeof(TK) == 2) {
+        for (int e = 0; e < D; e += 8) {
+          const bf16x8 f = *(const bf16x8*)(kr + e);
 #pragma unroll
-        for (int h = 0; h < HB; ++h)
-          if (h < nh)
+          for (int h = 0; h < HB; ++h)
+            if (h < nh) acc[h] = dot8_bf16(*(const bf16x8*)(qh + h * D + e), f, acc[h]);
+        }
+      } else {
+        for (int e = 0; e < D; e += 8) {
+          float f[8];
+          ld8(kr + e, f);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[h] = fmaf(qs[h * D + e + i], f[i], acc[h]);
+          for (int h = 0; h < HB; ++h)
+            if (h < nh)
+#pragma unroll
+              for (int i = 0; i < 8; ++i) acc[h] = fmaf(qs[h * D + e + i], f[i], acc[h]);
+        }
       }
 #pragma unroll
       for (int h = 0; h < HB; ++h)
@@ -142,6 +167,7 @@ __device__ void bwd_branch_rows(const float* qs, const float* dos, const TK* kb,
     E[h] = 0.f;
   }
   // pass B: E = sum P dpv, and per channel A1 = sum P dpv k, A2 = sum P k
+  const int np = BWD_THREADS / D, ch = tid % D, pt = tid / D;
   float a1[HB], a2[HB];
 #pragma unroll
   for (int h = 0; h < HB; ++h) a1[h] = a2[h] = 0.f;
@@ -157,18 +183,30 @@ __device__ void bwd_branch_rows(const float* qs, const float* dos, const TK* kb,
       float aq[HB], ad[HB];
 #pragma unroll
       for (int h = 0; h < HB; ++h) aq[h] = ad[h] = 0.f;
-      for (int e = 0; e < D; e += 8) {
-        float fk[8], fv[8];
-        ld8(kr + e, fk);
-        ld8(vr + e, fv);
+      if constexpr (sizeof(TK) == 2) {
+        for (int e = 0; e < D; e += 8) {
+          const bf16x8 fk = *(const bf16x8*)(kr + e), fv = *(const bf16x8*)(vr + e);
 #pragma unroll
-        for (int h = 0; h < HB; ++h)
-          if (h < nh)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              aq[h] = fmaf(qs[h * D + e + i], fk[i], aq[h]);
-              ad[h] = fmaf(dos[h * D + e + i], fv[i], ad[h]);
+          for (int h = 0; h < HB; ++h)
+            if (h < nh) {
+              aq[h] = dot8_bf16(*(const bf16x8*)(qh + h * D + e), fk, aq[h]);
+              ad[h] = dot8_bf16(*(const bf16x8*)(dh + h * D + e), fv, ad[h]);
             }
+        }
+      } else {
+        for (int e = 0; e < D; e += 8) {
+          float fk[8], fv[8];
+          ld8(kr + e, fk);
+          ld8(vr + e, fv);
+#pragma unroll
+          for (int h = 0; h < HB; ++h)
+            if (h < nh)
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                aq[h] = fmaf(qs[h * D + e + i], fk[i], aq[h]);
+                ad[h] = fmaf(dos[h * D + e + i], fv[i], ad[h]);
+              }
+        }
       }
 #pragma unroll
       for (int h = 0; h < HB; ++h)
@@ -194,31 +232,50 @@ __device__ void bwd_branch_rows(const float* qs, const float* dos, const TK* kb,
 #pragma unroll
     for (int h = 0; h < HB; ++h)
       for (int w2 = 0; w2 < BWD_THREADS / 64; ++w2) E[h] += wred[w2 * HB + h];
-    if (tid < D) {
-      // 8 keys at a time, their loads issued together (a slot without a key has P = 0)
+    if (pt < np) {
+      // thread = (channel e, part): part pt of the np = 256 / D parts takes the slots c = pt mod np,
+      // 8 at a time with their loads issued together (a slot without a key has P = 0)
       const int64_t cnt = (nslots - a0 < BWD_THREADS) ? nslots - a0 : BWD_THREADS;
-      for (int c0 = 0; c0 < cnt; c0 += 8) {
+      for (int c0 = pt; c0 < cnt; c0 += 8 * np) {
         float kv[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const int64_t uu = c0 + i < cnt ? us[c0 + i] : -1;
-          const float x = to_f32(kb[(uu >= 0 ? uu : 0) * kstride + tid]);
+          const int c = c0 + i * np;
+          const int64_t uu = c < cnt ? us[c] : -1;
+          const float x = to_f32(kb[(uu >= 0 ? uu : 0) * kstride + ch]);
           kv[i] = uu >= 0 ? x : 0.f;
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 8; ++i) {
+          const int c = c0 + i * np < BWD_THREADS ? c0 + i * np : BWD_THREADS - 1;
 #pragma unroll
           for (int h = 0; h < HB; ++h) {
-            a1[h] = fmaf(pds[h * BWD_THREADS + c0 + i], kv[i], a1[h]);
-            a2[h] = fmaf(ps[h * BWD_THREADS + c0 + i], kv[i], a2[h]);
+            a1[h] = fmaf(pds[h * BWD_THREADS + c], kv[i], a1[h]);
+            a2[h] = fmaf(ps[h * BWD_THREADS + c], kv[i], a2[h]);
           }
+        }
       }
     }
   }
+  // the parts' sums, in part order
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < HB; ++h) {
+    ps[h * BWD_THREADS + tid] = a1[h];
+    pds[h * BWD_THREADS + tid] = a2[h];
+  }
+  __syncthreads();
   if (tid < D)
 #pragma unroll
     for (int h = 0; h < HB; ++h)
-      if (h < nh) dqs[h * D + tid] += gate[h] * scale * (a1[h] - E[h] * a2[h]);
+      if (h < nh) {
+        float s1 = 0.f, s2 = 0.f;
+        for (int q2 = 0; q2 < np; ++q2) {
+          s1 += ps[h * BWD_THREADS + q2 * D + tid];
+          s2 += pds[h * BWD_THREADS + q2 * D + tid];
+        }
+        dqs[h * D + tid] += gate[h] * scale * (s1 - E[h] * s2);
+      }
 }
 
 template <typename T>
@@ -229,6 +286,7 @@ __global__ void __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_e
                    float* __restrict__ dq, float* __restrict__ dgates, float* __restrict__ st_l,
                    float* __restrict__ st_e, Dims dm) {
   __shared__ float qs[HB * 256], dos[HB * 256], dqs[HB * 256];
+  __shared__ __attribute__((aligned(16))) bf16 qh[sizeof(T) == 2 ? HB * 256 : 8], dh[sizeof(T) == 2 ? HB * 256 : 8];
   __shared__ float ps[HB * BWD_THREADS], pds[HB * BWD_THREADS];
   __shared__ int64_t us[BWD_THREADS];
   __shared__ float wred[(BWD_THREADS / 64) * HB];
@@ -255,6 +313,10 @@ __global__ void __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_e
       qs[x] = to_f32(q[o]);
       dos[x] = to_f32(dout[o]);
       dqs[x] = 0.f;
+      if constexpr (sizeof(T) == 2) {
+        qh[x] = q[o];
+        dh[x] = dout[o];
+      }
     }
     __syncthreads();
     float L0[HB], E0[HB], L1[HB], E1[HB], L2[HB], E2[HB], gt[HB];
@@ -266,14 +328,14 @@ __global__ void __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_e
     if (!is_vid) {
 #pragma unroll
       for (int h = 0; h < HB; ++h) gt[h] = 1.f;
-      bwd_branch_rows(qs, dos, kb, vb, kstride, D, t + 1, [=](int64_t a) { return a; }, dm.scale, gt, nh, dqs, ps,
+      bwd_branch_rows(qs, dos, qh, dh, kb, vb, kstride, D, t + 1, [=](int64_t a) { return a; }, dm.scale, gt, nh, dqs, ps,
                       pds, us, wred, L0, E0);
     } else {
       const float* gg = gates + (row0 + hb) * 3;
 #pragma unroll
       for (int h = 0; h < HB; ++h) gt[h] = h < nh ? gg[3 * h] : 0.f;
       const int64_t nvis = cmp_visible(t, dm.l, dm.d, dm.Nc);
-      bwd_branch_rows(qs, dos, kcb, vcb, kstride, D, nvis, [=](int64_t a) { return a; }, dm.scale, gt, nh, dqs, ps,
+      bwd_branch_rows(qs, dos, qh, dh, kcb, vcb, kstride, D, nvis, [=](int64_t a) { return a; }, dm.scale, gt, nh, dqs, ps,
                       pds, us, wred, L0, E0);
       auto slc_key = [=](int64_t a) -> int64_t {
         const int32_t j = sel[a / ls];
@@ -283,12 +345,12 @@ __global__ void __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_e
       };
 #pragma unroll
       for (int h = 0; h < HB; ++h) gt[h] = h < nh ? gg[3 * h + 1] : 0.f;
-      bwd_branch_rows(qs, dos, kb, vb, kstride, D, (int64_t)dm.n * ls, slc_key, dm.scale, gt, nh, dqs, ps, pds, us,
+      bwd_branch_rows(qs, dos, qh, dh, kb, vb, kstride, D, (int64_t)dm.n * ls, slc_key, dm.scale, gt, nh, dqs, ps, pds, us,
                       wred, L1, E1);
       const int64_t lo = t - dm.w + 1 > 0 ? t - dm.w + 1 : 0;
 #pragma unroll
       for (int h = 0; h < HB; ++h) gt[h] = h < nh ? gg[3 * h + 2] : 0.f;
-      bwd_branch_rows(qs, dos, kb, vb, kstride, D, t - lo + 1, [=](int64_t a) { return lo + a; }, dm.scale, gt, nh,
+      bwd_branch_rows(qs, dos, qh, dh, kb, vb, kstride, D, t - lo + 1, [=](int64_t a) { return lo + a; }, dm.scale, gt, nh,
                       dqs, ps, pds, us, wred, L2, E2);
     }
     __syncthreads();
@@ -367,13 +429,15 @@ static RowChunks make_chunks(const Dims& dm, int max_chunks, int64_t min_rows, b
 // when gs1 < 0); branch 2, when TWO, the window's slot 2.  Per head and branch b:
 //   P_b = exp(scale <q, k> - L_b),  ds = sum_b g_b P_b (<d_out, v> - E_b),
 //   dk += scale ds q,  dv += (sum_b g_b P_b) d_out,
-// the branches sharing the loads and the dot products.
-template <typename T, int MAXC, bool TWO>
+// the branches sharing the loads and the dot products.  K8: the key's channels also come packed
+// as bf16 (k8, v8; bf16 q and d_out), and the dot products run on v_dot2_f32_bf16.
+template <typename T, int MAXC, bool TWO, bool K8>
 __device__ __forceinline__ void bwd_row_terms(const T* __restrict__ q, const T* __restrict__ dout,
                                               const float* __restrict__ st_l, const float* __restrict__ st_e,
                                               const float* __restrict__ gates, int64_t row0, const Dims& dm,
                                               int c8, int s1, int gs1, bool on1, bool on2, const float* kf,
-                                              const float* vf, float* ak, float* av) {
+                                              const float* vf, const bf16x8* k8, const bf16x8* v8, float* ak,
+                                              float* av) {
   constexpr int E = 16 / (int)sizeof(T);  // elements per 16-byte load
   constexpr int NV = MAXC / E;
   constexpr int HG = 128 / (MAXC * (int)sizeof(T)) > 1 ? 128 / (MAXC * (int)sizeof(T)) : 1;
@@ -406,14 +470,23 @@ __device__ __forceinline__ void bwd_row_terms(const T* __restrict__ q, const T* 
 #pragma unroll
     for (int i = 0; i < HG; ++i) {
       float zq = 0.f, zd = 0.f;
+      if constexpr (K8) {
 #pragma unroll
-      for (int j = 0; j < NV; ++j)
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-          if (j * E + e < nc) {
-            zq = fmaf(to_f32(qv[i][j][e]), kf[j * E + e], zq);
-            zd = fmaf(to_f32(dw[i][j][e]), vf[j * E + e], zd);
+        for (int j = 0; j < NV; ++j)
+          if (j * E < nc) {
+            zq = dot8_bf16(qv[i][j], k8[j], zq);
+            zd = dot8_bf16(dw[i][j], v8[j], zd);
           }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            if (j * E + e < nc) {
+              zq = fmaf(to_f32(qv[i][j][e]), kf[j * E + e], zq);
+              zd = fmaf(to_f32(dw[i][j][e]), vf[j * E + e], zd);
+            }
+      }
 #pragma unroll
       for (int o = LPK / 2; o >= 1; o >>= 1) {
         zq += __shfl_xor(zq, o, 64);
@@ -496,6 +569,15 @@ __global__ void __launch_bounds__(BWD_THREADS)
   for (int i = 0; i < MAXC; ++i) ak[i] = av[i] = kf[i] = vf[i] = 0.f;
   load_key<MAXC>(k + (b * dm.T + ur) * kstride + (int64_t)g * D + c8 * nc,
                  v + (b * dm.T + ur) * kstride + (int64_t)g * D + c8 * nc, nc, kf, vf);
+  constexpr bool K8 = sizeof(T) == 2;
+  bf16x8 k8[MAXC / 8], v8[MAXC / 8];  // bf16 keys: the same channels packed (exact)
+#pragma unroll
+  for (int j = 0; j < MAXC / 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      k8[j][e] = (bf16)kf[8 * j + e];
+      v8[j][e] = (bf16)vf[8 * j + e];
+    }
   const int64_t ulast = (u0 + KB - 1 < dm.T - 1) ? u0 + KB - 1 : dm.T - 1;
   // Rows that can see a key of the block (t >= u0) among the chunk's rows [ra, rb).  Only rows
   // that can take part are visited, 32 at a time from bit masks: text rows, the window range of
@@ -533,8 +615,8 @@ __global__ void __launch_bounds__(BWD_THREADS)
           if (__any(sj == (int32_t)j) && j == ju) on1 = kvalid && u <= t;
       }
       if (!__any(on1 || on2)) continue;  // no key of this wave takes part
-      bwd_row_terms<T, MAXC, true>(q, dout, st_l, st_e, gates, (b * dm.Tq + r) * dm.Hq + (int64_t)g * dm.G, dm,
-                                   c8, is_vid ? 1 : 0, is_vid ? 1 : -1, on1, on2, kf, vf, ak, av);
+      bwd_row_terms<T, MAXC, true, K8>(q, dout, st_l, st_e, gates, (b * dm.Tq + r) * dm.Hq + (int64_t)g * dm.G,
+                                       dm, c8, is_vid ? 1 : 0, is_vid ? 1 : -1, on1, on2, kf, vf, k8, v8, ak, av);
     }
   }
   if (kvalid && u < ch.keys[c]) store_key_grads<MAXC>(ak, av, dk, dv, part, ch, c, b, u, dm.T, g, dm, c8);
@@ -574,8 +656,8 @@ __global__ void __launch_bounds__(BWD_THREADS)
       const int64_t r = base + __builtin_ctz(m);
       const bool on = kvalid && end_i <= dm.q0 + r;
       if (!__any(on)) continue;
-      bwd_row_terms<T, MAXC, false>(q, dout, st_l, st_e, gates, (b * dm.Tq + r) * dm.Hq + (int64_t)g * dm.G, dm,
-                                    c8, 0, 0, on, false, kf, vf, ak, av);
+      bwd_row_terms<T, MAXC, false, false>(q, dout, st_l, st_e, gates, (b * dm.Tq + r) * dm.Hq + (int64_t)g * dm.G,
+                                           dm, c8, 0, 0, on, false, kf, vf, nullptr, nullptr, ak, av);
     }
   }
   if (kvalid && i < ch.keys[c]) store_key_grads<MAXC>(ak, av, dkc, dvc, part, ch, c, b, i, dm.Nc, g, dm, c8);
