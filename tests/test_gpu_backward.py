@@ -90,3 +90,67 @@ def test_layer_backward(case):
         stats[key] = (err, lim)
         assert err <= lim, (key, err, lim)
     flush("  %s" % {k: "%.2e/%.2e" % v for k, v in stats.items()})
+
+
+def _block_sets(wl, rng):
+    """Seeded valid chosen-block sets [Tq, Hkv, n] for every row: the forced first and local blocks
+    plus distinct random earlier blocks, ascending, -1 padded (test input only; any valid set is a
+    legal input of the backward)."""
+    p = wl.params()
+    n, ls, ni, nl = p["top_n"], p["sel_block"], p["n_init"], p["n_local"]
+    idx = np.full((wl.q_len, wl.num_kv_heads, n), -1, dtype=np.int32)
+    for r in range(wl.q_len):
+        jt = (wl.q_start + r) // ls
+        if jt + 1 <= n:
+            idx[r, :, :jt + 1] = np.arange(jt + 1)
+            continue
+        forced = list(range(ni)) + list(range(jt - nl + 1, jt + 1))
+        pool = jt - nl + 1 - ni  # blocks ni .. jt - nl
+        for g in range(wl.num_kv_heads):
+            pick = rng.choice(pool, n - len(forced), replace=False) + ni
+            idx[r, g] = np.sort(np.concatenate([np.array(forced), pick]))
+    return idx
+
+
+def test_layer_backward_36k_sampled_rows():
+    """The 36K backward in the bench's launch configuration with the upstream gradient zero except
+    on sampled rows: those rows' dq and d gates (every other row's exactly zero) and the whole dk,
+    dv, dw_k, dw_v (which then hold only the sampled rows' contributions) against the oracle
+    restricted to the same rows.  Rows sit at the row-chunk boundaries of both key kernels, at the
+    text/video edges and at random; every other row carries a seeded valid block set."""
+    wl = synth.WORKLOADS["36k"]
+    flush("backward 36k sampled rows")
+    inp = synth.make_inputs(wl, DEV)
+    B, Tq, Hq, D = inp["q"].shape
+    rng = np.random.default_rng(4321)
+    rows = {3, 255, 256, 300, 1151, 1152, 9087, 9088, 18175, 18176, 27263, 27264, 36095, 36096, Tq - 1}
+    rows |= set(int(x) for x in rng.integers(256, Tq - 256, 6))
+    rows = np.array(sorted(rows), dtype=np.int64)
+    idx = _block_sets(wl, rng)
+    q0, k0, v0 = host(inp["q"][0]), host(inp["k"][0]), host(inp["v"][0])
+    wk, wv, g0, vid0 = host(inp["w_k"]), host(inp["w_v"]), host(inp["gates"][0]), host(inp["is_video"][0])
+    fwd = oracle.layer(q0, k0, v0, wk, wv, g0, vid0, wl.params(), q_start=wl.q_start, rows=rows)
+    idx[rows] = fwd["idx"]
+    mask = torch.zeros((B, Tq, 1, 1), dtype=torch.bfloat16)
+    mask[0, torch.from_numpy(rows)] = 1
+    dout = (synth.normal(1000 * wl.index + 900, (B, Tq, Hq, D), "cpu").to(torch.bfloat16) * mask).to(DEV)
+    got = _run(wl, inp, dout, torch.from_numpy(idx)[None].to(DEV))
+    ref = oracle.layer_bwd(q0, k0, v0, wk, wv, g0, vid0, wl.params(), host(dout[0]), q_start=wl.q_start, idx=idx,
+                           rows=rows)
+    stats = {}
+    others = np.setdiff1d(np.arange(Tq), rows)
+    for key in ("dq", "dgates"):
+        g = host(got[KEYS[key]][0]).astype(np.float64)
+        assert not np.any(g[others]), key  # rows with zero upstream gradient pass none
+        err = float(np.abs(g[rows] - ref[key]).max())
+        lim = REL[key] * float(np.abs(ref[key]).max()) + 1e-5
+        stats[key] = (err, lim)
+        assert err <= lim, (key, err, lim)
+    for key in ("dk", "dv", "dw_k", "dw_v"):
+        g = host(got[KEYS[key]]).astype(np.float64)
+        g = g[0] if key in ("dk", "dv") else g
+        err = float(np.abs(g - ref[key]).max())
+        lim = REL[key] * float(np.abs(ref[key]).max()) + 1e-5
+        stats[key] = (err, lim)
+        assert err <= lim, (key, err, lim)
+    flush("  %s" % {k: "%.2e/%.2e" % v for k, v in stats.items()})
