@@ -28,6 +28,15 @@
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null
  *    stream) and returns an nsa_status.  Arguments are validated before any
  *    launch; on failure nothing is launched and nsa_last_error() describes it.
+ *  - nsa_hybrid_layer_fwd(_branch_kv) and nsa_sparse_attn_fwd may run their
+ *    window pass (window branch and text rows) on a second stream that the
+ *    library creates once per calling thread and device (default priority,
+ *    kept until the process ends): it is forked from `stream` after earlier
+ *    work there and joined back into `stream` before the call's last kernel,
+ *    so all of the call's work is ordered after what precedes it on `stream`
+ *    and complete before what follows.  The first call of a thread made while
+ *    `stream` is being captured into a graph, and every call while phase
+ *    timing is on, keeps to `stream` alone.
  *  - Layouts are row-major and token-major:
  *      q, o_* , out   [B, q_len, Hq, D]      (dtype)
  *      k, v           [B, kv_len, Hkv, D]    (dtype)
@@ -307,7 +316,9 @@ int32_t nsa_set_force_generic(int32_t on);
  * boundary (compress | compression branch + importance | top-n | window and
  * text rows | selection + combine); nsa_profile_read waits for the last event
  * of the most recent call and writes the phase durations in ms (returns their
- * count, or a negative status).  Process-wide, not for concurrent use. */
+ * count, or a negative status).  While it is on, the window pass runs in order
+ * on the caller's stream (no second stream), so each phase is timed alone.
+ * Process-wide, not for concurrent use. */
 int32_t nsa_profile_enable(int32_t on);
 int32_t nsa_profile_read(float* ms, int32_t max_phases);
 

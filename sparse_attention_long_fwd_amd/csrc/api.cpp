@@ -174,7 +174,7 @@ int run_sparse(int32_t dtype, const Dims& dm, const void* q, const BranchKV& kv,
                void* o_swa, void* ws, hipStream_t s, bool forced_local = false) {
   hipError_t e = use_fast(dtype, dm)
                      ? launch_sparse_fast(dm, q, kv.ks, kv.vs, kv.kw, kv.vw, idx, vid, o_cmp, ocmp_f32, gates, out,
-                                          o_slc, o_swa, ws, s, prof_mark, forced_local)
+                                          o_slc, o_swa, ws, s, prof_mark, forced_local, !g_profiling)
                      : launch_sparse_generic(dtype, dm, q, kv.ks, kv.vs, kv.kw, kv.vw, idx, vid, o_cmp, gates, out,
                                              o_slc, o_swa, s);
   if (e != hipSuccess) return hip_fail(e, "selection/window kernel");
@@ -436,9 +436,23 @@ int32_t layer_fwd(const void* q, const BranchKV& kv, const void* k_cmp_in, const
   st = run_cmp(dtype, cdtype, dm, q, kc_use, kl_use, ksc_use, vc_use, vl_use, is_video, ocmp, ocmp32, lse, imp, s);
   if (st != NSA_OK) return st;
   prof_mark(s);
+  // The window pass needs neither the compression branch nor the top-n: outside phase timing it
+  // starts here on the side stream, beside the top-n and the selection kernels.
+  const SideStream* side = (fast && !g_profiling) ? side_stream(s) : nullptr;
+  if (side) {
+    hipError_t e = launch_sparse_window(dm, q, kv.ks, kv.vs, kv.kw, kv.vw, is_video, out, o_swa, sparse_ws_ptr, s,
+                                        side, true);
+    if (e != hipSuccess) return hip_fail(e, "window kernel");
+  }
   hipError_t e = launch_topk(dm, imp, is_video, idx, s);
   if (e != hipSuccess) return hip_fail(e, "top-n kernel");
   prof_mark(s);
+  if (side) {
+    e = launch_sparse_select(dm, q, kv.ks, kv.vs, kv.kw, kv.vw, idx, is_video, ocmp32, true, gates, out, o_slc,
+                             sparse_ws_ptr, s, side, true);
+    if (e != hipSuccess) return hip_fail(e, "selection kernels");
+    return NSA_OK;
+  }
   if (fast) {
     st = run_sparse(dtype, dm, q, kv, idx, is_video, ocmp32, true, gates, out, o_slc, o_swa, sparse_ws_ptr, s,
                     true);

@@ -36,11 +36,37 @@ hipError_t launch_compress_vt(const Dims& dm, const void* v, const float* w_v, v
 // of the selection branch; kw / vw: of the window branch and text rows.  forced_local: idx comes
 // from the layer's own top-n, so each video row's last min(n_local, jt + 1) entries are its forced
 // local blocks jt - n_local + 1 .. jt (the window pass may then take them over).
+// concurrent: the window pass runs on the calling thread's side stream (side_stream) beside the
+// selection kernels; otherwise the two passes run in order on s (mark is called between them).
 hipError_t launch_sparse_fast(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
                               const void* vw, const int32_t* idx,
                               const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out,
                               void* o_slc, void* o_swa, void* ws, hipStream_t s,
-                              void (*mark)(hipStream_t) = nullptr, bool forced_local = false);
+                              void (*mark)(hipStream_t) = nullptr, bool forced_local = false,
+                              bool concurrent = false);
+
+// The calling thread's second stream on the current device (non-blocking, default priority) and a
+// fork / join event pair.  The window pass (window branch, dense text rows, the forced local
+// selection partials) reads only q, k, v and the row flags, so it can run there beside the top-n
+// and the selection kernels; only the selection merge reads its outputs.  Created on the first
+// call outside stream capture and kept until the process ends; null when that fails or the first
+// call comes during a capture (the passes then run in order on the caller's stream).
+struct SideStream {
+  hipStream_t s;
+  hipEvent_t fork, join;
+};
+SideStream* side_stream(hipStream_t caller);
+// The two passes of launch_sparse_fast.  With side, the window pass runs on side->s once the
+// caller's stream reaches the launch (side->fork) and records side->join when done; the selection
+// pass's merge waits for side->join on the caller's stream.  Both passes take the same side (or
+// null) and the same workspace.
+hipError_t launch_sparse_window(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
+                                const void* vw, const uint8_t* vid, void* out, void* o_swa, void* ws, hipStream_t s,
+                                const SideStream* side, bool forced_local);
+hipError_t launch_sparse_select(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
+                                const void* vw, const int32_t* idx, const uint8_t* vid, const void* o_cmp,
+                                bool ocmp_f32, const float* gates, void* out, void* o_slc, void* ws, hipStream_t s,
+                                const SideStream* side, bool forced_local);
 
 // Window / text-row flash kernel: swa32 / swa_bf window outputs (either may be
 // NULL), text: output of text rows (NULL: skip them); ws: flash_workspace(dm).

@@ -6,7 +6,7 @@ void slc_partial_arrays(const Dims& dm, void* ws, void** ml, void** o);
 hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
                             const uint8_t* vid, const void* ocmp, bool ocmp_f32, const float* swa32,
                             const float* gates, void* out, void* o_slc, void* ws, hipStream_t s,
-                            bool local_fused);
+                            bool local_fused, hipEvent_t before_merge);
 
 // Block-major selection packs (row, slot) into 32 bits: rows below 2^26.
 bool fast_supported(int32_t dtype, const Dims& dm) {
@@ -21,23 +21,76 @@ size_t fast_sparse_workspace(const Dims& dm) {
   return rup((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 4) + rup(flash_workspace(dm)) + rup(slc_block_workspace(dm));
 }
 
+// The window pass takes over the forced local blocks of the selection (they lie inside the window
+// and are scored there anyway) when the layer chose the blocks and the keys are shared.
+static bool fuse_local(const Dims& dm, const void* ks, const void* vs, const void* kw, const void* vw,
+                       bool forced_local) {
+  return forced_local && ks == kw && vs == vw && local_fusable(dm);
+}
+
+SideStream* side_stream(hipStream_t caller) {
+  struct Slot {
+    SideStream ss{};
+    bool tried = false, ok = false;
+  };
+  constexpr int kMaxDev = 64;
+  thread_local Slot tab[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+  Slot& sl = tab[dev];
+  if (!sl.tried) {
+    // no stream or event creation while the caller's stream is being captured
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    sl.tried = true;
+    sl.ok = hipStreamCreateWithFlags(&sl.ss.s, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&sl.ss.fork, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&sl.ss.join, hipEventDisableTiming) == hipSuccess;
+  }
+  return sl.ok ? &sl.ss : nullptr;
+}
+
+hipError_t launch_sparse_window(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
+                                const void* vw, const uint8_t* vid, void* out, void* o_swa, void* ws, hipStream_t s,
+                                const SideStream* side, bool forced_local) {
+  float* swa32 = (float*)ws;
+  char* fws = (char*)ws + rup((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 4);
+  char* sws = fws + rup(flash_workspace(dm));
+  void *lml = nullptr, *lo = nullptr;
+  if (fuse_local(dm, ks, vs, kw, vw, forced_local)) slc_partial_arrays(dm, sws, &lml, &lo);
+  hipStream_t sw = s;
+  if (side) {
+    hipError_t e = hipEventRecord(side->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (e != hipSuccess) return e;
+    sw = side->s;
+  }
+  // window branch (fp32 for the combine, bf16 copy if asked) and dense text rows
+  hipError_t e = launch_flash_fast(dm, q, kw, vw, vid, swa32, o_swa, out, fws, sw, lml, lo);
+  if (e == hipSuccess && side) e = hipEventRecord(side->join, sw);
+  return e;
+}
+
+hipError_t launch_sparse_select(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
+                                const void* vw, const int32_t* idx, const uint8_t* vid, const void* o_cmp,
+                                bool ocmp_f32, const float* gates, void* out, void* o_slc, void* ws, hipStream_t s,
+                                const SideStream* side, bool forced_local) {
+  float* swa32 = (float*)ws;
+  char* sws = (char*)ws + rup((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 4) + rup(flash_workspace(dm));
+  // selection branch and the gated combine of video rows
+  return launch_slc_block(dm, q, ks, vs, idx, vid, o_cmp, ocmp_f32, swa32, gates, out, o_slc, sws, s,
+                          fuse_local(dm, ks, vs, kw, vw, forced_local), side ? side->join : nullptr);
+}
+
 hipError_t launch_sparse_fast(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
                               const void* vw, const int32_t* idx,
                               const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out,
                               void* o_slc, void* o_swa, void* ws, hipStream_t s, void (*mark)(hipStream_t),
-                              bool forced_local) {
-  float* swa32 = (float*)ws;
-  char* fws = (char*)ws + rup((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 4);
-  char* sws = fws + rup(flash_workspace(dm));
-  // The window pass takes over the forced local blocks of the selection (they lie inside the
-  // window and are scored there anyway) when the layer chose the blocks and the keys are shared.
-  const bool fuse = forced_local && ks == kw && vs == vw && local_fusable(dm);
-  void *lml = nullptr, *lo = nullptr;
-  if (fuse) slc_partial_arrays(dm, sws, &lml, &lo);
-  // window branch (fp32 for the combine, bf16 copy if asked) and dense text rows
-  hipError_t e = launch_flash_fast(dm, q, kw, vw, vid, swa32, o_swa, out, fws, s, lml, lo);
+                              bool forced_local, bool concurrent) {
+  const SideStream* side = concurrent ? side_stream(s) : nullptr;
+  hipError_t e = launch_sparse_window(dm, q, ks, vs, kw, vw, vid, out, o_swa, ws, s, side, forced_local);
   if (e != hipSuccess) return e;
-  if (mark) mark(s);
-  // selection branch and the gated combine of video rows
-  return launch_slc_block(dm, q, ks, vs, idx, vid, o_cmp, ocmp_f32, swa32, gates, out, o_slc, sws, s, fuse);
+  if (mark && !side) mark(s);
+  return launch_sparse_select(dm, q, ks, vs, kw, vw, idx, vid, o_cmp, ocmp_f32, gates, out, o_slc, ws, s, side,
+                              forced_local);
 }

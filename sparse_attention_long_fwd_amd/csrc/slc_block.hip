@@ -436,7 +436,8 @@ void slc_partial_arrays(const Dims& dm, void* ws, void** ml, void** o) {
 
 hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
                             const uint8_t* vid, const void* ocmp, bool ocmp_f32, const float* swa32,
-                            const float* gates, void* out, void* o_slc, void* ws, hipStream_t s, bool local_fused) {
+                            const float* gates, void* out, void* o_slc, void* ws, hipStream_t s, bool local_fused,
+                            hipEvent_t before_merge) {
   if (dm.B <= 0 || dm.Tq <= 0) return hipSuccess;
   const int bgs = (int)(dm.B * dm.Hkv);
   char* p = (char*)ws;
@@ -472,6 +473,11 @@ hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const 
                                                                    local_fused ? 1 : 0);
   slc_chunk_kernel<<<dim3((unsigned)bgs * bk.cap_c), dim3(dm.G * 64), 0, s>>>((const bf16*)q, (const bf16*)k,
                                                                              (const bf16*)v, bk, pml, po, dm);
+  // the merge reads the window pass's outputs (run on another stream when before_merge is given)
+  if (before_merge) {
+    e = hipStreamWaitEvent(s, before_merge, 0);
+    if (e != hipSuccess) return e;
+  }
   const int64_t items = dm.B * dm.Tq * dm.Hkv;
   const dim3 mg((unsigned)((items + 3) / 4));
   if (ocmp_f32)
