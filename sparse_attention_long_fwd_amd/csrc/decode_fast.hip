@@ -17,11 +17,13 @@
 //     on the window blocks, which need no selection; then every wave takes one
 //     chosen block below the window.  A block is scored once for both the
 //     selection and the window branch; each workgroup leaves one partial per
-//     (branch, head).
-//  3. dmerge: one workgroup per (sequence, group) merges those partials per
-//     head and applies the gated combine with the compression output.  Text rows (dense causal
-//     attention, ungated): their split workgroups exit at once; here each wave
-//     runs an online softmax over a strided share of the blocks.
+//     (branch, head), and the first one the split weights of the compression
+//     output.
+//  3. dmerge: one thread per (head, channel) merges those partials and the
+//     compression split partials and applies the gated combine.  Text rows
+//     (dense causal attention, ungated): their split workgroups exit at once;
+//     in dsel each wave runs an online softmax over a strided share of the
+//     blocks.
 #include "fast_common.hpp"
 #include "topk_wave.hpp"
 
@@ -399,33 +401,37 @@ __global__ void __launch_bounds__(256) dcmp_pipe_kernel(const bf16* __restrict__
 // ---------------------------------------------------------------------------
 // 2. selection, window and the final merge
 
-// Per-head softmax statistics of the split partials, one wave per head (waves loop over heads):
+// Per-head softmax statistics of the split partials, 32 lanes per head (heads threadIdx.x / 32,
+// so one load round for up to blockDim.x / 32 heads and 32 splits; more loop):
 // s_fac[h][s] = exp2(m_s - M_h) / L_h (0 for empty splits), s_M[h], s_L[h].
 __device__ __forceinline__ void dsplit_stats(const float* pu, int G, int nsplit, float* s_fac, float* s_M,
                                              float* s_L) {
-  const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
-  for (int hh = threadIdx.x >> 6; hh < G; hh += nw) {
-    // one load round for up to 64 splits (the usual case); more splits loop
+  const int sl = threadIdx.x & 31, nh = blockDim.x >> 5;
+  for (int hh = threadIdx.x >> 5; hh < G; hh += nh) {
     float m0 = -INFINITY, l0 = 0.f;
-    if (lane < nsplit) {
-      m0 = pu[(lane * G + hh) * PSTRIDE];
-      l0 = pu[(lane * G + hh) * PSTRIDE + 1];
+    if (sl < nsplit) {
+      m0 = pu[(sl * G + hh) * PSTRIDE];
+      l0 = pu[(sl * G + hh) * PSTRIDE + 1];
     }
     float m = m0;
-    for (int s = lane + 64; s < nsplit; s += 64) m = fmaxf(m, pu[(s * G + hh) * PSTRIDE]);
-    const float M = wave_max(m);
+    for (int s = sl + 32; s < nsplit; s += 32) m = fmaxf(m, pu[(s * G + hh) * PSTRIDE]);
+    float M = m;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
     float l = m0 > -INFINITY ? l0 * fexp2(m0 - M) : 0.f;
-    for (int s = lane + 64; s < nsplit; s += 64) {
+    for (int s = sl + 32; s < nsplit; s += 32) {
       const float ms = pu[(s * G + hh) * PSTRIDE];
       if (ms > -INFINITY) l += pu[(s * G + hh) * PSTRIDE + 1] * fexp2(ms - M);
     }
-    const float L = wave_sum(l);
-    if (lane < nsplit) s_fac[hh * nsplit + lane] = (m0 > -INFINITY && L > 0.f) ? fexp2(m0 - M) / L : 0.f;
-    for (int s = lane + 64; s < nsplit; s += 64) {
+    float L = l;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+    if (sl < nsplit) s_fac[hh * nsplit + sl] = (m0 > -INFINITY && L > 0.f) ? fexp2(m0 - M) / L : 0.f;
+    for (int s = sl + 32; s < nsplit; s += 32) {
       const float ms = pu[(s * G + hh) * PSTRIDE];
       s_fac[hh * nsplit + s] = (ms > -INFINITY && L > 0.f) ? fexp2(ms - M) / L : 0.f;
     }
-    if (lane == 0) {
+    if (sl == 0) {
       s_M[hh] = M;
       s_L[hh] = L;
     }
@@ -439,16 +445,15 @@ __device__ __forceinline__ void dsplit_stats(const float* pu, int G, int nsplit,
 // (scores once, a window partial, and after the selection a selection partial if the block
 // was chosen).  Then wave w takes chosen block sg*4 + w of those below the window.  A wave's
 // blocks accumulate online into one selection and one window partial (max, sum, O), which the
-// workgroup merges in LDS; the last workgroup of the unit to finish (device-scope counter,
-// zeroed by the split kernel) merges the compression, selection and window partials per head
-// and writes the gated outputs.  Text rows: dense causal attention, every wave an online
-// softmax over blocks sg*4+w, +4*wgs, ...
+// workgroup merges in LDS and writes as one partial per (branch, head); workgroup 0 of the unit
+// also writes the split weights of the compression partials (facw).  dmerge_kernel combines them.
+// Text rows: dense causal attention, every wave an online softmax over blocks sg*4+w, +4*wgs, ...
 __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                    const bf16* __restrict__ v, const float* __restrict__ part,
                                                    const uint8_t* __restrict__ vid, float* __restrict__ lse,
                                                    int32_t* __restrict__ idx,
                                                    float* __restrict__ imp_out, float* __restrict__ part3,
-                                                   float* __restrict__ ocmp32, Dims dm,
+                                                   float* __restrict__ facw, Dims dm,
                                                    DecVar dv, int nsplit, int wgs) {
   extern __shared__ float dsm[];
   const int G = dm.G;
@@ -569,6 +574,9 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
     __syncthreads();
     if (sg == 0 && lse && tid < G)
       lse[b * dm.Hq + g * G + tid] = s_L[tid] > 0.f ? (s_M[tid] + flog2(s_L[tid])) * LN2_F : -INFINITY;
+    // the split weights, for the merge kernel's compression output
+    if (sg == 0)
+      for (int i = tid; i < G * nsplit; i += blockDim.x) facw[(int64_t)unit * G * nsplit + i] = s_fac[i];
     // 4 blocks a thread per pass; loads clamped to valid addresses and unconditional, so a
     // pass has all of them in flight at once (invalid terms get weight 0)
     for (int j0 = 0; j0 <= jt; j0 += 4 * blockDim.x) {
@@ -619,15 +627,6 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
         block_scores(jw, scw);
         masked(jw, scw, 1, x);
         accumulate(1, x);
-      }
-      // then this workgroup's slice of the compression output, merged over the splits
-      const int per = (G * HD + wgs - 1) / wgs;
-      for (int i = sg * per + tid - 64; i < (sg + 1) * per && i < G * HD; i += blockDim.x - 64) {
-        const int hh = i / HD, e = i % HD;
-        float oc = 0.f;
-#pragma unroll 16
-        for (int s = 0; s < nsplit; ++s) oc += s_fac[hh * nsplit + s] * pc[(s * G + hh) * PSTRIDE + 2 + e];
-        ocmp32[(int64_t)unit * G * HD + i] = oc;
       }
     }
     __syncthreads();
@@ -726,98 +725,65 @@ __global__ void __launch_bounds__(256) dsel_kernel(const bf16* __restrict__ q, c
 
 
 // ---------------------------------------------------------------------------
-// One workgroup per (sequence, KV group): merges the selection kernel's workgroup partials of the
-// selection and window branches (text rows: the dense partials) per head and writes the outputs,
-// gated for video rows with the compression output.
-__global__ void __launch_bounds__(256) dmerge_kernel(const float* __restrict__ part3,
-                                                     const float* __restrict__ ocmp32,
+// One thread per (head, channel) of a (sequence, KV group), mq workgroups per (sequence, group):
+// merges per head the selection kernel's workgroup partials of the selection and window branches
+// (text rows: the dense partials) and, for video rows, the compression split partials with the
+// weights the selection kernel derived (2^(m_s - M) / L per split, summed over the splits in
+// order), then writes the outputs, gated for video rows.  Every load of a thread is independent of
+// the others (partials of empty entries are read and then given weight 0), so they go out
+// together.
+__global__ void __launch_bounds__(256) dmerge_kernel(const float* __restrict__ part3, const float* __restrict__ part,
+                                                     const float* __restrict__ facw,
                                                      const uint8_t* __restrict__ vid, const float* __restrict__ gates,
                                                      bf16* __restrict__ out, bf16* __restrict__ o_cmp,
                                                      bf16* __restrict__ o_slc, bf16* __restrict__ o_swa, Dims dm,
-                                                     int wgs) {
+                                                     int wgs, int nsplit, int mq) {
   constexpr int PO = 4;        // O offset within a partial (16-byte aligned rows)
   constexpr int PW = HD + PO;  // partial of one (branch, head): max, sum, -, -, O[128]
-  extern __shared__ float s_wgt[];  // [wgs][2][G] weights 2^(m - M) / L of the workgroup partials
-  const int G = dm.G, tid = threadIdx.x;
-  const int unit = blockIdx.x;
+  const int G = dm.G;
+  const int unit = blockIdx.x / mq;
+  const int i = (blockIdx.x % mq) * blockDim.x + threadIdx.x;
+  if (i >= G * HD) return;
+  const int hh = i / HD, e = i % HD;
   const int64_t b = unit / dm.Hkv;
   const int g = unit % dm.Hkv;
   const bool text = vid && !vid[b];
   const float* pu = part3 + (int64_t)unit * wgs * 2 * G * PW;
-  // statistics of the (branch, head) pairs: 16 lanes a pair, one load round for <= 16 partials
-  for (int pr0 = 0; pr0 < 2 * G; pr0 += 16) {
-    const int pr = pr0 + (tid >> 4), sl = tid & 15;
-    float m = -INFINITY, ls = 0.f;
-    if (pr < 2 * G)
-      for (int s = sl; s < wgs; s += 16) {
-        const float* ph = pu + (s * 2 * G + pr) * PW;
-        const float l1 = ph[1], m1 = ph[0];
-        if (l1 > 0.f) {
-          const float M1 = fmaxf(m, m1);
-          ls = ls * fexp2(m - M1) + l1 * fexp2(m1 - M1);
-          m = M1;
-        }
-      }
-    float M = m;
+  float ob[2];
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    float L = m > -INFINITY ? ls * fexp2(m - M) : 0.f;
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
-    if (pr < 2 * G)
-      for (int s = sl; s < wgs; s += 16) {
-        const float* ph = pu + (s * 2 * G + pr) * PW;
-        s_wgt[s * 2 * G + pr] = (ph[1] > 0.f && L > 0.f) ? fexp2(ph[0] - M) / L : 0.f;
-      }
+  for (int br = 0; br < 2; ++br) {
+    // online over the workgroup partials: (max, sum, O) rescaled as the maximum grows
+    float M = -INFINITY, L = 0.f, o = 0.f;
+#pragma unroll 4
+    for (int s = 0; s < wgs; ++s) {
+      const float* ph = pu + (s * 2 * G + br * G + hh) * PW;
+      const float m1 = ph[0], l1 = ph[1], x = ph[PO + e];
+      const bool live = l1 > 0.f;  // the O of empty partials is never written: selected away
+      const float Mn = live ? fmaxf(M, m1) : M;
+      const float a = M > -INFINITY ? fexp2(M - Mn) : 0.f;
+      const float c = live ? fexp2(m1 - Mn) : 0.f;
+      L = L * a + l1 * c;
+      o = o * a + (live ? x * c : 0.f);
+      M = Mn;
+    }
+    ob[br] = L > 0.f ? o / L : 0.f;
   }
-  __syncthreads();
-  for (int i = tid; i < G * HD / 4; i += blockDim.x) {
-    const int hh = (4 * i) / HD, e = (4 * i) % HD;
-    float ob[2][4];
-#pragma unroll
-    for (int br = 0; br < 2; ++br) {
-      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-      for (int s = 0; s < wgs; ++s) {
-        const float f = s_wgt[s * 2 * G + br * G + hh];
-        const float4 x = *(const float4*)(pu + (s * 2 * G + br * G + hh) * PW + PO + e);
-        if (f != 0.f) {  // the O of empty partials is never written
-          o.x += f * x.x;
-          o.y += f * x.y;
-          o.z += f * x.z;
-          o.w += f * x.w;
-        }
-      }
-      ob[br][0] = o.x;
-      ob[br][1] = o.y;
-      ob[br][2] = o.z;
-      ob[br][3] = o.w;
-    }
-    const int hq = g * G + hh;
-    const int64_t off = (b * dm.Hq + hq) * (int64_t)HD + e;
-    if (text) {  // dense attention, ungated
-      bf16x4 v4;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) v4[c] = (bf16)ob[0][c];
-      if (out) *(bf16x4*)(out + off) = v4;
-      continue;
-    }
-    const float4 oc4 = *(const float4*)(ocmp32 + (int64_t)unit * G * HD + 4 * i);
-    const float oc[4] = {oc4.x, oc4.y, oc4.z, oc4.w};
-    const float* gg = gates + (b * dm.Hq + hq) * 3;
-    bf16x4 vc, vs, vw, vo;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      vc[c] = (bf16)oc[c];
-      vs[c] = (bf16)ob[0][c];
-      vw[c] = (bf16)ob[1][c];
-      vo[c] = (bf16)(gg[0] * oc[c] + gg[1] * ob[0][c] + gg[2] * ob[1][c]);
-    }
-    if (o_cmp) *(bf16x4*)(o_cmp + off) = vc;
-    if (o_slc) *(bf16x4*)(o_slc + off) = vs;
-    if (o_swa) *(bf16x4*)(o_swa + off) = vw;
-    if (out) *(bf16x4*)(out + off) = vo;
+  const int hq = g * G + hh;
+  const int64_t off = (b * dm.Hq + hq) * (int64_t)HD + e;
+  if (text) {  // dense attention, ungated
+    if (out) out[off] = (bf16)ob[0];
+    return;
   }
+  const float* pc = part + (int64_t)unit * nsplit * G * PSTRIDE + hh * PSTRIDE + 2 + e;
+  const float* fu = facw + ((int64_t)unit * G + hh) * nsplit;
+  float oc = 0.f;
+#pragma unroll 16
+  for (int s = 0; s < nsplit; ++s) oc += fu[s] * pc[(int64_t)s * G * PSTRIDE];
+  const float* gg = gates + (b * dm.Hq + hq) * 3;
+  if (o_cmp) o_cmp[off] = (bf16)oc;
+  if (o_slc) o_slc[off] = (bf16)ob[0];
+  if (o_swa) o_swa[off] = (bf16)ob[1];
+  if (out) out[off] = (bf16)(gg[0] * oc + gg[1] * ob[0] + gg[2] * ob[1]);
 }
 
 // ---------------------------------------------------------------------------
@@ -843,7 +809,7 @@ size_t decode_workspace(const Dims& dm) {
   const size_t units = (size_t)dm.B * dm.Hkv;
   const size_t wgs = dwgs(dm);
   return drup(units * dsplits(dm) * dm.G * PSTRIDE * 4) + drup(units * wgs * 2 * dm.G * (HD + 4) * 4) +
-         drup(units * dm.G * HD * 4);
+         drup(units * dm.G * dsplits(dm) * 4);
 }
 
 // kh/vh: compressed cache (bf16), kl/vl: low parts or NULL.  Text rows take dense causal
@@ -861,7 +827,7 @@ hipError_t launch_decode_fast(const Dims& dm, const DecVar& dv, const void* q, c
   const int wgs = dwgs(dm);
   float* part3 = (float*)p;
   p += drup((size_t)units * wgs * 2 * dm.G * (HD + 4) * 4);
-  float* ocmp32 = (float*)p;
+  float* facw = (float*)p;
   if (kl)
     dcmp_split_kernel<true><<<dim3(units * ns), dim3(256), 0, s>>>((const bf16*)q, (const bf16*)kh, (const bf16*)kl,
                                                                    (const bf16*)vh, (const bf16*)vl, vid, part,
@@ -876,11 +842,12 @@ hipError_t launch_decode_fast(const Dims& dm, const DecVar& dv, const void* q, c
   e = hipFuncSetAttribute((const void*)dsel_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   dsel_kernel<<<dim3(units * wgs), dim3(256), shm, s>>>(
-      (const bf16*)q, (const bf16*)k, (const bf16*)v, part, vid, lse, idx, imp, part3, ocmp32, dm, dv, ns, wgs);
+      (const bf16*)q, (const bf16*)k, (const bf16*)v, part, vid, lse, idx, imp, part3, facw, dm, dv, ns, wgs);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dmerge_kernel<<<dim3(units), dim3(256), (size_t)wgs * 2 * dm.G * 4, s>>>(
-      part3, ocmp32, vid, gates, (bf16*)out, (bf16*)o_cmp, (bf16*)o_slc, (bf16*)o_swa, dm, wgs);
+  const int mq = (int)((dm.G * HD + 255) / 256);
+  dmerge_kernel<<<dim3(units * mq), dim3(256), 0, s>>>(part3, part, facw, vid, gates, (bf16*)out, (bf16*)o_cmp,
+                                                        (bf16*)o_slc, (bf16*)o_swa, dm, wgs, ns, mq);
   return hipGetLastError();
 }
 
