@@ -3,7 +3,8 @@
 // (top168.com digest of VideoNSA, section 一: the selection branch keeps the most important
 // segments).
 //
-// Threshold method: each lane takes up to TK_REG candidates (strided by 64).  The kk-th largest
+// Threshold method: each lane takes up to TK candidates (strided by 64; TK = 4, 8, 16 or 32, the
+// smallest that holds the row's candidates, so short rows load and scan fewer slots).  The kk-th largest
 // of the 64 lane maxima, th, is a lower bound of the kk-th largest candidate (the kk lanes with
 // the largest maxima each hold a value >= th), so the candidates >= th contain the answer.  They
 // are compacted into LDS, one per lane (a wave prefix sum gives each lane its slots), and the
@@ -14,7 +15,7 @@
 #pragma once
 #include "common.hpp"
 
-constexpr int TK_REG = 32;
+constexpr int TK_REG = 32;  // most candidates a lane holds in registers
 
 // (a, ja) ranks before (b, jb)
 __device__ __forceinline__ bool tk_before(float a, int ja, float b, int jb) { return a > b || (a == b && ja < jb); }
@@ -56,9 +57,10 @@ __device__ __forceinline__ uint32_t tk_kth_key(uint32_t key, int kk) {
 
 // x: importance indexed by block (global or LDS).  Free candidates [lo, hi); forced blocks
 // [0, lo) and [hi, nj); kk = places for free candidates (n minus the forced count); out: n
-// entries.  Whole wave, uniform arguments.
-__device__ inline void wave_select(const float* __restrict__ x, int lo, int hi, int nj, int kk, int n,
-                                   TopkScratch* sc, int32_t* __restrict__ out, int lane) {
+// entries.  Whole wave, uniform arguments.  TK: register slots a lane takes (see wave_select).
+template <int TK>
+__device__ inline void wave_select_tk(const float* __restrict__ x, int lo, int hi, int nj, int kk, int n,
+                                      TopkScratch* sc, int32_t* __restrict__ out, int lane) {
   uint64_t chosen = 0;  // lanes whose (sc_v, sc_j) entry is chosen (threshold path)
   int cj = 0;           // this lane's entry index (threshold path)
   int nsel = 0;         // chosen free blocks
@@ -71,16 +73,16 @@ __device__ inline void wave_select(const float* __restrict__ x, int lo, int hi, 
       in_sel = true;
     } else {
       bool done = false;
-      if (nc <= 64 * TK_REG) {
-        float cv[TK_REG];
+      if (nc <= 64 * TK) {
+        float cv[TK];
         float lm = -INFINITY;
 #pragma unroll
-        for (int c = 0; c < TK_REG; ++c) {  // unconditional (clamped) loads, all in flight at once
+        for (int c = 0; c < TK; ++c) {  // unconditional (clamped) loads, all in flight at once
           const int j = lo + lane + 64 * c;
           cv[c] = x[j < hi ? j : hi - 1];
         }
 #pragma unroll
-        for (int c = 0; c < TK_REG; ++c) {
+        for (int c = 0; c < TK; ++c) {
           if (lo + lane + 64 * c >= hi) cv[c] = -INFINITY;
           else lm = fmaxf(lm, cv[c]);
         }
@@ -89,7 +91,7 @@ __device__ inline void wave_select(const float* __restrict__ x, int lo, int hi, 
         // compact the candidates >= th into LDS, one ballot per register slot that has any
         int total = 0;
 #pragma unroll
-        for (int c = 0; c < TK_REG; ++c) {
+        for (int c = 0; c < TK; ++c) {
           const int j = lo + lane + 64 * c;
           const bool take = j < hi && tk_key(cv[c]) >= thk;
           const uint64_t bal = __ballot(take);
@@ -168,6 +170,17 @@ __device__ inline void wave_select(const float* __restrict__ x, int lo, int hi, 
   const int a = lo + nsel;
   if (lane >= a && lane < n) out[lane] = lane - a < nj - hi ? hi + (lane - a) : -1;
   tk_wave_sync();  // the scratch may be reused by the next call
+}
+
+// The selection with the fewest register slots that hold the row's free candidates (the result
+// does not depend on the slot count: lane l always takes candidates lo + l + 64 c).
+__device__ inline void wave_select(const float* __restrict__ x, int lo, int hi, int nj, int kk, int n,
+                                   TopkScratch* sc, int32_t* __restrict__ out, int lane) {
+  const int nc = hi - lo;
+  if (nc <= 64 * 4) wave_select_tk<4>(x, lo, hi, nj, kk, n, sc, out, lane);
+  else if (nc <= 64 * 8) wave_select_tk<8>(x, lo, hi, nj, kk, n, sc, out, lane);
+  else if (nc <= 64 * 16) wave_select_tk<16>(x, lo, hi, nj, kk, n, sc, out, lane);
+  else wave_select_tk<TK_REG>(x, lo, hi, nj, kk, n, sc, out, lane);
 }
 
 // Forced-block bounds of the row at absolute position t: free candidates [*lo, *hi), forced
