@@ -409,6 +409,23 @@ def test_layer_deterministic():
         assert torch.equal(a[key], b[key]), key
 
 
+def test_layer_side_stream_equals_in_order():
+    """The window pass forked onto the library's second stream (the default) and the two passes in
+    order on the caller's stream (as while phase timing is on) give the same bits, text rows
+    included."""
+    wl = _wl(T=3000, lead=128, tail=128)
+    inp = synth.make_inputs(wl, DEV)
+    a = run_layer(wl, inp)
+    nsa.profile_enable(True)
+    try:
+        b = run_layer(wl, inp)
+        torch.cuda.synchronize()
+    finally:
+        nsa.profile_enable(False)
+    for key in ("out", "o_cmp", "o_slc", "o_swa", "idx"):
+        assert torch.equal(a[key], b[key]), key
+
+
 @pytest.mark.parametrize("case", ["internal-compress", "text-row", "early-row", "batch3-mixed"])
 def test_decode_single_row(case, path):
     """One query row per sequence (the split decode kernels), compressed inside the layer."""
