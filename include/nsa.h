@@ -35,8 +35,9 @@
  *    work there and joined back into `stream` before the call's last kernel,
  *    so all of the call's work is ordered after what precedes it on `stream`
  *    and complete before what follows.  The first call of a thread made while
- *    `stream` is being captured into a graph, and every call while phase
- *    timing is on, keeps to `stream` alone.
+ *    `stream` is being captured into a graph, every call while phase timing
+ *    is on, and calls whose `stream` belongs to another device than the
+ *    current one keep to `stream` alone.
  *  - Layouts are row-major and token-major:
  *      q, o_* , out   [B, q_len, Hq, D]      (dtype)
  *      k, v           [B, kv_len, Hkv, D]    (dtype)

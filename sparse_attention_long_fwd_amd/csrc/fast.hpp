@@ -49,8 +49,9 @@ hipError_t launch_sparse_fast(const Dims& dm, const void* q, const void* ks, con
 // fork / join event pair.  The window pass (window branch, dense text rows, the forced local
 // selection partials) reads only q, k, v and the row flags, so it can run there beside the top-n
 // and the selection kernels; only the selection merge reads its outputs.  Created on the first
-// call outside stream capture and kept until the process ends; null when that fails or the first
-// call comes during a capture (the passes then run in order on the caller's stream).
+// call outside stream capture and kept until the process ends; null when that fails, the first
+// call comes during a capture, or the caller's stream belongs to another device than the current
+// one (the passes then run in order on the caller's stream).
 struct SideStream {
   hipStream_t s;
   hipEvent_t fork, join;

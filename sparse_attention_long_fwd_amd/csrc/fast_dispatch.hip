@@ -35,8 +35,11 @@ SideStream* side_stream(hipStream_t caller) {
   };
   constexpr int kMaxDev = 64;
   thread_local Slot tab[kMaxDev];
+  // only for a stream of the current device (the side stream is created there)
   int dev = 0;
+  hipDevice_t sdev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+  if (hipStreamGetDevice(caller, &sdev) != hipSuccess || sdev != dev) return nullptr;
   Slot& sl = tab[dev];
   if (!sl.tried) {
     // no stream or event creation while the caller's stream is being captured
