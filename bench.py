@@ -77,11 +77,13 @@ def parse():
                     help="skip the fixed-budget (top-n, window) performance surface")
     ap.add_argument("--sweep-steps", type=int, default=5, help="timed steps per budget point")
     ap.add_argument("--no-branch-kv", action="store_true", help="skip the per-branch K/V prefill measurement")
+    ap.add_argument("--no-36k", action="store_true", help="skip the 36K prefill measurement")
+    ap.add_argument("--no-sweep-runs", action="store_true",
+                    help="skip the six 1 %%-text budget / gate runs at 128K")
     ap.add_argument("--varlen-only", action="store_true",
                     help="with --no-prefill: only the variable-length paged decode (for profiling)")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the variable-length paged decode measurement")
-    ap.add_argument("--cpu-sample-rows", type=int, default=0, help="oracle row sample (0: auto)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run one elementwise copy of 1 GiB (reference for counter runs)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -277,14 +279,19 @@ def phase_rates(wl, ms):
     return out
 
 
-def prefill(args, wl):
+def prefill(args, wl, steps=None, warmup=None, inp=None):
+    """Time `steps` calls of the layer on `wl` (inputs drawn unless given); the per-phase pass unless
+    --no-kernels.  Returns the timing record and the inputs."""
     import torch
     from sparse_attention_long_fwd_amd import accounting, nsa, synth
 
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     dev = "cuda"
     stream = torch.cuda.current_stream()
-    log("generating %s inputs" % wl.name)
-    inp = synth.make_inputs(wl, dev)
+    if inp is None:
+        log("generating %s inputs" % wl.name)
+        inp = synth.make_inputs(wl, dev)
     q, k, v, g, vid = inp["q"], inp["k"], inp["v"], inp["gates"], inp["is_video"]
     B, Tq, Hq, D = q.shape
     Hkv = k.shape[2]
@@ -298,31 +305,51 @@ def prefill(args, wl):
         nsa.nsa_hybrid_layer_fwd(q, k, v, g, sh, pr, w_k=inp["w_k"], w_v=inp["w_v"], is_video=vid, out=out,
                                  workspace=ws, stream=stream)
 
-    log("warmup %d" % args.warmup)
-    for _ in range(args.warmup):
+    log("%s: warmup %d" % (wl.name, warmup))
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    log("timing %d steps" % args.steps)
+    log("%s: timing %d steps" % (wl.name, steps))
     t0 = time.perf_counter()
     each = []
-    ms = time_calls(step, args.steps, stream, each)
+    ms = time_calls(step, steps, stream, each)
     wall = time.perf_counter() - t0
     fl = accounting.flops(wl)
-    res = dict(ms_per_step=ms, ms_median=float(np.median(each)), ms_min=float(np.min(each)), wall_s=wall,
-               tokens_per_s=wl.q_len * wl.batch / (ms * 1e-3),
-               algo_flops=fl, mfma_util=fl["total"] / (ms * 1e-3) / PEAK_BF16_MFMA)
+    res = dict(workload=wl.name, steps=steps, ms_per_step=ms, ms_median=float(np.median(each)),
+               ms_min=float(np.min(each)), wall_s=wall, tokens_per_s=wl.q_len * wl.batch / (ms * 1e-3),
+               algo_flops=fl, algo_tflops=fl["total"] / (ms * 1e-3) / 1e12,
+               mfma_util=fl["total"] / (ms * 1e-3) / PEAK_BF16_MFMA)
     if not args.no_kernels:
-        log("per-phase timing (%d steps)" % args.steps)
+        log("%s: per-phase timing (%d steps)" % (wl.name, steps))
         nsa.profile_enable(True)
         acc = None
-        for _ in range(args.steps):
+        for _ in range(steps):
             step()
             ph = np.array(nsa.profile_read())
             acc = ph if acc is None else acc + ph
         nsa.profile_enable(False)
-        res["kernels"] = phase_rates(wl, list(acc / args.steps))
+        res["kernels"] = phase_rates(wl, list(acc / steps))
     del ws
     return res, inp
+
+
+def branch_outputs(wl, inp):
+    """One more layer call (untimed) that also returns the branch outputs and the chosen blocks,
+    for the parity statistics of the CPU-baseline leg."""
+    import torch
+    from sparse_attention_long_fwd_amd import nsa
+
+    q, k = inp["q"], inp["k"]
+    B, Tq, Hq, D = q.shape
+    sh = nsa.make_shape(B, Tq, wl.kv_len, wl.q_start, Hq, k.shape[2], D)
+    pr = nsa.make_params(**wl.params())
+    got = dict(o_cmp=torch.empty_like(q), o_slc=torch.empty_like(q), o_swa=torch.empty_like(q),
+               idx=torch.full((B, Tq, k.shape[2], wl.top_n), -1, dtype=torch.int32, device=q.device))
+    got["out"] = nsa.nsa_hybrid_layer_fwd(q, k, inp["v"], inp["gates"], sh, pr, w_k=inp["w_k"], w_v=inp["w_v"],
+                                          is_video=inp["is_video"], o_cmp=got["o_cmp"], o_slc=got["o_slc"],
+                                          o_swa=got["o_swa"], block_idx_out=got["idx"])
+    torch.cuda.synchronize()
+    return got
 
 
 BUDGET = 16 * 64 + 512   # tokens each video row attends in the selection + window branches
@@ -627,35 +654,200 @@ def gate_proj(args, wl):
                 roofline=dict(bound="hbm", achieved=bw / 1e9, peak=PEAK_HBM / 1e9, unit="GB/s", frac=bw / PEAK_HBM))
 
 
-def cpu_baseline(args, wl, inp):
-    """The fp64 oracle on a bounded row sample of the same prefill (rank 0)."""
+def _host(t):
     import torch
+    return (t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy()
+
+
+def cpu_sample_rows(wl, seed):
+    """The oracle's row sample of a prefill: one video row per 64-token frame at a seeded offset
+    inside the frame, every text row, and the first and last 1,024 rows."""
+    T = wl.q_len
+    rng = np.random.default_rng(seed)
+    off = int(rng.integers(0, wl.frame))
+    pos = np.arange(wl.q_start, wl.q_start + T)
+    vid = (pos >= wl.text_lead) & (pos < wl.kv_len - wl.text_tail)
+    rows = set(np.nonzero(~vid)[0].tolist())
+    rows |= set(range(min(1024, T))) | set(range(max(0, T - 1024), T))
+    rows |= set((np.arange(wl.text_lead + off, wl.kv_len - wl.text_tail, wl.frame) - wl.q_start).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < T), dtype=np.int64)
+
+
+def cpu_baseline_parity(wl, inp, got, rows, ref):
+    """Parity of the GPU's layer outputs against the oracle's on the sampled rows (CPU-baseline leg):
+    max-abs error per branch and of the output, and the selection statistics of the index rule --
+    chosen blocks identical wherever the oracle's gap exceeds 1e-3; where they differ (undecided
+    rows) the selection and final outputs are compared against the oracle run on the GPU's set."""
     import oracle
 
-    def host(t):
-        return (t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy()
+    import torch
 
-    k, v = host(inp["k"][0]), host(inp["v"][0])
-    q = inp["q"][0]
-    vid = inp["is_video"][0].cpu().numpy().astype(bool)
-    T = wl.q_len
-    n_rows = args.cpu_sample_rows or 4096
-    vr = np.nonzero(vid)[0]
-    tr = np.nonzero(~vid)[0]
-    rng = np.random.default_rng(wl.index)
-    stride = max(1, len(vr) // n_rows)
-    rows = vr[int(rng.integers(0, stride))::stride][:n_rows]
-    trows = tr[::max(1, len(tr) // 4)][:4] if tr.size else tr
-    sample = np.concatenate([rows, trows])
+    q = _host(inp["q"][0])
+    k, v = _host(inp["k"][0]), _host(inp["v"][0])
+    vid = _host(inp["is_video"][0])[rows].astype(bool)
+    sel = torch.from_numpy(rows).to(inp["q"].device)
+    # the GPU's outputs on the sampled rows only (gathered on the device)
+    gr = {key: _host(t[0].index_select(0, sel)) for key, t in got.items()}
+    gidx = gr["idx"]
+    st = dict(rows=int(len(rows)), video_rows=int(vid.sum()))
+    err = {}
+    if vid.any():
+        same = np.all(gidx[vid] == ref["idx"][vid], axis=-1)
+        dec = ref["gap"][vid] > 1e-3
+        st.update(row_groups=int(same.size), decided=int(dec.sum()), decided_frac=float(dec.mean()),
+                  idx_equal_frac=float(same.mean()), decided_mismatches=int((dec & ~same).sum()),
+                  substituted_rows=int((~same.all(axis=1)).sum()))
+        ref_slc, ref_out = ref["o_slc"][vid].copy(), ref["out"][vid].copy()
+        sub = np.nonzero(~same.all(axis=1))[0]
+        if sub.size:
+            vr = rows[vid][sub]
+            o_sub, _ = oracle.sparse_rows(q[vr], vr + wl.q_start, k, v, gidx[vid][sub], wl.sel_block, wl.window,
+                                          oracle.default_scale(wl.head_dim), swa=False)
+            gg = _host(inp["gates"][0])[vr].astype(np.float64)
+            ref_slc[sub] = o_sub
+            ref_out[sub] = (gg[..., 0:1] * ref["o_cmp"][vid][sub] + gg[..., 1:2] * o_sub +
+                            gg[..., 2:3] * ref["o_swa"][vid][sub])
+        for name, r in (("cmp", ref["o_cmp"][vid]), ("swa", ref["o_swa"][vid]), ("slc", ref_slc)):
+            err[name] = float(np.max(np.abs(gr["o_" + name][vid] - r)))
+        err["out"] = float(np.max(np.abs(gr["out"][vid] - ref_out)))
+    if (~vid).any():
+        err["text"] = float(np.max(np.abs(gr["out"][~vid] - ref["out"][~vid])))
+    st["max_abs"] = err
+    tol = 2e-2 if wl.dtype == "bf16" else 1e-4
+    st["tolerance"] = tol
+    st["pass"] = bool(all(x <= tol for x in err.values()) and st.get("decided_mismatches", 0) == 0)
+    return st
+
+
+def cpu_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(args, wl, inp, got):
+    """The fp64 oracle on the stated row sample of the same prefill (rank 0), timed on the host's
+    cores; the same run checks the GPU's outputs on those rows against it."""
+    import oracle
+    from sparse_attention_long_fwd_amd import accounting
+
+    rows = cpu_sample_rows(wl, wl.index)
+    q = _host(inp["q"][0])
+    k, v = _host(inp["k"][0]), _host(inp["v"][0])
     oracle.build()
     t0 = time.perf_counter()
-    oracle.layer(host(q), k, v, host(inp["w_k"]), host(inp["w_v"]), host(inp["gates"][0]), vid.astype(np.uint8),
-                 wl.params(), rows=sample)
+    ref = oracle.layer(q, k, v, _host(inp["w_k"]), _host(inp["w_v"]), _host(inp["gates"][0]),
+                       _host(inp["is_video"][0]), wl.params(), q_start=wl.q_start, rows=rows)
     dt = time.perf_counter() - t0
-    return dict(value=len(sample) / dt, unit="tokens/s (query rows per second over the sample)",
-                cores=oracle.num_threads(), kind="oracle", seconds=dt,
-                sample="%d video rows (every %d-th, seeded offset) + %d text rows of the %d-row %s prefill; "
-                       "compression of the whole sequence included" % (len(rows), stride, len(trows), T, wl.name))
+    # extrapolation to the whole layer by the algorithmic work of the rows (compression included)
+    pos = np.arange(wl.q_start, wl.q_start + wl.q_len)
+    vid = (pos >= wl.text_lead) & (pos < wl.kv_len - wl.text_tail)
+
+    def work(p, v_):
+        c = accounting.cmp_visible(p, wl.cmp_block, wl.cmp_stride, wl.kv_len)
+        sel = accounting.slc_keys(p, wl.sel_block, wl.top_n)
+        swa = accounting.swa_keys(p, wl.window)
+        return float(np.where(v_, c + sel + swa, p + 1).sum())
+
+    frac = work(pos[rows], vid[rows]) / work(pos, vid)
+    model, visible = cpu_info()
+    parity = cpu_baseline_parity(wl, inp, got, rows, ref)
+    return dict(value=len(rows) / dt, unit="query rows/s over the sample (extrapolated to the layer: see "
+                "extrapolated_layer_s)", cores=oracle.num_threads(), cores_visible=visible, cpu_model=model,
+                kind="oracle", seconds=dt, extrapolated=True, extrapolated_layer_s=dt / frac,
+                extrapolated_tokens_per_s=wl.q_len / (dt / frac),
+                sample="%d rows of the %d-row %s prefill: one video row per 64-token frame at a seeded offset, "
+                       "all %d text rows, the first and last 1024 rows (%.2f %% of the layer's attended pairs); "
+                       "compression of the whole sequence included" % (
+                           len(rows), wl.q_len, wl.name, int((~vid).sum()), 100 * frac),
+                parity=parity)
+
+
+def sampled_rows(wl, n_video, seed, text=4, edge=16):
+    """A small seeded row sample for the parity of the secondary runs: evenly spaced video rows at a
+    seeded offset, a few text rows from each end, the first and last rows."""
+    T = wl.q_len
+    rng = np.random.default_rng(seed)
+    stride = max(1, (T - wl.text_lead - wl.text_tail) // n_video)
+    off = int(rng.integers(0, stride))
+    rows = set(range(wl.text_lead + off, T - wl.text_tail, stride))
+    rows |= set(range(edge)) | set(range(T - edge, T))
+    rows |= set(range(wl.text_lead, wl.text_lead + text // 2)) | set(range(T - wl.text_tail - text // 2,
+                                                                            T - wl.text_tail))
+    if wl.text_lead:
+        rows |= set(range(wl.text_lead - text // 2, wl.text_lead))
+    if wl.text_tail:
+        rows |= set(range(T - wl.text_tail, T - wl.text_tail + text // 2))
+    return np.array(sorted(r for r in rows if 0 <= r < T), dtype=np.int64)
+
+
+def cpu_baseline_run_parity(wl, inp, n_video, seed):
+    """CPU-baseline leg of a secondary prefill run: the oracle on a small row sample and the parity
+    statistics of the GPU's outputs there."""
+    import oracle
+
+    got = branch_outputs(wl, inp)
+    rows = sampled_rows(wl, n_video, seed)
+    ref = oracle.layer(_host(inp["q"][0]), _host(inp["k"][0]), _host(inp["v"][0]), _host(inp["w_k"]),
+                       _host(inp["w_v"]), _host(inp["gates"][0]), _host(inp["is_video"][0]), wl.params(),
+                       q_start=wl.q_start, rows=rows)
+    st = cpu_baseline_parity(wl, inp, got, rows, ref)
+    del got
+    return st
+
+
+def prefill_36k(args):
+    """The 36K-token Qwen2.5-VL-7B-shaped prefill (560 frames + 512 text tokens): throughput and
+    algorithmic MFMA rate, and its parity on sampled rows (CPU-baseline leg)."""
+    import torch
+    from sparse_attention_long_fwd_amd import synth
+
+    wl = synth.WORKLOADS["36k"]
+    res, inp = prefill(args, wl, steps=max(10, args.steps), warmup=2)
+    if not args.no_cpu_baseline:
+        res["parity"] = cpu_baseline_run_parity(wl, inp, 256, wl.index)
+    del inp
+    torch.cuda.empty_cache()
+    return res
+
+
+def sweep_runs(args):
+    """The six 128K runs with 1 % text (640 + 2,028 frames x 64 + 640 tokens): budget (top-n, window)
+    in {(16, 512), (8, 256)} x gates {sigmoid(N(0,1)), CMP-dominant, SLC-dominant}; tokens/s and
+    algorithmic TFLOP/s each, and parity on sampled rows (CPU-baseline leg)."""
+    import torch
+    from sparse_attention_long_fwd_amd import synth
+
+    base = synth.WORKLOADS["sweep"]
+    inp = synth.make_inputs(base, "cuda")  # gates sigmoid(N(0,1)); q, k, v are the same in every run
+    g_sig = inp["gates"]
+    out = []
+    for i, (n, w, gates) in enumerate(synth.SWEEP_VARIANTS):
+        wl = base.with_(top_n=n, window=w, gates=gates)
+        if gates == "sigmoid":
+            inp["gates"] = g_sig
+        else:  # the fixed regime of every (row, head), as make_inputs draws it
+            inp["gates"] = torch.tensor(synth.GATE_REGIMES[gates], dtype=torch.float32,
+                                        device="cuda").expand_as(g_sig).contiguous()
+        res, _ = prefill(args, wl, steps=args.sweep_steps, warmup=2, inp=inp)
+        rec = dict(top_n=n, window=w, gates=gates, ms_per_step=res["ms_per_step"], tokens_per_s=res["tokens_per_s"],
+                   algo_tflops=res["algo_tflops"], mfma_util=res["mfma_util"])
+        if "kernels" in res:
+            rec["phase_ms"] = {k: round(v["ms"], 4) for k, v in res["kernels"].items()}
+        if not args.no_cpu_baseline:
+            rec["parity"] = cpu_baseline_run_parity(wl, inp, 96, i)
+        log("sweep n=%d w=%d gates=%s: %.2f ms" % (n, w, gates, res["ms_per_step"]))
+        out.append(rec)
+    del inp
+    torch.cuda.empty_cache()
+    return dict(workload=base.name, text_tokens=base.text_lead + base.text_tail, runs=out)
 
 
 def main():
@@ -689,6 +881,7 @@ def main():
         print(json.dumps(res))
         return
     res, inp = prefill(args, wl)
+    got = None if args.no_cpu_baseline else branch_outputs(wl, inp)
     ker = res.get("kernels", {})
     roofline = None
     if ker:
@@ -711,10 +904,18 @@ def main():
         bkv = branch_kv(args, wl, inp)
     cpu = None
     if not args.no_cpu_baseline:
-        log("oracle timing")
-        cpu = cpu_baseline(args, wl, inp)
-    del inp
+        log("oracle timing and parity on the sampled rows")
+        cpu = cpu_baseline(args, wl, inp, got)
+    del inp, got
     torch.cuda.empty_cache()
+    p36 = None
+    if not args.no_36k and wl.name == synth.WORKLOADS["128k"].name:
+        log("36K prefill")
+        p36 = prefill_36k(args)
+    sw5 = None
+    if not args.no_sweep_runs and wl.name == synth.WORKLOADS["128k"].name:
+        log("budget / gate runs (1 % text)")
+        sw5 = sweep_runs(args)
     gp = None
     if not args.no_gate_proj:
         log("gate projection")
@@ -760,6 +961,8 @@ def main():
         "backward": bwd,
         "budget_sweep": sweep,
         "branch_kv": bkv,
+        "prefill_36k": p36,
+        "budget_gate_runs": sw5,
         "cpu_baseline": cpu,
         "counters": kernel_counters(),
     }

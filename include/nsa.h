@@ -163,7 +163,8 @@ int32_t nsa_topk_blocks(const float* importance, const nsa_shape* shape, const n
  *       ungated ([A] abstract, [D]).
  * o_slc, o_swa, out may each be NULL (at least one given).  out needs o_cmp
  * and gates.  block_idx must hold valid sets (entries < Ns, ascending, the
- * block of t among them) for every video row.
+ * block of t among them, -1 for unused places) for every video row; an entry
+ * after the block of t holds no key u <= t and contributes nothing.
  * workspace: device scratch of nsa_sparse_attn_workspace_size() bytes (may
  * be NULL when that size is 0).
  */

@@ -34,6 +34,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "nsa_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libnsa_oracle.so")
+# NSA_ORACLE_LIB_PATH loads another, prebuilt copy of this oracle (the host-sanitizer test's
+# instrumented build) instead of building and loading the default one.
+_LIB_OVERRIDE = os.environ.get("NSA_ORACLE_LIB_PATH")
 _lib = None
 
 _i64 = ctypes.c_int64
@@ -54,8 +57,11 @@ def build(force: bool = False) -> str:
 def lib():
     global _lib
     if _lib is None:
-        build()
-        L = ctypes.CDLL(_LIB_PATH)
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            build()
+            L = ctypes.CDLL(_LIB_PATH)
         L.oracle_num_cmp_blocks.restype = _i64
         L.oracle_num_cmp_blocks.argtypes = [_i64, _i64, _i64]
         L.oracle_num_sel_blocks.restype = _i64

@@ -442,17 +442,25 @@ int32_t layer_fwd(const void* q, const BranchKV& kv, const void* k_cmp_in, const
   if (side) {
     hipError_t e = launch_sparse_window(dm, q, kv.ks, kv.vs, kv.kw, kv.vw, is_video, out, o_swa, sparse_ws_ptr, s,
                                         side, true);
-    if (e != hipSuccess) return hip_fail(e, "window kernel");
+    const char* where = "window kernel";
+    if (e == hipSuccess) {
+      e = launch_topk(dm, imp, is_video, idx, s);
+      where = "top-n kernel";
+    }
+    if (e == hipSuccess) {
+      e = launch_sparse_select(dm, q, kv.ks, kv.vs, kv.kw, kv.vw, idx, is_video, ocmp32, true, gates, out, o_slc,
+                               sparse_ws_ptr, s, side, true);
+      where = "selection kernels";
+    }
+    if (e != hipSuccess) {
+      (void)join_side_stream(side, s);  // the caller's stream still waits for the forked window pass
+      return hip_fail(e, where);
+    }
+    return NSA_OK;
   }
   hipError_t e = launch_topk(dm, imp, is_video, idx, s);
   if (e != hipSuccess) return hip_fail(e, "top-n kernel");
   prof_mark(s);
-  if (side) {
-    e = launch_sparse_select(dm, q, kv.ks, kv.vs, kv.kw, kv.vw, idx, is_video, ocmp32, true, gates, out, o_slc,
-                             sparse_ws_ptr, s, side, true);
-    if (e != hipSuccess) return hip_fail(e, "selection kernels");
-    return NSA_OK;
-  }
   if (fast) {
     st = run_sparse(dtype, dm, q, kv, idx, is_video, ocmp32, true, gates, out, o_slc, o_swa, sparse_ws_ptr, s,
                     true);
@@ -583,6 +591,8 @@ int32_t nsa_compress_append(const void* k, const void* v, int32_t dtype, int64_t
   dm.d = cmp_stride;
   dm.Nc = ncmp(kv_len, cmp_block, cmp_stride);
   if (dm.Nc == 0 || batch == 0 || n_new == 0) return NSA_OK;
+  // no sequence holds more than kv_len tokens, so no block completes earlier than that
+  if ((int64_t)n_new > kv_len) n_new = (int32_t)kv_len;
   if (!k || !v || !w_k || !w_v || !k_cmp || !v_cmp) return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_cmp) || !aligned16(v_cmp))
     return fail(NSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");

@@ -54,6 +54,17 @@ constexpr int TILE = CK * HD;  // bf16 elements of one staged array
 // Scores always use both parts of K: the block importance that decides the top-n moves by
 // up to a few 1e-3 with bf16 Kc.
 constexpr int64_t kVloBelow = 256;
+// Row tiles whose first row sees at least this many compressed blocks form the log-sum-exp of
+// the first sweep from the keys' bf16 high parts alone (no fp8 remainder product, no low parts
+// staged in that sweep); the second sweep, whose probabilities make the importance, keeps both
+// parts.  A normaliser error dL scales all of a head's probabilities by exp(-dL), so it moves
+// each importance by about imp * dL, and from a few hundred blocks on dL (a probability-weighted
+// mean of the score errors) and the importances are both small: in an fp64 emulation on the 128K
+// and 36K workloads (random rows of every group) the importance moves by at most a few 1e-5 from
+// here on, against the 5e-4 that keeps every selection whose gap exceeds 1e-3 unchanged.  With
+// the high parts in both sweeps it moved by up to 3.8e-4 at 12K tokens, which is why the second
+// sweep keeps the remainder.
+constexpr int64_t kLseHiFrom = 512;
 }  // namespace
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -114,14 +125,15 @@ struct CmpLds {
 // SPLIT: keys as bf16 high parts (kh) + fp8 low parts (kl8) with scales (ksc).
 // ipart_bufs: 2 = importance partials double-buffered by tile parity, 1 = one buffer (one more
 // barrier a tile; used where two do not fit in LDS).
-template <bool SPLIT, bool VT>
+// LSE_HI: the first sweep uses the keys' high parts only (split keys, long rows; see kLseHiFrom).
+template <bool SPLIT, bool VT, bool LSE_HI>
 __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kh,
                                                        const uint8_t* __restrict__ kl8,
                                                        const uint8_t* __restrict__ ksc, const bf16* __restrict__ vh,
                                                        const bf16* __restrict__ vl, const uint8_t* __restrict__ vid,
                                                        bf16* __restrict__ o_bf, float* __restrict__ o_f32,
                                                        float* __restrict__ lse, float* __restrict__ imp, Dims dm,
-                                                       int ntq, int ipart_bufs) {
+                                                       int tile_lo, int ntiles, int ipart_bufs) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   using LY = CmpLds<SPLIT>;
   float* ipart0 = (float*)(smem + 2 * LY::BUF);  // [ipart_bufs][G][CQ][IPS]
@@ -133,10 +145,10 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
   const int w = tid >> 6, l = tid & 63, hl = l >> 5, n = l & 31;
   const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index as a uniform value
   int unit, rank;
-  if (!xcd_remap(blockIdx.x, (int)(dm.B * dm.Hkv), ntq, &unit, &rank)) return;
+  if (!xcd_remap(blockIdx.x, (int)(dm.B * dm.Hkv), ntiles, &unit, &rank)) return;
   const int64_t b = unit / dm.Hkv;
   const int g = unit % dm.Hkv;
-  const int64_t rt0 = (int64_t)(ntq - 1 - rank) * CQ;  // heaviest tiles first
+  const int64_t rt0 = (int64_t)(tile_lo + ntiles - 1 - rank) * CQ;  // row tiles [tile_lo, +ntiles), heaviest first
 
   if (tid == 0) s_any = 0;
   __syncthreads();
@@ -226,9 +238,9 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
   };
   // fp8 low parts: 8 instructions of 64 lanes x 16 bytes (rows 8 ins .. 8 ins + 7, the swz8
   // layout), then the 64 keys' scale words (one 4-byte load a lane) from the last wave
-  auto stage_k = [&](int tile, int bufi) {
+  auto stage_k = [&](int tile, int bufi, auto lo_c) {
     stage64(khs_of(bufi), kh + base, tile);
-    if constexpr (SPLIT) {
+    if constexpr (decltype(lo_c)::value) {
       const int64_t left64 = dm.Nc - (int64_t)tile * CK;
       const int left = left64 < CK ? (int)left64 : CK;
       const int64_t key0 = (b * dm.Nc + (int64_t)tile * CK) * dm.Hkv + g;  // (key, head) row index
@@ -262,7 +274,7 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
     }
   };
   // S^T blocks 0 and 1 (32 keys each) of the staged tile; the two accumulation chains alternate
-  auto scores2 = [&](int bufi, f32x16& s0, f32x16& s1) {
+  auto scores2 = [&](int bufi, f32x16& s0, f32x16& s1, auto lo_c) {
     s0 = f32x16{};
     s1 = f32x16{};
     const bf16* khs = khs_of(bufi);
@@ -272,7 +284,7 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
       s0 = mfma32(lds_read8(khs + off0), qf[ks], s0);
       s1 = mfma32(lds_read8(khs + off1), qf[ks], s1);
     }
-    if constexpr (SPLIT) {
+    if constexpr (decltype(lo_c)::value) {
       const unsigned char* lo = lds_at(bufi, LY::KL);
       const int* sc = (const int*)lds_at(bufi, LY::KS);
       // scale bytes 2c + hl of the lane's key row, moved so byte 2c belongs to this lane half
@@ -300,6 +312,9 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
   // tiles whose keys every row of the workgroup sees need no mask
   auto full = [&](int tile) { return (tile + 1) * CK <= nvmin; };
 
+  // keys' low parts: in the first sweep unless LSE_HI, always in the second (split keys)
+  constexpr std::integral_constant<bool, SPLIT && !LSE_HI> lo1{};
+  constexpr std::integral_constant<bool, SPLIT> lo2{};
   // ---- sweep 1: log-sum-exp per (row, head) column.  mr: running maximum of the raw scores,
   // lsum: sum of 2^((s - mr) c2).  The scores of tile i are formed (MFMA) while the exponentials
   // of tile i - 1 run (VALU).
@@ -325,7 +340,7 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
   };
   const int nt1 = (nvmax + CK - 1) / CK;
   if (nt1 > 0) {
-    stage_k(0, 0);
+    stage_k(0, 0, lo1);
     wait_loads();
   }
   __syncthreads();
@@ -337,15 +352,15 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
     f32x16 p0, p1;  // formed scores not yet summed: those of tile t - 1
     int t = 0;
     if (nt1 > 0) {
-      if (nt1 > 1) stage_k(1, 1);
-      scores2(0, p0, p1);
+      if (nt1 > 1) stage_k(1, 1, lo1);
+      scores2(0, p0, p1, lo1);
       wait_loads();
       __syncthreads();
       t = 1;
       for (; t < nt1 && t <= nfull; ++t) {
-        if (t + 1 < nt1) stage_k(t + 1, (t + 1) & 1);
+        if (t + 1 < nt1) stage_k(t + 1, (t + 1) & 1, lo1);
         f32x16 s0, s1;
-        scores2(t & 1, s0, s1);
+        scores2(t & 1, s0, s1, lo1);
         lse_block(p0, t - 1, 0, false);
         lse_block(p1, t - 1, 1, false);
         SG(SG_DSR, 8);
@@ -368,8 +383,8 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
       lse_block(p0, t - 1, 0, !full(t - 1));
       lse_block(p1, t - 1, 1, !full(t - 1));
       for (; t < nt1; ++t) {
-        if (t + 1 < nt1) stage_k(t + 1, (t + 1) & 1);
-        scores2(t & 1, p0, p1);
+        if (t + 1 < nt1) stage_k(t + 1, (t + 1) & 1, lo1);
+        scores2(t & 1, p0, p1, lo1);
         lse_block(p0, t, 0, !full(t));
         lse_block(p1, t, 1, !full(t));
         wait_loads();
@@ -470,16 +485,16 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
   const int nt2 = nvmax > 0 ? nvmax / CK + 1 : 0;
   f32x16 s0, s1;
   if (nt2 > 0) {
-    stage_k(0, 0);
+    stage_k(0, 0, lo2);
     stage_v(0, 0);
     wait_loads();
   }
   __syncthreads();
-  if (nt2 > 0) scores2(0, s0, s1);
+  if (nt2 > 0) scores2(0, s0, s1, lo2);
   for (int tile = 0; tile < nt2; ++tile) {
     const int bufi = tile & 1;
     if (tile + 1 < nt2) {
-      stage_k(tile + 1, bufi ^ 1);
+      stage_k(tile + 1, bufi ^ 1, lo2);
       stage_v(tile + 1, bufi ^ 1);
     }
     float* ipb = ipart0 + (ipart_bufs == 2 ? bufi : 0) * G * CQ * IPS;
@@ -488,7 +503,7 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
     pv_block(s1, bufi, tile, 1, ipb, m);
     wait_loads();
     __syncthreads();
-    if (tile + 1 < nt2) scores2(bufi ^ 1, s0, s1);
+    if (tile + 1 < nt2) scores2(bufi ^ 1, s0, s1, lo2);
     // sum the group's heads in a fixed order; write the tile's 16 selection blocks
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
@@ -541,6 +556,12 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
   }
 }
 
+// Compressed blocks visible from absolute position t (host side of cmp_visible).
+static int64_t cmp_host_visible(int64_t t, const Dims& dm) {
+  const int64_t v = (t + 1 >= dm.l) ? (t + 1 - dm.l) / dm.d + 1 : 0;
+  return v < dm.Nc ? v : dm.Nc;
+}
+
 // Dynamic LDS: the staged K / V buffers, then 1 or 2 buffers of importance partials (2 when
 // they fit next to the static LDS of the kernel).
 static int cmp_ipart_bufs(const Dims& dm, bool split, size_t* bytes) {
@@ -557,25 +578,35 @@ hipError_t launch_cmp_fast(const Dims& dm, const void* q, const void* kh, const 
   if (dm.Tq <= 0 || dm.B <= 0) return hipSuccess;
   const int ntq = (int)((dm.Tq + CQ - 1) / CQ);
   const int units = (int)(dm.B * dm.Hkv);
-  dim3 grid(xcd_grid(units, ntq)), block(dm.G * 64);
   const bool split = kl8 != nullptr;
   if (split && !ksc) return hipErrorInvalidValue;
-  size_t shm;
-  const int bufs = cmp_ipart_bufs(dm, split, &shm);
   // the MFMA layer path always brings split parts with V^T tiles; standalone calls bring neither
   if (split != vt) return hipErrorInvalidValue;
-  const void* fn = split ? (const void*)cmp_fast_kernel<true, true> : (const void*)cmp_fast_kernel<false, false>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-  if (e != hipSuccess) return e;
-  if (split)
-    cmp_fast_kernel<true, true><<<grid, block, shm, s>>>((const bf16*)q, (const bf16*)kh, (const uint8_t*)kl8,
-                                                         (const uint8_t*)ksc, (const bf16*)vh, (const bf16*)vl, vid,
-                                                         (bf16*)o, o32, lse, imp, dm, ntq, bufs);
-  else
-    cmp_fast_kernel<false, false><<<grid, block, shm, s>>>((const bf16*)q, (const bf16*)kh, nullptr, nullptr,
-                                                           (const bf16*)vh, nullptr, vid, (bf16*)o, o32, lse, imp,
-                                                           dm, ntq, bufs);
-  return hipGetLastError();
+  // One launch of a kernel variant over a contiguous range of row tiles [lo, lo + n).
+  auto launch = [&](const void* fn, bool sp, int lo, int n, auto kernel) -> hipError_t {
+    if (n <= 0) return hipSuccess;
+    size_t shm;
+    const int bufs = cmp_ipart_bufs(dm, sp, &shm);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    kernel<<<dim3(xcd_grid(units, n)), dim3(dm.G * 64), shm, s>>>(
+        (const bf16*)q, (const bf16*)kh, (const uint8_t*)kl8, (const uint8_t*)ksc, (const bf16*)vh,
+        (const bf16*)vl, vid, (bf16*)o, o32, lse, imp, dm, lo, n, bufs);
+    return hipGetLastError();
+  };
+  if (!split) {
+    auto* k = cmp_fast_kernel<false, false, false>;
+    return launch((const void*)k, false, 0, ntq, k);
+  }
+  // split parts: row tiles whose first row sees >= kLseHiFrom blocks take the high parts alone in
+  // the first sweep; they are the heavier launch and go first
+  int lo = ntq;
+  while (lo > 0 && cmp_host_visible(dm.q0 + (int64_t)(lo - 1) * CQ, dm) >= kLseHiFrom) --lo;
+  auto* kl = cmp_fast_kernel<true, true, true>;
+  auto* ks = cmp_fast_kernel<true, true, false>;
+  hipError_t e = launch((const void*)kl, true, lo, ntq - lo, kl);
+  if (e == hipSuccess) e = launch((const void*)ks, true, 0, lo, ks);
+  return e;
 }
 
 // Compressed values as V^T tiles (high and low bf16 parts of the fp32 sum), one workgroup per

@@ -64,6 +64,9 @@ SideStream* side_stream(hipStream_t caller);
 hipError_t launch_sparse_window(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
                                 const void* vw, const uint8_t* vid, void* out, void* o_swa, void* ws, hipStream_t s,
                                 const SideStream* side, bool forced_local);
+// Make s wait for the window pass forked onto side (no-op for a null side); every error return after
+// a fork calls it, so no work of the call is left running unordered beside the caller's stream.
+hipError_t join_side_stream(const SideStream* side, hipStream_t s);
 hipError_t launch_sparse_select(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
                                 const void* vw, const int32_t* idx, const uint8_t* vid, const void* o_cmp,
                                 bool ocmp_f32, const float* gates, void* out, void* o_slc, void* ws, hipStream_t s,

@@ -68,10 +68,18 @@ hipError_t launch_sparse_window(const Dims& dm, const void* q, const void* ks, c
     if (e != hipSuccess) return e;
     sw = side->s;
   }
-  // window branch (fp32 for the combine, bf16 copy if asked) and dense text rows
+  // window branch (fp32 for the combine, bf16 copy if asked) and dense text rows; the join event
+  // is recorded even when the launch failed, so that the caller can always rejoin the side stream
   hipError_t e = launch_flash_fast(dm, q, kw, vw, vid, swa32, o_swa, out, fws, sw, lml, lo);
-  if (e == hipSuccess && side) e = hipEventRecord(side->join, sw);
+  if (side) {
+    const hipError_t ej = hipEventRecord(side->join, sw);
+    if (e == hipSuccess) e = ej;
+  }
   return e;
+}
+
+hipError_t join_side_stream(const SideStream* side, hipStream_t s) {
+  return side ? hipStreamWaitEvent(s, side->join, 0) : hipSuccess;
 }
 
 hipError_t launch_sparse_select(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
@@ -92,8 +100,12 @@ hipError_t launch_sparse_fast(const Dims& dm, const void* q, const void* ks, con
                               bool forced_local, bool concurrent) {
   const SideStream* side = concurrent ? side_stream(s) : nullptr;
   hipError_t e = launch_sparse_window(dm, q, ks, vs, kw, vw, vid, out, o_swa, ws, s, side, forced_local);
-  if (e != hipSuccess) return e;
-  if (mark && !side) mark(s);
-  return launch_sparse_select(dm, q, ks, vs, kw, vw, idx, vid, o_cmp, ocmp_f32, gates, out, o_slc, ws, s, side,
-                              forced_local);
+  if (e == hipSuccess) {
+    if (mark && !side) mark(s);
+    e = launch_sparse_select(dm, q, ks, vs, kw, vw, idx, vid, o_cmp, ocmp_f32, gates, out, o_slc, ws, s, side,
+                             forced_local);
+  }
+  // on failure the caller's stream still waits for the window pass (a no-op once the merge did)
+  if (e != hipSuccess) (void)join_side_stream(side, s);
+  return e;
 }

@@ -63,10 +63,13 @@ __global__ void __launch_bounds__(256) slc_zero_kernel(int* __restrict__ p, int6
   if (i < n) p[i] = 0;
 }
 
-// A pair (row, slot) is left to the window pass when that pass forms the row's forced local
-// blocks (local_fused): blocks jt - n_local + 1 .. jt of the row's own block jt.
+// A pair (row, slot) takes part when its block holds a key at or before the row (blocks after
+// the row's own block jt, which a caller's set may list, contribute no key, and every such id
+// would index past the block tables), and it is left to the window pass when that pass forms the
+// row's forced local blocks (local_fused): blocks jt - n_local + 1 .. jt.
 __device__ __forceinline__ bool slc_pair_kept(int j, int64_t r, const Dims& dm, int local_fused) {
-  return j >= 0 && !(local_fused && (int64_t)j > (dm.q0 + r) / dm.ls - dm.n_local);
+  const int64_t jt = (dm.q0 + r) / dm.ls;  // < Ns for every row of the sequence
+  return j >= 0 && (int64_t)j <= jt && !(local_fused && (int64_t)j > jt - dm.n_local);
 }
 
 __global__ void __launch_bounds__(256) slc_count_kernel(const int32_t* __restrict__ idx,
@@ -339,9 +342,12 @@ __global__ void __launch_bounds__(256) slc_merge_kernel(const float2* __restrict
   const int32_t* sel = idx + item * dm.n;
   const float2* mls = pml + item * dm.n * G;
   const _Float16* ors = po + item * dm.n * G * (int64_t)HD;
-  // weights: lane s (< n) holds slot s; one load round for the (max, sum) of every head
+  // weights: lane s (< n) holds slot s; one load round for the (max, sum) of every head.  Slots
+  // whose block lies after the row (no key, no partial: see slc_pair_kept) weigh nothing.
   {
-    const bool lv = l < dm.n && sel[l < dm.n ? l : 0] >= 0;
+    const int64_t jt = (dm.q0 + br % dm.Tq) / dm.ls;
+    const int js = sel[l < dm.n ? l : 0];
+    const bool lv = l < dm.n && js >= 0 && (int64_t)js <= jt;
     float2 ml[8];
 #pragma unroll
     for (int w = 0; w < 8; ++w)

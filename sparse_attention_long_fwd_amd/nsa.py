@@ -14,7 +14,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libnsa.so")
+# NSA_LIB_PATH selects another build of the same library (the host-sanitizer test's instrumented
+# build); by default the in-tree libnsa.so.
+LIB_PATH = os.environ.get("NSA_LIB_PATH") or os.path.join(_PKG, "libnsa.so")
 
 NSA_OK, NSA_ERR_INVALID_ARG, NSA_ERR_UNSUPPORTED, NSA_ERR_HIP, NSA_ERR_WORKSPACE_TOO_SMALL = 0, -1, -2, -3, -4
 NSA_F32, NSA_BF16 = 0, 1

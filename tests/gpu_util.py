@@ -38,8 +38,10 @@ def check_indices(gpu_idx, ref_idx, ref_gap, ref_imp, pos, ls, n, n_init, n_loca
 
     Where the oracle's gap exceeds GAP the sets must be identical.  Everywhere
     else the GPU set must be a valid selection: ascending, -1 padded, the forced
-    blocks present, the right size, and every free pick within GAP of the
-    oracle's last taken free candidate.
+    blocks present, the right size, every free pick within GAP of the oracle's
+    last taken free candidate, and every free candidate that lies more than GAP
+    above that last taken value taken (a set that drops a clearly better block
+    for one inside the band is a mis-ranking, not a tie).
     """
     gpu_idx = np.asarray(gpu_idx)
     same = np.all(gpu_idx == ref_idx, axis=-1)
@@ -61,5 +63,9 @@ def check_indices(gpu_idx, ref_idx, ref_gap, ref_imp, pos, ls, n, n_init, n_loca
         kth = min(ref_imp[r, g, j] for j in ref_free) if ref_free else np.inf
         for x in sel:
             if x not in forced:
-                assert ref_imp[r, g, x] >= kth - GAP
+                assert ref_imp[r, g, x] >= kth - GAP, (r, g, x)
+        clear = set(np.nonzero(np.asarray(ref_imp[r, g, :jt + 1]) > kth + GAP)[0].tolist()) - forced
+        missing = clear - set(sel)
+        assert not missing, "row %d group %d leaves out blocks %s scored clearly above the band" % (
+            r, g, sorted(missing))
     return same
