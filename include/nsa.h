@@ -226,6 +226,25 @@ int32_t nsa_decode_fwd(const void* q, const void* k, const void* v, const void* 
                        int32_t* block_idx_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * nsa_decode_fwd_noalloc -- nsa_decode_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments, outputs and kernels, without the
+ * workspace arguments.  Its scratch is a device array inside the library, 64
+ * MiB per GPU, held from the library's first use on that GPU until the process
+ * ends; the call allocates nothing.  A batch whose workspace
+ * (nsa_decode_workspace_size) exceeds that array is rejected with
+ * NSA_ERR_WORKSPACE_TOO_SMALL before any launch (16 sequences of 64K tokens
+ * need about 11 MB).  Every call on a GPU uses the same array: calls that
+ * overlap in time on one GPU (concurrent streams or threads) race and must be
+ * ordered by the caller.
+ */
+int32_t nsa_decode_fwd_noalloc(const void* q, const void* k, const void* v, const void* k_cmp, const void* v_cmp,
+                               const float* gates, const uint8_t* is_video, int32_t dtype, const nsa_shape* shape,
+                               const nsa_params* params, const int32_t* kv_lens, const int32_t* page_table,
+                               int32_t max_pages, int64_t num_pages, void* out, void* o_cmp, void* o_slc,
+                               void* o_swa, int32_t* block_idx_out, void* stream);
+
+/*
  * nsa_compress_append -- incremental update of a compressed cache ([B]
  * section 一, [C] section 2.2; the weighted block sum of nsa_compress_kv).
  * After n_new tokens were appended to every sequence (kv_lens[b] = L_b

@@ -562,6 +562,44 @@ int32_t nsa_decode_fwd(const void* q, const void* k, const void* v, const void* 
   return NSA_OK;
 }
 
+int32_t nsa_decode_fwd_noalloc(const void* q, const void* k, const void* v, const void* k_cmp, const void* v_cmp,
+                               const float* gates, const uint8_t* is_video, int32_t dtype, const nsa_shape* shape,
+                               const nsa_params* params, const int32_t* kv_lens, const int32_t* page_table,
+                               int32_t max_pages, int64_t num_pages, void* out, void* o_cmp, void* o_slc,
+                               void* o_swa, int32_t* block_idx_out, void* stream) {
+  g_err[0] = 0;
+  Dims dm;
+  int st = decode_dims(shape, params, dtype, page_table, max_pages, num_pages, &dm);
+  if (st != NSA_OK) return st;
+  if (!out) return fail(NSA_ERR_INVALID_ARG, "out must not be NULL");
+  if (dm.B == 0) return NSA_OK;
+  if (!q || !k || !v || !k_cmp || !v_cmp || !gates) return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_cmp) || !aligned16(v_cmp) ||
+      !aligned16(out) || !aligned16(o_cmp) || !aligned16(o_slc) || !aligned16(o_swa))
+    return fail(NSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  const size_t need = decode_ws_bytes(dm);
+  if (need > noalloc_scratch_bytes())
+    return fail(NSA_ERR_WORKSPACE_TOO_SMALL,
+                "this decode batch needs %zu bytes of scratch; the library's device array holds %zu "
+                "(use nsa_decode_fwd with a caller workspace)", need, noalloc_scratch_bytes());
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  hipError_t e = noalloc_scratch(&ws, &ws_bytes);
+  if (e != hipSuccess) return hip_fail(e, "scratch address (hipGetSymbolAddress)");
+  DecVar dv;
+  dv.lens = kv_lens;
+  dv.pages = page_table;
+  dv.max_pages = page_table ? max_pages : 0;
+  dv.num_pages = page_table ? num_pages : 0;
+  char* p = (char*)ws;
+  int32_t* idx = block_idx_out ? block_idx_out : (int32_t*)p;
+  p += round_up((size_t)dm.B * dm.Hkv * dm.n * 4);
+  e = launch_decode_fast(dm, dv, q, k_cmp, nullptr, v_cmp, nullptr, k, v, is_video, gates, out, o_cmp, o_slc, o_swa,
+                         idx, nullptr, nullptr, p, (hipStream_t)stream, nullptr);
+  if (e != hipSuccess) return hip_fail(e, "decode kernels");
+  return NSA_OK;
+}
+
 int32_t nsa_compress_append(const void* k, const void* v, int32_t dtype, int64_t batch, int64_t kv_len,
                             int32_t num_kv_heads, int32_t head_dim, const float* w_k, const float* w_v,
                             int32_t cmp_block, int32_t cmp_stride, const int32_t* kv_lens, const int32_t* page_table,

@@ -114,3 +114,8 @@ hipError_t launch_decode_fast(const Dims& dm, const DecVar& dv, const void* q, c
 // last token is among them (per sequence), from the (possibly paged) K / V cache.
 hipError_t launch_compress_append(const Dims& dm, const DecVar& dv, const void* k, const void* v, const float* w_k,
                                   const float* w_v, void* kc, void* vc, int n_new, hipStream_t s);
+
+// Scratch of nsa_decode_fwd_noalloc: the current device's copy of a file-scope device array
+// (address from hipGetSymbolAddress, kept per device) and its size.
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+size_t noalloc_scratch_bytes();

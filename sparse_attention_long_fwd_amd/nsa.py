@@ -61,6 +61,8 @@ EXPORTS = {
     "nsa_decode_workspace_size": (_SZ, [_SH, _PR, _I32]),
     "nsa_decode_fwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _SH, _PR, _P, _P, _I32, _I64, _P, _P, _P, _P, _P,
                               _P, _SZ, _P]),
+    "nsa_decode_fwd_noalloc": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _SH, _PR, _P, _P, _I32, _I64, _P, _P, _P, _P,
+                                      _P, _P]),
     "nsa_compress_append": (_I32, [_P, _P, _I32, _I64, _I64, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _I32, _I64,
                                    _I32, _P, _P, _P]),
     "nsa_gate_proj": (_I32, [_P, _P, _P, _I32, _I64, _I64, _I32, _I32, _P, _P]),
@@ -263,6 +265,24 @@ def nsa_decode_fwd(q, k, v, k_cmp, v_cmp, gates, shape: NsaShape, params: NsaPar
                                 dt, ctypes.byref(shape), ctypes.byref(params), _ptr(kv_lens), _ptr(page_table),
                                 max_pages, num_pages, _ptr(out), _ptr(o_cmp), _ptr(o_slc), _ptr(o_swa),
                                 _ptr(block_idx_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def nsa_decode_fwd_noalloc(q, k, v, k_cmp, v_cmp, gates, shape: NsaShape, params: NsaParams, kv_lens=None,
+                           page_table=None, num_pages=0, is_video=None, out=None, o_cmp=None, o_slc=None,
+                           o_swa=None, block_idx_out=None, stream=None):
+    """nsa_decode_fwd with the library's own device scratch instead of a workspace (the call allocates
+    nothing on the device; `out` must then be given by the caller to keep it that way)."""
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    max_pages = 0 if page_table is None else page_table.shape[1]
+    if page_table is not None and not num_pages:
+        num_pages = k.shape[0]
+    _check(lib().nsa_decode_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cmp), _ptr(v_cmp), _ptr(gates),
+                                        _ptr(is_video), dt, ctypes.byref(shape), ctypes.byref(params), _ptr(kv_lens),
+                                        _ptr(page_table), max_pages, num_pages, _ptr(out), _ptr(o_cmp), _ptr(o_slc),
+                                        _ptr(o_swa), _ptr(block_idx_out), _stream(stream)))
     return out
 
 

@@ -146,6 +146,27 @@ def test_decode_varlen_validates_first():
     assert _decode(_dshape(batch=0)) == nsa.NSA_OK                       # empty batch launches nothing
 
 
+def test_decode_noalloc_validates_first():
+    """The no-allocation decode rejects what nsa_decode_fwd rejects, and batches whose workspace
+    exceeds the library's 64 MiB device scratch, before any launch."""
+    L = nsa.lib()
+    pr = _params(top_n=16, window=512)
+
+    def call(shape, dtype=nsa.NSA_BF16, kc=FAKE):
+        return L.nsa_decode_fwd_noalloc(FAKE, FAKE, FAKE, kc, FAKE, FAKE, None, dtype, ctypes.byref(shape),
+                                        ctypes.byref(pr), FAKE, None, 0, 0, FAKE, None, None, None, None, None)
+
+    assert call(_dshape(q_len=2)) == nsa.NSA_ERR_INVALID_ARG
+    assert call(_dshape(), dtype=nsa.NSA_F32) == nsa.NSA_ERR_UNSUPPORTED
+    assert call(_dshape(), kc=None) == nsa.NSA_ERR_INVALID_ARG
+    big = _dshape(batch=64, kv_len=1 << 19)
+    assert nsa.nsa_decode_workspace_size(big, pr, nsa.NSA_BF16) > 64 << 20
+    assert call(big) == nsa.NSA_ERR_WORKSPACE_TOO_SMALL
+    assert "scratch" in nsa.last_error()
+    assert nsa.nsa_decode_workspace_size(_dshape(batch=16, kv_len=65536), pr, nsa.NSA_BF16) < 64 << 20
+    assert call(_dshape(batch=0)) == nsa.NSA_OK
+
+
 def test_compress_append_validates_first():
     L = nsa.lib()
 
