@@ -111,7 +111,7 @@ SparseWs sparse_ws(const Dims& dm, int32_t dtype) {
 }
 
 struct LayerWs {
-  size_t kc, vc, o_cmp, lse, imp, idx, o_swa, sparse, dec, total;
+  size_t kc, vc, kv16, o_cmp, lse, imp, idx, o_swa, sparse, dec, total;
 };
 // One query row per sequence on the MFMA path: the split decode kernels.
 bool use_decode(int32_t dtype, const Dims& dm) { return use_fast(dtype, dm) && decode_supported(dm); }
@@ -132,9 +132,11 @@ LayerWs layer_ws(const Dims& dm, int32_t dtype) {
   if (fast && decode_supported(dm)) {
     w.dec = round_up(decode_workspace(dm));
   } else if (fast) {
-    // values as V^T tiles (padded to whole 64-key tiles), high + low parts
-    const size_t vt = round_up(vt_tiles_bytes(dm)) * 2;
-    if (vt > w.vc) w.vc = vt;
+    if (cmp_group_supported(dm)) {
+      // the group kernel's fp16 key / value tiles replace the row-major compressed keys / values
+      w.kc = w.vc = 0;
+      w.kv16 = round_up(kv16_tiles_bytes(dm));
+    }
     // fp32 branch output of the compression path (read by the combine)
     w.o_cmp = round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 4);
     w.imp = round_up((size_t)dm.B * dm.Tq * dm.Hkv * dm.Ns * 4);
@@ -144,19 +146,26 @@ LayerWs layer_ws(const Dims& dm, int32_t dtype) {
     w.imp = round_up((size_t)dm.B * dm.Tq * dm.Hkv * dm.Ns * 4);
     w.o_swa = round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * es);
   }
-  w.total = w.kc + w.vc + w.o_cmp + w.lse + w.imp + w.idx + w.o_swa + w.sparse + w.dec;
+  w.total = w.kc + w.vc + w.kv16 + w.o_cmp + w.lse + w.imp + w.idx + w.o_swa + w.sparse + w.dec;
   return w;
 }
 
 // kc/vc: compressed keys/values (bf16 high parts on the MFMA path, or cdtype on the generic path);
-// kl/vl: low parts on the MFMA path when the layer compressed them itself.
+// kl8 / ksc / vl: on the MFMA path when the layer compressed them itself, the keys' fp8 low parts
+// and their scales and the values' bf16 low parts; kv16: instead of all these, the group kernel's
+// fp16 key / value tiles.
 int run_cmp(int32_t dtype, int32_t cdtype, const Dims& dm, const void* q, const void* kc, const void* kl8,
-            const void* ksc, const void* vc, const void* vl, const uint8_t* vid, void* o, float* o32, float* lse,
-            float* imp, hipStream_t s) {
-  // low parts come only from the layer's own compression, which writes V as V^T tiles
-  hipError_t e = use_fast(dtype, dm) ? launch_cmp_fast(dm, q, kc, kl8, ksc, vc, vl, vid, o, o32, lse, imp,
-                                                       kl8 != nullptr, s)
-                                     : launch_cmp_generic(dtype, cdtype, dm, q, kc, vc, vid, o, lse, imp, s);
+            const void* ksc, const void* vc, const void* vl, const void* kv16, const uint8_t* vid, void* o, float* o32,
+            float* lse, float* imp, hipStream_t s) {
+  hipError_t e;
+  if (!use_fast(dtype, dm)) {
+    e = launch_cmp_generic(dtype, cdtype, dm, q, kc, vc, vid, o, lse, imp, s);
+  } else if (kv16) {
+    const int R = cmp_group_rows();
+    e = launch_cmp_group(dm, q, kv16, vid, o, o32, lse, imp, 0, (int)((dm.Tq + R - 1) / R), s);
+  } else {
+    e = launch_cmp_fast(dm, q, kc, kl8, ksc, vc, vl, vid, o, o32, lse, imp, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "compression-branch kernel");
   return NSA_OK;
 }
@@ -276,7 +285,7 @@ int32_t nsa_cmp_attn_scores(const void* q, const void* k_cmp, const void* v_cmp,
     return fail(NSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
   if (!use_fast(dtype, dm) && dm.Ns > 16384)
     return fail(NSA_ERR_UNSUPPORTED, "generic kernel handles at most 16384 selection blocks");
-  return run_cmp(dtype, dtype, dm, q, k_cmp, nullptr, nullptr, v_cmp, nullptr, is_video, o_cmp, nullptr, lse,
+  return run_cmp(dtype, dtype, dm, q, k_cmp, nullptr, nullptr, v_cmp, nullptr, nullptr, is_video, o_cmp, nullptr, lse,
                  importance,
                  (hipStream_t)stream);
 }
@@ -371,6 +380,9 @@ int32_t layer_fwd(const void* q, const BranchKV& kv, const void* k_cmp_in, const
   p += w.kc;
   void* vc = p;
   p += w.vc;
+  // the group kernel's key / value tiles, when the layer compresses K / V itself
+  void* kv16 = w.kv16 && !k_cmp_in ? p : nullptr;
+  p += w.kv16;
   void* ocmp_ws = p;
   p += w.o_cmp;
   float* lse = (float*)p;
@@ -393,21 +405,25 @@ int32_t layer_fwd(const void* q, const BranchKV& kv, const void* k_cmp_in, const
   int32_t cdtype = dtype;
   if (!kc_use) {
     // Compressed inside the layer, carried at fp32 precision: the MFMA path as bf16 high + low
-    // parts (both enter every product), the generic path as fp32.
-    // Prefill on the MFMA path takes the values as V^T tiles and the keys' low parts in fp8
-    // with per-group scales (the scaled fp8 product of the compression branch).
+    // parts (both enter every product), the generic path as fp32.  Prefill on the MFMA path: with
+    // 4..7 query heads per KV head the group kernel's fp16 key / value tiles instead; with 8, the
+    // keys' low parts in fp8 with per-group scales (the scaled fp8 product of cmp_fast_kernel).
     const bool fast = use_fast(dtype, dm);
-    const bool vt = fast && !decode_supported(dm);
+    const bool k8 = fast && !decode_supported(dm) && !kv16;
     void* kl = fast ? (char*)kc + round_up((size_t)dm.B * dm.Nc * dm.Hkv * dm.D * 2) : nullptr;
     void* vl = fast ? (char*)vc + w.vc / 2 : nullptr;
-    void* ksc = vt ? (char*)kl + round_up(k8_lo_bytes(dm)) : nullptr;
-    hipError_t e = vt ? launch_compress_k8(dm, kv.kc, w_k, kc, kl, ksc, s)
-                      : launch_compress(dtype, fast ? 2 : 1, kv.kc, w_k, kc, kl, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d,
-                                        dm.Nc, s);
-    if (e == hipSuccess)
-      e = vt ? launch_compress_vt(dm, kv.vc, w_v, vc, vl, s)
-             : launch_compress(dtype, fast ? 2 : 1, kv.vc, w_v, vc, vl, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d, dm.Nc,
+    void* ksc = k8 ? (char*)kl + round_up(k8_lo_bytes(dm)) : nullptr;
+    hipError_t e;
+    if (kv16) {
+      e = launch_compress_kv16(dm, kv.kc, w_k, kv.vc, w_v, kv16, s);
+      kl = vl = nullptr;
+    } else {
+      e = k8 ? launch_compress_k8(dm, kv.kc, w_k, kc, kl, ksc, s)
+             : launch_compress(dtype, fast ? 2 : 1, kv.kc, w_k, kc, kl, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d, dm.Nc,
                                s);
+      if (e == hipSuccess)
+        e = launch_compress(dtype, fast ? 2 : 1, kv.vc, w_v, vc, vl, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d, dm.Nc, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "compress kernel");
     kc_use = kc;
     vc_use = vc;
@@ -433,7 +449,8 @@ int32_t layer_fwd(const void* q, const BranchKV& kv, const void* k_cmp_in, const
   void* ocmp = fast ? o_cmp : (o_cmp ? o_cmp : ocmp_ws);
   float* ocmp32 = fast ? (float*)ocmp_ws : nullptr;
   int32_t* idx = block_idx_out ? block_idx_out : idx_ws;
-  st = run_cmp(dtype, cdtype, dm, q, kc_use, kl_use, ksc_use, vc_use, vl_use, is_video, ocmp, ocmp32, lse, imp, s);
+  st = run_cmp(dtype, cdtype, dm, q, kc_use, kl_use, ksc_use, vc_use, vl_use, kv16, is_video,
+               ocmp, ocmp32, lse, imp, s);
   if (st != NSA_OK) return st;
   prof_mark(s);
   // The window pass needs neither the compression branch nor the top-n: outside phase timing it

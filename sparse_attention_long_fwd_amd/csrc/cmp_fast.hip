@@ -9,6 +9,11 @@
 // with compressed block 32 / stride 16 and selection block 64, so that block j
 // takes compressed blocks 4j .. 4j+2 whole and half of 4j-1 and 4j+3.
 //
+// This kernel serves 8 query heads per KV head and compressed keys / values that
+// the caller passes in; with 4..7 heads per KV head the layer's own compression
+// runs on cmp_group_kernel (fp16 key / value tiles, all heads of a group in one
+// wave).
+//
 // Layout on the chip: one workgroup = 32 consecutive query rows x the G heads
 // of one KV group, one wave per head.  Scores are formed transposed,
 // S^T = Kc Q^T (v_mfma_f32_32x32x16_bf16, keys on M, the wave's 32 rows on N),
@@ -34,11 +39,11 @@
 // sum).  K then comes as a bf16 high part plus the remainder in fp8 (e4m3) with
 // one power-of-two scale per 32 channels of a key (compress_k8_kernel); the
 // remainder enters every score through the scaled fp8 MFMA
-// (v_mfma_scale_f32_32x32x64_f8f6f4) against an fp8 copy of Q with per-lane
-// scales.  The remainder is below 2^-8 of the key and its product carries an
+// (v_mfma_scale_f32_32x32x64_f8f6f4) against an fp8 copy of Q with one scale
+// per row.  The remainder is below 2^-8 of the key and its product carries an
 // error near 2^-4 of itself, so the scores keep about 2^-12 relative precision
-// instead of the 2^-8 of bf16 keys, at a quarter of the matrix-core time of a
-// second bf16 product.  V comes as bf16 high + low parts; both enter the value
+// instead of the 2^-8 of bf16 keys, at half the matrix-core time of a second
+// bf16 product.  V comes as bf16 high + low parts; both enter the value
 // sum for workgroups whose rows see fewer than kVloBelow compressed blocks,
 // longer rows use the high part alone.
 #include "fast_common.hpp"
@@ -54,17 +59,7 @@ constexpr int TILE = CK * HD;  // bf16 elements of one staged array
 // Scores always use both parts of K: the block importance that decides the top-n moves by
 // up to a few 1e-3 with bf16 Kc.
 constexpr int64_t kVloBelow = 256;
-// Row tiles whose first row sees at least this many compressed blocks form the log-sum-exp of
-// the first sweep from the keys' bf16 high parts alone (no fp8 remainder product, no low parts
-// staged in that sweep); the second sweep, whose probabilities make the importance, keeps both
-// parts.  A normaliser error dL scales all of a head's probabilities by exp(-dL), so it moves
-// each importance by about imp * dL, and from a few hundred blocks on dL (a probability-weighted
-// mean of the score errors) and the importances are both small: in an fp64 emulation on the 128K
-// and 36K workloads (random rows of every group) the importance moves by at most a few 1e-5 from
-// here on, against the 5e-4 that keeps every selection whose gap exceeds 1e-3 unchanged.  With
-// the high parts in both sweeps it moved by up to 3.8e-4 at 12K tokens, which is why the second
-// sweep keeps the remainder.
-constexpr int64_t kLseHiFrom = 512;
+
 }  // namespace
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -74,28 +69,11 @@ __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)"
 #define SG(kind, n) __builtin_amdgcn_sched_group_barrier(kind, n, 0)
 constexpr int SG_VALU = 0x2, SG_MFMA = 0x8, SG_DSR = 0x100;
 
-// Compressed values as V^T tiles (the layout compress_vt_kernel writes): per (b, KV head) a run
-// of ceil(Nc / 64) tiles of [128 dims][64 keys], keys zero-padded past Nc.  Inside a 16-key
-// group the key at offset o sits at slot 8*((o>>2)&1) + 4*(o>>3) + (o&3): the eight keys one
-// lane half feeds to an MFMA step (C-register order of the score tile) are adjacent, and the
-// A operand of O^T += Vc^T P^T is one 16-byte read.  16-byte chunks are XOR-swizzled by
-// (dim & 7) so 8 consecutive dims hit distinct banks.  A tile is its own LDS image.
-__device__ __forceinline__ int vt_slot(int dim, int key) {
-  const int o = key & 15;
-  const int kidx = (key & ~15) + 8 * ((o >> 2) & 1) + 4 * (o >> 3) + (o & 3);
-  return dim * CK + ((((kidx >> 3) ^ (dim & 7))) << 3) + (kidx & 7);
-}
-
 // Split keys, low part (compress_k8_kernel, launch_compress_k8): [B, Nc, Hkv, 128] bytes of fp8
-// e4m3 plus [B, Nc, Hkv, 4] scale bytes (E8M0: 2^(byte - 127)).  Inside a key row channel d sits
-// at byte k8_pos(d): the 32 channels lane half hl of an MFMA step-pair feeds to scaled fp8 MFMA c
-// (the channels 16 ks + 8 hl + e, ks = 4c .. 4c + 3, e = 0 .. 7, which are the ones its bf16 Q
-// registers hold) are the 32 contiguous bytes [64 c + 32 hl, +32), and they share scale byte
-// 2 c + hl.
-__host__ __device__ __forceinline__ int k8_pos(int d) {
-  const int ks = d >> 4, hb = (d >> 3) & 1;
-  return (ks >> 2) * 64 + hb * 32 + (ks & 3) * 8 + (d & 7);
-}
+// e4m3 in channel order plus [B, Nc, Hkv, 4] scale bytes (E8M0: 2^(byte - 127)), scale s for
+// channels 32 s .. 32 s + 31.  Lane half hl of scaled MFMA c (32x32x64) reads channels
+// [64 c + 16 hl, +16) and [64 c + 32 + 16 hl, +16) and supplies scale byte 2 c + hl (see the
+// operand note in fast_common.hpp).
 // Staged fp8 tile: 64 rows of 128 bytes, 16-byte chunk c of row r at chunk c ^ ((r >> 1) & 7), so
 // the 16 lanes reading one chunk of 16 consecutive rows hit distinct banks.
 __device__ __forceinline__ int swz8(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
@@ -121,12 +99,10 @@ struct CmpLds {
   static constexpr int BUF = SPLIT ? VL + TILE * 2 : VH + TILE * 2;
 };
 
-// VT: values come as V^T tiles (high parts in vh, low parts in vl) instead of [B, Nc, Hkv, D].
 // SPLIT: keys as bf16 high parts (kh) + fp8 low parts (kl8) with scales (ksc).
 // ipart_bufs: 2 = importance partials double-buffered by tile parity, 1 = one buffer (one more
 // barrier a tile; used where two do not fit in LDS).
-// LSE_HI: the first sweep uses the keys' high parts only (split keys, long rows; see kLseHiFrom).
-template <bool SPLIT, bool VT, bool LSE_HI>
+template <bool SPLIT>
 __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kh,
                                                        const uint8_t* __restrict__ kl8,
                                                        const uint8_t* __restrict__ ksc, const bf16* __restrict__ vh,
@@ -178,37 +154,20 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = rvalid ? *(const bf16x8*)(qrow + 16 * ks) : zero8();
   }
-  // fp8 copy of Q for the low parts of K: B operand of scaled MFMA c = the 32 values of
-  // qf[4c .. 4c+3] in order, scaled by 2^(8 - E) (E: the smallest power of two above their
-  // magnitudes, so every value stays below 256 in e4m3); scale byte 119 + E undoes it.
+  // fp8 copy of Q for the low parts of K: B operand of scaled MFMA c (channels 64 c .. 64 c + 63):
+  // lane half hl holds the pieces [64 c + 16 hl, +16) and [64 c + 32 + 16 hl, +16) (the operand
+  // byte order of fast_common.hpp), one power-of-two scale for the whole row
   i32x8 q8[2] = {};
-  int q8s[2] = {127, 127};
+  int q8s = 127;
   if constexpr (SPLIT) {
+    const bf16* qn = q + ((b * dm.Tq + (rvalid ? r : 0)) * dm.Hq + h) * (int64_t)HD;
+    bf16x8 pv[2][4];
+    float m = 0.f;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float mq = 0.f;
+    for (int c = 0; c < 2; ++c) m = fmaxf(m, load_pieces(qn, 64 * c + 16 * hl, 64 * c + 32 + 16 * hl, rvalid, pv[c]));
+    m = fmaxf(m, xchg32(m, hl));  // the row's other half
 #pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mq = fmaxf(mq, fabsf((float)qf[4 * c + k4][e]));
-      int E = 0;
-      (void)frexpf(mq, &E);
-      const bool ok = mq > 0.f && 119 + E >= 1;
-      q8s[c] = ok ? 119 + E : 127;
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4)
-#pragma unroll
-        for (int e2 = 0; e2 < 2; ++e2) {
-          const bf16x8& v8 = qf[4 * c + k4];
-          const float f0 = ok ? ldexpf((float)v8[4 * e2 + 0], 8 - E) : 0.f;
-          const float f1 = ok ? ldexpf((float)v8[4 * e2 + 1], 8 - E) : 0.f;
-          const float f2 = ok ? ldexpf((float)v8[4 * e2 + 2], 8 - E) : 0.f;
-          const float f3 = ok ? ldexpf((float)v8[4 * e2 + 3], 8 - E) : 0.f;
-          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
-          wd = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, wd, true);
-          q8[c][2 * k4 + e2] = wd;
-        }
-    }
+    for (int c = 0; c < 2; ++c) fp8_pieces(pv[c], m, q8[c], q8s);
   }
 
   // VLO: the low parts of V enter the value sum (see kVloBelow); a uniform choice per workgroup
@@ -261,17 +220,9 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
       }
     }
   };
-  const int ntv = (int)((dm.Nc + CK - 1) / CK);
   auto stage_v = [&](int tile, int bufi) {
-    if constexpr (VT) {
-      // past the last tile (only the importance carry is flushed there, every p is 0): restage it
-      const int64_t t0 = ((b * dm.Hkv + g) * ntv + (tile < ntv ? tile : ntv - 1)) * (int64_t)TILE;
-      stage_lin16k(vhs_of(bufi), vh + t0, wu, G, l);
-      if constexpr (VLO) stage_lin16k(vls_of(bufi), vl + t0, wu, G, l);
-    } else {
-      stage64(vhs_of(bufi), vh + base, tile);
-      if constexpr (VLO) stage64(vls_of(bufi), vl + base, tile);
-    }
+    stage64(vhs_of(bufi), vh + base, tile);
+    if constexpr (VLO) stage64(vls_of(bufi), vl + base, tile);
   };
   // S^T blocks 0 and 1 (32 keys each) of the staged tile; the two accumulation chains alternate
   auto scores2 = [&](int bufi, f32x16& s0, f32x16& s1, auto lo_c) {
@@ -287,22 +238,25 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
     if constexpr (decltype(lo_c)::value) {
       const unsigned char* lo = lds_at(bufi, LY::KL);
       const int* sc = (const int*)lds_at(bufi, LY::KS);
-      // scale bytes 2c + hl of the lane's key row, moved so byte 2c belongs to this lane half
+      // scale bytes 2c + hl of the lane's key row (channels [64 c + 32 hl, +32), the scale of K block
+      // hl of MFMA c), moved so byte 2c belongs to this lane half
       const int sa0 = sc[n] >> (8 * hl), sa1 = sc[32 + n] >> (8 * hl);
+      // A operand of MFMA c, lane half hl: the 16-byte chunks 4 c + hl and 4 c + 2 + hl of the key's
+      // remainder row (channels [64 c + 16 hl, +16) and [64 c + 32 + 16 hl, +16))
       i32x8 a[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const int row = kb * 32 + n;
-          const i32x4 x0 = *(const i32x4*)(lo + swz8(row, 4 * c + 2 * hl));
-          const i32x4 x1 = *(const i32x4*)(lo + swz8(row, 4 * c + 2 * hl + 1));
+          const i32x4 x0 = *(const i32x4*)(lo + swz8(row, 4 * c + hl));
+          const i32x4 x1 = *(const i32x4*)(lo + swz8(row, 4 * c + 2 + hl));
           a[kb][c] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-      s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0][0], q8[0], s0, 0, 0, 0, sa0, 0, q8s[0]);
-      s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1][0], q8[0], s1, 0, 0, 0, sa1, 0, q8s[0]);
-      s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0][1], q8[1], s0, 0, 0, 2, sa0, 0, q8s[1]);
-      s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1][1], q8[1], s1, 0, 0, 2, sa1, 0, q8s[1]);
+      s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0][0], q8[0], s0, 0, 0, 0, sa0, 0, q8s);
+      s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1][0], q8[0], s1, 0, 0, 0, sa1, 0, q8s);
+      s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0][1], q8[1], s0, 0, 0, 2, sa0, 0, q8s);
+      s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1][1], q8[1], s1, 0, 0, 2, sa1, 0, q8s);
     }
   };
   // Score register j of block kb in tile `tile` holds key tile CK + kb 32 + 4 hl + koff(j); it is
@@ -312,8 +266,8 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
   // tiles whose keys every row of the workgroup sees need no mask
   auto full = [&](int tile) { return (tile + 1) * CK <= nvmin; };
 
-  // keys' low parts: in the first sweep unless LSE_HI, always in the second (split keys)
-  constexpr std::integral_constant<bool, SPLIT && !LSE_HI> lo1{};
+  // keys' low parts (split keys) in both sweeps
+  constexpr std::integral_constant<bool, SPLIT> lo1{};
   constexpr std::integral_constant<bool, SPLIT> lo2{};
   // ---- sweep 1: log-sum-exp per (row, head) column.  mr: running maximum of the raw scores,
   // lsum: sum of 2^((s - mr) c2).  The scores of tile i are formed (MFMA) while the exponentials
@@ -461,13 +415,6 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
       const int vr = kb * 32 + 16 * st + 4 * (g16 >> 1) + (i16 >> 2);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        if constexpr (VT) {
-          // A operand: dims 32 db + n, the lane half's 8 keys of this 16-key step
-          const int off = (32 * db + n) * CK + (((2 * (2 * kb + st) + hl) ^ (n & 7)) << 3);
-          oacc[db] = mfma32(lds_read8(vhs_of(bufi) + off), pb, oacc[db]);
-          if constexpr (VLO) oacc[db] = mfma32(lds_read8(vls_of(bufi) + off), pb, oacc[db]);
-          continue;
-        }
         const int col = 32 * db + (g16 & 1) * 16 + 4 * (i16 & 3);
         const int o0 = swz128(vr, col >> 3) + (col & 7);
         const int o1 = swz128(vr + 8, col >> 3) + (col & 7);
@@ -556,12 +503,6 @@ __global__ void __launch_bounds__(512) cmp_fast_kernel(const bf16* __restrict__ 
   }
 }
 
-// Compressed blocks visible from absolute position t (host side of cmp_visible).
-static int64_t cmp_host_visible(int64_t t, const Dims& dm) {
-  const int64_t v = (t + 1 >= dm.l) ? (t + 1 - dm.l) / dm.d + 1 : 0;
-  return v < dm.Nc ? v : dm.Nc;
-}
-
 // Dynamic LDS: the staged K / V buffers, then 1 or 2 buffers of importance partials (2 when
 // they fit next to the static LDS of the kernel).
 static int cmp_ipart_bufs(const Dims& dm, bool split, size_t* bytes) {
@@ -574,105 +515,33 @@ static int cmp_ipart_bufs(const Dims& dm, bool split, size_t* bytes) {
 
 hipError_t launch_cmp_fast(const Dims& dm, const void* q, const void* kh, const void* kl8, const void* ksc,
                            const void* vh, const void* vl, const uint8_t* vid, void* o, float* o32, float* lse,
-                           float* imp, bool vt, hipStream_t s) {
+                           float* imp, hipStream_t s) {
   if (dm.Tq <= 0 || dm.B <= 0) return hipSuccess;
   const int ntq = (int)((dm.Tq + CQ - 1) / CQ);
   const int units = (int)(dm.B * dm.Hkv);
   const bool split = kl8 != nullptr;
-  if (split && !ksc) return hipErrorInvalidValue;
-  // the MFMA layer path always brings split parts with V^T tiles; standalone calls bring neither
-  if (split != vt) return hipErrorInvalidValue;
-  // One launch of a kernel variant over a contiguous range of row tiles [lo, lo + n).
-  auto launch = [&](const void* fn, bool sp, int lo, int n, auto kernel) -> hipError_t {
-    if (n <= 0) return hipSuccess;
+  if (split && (!ksc || !vl)) return hipErrorInvalidValue;
+  auto launch = [&](bool sp, auto kernel) -> hipError_t {
     size_t shm;
     const int bufs = cmp_ipart_bufs(dm, sp, &shm);
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     if (e != hipSuccess) return e;
-    kernel<<<dim3(xcd_grid(units, n)), dim3(dm.G * 64), shm, s>>>(
+    kernel<<<dim3(xcd_grid(units, ntq)), dim3(dm.G * 64), shm, s>>>(
         (const bf16*)q, (const bf16*)kh, (const uint8_t*)kl8, (const uint8_t*)ksc, (const bf16*)vh,
-        (const bf16*)vl, vid, (bf16*)o, o32, lse, imp, dm, lo, n, bufs);
+        (const bf16*)vl, vid, (bf16*)o, o32, lse, imp, dm, 0, ntq, bufs);
     return hipGetLastError();
   };
-  if (!split) {
-    auto* k = cmp_fast_kernel<false, false, false>;
-    return launch((const void*)k, false, 0, ntq, k);
-  }
-  // split parts: row tiles whose first row sees >= kLseHiFrom blocks take the high parts alone in
-  // the first sweep; they are the heavier launch and go first
-  int lo = ntq;
-  while (lo > 0 && cmp_host_visible(dm.q0 + (int64_t)(lo - 1) * CQ, dm) >= kLseHiFrom) --lo;
-  auto* kl = cmp_fast_kernel<true, true, true>;
-  auto* ks = cmp_fast_kernel<true, true, false>;
-  hipError_t e = launch((const void*)kl, true, lo, ntq - lo, kl);
-  if (e == hipSuccess) e = launch((const void*)ks, true, 0, lo, ks);
-  return e;
-}
-
-// Compressed values as V^T tiles (high and low bf16 parts of the fp32 sum), one workgroup per
-// (b, KV head, 64-key tile).  Threads sum 8 channels of one compressed key (16 threads read a
-// token row with 16-byte loads), place the results at their tile slots in LDS and the tile
-// leaves as one contiguous 16 KB run per part.
-__global__ void __launch_bounds__(256) compress_vt_kernel(const bf16* __restrict__ x, const float* __restrict__ w,
-                                                          bf16* __restrict__ hi, bf16* __restrict__ lo, int64_t T_len,
-                                                          int H, int l, int d, int64_t Nc, int ntv) {
-  __shared__ float ws[64];
-  __shared__ __attribute__((aligned(16))) bf16 s_hi[TILE], s_lo[TILE];
-  const int tile = blockIdx.x % ntv;
-  const int64_t bh = blockIdx.x / ntv;
-  const int h = (int)(bh % H);
-  const int64_t b = bh / H;
-  for (int m = threadIdx.x; m < l; m += blockDim.x) ws[m] = w[m];
-  __syncthreads();
-  for (int it = threadIdx.x; it < CK * (HD / 8); it += blockDim.x) {
-    const int key = it >> 4, c8 = it & 15;
-    const int64_t i = (int64_t)tile * CK + key;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (i < Nc) {
-      const bf16* src = x + ((b * T_len + i * d) * H + h) * (int64_t)HD + c8 * 8;
-      for (int m = 0; m < l; ++m) {
-        const bf16x8 u = *(const bf16x8*)(src + (int64_t)m * H * HD);
-        const float wm = ws[m];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(wm, (float)u[e], acc[e]);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bf16 vh = (bf16)acc[e];
-      const int slot = vt_slot(c8 * 8 + e, key);
-      s_hi[slot] = vh;
-      s_lo[slot] = (bf16)(acc[e] - (float)vh);
-    }
-  }
-  __syncthreads();
-  const int64_t t0 = (bh * ntv + tile) * (int64_t)TILE;
-  for (int c = threadIdx.x; c < TILE / 8; c += blockDim.x) {
-    *(bf16x8*)(hi + t0 + c * 8) = *(const bf16x8*)(s_hi + c * 8);
-    *(bf16x8*)(lo + t0 + c * 8) = *(const bf16x8*)(s_lo + c * 8);
-  }
-}
-
-size_t vt_tiles_bytes(const Dims& dm) { return (size_t)dm.B * dm.Hkv * ((dm.Nc + CK - 1) / CK) * TILE * 2; }
-
-hipError_t launch_compress_vt(const Dims& dm, const void* v, const float* w_v, void* hi, void* lo, hipStream_t s) {
-  if (dm.Nc <= 0 || dm.B <= 0) return hipSuccess;
-  if (dm.D != HD || dm.l > 64) return hipErrorInvalidValue;
-  const int ntv = (int)((dm.Nc + CK - 1) / CK);
-  compress_vt_kernel<<<(unsigned)(dm.B * dm.Hkv * ntv), 256, 0, s>>>((const bf16*)v, w_v, (bf16*)hi, (bf16*)lo, dm.T,
-                                                                    dm.Hkv, dm.l, dm.d, dm.Nc, ntv);
-  return hipGetLastError();
+  return split ? launch(true, cmp_fast_kernel<true>) : launch(false, cmp_fast_kernel<false>);
 }
 
 // Split keys for the compression branch: the fp32 sum x of each compressed key is stored as
-// its bf16 high part hi (row-major [B, Nc, Hkv, 128]) and the remainder x - hi in fp8 e4m3 at
-// the k8_pos layout, with one scale per group of 32 channels (the groups scaled fp8 MFMA c of
-// lane half hl reads).  Every |x| of a group lies below 2^E, so |x - hi| <= 2^(E - 9); the
-// remainder is stored times 2^(17 - E) (at most 256, inside e4m3's range) and scale byte
-// 110 + E (E8M0) undoes it.  Groups whose magnitudes are all below 2^-100 store zeros.
-// One thread per 8 channels of a compressed key; the 16 threads of a key row are 16
-// consecutive lanes, and the four of one group (channel chunks of equal parity inside one
-// half of the row) reduce their maximum with two lane exchanges.
+// its bf16 high part hi (row-major [B, Nc, Hkv, 128]) and the remainder x - hi in fp8 e4m3 in
+// channel order, with one scale per group of 32 consecutive channels.  Every |x| of a group lies
+// below 2^E, so |x - hi| <= 2^(E - 9); the remainder is stored times 2^(17 - E) (at most 256,
+// inside e4m3's range) and scale byte 110 + E (E8M0) undoes it.  Groups whose magnitudes are all
+// below 2^-100 store zeros.  One thread per 8 channels of a compressed key; the 16 threads of a
+// key row are 16 consecutive lanes, and the four of one group reduce their maximum with two lane
+// exchanges.
 __global__ void __launch_bounds__(256) compress_k8_kernel(const bf16* __restrict__ x, const float* __restrict__ w,
                                                           bf16* __restrict__ hi, uint8_t* __restrict__ lo8,
                                                           uint8_t* __restrict__ sc, int64_t T_len, int H, int l,
@@ -698,8 +567,8 @@ __global__ void __launch_bounds__(256) compress_k8_kernel(const bf16* __restrict
   float mx = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(acc[e]));
+  mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
   int E = 0;
   (void)frexpf(mx, &E);
   const bool keep = mx > 0.f && E >= -100;
@@ -716,9 +585,9 @@ __global__ void __launch_bounds__(256) compress_k8_kernel(const bf16* __restrict
   w1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[6], r[7], w1, true);
   if (!valid) return;
   *(bf16x8*)(hi + row * HD + c8 * 8) = vh;
-  *(int2*)(lo8 + row * HD + k8_pos(c8 * 8)) = make_int2(w0, w1);
-  // one thread of each group writes its scale byte 2 (group half of the row) + parity
-  if (((c8 >> 1) & 3) == 0) sc[row * 4 + 2 * (c8 >> 3) + (c8 & 1)] = (uint8_t)(keep ? 110 + E : 127);
+  *(int2*)(lo8 + row * HD + c8 * 8) = make_int2(w0, w1);
+  // the first thread of each group of 32 channels writes its scale byte
+  if ((c8 & 3) == 0) sc[row * 4 + (c8 >> 2)] = (uint8_t)(keep ? 110 + E : 127);
 }
 
 size_t k8_lo_bytes(const Dims& dm) { return (size_t)dm.B * dm.Nc * dm.Hkv * HD; }

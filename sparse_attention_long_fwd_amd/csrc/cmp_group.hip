@@ -1,0 +1,507 @@
+// Compression-branch attention fused with block importance, one wave per 16 query rows x the
+// whole GQA group (gfx950, MFMA 16x16x32).
+//
+// What it computes (top168.com digest of VideoNSA, section 一: the selection branch scores
+// segments by importance, read here from the compression branch's probabilities): for each
+// video row t and head h,
+//   p_i = softmax_i(scale * <q_t,h, kc_i>) over the compressed blocks i whose tokens all lie at
+//         or before t,  o_cmp = sum_i p_i vc_i,
+//   imp[t, g, j] = sum_{h in group g} sum_i frac(i, j) p_{h,i},
+// with compressed block 32 / stride 16 and selection block 64, so block j takes compressed
+// blocks 4j .. 4j+2 whole and half of 4j-1 and 4j+3.
+//
+// Layout on the chip.  A workgroup is 64 consecutive query rows of one KV group on four waves,
+// one wave per SIMD; a wave owns 16 rows and all G heads of the group.  Scores are formed
+// transposed per head, S^T = Kc Q^T with v_mfma_f32_16x16x32_bf16 (16 keys on M, the wave's 16
+// rows on N): every key fragment read from LDS feeds G matrix products, and a lane holds four
+// consecutive compressed keys of one row for each head -- exactly one selection block's aligned
+// run of four -- so the importance is summed over the heads in registers and the half-block
+// shares cross to the next lane group with one lane shuffle per 16 keys.  Values enter through
+// O^T += Vc^T P^T (dims on M, 32 keys per step) from pre-transposed tiles whose key order matches
+// the score registers, so P needs no shuffles; the G x 128 x 16 fp32 accumulators (224 registers
+// for G = 7) stay in the accumulation registers for the whole sweep.
+//
+// The importance needs the final softmax normaliser, hence two sweeps over the keys: the first
+// forms each (row, head)'s log-sum-exp, the second the exact probabilities, the value sum and the
+// importance; both form the same scores.  All matrix products take fp16 operands: the compressed
+// keys and values are fp32 block sums, and fp16's 10 mantissa bits keep the block importances
+// within about 2e-4 of exact (bf16 keys move them by up to about 1e-3, which can reorder blocks
+// that the top-n must keep apart), and the value sum within a few 1e-3 (with bf16 probabilities
+// and values, whose roundings are 2^-9 relative each, rows dominated by one compressed value lose
+// up to 0.013).  fp16's range is kept by power-of-two scales: one per query row and one per
+// 64-key tile of compressed keys, which bring the largest magnitude to [2^14, 2^15) and
+// [2^13, 2^14) (so the scores' precision does not depend on the inputs' magnitude), and one per
+// 64-key value tile, zero unless the tile's largest magnitude reaches 2^14.  The query and key
+// scales enter the score factor; against the largest value-tile scale s_ref of the sequence and
+// KV head, a tile's probabilities are scaled by 2^(s_tile - s_ref) and the output by 2^s_ref.
+//
+// Compressed K / V tiles of 64 keys are written by compress_kv16_kernel in their LDS image, so
+// they go global -> LDS as linear 16 KB runs (global_load_lds, 16 bytes a lane), double-buffered.
+#include "fast_common.hpp"
+
+namespace {
+constexpr int WR = 16;        // query rows per wave
+constexpr int NWV = 4;        // waves per workgroup (one per SIMD)
+constexpr int RQ = WR * NWV;  // query rows per workgroup
+constexpr int CK = 64;        // compressed keys per tile
+constexpr int HD = 128;       // head dim
+constexpr int TILE = CK * HD;
+// One LDS staging buffer (bytes): the key tile (64 rows of 128 fp16, 16-byte chunks swizzled as
+// swz128) and the value tile (V^T, 128 dims x 64 keys, fp16).
+constexpr int L_KT = 0;
+constexpr int L_VT = L_KT + TILE * 2;
+constexpr int L_BUF = L_VT + TILE * 2;
+}  // namespace
+
+// Key and value tiles (written by compress_kv16_kernel): per (b, KV head) ceil(Nc / 64) tiles of
+// 64 compressed keys, 8192 fp16 each (the block sums times 2^-s of the tile's scale s, a signed
+// byte per tile), keys past Nc zero.
+//  key tile:   row = key, 16-byte chunk c of the row at position c ^ (key & 15) (the swz128 image);
+//  value tile: V^T, [128 dims][64 key slots]: in each 32-key half the slot of key offset o is
+//              8 ((o & 15) >> 2) + 4 (o >> 4) + (o & 3), so lane group gi's 8 slots are the keys
+//              4 gi .. 4 gi + 3 and 16 + 4 gi .. +3 of the half, the order its score registers of
+//              the half's two 16-key M-blocks hold them in; 16-byte chunks XOR-swizzled by (dim & 7).
+// Buffer: all key tiles, all value tiles, the key tiles' scale bytes, the value tiles' scale bytes.
+__host__ __device__ __forceinline__ int kt16_pos(int key, int dim) {
+  return key * HD + ((((dim >> 3) ^ (key & 15))) << 3) + (dim & 7);
+}
+__host__ __device__ __forceinline__ int vt16_slot(int dim, int key) {
+  const int h = key >> 5, o = key & 31;
+  const int s = 32 * h + 8 * ((o & 15) >> 2) + 4 * (o >> 4) + (o & 3);
+  return dim * CK + (((s >> 3) ^ (dim & 7)) << 3) + (s & 7);
+}
+
+struct Kv16Layout {
+  size_t ntiles;  // tiles of one kind: B * Hkv * ceil(Nc / 64)
+  __host__ __device__ size_t kt() const { return 0; }
+  __host__ __device__ size_t vt() const { return ntiles * TILE * 2; }
+  __host__ __device__ size_t ks() const { return 2 * ntiles * TILE * 2; }
+  __host__ __device__ size_t vs() const { return ks() + ntiles; }
+  __host__ __device__ size_t bytes() const { return vs() + ntiles; }
+};
+
+// Power-of-two range scale of fp16 data whose largest magnitude is m: s with m 2^-s in
+// [2^(lim - 1), 2^lim) (for m = 0: -lim), clamped to [-127, 127]; with nonneg, at least 0.
+__device__ __forceinline__ int f16_range_scale(float m, int lim, bool nonneg) {
+  int E = 0;
+  (void)frexpf(m, &E);  // m in [2^(E - 1), 2^E)
+  int s = E - lim;
+  s = s < -127 ? -127 : (s > 127 ? 127 : s);
+  return nonneg && s < 0 ? 0 : s;
+}
+
+__device__ __forceinline__ void gwait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int G>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ kv16, const uint8_t* __restrict__ vid,
+                 bf16* __restrict__ o_bf, float* __restrict__ o_f32, float* __restrict__ lse,
+                 float* __restrict__ imp, Dims dm, int tile_lo, int ntiles) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int s_any, s_scale;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, gi = l >> 4, c = l & 15;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  int unit, rank;
+  if (!xcd_remap(blockIdx.x, (int)(dm.B * dm.Hkv), ntiles, &unit, &rank)) return;
+  const int64_t b = unit / dm.Hkv;
+  const int g = unit % dm.Hkv;
+  const int64_t rt0 = (int64_t)(tile_lo + ntiles - 1 - rank) * RQ;  // heaviest row tiles first
+  const int ntv = (int)((dm.Nc + CK - 1) / CK);
+  const Kv16Layout ly{(size_t)dm.B * dm.Hkv * ntv};
+  const int64_t tile0 = (b * dm.Hkv + g) * ntv;  // this (sequence, KV head)'s first tile
+  const _Float16* kt = (const _Float16*)(kv16 + ly.kt()) + tile0 * TILE;
+  const _Float16* vt = (const _Float16*)(kv16 + ly.vt()) + tile0 * TILE;
+  const uint8_t* ksc = kv16 + ly.ks() + tile0;
+  const uint8_t* vsc = kv16 + ly.vs() + tile0;
+
+  // skip row tiles without a video row; the largest value-tile scale of this (sequence, KV head)
+  if (tid == 0) {
+    s_any = 0;
+    s_scale = 0;
+  }
+  __syncthreads();
+  if (tid < RQ) {
+    const int64_t rr = rt0 + tid;
+    if (rr < dm.Tq && (!vid || vid[b * dm.Tq + rr])) s_any = 1;
+  }
+  for (int i = tid; i < ntv; i += blockDim.x) {
+    const int sc = vsc[i];
+    if (sc) atomicMax(&s_scale, sc);
+  }
+  __syncthreads();
+  if (!s_any) return;
+  const int s_ref = s_scale;  // the value accumulators hold O 2^-s_ref
+
+  const int64_t r = rt0 + WR * w + c;  // this lane's query row
+  const bool rvalid = r < dm.Tq;
+  const bool isv = rvalid && (!vid || vid[b * dm.Tq + r]);
+  const int nv = rvalid ? (int)cmp_visible(dm.q0 + r, dm.l, dm.d, dm.Nc) : 0;
+  const int64_t rlast = (rt0 + RQ < dm.Tq ? rt0 + RQ : dm.Tq) - 1;
+  const int nvmax = (int)cmp_visible(dm.q0 + rlast, dm.l, dm.d, dm.Nc);
+  const int nvmin = (int)cmp_visible(dm.q0 + rt0, dm.l, dm.d, dm.Nc);
+  const float c2 = dm.scale * LOG2E_F;
+
+  // Q, B operand of step ks: Q[row c][32 ks + 8 gi .. +8] for every head of the group, in fp16
+  // times 2^-eq, eq the row's range scale (the four lane groups of a row share it)
+  const bf16* qrow = q + ((b * dm.Tq + (rvalid ? r : 0)) * dm.Hq + (int64_t)g * G) * HD;
+  f16x8 qf[G][4];
+  int eq;
+  {
+    bf16x8 qb[G][4];
+    float m = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        qb[h][ks] = rvalid ? *(const bf16x8*)(qrow + h * HD + 32 * ks + 8 * gi) : zero8();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)qb[h][ks][e]));
+      }
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    eq = f16_range_scale(m, 15, false);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[h][ks][e] = (_Float16)ldexpf((float)qb[h][ks][e], -eq);
+  }
+
+  auto lds_at = [&](int bi, int off) { return smem + bi * L_BUF + off; };
+  // past the last tile (only importances of blocks no compressed key reaches are flushed there,
+  // every probability is 0): restage the last one
+  auto tclamp = [&](int tile) { return tile < ntv ? tile : ntv - 1; };
+  auto stage_k = [&](int tile, int bi) {
+    stage_lin16k((bf16*)lds_at(bi, L_KT), (const bf16*)(kt + (int64_t)tclamp(tile) * TILE), wu, NWV, l);
+  };
+  auto stage_v = [&](int tile, int bi) {
+    stage_lin16k((bf16*)lds_at(bi, L_VT), (const bf16*)(vt + (int64_t)tclamp(tile) * TILE), wu, NWV, l);
+  };
+  // log2 units per raw score unit of tile `tile`
+  auto c2_of = [&](int tile) { return ldexpf(c2, eq + (int)(int8_t)ksc[tclamp(tile)]); };
+  // Scores S^T of 16-key M-block mb (keys 16 mb .. +16 of the staged tile) for every head: each key
+  // fragment read from LDS feeds the G heads' products
+  auto scores = [&](int bi, int mb, f32x4 (&S)[G]) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) S[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const _Float16* kts = (const _Float16*)lds_at(bi, L_KT);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const f16x8 kf = *(const f16x8*)(kts + swz128(16 * mb + c, 4 * ks + gi));
+#pragma unroll
+      for (int h = 0; h < G; ++h) S[h] = mfma16h(kf, qf[h][ks], S[h]);
+    }
+  };
+  // Score register j of M-block mb of tile `tile` holds compressed key tile CK + 16 mb + 4 gi + j;
+  // it is visible when j < lim
+  auto lim_of = [&](int tile, int mb) { return nv - (tile * CK + 16 * mb + 4 * gi); };
+  auto full = [&](int tile) { return (tile + 1) * CK <= nvmin; };
+
+  // ---- sweep 1: log-sum-exp per (row, head), each lane over its own keys, in log2 units y =
+  // score c2: the sum of 2^(y - mr) against a whole-number reference mr, the largest floor(y) so
+  // far.  When mr moves the sum is rescaled by an exact power of two (ldexp), so every term is
+  // below 2 and no step branches.  The four lanes of a row are merged at the end.
+  constexpr float kNoKey = -1e30f;  // reference before the first visible key (below every score)
+  float mr[G], ls[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    mr[h] = kNoKey;
+    ls[h] = 0.f;
+  }
+  // one 16-key M-block's scores; MASK: register j counts only when j < lm (else -inf)
+  auto lse_block = [&](const f32x4 (&S)[G], float ct, int lm, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = (MASK && j >= lm) ? -INFINITY : S[h][j];
+      const float mn = fmaxf(mr[h], floorf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])) * ct));
+      float acc = ldexpf(ls[h], (int)fmaxf(mr[h] - mn, -256.f));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc += fexp2(fmaf(v[j], ct, -mn));
+      ls[h] = acc;
+      mr[h] = mn;
+    }
+  };
+  // one tile: the products of M-block mb + 1 are issued before the exponentials of M-block mb
+  auto lse_tile = [&](int tile, int bi, auto mask_c) {
+    const float ct = c2_of(tile);
+    f32x4 Sa[G], Sb[G];
+    scores(bi, 0, Sa);
+#pragma unroll
+    for (int mb = 0; mb < 4; mb += 2) {
+      scores(bi, mb + 1, Sb);
+      lse_block(Sa, ct, lim_of(tile, mb), mask_c);
+      if (mb + 2 < 4) scores(bi, mb + 2, Sa);
+      lse_block(Sb, ct, lim_of(tile, mb + 1), mask_c);
+    }
+  };
+  const int nt1 = (nvmax + CK - 1) / CK;
+  if (nt1 > 0) {
+    stage_k(0, 0);
+    gwait_loads();
+  }
+  __syncthreads();
+  for (int tile = 0; tile < nt1; ++tile) {
+    const int bi = tile & 1;
+    if (tile + 1 < nt1) stage_k(tile + 1, bi ^ 1);
+    if (full(tile))
+      lse_tile(tile, bi, std::false_type{});
+    else
+      lse_tile(tile, bi, std::true_type{});
+    gwait_loads();
+    __syncthreads();
+  }
+  // merge the four lanes of each row (lane groups gi = 0..3): log2-domain normaliser L2
+  float L2[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float M = mr[h];
+    M = fmaxf(M, __shfl_xor(M, 16, 64));
+    M = fmaxf(M, __shfl_xor(M, 32, 64));
+    float tot = ls[h] * fexp2(mr[h] - M);
+    tot += __shfl_xor(tot, 16, 64);
+    tot += __shfl_xor(tot, 32, 64);
+    L2[h] = M > kNoKey ? M + flog2(tot) : INFINITY;  // no visible block: every p is zero
+  }
+
+  // ---- sweep 2: probabilities, value sum, importance
+  int64_t jmax = -1;  // this lane's row's last candidate block (-1: text row or past the end)
+  if (isv) {
+    const int64_t jt = (dm.q0 + r) / dm.ls;
+    jmax = jt < dm.Ns ? jt : dm.Ns - 1;
+  }
+  float* imp_row = imp ? imp + ((b * dm.Tq + (rvalid ? r : 0)) * dm.Hkv + g) * dm.Ns : nullptr;
+  f32x4 O[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) O[h][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int sh_prev = 0;    // the range scale shift folded into L2
+  float rprev = 0.f;  // half share of the previous M-block's last compressed key (lane group 3's, shifted)
+  const int srcl = (l + 48) & 63;  // lane group gi - 1 (group 3 for gi = 0)
+  // one tile: per 32-key half, the scores and probabilities of its two M-blocks, the value product and
+  // the importance of their two selection blocks per lane; MASK as in sweep 1.  The value
+  // tile's range scale sh = s_tile - s_ref (<= 0) enters the probabilities' exponent; their sums
+  // over the heads are scaled back by 2^-sh for the importance.
+  auto pv_tile = [&](int tile, int bi, int sh, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    const float ct = c2_of(tile);
+    const float unscale = ldexpf(1.f, -sh);
+    // L2 - sh for this tile (L2 holds L2 - sh of the previous tile)
+#pragma unroll
+    for (int h = 0; h < G; ++h) L2[h] += (float)(sh_prev - sh);
+    sh_prev = sh;
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+      f32x4 S0[G], S1[G];
+      scores(bi, 2 * half, S0);
+      f16x8 pb[G];  // P^T operands of the half's 32 keys: M-block 2 half in slots 0..3, the next in 4..7
+      float P0[4] = {0.f, 0.f, 0.f, 0.f}, P1[4] = {0.f, 0.f, 0.f, 0.f};  // sums over the heads
+      const int lm0 = lim_of(tile, 2 * half), lm1 = lim_of(tile, 2 * half + 1);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float p = fexp2(fmaf(S0[h][j], ct, -L2[h]));
+          if constexpr (MASK) p = j < lm0 ? p : 0.f;
+          P0[j] += p;
+          pb[h][j] = (_Float16)p;
+        }
+      scores(bi, 2 * half + 1, S1);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float p = fexp2(fmaf(S1[h][j], ct, -L2[h]));
+          if constexpr (MASK) p = j < lm1 ? p : 0.f;
+          P1[j] += p;
+          pb[h][4 + j] = (_Float16)p;
+        }
+      }
+      // O^T += Vc^T P^T over the half's 32 keys: dims 16 db + c, this lane group's 8 key slots
+      const _Float16* vts = (const _Float16*)lds_at(bi, L_VT);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const int dim = 16 * db + c;
+        const f16x8 vf = *(const f16x8*)(vts + dim * CK + (((4 * half + gi) ^ (dim & 7)) << 3));
+#pragma unroll
+        for (int h = 0; h < G; ++h) O[h][db] = mfma16h(vf, pb[h], O[h][db]);
+      }
+      // importance of selection blocks 16 tile + 4 mb + gi of this lane's row, mb = 2 half, 2 half + 1
+      float impv[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const float* P = mi ? P1 : P0;
+        const float t = 0.5f * P[3] * unscale;
+        const float x = (P[0] + P[1] + P[2]) * unscale + t;
+        const float rc = __shfl(t, srcl, 64);  // t of lane group gi - 1, or of group 3 for gi = 0
+        impv[mi] = x + (gi ? rc : rprev);
+        rprev = rc;
+      }
+      if (imp_row) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+          const int64_t J = (int64_t)tile * 16 + 4 * (2 * half + mi) + gi;
+          if (J <= jmax) imp_row[J] = impv[mi];
+        }
+      }
+    }
+  };
+  const int nt2 = nvmax > 0 ? nvmax / CK + 1 : 0;
+  if (nt2 > 0) {
+    stage_k(0, 0);
+    stage_v(0, 0);
+    gwait_loads();
+  }
+  __syncthreads();
+  for (int tile = 0; tile < nt2; ++tile) {
+    const int bi = tile & 1;
+    if (tile + 1 < nt2) {
+      stage_k(tile + 1, bi ^ 1);
+      stage_v(tile + 1, bi ^ 1);
+    }
+    // fp16 range of the value tile: its probabilities times 2^(s_tile - s_ref) <= 1
+    const int sh = (int)vsc[tclamp(tile)] - s_ref;
+    if (full(tile))
+      pv_tile(tile, bi, sh, std::false_type{});
+    else
+      pv_tile(tile, bi, sh, std::true_type{});
+    gwait_loads();
+    __syncthreads();
+  }
+  // blocks up to the row's own block that no compressed block reaches
+  if (imp_row) {
+    for (int64_t J = (int64_t)nt2 * 16 + gi; J <= jmax; J += 4) imp_row[J] = 0.f;
+  }
+
+  if (!isv) return;
+  const int64_t orow = (b * dm.Tq + r) * dm.Hq + (int64_t)g * G;
+  const float oscale = ldexpf(1.f, s_ref);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int d0 = 16 * db + 4 * gi;
+      f32x4 o4 = O[h][db];
+      if (s_ref) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] *= oscale;
+      }
+      if (o_f32) *(f32x4*)(o_f32 + (orow + h) * HD + d0) = o4;
+      if (o_bf) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (bf16)o4[e];
+        *(bf16x4*)(o_bf + (orow + h) * HD + d0) = v4;
+      }
+    }
+    if (lse && gi == 0) lse[orow + h] = nv > 0 ? L2[h] * LN2_F : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Key and value tiles for cmp_group_kernel: the fp32 block sums of a 64-key tile (weights w over
+// l tokens, stride d), their range scale s (keys: the largest magnitude times 2^-s lies in
+// [2^13, 2^14); values: zero unless the largest magnitude reaches 2^14) and the sums times 2^-s in
+// fp16, at kt16_pos (keys) or vt16_slot (values).  One workgroup per
+// (b, KV head, 64-key tile) and kind: blocks [0, n) make key tiles, [n, 2n) value tiles.  A tile
+// leaves as one contiguous 16 KB run.
+__global__ void __launch_bounds__(256) compress_kv16_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
+                                                            const float* __restrict__ w_k,
+                                                            const float* __restrict__ w_v,
+                                                            unsigned char* __restrict__ out, int64_t T_len, int H,
+                                                            int l, int d, int64_t Nc, int ntv) {
+  __shared__ float ws[64];
+  __shared__ float s_max[4];
+  __shared__ __attribute__((aligned(16))) float s_v[CK * (HD + 1)];  // fp32 sums, padded rows
+  __shared__ __attribute__((aligned(16))) _Float16 s_t[TILE];
+  const Kv16Layout ly{(size_t)gridDim.x / 2};
+  const bool is_v = blockIdx.x >= ly.ntiles;
+  const int64_t id = is_v ? blockIdx.x - (int64_t)ly.ntiles : blockIdx.x;  // (b, h, tile) index
+  const int tile = (int)(id % ntv);
+  const int64_t bh = id / ntv;
+  const int h = (int)(bh % H);
+  const int64_t b = bh / H;
+  const bf16* x = is_v ? v : k;
+  const float* w = is_v ? w_v : w_k;
+  for (int m = threadIdx.x; m < l; m += blockDim.x) ws[m] = w[m];
+  __syncthreads();
+  float mx = 0.f;
+  for (int it = threadIdx.x; it < CK * (HD / 8); it += blockDim.x) {
+    const int key = it >> 4, c8 = it & 15;
+    const int64_t i = (int64_t)tile * CK + key;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (i < Nc) {
+      const bf16* src = x + ((b * T_len + i * d) * H + h) * (int64_t)HD + c8 * 8;
+      for (int m = 0; m < l; ++m) {
+        const bf16x8 u = *(const bf16x8*)(src + (int64_t)m * H * HD);
+        const float wm = ws[m];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(wm, (float)u[e], acc[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s_v[key * (HD + 1) + c8 * 8 + e] = acc[e];
+      mx = fmaxf(mx, fabsf(acc[e]));
+    }
+  }
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  const int sc = f16_range_scale(fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3])), 14, is_v);
+  for (int it = threadIdx.x; it < CK * HD; it += blockDim.x) {
+    const int key = it >> 7, dim = it & 127;
+    s_t[is_v ? vt16_slot(dim, key) : kt16_pos(key, dim)] = (_Float16)ldexpf(s_v[key * (HD + 1) + dim], -sc);
+  }
+  __syncthreads();
+  unsigned char* dst = out + (is_v ? ly.vt() : ly.kt()) + (size_t)id * TILE * 2;
+  for (int c = threadIdx.x; c < TILE / 8; c += blockDim.x) *(f16x8*)(dst + c * 16) = *(const f16x8*)(s_t + c * 8);
+  if (threadIdx.x == 0) out[(is_v ? ly.vs() : ly.ks()) + id] = (unsigned char)(int8_t)sc;
+}
+
+static size_t kv16_ntiles(const Dims& dm) { return (size_t)dm.B * dm.Hkv * ((dm.Nc + CK - 1) / CK); }
+
+size_t kv16_tiles_bytes(const Dims& dm) { return Kv16Layout{kv16_ntiles(dm)}.bytes(); }
+
+hipError_t launch_compress_kv16(const Dims& dm, const void* k, const float* w_k, const void* v, const float* w_v,
+                                void* out, hipStream_t s) {
+  if (dm.Nc <= 0 || dm.B <= 0) return hipSuccess;
+  if (dm.D != HD || dm.l > 64) return hipErrorInvalidValue;
+  const size_t n = kv16_ntiles(dm);
+  compress_kv16_kernel<<<(unsigned)(2 * n), 256, 0, s>>>((const bf16*)k, (const bf16*)v, w_k, w_v,
+                                                        (unsigned char*)out, dm.T, dm.Hkv, dm.l, dm.d, dm.Nc,
+                                                        (int)((dm.Nc + CK - 1) / CK));
+  return hipGetLastError();
+}
+
+bool cmp_group_supported(const Dims& dm) { return dm.D == HD && dm.G >= 4 && dm.G <= 7; }
+int cmp_group_rows() { return RQ; }
+
+// Row tiles [tile_lo, tile_lo + ntiles) of 64 rows.
+hipError_t launch_cmp_group(const Dims& dm, const void* q, const void* kv16, const uint8_t* vid, void* o_bf,
+                            float* o32, float* lse, float* imp, int tile_lo, int ntiles, hipStream_t s) {
+  if (ntiles <= 0 || dm.B <= 0) return hipSuccess;
+  if (!cmp_group_supported(dm) || !kv16) return hipErrorInvalidValue;
+  const size_t shm = (size_t)2 * L_BUF;
+  const int units = (int)(dm.B * dm.Hkv);
+  const dim3 grid(xcd_grid(units, ntiles)), block(NWV * 64);
+  auto go = [&](auto kernel) -> hipError_t {
+    hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    kernel<<<grid, block, shm, s>>>((const bf16*)q, (const unsigned char*)kv16, vid, (bf16*)o_bf, o32, lse, imp, dm,
+                                    tile_lo, ntiles);
+    return hipGetLastError();
+  };
+  switch (dm.G) {
+    case 4: return go(cmp_group_kernel<4>);
+    case 5: return go(cmp_group_kernel<5>);
+    case 6: return go(cmp_group_kernel<6>);
+    case 7: return go(cmp_group_kernel<7>);
+    default: return hipErrorInvalidValue;
+  }
+}

@@ -9,15 +9,13 @@ bool fast_supported(int32_t dtype, const Dims& dm);
 // Scratch bytes the MFMA selection/window path needs.
 size_t fast_sparse_workspace(const Dims& dm);
 
-// Compression branch + importance.  kh/vh: compressed keys/values (bf16).  When
-// they come from an fp32 sum: kl8/ksc the fp8 low parts and scales of the keys
-// (launch_compress_k8) and vl the bf16 low parts of the values (all NULL otherwise).
-// vt: the values come as V^T tiles from launch_compress_vt (required with low
-// parts).  o (bf16) and o32 (fp32) are optional copies of the branch output; imp
-// (optional) the block importance.
+// Compression branch + importance.  kh/vh: compressed keys/values (bf16, row-major).  When they
+// come from an fp32 sum: kl8/ksc the fp8 low parts and scales of the keys (launch_compress_k8),
+// vl the bf16 low parts of the values.  o (bf16) and o32 (fp32) are optional copies of the branch
+// output; imp (optional) the block importance.
 hipError_t launch_cmp_fast(const Dims& dm, const void* q, const void* kh, const void* kl8, const void* ksc,
                            const void* vh, const void* vl, const uint8_t* vid, void* o, float* o32, float* lse,
-                           float* imp, bool vt, hipStream_t s);
+                           float* imp, hipStream_t s);
 
 // Compressed keys split for launch_cmp_fast: bf16 high parts [B, Nc, Hkv, 128] in hi,
 // fp8 low parts (k8_lo_bytes) in lo8, their scales (k8_sc_bytes) in sc.
@@ -26,10 +24,17 @@ size_t k8_sc_bytes(const Dims& dm);
 hipError_t launch_compress_k8(const Dims& dm, const void* k, const float* w_k, void* hi, void* lo8, void* sc,
                               hipStream_t s);
 
-// Compressed values (bf16 high + low parts of the fp32 sum) as the V^T tiles the
-// compression-branch kernel stages; each part takes vt_tiles_bytes(dm) bytes.
-size_t vt_tiles_bytes(const Dims& dm);
-hipError_t launch_compress_vt(const Dims& dm, const void* v, const float* w_v, void* hi, void* lo, hipStream_t s);
+// Compression branch + importance on the group kernel (one wave per 16 rows x all 4..7 query heads
+// of a KV head), for keys and values compressed from the raw k / v: launch_compress_kv16 writes them
+// as fp16 key and value tiles with power-of-two range scales (kv16_tiles_bytes(dm) bytes), which
+// launch_cmp_group reads; 64-row tiles [tile_lo, tile_lo + ntiles).
+bool cmp_group_supported(const Dims& dm);
+int cmp_group_rows();
+size_t kv16_tiles_bytes(const Dims& dm);
+hipError_t launch_compress_kv16(const Dims& dm, const void* k, const float* w_k, const void* v, const float* w_v,
+                                void* out, hipStream_t s);
+hipError_t launch_cmp_group(const Dims& dm, const void* q, const void* kv16, const uint8_t* vid, void* o_bf,
+                            float* o32, float* lse, float* imp, int tile_lo, int ntiles, hipStream_t s);
 
 // Window branch, text rows, selection branch and the gated combine.  o_cmp is
 // fp32 when ocmp_f32, else bf16.  ws: fast_sparse_workspace(dm) bytes.  ks / vs: keys and values
