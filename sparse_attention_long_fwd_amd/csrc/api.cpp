@@ -161,8 +161,7 @@ int run_cmp(int32_t dtype, int32_t cdtype, const Dims& dm, const void* q, const 
   if (!use_fast(dtype, dm)) {
     e = launch_cmp_generic(dtype, cdtype, dm, q, kc, vc, vid, o, lse, imp, s);
   } else if (kv16) {
-    const int R = cmp_group_rows();
-    e = launch_cmp_group(dm, q, kv16, vid, o, o32, lse, imp, 0, (int)((dm.Tq + R - 1) / R), s);
+    e = launch_cmp_group(dm, q, kv16, vid, o, o32, lse, imp, s);
   } else {
     e = launch_cmp_fast(dm, q, kc, kl8, ksc, vc, vl, vid, o, o32, lse, imp, s);
   }

@@ -41,8 +41,10 @@
 
 namespace {
 constexpr int WR = 16;        // query rows per wave
-constexpr int NWV = 4;        // waves per workgroup (one per SIMD)
-constexpr int RQ = WR * NWV;  // query rows per workgroup
+constexpr int NWV = 4;        // waves per workgroup of the second sweep (one per SIMD)
+constexpr int RQ = WR * NWV;  // query rows per workgroup of the second sweep
+constexpr int NWA = 8;        // waves per workgroup of the first sweep (two per SIMD)
+constexpr int RA = WR * NWA;  // query rows per workgroup of the first sweep
 constexpr int CK = 64;        // compressed keys per tile
 constexpr int HD = 128;       // head dim
 constexpr int TILE = CK * HD;
@@ -92,13 +94,88 @@ __device__ __forceinline__ int f16_range_scale(float m, int lim, bool nonneg) {
 
 __device__ __forceinline__ void gwait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// The tiles of one (sequence b, KV head g) in the kv16 buffer.
+struct GroupTiles {
+  const _Float16* kt;  // key tiles
+  const _Float16* vt;  // value tiles
+  const uint8_t* ksc;  // key tile scales (signed bytes)
+  const uint8_t* vsc;  // value tile scales
+  int ntv;             // tiles
+  __device__ GroupTiles(const unsigned char* kv16, const Dims& dm, int64_t b, int g) {
+    ntv = (int)((dm.Nc + CK - 1) / CK);
+    const Kv16Layout ly{(size_t)dm.B * dm.Hkv * ntv};
+    const int64_t t0 = (b * dm.Hkv + g) * ntv;
+    kt = (const _Float16*)(kv16 + ly.kt()) + t0 * TILE;
+    vt = (const _Float16*)(kv16 + ly.vt()) + t0 * TILE;
+    ksc = kv16 + ly.ks() + t0;
+    vsc = kv16 + ly.vs() + t0;
+  }
+  // past the last tile (only importances of blocks no compressed key reaches are flushed there,
+  // every probability is 0): the last one
+  __device__ int clamp(int tile) const { return tile < ntv ? tile : ntv - 1; }
+};
+
+// Q of one row for every head of the group as B operands of the score products (step ks:
+// Q[row][32 ks + 8 gi .. +8]), in fp16 times 2^-eq, eq the row's range scale (the four lane groups
+// of a row share it); returns eq.
 template <int G>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ kv16, const uint8_t* __restrict__ vid,
-                 bf16* __restrict__ o_bf, float* __restrict__ o_f32, float* __restrict__ lse,
-                 float* __restrict__ imp, Dims dm, int tile_lo, int ntiles) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ int s_any, s_scale;
+__device__ __forceinline__ int load_q16(const bf16* qrow, bool rvalid, int gi, f16x8 (&qf)[G][4]) {
+  // two passes over the row (the second from cache), so that the bf16 and fp16 copies are never
+  // live together
+  float m = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 x = rvalid ? *(const bf16x8*)(qrow + h * HD + 32 * ks + 8 * gi) : zero8();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)x[e]));
+    }
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  const int eq = f16_range_scale(m, 15, false);
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 x = rvalid ? *(const bf16x8*)(qrow + h * HD + 32 * ks + 8 * gi) : zero8();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[h][ks][e] = (_Float16)ldexpf((float)x[e], -eq);
+    }
+  return eq;
+}
+
+// Scores S^T of 16-key M-block mb (keys 16 mb .. +16 of the staged key tile kts) for every head:
+// each key fragment read from LDS feeds the G heads' products.  Lane (gi, c) gets the scores of
+// keys 16 mb + 4 gi + j, j = 0..3, for row c.
+template <int G>
+__device__ __forceinline__ void scores16(const _Float16* kts, int mb, int c, int gi, const f16x8 (&qf)[G][4],
+                                         f32x4 (&S)[G]) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) S[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const f16x8 kf = *(const f16x8*)(kts + swz128(16 * mb + c, 4 * ks + gi));
+#pragma unroll
+    for (int h = 0; h < G; ++h) S[h] = mfma16h(kf, qf[h][ks], S[h]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// First sweep: the log-sum-exp of every (video row, head), written to lse (natural log; -inf for a
+// row with no visible compressed block).  Eight waves of 16 rows each (two per SIMD: no value
+// accumulators here, so a wave fits in half the register file), the key tiles staged once for 128
+// rows.  Each lane sums over its own keys in log2 units y = score c2: the sum of 2^(y - mr) against
+// a whole-number reference mr, the largest floor(y) so far.  When mr moves the sum is rescaled by
+// an exact power of two (ldexp), so every term is below 2 and no step branches (the two waves on a
+// SIMD overlap one's products with the other's exponentials).  The four lanes of a row are merged
+// at the end.
+template <int G>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NWA * 64, NWA * 64), amdgpu_waves_per_eu(2, 2)))
+cmp_lse_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ kv16, const uint8_t* __restrict__ vid,
+               float* __restrict__ lse, Dims dm, int ntiles) {
+  __shared__ __attribute__((aligned(16))) _Float16 kbuf[2][TILE];
+  __shared__ int s_any;
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, gi = l >> 4, c = l & 15;
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -106,103 +183,31 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
   if (!xcd_remap(blockIdx.x, (int)(dm.B * dm.Hkv), ntiles, &unit, &rank)) return;
   const int64_t b = unit / dm.Hkv;
   const int g = unit % dm.Hkv;
-  const int64_t rt0 = (int64_t)(tile_lo + ntiles - 1 - rank) * RQ;  // heaviest row tiles first
-  const int ntv = (int)((dm.Nc + CK - 1) / CK);
-  const Kv16Layout ly{(size_t)dm.B * dm.Hkv * ntv};
-  const int64_t tile0 = (b * dm.Hkv + g) * ntv;  // this (sequence, KV head)'s first tile
-  const _Float16* kt = (const _Float16*)(kv16 + ly.kt()) + tile0 * TILE;
-  const _Float16* vt = (const _Float16*)(kv16 + ly.vt()) + tile0 * TILE;
-  const uint8_t* ksc = kv16 + ly.ks() + tile0;
-  const uint8_t* vsc = kv16 + ly.vs() + tile0;
-
-  // skip row tiles without a video row; the largest value-tile scale of this (sequence, KV head)
-  if (tid == 0) {
-    s_any = 0;
-    s_scale = 0;
-  }
+  const int64_t rt0 = (int64_t)(ntiles - 1 - rank) * RA;  // heaviest row tiles first
+  const GroupTiles gt(kv16, dm, b, g);
+  if (tid == 0) s_any = 0;
   __syncthreads();
-  if (tid < RQ) {
+  if (tid < RA) {
     const int64_t rr = rt0 + tid;
     if (rr < dm.Tq && (!vid || vid[b * dm.Tq + rr])) s_any = 1;
   }
-  for (int i = tid; i < ntv; i += blockDim.x) {
-    const int sc = vsc[i];
-    if (sc) atomicMax(&s_scale, sc);
-  }
   __syncthreads();
   if (!s_any) return;
-  const int s_ref = s_scale;  // the value accumulators hold O 2^-s_ref
 
   const int64_t r = rt0 + WR * w + c;  // this lane's query row
   const bool rvalid = r < dm.Tq;
   const bool isv = rvalid && (!vid || vid[b * dm.Tq + r]);
   const int nv = rvalid ? (int)cmp_visible(dm.q0 + r, dm.l, dm.d, dm.Nc) : 0;
-  const int64_t rlast = (rt0 + RQ < dm.Tq ? rt0 + RQ : dm.Tq) - 1;
+  const int64_t rlast = (rt0 + RA < dm.Tq ? rt0 + RA : dm.Tq) - 1;
   const int nvmax = (int)cmp_visible(dm.q0 + rlast, dm.l, dm.d, dm.Nc);
   const int nvmin = (int)cmp_visible(dm.q0 + rt0, dm.l, dm.d, dm.Nc);
   const float c2 = dm.scale * LOG2E_F;
-
-  // Q, B operand of step ks: Q[row c][32 ks + 8 gi .. +8] for every head of the group, in fp16
-  // times 2^-eq, eq the row's range scale (the four lane groups of a row share it)
-  const bf16* qrow = q + ((b * dm.Tq + (rvalid ? r : 0)) * dm.Hq + (int64_t)g * G) * HD;
   f16x8 qf[G][4];
-  int eq;
-  {
-    bf16x8 qb[G][4];
-    float m = 0.f;
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        qb[h][ks] = rvalid ? *(const bf16x8*)(qrow + h * HD + 32 * ks + 8 * gi) : zero8();
-#pragma unroll
-        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)qb[h][ks][e]));
-      }
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
-    eq = f16_range_scale(m, 15, false);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[h][ks][e] = (_Float16)ldexpf((float)qb[h][ks][e], -eq);
-  }
-
-  auto lds_at = [&](int bi, int off) { return smem + bi * L_BUF + off; };
-  // past the last tile (only importances of blocks no compressed key reaches are flushed there,
-  // every probability is 0): restage the last one
-  auto tclamp = [&](int tile) { return tile < ntv ? tile : ntv - 1; };
+  const int eq = load_q16<G>(q + ((b * dm.Tq + (rvalid ? r : 0)) * dm.Hq + (int64_t)g * G) * HD, rvalid, gi, qf);
   auto stage_k = [&](int tile, int bi) {
-    stage_lin16k((bf16*)lds_at(bi, L_KT), (const bf16*)(kt + (int64_t)tclamp(tile) * TILE), wu, NWV, l);
+    stage_lin16k((bf16*)kbuf[bi], (const bf16*)(gt.kt + (int64_t)gt.clamp(tile) * TILE), wu, NWA, l);
   };
-  auto stage_v = [&](int tile, int bi) {
-    stage_lin16k((bf16*)lds_at(bi, L_VT), (const bf16*)(vt + (int64_t)tclamp(tile) * TILE), wu, NWV, l);
-  };
-  // log2 units per raw score unit of tile `tile`
-  auto c2_of = [&](int tile) { return ldexpf(c2, eq + (int)(int8_t)ksc[tclamp(tile)]); };
-  // Scores S^T of 16-key M-block mb (keys 16 mb .. +16 of the staged tile) for every head: each key
-  // fragment read from LDS feeds the G heads' products
-  auto scores = [&](int bi, int mb, f32x4 (&S)[G]) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) S[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const _Float16* kts = (const _Float16*)lds_at(bi, L_KT);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const f16x8 kf = *(const f16x8*)(kts + swz128(16 * mb + c, 4 * ks + gi));
-#pragma unroll
-      for (int h = 0; h < G; ++h) S[h] = mfma16h(kf, qf[h][ks], S[h]);
-    }
-  };
-  // Score register j of M-block mb of tile `tile` holds compressed key tile CK + 16 mb + 4 gi + j;
-  // it is visible when j < lim
-  auto lim_of = [&](int tile, int mb) { return nv - (tile * CK + 16 * mb + 4 * gi); };
-  auto full = [&](int tile) { return (tile + 1) * CK <= nvmin; };
 
-  // ---- sweep 1: log-sum-exp per (row, head), each lane over its own keys, in log2 units y =
-  // score c2: the sum of 2^(y - mr) against a whole-number reference mr, the largest floor(y) so
-  // far.  When mr moves the sum is rescaled by an exact power of two (ldexp), so every term is
-  // below 2 and no step branches.  The four lanes of a row are merged at the end.
   constexpr float kNoKey = -1e30f;  // reference before the first visible key (below every score)
   float mr[G], ls[G];
 #pragma unroll
@@ -226,17 +231,15 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
       mr[h] = mn;
     }
   };
-  // one tile: the products of M-block mb + 1 are issued before the exponentials of M-block mb
+  // Score register j of M-block mb of tile `tile` holds compressed key 64 tile + 16 mb + 4 gi + j
+  auto lim_of = [&](int tile, int mb) { return nv - (tile * CK + 16 * mb + 4 * gi); };
   auto lse_tile = [&](int tile, int bi, auto mask_c) {
-    const float ct = c2_of(tile);
-    f32x4 Sa[G], Sb[G];
-    scores(bi, 0, Sa);
+    const float ct = ldexpf(c2, eq + (int)(int8_t)gt.ksc[gt.clamp(tile)]);  // log2 units per raw score
 #pragma unroll
-    for (int mb = 0; mb < 4; mb += 2) {
-      scores(bi, mb + 1, Sb);
-      lse_block(Sa, ct, lim_of(tile, mb), mask_c);
-      if (mb + 2 < 4) scores(bi, mb + 2, Sa);
-      lse_block(Sb, ct, lim_of(tile, mb + 1), mask_c);
+    for (int mb = 0; mb < 4; ++mb) {
+      f32x4 S[G];
+      scores16<G>(kbuf[bi], mb, c, gi, qf, S);
+      lse_block(S, ct, lim_of(tile, mb), mask_c);
     }
   };
   const int nt1 = (nvmax + CK - 1) / CK;
@@ -248,15 +251,13 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
   for (int tile = 0; tile < nt1; ++tile) {
     const int bi = tile & 1;
     if (tile + 1 < nt1) stage_k(tile + 1, bi ^ 1);
-    if (full(tile))
+    if ((tile + 1) * CK <= nvmin)
       lse_tile(tile, bi, std::false_type{});
     else
       lse_tile(tile, bi, std::true_type{});
     gwait_loads();
     __syncthreads();
   }
-  // merge the four lanes of each row (lane groups gi = 0..3): log2-domain normaliser L2
-  float L2[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float M = mr[h];
@@ -265,8 +266,84 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
     float tot = ls[h] * fexp2(mr[h] - M);
     tot += __shfl_xor(tot, 16, 64);
     tot += __shfl_xor(tot, 32, 64);
-    L2[h] = M > kNoKey ? M + flog2(tot) : INFINITY;  // no visible block: every p is zero
+    if (isv && gi == 0)
+      lse[(b * dm.Tq + r) * dm.Hq + (int64_t)g * G + h] = M > kNoKey ? (M + flog2(tot)) * LN2_F : -INFINITY;
   }
+}
+
+// Second sweep: exact probabilities from the log-sum-exp, the value sum and the block importance.
+// Four waves of 16 rows each, one per SIMD (the value accumulators of all G heads fill the
+// accumulation registers).
+template <int G>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NWV * 64, NWV * 64), amdgpu_waves_per_eu(1, 1)))
+cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ kv16, const uint8_t* __restrict__ vid,
+                 const float* __restrict__ lse, bf16* __restrict__ o_bf, float* __restrict__ o_f32,
+                 float* __restrict__ imp, Dims dm, int ntiles) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int s_any, s_scale;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, gi = l >> 4, c = l & 15;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  int unit, rank;
+  if (!xcd_remap(blockIdx.x, (int)(dm.B * dm.Hkv), ntiles, &unit, &rank)) return;
+  const int64_t b = unit / dm.Hkv;
+  const int g = unit % dm.Hkv;
+  const int64_t rt0 = (int64_t)(ntiles - 1 - rank) * RQ;  // heaviest row tiles first
+  const GroupTiles gt(kv16, dm, b, g);
+
+  // skip row tiles without a video row; the largest value-tile scale of this (sequence, KV head)
+  if (tid == 0) {
+    s_any = 0;
+    s_scale = 0;
+  }
+  __syncthreads();
+  if (tid < RQ) {
+    const int64_t rr = rt0 + tid;
+    if (rr < dm.Tq && (!vid || vid[b * dm.Tq + rr])) s_any = 1;
+  }
+  for (int i = tid; i < gt.ntv; i += blockDim.x) {
+    const int sc = gt.vsc[i];
+    if (sc) atomicMax(&s_scale, sc);
+  }
+  __syncthreads();
+  if (!s_any) return;
+  const int s_ref = s_scale;  // the value accumulators hold O 2^-s_ref
+
+  const int64_t r = rt0 + WR * w + c;  // this lane's query row
+  const bool rvalid = r < dm.Tq;
+  const bool isv = rvalid && (!vid || vid[b * dm.Tq + r]);
+  const int nv = rvalid ? (int)cmp_visible(dm.q0 + r, dm.l, dm.d, dm.Nc) : 0;
+  const int64_t rlast = (rt0 + RQ < dm.Tq ? rt0 + RQ : dm.Tq) - 1;
+  const int nvmax = (int)cmp_visible(dm.q0 + rlast, dm.l, dm.d, dm.Nc);
+  const int nvmin = (int)cmp_visible(dm.q0 + rt0, dm.l, dm.d, dm.Nc);
+  const float c2 = dm.scale * LOG2E_F;
+
+  f16x8 qf[G][4];
+  const int eq = load_q16<G>(q + ((b * dm.Tq + (rvalid ? r : 0)) * dm.Hq + (int64_t)g * G) * HD, rvalid, gi, qf);
+
+  auto lds_at = [&](int bi, int off) { return smem + bi * L_BUF + off; };
+  auto stage_k = [&](int tile, int bi) {
+    stage_lin16k((bf16*)lds_at(bi, L_KT), (const bf16*)(gt.kt + (int64_t)gt.clamp(tile) * TILE), wu, NWV, l);
+  };
+  auto stage_v = [&](int tile, int bi) {
+    stage_lin16k((bf16*)lds_at(bi, L_VT), (const bf16*)(gt.vt + (int64_t)gt.clamp(tile) * TILE), wu, NWV, l);
+  };
+  // log2 units per raw score unit of tile `tile`
+  auto c2_of = [&](int tile) { return ldexpf(c2, eq + (int)(int8_t)gt.ksc[gt.clamp(tile)]); };
+  auto scores = [&](int bi, int mb, f32x4 (&S)[G]) {
+    scores16<G>((const _Float16*)lds_at(bi, L_KT), mb, c, gi, qf, S);
+  };
+  // Score register j of M-block mb of tile `tile` holds compressed key tile CK + 16 mb + 4 gi + j;
+  // it is visible when j < lim
+  auto lim_of = [&](int tile, int mb) { return nv - (tile * CK + 16 * mb + 4 * gi); };
+  auto full = [&](int tile) { return (tile + 1) * CK <= nvmin; };
+
+  // log2-domain normaliser of each head from the first sweep (+inf, every p zero, for rows with
+  // no visible block and rows that are not computed)
+  float L2[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    L2[h] = (isv && nv > 0) ? lse[(b * dm.Tq + r) * dm.Hq + (int64_t)g * G + h] * LOG2E_F : INFINITY;
 
   // ---- sweep 2: probabilities, value sum, importance
   int64_t jmax = -1;  // this lane's row's last candidate block (-1: text row or past the end)
@@ -302,8 +379,13 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
       f16x8 pb[G];  // P^T operands of the half's 32 keys: M-block 2 half in slots 0..3, the next in 4..7
       float P0[4] = {0.f, 0.f, 0.f, 0.f}, P1[4] = {0.f, 0.f, 0.f, 0.f};  // sums over the heads
       const int lm0 = lim_of(tile, 2 * half), lm1 = lim_of(tile, 2 * half + 1);
+      // the second M-block's products, head by head beside the first M-block's probabilities
+      const _Float16* kts = (const _Float16*)lds_at(bi, L_KT);
+      f16x8 k1[4];
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+      for (int ks = 0; ks < 4; ++ks) k1[ks] = *(const f16x8*)(kts + swz128(16 * (2 * half + 1) + c, 4 * ks + gi));
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float p = fexp2(fmaf(S0[h][j], ct, -L2[h]));
@@ -311,7 +393,10 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
           P0[j] += p;
           pb[h][j] = (_Float16)p;
         }
-      scores(bi, 2 * half + 1, S1);
+        S1[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) S1[h] = mfma16h(k1[ks], qf[h][ks], S1[h]);
+      }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
 #pragma unroll
@@ -365,7 +450,7 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
       stage_v(tile + 1, bi ^ 1);
     }
     // fp16 range of the value tile: its probabilities times 2^(s_tile - s_ref) <= 1
-    const int sh = (int)vsc[tclamp(tile)] - s_ref;
+    const int sh = (int)gt.vsc[gt.clamp(tile)] - s_ref;
     if (full(tile))
       pv_tile(tile, bi, sh, std::false_type{});
     else
@@ -399,7 +484,6 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
         *(bf16x4*)(o_bf + (orow + h) * HD + d0) = v4;
       }
     }
-    if (lse && gi == 0) lse[orow + h] = nv > 0 ? L2[h] * LN2_F : -INFINITY;
   }
 }
 
@@ -480,28 +564,30 @@ hipError_t launch_compress_kv16(const Dims& dm, const void* k, const float* w_k,
 }
 
 bool cmp_group_supported(const Dims& dm) { return dm.D == HD && dm.G >= 4 && dm.G <= 7; }
-int cmp_group_rows() { return RQ; }
 
-// Row tiles [tile_lo, tile_lo + ntiles) of 64 rows.
 hipError_t launch_cmp_group(const Dims& dm, const void* q, const void* kv16, const uint8_t* vid, void* o_bf,
-                            float* o32, float* lse, float* imp, int tile_lo, int ntiles, hipStream_t s) {
-  if (ntiles <= 0 || dm.B <= 0) return hipSuccess;
-  if (!cmp_group_supported(dm) || !kv16) return hipErrorInvalidValue;
+                            float* o32, float* lse, float* imp, hipStream_t s) {
+  if (dm.Tq <= 0 || dm.B <= 0) return hipSuccess;
+  if (!cmp_group_supported(dm) || !kv16 || !lse) return hipErrorInvalidValue;
   const size_t shm = (size_t)2 * L_BUF;
   const int units = (int)(dm.B * dm.Hkv);
-  const dim3 grid(xcd_grid(units, ntiles)), block(NWV * 64);
-  auto go = [&](auto kernel) -> hipError_t {
-    hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  const int ta = (int)((dm.Tq + RA - 1) / RA), tb = (int)((dm.Tq + RQ - 1) / RQ);
+  auto go = [&](auto lse_kernel, auto kernel) -> hipError_t {
+    lse_kernel<<<dim3(xcd_grid(units, ta)), dim3(NWA * 64), 0, s>>>((const bf16*)q, (const unsigned char*)kv16, vid,
+                                                                    lse, dm, ta);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    kernel<<<grid, block, shm, s>>>((const bf16*)q, (const unsigned char*)kv16, vid, (bf16*)o_bf, o32, lse, imp, dm,
-                                    tile_lo, ntiles);
+    e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    kernel<<<dim3(xcd_grid(units, tb)), dim3(NWV * 64), shm, s>>>((const bf16*)q, (const unsigned char*)kv16, vid,
+                                                                  lse, (bf16*)o_bf, o32, imp, dm, tb);
     return hipGetLastError();
   };
   switch (dm.G) {
-    case 4: return go(cmp_group_kernel<4>);
-    case 5: return go(cmp_group_kernel<5>);
-    case 6: return go(cmp_group_kernel<6>);
-    case 7: return go(cmp_group_kernel<7>);
+    case 4: return go(cmp_lse_kernel<4>, cmp_group_kernel<4>);
+    case 5: return go(cmp_lse_kernel<5>, cmp_group_kernel<5>);
+    case 6: return go(cmp_lse_kernel<6>, cmp_group_kernel<6>);
+    case 7: return go(cmp_lse_kernel<7>, cmp_group_kernel<7>);
     default: return hipErrorInvalidValue;
   }
 }

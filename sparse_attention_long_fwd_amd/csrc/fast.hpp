@@ -27,14 +27,13 @@ hipError_t launch_compress_k8(const Dims& dm, const void* k, const float* w_k, v
 // Compression branch + importance on the group kernel (one wave per 16 rows x all 4..7 query heads
 // of a KV head), for keys and values compressed from the raw k / v: launch_compress_kv16 writes them
 // as fp16 key and value tiles with power-of-two range scales (kv16_tiles_bytes(dm) bytes), which
-// launch_cmp_group reads; 64-row tiles [tile_lo, tile_lo + ntiles).
+// launch_cmp_group reads.  lse (required) receives the log-sum-exp of the video rows.
 bool cmp_group_supported(const Dims& dm);
-int cmp_group_rows();
 size_t kv16_tiles_bytes(const Dims& dm);
 hipError_t launch_compress_kv16(const Dims& dm, const void* k, const float* w_k, const void* v, const float* w_v,
                                 void* out, hipStream_t s);
 hipError_t launch_cmp_group(const Dims& dm, const void* q, const void* kv16, const uint8_t* vid, void* o_bf,
-                            float* o32, float* lse, float* imp, int tile_lo, int ntiles, hipStream_t s);
+                            float* o32, float* lse, float* imp, hipStream_t s);
 
 // Window branch, text rows, selection branch and the gated combine.  o_cmp is
 // fp32 when ocmp_f32, else bf16.  ws: fast_sparse_workspace(dm) bytes.  ks / vs: keys and values
