@@ -183,11 +183,25 @@ int32_t nsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t
  * q_start = kv_len - 1 with the compressed cache passed in.
  * out is required; o_cmp / o_slc / o_swa / block_idx_out may be NULL (when
  * given they receive the branch outputs and the chosen blocks of the video
- * rows).  workspace: nsa_hybrid_layer_workspace_size() bytes of device memory;
- * the size depends on the kernels the call dispatches to, so query it after
- * any nsa_set_force_generic change.
+ * rows).  workspace: device scratch; the size depends on the kernels the call
+ * dispatches to, so query it after any nsa_set_force_generic change.
+ * Row chunks: a prefill on the MFMA path (bf16, head_dim 128, cmp_block 32 /
+ * stride 16, sel_block 64, 4..8 query heads per KV head) may run as passes
+ * over chunks of query rows.  Every stage except the compression of K / V is
+ * independent across rows, so the results are bit-identical to one pass; each
+ * batch element's K / V are compressed once.  The call takes the largest chunk
+ * (all rows, else a multiple of 64) whose scratch fits workspace_bytes, and
+ * fails with NSA_ERR_WORKSPACE_TOO_SMALL when not even 64 rows fit (any
+ * other dispatch needs the one-pass size).
+ * nsa_hybrid_layer_workspace_size_rows: the scratch when at most
+ * rows_per_chunk query rows run in one pass (0: all rows; < 0: returns 0).
+ * nsa_hybrid_layer_workspace_size: the size for the default chunk, the
+ * largest whose scratch stays within 7 GiB (all rows when they fit).
+ * Both return 0 for invalid arguments.
  */
 size_t nsa_hybrid_layer_workspace_size(const nsa_shape* shape, const nsa_params* params, int32_t dtype);
+size_t nsa_hybrid_layer_workspace_size_rows(const nsa_shape* shape, const nsa_params* params, int32_t dtype,
+                                            int64_t rows_per_chunk);
 int32_t nsa_hybrid_layer_fwd(const void* q, const void* k, const void* v, const void* k_cmp_in,
                              const void* v_cmp_in, const float* w_k, const float* w_v, const float* gates,
                              const uint8_t* is_video, int32_t dtype, const nsa_shape* shape,

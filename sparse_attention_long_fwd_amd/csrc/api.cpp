@@ -22,11 +22,16 @@ std::atomic<int> g_force_generic{0};
 // call records a HIP event on its stream at each phase boundary.
 constexpr int kMaxMarks = 8;
 hipEvent_t g_marks[kMaxMarks];
-int g_nmarks = 0;        // events recorded by the last profiled call
+int g_nmarks = 0;        // events recorded by the current pass of a profiled call
 bool g_profiling = false;
+// A layer call that runs in row chunks adds each pass's phase times here (g_nacc phases; 0 when the
+// last call ran in one pass).
+float g_acc[kMaxMarks];
+int g_nacc = 0;
 void prof_mark(hipStream_t s) {
   if (g_profiling && g_nmarks < kMaxMarks) (void)hipEventRecord(g_marks[g_nmarks++], s);
 }
+
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -38,6 +43,24 @@ int fail(int code, const char* fmt, ...) {
 
 int hip_fail(hipError_t e, const char* where) {
   return fail(NSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// Adds the phase times of the pass just recorded to g_acc (waits for its last event).
+int32_t prof_accumulate() {
+  if (g_nmarks < 2) return NSA_OK;
+  hipError_t e = hipEventSynchronize(g_marks[g_nmarks - 1]);
+  if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+  if (g_nacc == 0)
+    for (int i = 0; i < kMaxMarks; ++i) g_acc[i] = 0.f;
+  for (int i = 0; i + 1 < g_nmarks; ++i) {
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, g_marks[i], g_marks[i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    g_acc[i] += ms;
+  }
+  g_nacc = g_nmarks - 1;
+  g_nmarks = 0;
+  return NSA_OK;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -150,6 +173,69 @@ LayerWs layer_ws(const Dims& dm, int32_t dtype) {
   return w;
 }
 
+// Row chunking of the layer.  Every stage is independent across query rows except the compression
+// of K / V, so a prefill on the MFMA path may run as passes over chunks of rows: per batch element,
+// the compression once, then each chunk's rows with q_start moved to the chunk (bit-identical
+// results).  The per-row scratch (fp32 branch outputs, importance, selection partials) then covers
+// one chunk only.  Chunks are multiples of 64 rows; decode (one row) never splits.
+constexpr int64_t kChunkAlign = 64;
+constexpr size_t kDefaultWsCap = (size_t)7 << 30;  // default workspace bound of the layer
+
+bool can_chunk(int32_t dtype, const Dims& dm) { return use_fast(dtype, dm) && !decode_supported(dm); }
+
+// Rows of the chunk a pass covers when at most `rows` rows run together (0: all).
+int64_t chunk_rows(const Dims& dm, int32_t dtype, int64_t rows) {
+  if (rows <= 0 || rows >= dm.Tq || !can_chunk(dtype, dm)) return dm.Tq;
+  return rows < kChunkAlign ? kChunkAlign : rows / kChunkAlign * kChunkAlign;
+}
+
+// The shape a chunk pass is sized for: one batch element, r rows, placed last in the sequence.
+// Some scratch grows with how far the rows reach (the key splits of long text rows in the window
+// pass follow q_start + rows), so the last chunk is the largest.
+Dims chunk_dims(const Dims& dm, int64_t r) {
+  Dims c = dm;
+  c.B = 1;
+  c.Tq = r;
+  c.q0 = dm.q0 + dm.Tq - r;
+  return c;
+}
+
+// Workspace of the layer when at most `rows` query rows run in one pass.
+size_t layer_ws_rows(const Dims& dm, int32_t dtype, int64_t rows) {
+  const int64_t r = chunk_rows(dm, dtype, rows);
+  if (r >= dm.Tq) return layer_ws(dm, dtype).total;
+  return layer_ws(chunk_dims(dm, r), dtype).total;
+}
+
+// True when every region of `need` fits the corresponding region of the carve `w`.
+bool ws_fits(const LayerWs& need, const LayerWs& w) {
+  return need.kc <= w.kc && need.vc <= w.vc && need.kv16 <= w.kv16 && need.o_cmp <= w.o_cmp &&
+         need.lse <= w.lse && need.imp <= w.imp && need.idx <= w.idx && need.o_swa <= w.o_swa &&
+         need.sparse <= w.sparse && need.dec <= w.dec;
+}
+
+// The largest chunk (all rows, else a multiple of 64) whose workspace fits `bytes`; 0 if none does.
+int64_t fit_chunk_rows(const Dims& dm, int32_t dtype, size_t bytes) {
+  if (layer_ws_rows(dm, dtype, 0) <= bytes) return dm.Tq;
+  if (!can_chunk(dtype, dm) || layer_ws_rows(dm, dtype, kChunkAlign) > bytes) return 0;
+  int64_t lo = 1, hi = (dm.Tq - 1) / kChunkAlign;  // in units of 64 rows; lo fits
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (layer_ws_rows(dm, dtype, mid * kChunkAlign) <= bytes)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo * kChunkAlign;
+}
+
+// Default: every row in one pass when that needs at most kDefaultWsCap bytes, else the largest
+// chunk that stays within it.
+int64_t default_chunk_rows(const Dims& dm, int32_t dtype) {
+  const int64_t r = fit_chunk_rows(dm, dtype, kDefaultWsCap);
+  return r > 0 ? r : chunk_rows(dm, dtype, kChunkAlign);
+}
+
 // kc/vc: compressed keys/values (bf16 high parts on the MFMA path, or cdtype on the generic path);
 // kl8 / ksc / vl: on the MFMA path when the layer compressed them itself, the keys' fp8 low parts
 // and their scales and the values' bf16 low parts; kv16: instead of all these, the group kernel's
@@ -235,7 +321,13 @@ int32_t nsa_profile_enable(int32_t on) {
 
 int32_t nsa_profile_read(float* ms, int32_t max_phases) {
   g_err[0] = 0;
-  if (!g_profiling || g_nmarks < 2) return 0;
+  if (!g_profiling) return 0;
+  if (g_nacc > 0) {
+    int n = 0;
+    for (; n < g_nacc && n < max_phases; ++n) ms[n] = g_acc[n];
+    return n;
+  }
+  if (g_nmarks < 2) return 0;
   hipError_t e = hipEventSynchronize(g_marks[g_nmarks - 1]);
   if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
   int n = 0;
@@ -333,47 +425,51 @@ int32_t nsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t
                     (hipStream_t)stream);
 }
 
+size_t nsa_hybrid_layer_workspace_size_rows(const nsa_shape* shape, const nsa_params* params, int32_t dtype,
+                                            int64_t rows_per_chunk) {
+  Dims dm;
+  if (check_dims(shape, params, dtype, &dm, true) != NSA_OK) return 0;
+  if (rows_per_chunk < 0) return 0;
+  return layer_ws_rows(dm, dtype, rows_per_chunk);
+}
+
 size_t nsa_hybrid_layer_workspace_size(const nsa_shape* shape, const nsa_params* params, int32_t dtype) {
   Dims dm;
   if (check_dims(shape, params, dtype, &dm, true) != NSA_OK) return 0;
-  return layer_ws(dm, dtype).total;
+  return layer_ws_rows(dm, dtype, default_chunk_rows(dm, dtype));
 }
 
 }  // extern "C"
 
 namespace {
 
-// The whole layer (nsa_hybrid_layer_fwd and its per-branch K/V form).
-int32_t layer_fwd(const void* q, const BranchKV& kv, const void* k_cmp_in, const void* v_cmp_in,
-                  const float* w_k, const float* w_v, const float* gates, const uint8_t* is_video, int32_t dtype,
-                  const nsa_shape* shape, const nsa_params* params, void* out, void* o_cmp, void* o_slc,
-                  void* o_swa, int32_t* block_idx_out, void* workspace, size_t workspace_bytes, void* stream) {
-  g_err[0] = 0;
-  Dims dm;
-  int st = check_dims(shape, params, dtype, &dm, true);
-  if (st != NSA_OK) return st;
-  if (!out) return fail(NSA_ERR_INVALID_ARG, "out must not be NULL");
-  if ((k_cmp_in == nullptr) != (v_cmp_in == nullptr))
-    return fail(NSA_ERR_INVALID_ARG, "give both k_cmp_in and v_cmp_in, or neither");
-  if (dm.B == 0 || dm.Tq == 0) return NSA_OK;
-  // the compression's keys / values are not read when the compressed cache is given
-  if (!q || (!k_cmp_in && (!kv.kc || !kv.vc)) || !kv.ks || !kv.vs || !kv.kw || !kv.vw || !gates)
-    return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
-  if (!k_cmp_in && dm.Nc > 0 && (!w_k || !w_v)) return fail(NSA_ERR_INVALID_ARG, "NULL compression weights");
-  if (!aligned16(q) || !aligned16(kv.kc) || !aligned16(kv.vc) || !aligned16(kv.ks) || !aligned16(kv.vs) ||
-      !aligned16(kv.kw) || !aligned16(kv.vw) || !aligned16(out) || !aligned16(o_cmp) || !aligned16(o_slc) ||
-      !aligned16(o_swa) || !aligned16(k_cmp_in) || !aligned16(v_cmp_in) || !aligned16(workspace))
-    return fail(NSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
-  // the decode kernels score a block once for the selection and the window branch
-  if (use_decode(dtype, dm) && !(kv.ks == kv.kw && kv.vs == kv.vw))
-    return fail(NSA_ERR_UNSUPPORTED, "one query row per sequence needs one K/V for selection and window");
-  if (!use_fast(dtype, dm) && dm.Ns > 16384)
-    return fail(NSA_ERR_UNSUPPORTED, "generic kernels handle at most 16384 selection blocks");
-  const LayerWs w = layer_ws(dm, dtype);
-  if (workspace_bytes < w.total)
-    return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, w.total);
-  if (!workspace) return fail(NSA_ERR_INVALID_ARG, "NULL workspace");
-  hipStream_t s = (hipStream_t)stream;
+// The tensors of one layer pass.
+struct LayerIO {
+  const void* q;
+  BranchKV kv;
+  const void *kc_in, *vc_in;
+  const float* gates;
+  const uint8_t* vid;
+  void *out, *o_cmp, *o_slc, *o_swa;
+  int32_t* idx_out;
+};
+
+// One pass of the layer over dm's rows with the workspace carved as w.  compress = false: the
+// compressed K / V of an earlier pass of the same batch element are still in the workspace.
+int32_t layer_pass(const Dims& dm, int32_t dtype, const LayerIO& io, const float* w_k, const float* w_v,
+                   const LayerWs& w, void* workspace, bool compress, hipStream_t s) {
+  const void* q = io.q;
+  const BranchKV& kv = io.kv;
+  const void* k_cmp_in = io.kc_in;
+  const void* v_cmp_in = io.vc_in;
+  const float* gates = io.gates;
+  const uint8_t* is_video = io.vid;
+  void* out = io.out;
+  void* o_cmp = io.o_cmp;
+  void* o_slc = io.o_slc;
+  void* o_swa = io.o_swa;
+  int32_t* block_idx_out = io.idx_out;
+  int st;
   char* p = (char*)workspace;
   void* kc = p;
   p += w.kc;
@@ -412,11 +508,11 @@ int32_t layer_fwd(const void* q, const BranchKV& kv, const void* k_cmp_in, const
     void* kl = fast ? (char*)kc + round_up((size_t)dm.B * dm.Nc * dm.Hkv * dm.D * 2) : nullptr;
     void* vl = fast ? (char*)vc + w.vc / 2 : nullptr;
     void* ksc = k8 ? (char*)kl + round_up(k8_lo_bytes(dm)) : nullptr;
-    hipError_t e;
+    hipError_t e = hipSuccess;
     if (kv16) {
-      e = launch_compress_kv16(dm, kv.kc, w_k, kv.vc, w_v, kv16, s);
+      if (compress) e = launch_compress_kv16(dm, kv.kc, w_k, kv.vc, w_v, kv16, s);
       kl = vl = nullptr;
-    } else {
+    } else if (compress) {
       e = k8 ? launch_compress_k8(dm, kv.kc, w_k, kc, kl, ksc, s)
              : launch_compress(dtype, fast ? 2 : 1, kv.kc, w_k, kc, kl, dm.B, dm.T, dm.Hkv, dm.D, dm.l, dm.d, dm.Nc,
                                s);
@@ -485,6 +581,94 @@ int32_t layer_fwd(const void* q, const BranchKV& kv, const void* k_cmp_in, const
   }
   void* oswa = o_swa ? o_swa : oswa_ws;
   return run_sparse(dtype, dm, q, kv, idx, is_video, ocmp, false, gates, out, o_slc, oswa, sparse_ws_ptr, s);
+}
+
+// The whole layer (nsa_hybrid_layer_fwd and its per-branch K/V form).
+int32_t layer_fwd(const void* q, const BranchKV& kv, const void* k_cmp_in, const void* v_cmp_in,
+                  const float* w_k, const float* w_v, const float* gates, const uint8_t* is_video, int32_t dtype,
+                  const nsa_shape* shape, const nsa_params* params, void* out, void* o_cmp, void* o_slc,
+                  void* o_swa, int32_t* block_idx_out, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  Dims dm;
+  int st = check_dims(shape, params, dtype, &dm, true);
+  if (st != NSA_OK) return st;
+  if (!out) return fail(NSA_ERR_INVALID_ARG, "out must not be NULL");
+  if ((k_cmp_in == nullptr) != (v_cmp_in == nullptr))
+    return fail(NSA_ERR_INVALID_ARG, "give both k_cmp_in and v_cmp_in, or neither");
+  if (dm.B == 0 || dm.Tq == 0) return NSA_OK;
+  // the compression's keys / values are not read when the compressed cache is given
+  if (!q || (!k_cmp_in && (!kv.kc || !kv.vc)) || !kv.ks || !kv.vs || !kv.kw || !kv.vw || !gates)
+    return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!k_cmp_in && dm.Nc > 0 && (!w_k || !w_v)) return fail(NSA_ERR_INVALID_ARG, "NULL compression weights");
+  if (!aligned16(q) || !aligned16(kv.kc) || !aligned16(kv.vc) || !aligned16(kv.ks) || !aligned16(kv.vs) ||
+      !aligned16(kv.kw) || !aligned16(kv.vw) || !aligned16(out) || !aligned16(o_cmp) || !aligned16(o_slc) ||
+      !aligned16(o_swa) || !aligned16(k_cmp_in) || !aligned16(v_cmp_in) || !aligned16(workspace))
+    return fail(NSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  // the decode kernels score a block once for the selection and the window branch
+  if (use_decode(dtype, dm) && !(kv.ks == kv.kw && kv.vs == kv.vw))
+    return fail(NSA_ERR_UNSUPPORTED, "one query row per sequence needs one K/V for selection and window");
+  if (!use_fast(dtype, dm) && dm.Ns > 16384)
+    return fail(NSA_ERR_UNSUPPORTED, "generic kernels handle at most 16384 selection blocks");
+  if (!workspace) return fail(NSA_ERR_INVALID_ARG, "NULL workspace");
+  int64_t rows = fit_chunk_rows(dm, dtype, workspace_bytes);
+  if (rows == 0)
+    return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes,
+                layer_ws_rows(dm, dtype, kChunkAlign));
+  hipStream_t s = (hipStream_t)stream;
+  const LayerIO io{q, kv, k_cmp_in, v_cmp_in, gates, is_video, out, o_cmp, o_slc, o_swa, block_idx_out};
+  g_nacc = 0;
+  if (rows >= dm.Tq) return layer_pass(dm, dtype, io, w_k, w_v, layer_ws(dm, dtype), workspace, true, s);
+  // as few chunks as fit, of equal size (a multiple of 64 rows, at most `rows`)
+  {
+    const int64_t nch = (dm.Tq + rows - 1) / rows;
+    const int64_t even = ((dm.Tq + nch - 1) / nch + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+    rows = even < rows ? even : rows;
+  }
+
+  // Row chunks of at most `rows` rows, one batch element at a time (the rows of one element are
+  // contiguous in every [B, q_len, ...] tensor).
+  Dims c = chunk_dims(dm, rows);
+  const LayerWs w = layer_ws(c, dtype);
+  // every chunk's scratch within the carve, checked before the first launch
+  for (int64_t r0 = 0; r0 < dm.Tq; r0 += rows) {
+    c.Tq = dm.Tq - r0 < rows ? dm.Tq - r0 : rows;
+    c.q0 = dm.q0 + r0;
+    if (!ws_fits(layer_ws(c, dtype), w))
+      return fail(NSA_ERR_UNSUPPORTED, "internal: scratch of rows %lld..%lld exceeds its chunk layout",
+                  (long long)r0, (long long)(r0 + c.Tq));
+  }
+  const int64_t qrow = (int64_t)dm.Hq * dm.D * esize(dtype);  // bytes per query row of q / out / o_*
+  auto off = [](const void* p, int64_t bytes) -> const void* { return p ? (const char*)p + bytes : nullptr; };
+  auto offm = [](void* p, int64_t bytes) -> void* { return p ? (char*)p + bytes : nullptr; };
+  for (int64_t b = 0; b < dm.B; ++b) {
+    const int64_t kvb = b * dm.T * dm.Hkv * dm.D * esize(dtype);
+    const int64_t kcb = b * dm.Nc * dm.Hkv * dm.D * esize(dtype);
+    for (int64_t r0 = 0; r0 < dm.Tq; r0 += rows) {
+      c.Tq = dm.Tq - r0 < rows ? dm.Tq - r0 : rows;
+      c.q0 = dm.q0 + r0;
+      const int64_t rb = b * dm.Tq + r0;  // row index into [B, q_len, ...]
+      LayerIO ic;
+      ic.q = off(q, rb * qrow);
+      ic.kv = BranchKV{off(kv.kc, kvb), off(kv.vc, kvb), off(kv.ks, kvb), off(kv.vs, kvb), off(kv.kw, kvb),
+                       off(kv.vw, kvb)};
+      ic.kc_in = off(k_cmp_in, kcb);
+      ic.vc_in = off(v_cmp_in, kcb);
+      ic.gates = gates + rb * dm.Hq * 3;
+      ic.vid = is_video ? is_video + rb : nullptr;
+      ic.out = offm(out, rb * qrow);
+      ic.o_cmp = offm(o_cmp, rb * qrow);
+      ic.o_slc = offm(o_slc, rb * qrow);
+      ic.o_swa = offm(o_swa, rb * qrow);
+      ic.idx_out = block_idx_out ? block_idx_out + rb * dm.Hkv * dm.n : nullptr;
+      st = layer_pass(c, dtype, ic, w_k, w_v, w, workspace, r0 == 0, s);
+      if (st != NSA_OK) return st;
+      if (g_profiling) {
+        st = prof_accumulate();
+        if (st != NSA_OK) return st;
+      }
+    }
+  }
+  return NSA_OK;
 }
 
 }  // namespace

@@ -56,6 +56,7 @@ EXPORTS = {
     "nsa_sparse_attn_workspace_size": (_SZ, [_SH, _PR, _I32]),
     "nsa_sparse_attn_fwd": (_I32, [_P, _P, _P, _I32, _SH, _PR, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "nsa_hybrid_layer_workspace_size": (_SZ, [_SH, _PR, _I32]),
+    "nsa_hybrid_layer_workspace_size_rows": (_SZ, [_SH, _PR, _I32, _I64]),
     "nsa_hybrid_layer_fwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _SH, _PR, _P, _P, _P, _P, _P, _P,
                                     _SZ, _P]),
     "nsa_decode_workspace_size": (_SZ, [_SH, _PR, _I32]),
@@ -226,15 +227,28 @@ def nsa_hybrid_layer_workspace_size(shape: NsaShape, params: NsaParams, dtype_co
     return int(lib().nsa_hybrid_layer_workspace_size(ctypes.byref(shape), ctypes.byref(params), dtype_code))
 
 
+def nsa_hybrid_layer_workspace_size_rows(shape: NsaShape, params: NsaParams, dtype_code: int,
+                                         rows_per_chunk: int) -> int:
+    return int(lib().nsa_hybrid_layer_workspace_size_rows(ctypes.byref(shape), ctypes.byref(params), dtype_code,
+                                                          rows_per_chunk))
+
+
+def _layer_workspace(shape, params, dt, rows_per_chunk, device):
+    n = (nsa_hybrid_layer_workspace_size(shape, params, dt) if rows_per_chunk is None else
+         nsa_hybrid_layer_workspace_size_rows(shape, params, dt, rows_per_chunk))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
 def nsa_hybrid_layer_fwd(q, k, v, gates, shape: NsaShape, params: NsaParams, w_k=None, w_v=None, k_cmp_in=None,
                          v_cmp_in=None, is_video=None, out=None, o_cmp=None, o_slc=None, o_swa=None,
-                         block_idx_out=None, workspace=None, stream=None):
+                         block_idx_out=None, workspace=None, stream=None, rows_per_chunk=None):
+    """rows_per_chunk (when no workspace is given): size the workspace for passes of at most that many
+    rows (0: one pass); None: the library's default size."""
     dt = _dtype_code(q)
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
-        workspace = torch.empty(nsa_hybrid_layer_workspace_size(shape, params, dt), dtype=torch.uint8,
-                                device=q.device)
+        workspace = _layer_workspace(shape, params, dt, rows_per_chunk, q.device)
     _check(lib().nsa_hybrid_layer_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cmp_in), _ptr(v_cmp_in), _ptr(w_k),
                                       _ptr(w_v), _ptr(gates), _ptr(is_video), dt, ctypes.byref(shape),
                                       ctypes.byref(params), _ptr(out), _ptr(o_cmp), _ptr(o_slc), _ptr(o_swa),
@@ -312,15 +326,15 @@ def nsa_gate_proj(x, w_g, b_g=None, gates=None, stream=None):
 
 def nsa_hybrid_layer_fwd_branch_kv(q, kv_c, kv_s, kv_w, gates, shape: NsaShape, params: NsaParams, w_k=None,
                                    w_v=None, k_cmp_in=None, v_cmp_in=None, is_video=None, out=None, o_cmp=None,
-                                   o_slc=None, o_swa=None, block_idx_out=None, workspace=None, stream=None):
+                                   o_slc=None, o_swa=None, block_idx_out=None, workspace=None, stream=None,
+                                   rows_per_chunk=None):
     """The layer with keys / values per branch: kv_c (compression), kv_s (selection), kv_w (window and
-    text rows), each a (k, v) pair."""
+    text rows), each a (k, v) pair; rows_per_chunk as for nsa_hybrid_layer_fwd."""
     dt = _dtype_code(q)
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
-        workspace = torch.empty(nsa_hybrid_layer_workspace_size(shape, params, dt), dtype=torch.uint8,
-                                device=q.device)
+        workspace = _layer_workspace(shape, params, dt, rows_per_chunk, q.device)
     _check(lib().nsa_hybrid_layer_fwd_branch_kv(
         _ptr(q), _ptr(kv_c[0]), _ptr(kv_c[1]), _ptr(kv_s[0]), _ptr(kv_s[1]), _ptr(kv_w[0]), _ptr(kv_w[1]),
         _ptr(k_cmp_in), _ptr(v_cmp_in), _ptr(w_k), _ptr(w_v), _ptr(gates), _ptr(is_video), dt, ctypes.byref(shape),

@@ -233,3 +233,45 @@ def test_backward_validates_first():
     need = nsa.nsa_hybrid_layer_bwd_workspace_size(_shape(), pr, nsa.NSA_BF16)
     assert need > 0 and call(_shape(), ws=need - 1) == nsa.NSA_ERR_WORKSPACE_TOO_SMALL
     assert call(_shape(q_len=0)) == nsa.NSA_OK                        # no rows: nothing launched
+
+
+def test_layer_workspace_rows():
+    """Row chunks: at 128K the default workspace stays within 7 GiB (one pass needs about 24 GB), the
+    size grows with the chunk, and a workspace below the 64-row size is refused before any launch."""
+    sh = _dshape(batch=1, q_len=131072, kv_len=131072)
+    pr = _params(top_n=16, window=512)
+    bf = nsa.NSA_BF16
+    full = nsa.nsa_hybrid_layer_workspace_size_rows(sh, pr, bf, 0)
+    dflt = nsa.nsa_hybrid_layer_workspace_size(sh, pr, bf)
+    assert full > 16 << 30 and 0 < dflt <= 7 << 30
+    sizes = [nsa.nsa_hybrid_layer_workspace_size_rows(sh, pr, bf, r) for r in (64, 1000, 1024, 32768, 131072)]
+    assert sizes[0] < sizes[2] < sizes[3] < sizes[4] == full
+    assert sizes[1] == nsa.nsa_hybrid_layer_workspace_size_rows(sh, pr, bf, 960)   # chunks are multiples of 64
+    assert nsa.nsa_hybrid_layer_workspace_size_rows(sh, pr, bf, -1) == 0
+    L = nsa.lib()
+    st = L.nsa_hybrid_layer_fwd(FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, bf, ctypes.byref(sh),
+                                ctypes.byref(pr), FAKE, None, None, None, None, FAKE, sizes[0] - 1, None)
+    assert st == nsa.NSA_ERR_WORKSPACE_TOO_SMALL and "workspace" in nsa.last_error()
+    # the generic path and decode run in one pass: their sizes do not depend on the chunk
+    f32 = nsa.NSA_F32
+    small = _dshape(batch=1, q_len=4096, kv_len=4096)
+    assert (nsa.nsa_hybrid_layer_workspace_size_rows(small, pr, f32, 64) ==
+            nsa.nsa_hybrid_layer_workspace_size_rows(small, pr, f32, 0))
+    dec = _dshape(batch=4, q_len=1, kv_len=8192, q_start=8191)
+    assert (nsa.nsa_hybrid_layer_workspace_size_rows(dec, pr, bf, 64) ==
+            nsa.nsa_hybrid_layer_workspace_size(dec, pr, bf))
+
+
+@pytest.mark.parametrize("T,B,q0,rows", [(131072, 1, 0, 40960), (131072, 1, 0, 1024), (36352, 2, 0, 4096),
+                                         (9000, 1, 0, 1024), (70000, 1, 5000, 8192)])
+def test_layer_chunk_workspace_covers_every_chunk(T, B, q0, rows):
+    """The chunked workspace must hold what every chunk needs as a call of its own (rows placed where
+    the chunk sits: scratch such as the key splits of long text rows grows with the position)."""
+    pr = _params(top_n=16, window=512)
+    bf = nsa.NSA_BF16
+    sh = _dshape(batch=B, q_len=T - q0, kv_len=T, q_start=q0)
+    carve = nsa.nsa_hybrid_layer_workspace_size_rows(sh, pr, bf, rows)
+    for r0 in range(0, T - q0, rows):
+        n = min(rows, T - q0 - r0)
+        one = _dshape(batch=1, q_len=n, kv_len=T, q_start=q0 + r0)
+        assert nsa.nsa_hybrid_layer_workspace_size_rows(one, pr, bf, 0) <= carve, (r0, n)
