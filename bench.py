@@ -30,16 +30,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # sources of each timed phase's main kernel (a counter record holds only while they are unchanged)
 PHASE_SOURCES = {
-    "cmp_attn_importance": ["sparse_attention_long_fwd_amd/csrc/cmp_fast.hip",
+    "cmp_attn_importance": ["sparse_attention_long_fwd_amd/csrc/cmp_group.hip",
                             "sparse_attention_long_fwd_amd/csrc/fast_common.hpp",
                             "sparse_attention_long_fwd_amd/csrc/mfma.hpp",
                             "sparse_attention_long_fwd_amd/csrc/common.hpp"],
 }
-PHASE_KERNELS = {"cmp_attn_importance": "cmp_fast_kernel"}
+# the kernels of each phase (name fragments); the compression branch runs its first sweep
+# (log-sum-exp) and its second sweep (probabilities, value sum, importance) as two kernels
+PHASE_KERNELS = {"cmp_attn_importance": ("cmp_lse_kernel", "cmp_group_kernel")}
+# one launch of this kernel per layer call and sequence: counts the calls in a counter run
+CALL_KERNEL = "compress_kv16_kernel"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 # kernels whose counters the bench line carries: name fragment -> sources
 COUNTER_KERNELS = {
-    "cmp_fast_kernel": PHASE_SOURCES["cmp_attn_importance"],
+    "cmp_lse_kernel": PHASE_SOURCES["cmp_attn_importance"],
+    "cmp_group_kernel": PHASE_SOURCES["cmp_attn_importance"],
     "flash_fast_kernel": ["sparse_attention_long_fwd_amd/csrc/flash_fast.hip",
                           "sparse_attention_long_fwd_amd/csrc/fast_common.hpp",
                           "sparse_attention_long_fwd_amd/csrc/mfma.hpp"],
@@ -105,8 +110,8 @@ def sources_sha(files):
 
 
 def kernel_traffic(phase):
-    """HBM bytes per launch of the phase's kernel, from the committed counter record, or None when
-    there is none or the kernel's sources changed since it was taken."""
+    """HBM bytes per layer call of the phase's kernels, from the committed counter record, or None when
+    there is none or the kernels' sources changed since it was taken."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)[phase]
@@ -114,12 +119,13 @@ def kernel_traffic(phase):
         return None
     if rec.get("sha256") != sources_sha(rec["sources"]):
         return None
-    return rec["bytes_per_launch"]
+    return rec["bytes_per_call"]
 
 
 def record_traffic(fetch_dir, write_dir):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each phase kernel, scaled by what the same
-    counter reads for the 1 GiB elementwise copy of --copy-probe, into profiles/traffic.json."""
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each phase's kernels, scaled by what the same
+    counter reads for the 1 GiB elementwise copy of --copy-probe, summed over the dispatches of one
+    layer call (all row chunks), into profiles/traffic.json."""
     import csv
     import glob
 
@@ -139,17 +145,21 @@ def record_traffic(fetch_dir, write_dir):
         if not copy:
             raise SystemExit("no copy-probe kernel in %s" % d)
         factor = COPY_PROBE_BYTES / (copy[0] * 1024.0)
-        for phase, kname in PHASE_KERNELS.items():
-            vals = [v for (_, name), v in per.items() if kname in name]
+        calls = sum(1 for (_, name) in per if CALL_KERNEL in name)
+        if calls < 1:
+            raise SystemExit("no %s dispatch in %s" % (CALL_KERNEL, d))
+        for phase, frags in PHASE_KERNELS.items():
+            vals = [v for (_, name), v in per.items() if any(f in name for f in frags)]
             if not vals:
                 continue
-            rec = out.setdefault(phase, {"kernel": kname, "sources": PHASE_SOURCES[phase],
+            rec = out.setdefault(phase, {"kernels": list(frags), "sources": PHASE_SOURCES[phase],
                                          "sha256": sources_sha(PHASE_SOURCES[phase])})
-            rec[counter.lower() + "_kib_per_launch"] = sum(vals) / len(vals)
+            rec[counter.lower() + "_kib_per_call"] = sum(vals) / calls
             rec[counter.lower() + "_copy_factor"] = factor
+            rec["dispatches_per_call"] = len(vals) / calls
     for rec in out.values():
-        rec["bytes_per_launch"] = (rec["fetch_size_kib_per_launch"] * rec["fetch_size_copy_factor"] +
-                                   rec["write_size_kib_per_launch"] * rec["write_size_copy_factor"]) * 1024.0
+        rec["bytes_per_call"] = (rec["fetch_size_kib_per_call"] * rec["fetch_size_copy_factor"] +
+                                 rec["write_size_kib_per_call"] * rec["write_size_copy_factor"]) * 1024.0
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1, sort_keys=True)
         fh.write("\n")
