@@ -161,6 +161,38 @@ __device__ __forceinline__ void scores16(const _Float16* kts, int mb, int c, int
   }
 }
 
+// Stores the importance of one row for a tile's 16 selection blocks j0 .. j0 + 15 (blocks after jmax
+// are not written).  On entry lane group gi holds blocks j0 + 4 mb + gi in v0..v3 (mb = 0..3); a 4 x 4
+// transpose among the row's four lanes (lanes c, c + 16, c + 32, c + 48) gives lane group gi blocks
+// j0 + 4 gi .. +3, so the row's 64 bytes leave in one instruction, 16 contiguous bytes a lane (the
+// whole row's run for the tile instead of four 16-byte pieces at different times).
+__device__ __forceinline__ void store_imp_tile(float* __restrict__ imp_row, int64_t j0, int64_t jmax, float v0,
+                                               float v1, float v2, float v3) {
+  const int l = threadIdx.x & 63, gi = l >> 4, c = l & 15;
+  auto pick = [](int i, float a, float b, float d, float e) { return i == 0 ? a : (i == 1 ? b : (i == 2 ? d : e)); };
+  float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    // this lane sends block (gi + r) & 3 of its run; it receives from lane group (gi - r) & 3
+    const float x = pick((gi + r) & 3, v0, v1, v2, v3);
+    const int k = (gi - r) & 3;
+    const float y = __shfl(x, (k << 4) | c, 64);
+    w0 = k == 0 ? y : w0;
+    w1 = k == 1 ? y : w1;
+    w2 = k == 2 ? y : w2;
+    w3 = k == 3 ? y : w3;
+  }
+  const int64_t j = j0 + 4 * gi;  // w0..w3 are blocks j .. j + 3
+  if (j + 3 <= jmax && (((uintptr_t)(imp_row + j)) & 15) == 0) {
+    *(float4*)(imp_row + j) = make_float4(w0, w1, w2, w3);
+  } else {
+    if (j <= jmax) imp_row[j] = w0;
+    if (j + 1 <= jmax) imp_row[j + 1] = w1;
+    if (j + 2 <= jmax) imp_row[j + 2] = w2;
+    if (j + 3 <= jmax) imp_row[j + 3] = w3;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // First sweep: the log-sum-exp of every (video row, head), written to lse (natural log; -inf for a
 // row with no visible compressed block).  Eight waves of 16 rows each (two per SIMD: no value
@@ -372,6 +404,8 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
 #pragma unroll
     for (int h = 0; h < G; ++h) L2[h] += (float)(sh_prev - sh);
     sh_prev = sh;
+    // importance of this lane's row in the tile: block 16 tile + 4 mb + gi for mb = 0..3
+    float im0 = 0.f, im1 = 0.f, im2 = 0.f, im3 = 0.f;
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
       f32x4 S0[G], S1[G];
@@ -427,14 +461,12 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
         impv[mi] = x + (gi ? rc : rprev);
         rprev = rc;
       }
-      if (imp_row) {
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
-          const int64_t J = (int64_t)tile * 16 + 4 * (2 * half + mi) + gi;
-          if (J <= jmax) imp_row[J] = impv[mi];
-        }
-      }
+      im0 = half ? im0 : impv[0];
+      im1 = half ? im1 : impv[1];
+      im2 = half ? impv[0] : im2;
+      im3 = half ? impv[1] : im3;
     }
+    if (imp_row) store_imp_tile(imp_row, (int64_t)tile * 16, jmax, im0, im1, im2, im3);
   };
   const int nt2 = nvmax > 0 ? nvmax / CK + 1 : 0;
   if (nt2 > 0) {
