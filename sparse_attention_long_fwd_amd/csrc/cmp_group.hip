@@ -198,8 +198,8 @@ __device__ __forceinline__ void store_imp_tile(float* __restrict__ imp_row, int6
 // row with no visible compressed block).  Eight waves of 16 rows each (two per SIMD: no value
 // accumulators here, so a wave fits in half the register file), the key tiles staged once for 128
 // rows.  Each lane sums over its own keys in log2 units y = score c2: the sum of 2^(y - mr) against
-// a whole-number reference mr, the largest floor(y) so far.  When mr moves the sum is rescaled by
-// an exact power of two (ldexp), so every term is below 2 and no step branches (the two waves on a
+// a whole-number reference mr, the largest floor(y) so far (updated per 32 keys).  When mr moves the
+// sum is rescaled by an exact power of two (ldexp), so every term is below 2 and no step branches (the two waves on a
 // SIMD overlap one's products with the other's exponentials).  The four lanes of a row are merged
 // at the end.
 template <int G>
@@ -248,17 +248,23 @@ cmp_lse_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ kv1
     ls[h] = 0.f;
   }
   // one 16-key M-block's scores; MASK: register j counts only when j < lm (else -inf)
-  auto lse_block = [&](const f32x4 (&S)[G], float ct, int lm, auto mask_c) {
+  // two 16-key M-blocks' scores (keys 16 mb .. +32); MASK: register j of block a counts only when
+  // j < lm[a] (else -inf)
+  auto lse_pair = [&](const f32x4 (&Sa)[G], const f32x4 (&Sb)[G], float ct, int lma, int lmb, auto mask_c) {
     constexpr bool MASK = decltype(mask_c)::value;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float v[4];
+      float v[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = (MASK && j >= lm) ? -INFINITY : S[h][j];
-      const float mn = fmaxf(mr[h], floorf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])) * ct));
+      for (int j = 0; j < 4; ++j) {
+        v[j] = (MASK && j >= lma) ? -INFINITY : Sa[h][j];
+        v[4 + j] = (MASK && j >= lmb) ? -INFINITY : Sb[h][j];
+      }
+      const float bm = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+      const float mn = fmaxf(mr[h], floorf(bm * ct));
       float acc = ldexpf(ls[h], (int)fmaxf(mr[h] - mn, -256.f));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc += fexp2(fmaf(v[j], ct, -mn));
+      for (int j = 0; j < 8; ++j) acc += fexp2(fmaf(v[j], ct, -mn));
       ls[h] = acc;
       mr[h] = mn;
     }
@@ -268,10 +274,11 @@ cmp_lse_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ kv1
   auto lse_tile = [&](int tile, int bi, auto mask_c) {
     const float ct = ldexpf(c2, eq + (int)(int8_t)gt.ksc[gt.clamp(tile)]);  // log2 units per raw score
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      f32x4 S[G];
-      scores16<G>(kbuf[bi], mb, c, gi, qf, S);
-      lse_block(S, ct, lim_of(tile, mb), mask_c);
+    for (int mb = 0; mb < 4; mb += 2) {
+      f32x4 Sa[G], Sb[G];
+      scores16<G>(kbuf[bi], mb, c, gi, qf, Sa);
+      scores16<G>(kbuf[bi], mb + 1, c, gi, qf, Sb);
+      lse_pair(Sa, Sb, ct, lim_of(tile, mb), lim_of(tile, mb + 1), mask_c);
     }
   };
   const int nt1 = (nvmax + CK - 1) / CK;
