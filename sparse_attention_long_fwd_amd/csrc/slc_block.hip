@@ -36,7 +36,7 @@ namespace {
 constexpr int HD = 128;
 constexpr int SB = 64;       // tokens per selection block
 constexpr int RC = 32;       // rows per chunk
-constexpr int RROWS = 2048;  // rows per bucketing workgroup
+constexpr int RROWS = 512;   // rows per bucketing workgroup
 }  // namespace
 
 // Bucketing layout in the workspace (per bg = b * Hkv + g):
@@ -72,6 +72,34 @@ __device__ __forceinline__ bool slc_pair_kept(int j, int64_t r, const Dims& dm, 
   return j >= 0 && (int64_t)j <= jt && !(local_fused && (int64_t)j > jt - dm.n_local);
 }
 
+// Calls f(r, s, j) for each kept pair (row r, slot s, block j) of group g among rows [r0, r1): one
+// entry (r, s) per thread and step, consecutive threads on consecutive entries (coalesced), eight
+// steps' loads issued before their uses so that the loop is not one load latency per entry.
+template <typename F>
+__device__ __forceinline__ void slc_for_pairs(const int32_t* __restrict__ idx, const uint8_t* __restrict__ vid,
+                                              const Dims& dm, int64_t b, int g, int64_t r0, int64_t r1,
+                                              int local_fused, F f) {
+  constexpr int U = 8;
+  const int64_t e1 = r1 * dm.n;
+  for (int64_t e0 = r0 * dm.n + threadIdx.x; e0 < e1; e0 += (int64_t)U * blockDim.x) {
+    int js[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = e0 + (int64_t)u * blockDim.x;
+      js[u] = -1;
+      if (e < e1) {
+        const int64_t r = e / dm.n;
+        if (!vid || vid[b * dm.Tq + r]) js[u] = idx[((b * dm.Tq + r) * dm.Hkv + g) * dm.n + e % dm.n];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = e0 + (int64_t)u * blockDim.x;
+      if (e < e1 && slc_pair_kept(js[u], e / dm.n, dm, local_fused)) f(e / dm.n, (int)(e % dm.n), js[u]);
+    }
+  }
+}
+
 __global__ void __launch_bounds__(256) slc_count_kernel(const int32_t* __restrict__ idx,
                                                         const uint8_t* __restrict__ vid, SlcBuckets bk, Dims dm,
                                                         int wgs_per_bg, int local_fused) {
@@ -83,13 +111,7 @@ __global__ void __launch_bounds__(256) slc_count_kernel(const int32_t* __restric
   __syncthreads();
   const int64_t r0 = (int64_t)part * RROWS;
   const int64_t r1 = r0 + RROWS < dm.Tq ? r0 + RROWS : dm.Tq;
-  for (int64_t e = r0 * dm.n + threadIdx.x; e < r1 * dm.n; e += blockDim.x) {
-    const int64_t r = e / dm.n;
-    const int s = (int)(e % dm.n);
-    if (vid && !vid[b * dm.Tq + r]) continue;
-    const int j = idx[((b * dm.Tq + r) * dm.Hkv + g) * dm.n + s];
-    if (slc_pair_kept(j, r, dm, local_fused)) atomicAdd(&hist[j], 1);
-  }
+  slc_for_pairs(idx, vid, dm, b, g, r0, r1, local_fused, [&](int64_t, int, int j) { atomicAdd(&hist[j], 1); });
   __syncthreads();
   for (int j = threadIdx.x; j < dm.Ns; j += blockDim.x)
     if (hist[j]) atomicAdd(&bk.count[(int64_t)bg * dm.Ns + j], hist[j]);
@@ -165,12 +187,7 @@ __global__ void __launch_bounds__(256) slc_scatter_kernel(const int32_t* __restr
   __syncthreads();
   const int64_t r0 = (int64_t)part * RROWS;
   const int64_t r1 = r0 + RROWS < dm.Tq ? r0 + RROWS : dm.Tq;
-  for (int64_t e = r0 * dm.n + threadIdx.x; e < r1 * dm.n; e += blockDim.x) {
-    const int64_t r = e / dm.n;
-    if (vid && !vid[b * dm.Tq + r]) continue;
-    const int j = idx[((b * dm.Tq + r) * dm.Hkv + g) * dm.n + e % dm.n];
-    if (slc_pair_kept(j, r, dm, local_fused)) atomicAdd(&hist[j], 1);
-  }
+  slc_for_pairs(idx, vid, dm, b, g, r0, r1, local_fused, [&](int64_t, int, int j) { atomicAdd(&hist[j], 1); });
   __syncthreads();
   const int64_t base = (int64_t)bg * dm.Ns;
   for (int j = threadIdx.x; j < dm.Ns; j += blockDim.x) {
@@ -180,13 +197,8 @@ __global__ void __launch_bounds__(256) slc_scatter_kernel(const int32_t* __restr
   }
   __syncthreads();
   int* pl = bk.pairs + (int64_t)bg * bk.cap_c * RC;
-  for (int64_t e = r0 * dm.n + threadIdx.x; e < r1 * dm.n; e += blockDim.x) {
-    const int64_t r = e / dm.n;
-    const int s = (int)(e % dm.n);
-    if (vid && !vid[b * dm.Tq + r]) continue;
-    const int j = idx[((b * dm.Tq + r) * dm.Hkv + g) * dm.n + s];
-    if (slc_pair_kept(j, r, dm, local_fused)) pl[pbase[j] + atomicAdd(&hist[j], 1)] = (int)(r << 5) | s;
-  }
+  slc_for_pairs(idx, vid, dm, b, g, r0, r1, local_fused,
+                [&](int64_t r, int s, int j) { pl[pbase[j] + atomicAdd(&hist[j], 1)] = (int)(r << 5) | s; });
 }
 
 // ---------------------------------------------------------------------------
