@@ -240,11 +240,16 @@ int64_t default_chunk_rows(const Dims& dm, int32_t dtype) {
 // kl8 / ksc / vl: on the MFMA path when the layer compressed them itself, the keys' fp8 low parts
 // and their scales and the values' bf16 low parts; kv16: instead of all these, the group kernel's
 // fp16 key / value tiles.
+// The MFMA compression kernels take 64-token selection blocks from row-major compressed keys and
+// 32-, 64- or 128-token blocks from the group kernel's tiles; other calls run the generic kernel
+// (its output in dtype, no fp32 copy).
+bool cmp_on_fast(int32_t dtype, const Dims& dm, bool kv16) { return use_fast(dtype, dm) && (kv16 || dm.ls == 64); }
+
 int run_cmp(int32_t dtype, int32_t cdtype, const Dims& dm, const void* q, const void* kc, const void* kl8,
             const void* ksc, const void* vc, const void* vl, const void* kv16, const uint8_t* vid, void* o, float* o32,
             float* lse, float* imp, hipStream_t s) {
   hipError_t e;
-  if (!use_fast(dtype, dm)) {
+  if (!cmp_on_fast(dtype, dm, kv16 != nullptr)) {
     e = launch_cmp_generic(dtype, cdtype, dm, q, kc, vc, vid, o, lse, imp, s);
   } else if (kv16) {
     e = launch_cmp_group(dm, q, kv16, vid, o, o32, lse, imp, s);
@@ -374,7 +379,7 @@ int32_t nsa_cmp_attn_scores(const void* q, const void* k_cmp, const void* v_cmp,
   if (!q || (dm.Nc > 0 && (!k_cmp || !v_cmp))) return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (!aligned16(q) || !aligned16(k_cmp) || !aligned16(v_cmp) || !aligned16(o_cmp))
     return fail(NSA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
-  if (!use_fast(dtype, dm) && dm.Ns > 16384)
+  if (!cmp_on_fast(dtype, dm, false) && dm.Ns > 16384)
     return fail(NSA_ERR_UNSUPPORTED, "generic kernel handles at most 16384 selection blocks");
   return run_cmp(dtype, dtype, dm, q, k_cmp, nullptr, nullptr, v_cmp, nullptr, nullptr, is_video, o_cmp, nullptr, lse,
                  importance,
@@ -539,10 +544,14 @@ int32_t layer_pass(const Dims& dm, int32_t dtype, const LayerIO& io, const float
     return NSA_OK;
   }
   const bool fast = use_fast(dtype, dm);
-  // MFMA path: the combine reads an fp32 copy of the compression output; the caller's bf16 copy is optional
+  // MFMA path: the combine reads an fp32 copy of the compression output; the caller's bf16 copy is
+  // optional.  Compression on the generic kernel (caller's compressed keys with 32- or 128-token
+  // selection blocks): its output in dtype, in the fp32 buffer's space when the caller gives none.
+  const bool c32 = cmp_on_fast(dtype, dm, kv16 != nullptr);
   prof_mark(s);
-  void* ocmp = fast ? o_cmp : (o_cmp ? o_cmp : ocmp_ws);
-  float* ocmp32 = fast ? (float*)ocmp_ws : nullptr;
+  void* ocmp = c32 ? o_cmp : (o_cmp ? o_cmp : ocmp_ws);
+  float* ocmp32 = c32 ? (float*)ocmp_ws : nullptr;
+  const void* ocmb = c32 ? (const void*)ocmp32 : ocmp;  // what the combine reads
   int32_t* idx = block_idx_out ? block_idx_out : idx_ws;
   st = run_cmp(dtype, cdtype, dm, q, kc_use, kl_use, ksc_use, vc_use, vl_use, kv16, is_video,
                ocmp, ocmp32, lse, imp, s);
@@ -560,7 +569,7 @@ int32_t layer_pass(const Dims& dm, int32_t dtype, const LayerIO& io, const float
       where = "top-n kernel";
     }
     if (e == hipSuccess) {
-      e = launch_sparse_select(dm, q, kv.ks, kv.vs, kv.kw, kv.vw, idx, is_video, ocmp32, true, gates, out, o_slc,
+      e = launch_sparse_select(dm, q, kv.ks, kv.vs, kv.kw, kv.vw, idx, is_video, ocmb, c32, gates, out, o_slc,
                                sparse_ws_ptr, s, side, true);
       where = "selection kernels";
     }
@@ -574,7 +583,7 @@ int32_t layer_pass(const Dims& dm, int32_t dtype, const LayerIO& io, const float
   if (e != hipSuccess) return hip_fail(e, "top-n kernel");
   prof_mark(s);
   if (fast) {
-    st = run_sparse(dtype, dm, q, kv, idx, is_video, ocmp32, true, gates, out, o_slc, o_swa, sparse_ws_ptr, s,
+    st = run_sparse(dtype, dm, q, kv, idx, is_video, ocmb, c32, gates, out, o_slc, o_swa, sparse_ws_ptr, s,
                     true);
     prof_mark(s);
     return st;
@@ -607,7 +616,7 @@ int32_t layer_fwd(const void* q, const BranchKV& kv, const void* k_cmp_in, const
   // the decode kernels score a block once for the selection and the window branch
   if (use_decode(dtype, dm) && !(kv.ks == kv.kw && kv.vs == kv.vw))
     return fail(NSA_ERR_UNSUPPORTED, "one query row per sequence needs one K/V for selection and window");
-  if (!use_fast(dtype, dm) && dm.Ns > 16384)
+  if (!cmp_on_fast(dtype, dm, !k_cmp_in && cmp_group_supported(dm)) && dm.Ns > 16384)
     return fail(NSA_ERR_UNSUPPORTED, "generic kernels handle at most 16384 selection blocks");
   if (!workspace) return fail(NSA_ERR_INVALID_ARG, "NULL workspace");
   int64_t rows = fit_chunk_rows(dm, dtype, workspace_bytes);

@@ -312,8 +312,14 @@ cmp_lse_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ kv1
 
 // Second sweep: exact probabilities from the log-sum-exp, the value sum and the block importance.
 // Four waves of 16 rows each, one per SIMD (the value accumulators of all G heads fill the
-// accumulation registers).
-template <int G>
+// accumulation registers).  LS: tokens per selection block (32, 64 or 128).  Compressed key i spans
+// tokens [16 i, 16 i + 31], so block J takes half of its first straddling key, the keys inside it
+// whole and half of its last straddling key: LS = 32: keys 2J - 1 (half), 2J, 2J + 1 (half);
+// LS = 64: 4J - 1 (half) .. 4J + 3 (half); LS = 128: 8J - 1 (half) .. 8J + 7 (half).  A lane holds
+// four consecutive keys 4k .. 4k + 3 of its row: with LS = 32 they make blocks 2k and 2k + 1, with
+// LS = 64 block k, with LS = 128 half of block k / 2 (the lane groups gi, gi ^ 1 are joined with one
+// lane exchange); the half share of a lane's first key comes from the previous lane group.
+template <int G, int LS>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NWV * 64, NWV * 64), amdgpu_waves_per_eu(1, 1)))
 cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ kv16, const uint8_t* __restrict__ vid,
                  const float* __restrict__ lse, bf16* __restrict__ o_bf, float* __restrict__ o_f32,
@@ -457,23 +463,54 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
 #pragma unroll
         for (int h = 0; h < G; ++h) O[h][db] = mfma16h(vf, pb[h], O[h][db]);
       }
-      // importance of selection blocks 16 tile + 4 mb + gi of this lane's row, mb = 2 half, 2 half + 1
-      float impv[2];
+      // importance of this lane's row from M-blocks mb = 2 half, 2 half + 1 (keys 4k .. 4k + 3,
+      // k = 16 tile + 4 mb + gi)
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) {
         const float* P = mi ? P1 : P0;
+        const int64_t kq = (int64_t)tile * 16 + 4 * (2 * half + mi) + gi;
         const float t = 0.5f * P[3] * unscale;
-        const float x = (P[0] + P[1] + P[2]) * unscale + t;
         const float rc = __shfl(t, srcl, 64);  // t of lane group gi - 1, or of group 3 for gi = 0
-        impv[mi] = x + (gi ? rc : rprev);
+        const float carry = gi ? rc : rprev;   // half of the key before this lane's first
         rprev = rc;
+        if constexpr (LS == 64) {
+          const float v = (P[0] + P[1] + P[2]) * unscale + t + carry;  // block k
+          if (mi == 0) {
+            im0 = half ? im0 : v;
+            im2 = half ? v : im2;
+          } else {
+            im1 = half ? im1 : v;
+            im3 = half ? v : im3;
+          }
+        } else if constexpr (LS == 32) {
+          const float hp1 = 0.5f * P[1] * unscale;
+          const float b0 = carry + P[0] * unscale + hp1;  // block 2k
+          const float b1 = hp1 + P[2] * unscale + t;      // block 2k + 1
+          if (imp_row) {
+            const int64_t J = 2 * kq;
+            if (J + 1 <= jmax && (((uintptr_t)(imp_row + J)) & 7) == 0) {
+              *(float2*)(imp_row + J) = make_float2(b0, b1);
+            } else {
+              if (J <= jmax) imp_row[J] = b0;
+              if (J + 1 <= jmax) imp_row[J + 1] = b1;
+            }
+          }
+        } else {
+          // lane groups 2m, 2m + 1 hold block k / 2: keys 8J .. 8J + 3 whole (and the half of 8J - 1),
+          // keys 8J + 4 .. 8J + 6 whole and half of 8J + 7
+          const float v = (gi & 1) ? (P[0] + P[1] + P[2]) * unscale + t
+                                   : (P[0] + P[1] + P[2] + P[3]) * unscale + carry;
+          const float blk = v + __shfl_xor(v, 16, 64);
+          if (imp_row && !(gi & 1)) {
+            const int64_t J = kq >> 1;
+            if (J <= jmax) imp_row[J] = blk;
+          }
+        }
       }
-      im0 = half ? im0 : impv[0];
-      im1 = half ? im1 : impv[1];
-      im2 = half ? impv[0] : im2;
-      im3 = half ? impv[1] : im3;
     }
-    if (imp_row) store_imp_tile(imp_row, (int64_t)tile * 16, jmax, im0, im1, im2, im3);
+    if constexpr (LS == 64) {
+      if (imp_row) store_imp_tile(imp_row, (int64_t)tile * 16, jmax, im0, im1, im2, im3);
+    }
   };
   const int nt2 = nvmax > 0 ? nvmax / CK + 1 : 0;
   if (nt2 > 0) {
@@ -497,9 +534,9 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
     gwait_loads();
     __syncthreads();
   }
-  // blocks up to the row's own block that no compressed block reaches
+  // blocks up to the row's own block that no compressed block reaches (1024 tokens a 64-key tile)
   if (imp_row) {
-    for (int64_t J = (int64_t)nt2 * 16 + gi; J <= jmax; J += 4) imp_row[J] = 0.f;
+    for (int64_t J = (int64_t)nt2 * (1024 / LS) + gi; J <= jmax; J += 4) imp_row[J] = 0.f;
   }
 
   if (!isv) return;
@@ -602,7 +639,10 @@ hipError_t launch_compress_kv16(const Dims& dm, const void* k, const float* w_k,
   return hipGetLastError();
 }
 
-bool cmp_group_supported(const Dims& dm) { return dm.D == HD && dm.G >= 4 && dm.G <= 7; }
+bool cmp_group_supported(const Dims& dm) {
+  return dm.D == HD && dm.G >= 4 && dm.G <= 7 && dm.l == 32 && dm.d == 16 &&
+         (dm.ls == 32 || dm.ls == 64 || dm.ls == 128);
+}
 
 hipError_t launch_cmp_group(const Dims& dm, const void* q, const void* kv16, const uint8_t* vid, void* o_bf,
                             float* o32, float* lse, float* imp, hipStream_t s) {
@@ -622,11 +662,14 @@ hipError_t launch_cmp_group(const Dims& dm, const void* q, const void* kv16, con
                                                                   lse, (bf16*)o_bf, o32, imp, dm, tb);
     return hipGetLastError();
   };
+  auto by_ls = [&](auto lse_kernel, auto k32, auto k64, auto k128) -> hipError_t {
+    return dm.ls == 32 ? go(lse_kernel, k32) : dm.ls == 128 ? go(lse_kernel, k128) : go(lse_kernel, k64);
+  };
   switch (dm.G) {
-    case 4: return go(cmp_lse_kernel<4>, cmp_group_kernel<4>);
-    case 5: return go(cmp_lse_kernel<5>, cmp_group_kernel<5>);
-    case 6: return go(cmp_lse_kernel<6>, cmp_group_kernel<6>);
-    case 7: return go(cmp_lse_kernel<7>, cmp_group_kernel<7>);
+    case 4: return by_ls(cmp_lse_kernel<4>, cmp_group_kernel<4, 32>, cmp_group_kernel<4, 64>, cmp_group_kernel<4, 128>);
+    case 5: return by_ls(cmp_lse_kernel<5>, cmp_group_kernel<5, 32>, cmp_group_kernel<5, 64>, cmp_group_kernel<5, 128>);
+    case 6: return by_ls(cmp_lse_kernel<6>, cmp_group_kernel<6, 32>, cmp_group_kernel<6, 64>, cmp_group_kernel<6, 128>);
+    case 7: return by_ls(cmp_lse_kernel<7>, cmp_group_kernel<7, 32>, cmp_group_kernel<7, 64>, cmp_group_kernel<7, 128>);
     default: return hipErrorInvalidValue;
   }
 }

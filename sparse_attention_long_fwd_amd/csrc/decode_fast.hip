@@ -803,7 +803,7 @@ static int dwgs(const Dims& dm) {
 }
 
 // The selection kernel keeps the importance of all Ns blocks in LDS.
-bool decode_supported(const Dims& dm) { return dm.Tq == 1 && dm.Nc > 0 && dm.Ns <= 16384; }
+bool decode_supported(const Dims& dm) { return dm.Tq == 1 && dm.Nc > 0 && dm.Ns <= 16384 && dm.ls == 64; }
 
 size_t decode_workspace(const Dims& dm) {
   const size_t units = (size_t)dm.B * dm.Hkv;

@@ -2,8 +2,8 @@
 #pragma once
 #include "common.hpp"
 
-// True when the MFMA kernels cover this problem: bf16, head_dim 128,
-// compressed block 32 / stride 16, selection block 64, 4 <= G <= 8.
+// True when the MFMA kernels cover this problem: bf16, head_dim 128, compressed block 32 /
+// stride 16, selection block 64 with 4 <= G <= 8, or selection block 32 or 128 with 4 <= G <= 7.
 bool fast_supported(int32_t dtype, const Dims& dm);
 
 // Scratch bytes the MFMA selection/window path needs.

@@ -8,9 +8,12 @@ hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const 
                             const float* gates, void* out, void* o_slc, void* ws, hipStream_t s,
                             bool local_fused, hipEvent_t before_merge);
 
-// Block-major selection packs (row, slot) into 32 bits: rows below 2^26.
+// Block-major selection packs (row, slot) into 32 bits: rows below 2^26.  Selection blocks of 64
+// tokens for 4..8 query heads per KV head; of 32 or 128 tokens for 4..7 (the group kernel of the
+// compression branch).
 bool fast_supported(int32_t dtype, const Dims& dm) {
-  return dtype == 1 && dm.D == 128 && dm.l == 32 && dm.d == 16 && dm.ls == 64 && dm.G >= 4 && dm.G <= 8 &&
+  const bool ls_ok = dm.ls == 64 || ((dm.ls == 32 || dm.ls == 128) && dm.G <= 7);
+  return dtype == 1 && dm.D == 128 && dm.l == 32 && dm.d == 16 && ls_ok && dm.G >= 4 && dm.G <= 8 &&
          dm.n <= 32 && dm.Tq < ((int64_t)1 << 26);
 }
 

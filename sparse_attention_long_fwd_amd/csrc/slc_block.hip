@@ -34,7 +34,6 @@
 
 namespace {
 constexpr int HD = 128;
-constexpr int SB = 64;       // tokens per selection block
 constexpr int RC = 32;       // rows per chunk
 constexpr int RROWS = 512;   // rows per bucketing workgroup
 }  // namespace
@@ -202,12 +201,32 @@ __global__ void __launch_bounds__(256) slc_scatter_kernel(const int32_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// One workgroup per chunk of up to 32 (row, slot) pairs of one block; wave w = head g*G + w.
+// Stage rows [key0, key0 + ROWS) of a [*, 128] bf16 array into a swizzled ROWS x 128 LDS tile (the
+// swz128 layout) with direct global -> LDS loads, ROWS / 4 instructions of 64 lanes x 16 bytes
+// spread over nw waves; rows at or past nrows repeat row nrows - 1 (masked by the caller).
+template <int ROWS>
+__device__ __forceinline__ void stage_rows(bf16* lds_tile, const bf16* src, int64_t stride, int64_t key0,
+                                           int64_t nrows, int w, int nw, int lane) {
+  for (int ins = w; ins < ROWS / 4; ins += nw) {
+    const int p = ins * 64 + lane;
+    const int row = p >> 4, c = (p & 15) ^ (row & 15);
+    int64_t key = key0 + row;
+    if (key >= nrows) key = nrows - 1;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + key * stride + c * 8),
+                                     (__attribute__((address_space(3))) void*)(lds_tile + ins * 512), 16, 0, 0);
+  }
+}
+
+// One workgroup per chunk of up to 32 (row, slot) pairs of one block of SB tokens (32, 64 or 128);
+// wave w = head g*G + w.
+template <int SB>
 __global__ void __launch_bounds__(512) slc_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                         const bf16* __restrict__ v, SlcBuckets bk,
                                                         float2* __restrict__ pml, _Float16* __restrict__ po, Dims dm) {
-  __shared__ __attribute__((aligned(16))) bf16 kt[SB * HD];
-  __shared__ __attribute__((aligned(16))) bf16 vt[SB * HD];
+  constexpr int NKB = SB / 32;  // 32-key blocks of the score tile
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  bf16* kt = (bf16*)smem;
+  bf16* vt = kt + SB * HD;
   const int G = dm.G;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, n = l & 31;
   const int bg = blockIdx.x / bk.cap_c, cc = blockIdx.x % bk.cap_c;
@@ -220,8 +239,8 @@ __global__ void __launch_bounds__(512) slc_chunk_kernel(const bf16* __restrict__
   const int g = bg % dm.Hkv;
   const int64_t stride = (int64_t)dm.Hkv * HD;
   const int64_t kvb = (b * dm.T * dm.Hkv + g) * (int64_t)HD;
-  stage_tile64(kt, k + kvb, stride, (int64_t)j * SB, dm.T, w, G, l);
-  stage_tile64(vt, v + kvb, stride, (int64_t)j * SB, dm.T, w, G, l);
+  stage_rows<SB>(kt, k + kvb, stride, (int64_t)j * SB, dm.T, w, G, l);
+  stage_rows<SB>(vt, v + kvb, stride, (int64_t)j * SB, dm.T, w, G, l);
   // the lane's query, loaded while the tile streams in
   const bool valid = pr >= 0;
   const int64_t row = valid ? (pr >> 5) : 0;
@@ -239,10 +258,10 @@ __global__ void __launch_bounds__(512) slc_chunk_kernel(const bf16* __restrict__
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks)
     if (!valid) qf[ks] = zero8();
-  // S^T: keys on M (two 32-key blocks), the chunk's rows on N
-  f32x16 s[2];
+  // S^T: keys on M (NKB 32-key blocks), the chunk's rows on N
+  f32x16 s[NKB];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < NKB; ++kb) {
     s[kb] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) s[kb] = mfma32(lds_read8(kt + swz128(kb * 32 + n, 2 * ks + hl)), qf[ks], s[kb]);
@@ -252,7 +271,7 @@ __global__ void __launch_bounds__(512) slc_chunk_kernel(const bf16* __restrict__
   const bool need_mask = u0 + SB - 1 > t || u0 + SB > dm.T;  // the row's own block, or past the end
   float mx = -INFINITY;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
       if (need_mask) {
@@ -270,7 +289,7 @@ __global__ void __launch_bounds__(512) slc_chunk_kernel(const bf16* __restrict__
   f32x16 oacc[4] = {};
   const int g16 = l >> 4, i16 = l & 15;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < NKB; ++kb) {
     float p[16];
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
@@ -489,8 +508,17 @@ hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const 
   slc_scan_kernel<<<dim3(bgs), dim3(1024), 2 * hist, s>>>(bk, dm);
   slc_scatter_kernel<<<dim3(bgs * wpb), dim3(256), 2 * hist, s>>>(idx, vid, bk, dm, wpb,
                                                                    local_fused ? 1 : 0);
-  slc_chunk_kernel<<<dim3((unsigned)bgs * bk.cap_c), dim3(dm.G * 64), 0, s>>>((const bf16*)q, (const bf16*)k,
-                                                                             (const bf16*)v, bk, pml, po, dm);
+  auto chunk = [&](auto kernel, int sb) -> hipError_t {
+    const int shm = 2 * sb * HD * 2;
+    hipError_t e2 = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, shm);
+    if (e2 != hipSuccess) return e2;
+    kernel<<<dim3((unsigned)bgs * bk.cap_c), dim3(dm.G * 64), shm, s>>>((const bf16*)q, (const bf16*)k,
+                                                                        (const bf16*)v, bk, pml, po, dm);
+    return hipGetLastError();
+  };
+  e = dm.ls == 32 ? chunk(slc_chunk_kernel<32>, 32)
+                  : dm.ls == 128 ? chunk(slc_chunk_kernel<128>, 128) : chunk(slc_chunk_kernel<64>, 64);
+  if (e != hipSuccess) return e;
   // the merge reads the window pass's outputs (run on another stream when before_merge is given)
   if (before_merge) {
     e = hipStreamWaitEvent(s, before_merge, 0);

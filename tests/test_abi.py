@@ -262,12 +262,14 @@ def test_layer_workspace_rows():
             nsa.nsa_hybrid_layer_workspace_size(dec, pr, bf))
 
 
-@pytest.mark.parametrize("T,B,q0,rows", [(131072, 1, 0, 40960), (131072, 1, 0, 1024), (36352, 2, 0, 4096),
-                                         (9000, 1, 0, 1024), (70000, 1, 5000, 8192)])
-def test_layer_chunk_workspace_covers_every_chunk(T, B, q0, rows):
+@pytest.mark.parametrize("T,B,q0,rows,ls", [(131072, 1, 0, 40960, 64), (131072, 1, 0, 1024, 64),
+                                            (36352, 2, 0, 4096, 64), (9000, 1, 0, 1024, 64),
+                                            (70000, 1, 5000, 8192, 64), (131072, 1, 0, 8192, 32),
+                                            (131072, 1, 0, 16384, 128), (20000, 2, 3000, 2048, 32)])
+def test_layer_chunk_workspace_covers_every_chunk(T, B, q0, rows, ls):
     """The chunked workspace must hold what every chunk needs as a call of its own (rows placed where
     the chunk sits: scratch such as the key splits of long text rows grows with the position)."""
-    pr = _params(top_n=16, window=512)
+    pr = _params(top_n=16, window=512, sel_block=ls)
     bf = nsa.NSA_BF16
     sh = _dshape(batch=B, q_len=T - q0, kv_len=T, q_start=q0)
     carve = nsa.nsa_hybrid_layer_workspace_size_rows(sh, pr, bf, rows)
