@@ -363,13 +363,16 @@ def branch_outputs(wl, inp):
 
 
 BUDGET = 16 * 64 + 512   # tokens each video row attends in the selection + window branches
-BUDGET_POINTS = [(8, 1024), (12, 768), (16, 512), (20, 256), (22, 128), (23, 64)]
+# (selection block l', top-n, window) with l' n + w = BUDGET
+BUDGET_POINTS = [(64, 8, 1024), (64, 12, 768), (64, 16, 512), (64, 20, 256), (64, 22, 128), (64, 23, 64),
+                 (32, 32, 512), (32, 40, 256), (128, 8, 512), (128, 10, 256)]
 
 
 def budget_sweep(args, wl, inp):
-    """Performance surface of the selection / window split at a fixed budget: top-n blocks of 64
-    tokens plus a window of w tokens with 64 n + w = 1536, on the same 128K inputs; per point the
-    step time, tokens/s, algorithmic FLOP rate and the library's phase times."""
+    """Performance surface of the selection / window split at a fixed budget: top-n blocks of l'
+    tokens plus a window of w tokens with l' n + w = 1536 (l' = 32, 64, 128), on the same 128K
+    inputs; per point the step time, tokens/s, algorithmic FLOP rate and the library's phase
+    times."""
     import torch
     from sparse_attention_long_fwd_amd import accounting, nsa
 
@@ -379,9 +382,9 @@ def budget_sweep(args, wl, inp):
     sh = nsa.make_shape(B, Tq, wl.kv_len, wl.q_start, Hq, k.shape[2], D)
     out = torch.empty_like(q)
     pts = []
-    for n, w in BUDGET_POINTS:
-        assert 64 * n + w == BUDGET
-        wv = wl.with_(top_n=n, window=w)
+    for ls, n, w in BUDGET_POINTS:
+        assert ls * n + w == BUDGET
+        wv = wl.with_(sel_block=ls, top_n=n, window=w)
         pr = nsa.make_params(**wv.params())
         ws = torch.empty(nsa.nsa_hybrid_layer_workspace_size(sh, pr, nsa.NSA_BF16), dtype=torch.uint8,
                          device="cuda")
@@ -401,12 +404,12 @@ def budget_sweep(args, wl, inp):
             acc = ph if acc is None else acc + ph
         nsa.profile_enable(False)
         fl = accounting.flops(wv)["total"]
-        pts.append(dict(top_n=n, window=w, ms_per_step=ms, tokens_per_s=Tq * B / (ms * 1e-3),
+        pts.append(dict(sel_block=ls, top_n=n, window=w, ms_per_step=ms, tokens_per_s=Tq * B / (ms * 1e-3),
                         algo_tflops=fl / (ms * 1e-3) / 1e12,
                         phase_ms={name: round(float(x), 4) for name, x in zip(nsa.PHASES, acc / args.sweep_steps)}))
-        log("budget point n=%d w=%d: %.2f ms" % (n, w, ms))
+        log("budget point l'=%d n=%d w=%d: %.2f ms" % (ls, n, w, ms))
         del ws
-    return dict(workload=wl.name, budget_tokens=BUDGET, sel_block=64, points=pts)
+    return dict(workload=wl.name, budget_tokens=BUDGET, points=pts)
 
 
 def branch_kv(args, wl, inp):

@@ -281,6 +281,41 @@ cmp_lse_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ kv1
       lse_pair(Sa, Sb, ct, lim_of(tile, mb), lim_of(tile, mb + 1), mask_c);
     }
   };
+  // A tile whose keys are all visible, after the first: the terms 2^(y - mr) against the reference
+  // as it stands, without the per-block maxima.  Their sum over the tile must stay below 2^100 for
+  // every lane (else false: the tile is redone by lse_tile from the unchanged state); then the
+  // running sum is brought back below 2^32 by an exact power of two.  The reference stays within
+  // 2^13 of the row's largest term (a sum of at most 2^13 terms only passes 2^32 with a term above
+  // 2^19), so no term that matters underflows.
+  auto lse_tile_fast = [&](int tile, int bi) -> bool {
+    const float ct = ldexpf(c2, eq + (int)(int8_t)gt.ksc[gt.clamp(tile)]);
+    float ts[G];
+#pragma unroll
+    for (int mb = 0; mb < 4; mb += 2) {
+      f32x4 Sa[G], Sb[G];
+      scores16<G>(kbuf[bi], mb, c, gi, qf, Sa);
+      scores16<G>(kbuf[bi], mb + 1, c, gi, qf, Sb);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a += fexp2(fmaf(Sa[h][j], ct, -mr[h])) + fexp2(fmaf(Sb[h][j], ct, -mr[h]));
+        ts[h] = mb ? ts[h] + a : a;
+      }
+    }
+    bool ok = true;
+#pragma unroll
+    for (int h = 0; h < G; ++h) ok = ok && ts[h] < 0x1p100f;  // false for inf and NaN
+    if (__builtin_amdgcn_ballot_w64(!ok)) return false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float acc = ls[h] + ts[h];
+      const int e = acc >= 0x1p32f ? __builtin_amdgcn_frexp_expf(acc) : 0;
+      ls[h] = ldexpf(acc, -e);
+      mr[h] += (float)e;
+    }
+    return true;
+  };
   const int nt1 = (nvmax + CK - 1) / CK;
   if (nt1 > 0) {
     stage_k(0, 0);
@@ -290,10 +325,11 @@ cmp_lse_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ kv1
   for (int tile = 0; tile < nt1; ++tile) {
     const int bi = tile & 1;
     if (tile + 1 < nt1) stage_k(tile + 1, bi ^ 1);
-    if ((tile + 1) * CK <= nvmin)
-      lse_tile(tile, bi, std::false_type{});
-    else
+    if ((tile + 1) * CK <= nvmin) {
+      if (tile == 0 || !lse_tile_fast(tile, bi)) lse_tile(tile, bi, std::false_type{});
+    } else {
       lse_tile(tile, bi, std::true_type{});
+    }
     gwait_loads();
     __syncthreads();
   }
@@ -375,9 +411,6 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
   };
   // log2 units per raw score unit of tile `tile`
   auto c2_of = [&](int tile) { return ldexpf(c2, eq + (int)(int8_t)gt.ksc[gt.clamp(tile)]); };
-  auto scores = [&](int bi, int mb, f32x4 (&S)[G]) {
-    scores16<G>((const _Float16*)lds_at(bi, L_KT), mb, c, gi, qf, S);
-  };
   // Score register j of M-block mb of tile `tile` holds compressed key tile CK + 16 mb + 4 gi + j;
   // it is visible when j < lim
   auto lim_of = [&](int tile, int mb) { return nv - (tile * CK + 16 * mb + 4 * gi); };
@@ -421,47 +454,72 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
     float im0 = 0.f, im1 = 0.f, im2 = 0.f, im3 = 0.f;
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
-      f32x4 S0[G], S1[G];
-      scores(bi, 2 * half, S0);
       f16x8 pb[G];  // P^T operands of the half's 32 keys: M-block 2 half in slots 0..3, the next in 4..7
-      float P0[4] = {0.f, 0.f, 0.f, 0.f}, P1[4] = {0.f, 0.f, 0.f, 0.f};  // sums over the heads
+      float P0[4], P1[4];  // sums over the heads
       const int lm0 = lim_of(tile, 2 * half), lm1 = lim_of(tile, 2 * half + 1);
-      // the second M-block's products, head by head beside the first M-block's probabilities
+      // key fragments of both M-blocks, read once for all heads
       const _Float16* kts = (const _Float16*)lds_at(bi, L_KT);
-      f16x8 k1[4];
+      f16x8 k0[4], k1[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) k1[ks] = *(const f16x8*)(kts + swz128(16 * (2 * half + 1) + c, 4 * ks + gi));
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float p = fexp2(fmaf(S0[h][j], ct, -L2[h]));
-          if constexpr (MASK) p = j < lm0 ? p : 0.f;
-          P0[j] += p;
-          pb[h][j] = (_Float16)p;
-        }
-        S1[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) S1[h] = mfma16h(k1[ks], qf[h][ks], S1[h]);
+      for (int ks = 0; ks < 4; ++ks) {
+        k0[ks] = *(const f16x8*)(kts + swz128(16 * (2 * half) + c, 4 * ks + gi));
+        k1[ks] = *(const f16x8*)(kts + swz128(16 * (2 * half + 1) + c, 4 * ks + gi));
       }
+      // head by head: the next head's two score chains go out before this head's probabilities,
+      // so only two heads' scores are live at a time
+      auto head_scores = [&](int h, f32x4& A, f32x4& B) {
+        A = f32x4{0.f, 0.f, 0.f, 0.f};
+        B = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float p = fexp2(fmaf(S1[h][j], ct, -L2[h]));
-          if constexpr (MASK) p = j < lm1 ? p : 0.f;
-          P1[j] += p;
-          pb[h][4 + j] = (_Float16)p;
+        for (int ks = 0; ks < 4; ++ks) {
+          A = mfma16h(k0[ks], qf[h][ks], A);
+          B = mfma16h(k1[ks], qf[h][ks], B);
         }
-      }
-      // O^T += Vc^T P^T over the half's 32 keys: dims 16 db + c, this lane group's 8 key slots
+      };
+      // value fragments of the half (dims 16 db + c, this lane group's 8 key slots) in a ring of four:
+      // the first four are read beside the last head's probabilities (the key fragments are dead
+      // by then), each later one once the products of the one four places before it went out
       const _Float16* vts = (const _Float16*)lds_at(bi, L_VT);
+      auto vfrag = [&](int db) {
+        const int dim = 16 * db + c;
+        return *(const f16x8*)(vts + dim * CK + (((4 * half + gi) ^ (dim & 7)) << 3));
+      };
+      f16x8 vr[4];
+      f32x4 Sa, Sb;
+      head_scores(0, Sa, Sb);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        f32x4 Na, Nb;
+        if (h + 1 < G) head_scores(h + 1, Na, Nb);
+        if (h + 1 == G) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vr[i] = vfrag(i);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float pa = fexp2(fmaf(Sa[j], ct, -L2[h]));
+          float pc = fexp2(fmaf(Sb[j], ct, -L2[h]));
+          if constexpr (MASK) {
+            pa = j < lm0 ? pa : 0.f;
+            pc = j < lm1 ? pc : 0.f;
+          }
+          P0[j] = h ? P0[j] + pa : pa;
+          P1[j] = h ? P1[j] + pc : pc;
+          pb[h][j] = (_Float16)pa;
+          pb[h][4 + j] = (_Float16)pc;
+        }
+        if (h + 1 < G) {
+          Sa = Na;
+          Sb = Nb;
+        }
+      }
+      // O^T += Vc^T P^T over the half's 32 keys
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const int dim = 16 * db + c;
-        const f16x8 vf = *(const f16x8*)(vts + dim * CK + (((4 * half + gi) ^ (dim & 7)) << 3));
+        const f16x8 vf = vr[db & 3];
 #pragma unroll
         for (int h = 0; h < G; ++h) O[h][db] = mfma16h(vf, pb[h], O[h][db]);
+        if (db + 4 < 8) vr[db & 3] = vfrag(db + 4);
       }
       // importance of this lane's row from M-blocks mb = 2 half, 2 half + 1 (keys 4k .. 4k + 3,
       // k = 16 tile + 4 mb + gi)
