@@ -365,7 +365,7 @@ def branch_outputs(wl, inp):
 BUDGET = 16 * 64 + 512   # tokens each video row attends in the selection + window branches
 # (selection block l', top-n, window) with l' n + w = BUDGET
 BUDGET_POINTS = [(64, 8, 1024), (64, 12, 768), (64, 16, 512), (64, 20, 256), (64, 22, 128), (64, 23, 64),
-                 (32, 32, 512), (32, 40, 256), (128, 8, 512), (128, 10, 256)]
+                 (32, 24, 768), (32, 32, 512), (128, 8, 512), (128, 10, 256)]
 
 
 def budget_sweep(args, wl, inp):

@@ -161,35 +161,55 @@ __device__ __forceinline__ void scores16(const _Float16* kts, int mb, int c, int
   }
 }
 
-// Stores the importance of one row for a tile's 16 selection blocks j0 .. j0 + 15 (blocks after jmax
-// are not written).  On entry lane group gi holds blocks j0 + 4 mb + gi in v0..v3 (mb = 0..3); a 4 x 4
-// transpose among the row's four lanes (lanes c, c + 16, c + 32, c + 48) gives lane group gi blocks
-// j0 + 4 gi .. +3, so the row's 64 bytes leave in one instruction, 16 contiguous bytes a lane (the
-// whole row's run for the tile instead of four 16-byte pieces at different times).
-__device__ __forceinline__ void store_imp_tile(float* __restrict__ imp_row, int64_t j0, int64_t jmax, float v0,
-                                               float v1, float v2, float v3) {
-  const int l = threadIdx.x & 63, gi = l >> 4, c = l & 15;
-  auto pick = [](int i, float a, float b, float d, float e) { return i == 0 ? a : (i == 1 ? b : (i == 2 ? d : e)); };
-  float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    // this lane sends block (gi + r) & 3 of its run; it receives from lane group (gi - r) & 3
-    const float x = pick((gi + r) & 3, v0, v1, v2, v3);
-    const int k = (gi - r) & 3;
-    const float y = __shfl(x, (k << 4) | c, 64);
-    w0 = k == 0 ? y : w0;
-    w1 = k == 1 ? y : w1;
-    w2 = k == 2 ? y : w2;
-    w3 = k == 3 ? y : w3;
-  }
-  const int64_t j = j0 + 4 * gi;  // w0..w3 are blocks j .. j + 3
-  if (j + 3 <= jmax && (((uintptr_t)(imp_row + j)) & 15) == 0) {
-    *(float4*)(imp_row + j) = make_float4(w0, w1, w2, w3);
+// 4 x 4 transpose among a row's four lanes (lanes c, c + 16, c + 32, c + 48): on entry lane group
+// gi holds items (mb, gi) in v0..v3 (mb = 0..3); on exit it holds items (gi, k) in w0..w3 (k = 0..3).
+// Two exchange steps of gfx950's lane swaps (no LDS round trip): v_permlane32_swap trades the upper
+// 32 lanes of its first operand with the lower 32 of its second (lane groups gi and gi ^ 2: v0 with
+// v2, v1 with v3), v_permlane16_swap the odd 16-lane rows of its first operand with the even rows of
+// its second (lane groups gi and gi ^ 1).
+__device__ __forceinline__ void row_transpose4(float v0, float v1, float v2, float v3, float& w0, float& w1,
+                                               float& w2, float& w3) {
+  const auto a02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v2), false, false);
+  const auto a13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v1), __float_as_uint(v3), false, false);
+  const auto b01 = __builtin_amdgcn_permlane16_swap(a02[0], a13[0], false, false);
+  const auto b23 = __builtin_amdgcn_permlane16_swap(a02[1], a13[1], false, false);
+  w0 = __uint_as_float(b01[0]);
+  w1 = __uint_as_float(b01[1]);
+  w2 = __uint_as_float(b23[0]);
+  w3 = __uint_as_float(b23[1]);
+}
+
+// The value of lane group gi - 1 (group 3 for gi = 0) of the same row, by lane swaps: odd lane
+// groups take their even neighbour directly, even ones the neighbour of their opposite group.
+__device__ __forceinline__ float row_rotate1(float x) {
+  const int gi = (threadIdx.x & 63) >> 4;
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // odd groups: a[0] = group gi - 1
+  const auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned y = gi < 2 ? b[1] : b[0];                              // group gi ^ 2
+  const auto d = __builtin_amdgcn_permlane16_swap(y, y, false, false);  // even groups: d[1] = y of gi + 1
+  return __uint_as_float((gi & 1) ? a[0] : d[1]);
+}
+
+// Stores the importance of one row for a tile's 32 selection blocks of 32 tokens, j0 .. j0 + 31
+// (blocks after jmax are not written): on entry lane group gi holds blocks j0 + 8 mb + 2 gi in
+// a0..a3 and j0 + 8 mb + 2 gi + 1 in b0..b3; after two transposes it holds blocks j0 + 8 gi .. +7
+// and stores them as 32 contiguous bytes.
+__device__ __forceinline__ void store_imp_tile32(float* __restrict__ imp_row, int64_t j0, int64_t jmax, float a0,
+                                                 float a1, float a2, float a3, float b0, float b1, float b2,
+                                                 float b3) {
+  const int gi = (threadIdx.x & 63) >> 4;
+  float w[8];
+  row_transpose4(a0, a1, a2, a3, w[0], w[2], w[4], w[6]);
+  row_transpose4(b0, b1, b2, b3, w[1], w[3], w[5], w[7]);
+  const int64_t j = j0 + 8 * gi;  // w[0..7] are blocks j .. j + 7
+  if (j + 7 <= jmax && (((uintptr_t)(imp_row + j)) & 15) == 0) {
+    *(float4*)(imp_row + j) = make_float4(w[0], w[1], w[2], w[3]);
+    *(float4*)(imp_row + j + 4) = make_float4(w[4], w[5], w[6], w[7]);
   } else {
-    if (j <= jmax) imp_row[j] = w0;
-    if (j + 1 <= jmax) imp_row[j + 1] = w1;
-    if (j + 2 <= jmax) imp_row[j + 2] = w2;
-    if (j + 3 <= jmax) imp_row[j + 3] = w3;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (j + e <= jmax) imp_row[j + e] = w[e];
   }
 }
 
@@ -436,8 +456,9 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
 #pragma unroll
     for (int db = 0; db < 8; ++db) O[h][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   int sh_prev = 0;    // the range scale shift folded into L2
-  float rprev = 0.f;  // half share of the previous M-block's last compressed key (lane group 3's, shifted)
-  const int srcl = (l + 48) & 63;  // lane group gi - 1 (group 3 for gi = 0)
+  // half share of the last compressed key before this lane's first (64-token blocks: of the previous
+  // tile's last block, in lane group 0; else of the previous M-block's, lane group 3's shifted)
+  float rprev = 0.f;
   // one tile: per 32-key half, the scores and probabilities of its two M-blocks, the value product and
   // the importance of their two selection blocks per lane; MASK as in sweep 1.  The value
   // tile's range scale sh = s_tile - s_ref (<= 0) enters the probabilities' exponent; their sums
@@ -452,21 +473,31 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
     sh_prev = sh;
     // importance of this lane's row in the tile: block 16 tile + 4 mb + gi for mb = 0..3
     float im0 = 0.f, im1 = 0.f, im2 = 0.f, im3 = 0.f;
+    // with 64-token blocks the carry-outs of the four M-blocks, with 32-token blocks the second block of each
+    float jm0 = 0.f, jm1 = 0.f, jm2 = 0.f, jm3 = 0.f;
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
-      f16x8 pb[G];  // P^T operands of the half's 32 keys: M-block 2 half in slots 0..3, the next in 4..7
       float P0[4], P1[4];  // sums over the heads
       const int lm0 = lim_of(tile, 2 * half), lm1 = lim_of(tile, 2 * half + 1);
-      // key fragments of both M-blocks, read once for all heads
+      // key fragments of both M-blocks and the value fragments (dims 16 db + c, this lane group's
+      // 8 key slots), read once for all heads
       const _Float16* kts = (const _Float16*)lds_at(bi, L_KT);
-      f16x8 k0[4], k1[4];
+      const _Float16* vts = (const _Float16*)lds_at(bi, L_VT);
+      f16x8 k0[4], k1[4], vr[8];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         k0[ks] = *(const f16x8*)(kts + swz128(16 * (2 * half) + c, 4 * ks + gi));
         k1[ks] = *(const f16x8*)(kts + swz128(16 * (2 * half + 1) + c, 4 * ks + gi));
       }
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const int dim = 16 * db + c;
+        vr[db] = *(const f16x8*)(vts + dim * CK + (((4 * half + gi) ^ (dim & 7)) << 3));
+      }
       // head by head: the next head's two score chains go out before this head's probabilities,
-      // so only two heads' scores are live at a time
+      // and this head's value products (O^T += Vc^T P^T over the half's 32 keys) right after
+      // them, so the matrix products of one head run beside the exponentials of the next and only
+      // two heads' scores are live at a time
       auto head_scores = [&](int h, f32x4& A, f32x4& B) {
         A = f32x4{0.f, 0.f, 0.f, 0.f};
         B = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -476,25 +507,13 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
           B = mfma16h(k1[ks], qf[h][ks], B);
         }
       };
-      // value fragments of the half (dims 16 db + c, this lane group's 8 key slots) in a ring of four:
-      // the first four are read beside the last head's probabilities (the key fragments are dead
-      // by then), each later one once the products of the one four places before it went out
-      const _Float16* vts = (const _Float16*)lds_at(bi, L_VT);
-      auto vfrag = [&](int db) {
-        const int dim = 16 * db + c;
-        return *(const f16x8*)(vts + dim * CK + (((4 * half + gi) ^ (dim & 7)) << 3));
-      };
-      f16x8 vr[4];
       f32x4 Sa, Sb;
       head_scores(0, Sa, Sb);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         f32x4 Na, Nb;
         if (h + 1 < G) head_scores(h + 1, Na, Nb);
-        if (h + 1 == G) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) vr[i] = vfrag(i);
-        }
+        f16x8 pb;  // P^T operand of the half's 32 keys: M-block 2 half in slots 0..3, the next in 4..7
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float pa = fexp2(fmaf(Sa[j], ct, -L2[h]));
@@ -505,21 +524,15 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
           }
           P0[j] = h ? P0[j] + pa : pa;
           P1[j] = h ? P1[j] + pc : pc;
-          pb[h][j] = (_Float16)pa;
-          pb[h][4 + j] = (_Float16)pc;
+          pb[j] = (_Float16)pa;
+          pb[4 + j] = (_Float16)pc;
         }
+#pragma unroll
+        for (int db = 0; db < 8; ++db) O[h][db] = mfma16h(vr[db], pb, O[h][db]);
         if (h + 1 < G) {
           Sa = Na;
           Sb = Nb;
         }
-      }
-      // O^T += Vc^T P^T over the half's 32 keys
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const f16x8 vf = vr[db & 3];
-#pragma unroll
-        for (int h = 0; h < G; ++h) O[h][db] = mfma16h(vf, pb[h], O[h][db]);
-        if (db + 4 < 8) vr[db & 3] = vfrag(db + 4);
       }
       // importance of this lane's row from M-blocks mb = 2 half, 2 half + 1 (keys 4k .. 4k + 3,
       // k = 16 tile + 4 mb + gi)
@@ -528,30 +541,40 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
         const float* P = mi ? P1 : P0;
         const int64_t kq = (int64_t)tile * 16 + 4 * (2 * half + mi) + gi;
         const float t = 0.5f * P[3] * unscale;
-        const float rc = __shfl(t, srcl, 64);  // t of lane group gi - 1, or of group 3 for gi = 0
+        if constexpr (LS == 64) {
+          // block k without the half of key 4k - 1 (x), and the half of key 4k + 3 that block k + 1
+          // takes (t); the carries are added once per tile, after the transpose
+          const float x = (P[0] + P[1] + P[2]) * unscale + t;
+          if (mi == 0) {
+            im0 = half ? im0 : x;
+            im2 = half ? x : im2;
+            jm0 = half ? jm0 : t;
+            jm2 = half ? t : jm2;
+          } else {
+            im1 = half ? im1 : x;
+            im3 = half ? x : im3;
+            jm1 = half ? jm1 : t;
+            jm3 = half ? t : jm3;
+          }
+          continue;
+        }
+        const float rc = row_rotate1(t);  // t of lane group gi - 1, or of group 3 for gi = 0
         const float carry = gi ? rc : rprev;   // half of the key before this lane's first
         rprev = rc;
-        if constexpr (LS == 64) {
-          const float v = (P[0] + P[1] + P[2]) * unscale + t + carry;  // block k
-          if (mi == 0) {
-            im0 = half ? im0 : v;
-            im2 = half ? v : im2;
-          } else {
-            im1 = half ? im1 : v;
-            im3 = half ? v : im3;
-          }
-        } else if constexpr (LS == 32) {
+        if constexpr (LS == 32) {
           const float hp1 = 0.5f * P[1] * unscale;
           const float b0 = carry + P[0] * unscale + hp1;  // block 2k
           const float b1 = hp1 + P[2] * unscale + t;      // block 2k + 1
-          if (imp_row) {
-            const int64_t J = 2 * kq;
-            if (J + 1 <= jmax && (((uintptr_t)(imp_row + J)) & 7) == 0) {
-              *(float2*)(imp_row + J) = make_float2(b0, b1);
-            } else {
-              if (J <= jmax) imp_row[J] = b0;
-              if (J + 1 <= jmax) imp_row[J + 1] = b1;
-            }
+          if (mi == 0) {
+            im0 = half ? im0 : b0;
+            im2 = half ? b0 : im2;
+            jm0 = half ? jm0 : b1;
+            jm2 = half ? b1 : jm2;
+          } else {
+            im1 = half ? im1 : b0;
+            im3 = half ? b0 : im3;
+            jm1 = half ? jm1 : b1;
+            jm3 = half ? b1 : jm3;
           }
         } else {
           // lane groups 2m, 2m + 1 hold block k / 2: keys 8J .. 8J + 3 whole (and the half of 8J - 1),
@@ -567,7 +590,29 @@ cmp_group_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ k
       }
     }
     if constexpr (LS == 64) {
-      if (imp_row) store_imp_tile(imp_row, (int64_t)tile * 16, jmax, im0, im1, im2, im3);
+      // lane group gi now holds blocks 16 tile + 4 gi + q (q = 0..3): X[q] and the carry-outs T[q];
+      // block 4 gi + q takes T[q - 1], and for q = 0 the last carry-out of lane group gi - 1, or for
+      // gi = 0 that of the previous tile's last block
+      float X0, X1, X2, X3, T0, T1, T2, T3;
+      row_transpose4(im0, im1, im2, im3, X0, X1, X2, X3);
+      row_transpose4(jm0, jm1, jm2, jm3, T0, T1, T2, T3);
+      const float R = row_rotate1(T3);
+      const float cin = gi ? R : rprev;
+      rprev = R;  // for lane group 0: this tile's block 15
+      if (imp_row) {
+        const int64_t j = (int64_t)tile * 16 + 4 * gi;
+        const float w0 = X0 + cin, w1 = X1 + T0, w2 = X2 + T1, w3 = X3 + T2;
+        if (j + 3 <= jmax && (((uintptr_t)(imp_row + j)) & 15) == 0) {
+          *(float4*)(imp_row + j) = make_float4(w0, w1, w2, w3);
+        } else {
+          if (j <= jmax) imp_row[j] = w0;
+          if (j + 1 <= jmax) imp_row[j + 1] = w1;
+          if (j + 2 <= jmax) imp_row[j + 2] = w2;
+          if (j + 3 <= jmax) imp_row[j + 3] = w3;
+        }
+      }
+    } else if constexpr (LS == 32) {
+      if (imp_row) store_imp_tile32(imp_row, (int64_t)tile * 32, jmax, im0, im1, im2, im3, jm0, jm1, jm2, jm3);
     }
   };
   const int nt2 = nvmax > 0 ? nvmax / CK + 1 : 0;

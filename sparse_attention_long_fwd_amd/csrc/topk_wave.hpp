@@ -10,8 +10,9 @@
 // are compacted into LDS, one per lane (a wave prefix sum gives each lane its slots), and the
 // exact kk-th largest value among them is found by a bitwise search on order-preserving integer
 // keys with wave ballots; ties at that value go to the lower block indices.  Rows with more
-// candidates than the registers hold, or more than 64 values >= th (heavy ties), take kk rounds
-// of a wave-wide arg-max instead, each strictly after the previous pick.
+// candidates than the registers hold take the same steps over two streamed passes; rows with more
+// than 64 values >= th (heavy ties) take kk rounds of a wave-wide arg-max instead, each strictly
+// after the previous pick.
 #pragma once
 #include "common.hpp"
 
@@ -57,7 +58,8 @@ __device__ __forceinline__ uint32_t tk_kth_key(uint32_t key, int kk) {
 
 // x: importance indexed by block (global or LDS).  Free candidates [lo, hi); forced blocks
 // [0, lo) and [hi, nj); kk = places for free candidates (n minus the forced count); out: n
-// entries.  Whole wave, uniform arguments.  TK: register slots a lane takes (see wave_select).
+// entries.  Whole wave, uniform arguments.  TK: register slots a lane takes (see wave_select);
+// 0: the candidates are streamed twice instead of held.
 template <int TK>
 __device__ inline void wave_select_tk(const float* __restrict__ x, int lo, int hi, int nj, int kk, int n,
                                       TopkScratch* sc, int32_t* __restrict__ out, int lane) {
@@ -73,36 +75,65 @@ __device__ inline void wave_select_tk(const float* __restrict__ x, int lo, int h
       in_sel = true;
     } else {
       bool done = false;
-      if (nc <= 64 * TK) {
-        float cv[TK];
-        float lm = -INFINITY;
-#pragma unroll
-        for (int c = 0; c < TK; ++c) {  // unconditional (clamped) loads, all in flight at once
-          const int j = lo + lane + 64 * c;
-          cv[c] = x[j < hi ? j : hi - 1];
-        }
-#pragma unroll
-        for (int c = 0; c < TK; ++c) {
-          if (lo + lane + 64 * c >= hi) cv[c] = -INFINITY;
-          else lm = fmaxf(lm, cv[c]);
-        }
-        // th: the kk-th largest lane maximum (lanes without a candidate take no part)
-        const uint32_t thk = tk_kth_key(lane < nc ? tk_key(lm) : 0u, kk);
-        // compact the candidates >= th into LDS, one ballot per register slot that has any
+      if (TK == 0 || nc <= 64 * TK) {
+        // compact the candidates >= th into LDS, one ballot per slot that has any
         int total = 0;
-#pragma unroll
-        for (int c = 0; c < TK; ++c) {
-          const int j = lo + lane + 64 * c;
-          const bool take = j < hi && tk_key(cv[c]) >= thk;
+        auto compact = [&](float v, int j, uint32_t thk) {
+          const bool take = j < hi && tk_key(v) >= thk;
           const uint64_t bal = __ballot(take);
-          if (bal == 0) continue;  // uniform
+          if (bal == 0) return;  // uniform
           const int pos = total + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
           if (take && pos < 64) {
-            sc->v[pos] = cv[c];
+            sc->v[pos] = v;
             sc->j[pos] = j;
           }
           total += (int)__popcll(bal);
+        };
+        if constexpr (TK > 0) {
+          float cv[TK > 0 ? TK : 1];
+          float lm = -INFINITY;
+#pragma unroll
+          for (int c = 0; c < TK; ++c) {  // unconditional (clamped) loads, all in flight at once
+            const int j = lo + lane + 64 * c;
+            cv[c] = x[j < hi ? j : hi - 1];
+          }
+#pragma unroll
+          for (int c = 0; c < TK; ++c) {
+            if (lo + lane + 64 * c >= hi) cv[c] = -INFINITY;
+            else lm = fmaxf(lm, cv[c]);
+          }
+          // th: the kk-th largest lane maximum (lanes without a candidate take no part)
+          const uint32_t thk = tk_kth_key(lane < nc ? tk_key(lm) : 0u, kk);
+#pragma unroll
+          for (int c = 0; c < TK; ++c) compact(cv[c], lo + lane + 64 * c, thk);
+        } else {
+          // more candidates than the registers hold: the same steps over two streamed passes
+          // (the second reads what the first brought into the caches), SB loads in flight a lane
+          constexpr int SB = 8;
+          float lm = -INFINITY;
+          for (int j0 = lo; j0 < hi; j0 += 64 * SB) {
+            float cv[SB];
+#pragma unroll
+            for (int c = 0; c < SB; ++c) {
+              const int j = j0 + lane + 64 * c;
+              cv[c] = x[j < hi ? j : hi - 1];
+            }
+#pragma unroll
+            for (int c = 0; c < SB; ++c)
+              if (j0 + lane + 64 * c < hi) lm = fmaxf(lm, cv[c]);
+          }
+          const uint32_t thk = tk_kth_key(lane < nc ? tk_key(lm) : 0u, kk);
+          for (int j0 = lo; j0 < hi; j0 += 64 * SB) {
+            float cv[SB];
+#pragma unroll
+            for (int c = 0; c < SB; ++c) {
+              const int j = j0 + lane + 64 * c;
+              cv[c] = x[j < hi ? j : hi - 1];
+            }
+#pragma unroll
+            for (int c = 0; c < SB; ++c) compact(cv[c], j0 + lane + 64 * c, thk);
+          }
         }
         if (total <= 64) {
           tk_wave_sync();
@@ -180,7 +211,8 @@ __device__ inline void wave_select(const float* __restrict__ x, int lo, int hi, 
   if (nc <= 64 * 4) wave_select_tk<4>(x, lo, hi, nj, kk, n, sc, out, lane);
   else if (nc <= 64 * 8) wave_select_tk<8>(x, lo, hi, nj, kk, n, sc, out, lane);
   else if (nc <= 64 * 16) wave_select_tk<16>(x, lo, hi, nj, kk, n, sc, out, lane);
-  else wave_select_tk<TK_REG>(x, lo, hi, nj, kk, n, sc, out, lane);
+  else if (nc <= 64 * TK_REG) wave_select_tk<TK_REG>(x, lo, hi, nj, kk, n, sc, out, lane);
+  else wave_select_tk<0>(x, lo, hi, nj, kk, n, sc, out, lane);
 }
 
 // Forced-block bounds of the row at absolute position t: free candidates [*lo, *hi), forced

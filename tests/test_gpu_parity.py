@@ -113,10 +113,16 @@ def test_cmp_attn_scores_optional_outputs(want, path):
 
 
 # --------------------------------------------------------------------------- top-n
-@pytest.mark.parametrize("n,n_init,n_local,Ns", [(4, 1, 2, 16), (16, 1, 2, 568), (16, 1, 2, 2048), (8, 2, 3, 300),
-                                                  (32, 1, 2, 2048), (3, 0, 3, 50)])
-def test_topk_blocks_exact(n, n_init, n_local, Ns):
-    flush("topk n=%d Ns=%d" % (n, Ns))
+@pytest.mark.parametrize("n,n_init,n_local,Ns,fine", [(4, 1, 2, 16, False), (16, 1, 2, 568, False),
+                                                       (16, 1, 2, 2048, False), (8, 2, 3, 300, False),
+                                                       (32, 1, 2, 2048, False), (3, 0, 3, 50, False),
+                                                       (16, 1, 2, 5000, False), (32, 1, 2, 4096, True),
+                                                       (16, 1, 2, 6000, True)])
+def test_topk_blocks_exact(n, n_init, n_local, Ns, fine):
+    """Against the oracle bit for bit.  Coarse values (many exact ties, decided by the lower index);
+    fine values for rows with more candidates than the per-lane registers hold (the streamed
+    threshold path; coarse values there take the arg-max rounds)."""
+    flush("topk n=%d Ns=%d fine=%s" % (n, Ns, fine))
     ls = 64
     T = Ns * ls
     R, Hkv = 700, 4
@@ -126,6 +132,8 @@ def test_topk_blocks_exact(n, n_init, n_local, Ns):
     pos[-1] = T - 1
     # coarse values: many exact ties, decided by the lower index on both sides
     imp = (rng.integers(0, 40, (R, Hkv, Ns)) / 64.0).astype(np.float32)
+    if fine:
+        imp = rng.random((R, Hkv, Ns)).astype(np.float32)
     # rows of q given explicitly: one batch element per row keeps arbitrary positions
     sh = nsa.make_shape(R, 1, T, 0, Hkv, Hkv, 8)
     imp_d = torch.from_numpy(imp).to(DEV).view(R, 1, Hkv, Ns)
