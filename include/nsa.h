@@ -186,8 +186,8 @@ int32_t nsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t
  * rows).  workspace: device scratch; the size depends on the kernels the call
  * dispatches to, so query it after any nsa_set_force_generic change.
  * Row chunks: a prefill on the MFMA path (bf16, head_dim 128, cmp_block 32 /
- * stride 16, sel_block 64, 4..8 query heads per KV head) may run as passes
- * over chunks of query rows.  Every stage except the compression of K / V is
+ * stride 16, and sel_block 64 with 4..8 query heads per KV head or sel_block
+ * 32 or 128 with 4..7) may run as passes over chunks of query rows.  Every stage except the compression of K / V is
  * independent across rows, so the results are bit-identical to one pass; each
  * batch element's K / V are compressed once.  The call takes the largest chunk
  * (all rows, else a multiple of 64) whose scratch fits workspace_bytes, and

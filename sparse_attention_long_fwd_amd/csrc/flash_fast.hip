@@ -61,6 +61,23 @@ __device__ __forceinline__ void flash_pass(const bf16* __restrict__ kbase, const
     for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
   }
   if (kt1 <= kt0) return;
+  // keys every active column admits: [lo_all, hi_all] (the largest klo, the smallest khi); tiles
+  // inside it need no key mask (inactive columns then take unmasked scores, which only their own
+  // output columns see)
+  int64_t lo_all = active ? klo : INT64_MIN, hi_all = active ? khi : INT64_MAX;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const int64_t a = __shfl_xor(lo_all, o, 64), b = __shfl_xor(hi_all, o, 64);
+    lo_all = a > lo_all ? a : lo_all;
+    hi_all = b < hi_all ? b : hi_all;
+  }
+  auto uniform64 = [](int64_t x) {  // the same in every lane: keep it in scalar registers
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+  };
+  lo_all = uniform64(lo_all);
+  hi_all = uniform64(hi_all);
   auto arr = [&](int bufi, int a) { return buf0 + (bufi * 2 + a) * TILE; };
   auto stage = [&](int kt, int bufi) {
     stage_tile64(arr(bufi, 0), kbase, stride, (int64_t)kt * FK, T, w, G, l);
@@ -74,6 +91,7 @@ __device__ __forceinline__ void flash_pass(const bf16* __restrict__ kbase, const
     const int bufi = (kt - kt0) & 1;
     if (kt + 1 < kt1) stage(kt + 1, bufi ^ 1);
     const bf16* ks_ = arr(bufi, 0);
+    const bool full = (int64_t)kt * FK >= lo_all && (int64_t)kt * FK + FK - 1 <= hi_all;  // uniform
     float x[32];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -81,10 +99,15 @@ __device__ __forceinline__ void flash_pass(const bf16* __restrict__ kbase, const
       const int row = kb * 32 + n;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) s = mfma32(lds_read8(ks_ + swz128(row, 2 * ks + hl)), qf[ks], s);
+      if (full) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int64_t key = (int64_t)kt * FK + kb * 32 + 8 * (j >> 2) + 4 * hl + (j & 3);
-        x[kb * 16 + j] = (active && key >= klo && key <= khi) ? s[j] * c2 : -INFINITY;
+        for (int j = 0; j < 16; ++j) x[kb * 16 + j] = s[j] * c2;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int64_t key = (int64_t)kt * FK + kb * 32 + 8 * (j >> 2) + 4 * hl + (j & 3);
+          x[kb * 16 + j] = (active && key >= klo && key <= khi) ? s[j] * c2 : -INFINITY;
+        }
       }
     }
     float mx = x[0];
