@@ -312,15 +312,37 @@ cmp_lse_kernel(const bf16* __restrict__ q, const unsigned char* __restrict__ kv1
     float ts[G];
 #pragma unroll
     for (int mb = 0; mb < 4; mb += 2) {
-      f32x4 Sa[G], Sb[G];
-      scores16<G>(kbuf[bi], mb, c, gi, qf, Sa);
-      scores16<G>(kbuf[bi], mb + 1, c, gi, qf, Sb);
+      // both M-blocks' key fragments read once; head by head, the next head's two score chains go
+      // out before this head's exponentials
+      f16x8 k0[4], k1[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        k0[ks] = *(const f16x8*)(kbuf[bi] + swz128(16 * mb + c, 4 * ks + gi));
+        k1[ks] = *(const f16x8*)(kbuf[bi] + swz128(16 * (mb + 1) + c, 4 * ks + gi));
+      }
+      auto head_scores = [&](int h, f32x4& A, f32x4& B) {
+        A = f32x4{0.f, 0.f, 0.f, 0.f};
+        B = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          A = mfma16h(k0[ks], qf[h][ks], A);
+          B = mfma16h(k1[ks], qf[h][ks], B);
+        }
+      };
+      f32x4 Sa, Sb;
+      head_scores(0, Sa, Sb);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
+        f32x4 Na, Nb;
+        if (h + 1 < G) head_scores(h + 1, Na, Nb);
         float a = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a += fexp2(fmaf(Sa[h][j], ct, -mr[h])) + fexp2(fmaf(Sb[h][j], ct, -mr[h]));
+        for (int j = 0; j < 4; ++j) a += fexp2(fmaf(Sa[j], ct, -mr[h])) + fexp2(fmaf(Sb[j], ct, -mr[h]));
         ts[h] = mb ? ts[h] + a : a;
+        if (h + 1 < G) {
+          Sa = Na;
+          Sb = Nb;
+        }
       }
     }
     bool ok = true;
