@@ -4,8 +4,11 @@
 // attends to keys [max(0, t - w + 1), t].  Text rows keep dense causal
 // attention over every key u <= t (shd-paper.top page, English abstract).
 //
-// One workgroup = 32 consecutive query rows x the G heads of one KV group (one
-// wave per head), the same tile as the compression branch: S^T = K Q^T with
+// One workgroup = 32 consecutive query rows x up to four heads of one KV group
+// (one wave per head; a group of G heads takes ceil(G / 4) workgroups, which
+// stage the same K/V tiles: two four-wave workgroups fit a compute unit at
+// this register count, so one's loads and barriers overlap the other's
+// products), the same tile as the compression branch: S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16, one (row, head) column per lane, online softmax in
 // the log2 domain with the running maximum shared by the two lane halves of a
 // column (one xor-32 exchange per 64-key tile), O^T += V^T P^T with V^T read
@@ -25,6 +28,7 @@
 namespace {
 constexpr int FQ = 32;
 constexpr int FK = 64;
+constexpr int FW = 4;  // waves (heads) per workgroup
 constexpr int HD = 128;
 constexpr int TILE = FK * HD;
 constexpr float RESCALE_SLACK = 8.f;
@@ -43,24 +47,30 @@ struct FlashOut {
   int max_split;  // tiles with rank < max_split are split
 };
 
-// One pass of online-softmax attention over key tiles [kt0, kt1) for the
-// lanes whose column is active; the key of each column is limited to
-// [klo, khi] (inclusive).  Returns (in the references) the running maximum,
-// the lane's partial sum and the accumulator (unnormalised).  RESUME: continue
-// from the state in the references instead of starting empty.
-template <bool RESUME = false>
-__device__ __forceinline__ void flash_pass(const bf16* __restrict__ kbase, const bf16* __restrict__ vbase,
-                                           int64_t stride, int64_t T, int kt0, int kt1, const bf16x8 (&qf)[8],
-                                           int64_t klo, int64_t khi, bool active, float c2, bf16* buf0, int w,
-                                           int G, int l, float& m_run, float& l_run, f32x16 (&oacc)[4]) {
+// One pass of online-softmax attention over key tiles [a0, a1) and then [b0, b1)
+// (one double-buffered stream: the first tile of the second range is staged
+// during the last of the first) for the lanes whose column is active; the key
+// of each column is limited to [klo, khi] (inclusive).  Returns (in the
+// references) the running maximum, the lane's partial sum and the accumulator
+// (unnormalised).  on_split() runs in every wave right after the last tile of
+// the first range, with the state over that range in the references.
+// compute = false: a wave without a head, which only stages tiles and keeps
+// the barriers.
+template <typename OnSplit>
+__device__ __forceinline__ void flash_pass2(const bf16* __restrict__ kbase, const bf16* __restrict__ vbase,
+                                            int64_t stride, int64_t T, int a0, int a1, int b0, int b1,
+                                            const bf16x8 (&qf)[8], int64_t klo, int64_t khi, bool active, float c2,
+                                            bf16* buf0, int w, int nw, int l, bool compute, float& m_run,
+                                            float& l_run, f32x16 (&oacc)[4], OnSplit on_split) {
   const int hl = l >> 5, n = l & 31, g16 = l >> 4, i16 = l & 15;
-  if (!RESUME) {
-    m_run = -INFINITY;
-    l_run = 0.f;
+  m_run = -INFINITY;
+  l_run = 0.f;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
-  }
-  if (kt1 <= kt0) return;
+  for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+  const int na = a1 > a0 ? a1 - a0 : 0, nt = na + (b1 > b0 ? b1 - b0 : 0);
+  if (na == 0) on_split();
+  if (nt == 0) return;
+  auto tile_of = [&](int i) { return i < na ? a0 + i : b0 + (i - na); };
   // keys every active column admits: [lo_all, hi_all] (the largest klo, the smallest khi); tiles
   // inside it need no key mask (inactive columns then take unmasked scores, which only their own
   // output columns see)
@@ -80,84 +90,99 @@ __device__ __forceinline__ void flash_pass(const bf16* __restrict__ kbase, const
   hi_all = uniform64(hi_all);
   auto arr = [&](int bufi, int a) { return buf0 + (bufi * 2 + a) * TILE; };
   auto stage = [&](int kt, int bufi) {
-    stage_tile64(arr(bufi, 0), kbase, stride, (int64_t)kt * FK, T, w, G, l);
-    stage_tile64(arr(bufi, 1), vbase, stride, (int64_t)kt * FK, T, w, G, l);
+    stage_tile64(arr(bufi, 0), kbase, stride, (int64_t)kt * FK, T, w, nw, l);
+    stage_tile64(arr(bufi, 1), vbase, stride, (int64_t)kt * FK, T, w, nw, l);
   };
   __syncthreads();  // previous users of the buffers are done
-  stage(kt0, 0);
+  stage(tile_of(0), 0);
   fwait_loads();
   __syncthreads();
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int bufi = (kt - kt0) & 1;
-    if (kt + 1 < kt1) stage(kt + 1, bufi ^ 1);
-    const bf16* ks_ = arr(bufi, 0);
-    const bool full = (int64_t)kt * FK >= lo_all && (int64_t)kt * FK + FK - 1 <= hi_all;  // uniform
-    float x[32];
+  for (int i = 0; i < nt; ++i) {
+    const int kt = tile_of(i);
+    const int bufi = i & 1;
+    if (i + 1 < nt) stage(tile_of(i + 1), bufi ^ 1);
+    if (compute) {
+      const bf16* ks_ = arr(bufi, 0);
+      const bool full = (int64_t)kt * FK >= lo_all && (int64_t)kt * FK + FK - 1 <= hi_all;  // uniform
+      float x[32];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = {};
-      const int row = kb * 32 + n;
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 s = {};
+        const int row = kb * 32 + n;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) s = mfma32(lds_read8(ks_ + swz128(row, 2 * ks + hl)), qf[ks], s);
-      if (full) {
+        for (int ks = 0; ks < 8; ++ks) s = mfma32(lds_read8(ks_ + swz128(row, 2 * ks + hl)), qf[ks], s);
+        if (full) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) x[kb * 16 + j] = s[j] * c2;
+          for (int j = 0; j < 16; ++j) x[kb * 16 + j] = s[j] * c2;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int64_t key = (int64_t)kt * FK + kb * 32 + 8 * (j >> 2) + 4 * hl + (j & 3);
+            x[kb * 16 + j] = (active && key >= klo && key <= khi) ? s[j] * c2 : -INFINITY;
+          }
+        }
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int j = 1; j < 32; ++j) mx = fmaxf(mx, x[j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (mx > m_run + RESCALE_SLACK) {
+        const float corr = fexp2(m_run - mx);  // 0 on the first raise from -inf
+        l_run *= corr;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) oacc[db][j] *= corr;
+        m_run = mx;
+      }
+      float p[32];
+      if (m_run > -INFINITY) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          p[j] = fexp2(x[j] - m_run);
+          l_run += p[j];
+        }
       } else {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int64_t key = (int64_t)kt * FK + kb * 32 + 8 * (j >> 2) + 4 * hl + (j & 3);
-          x[kb * 16 + j] = (active && key >= klo && key <= khi) ? s[j] * c2 : -INFINITY;
+        for (int j = 0; j < 32; ++j) p[j] = 0.f;
+      }
+      const bf16* vs_ = arr(bufi, 1);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          bf16x8 pb;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pb[e] = (bf16)p[kb * 16 + 8 * st + e];
+          const int vr = kb * 32 + 16 * st + 4 * (g16 >> 1) + (i16 >> 2);
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const int col = 32 * db + (g16 & 1) * 16 + 4 * (i16 & 3);
+            const int o0 = swz128(vr, col >> 3) + (col & 7);
+            const int o1 = swz128(vr + 8, col >> 3) + (col & 7);
+            oacc[db] = mfma32(cat(lds_read_tr(vs_ + o0), lds_read_tr(vs_ + o1)), pb, oacc[db]);
+          }
         }
       }
     }
-    float mx = x[0];
-#pragma unroll
-    for (int j = 1; j < 32; ++j) mx = fmaxf(mx, x[j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (mx > m_run + RESCALE_SLACK) {
-      const float corr = fexp2(m_run - mx);  // 0 on the first raise from -inf
-      l_run *= corr;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[db][j] *= corr;
-      m_run = mx;
-    }
-    float p[32];
-    if (m_run > -INFINITY) {
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        p[j] = fexp2(x[j] - m_run);
-        l_run += p[j];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 32; ++j) p[j] = 0.f;
-    }
-    const bf16* vs_ = arr(bufi, 1);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (bf16)p[kb * 16 + 8 * st + e];
-        const int vr = kb * 32 + 16 * st + 4 * (g16 >> 1) + (i16 >> 2);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int col = 32 * db + (g16 & 1) * 16 + 4 * (i16 & 3);
-          const int o0 = swz128(vr, col >> 3) + (col & 7);
-          const int o1 = swz128(vr + 8, col >> 3) + (col & 7);
-          oacc[db] = mfma32(cat(lds_read_tr(vs_ + o0), lds_read_tr(vs_ + o1)), pb, oacc[db]);
-        }
-      }
-    }
+    if (i + 1 == na) on_split();
     fwait_loads();
     __syncthreads();
   }
 }
 
-__global__ void __launch_bounds__(512) flash_fast_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+// The same over one range [kt0, kt1).
+__device__ __forceinline__ void flash_pass(const bf16* __restrict__ kbase, const bf16* __restrict__ vbase,
+                                           int64_t stride, int64_t T, int kt0, int kt1, const bf16x8 (&qf)[8],
+                                           int64_t klo, int64_t khi, bool active, float c2, bf16* buf0, int w,
+                                           int nw, int l, bool compute, float& m_run, float& l_run,
+                                           f32x16 (&oacc)[4]) {
+  flash_pass2(kbase, vbase, stride, T, kt0, kt1, 0, 0, qf, klo, khi, active, c2, buf0, w, nw, l, compute, m_run,
+              l_run, oacc, [] {});
+}
+
+__global__ void __launch_bounds__(FW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+flash_fast_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                          const bf16* __restrict__ v, const uint8_t* __restrict__ vid,
                                                          FlashOut fo, Dims dm, int ntq, int do_swa, int do_text) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -168,10 +193,15 @@ __global__ void __launch_bounds__(512) flash_fast_kernel(const bf16* __restrict_
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, hl = l >> 5, n = l & 31;
   const int nsplit = fo.nsplit;
-  // ranks [0, max_split * nsplit): (tile, chunk) of the split tiles; then one rank per remaining tile
+  // ranks [0, max_split * nsplit): (tile, chunk) of the split tiles; then one rank per remaining tile;
+  // each rank in nhs workgroups of up to FW heads (adjacent workgroup ranks)
   const int nsr = fo.max_split * nsplit;
-  int unit, rank;
-  if (!xcd_remap(blockIdx.x, (int)(dm.B * dm.Hkv), nsr + ntq - fo.max_split, &unit, &rank)) return;
+  const int nhs = (G + FW - 1) / FW;
+  int unit, wrank;
+  if (!xcd_remap(blockIdx.x, (int)(dm.B * dm.Hkv), (nsr + ntq - fo.max_split) * nhs, &unit, &wrank)) return;
+  const int rank = wrank / nhs;
+  const int hw = (wrank % nhs) * FW + w;  // this wave's head within the group
+  const bool hact = hw < G;               // a wave without a head stages tiles and keeps the barriers
   const bool split = rank < nsr;
   const int chunk = split ? rank % nsplit : 0;
   const int trank = split ? rank / nsplit : fo.max_split + (rank - nsr);  // tile rank, last tile first
@@ -195,7 +225,7 @@ __global__ void __launch_bounds__(512) flash_fast_kernel(const bf16* __restrict_
   const bool rvalid = r < dm.Tq;
   const bool isv = rvalid && (!vid || vid[b * dm.Tq + r]);
   const int64_t t = dm.q0 + r;
-  const int h = g * G + w;
+  const int h = g * G + (hact ? hw : 0);
   const float c2 = dm.scale * LOG2E_F;
   const int64_t rlast = (rt0 + FQ < dm.Tq ? rt0 + FQ : dm.Tq) - 1;
   const int64_t tfirst = dm.q0 + rt0, tlast = dm.q0 + rlast;
@@ -204,7 +234,7 @@ __global__ void __launch_bounds__(512) flash_fast_kernel(const bf16* __restrict_
   {
     const bf16* qrow = q + ((b * dm.Tq + (rvalid ? r : 0)) * dm.Hq + h) * (int64_t)HD + 8 * hl;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = rvalid ? *(const bf16x8*)(qrow + 16 * ks) : zero8();
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = (rvalid && hact) ? *(const bf16x8*)(qrow + 16 * ks) : zero8();
   }
   const int64_t stride = (int64_t)dm.Hkv * HD;
   const bf16* kbase = k + (b * dm.T * dm.Hkv + g) * (int64_t)HD;
@@ -227,36 +257,37 @@ __global__ void __launch_bounds__(512) flash_fast_kernel(const bf16* __restrict_
       const int jt = kt1 - 1;
       const int nle = dm.n_local < jt + 1 ? dm.n_local : jt + 1;
       const int ktl = jt - nle + 1 > kt0 ? jt - nle + 1 : kt0;
-      flash_pass(kbase, vbase, stride, dm.T, ktl, kt1, qf, klo, t, isv, c2, buf0, w, G, l, m_run, l_run, oacc);
-      const float lt = l_run + __shfl_xor(l_run, 32, 64);
-      if (isv) {
-        const int nvalid = dm.n < jt + 1 ? dm.n : jt + 1;
-        const int64_t rec0 = (((b * dm.Tq + r) * dm.Hkv + g) * dm.n + (nvalid - nle)) * G + w;
-        // normalised to sum 1 (the maximum is kept lazily and the fp16 record needs bounded values)
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+      flash_pass2(kbase, vbase, stride, dm.T, ktl, kt1, kt0, ktl, qf, klo, t, isv, c2, buf0, w, FW, l, hact, m_run,
+                  l_run, oacc, [&] {
+        const float lt = l_run + __shfl_xor(l_run, 32, 64);
+        if (isv && hact) {
+          const int nvalid = dm.n < jt + 1 ? dm.n : jt + 1;
+          const int64_t rec0 = (((b * dm.Tq + r) * dm.Hkv + g) * dm.n + (nvalid - nle)) * G + hw;
+          // normalised to sum 1 (the maximum is kept lazily and the fp16 record needs bounded values)
+          const float inv = lt > 0.f ? 1.f / lt : 0.f;
+          typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+          for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int j4 = 0; j4 < 4; ++j4) {
-            h4 x;
+            for (int j4 = 0; j4 < 4; ++j4) {
+              h4 x;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = (_Float16)(oacc[db][4 * j4 + e] * inv);
-            *(h4*)(fo.lo + rec0 * HD + 32 * db + 8 * j4 + 4 * hl) = x;
+              for (int e = 0; e < 4; ++e) x[e] = (_Float16)(oacc[db][4 * j4 + e] * inv);
+              *(h4*)(fo.lo + rec0 * HD + 32 * db + 8 * j4 + 4 * hl) = x;
+            }
+          if (hl == 0) {
+            fo.lml[rec0] = lt > 0.f ? make_float2(m_run + flog2(lt), 1.f) : make_float2(-INFINITY, 0.f);
+            for (int e = 1; e < nle; ++e) fo.lml[rec0 + (int64_t)e * G] = make_float2(-INFINITY, 0.f);
           }
-        if (hl == 0) {
-          fo.lml[rec0] = lt > 0.f ? make_float2(m_run + flog2(lt), 1.f) : make_float2(-INFINITY, 0.f);
-          for (int e = 1; e < nle; ++e) fo.lml[rec0 + (int64_t)e * G] = make_float2(-INFINITY, 0.f);
         }
-      }
-      flash_pass<true>(kbase, vbase, stride, dm.T, kt0, ktl, qf, klo, t, isv, c2, buf0, w, G, l, m_run, l_run,
-                       oacc);
+      });
     } else {
-      flash_pass(kbase, vbase, stride, dm.T, kt0, kt1, qf, klo, t, isv, c2, buf0, w, G, l, m_run, l_run, oacc);
+      flash_pass(kbase, vbase, stride, dm.T, kt0, kt1, qf, klo, t, isv, c2, buf0, w, FW, l, hact, m_run, l_run,
+                 oacc);
     }
     const float lt = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (isv) {
+    if (isv && hact) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -287,11 +318,13 @@ __global__ void __launch_bounds__(512) flash_fast_kernel(const bf16* __restrict_
       kt0 = chunk * per;
       kt1 = kt0 + per < ktall ? kt0 + per : ktall;
     }
-    flash_pass(kbase, vbase, stride, dm.T, kt0, kt1, qf, 0, t, ist, c2, buf0, w, G, l, m_run, l_run, oacc);
+    flash_pass(kbase, vbase, stride, dm.T, kt0, kt1, qf, 0, t, ist, c2, buf0, w, FW, l, hact, m_run, l_run, oacc);
     const float lt = l_run + __shfl_xor(l_run, 32, 64);
-    if (split) {
-      // partial for (tile slot, chunk, column w*32+n): [D] normalised output, then max and sum
-      float* pp = fo.part + (((int64_t)(unit * fo.max_split + trank) * nsplit + chunk) * (G * FQ) + w * FQ + n) *
+    if (!hact) {
+      // no head: nothing to store
+    } else if (split) {
+      // partial for (tile slot, chunk, column hw*32+n): [D] normalised output, then max and sum
+      float* pp = fo.part + (((int64_t)(unit * fo.max_split + trank) * nsplit + chunk) * (G * FQ) + hw * FQ + n) *
                                 (HD + 2);
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
@@ -415,7 +448,8 @@ hipError_t launch_flash_fast(const Dims& dm, const void* q, const void* k, const
   const int do_swa = (swa32 || swa_bf || local_ml) ? 1 : 0;
   const int do_text = text ? 1 : 0;
   if (!do_swa && !do_text) return hipSuccess;
-  dim3 grid(xcd_grid(units, fo.max_split * fo.nsplit + ntq - fo.max_split)), block(dm.G * 64);
+  const int nhs = (dm.G + FW - 1) / FW;
+  dim3 grid(xcd_grid(units, (fo.max_split * fo.nsplit + ntq - fo.max_split) * nhs)), block(FW * 64);
   const size_t shm = (size_t)2 * 2 * TILE * 2;
   hipError_t e = hipFuncSetAttribute((const void*)flash_fast_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)shm);
