@@ -65,6 +65,41 @@ PEAK_HBM = 8.0e12         # B/s, MI355X HBM3E
 METRIC = "NSA layer prefill tokens/s @128K (MFMA util %); decode GB/s @64K"
 
 
+def device_clock():
+    """The GPU's compute units and shader clock (the runtime's peak clock, and the current one from
+    the driver's sysfs table when readable), with the dense bf16 MFMA peak they give at 4,096
+    FLOP per cycle and compute unit (2.5 PFLOP/s at 256 units and 2.4 GHz).  The roofline keeps the
+    published peak; this records the clock it rests on."""
+    import ctypes
+    import glob
+    out = {}
+    try:
+        # the HIP runtime this process already runs on (no second copy)
+        path = next((ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln), None)
+        if path is None:
+            return out
+        hip = ctypes.CDLL(path)
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) == 0:  # hipDeviceAttributeClockRate, kHz
+            out["sclk_peak_mhz"] = v.value / 1000.0
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 63, 0) == 0:  # hipDeviceAttributeMultiprocessorCount
+            out["compute_units"] = v.value
+    except OSError:
+        pass
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for ln in open(f).read().splitlines():
+                if ln.strip().endswith("*"):
+                    out["sclk_now_mhz"] = float(ln.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+        except (OSError, ValueError, IndexError):
+            continue
+        if "sclk_now_mhz" in out:
+            break
+    if "sclk_peak_mhz" in out and "compute_units" in out:
+        out["bf16_dense_peak_tflops_from_clock"] = out["compute_units"] * 4096 * out["sclk_peak_mhz"] * 1e6 / 1e12
+    return out
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -978,6 +1013,7 @@ def main():
         "budget_gate_runs": sw5,
         "cpu_baseline": cpu,
         "counters": kernel_counters(),
+        "device": device_clock(),
     }
     print(json.dumps(line))
 
