@@ -875,7 +875,11 @@ int32_t nsa_gate_proj(const void* x, const void* w_g, const float* b_g, int32_t 
 size_t nsa_hybrid_layer_bwd_workspace_size(const nsa_shape* shape, const nsa_params* params, int32_t dtype) {
   Dims dm;
   if (check_dims(shape, params, dtype, &dm, true) != NSA_OK) return 0;
-  return bwd_workspace(dm);
+  // enough for either set of kernels (the matrix-core one needs 16-byte aligned tensors)
+  const size_t gen = bwd_workspace(dm);
+  if (g_force_generic.load() || !bwd_fast_supported(dtype, dm)) return gen;
+  const size_t fast = bwd_fast_workspace(dm);
+  return fast > gen ? fast : gen;
 }
 
 int32_t nsa_hybrid_layer_bwd(const void* q, const void* k, const void* v, const float* w_k, const float* w_v,
@@ -891,13 +895,18 @@ int32_t nsa_hybrid_layer_bwd(const void* q, const void* k, const void* v, const 
   if (!q || !k || !v || !gates || !block_idx || !d_out || !dq || !dk || !dv || !d_gates || !dw_k || !dw_v)
     return fail(NSA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (dm.Nc > 0 && (!w_k || !w_v)) return fail(NSA_ERR_INVALID_ARG, "NULL compression weights");
-  if (!bwd_supported(dm)) return fail(NSA_ERR_UNSUPPORTED, "backward kernels cover head_dim 64, 128, 192, 256");
-  const size_t need = bwd_workspace(dm);
+  const bool fast = !g_force_generic.load() && bwd_fast_supported(dtype, dm) && aligned16(q) && aligned16(k) &&
+                    aligned16(v) && aligned16(d_out) && aligned16(dq) && aligned16(dk) && aligned16(dv);
+  if (!fast && !bwd_supported(dm))
+    return fail(NSA_ERR_UNSUPPORTED, "backward kernels cover head_dim 64, 128, 192, 256");
+  const size_t need = fast ? bwd_fast_workspace(dm) : bwd_workspace(dm);
   if (workspace_bytes < need)
     return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, need);
   if (need > 0 && !workspace) return fail(NSA_ERR_INVALID_ARG, "NULL workspace");
-  hipError_t e = launch_layer_bwd(dtype, dm, q, k, v, w_k, w_v, gates, is_video, block_idx, d_out, dq, dk, dv,
-                                  d_gates, dw_k, dw_v, workspace, (hipStream_t)stream);
+  hipError_t e = fast ? launch_layer_bwd_fast(dm, q, k, v, w_k, w_v, gates, is_video, block_idx, d_out, dq, dk, dv,
+                                              d_gates, dw_k, dw_v, workspace, (hipStream_t)stream)
+                      : launch_layer_bwd(dtype, dm, q, k, v, w_k, w_v, gates, is_video, block_idx, d_out, dq, dk,
+                                         dv, d_gates, dw_k, dw_v, workspace, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "backward kernels");
   return NSA_OK;
 }

@@ -854,6 +854,27 @@ static hipError_t launch_bwd_t(const Dims& dm, const void* q, const void* k, con
   return hipGetLastError();
 }
 
+// The compression's share of dk, dv (dk[u] += sum_i w_k[u - i d] dkc[i], likewise v) and the
+// compression weight gradients dw_k, dw_v (cleared here, then summed over the batch) from the
+// gradients dkc, dvc of the compressed keys and values.
+hipError_t launch_bwd_compress_grads(int dtype, const Dims& dm, const float* dkc, const float* dvc, const float* w_k,
+                                     const float* w_v, const void* k, const void* v, float* dk, float* dv,
+                                     float* dw_k, float* dw_v, hipStream_t s) {
+  bwd_fill_kernel<<<dim3((unsigned)((dm.l + 255) / 256)), dim3(256), 0, s>>>(dw_k, dm.l);
+  bwd_fill_kernel<<<dim3((unsigned)((dm.l + 255) / 256)), dim3(256), 0, s>>>(dw_v, dm.l);
+  if (dm.Nc <= 0) return hipGetLastError();
+  const int64_t tot = dm.B * dm.T * dm.Hkv * dm.D;
+  bwd_compress_kernel<<<dim3((unsigned)((tot + BWD_THREADS - 1) / BWD_THREADS)), dim3(BWD_THREADS), 0, s>>>(
+      dkc, dvc, w_k, w_v, dk, dv, dm);
+  const dim3 gd((unsigned)((dm.Nc + 15) / 16), (unsigned)dm.B);
+  if (dtype == 1)
+    bwd_dw_kernel<bf16><<<gd, dim3(BWD_THREADS), 0, s>>>(dkc, dvc, (const bf16*)k, (const bf16*)v, dw_k, dw_v, dm);
+  else
+    bwd_dw_kernel<float><<<gd, dim3(BWD_THREADS), 0, s>>>(dkc, dvc, (const float*)k, (const float*)v, dw_k, dw_v,
+                                                          dm);
+  return hipGetLastError();
+}
+
 hipError_t launch_layer_bwd(int dtype, const Dims& dm, const void* q, const void* k, const void* v, const float* w_k,
                             const float* w_v, const float* gates, const uint8_t* vid, const int32_t* idx,
                             const void* dout, float* dq, float* dk, float* dv, float* dgates, float* dw_k,

@@ -1,0 +1,1027 @@
+// Backward pass of the hybrid layer on the matrix cores (bf16 inputs, head_dim 128, gfx950).
+//
+// The forward is the layer of the other kernels (top168.com digest of VideoNSA, section 一; csdn
+// page "VideoNSA：重新定义视频理解的稀疏注意力机制", sections 2.2 and 3.1): for video rows
+// out = g_c o_c + g_s o_s + g_w o_w over the compression, selection and window branches, for text
+// rows dense causal attention.  Per branch b of one (row, head), with P the probabilities over its
+// keys and E_b = sum_u P_u <d_out, v_u>:
+//   d g_b = E_b,   ds_u = g_b P_u (<d_out, v_u> - E_b),
+//   dq += scale sum_u ds_u k_u,   dk_u += scale ds_u q,   dv_u += g_b P_u d_out
+// (text rows: one branch over the keys [0, t], g = 1).  The chosen blocks are an input and pass no
+// gradient.  Compressed keys and values are weighted block sums of k and v; their gradients go
+// back through the weights afterwards (launch_bwd_compress_grads).
+//
+// Every score is formed again from bf16 q, k, v and d_out (exact products, fp32 sums): once for the
+// branch statistics (log-sum-exp and E) and once for each gradient product.  P and ds enter the
+// matrix products as a bf16 high part plus a bf16 remainder (two products, within 2^-17 of the
+// fp32 value), and so do the compressed keys and values (their fp32 sums split at compression),
+// so the gradients keep the accuracy of fp32 accumulation.
+//
+// Kernels, per (batch, KV group):
+//  bwdf_row_kernel<CMP>: 16 query rows x the group's heads (a wave per head); two sweeps over the
+//    rows' keys, staged 64 at a time in LDS: the statistics (online max, sum and sum P dP), then
+//    dq^T += K^T ds^T.  CMP: the compressed keys visible to the video rows (the first writer of dq
+//    and of statistics slot 0); else the window keys of video rows and the keys [0, t] of text rows
+//    (adds to dq; slot 2).
+//  bwdf_key_kernel<CMP>: 64 keys (16 a wave) x the rows that can see them, 32 rows of one head at a
+//    time with their q and d_out staged in LDS: S = Q K^T, dv^T += d_out^T (g P),
+//    dk^T += Q^T ds.  Row tiles are split into chunks whose sums go out with atomic adds.
+//  Selection, block-major over the pair lists of launch_slc_pair_lists (32 (row, slot) pairs of one
+//    chosen block per workgroup): bwdf_sel_stats_kernel leaves per (row, slot, head) the block's
+//    max, sum and sum P dP; bwdf_sel_merge_kernel combines a row's slots (statistics slot 1, d
+//    gates); bwdf_sel_dq_kernel adds dq and bwdf_sel_kv_kernel dk, dv (atomic adds).
+// The order of the atomic adds depends on scheduling: the last bits of dq, dk and dv can differ
+// from one call to the next.
+#include "fast_common.hpp"
+
+namespace {
+constexpr int HD = 128;
+constexpr int RT = 16;                 // query rows per row-kernel tile
+constexpr int KT = 64;                 // keys per key tile
+constexpr int KR = 32;                 // query rows per key-kernel row tile
+constexpr int PRC = 32;                // pairs per selection chunk
+constexpr int NOKEY = 0x7fffffff;      // first key of a row that sees none
+constexpr int RTC_WIN = 128, RTC_CMP = 32;  // row tiles per chunk of the key kernels
+}  // namespace
+
+// Element i of hv / lv: the bf16 high part and remainder of x (x - hi is exact in fp32; hi + lo is
+// within 2^-17 |x| of x)
+__device__ __forceinline__ void split2(float x, bf16x8& hv, bf16x8& lv, int i) {
+  const bf16 hi = (bf16)x;
+  hv[i] = hi;
+  lv[i] = (bf16)(x - (float)hi);
+}
+
+// Rows [row0, row0 + ROWS) of a [*, 128] bf16 array (row stride `stride` elements) into a swizzled
+// ROWS x 128 LDS tile (swz128) with direct global -> LDS loads, ROWS / 4 instructions of 64 lanes x
+// 16 bytes over nw waves; rows at or past nrows repeat row nrows - 1 (masked by the callers).
+template <int ROWS>
+__device__ __forceinline__ void stage_rows_bw(bf16* lds_tile, const bf16* src, int64_t stride, int64_t row0,
+                                              int64_t nrows, int w, int nw, int lane) {
+  for (int ins = w; ins < ROWS / 4; ins += nw) {
+    const int p = ins * 64 + lane;
+    const int row = p >> 4, c = (p & 15) ^ (row & 15);
+    int64_t r = row0 + row;
+    if (r >= nrows) r = nrows - 1;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + r * stride + c * 8),
+                                     (__attribute__((address_space(3))) void*)(lds_tile + ins * 512), 16, 0, 0);
+  }
+}
+
+// A operand of a 16x16x32 product, read transposed from a swizzled [rows][128] LDS tile: lane
+// (c = l % 16, gi = l / 16) gets column 16 db + c of rows r0 + 4 gi .. +3, then of rows
+// r0 + 16 + 4 gi .. +3 — the K order of a B operand built from two 16-row accumulator blocks
+// (elements j = 0..3 of the first block, then of the second).
+__device__ __forceinline__ bf16x8 tr_a16(const bf16* tile, int r0, int db, int c, int gi) {
+  const int col = 16 * db + 4 * (c & 3);
+  const int ra = r0 + 4 * gi + (c >> 2);
+  return cat(lds_read_tr(tile + swz128(ra, col >> 3) + (col & 7)),
+             lds_read_tr(tile + swz128(ra + 16, col >> 3) + (col & 7)));
+}
+
+__device__ __forceinline__ float swap_halves(float x, int hl) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(hl ? r[0] : r[1]);
+}
+
+// Keys [klo, khi] of a row in the branch's key index space (klo = NOKEY, khi = -1: none).  CMP: the
+// compressed keys a video row sees; else the window keys of a video row and [0, t] for a text row.
+template <bool CMP>
+__device__ __forceinline__ void row_keys(int64_t t, bool isv, const Dims& dm, int& klo, int& khi) {
+  klo = NOKEY;
+  khi = -1;
+  if (CMP) {
+    if (isv) {
+      const int64_t nv = cmp_visible(t, dm.l, dm.d, dm.Nc);
+      if (nv > 0) {
+        klo = 0;
+        khi = (int)nv - 1;
+      }
+    }
+  } else {
+    klo = isv ? (int)(t - dm.w + 1 > 0 ? t - dm.w + 1 : 0) : 0;
+    khi = (int)t;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row kernel: one workgroup per (batch, 16-row tile, KV group), wave w = head g G + w.  S^T = K Q^T
+// (keys on M, the tile's rows on N: lane (c, gi) holds rows c, keys 16 mb + 4 gi + j), the row
+// statistics per lane, dq^T = K^T ds^T with K^T read transposed from the key tile.
+template <bool CMP>
+__global__ void __launch_bounds__(512)
+    bwdf_row_kernel(const bf16* __restrict__ q, const bf16* __restrict__ dout, const bf16* __restrict__ kh,
+                    const bf16* __restrict__ kl, const bf16* __restrict__ vh, const bf16* __restrict__ vl,
+                    const uint8_t* __restrict__ vid, const float* __restrict__ gates, float* __restrict__ dq,
+                    float* __restrict__ dgates, float* __restrict__ st_l, float* __restrict__ st_e, Dims dm) {
+  constexpr int NT = CMP ? 4 : 2;  // LDS tiles per key tile: K, V (and their remainders)
+  constexpr int SLOT = CMP ? 0 : 2;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  bf16* lds = (bf16*)smem;
+  const int G = dm.G;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gi = l >> 4;
+  const int ntile = (int)((dm.Tq + RT - 1) / RT);
+  const int64_t r0 = (int64_t)(ntile - 1 - (int)blockIdx.x) * RT;  // later (longer) tiles first
+  const int g = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int64_t r = r0 + c;
+  const bool rvalid = r < dm.Tq;
+  const int64_t rr = rvalid ? r : dm.Tq - 1;
+  const int64_t t = dm.q0 + rr;
+  const bool isv = vid ? vid[b * dm.Tq + rr] != 0 : true;
+  const int h = g * G + w;
+  const int64_t row = (b * dm.Tq + rr) * dm.Hq + h;
+  const int64_t N = CMP ? dm.Nc : dm.T;
+  int klo, khi;
+  row_keys<CMP>(t, isv, dm, klo, khi);
+  if (!rvalid) {
+    klo = NOKEY;
+    khi = -1;
+  }
+  // the tile's key range and the range every row sees in full (the same in every wave)
+  int kmin = klo, kmax = khi, maxlo = klo, minhi = khi;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    kmin = min(kmin, __shfl_xor(kmin, o, 64));
+    kmax = max(kmax, __shfl_xor(kmax, o, 64));
+    maxlo = max(maxlo, __shfl_xor(maxlo, o, 64));
+    minhi = min(minhi, __shfl_xor(minhi, o, 64));
+  }
+  kmin = __builtin_amdgcn_readfirstlane(kmin);
+  kmax = __builtin_amdgcn_readfirstlane(kmax);
+  maxlo = __builtin_amdgcn_readfirstlane(maxlo);
+  minhi = __builtin_amdgcn_readfirstlane(minhi);
+  const int kt0 = kmax >= kmin ? kmin / KT : 0;
+  const int nk = kmax >= kmin ? kmax / KT - kmin / KT + 1 : 0;
+
+  bf16x8 qf[4], df[4];  // Q^T and d_out^T operands: row c, dims 32 ks + 8 gi .. +8
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    qf[ks] = *(const bf16x8*)(q + row * HD + 32 * ks + 8 * gi);
+    df[ks] = *(const bf16x8*)(dout + row * HD + 32 * ks + 8 * gi);
+  }
+  const float gate = CMP ? (isv ? gates[row * 3] : 0.f) : (isv ? gates[row * 3 + 2] : 1.f);
+  const float cs = dm.scale * LOG2E_F;
+
+  const int64_t kstride = (int64_t)dm.Hkv * HD;
+  const int64_t koff = (b * N * dm.Hkv + g) * (int64_t)HD;
+  auto stage = [&](int buf, int kt) {
+    bf16* base = lds + (size_t)buf * NT * KT * HD;
+    stage_rows_bw<KT>(base, kh + koff, kstride, (int64_t)kt * KT, N, w, G, l);
+    stage_rows_bw<KT>(base + KT * HD, vh + koff, kstride, (int64_t)kt * KT, N, w, G, l);
+    if constexpr (CMP) {
+      stage_rows_bw<KT>(base + 2 * KT * HD, kl + koff, kstride, (int64_t)kt * KT, N, w, G, l);
+      stage_rows_bw<KT>(base + 3 * KT * HD, vl + koff, kstride, (int64_t)kt * KT, N, w, G, l);
+    }
+  };
+  // one pass over the key tiles, each staged one ahead into the other buffer
+  auto sweep = [&](auto body) {
+    if (nk <= 0) return;
+    stage(0, kt0);
+    for (int i = 0; i < nk; ++i) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (i + 1 < nk) stage((i + 1) & 1, kt0 + i + 1);
+      body((const bf16*)(lds + (size_t)(i & 1) * NT * KT * HD), kt0 + i);
+    }
+    __syncthreads();  // every wave is done with the buffers before they are staged again
+  };
+  // S^T and dP^T = V d_out^T of one key tile
+  auto scores = [&](const bf16* base, f32x4(&S)[4], f32x4(&P)[4]) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) S[mb] = P[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int o = swz128(16 * mb + c, 4 * ks + gi);
+        S[mb] = mfma16(lds_read8(base + o), qf[ks], S[mb]);
+        P[mb] = mfma16(lds_read8(base + KT * HD + o), df[ks], P[mb]);
+        if constexpr (CMP) {
+          S[mb] = mfma16(lds_read8(base + 2 * KT * HD + o), qf[ks], S[mb]);
+          P[mb] = mfma16(lds_read8(base + 3 * KT * HD + o), df[ks], P[mb]);
+        }
+      }
+  };
+  auto full_tile = [&](int kt) { return kt * KT >= maxlo && kt * KT + KT - 1 <= minhi; };
+
+  // sweep 1: this lane's share of the row's max, sum and sum P dP (log2 units)
+  float m_run = -INFINITY, l_run = 0.f, e_run = 0.f;
+  sweep([&](const bf16* base, int kt) {
+    f32x4 S[4], P[4];
+    scores(base, S, P);
+    const bool full = full_tile(kt);
+    float x[16], mt = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v = S[mb][j] * cs;
+        if (!full) {
+          const int u = kt * KT + 16 * mb + 4 * gi + j;
+          if (u < klo || u > khi) v = -INFINITY;
+        }
+        x[4 * mb + j] = v;
+        mt = fmaxf(mt, v);
+      }
+    const float mn = fmaxf(m_run, mt), mref = mn == -INFINITY ? 0.f : mn;
+    const float a = fexp2(m_run - mref);
+    float ls = 0.f, es = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fexp2(x[i] - mref);
+      ls += p;
+      es = fmaf(p, P[i >> 2][i & 3], es);
+    }
+    l_run = fmaf(l_run, a, ls);
+    e_run = fmaf(e_run, a, es);
+    m_run = mn;
+  });
+#pragma unroll
+  for (int o = 16; o < 64; o <<= 1) {
+    const float mo = __shfl_xor(m_run, o, 64), lo = __shfl_xor(l_run, o, 64), eo = __shfl_xor(e_run, o, 64);
+    const float mn = fmaxf(m_run, mo), mref = mn == -INFINITY ? 0.f : mn;
+    const float a = fexp2(m_run - mref), a2 = fexp2(mo - mref);
+    l_run = l_run * a + lo * a2;
+    e_run = e_run * a + eo * a2;
+    m_run = mn;
+  }
+  const bool has = l_run > 0.f;
+  const float L2 = has ? m_run + log2f(l_run) : INFINITY;  // P = 2^(S cs - L2); none when empty
+  const float E = has ? e_run / l_run : 0.f;
+
+  // sweep 2: dq^T += K^T ds^T, ds = g P (dP - E) as bf16 high part + remainder
+  f32x4 dqa[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) dqa[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  sweep([&](const bf16* base, int kt) {
+    f32x4 S[4], P[4];
+    scores(base, S, P);
+    const bool full = full_tile(kt);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      bf16x8 bh, bl;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int mb = 2 * hh + sub;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float p = fexp2(fmaf(S[mb][j], cs, -L2));
+          if (!full) {
+            const int u = kt * KT + 16 * mb + 4 * gi + j;
+            if (u < klo || u > khi) p = 0.f;
+          }
+          split2(gate * p * (P[mb][j] - E), bh, bl, 4 * sub + j);
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const bf16x8 a = tr_a16(base, 32 * hh, db, c, gi);
+        dqa[db] = mfma16(a, bh, dqa[db]);
+        dqa[db] = mfma16(a, bl, dqa[db]);
+        if constexpr (CMP) dqa[db] = mfma16(tr_a16(base + 2 * KT * HD, 32 * hh, db, c, gi), bh, dqa[db]);
+      }
+    }
+  });
+  if (!rvalid) return;
+  // dq^T register j of dims block db holds dim 16 db + 4 gi + j of row c
+  float* dst = dq + row * HD + 4 * gi;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    float4 v = make_float4(dqa[db][0] * dm.scale, dqa[db][1] * dm.scale, dqa[db][2] * dm.scale,
+                           dqa[db][3] * dm.scale);
+    if constexpr (!CMP) {
+      const float4 o = *(const float4*)(dst + 16 * db);
+      v.x += o.x;
+      v.y += o.y;
+      v.z += o.z;
+      v.w += o.w;
+    }
+    *(float4*)(dst + 16 * db) = v;
+  }
+  if (gi == 0) {
+    st_l[row * 3 + SLOT] = L2;
+    st_e[row * 3 + SLOT] = E;
+    dgates[row * 3 + SLOT] = isv ? E : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Key kernel: one workgroup per (batch, 64 keys, row chunk, KV group); wave w owns keys
+// kbase + 16 w .. +15 (N of the products; K and V operands in registers) and sums over the heads and
+// the rows that see them.  S = Q K^T (the rows on M: lane (c, gi) holds rows 16 mb + 4 gi + j,
+// key c), dv^T += d_out^T (g P), dk^T += Q^T ds with Q and d_out read transposed from LDS.
+template <bool CMP>
+__global__ void __launch_bounds__(256)
+    bwdf_key_kernel(const bf16* __restrict__ q, const bf16* __restrict__ dout, const bf16* __restrict__ kh,
+                    const bf16* __restrict__ kl, const bf16* __restrict__ vh, const bf16* __restrict__ vl,
+                    const uint8_t* __restrict__ vid, const float* __restrict__ gates, const float* __restrict__ st_l,
+                    const float* __restrict__ st_e, const uint32_t* __restrict__ tbits, float* __restrict__ dk,
+                    float* __restrict__ dv, Dims dm, int nch) {
+  constexpr int SLOT = CMP ? 0 : 2;
+  constexpr int RTC = CMP ? RTC_CMP : RTC_WIN;
+  __shared__ __attribute__((aligned(16))) bf16 tq[2][KR * HD];
+  __shared__ __attribute__((aligned(16))) bf16 tdo[2][KR * HD];
+  __shared__ __attribute__((aligned(16))) float sL[2][KR], sE[2][KR], sG[2][KR];
+  __shared__ __attribute__((aligned(16))) int sLo[2][KR], sHi[2][KR];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gi = l >> 4;
+  const int64_t ktile = blockIdx.x / nch;
+  const int ch = (int)(blockIdx.x % nch);
+  const int g = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int G = dm.G;
+  const int64_t N = CMP ? dm.Nc : dm.T;
+  const int64_t kbase = ktile * KT;
+  const int64_t ntr = (dm.Tq + KR - 1) / KR;
+  // the first position that sees a key of the tile, the chunk's row tiles from there
+  const int64_t tfirst = CMP ? kbase * dm.d + dm.l - 1 : kbase;
+  const int64_t rfirst = tfirst - dm.q0 > 0 ? tfirst - dm.q0 : 0;
+  int64_t ra = rfirst / KR;
+  if (ra < (int64_t)ch * RTC) ra = (int64_t)ch * RTC;
+  const int64_t rb = (int64_t)(ch + 1) * RTC < ntr ? (int64_t)(ch + 1) * RTC : ntr;
+  // window rows past row tile `band` see none of the tile's keys; text rows see every key before them
+  const int64_t lastw = kbase + KT + dm.w - 2 - dm.q0;
+  const int64_t band = CMP ? ntr : (lastw < 0 ? 0 : lastw / KR + 1);
+  auto visit = [&](int64_t rt) -> bool { return rt < band || tbits[b * ntr + rt] != 0u; };
+  auto next_rt = [&](int64_t rt) -> int64_t {
+    for (++rt; rt < rb; ++rt)
+      if (visit(rt)) break;
+    return rt;
+  };
+  int64_t rt_first = ra;
+  if (rt_first < rb && !visit(rt_first)) rt_first = next_rt(rt_first);
+  if (rt_first >= rb) return;  // no row of the chunk sees the tile
+
+  const int64_t u = kbase + 16 * w + c;
+  const bool uvalid = u < N;
+  const int64_t ur = uvalid ? u : N - 1;
+  bf16x8 kf[4], vf[4], kfl[4], vfl[4];  // K^T, V^T operands: key c, dims 32 ks + 8 gi .. +8
+  {
+    const int64_t o = ((b * N + ur) * dm.Hkv + g) * (int64_t)HD + 8 * gi;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      kf[ks] = *(const bf16x8*)(kh + o + 32 * ks);
+      vf[ks] = *(const bf16x8*)(vh + o + 32 * ks);
+      if constexpr (CMP) {
+        kfl[ks] = *(const bf16x8*)(kl + o + 32 * ks);
+        vfl[ks] = *(const bf16x8*)(vl + o + 32 * ks);
+      }
+    }
+  }
+  const int64_t qstride = (int64_t)dm.Hq * HD;
+  auto stage = [&](int buf, int h, int64_t rt) {
+    const int64_t qo = (b * dm.Tq * dm.Hq + g * G + h) * (int64_t)HD;
+    stage_rows_bw<KR>(tq[buf], q + qo, qstride, rt * KR, dm.Tq, w, 4, l);
+    stage_rows_bw<KR>(tdo[buf], dout + qo, qstride, rt * KR, dm.Tq, w, 4, l);
+  };
+  // statistics of row rt KR + tid (tid < KR) of head g G + h
+  struct RowSt {
+    float L, E, G;
+    int lo, hi;
+  };
+  auto load_st = [&](int h, int64_t rt) -> RowSt {
+    RowSt s{INFINITY, 0.f, 0.f, NOKEY, -1};
+    const int64_t r = rt * KR + tid;
+    if (r < dm.Tq) {
+      const int64_t ri = (b * dm.Tq + r) * dm.Hq + g * G + h;
+      const bool isv = vid ? vid[b * dm.Tq + r] != 0 : true;
+      s.L = st_l[ri * 3 + SLOT];
+      s.E = st_e[ri * 3 + SLOT];
+      s.G = CMP ? (isv ? gates[ri * 3] : 0.f) : (isv ? gates[ri * 3 + 2] : 1.f);
+      row_keys<CMP>(dm.q0 + r, isv, dm, s.lo, s.hi);
+    }
+    return s;
+  };
+  auto put_st = [&](int buf, const RowSt& s) {
+    sL[buf][tid] = s.L;
+    sE[buf][tid] = s.E;
+    sG[buf][tid] = s.G;
+    sLo[buf][tid] = s.lo;
+    sHi[buf][tid] = s.hi;
+  };
+  const float cs = dm.scale * LOG2E_F;
+  f32x4 dka[8], dva[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) dka[db] = dva[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  stage(0, 0, rt_first);
+  if (tid < KR) put_st(0, load_st(0, rt_first));
+  int hcur = 0, buf = 0;
+  int64_t rtcur = rt_first;
+  for (;;) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    int hn = hcur;
+    int64_t rtn = next_rt(rtcur);
+    if (rtn >= rb) {
+      hn = hcur + 1;
+      rtn = rt_first;
+    }
+    const bool more = hn < G;
+    RowSt nst{};
+    if (more) {
+      stage(buf ^ 1, hn, rtn);
+      if (tid < KR) nst = load_st(hn, rtn);
+    }
+    // this item: head hcur, rows rtcur KR .. +31
+    {
+      const bf16* Qt = tq[buf];
+      const bf16* Dt = tdo[buf];
+      f32x4 S[2], P[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) S[mb] = P[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const int o = swz128(16 * mb + c, 4 * ks + gi);
+          const bf16x8 qa = lds_read8(Qt + o), da = lds_read8(Dt + o);
+          S[mb] = mfma16(qa, kf[ks], S[mb]);
+          P[mb] = mfma16(da, vf[ks], P[mb]);
+          if constexpr (CMP) {
+            S[mb] = mfma16(qa, kfl[ks], S[mb]);
+            P[mb] = mfma16(da, vfl[ks], P[mb]);
+          }
+        }
+      bf16x8 ph, pl, sh, sl;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int rq = 16 * mb + 4 * gi;
+        const float4 L4 = *(const float4*)&sL[buf][rq];
+        const float4 E4 = *(const float4*)&sE[buf][rq];
+        const float4 G4 = *(const float4*)&sG[buf][rq];
+        const int4 lo4 = *(const int4*)&sLo[buf][rq];
+        const int4 hi4 = *(const int4*)&sHi[buf][rq];
+        const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Ev[4] = {E4.x, E4.y, E4.z, E4.w};
+        const float Gv[4] = {G4.x, G4.y, G4.z, G4.w};
+        const int lov[4] = {lo4.x, lo4.y, lo4.z, lo4.w}, hiv[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float p = fexp2(fmaf(S[mb][j], cs, -Lv[j]));
+          if (!(uvalid && u >= lov[j] && u <= hiv[j])) p = 0.f;
+          const float gp = Gv[j] * p;
+          split2(gp, ph, pl, 4 * mb + j);
+          split2(gp * (P[mb][j] - Ev[j]), sh, sl, 4 * mb + j);
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const bf16x8 ad = tr_a16(Dt, 0, db, c, gi);
+        dva[db] = mfma16(ad, ph, dva[db]);
+        dva[db] = mfma16(ad, pl, dva[db]);
+        const bf16x8 aq = tr_a16(Qt, 0, db, c, gi);
+        dka[db] = mfma16(aq, sh, dka[db]);
+        dka[db] = mfma16(aq, sl, dka[db]);
+      }
+    }
+    if (!more) break;
+    if (tid < KR) put_st(buf ^ 1, nst);
+    hcur = hn;
+    rtcur = rtn;
+    buf ^= 1;
+  }
+  if (!uvalid) return;
+  // dk^T / dv^T register j of dims block db holds dim 16 db + 4 gi + j of key c
+  float* dkp = dk + ((b * N + u) * dm.Hkv + g) * (int64_t)HD + 4 * gi;
+  float* dvp = dv + ((b * N + u) * dm.Hkv + g) * (int64_t)HD + 4 * gi;
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      unsafeAtomicAdd(dkp + 16 * db + j, dka[db][j] * dm.scale);
+      unsafeAtomicAdd(dvp + 16 * db + j, dva[db][j]);
+    }
+}
+
+// tbits[b][wi] bit i: row 32 wi + i of batch b is a text row.
+__global__ void __launch_bounds__(256) bwdf_tbits_kernel(const uint8_t* __restrict__ vid, uint32_t* __restrict__ tbits,
+                                                         Dims dm) {
+  const int64_t ntr = (dm.Tq + 31) / 32;
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (x >= dm.B * ntr) return;
+  const int64_t b = x / ntr, wi = x % ntr;
+  uint32_t m = 0;
+  if (vid)
+    for (int i = 0; i < 32; ++i) {
+      const int64_t r = wi * 32 + i;
+      if (r < dm.Tq && !vid[b * dm.Tq + r]) m |= 1u << i;
+    }
+  tbits[x] = m;
+}
+
+__global__ void __launch_bounds__(256) bwdf_zero_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i + 3 < n) {
+    *(float4*)(p + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+  } else {
+    for (int64_t j = i; j < n; ++j) p[j] = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Selection, block-major.  One workgroup per chunk of up to 32 (row, slot) pairs of one block of SB
+// tokens.  The stats and dq kernels take a wave per head (wave w = head g G + w) with the block's K
+// and V staged in LDS and the pair's row on N (lane n = l % 32): S^T = K Q^T, dP^T = V d_out^T.
+template <int SB>
+struct SelChunk {
+  int64_t b, row, t, rowi;
+  int g, slot, j;
+  bool valid;
+};
+
+template <int SB>
+__device__ __forceinline__ bool sel_chunk_setup(const SlcPairLists& pl, const Dims& dm, int w, int n,
+                                                SelChunk<SB>& sc) {
+  const int bg = blockIdx.x / pl.cap_c, cc = blockIdx.x % pl.cap_c;
+  const int64_t ci = (int64_t)bg * pl.cap_c + cc;
+  sc.j = pl.chunk_blk[ci];
+  const int pr = pl.pairs[ci * PRC + n];
+  if (sc.j < 0) return false;
+  sc.b = bg / dm.Hkv;
+  sc.g = bg % dm.Hkv;
+  sc.valid = pr >= 0;
+  sc.row = sc.valid ? (pr >> 5) : 0;
+  sc.slot = pr & 31;
+  sc.t = dm.q0 + sc.row;
+  sc.rowi = (sc.b * dm.Tq + sc.row) * dm.Hq + sc.g * dm.G + w;
+  return true;
+}
+
+// S^T and dP^T of the chunk's block (keys kb 32 + 8 (jj / 4) + 4 hl + jj % 4 of register jj),
+// scaled to log2 units, keys after the row or past the sequence at -inf.
+template <int SB>
+__device__ __forceinline__ void sel_scores(const bf16* kt, const bf16* vt, const bf16x8 (&qf)[8],
+                                           const bf16x8 (&df)[8], const SelChunk<SB>& sc, const Dims& dm, int n,
+                                           int hl, float cs, f32x16 (&s)[SB / 32], f32x16 (&dp)[SB / 32]) {
+  constexpr int NKB = SB / 32;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    s[kb] = f32x16{};
+    dp[kb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int o = swz128(kb * 32 + n, 2 * ks + hl);
+      s[kb] = mfma32(lds_read8(kt + o), qf[ks], s[kb]);
+      dp[kb] = mfma32(lds_read8(vt + o), df[ks], dp[kb]);
+    }
+  }
+  const int64_t u0 = (int64_t)sc.j * SB;
+  const bool need_mask = u0 + SB - 1 > sc.t || u0 + SB > dm.T;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      float x = s[kb][jj] * cs;
+      if (need_mask) {
+        const int64_t u = u0 + kb * 32 + 8 * (jj >> 2) + 4 * hl + (jj & 3);
+        if (u > sc.t || u >= dm.T) x = -INFINITY;
+      }
+      s[kb][jj] = x;
+    }
+}
+
+template <int SB>
+__device__ __forceinline__ void sel_load_rows(const bf16* q, const bf16* dout, const SelChunk<SB>& sc, int hl,
+                                              bf16x8 (&qf)[8], bf16x8 (&df)[8]) {
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    qf[ks] = sc.valid ? *(const bf16x8*)(q + sc.rowi * HD + 16 * ks + 8 * hl) : zero8();
+    df[ks] = sc.valid ? *(const bf16x8*)(dout + sc.rowi * HD + 16 * ks + 8 * hl) : zero8();
+  }
+}
+
+// Per (pair, head): the block's max (log2 units), sum of 2^(x - max) and sum of 2^(x - max) dP.
+template <int SB>
+__global__ void __launch_bounds__(512)
+    bwdf_sel_stats_kernel(const bf16* __restrict__ q, const bf16* __restrict__ dout, const bf16* __restrict__ k,
+                          const bf16* __restrict__ v, SlcPairLists pl, float4* __restrict__ rec, Dims dm) {
+  constexpr int NKB = SB / 32;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  bf16* kt = (bf16*)smem;
+  bf16* vt = kt + SB * HD;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, n = l & 31;
+  SelChunk<SB> sc;
+  if (!sel_chunk_setup<SB>(pl, dm, w, n, sc)) return;
+  const int64_t stride = (int64_t)dm.Hkv * HD;
+  const int64_t kvb = (sc.b * dm.T * dm.Hkv + sc.g) * (int64_t)HD;
+  stage_rows_bw<SB>(kt, k + kvb, stride, (int64_t)sc.j * SB, dm.T, w, dm.G, l);
+  stage_rows_bw<SB>(vt, v + kvb, stride, (int64_t)sc.j * SB, dm.T, w, dm.G, l);
+  bf16x8 qf[8], df[8];
+  sel_load_rows<SB>(q, dout, sc, hl, qf, df);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  f32x16 s[NKB], dp[NKB];
+  sel_scores<SB>(kt, vt, qf, df, sc, dm, n, hl, dm.scale * LOG2E_F, s, dp);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s[kb][jj]);
+  mx = fmaxf(mx, swap_halves(mx, hl));
+  const float mref = mx == -INFINITY ? 0.f : mx;
+  float ls = 0.f, es = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const float p = fexp2(s[kb][jj] - mref);
+      ls += p;
+      es = fmaf(p, dp[kb][jj], es);
+    }
+  ls += swap_halves(ls, hl);
+  es += swap_halves(es, hl);
+  if (sc.valid && hl == 0)
+    rec[(((sc.b * dm.Tq + sc.row) * dm.Hkv + sc.g) * dm.n + sc.slot) * dm.G + w] = make_float4(mx, ls, es, 0.f);
+}
+
+// One thread per (batch, row, head): the selection branch's log-sum-exp (log2 units) and E over the
+// row's kept slots; d gates slot 1.  Text rows and rows with no kept slot: no keys.
+__global__ void __launch_bounds__(256)
+    bwdf_sel_merge_kernel(const float4* __restrict__ rec, const int32_t* __restrict__ idx,
+                          const uint8_t* __restrict__ vid, float* __restrict__ st_l, float* __restrict__ st_e,
+                          float* __restrict__ dgates, Dims dm) {
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (x >= dm.B * dm.Tq * dm.Hq) return;
+  const int64_t br = x / dm.Hq;
+  const int h = (int)(x % dm.Hq), g = h / dm.G, w = h % dm.G;
+  const int64_t jt = (dm.q0 + br % dm.Tq) / dm.ls;
+  const bool isv = vid ? vid[br] != 0 : true;
+  const int32_t* sel = idx + (br * dm.Hkv + g) * dm.n;
+  const float4* rr = rec + (br * dm.Hkv + g) * dm.n * dm.G + w;
+  float M = -INFINITY;
+  if (isv)
+    for (int s = 0; s < dm.n; ++s) {
+      const int j = sel[s];
+      if (j >= 0 && j <= jt) M = fmaxf(M, rr[s * dm.G].x);
+    }
+  float ls = 0.f, es = 0.f;
+  if (M > -INFINITY)
+    for (int s = 0; s < dm.n; ++s) {
+      const int j = sel[s];
+      if (j >= 0 && j <= jt) {
+        const float4 r4 = rr[s * dm.G];
+        const float a = fexp2(r4.x - M);
+        ls = fmaf(a, r4.y, ls);
+        es = fmaf(a, r4.z, es);
+      }
+    }
+  const bool has = ls > 0.f;
+  const float E = has ? es / ls : 0.f;
+  st_l[x * 3 + 1] = has ? M + log2f(ls) : INFINITY;
+  st_e[x * 3 + 1] = E;
+  dgates[x * 3 + 1] = isv ? E : 0.f;
+}
+
+// dq += scale K^T ds^T over the block's keys, per (pair, head), with atomic adds.
+template <int SB>
+__global__ void __launch_bounds__(512)
+    bwdf_sel_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ dout, const bf16* __restrict__ k,
+                       const bf16* __restrict__ v, const float* __restrict__ gates, const float* __restrict__ st_l,
+                       const float* __restrict__ st_e, SlcPairLists pl, float* __restrict__ dq, Dims dm) {
+  constexpr int NKB = SB / 32;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  bf16* kt = (bf16*)smem;
+  bf16* vt = kt + SB * HD;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, n = l & 31;
+  const int g16 = l >> 4, i16 = l & 15;
+  SelChunk<SB> sc;
+  if (!sel_chunk_setup<SB>(pl, dm, w, n, sc)) return;
+  const int64_t stride = (int64_t)dm.Hkv * HD;
+  const int64_t kvb = (sc.b * dm.T * dm.Hkv + sc.g) * (int64_t)HD;
+  stage_rows_bw<SB>(kt, k + kvb, stride, (int64_t)sc.j * SB, dm.T, w, dm.G, l);
+  stage_rows_bw<SB>(vt, v + kvb, stride, (int64_t)sc.j * SB, dm.T, w, dm.G, l);
+  bf16x8 qf[8], df[8];
+  sel_load_rows<SB>(q, dout, sc, hl, qf, df);
+  const float L2 = st_l[sc.rowi * 3 + 1], E = st_e[sc.rowi * 3 + 1], gate = gates[sc.rowi * 3 + 1];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  f32x16 s[NKB], dp[NKB];
+  sel_scores<SB>(kt, vt, qf, df, sc, dm, n, hl, dm.scale * LOG2E_F, s, dp);
+  f32x16 dqa[4] = {};
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      bf16x8 bh, bl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = fexp2(s[kb][8 * st + e] - L2);
+        split2(gate * p * (dp[kb][8 * st + e] - E), bh, bl, e);
+      }
+      // K^T operand: dims 32 db + l % 32, the 16 keys of (kb, st) in the order of the B operand
+      const int vr = kb * 32 + 16 * st + 4 * (g16 >> 1) + (i16 >> 2);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int col = 32 * db + (g16 & 1) * 16 + 4 * (i16 & 3);
+        const bf16x8 a = cat(lds_read_tr(kt + swz128(vr, col >> 3) + (col & 7)),
+                             lds_read_tr(kt + swz128(vr + 8, col >> 3) + (col & 7)));
+        dqa[db] = mfma32(a, bh, dqa[db]);
+        dqa[db] = mfma32(a, bl, dqa[db]);
+      }
+    }
+  if (!sc.valid) return;
+  // dq^T register jj of dims block db holds dim 32 db + 8 (jj / 4) + 4 hl + jj % 4 of row n
+  float* dst = dq + sc.rowi * HD + 4 * hl;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) unsafeAtomicAdd(dst + 32 * db + 8 * (jj >> 2) + (jj & 3), dqa[db][jj] * dm.scale);
+}
+
+// dk, dv of the block's keys from the chunk's pairs: SB / 16 waves of 16 keys each, the heads one
+// after the other with the pairs' q and d_out rows gathered into LDS (rows on M, as in the key
+// kernel), atomic adds.
+template <int SB>
+__global__ void __launch_bounds__(512)
+    bwdf_sel_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ dout, const bf16* __restrict__ k,
+                       const bf16* __restrict__ v, const float* __restrict__ gates, const float* __restrict__ st_l,
+                       const float* __restrict__ st_e, SlcPairLists pl, float* __restrict__ dk,
+                       float* __restrict__ dv, Dims dm) {
+  constexpr int NW = SB / 16;
+  __shared__ __attribute__((aligned(16))) bf16 tq[2][PRC * HD];
+  __shared__ __attribute__((aligned(16))) bf16 tdo[2][PRC * HD];
+  __shared__ __attribute__((aligned(16))) float sL[2][PRC], sE[2][PRC], sG[2][PRC];
+  __shared__ __attribute__((aligned(16))) int sT[PRC];
+  __shared__ int sRow[PRC];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gi = l >> 4;
+  const int bg = blockIdx.x / pl.cap_c, cc = blockIdx.x % pl.cap_c;
+  const int64_t ci = (int64_t)bg * pl.cap_c + cc;
+  const int j = pl.chunk_blk[ci];
+  if (j < 0) return;
+  const int64_t b = bg / dm.Hkv;
+  const int g = bg % dm.Hkv;
+  const int G = dm.G;
+  if (tid < PRC) {
+    const int pr = pl.pairs[ci * PRC + tid];
+    sRow[tid] = pr >= 0 ? (pr >> 5) : -1;
+    sT[tid] = pr >= 0 ? (int)(dm.q0 + (pr >> 5)) : -1;
+  }
+  const int64_t u = (int64_t)j * SB + 16 * w + c;
+  const bool uvalid = u < dm.T;
+  bf16x8 kf[4], vf[4];
+  {
+    const int64_t o = ((b * dm.T + (uvalid ? u : dm.T - 1)) * dm.Hkv + g) * (int64_t)HD + 8 * gi;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      kf[ks] = *(const bf16x8*)(k + o + 32 * ks);
+      vf[ks] = *(const bf16x8*)(v + o + 32 * ks);
+    }
+  }
+  __syncthreads();  // sRow, sT
+  // gathered rows: instruction ins fills LDS chunks [64 ins, +64) = pair rows 4 ins .. 4 ins + 3
+  auto stage = [&](int buf, int h) {
+    for (int ins = w; ins < PRC / 4; ins += NW) {
+      const int p = ins * 64 + l;
+      const int pr = p >> 4, cpos = p & 15, cl = cpos ^ (pr & 15);
+      const int rw = sRow[pr] >= 0 ? sRow[pr] : 0;
+      const int64_t o = ((b * dm.Tq + rw) * dm.Hq + g * G + h) * (int64_t)HD + cl * 8;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(q + o),
+                                       (__attribute__((address_space(3))) void*)(tq[buf] + ins * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(dout + o),
+                                       (__attribute__((address_space(3))) void*)(tdo[buf] + ins * 512), 16, 0, 0);
+    }
+  };
+  auto load_st = [&](int h, float& L, float& E, float& Gt) {
+    L = INFINITY;
+    E = 0.f;
+    Gt = 0.f;
+    if (sRow[tid] >= 0) {
+      const int64_t ri = (b * dm.Tq + sRow[tid]) * dm.Hq + g * G + h;
+      L = st_l[ri * 3 + 1];
+      E = st_e[ri * 3 + 1];
+      Gt = gates[ri * 3 + 1];
+    }
+  };
+  const float cs = dm.scale * LOG2E_F;
+  f32x4 dka[8], dva[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) dka[db] = dva[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  stage(0, 0);
+  if (tid < PRC) {
+    float L, E, Gt;
+    load_st(0, L, E, Gt);
+    sL[0][tid] = L;
+    sE[0][tid] = E;
+    sG[0][tid] = Gt;
+  }
+  for (int h = 0; h < G; ++h) {
+    const int buf = h & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    float nL = 0.f, nE = 0.f, nG = 0.f;
+    if (h + 1 < G) {
+      stage(buf ^ 1, h + 1);
+      if (tid < PRC) load_st(h + 1, nL, nE, nG);
+    }
+    const bf16* Qt = tq[buf];
+    const bf16* Dt = tdo[buf];
+    f32x4 S[2], P[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) S[mb] = P[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int o = swz128(16 * mb + c, 4 * ks + gi);
+        S[mb] = mfma16(lds_read8(Qt + o), kf[ks], S[mb]);
+        P[mb] = mfma16(lds_read8(Dt + o), vf[ks], P[mb]);
+      }
+    bf16x8 ph, pl2, sh, sl;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int rq = 16 * mb + 4 * gi;
+      const float4 L4 = *(const float4*)&sL[buf][rq];
+      const float4 E4 = *(const float4*)&sE[buf][rq];
+      const float4 G4 = *(const float4*)&sG[buf][rq];
+      const int4 T4 = *(const int4*)&sT[rq];
+      const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Ev[4] = {E4.x, E4.y, E4.z, E4.w};
+      const float Gv[4] = {G4.x, G4.y, G4.z, G4.w};
+      const int Tv[4] = {T4.x, T4.y, T4.z, T4.w};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float p = fexp2(fmaf(S[mb][jj], cs, -Lv[jj]));
+        if (!(uvalid && u <= (int64_t)Tv[jj])) p = 0.f;
+        const float gp = Gv[jj] * p;
+        split2(gp, ph, pl2, 4 * mb + jj);
+        split2(gp * (P[mb][jj] - Ev[jj]), sh, sl, 4 * mb + jj);
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const bf16x8 ad = tr_a16(Dt, 0, db, c, gi);
+      dva[db] = mfma16(ad, ph, dva[db]);
+      dva[db] = mfma16(ad, pl2, dva[db]);
+      const bf16x8 aq = tr_a16(Qt, 0, db, c, gi);
+      dka[db] = mfma16(aq, sh, dka[db]);
+      dka[db] = mfma16(aq, sl, dka[db]);
+    }
+    if (h + 1 < G && tid < PRC) {
+      sL[buf ^ 1][tid] = nL;
+      sE[buf ^ 1][tid] = nE;
+      sG[buf ^ 1][tid] = nG;
+    }
+  }
+  if (!uvalid) return;
+  float* dkp = dk + ((b * dm.T + u) * dm.Hkv + g) * (int64_t)HD + 4 * gi;
+  float* dvp = dv + ((b * dm.T + u) * dm.Hkv + g) * (int64_t)HD + 4 * gi;
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      unsafeAtomicAdd(dkp + 16 * db + jj, dka[db][jj] * dm.scale);
+      unsafeAtomicAdd(dvp + 16 * db + jj, dva[db][jj]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+bool bwd_fast_supported(int32_t dtype, const Dims& dm) {
+  if (dtype != 1 || dm.D != HD || dm.G < 1 || dm.G > 8 || dm.n < 0 || dm.n > 32) return false;
+  if (dm.ls != 32 && dm.ls != 64 && dm.ls != 128) return false;
+  return dm.T < (1ll << 31) - 2 * KT && dm.Tq < (1ll << 26) && dm.w >= 1;
+}
+
+static size_t frup(size_t x) { return (x + 255) & ~(size_t)255; }
+
+namespace {
+struct BwdWs {
+  bf16 *kch, *kcl, *vch, *vcl;
+  float *dkc, *dvc, *st_l, *st_e;
+  uint32_t* tbits;
+  float4* rec;
+  void* buckets;
+  size_t total;
+};
+}  // namespace
+
+static BwdWs bwd_fast_carve(const Dims& dm, void* ws) {
+  BwdWs w{};
+  char* p = (char*)ws;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    char* r = p ? p + o : nullptr;
+    o += frup(bytes);
+    return r;
+  };
+  const size_t nc = (size_t)dm.B * dm.Nc * dm.Hkv * HD;
+  w.kch = (bf16*)take(nc * 2);
+  w.kcl = (bf16*)take(nc * 2);
+  w.vch = (bf16*)take(nc * 2);
+  w.vcl = (bf16*)take(nc * 2);
+  w.dkc = (float*)take(nc * 4);
+  w.dvc = (float*)take(nc * 4);
+  const size_t rows = (size_t)dm.B * dm.Tq * dm.Hq * 3;
+  w.st_l = (float*)take(rows * 4);
+  w.st_e = (float*)take(rows * 4);
+  w.tbits = (uint32_t*)take((size_t)dm.B * ((dm.Tq + 31) / 32) * 4);
+  w.rec = (float4*)take((size_t)dm.B * dm.Tq * dm.Hkv * dm.n * dm.G * 16);
+  w.buckets = take(slc_bucket_bytes(dm));
+  w.total = o;
+  return w;
+}
+
+size_t bwd_fast_workspace(const Dims& dm) { return bwd_fast_carve(dm, nullptr).total; }
+
+static void zero_f32(float* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return;
+  bwdf_zero_kernel<<<dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, s>>>(p, n);
+}
+
+template <int SB>
+static hipError_t launch_sel_bwd(const Dims& dm, const bf16* q, const bf16* dout, const bf16* k, const bf16* v,
+                                 const float* gates, const SlcPairLists& pl, const BwdWs& w, float* dq, float* dk,
+                                 float* dv, hipStream_t s) {
+  const unsigned grid = (unsigned)(dm.B * dm.Hkv) * (unsigned)pl.cap_c;
+  const int shm = 2 * SB * HD * 2;
+  for (const void* fn : {(const void*)bwdf_sel_stats_kernel<SB>, (const void*)bwdf_sel_dq_kernel<SB>}) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, shm);
+    if (e != hipSuccess) return e;
+  }
+  bwdf_sel_stats_kernel<SB><<<dim3(grid), dim3(dm.G * 64), shm, s>>>(q, dout, k, v, pl, w.rec, dm);
+  return hipGetLastError();
+}
+
+template <int SB>
+static hipError_t launch_sel_bwd_grads(const Dims& dm, const bf16* q, const bf16* dout, const bf16* k,
+                                       const bf16* v, const float* gates, const SlcPairLists& pl, const BwdWs& w,
+                                       float* dq, float* dk, float* dv, hipStream_t s) {
+  const unsigned grid = (unsigned)(dm.B * dm.Hkv) * (unsigned)pl.cap_c;
+  const int shm = 2 * SB * HD * 2;
+  bwdf_sel_dq_kernel<SB><<<dim3(grid), dim3(dm.G * 64), shm, s>>>(q, dout, k, v, gates, w.st_l, w.st_e, pl, dq,
+                                                                   dm);
+  bwdf_sel_kv_kernel<SB><<<dim3(grid), dim3(SB / 16 * 64), 0, s>>>(q, dout, k, v, gates, w.st_l, w.st_e, pl, dk,
+                                                                    dv, dm);
+  return hipGetLastError();
+}
+
+hipError_t launch_layer_bwd_fast(const Dims& dm, const void* q_, const void* k_, const void* v_, const float* w_k,
+                                 const float* w_v, const float* gates, const uint8_t* vid, const int32_t* idx,
+                                 const void* dout_, float* dq, float* dk, float* dv, float* dgates, float* dw_k,
+                                 float* dw_v, void* ws, hipStream_t s) {
+  if (dm.B <= 0 || dm.Tq <= 0) return hipSuccess;
+  const bf16* q = (const bf16*)q_;
+  const bf16* k = (const bf16*)k_;
+  const bf16* v = (const bf16*)v_;
+  const bf16* dout = (const bf16*)dout_;
+  const BwdWs w = bwd_fast_carve(dm, ws);
+  hipError_t e = hipSuccess;
+  const int64_t nkv = dm.B * dm.T * dm.Hkv * HD, nc = dm.B * dm.Nc * dm.Hkv * HD;
+  zero_f32(dk, nkv, s);
+  zero_f32(dv, nkv, s);
+  zero_f32(w.dkc, nc, s);
+  zero_f32(w.dvc, nc, s);
+  if (dm.Nc > 0) {
+    e = launch_compress(1, 2, k, w_k, w.kch, w.kcl, dm.B, dm.T, dm.Hkv, HD, dm.l, dm.d, dm.Nc, s);
+    if (e == hipSuccess) e = launch_compress(1, 2, v, w_v, w.vch, w.vcl, dm.B, dm.T, dm.Hkv, HD, dm.l, dm.d, dm.Nc, s);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t ntr = (dm.Tq + 31) / 32;
+  bwdf_tbits_kernel<<<dim3((unsigned)((dm.B * ntr + 255) / 256)), dim3(256), 0, s>>>(vid, w.tbits, dm);
+  // row kernels: the compression branch first (it writes dq), then the window / text rows
+  {
+    const dim3 grid((unsigned)((dm.Tq + RT - 1) / RT), (unsigned)dm.Hkv, (unsigned)dm.B);
+    const int shc = 4 * 2 * KT * HD * 2, shw = 2 * 2 * KT * HD * 2;
+    e = hipFuncSetAttribute((const void*)bwdf_row_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, shc);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)bwdf_row_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, shw);
+    if (e != hipSuccess) return e;
+    bwdf_row_kernel<true><<<grid, dim3(dm.G * 64), shc, s>>>(q, dout, w.kch, w.kcl, w.vch, w.vcl, vid, gates, dq,
+                                                             dgates, w.st_l, w.st_e, dm);
+    bwdf_row_kernel<false><<<grid, dim3(dm.G * 64), shw, s>>>(q, dout, k, nullptr, v, nullptr, vid, gates, dq,
+                                                              dgates, w.st_l, w.st_e, dm);
+  }
+  // selection branch
+  SlcPairLists pl{};
+  if (dm.n > 0) {
+    e = launch_slc_pair_lists(dm, idx, vid, w.buckets, &pl, s);
+    if (e != hipSuccess) return e;
+    e = dm.ls == 32 ? launch_sel_bwd<32>(dm, q, dout, k, v, gates, pl, w, dq, dk, dv, s)
+                    : dm.ls == 128 ? launch_sel_bwd<128>(dm, q, dout, k, v, gates, pl, w, dq, dk, dv, s)
+                                   : launch_sel_bwd<64>(dm, q, dout, k, v, gates, pl, w, dq, dk, dv, s);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t nrh = dm.B * dm.Tq * dm.Hq;
+  bwdf_sel_merge_kernel<<<dim3((unsigned)((nrh + 255) / 256)), dim3(256), 0, s>>>(w.rec, idx, vid, w.st_l, w.st_e,
+                                                                                  dgates, dm);
+  if (dm.n > 0) {
+    e = dm.ls == 32 ? launch_sel_bwd_grads<32>(dm, q, dout, k, v, gates, pl, w, dq, dk, dv, s)
+                    : dm.ls == 128 ? launch_sel_bwd_grads<128>(dm, q, dout, k, v, gates, pl, w, dq, dk, dv, s)
+                                   : launch_sel_bwd_grads<64>(dm, q, dout, k, v, gates, pl, w, dq, dk, dv, s);
+    if (e != hipSuccess) return e;
+  }
+  // key kernels: window / text rows over the full-resolution keys, compression over the compressed ones
+  {
+    const int nchw = (int)((ntr + RTC_WIN - 1) / RTC_WIN);
+    const dim3 gw((unsigned)(((dm.T + KT - 1) / KT) * nchw), (unsigned)dm.Hkv, (unsigned)dm.B);
+    bwdf_key_kernel<false><<<gw, dim3(256), 0, s>>>(q, dout, k, nullptr, v, nullptr, vid, gates, w.st_l, w.st_e,
+                                                    w.tbits, dk, dv, dm, nchw);
+    if (dm.Nc > 0) {
+      const int nchc = (int)((ntr + RTC_CMP - 1) / RTC_CMP);
+      const dim3 gc((unsigned)(((dm.Nc + KT - 1) / KT) * nchc), (unsigned)dm.Hkv, (unsigned)dm.B);
+      bwdf_key_kernel<true><<<gc, dim3(256), 0, s>>>(q, dout, w.kch, w.kcl, w.vch, w.vcl, vid, gates, w.st_l,
+                                                     w.st_e, w.tbits, w.dkc, w.dvc, dm, nchc);
+    }
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_bwd_compress_grads(1, dm, w.dkc, w.dvc, w_k, w_v, k, v, dk, dv, dw_k, dw_v, s);
+}

@@ -76,6 +76,19 @@ hipError_t launch_sparse_select(const Dims& dm, const void* q, const void* ks, c
                                 bool ocmp_f32, const float* gates, void* out, void* o_slc, void* ws, hipStream_t s,
                                 const SideStream* side, bool forced_local);
 
+// The kept (row, slot) pairs of the video rows bucketed by chosen block (every pair whose block holds a
+// key at or before its row): chunk c of (batch, group) bg covers block chunk_blk[bg * cap_c + c]
+// (-1: unused) and its 32 pairs pairs[(bg * cap_c + c) * 32 + i] = (row << 5) | slot (-1 past the
+// list's end).  The arrays sit at the start of ws (slc_bucket_bytes(dm) bytes).
+struct SlcPairLists {
+  const int* chunk_blk;
+  const int* pairs;
+  int cap_c;
+};
+size_t slc_bucket_bytes(const Dims& dm);
+hipError_t launch_slc_pair_lists(const Dims& dm, const int32_t* idx, const uint8_t* vid, void* ws, SlcPairLists* pl,
+                                 hipStream_t s);
+
 // Window / text-row flash kernel: swa32 / swa_bf window outputs (either may be
 // NULL), text: output of text rows (NULL: skip them); ws: flash_workspace(dm).
 // local_ml / local_o (both or neither): the selection partial arrays of the selection kernels;

@@ -454,28 +454,30 @@ __global__ void __launch_bounds__(256) slc_merge_kernel(const float2* __restrict
 // ---------------------------------------------------------------------------
 static size_t srup(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t slc_block_workspace(const Dims& dm) {
+// Bytes of the bucketing arrays (counts, offsets, first chunks, cursors, the chunk -> block map and
+// the pair lists); the selection partials follow them in the forward's workspace.
+size_t slc_bucket_bytes(const Dims& dm) {
   const size_t bgs = (size_t)dm.B * dm.Hkv;
+  return 4 * srup(bgs * dm.Ns * 4) + srup(bgs * slc_cap_chunks(dm) * 4) + srup(bgs * slc_cap_chunks(dm) * RC * 4);
+}
+
+size_t slc_block_workspace(const Dims& dm) {
   const size_t recs = (size_t)dm.B * dm.Tq * dm.Hkv * dm.n * dm.G;
-  return 4 * srup(bgs * dm.Ns * 4) + srup(bgs * slc_cap_chunks(dm) * 4) + srup(bgs * slc_cap_chunks(dm) * RC * 4) +
-         srup(recs * 8) + srup(recs * HD * 2);
+  return slc_bucket_bytes(dm) + srup(recs * 8) + srup(recs * HD * 2);
 }
 
 // The (max, sum) and value-record arrays of the selection partials inside the workspace.
 void slc_partial_arrays(const Dims& dm, void* ws, void** ml, void** o) {
-  const size_t bgs = (size_t)dm.B * dm.Hkv;
   const size_t recs = (size_t)dm.B * dm.Tq * dm.Hkv * dm.n * dm.G;
-  char* p = (char*)ws + 4 * srup(bgs * dm.Ns * 4) + srup(bgs * slc_cap_chunks(dm) * 4) +
-            srup(bgs * slc_cap_chunks(dm) * RC * 4);
+  char* p = (char*)ws + slc_bucket_bytes(dm);
   *ml = p;
   *o = p + srup(recs * 8);
 }
 
-hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
-                            const uint8_t* vid, const void* ocmp, bool ocmp_f32, const float* swa32,
-                            const float* gates, void* out, void* o_slc, void* ws, hipStream_t s, bool local_fused,
-                            hipEvent_t before_merge) {
-  if (dm.B <= 0 || dm.Tq <= 0) return hipSuccess;
+// Buckets the kept (row, slot) pairs by chosen block (slc_count, slc_scan, slc_scatter) into the
+// arrays at the start of ws (slc_bucket_bytes(dm) bytes).
+static hipError_t slc_buckets(const Dims& dm, const int32_t* idx, const uint8_t* vid, void* ws, bool local_fused,
+                              SlcBuckets* out, hipStream_t s) {
   const int bgs = (int)(dm.B * dm.Hkv);
   char* p = (char*)ws;
   SlcBuckets bk;
@@ -489,25 +491,44 @@ hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const 
   bk.chunk_blk = (int*)p;
   p += srup((size_t)bgs * bk.cap_c * 4);
   bk.pairs = (int*)p;
-  p += srup((size_t)bgs * bk.cap_c * RC * 4);
-  const size_t recs = (size_t)dm.B * dm.Tq * dm.Hkv * dm.n * dm.G;
-  float2* pml = (float2*)p;
-  p += srup(recs * 8);
-  _Float16* po = (_Float16*)p;
   const int wpb = (int)((dm.Tq + RROWS - 1) / RROWS);
   const size_t hist = (size_t)dm.Ns * 4;
-  hipError_t e;
   // counts start at zero (a kernel, not a memset: callers may capture the launch in a graph)
   const int64_t ncount = (int64_t)bgs * dm.Ns;
   slc_zero_kernel<<<dim3((unsigned)((ncount + 255) / 256)), dim3(256), 0, s>>>(bk.count, ncount);
   for (const void* fn : {(const void*)slc_count_kernel, (const void*)slc_scatter_kernel, (const void*)slc_scan_kernel}) {
-    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * hist));
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * hist));
     if (e != hipSuccess) return e;
   }
   slc_count_kernel<<<dim3(bgs * wpb), dim3(256), hist, s>>>(idx, vid, bk, dm, wpb, local_fused ? 1 : 0);
   slc_scan_kernel<<<dim3(bgs), dim3(1024), 2 * hist, s>>>(bk, dm);
-  slc_scatter_kernel<<<dim3(bgs * wpb), dim3(256), 2 * hist, s>>>(idx, vid, bk, dm, wpb,
-                                                                   local_fused ? 1 : 0);
+  slc_scatter_kernel<<<dim3(bgs * wpb), dim3(256), 2 * hist, s>>>(idx, vid, bk, dm, wpb, local_fused ? 1 : 0);
+  *out = bk;
+  return hipGetLastError();
+}
+
+hipError_t launch_slc_pair_lists(const Dims& dm, const int32_t* idx, const uint8_t* vid, void* ws, SlcPairLists* pl,
+                                 hipStream_t s) {
+  SlcBuckets bk;
+  const hipError_t e = slc_buckets(dm, idx, vid, ws, false, &bk, s);
+  pl->chunk_blk = bk.chunk_blk;
+  pl->pairs = bk.pairs;
+  pl->cap_c = bk.cap_c;
+  return e;
+}
+
+hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
+                            const uint8_t* vid, const void* ocmp, bool ocmp_f32, const float* swa32,
+                            const float* gates, void* out, void* o_slc, void* ws, hipStream_t s, bool local_fused,
+                            hipEvent_t before_merge) {
+  if (dm.B <= 0 || dm.Tq <= 0) return hipSuccess;
+  const int bgs = (int)(dm.B * dm.Hkv);
+  SlcBuckets bk;
+  hipError_t e = slc_buckets(dm, idx, vid, ws, local_fused, &bk, s);
+  if (e != hipSuccess) return e;
+  const size_t recs = (size_t)dm.B * dm.Tq * dm.Hkv * dm.n * dm.G;
+  float2* pml = (float2*)((char*)ws + slc_bucket_bytes(dm));
+  _Float16* po = (_Float16*)((char*)pml + srup(recs * 8));
   auto chunk = [&](auto kernel, int sb) -> hipError_t {
     const int shm = 2 * sb * HD * 2;
     hipError_t e2 = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, shm);
