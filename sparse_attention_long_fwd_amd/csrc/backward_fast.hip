@@ -672,12 +672,13 @@ __global__ void __launch_bounds__(256)
   dgates[x * 3 + 1] = isv ? E : 0.f;
 }
 
-// dq += scale K^T ds^T over the block's keys, per (pair, head), with atomic adds.
+// Per (pair, head): scale K^T ds^T over the block's keys, into the pair's fp32 record
+// dqrec[((b Tq + row) Hkv + g) n + slot][head][128] (summed per row by bwdf_sel_dq_merge_kernel).
 template <int SB>
 __global__ void __launch_bounds__(512)
     bwdf_sel_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ dout, const bf16* __restrict__ k,
                        const bf16* __restrict__ v, const float* __restrict__ gates, const float* __restrict__ st_l,
-                       const float* __restrict__ st_e, SlcPairLists pl, float* __restrict__ dq, Dims dm) {
+                       const float* __restrict__ st_e, SlcPairLists pl, float* __restrict__ dqrec, Dims dm) {
   constexpr int NKB = SB / 32;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   bf16* kt = (bf16*)smem;
@@ -721,16 +722,52 @@ __global__ void __launch_bounds__(512)
     }
   if (!sc.valid) return;
   // dq^T register jj of dims block db holds dim 32 db + 8 (jj / 4) + 4 hl + jj % 4 of row n
-  float* dst = dq + sc.rowi * HD + 4 * hl;
+  float* dst = dqrec + ((((sc.b * dm.Tq + sc.row) * dm.Hkv + sc.g) * dm.n + sc.slot) * dm.G + w) * HD + 4 * hl;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) unsafeAtomicAdd(dst + 32 * db + 8 * (jj >> 2) + (jj & 3), dqa[db][jj] * dm.scale);
+    for (int qd = 0; qd < 4; ++qd)
+      *(float4*)(dst + 32 * db + 8 * qd) = make_float4(dqa[db][4 * qd] * dm.scale, dqa[db][4 * qd + 1] * dm.scale,
+                                                        dqa[db][4 * qd + 2] * dm.scale, dqa[db][4 * qd + 3] * dm.scale);
 }
 
-// dk, dv of the block's keys from the chunk's pairs: SB / 16 waves of 16 keys each, the heads one
-// after the other with the pairs' q and d_out rows gathered into LDS (rows on M, as in the key
-// kernel), atomic adds.
+// dq[row, head] += the records of the row's kept slots, in slot order: a thread per 4 channels.
+__global__ void __launch_bounds__(256)
+    bwdf_sel_dq_merge_kernel(const float* __restrict__ dqrec, const int32_t* __restrict__ idx,
+                             const uint8_t* __restrict__ vid, float* __restrict__ dq, Dims dm) {
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (x >= dm.B * dm.Tq * dm.Hq * (HD / 4)) return;
+  const int64_t rh = x / (HD / 4);  // (b Tq + row) Hq + head
+  const int c4 = (int)(x % (HD / 4));
+  const int64_t br = rh / dm.Hq;
+  const int h = (int)(rh % dm.Hq), g = h / dm.G, w = h % dm.G;
+  if (vid && !vid[br]) return;
+  const int64_t jt = (dm.q0 + br % dm.Tq) / dm.ls;
+  const int32_t* sel = idx + (br * dm.Hkv + g) * dm.n;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < dm.n; ++s) {
+    const int j = sel[s];
+    if (j < 0 || j > jt) continue;
+    const float4 r = *(const float4*)(dqrec + (((br * dm.Hkv + g) * dm.n + s) * dm.G + w) * HD + 4 * c4);
+    acc.x += r.x;
+    acc.y += r.y;
+    acc.z += r.z;
+    acc.w += r.w;
+  }
+  float4* d = (float4*)(dq + rh * HD + 4 * c4);
+  float4 o = *d;
+  o.x += acc.x;
+  o.y += acc.y;
+  o.z += acc.z;
+  o.w += acc.w;
+  *d = o;
+}
+
+// dk, dv of a block's keys: one workgroup per run of up to CPW consecutive chunks of the block (the
+// workgroup of the run's first chunk; the others exit), SB / 16 waves of 16 keys each, the (chunk,
+// head) items one after the other with the pairs' q and d_out rows gathered into LDS (rows on M, as
+// in the key kernel); one atomic add per key and channel at the end.
+constexpr int CPW = 32;
 template <int SB>
 __global__ void __launch_bounds__(512)
     bwdf_sel_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ dout, const bf16* __restrict__ k,
@@ -741,8 +778,7 @@ __global__ void __launch_bounds__(512)
   __shared__ __attribute__((aligned(16))) bf16 tq[2][PRC * HD];
   __shared__ __attribute__((aligned(16))) bf16 tdo[2][PRC * HD];
   __shared__ __attribute__((aligned(16))) float sL[2][PRC], sE[2][PRC], sG[2][PRC];
-  __shared__ __attribute__((aligned(16))) int sT[PRC];
-  __shared__ int sRow[PRC];
+  __shared__ __attribute__((aligned(16))) int sT[2][PRC];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gi = l >> 4;
   const int bg = blockIdx.x / pl.cap_c, cc = blockIdx.x % pl.cap_c;
   const int64_t ci = (int64_t)bg * pl.cap_c + cc;
@@ -751,11 +787,10 @@ __global__ void __launch_bounds__(512)
   const int64_t b = bg / dm.Hkv;
   const int g = bg % dm.Hkv;
   const int G = dm.G;
-  if (tid < PRC) {
-    const int pr = pl.pairs[ci * PRC + tid];
-    sRow[tid] = pr >= 0 ? (pr >> 5) : -1;
-    sT[tid] = pr >= 0 ? (int)(dm.q0 + (pr >> 5)) : -1;
-  }
+  if ((cc - pl.cfirst[(int64_t)bg * dm.Ns + j]) % CPW != 0) return;
+  int nchk = 1;
+  while (nchk < CPW && cc + nchk < pl.cap_c && pl.chunk_blk[ci + nchk] == j) ++nchk;
+  const int nitems = nchk * G;
   const int64_t u = (int64_t)j * SB + 16 * w + c;
   const bool uvalid = u < dm.T;
   bf16x8 kf[4], vf[4];
@@ -767,51 +802,61 @@ __global__ void __launch_bounds__(512)
       vf[ks] = *(const bf16x8*)(v + o + 32 * ks);
     }
   }
-  __syncthreads();  // sRow, sT
-  // gathered rows: instruction ins fills LDS chunks [64 ins, +64) = pair rows 4 ins .. 4 ins + 3
-  auto stage = [&](int buf, int h) {
+  // item i: chunk ci + i / G, head g G + i % G.  Gathered rows: instruction ins fills LDS chunks
+  // [64 ins, +64) = pair rows 4 ins .. 4 ins + 3 (an empty pair reads row 0, masked).
+  auto stage = [&](int buf, int i) {
+    const int* prs = pl.pairs + (ci + i / G) * PRC;
+    const int hq = g * G + i % G;
     for (int ins = w; ins < PRC / 4; ins += NW) {
       const int p = ins * 64 + l;
       const int pr = p >> 4, cpos = p & 15, cl = cpos ^ (pr & 15);
-      const int rw = sRow[pr] >= 0 ? sRow[pr] : 0;
-      const int64_t o = ((b * dm.Tq + rw) * dm.Hq + g * G + h) * (int64_t)HD + cl * 8;
+      const int pw = prs[pr];
+      const int64_t rw = pw >= 0 ? (pw >> 5) : 0;
+      const int64_t o = ((b * dm.Tq + rw) * dm.Hq + hq) * (int64_t)HD + cl * 8;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(q + o),
                                        (__attribute__((address_space(3))) void*)(tq[buf] + ins * 512), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(dout + o),
                                        (__attribute__((address_space(3))) void*)(tdo[buf] + ins * 512), 16, 0, 0);
     }
   };
-  auto load_st = [&](int h, float& L, float& E, float& Gt) {
-    L = INFINITY;
-    E = 0.f;
-    Gt = 0.f;
-    if (sRow[tid] >= 0) {
-      const int64_t ri = (b * dm.Tq + sRow[tid]) * dm.Hq + g * G + h;
-      L = st_l[ri * 3 + 1];
-      E = st_e[ri * 3 + 1];
-      Gt = gates[ri * 3 + 1];
+  struct PairSt {
+    float L, E, G;
+    int t;
+  };
+  // statistics of pair tid (tid < PRC) of item i
+  auto load_st = [&](int i) -> PairSt {
+    PairSt st{INFINITY, 0.f, 0.f, -1};
+    const int pw = pl.pairs[(ci + i / G) * PRC + tid];
+    if (pw >= 0) {
+      const int64_t row = pw >> 5;
+      const int64_t ri = (b * dm.Tq + row) * dm.Hq + g * G + i % G;
+      st.L = st_l[ri * 3 + 1];
+      st.E = st_e[ri * 3 + 1];
+      st.G = gates[ri * 3 + 1];
+      st.t = (int)(dm.q0 + row);
     }
+    return st;
+  };
+  auto put_st = [&](int buf, const PairSt& st) {
+    sL[buf][tid] = st.L;
+    sE[buf][tid] = st.E;
+    sG[buf][tid] = st.G;
+    sT[buf][tid] = st.t;
   };
   const float cs = dm.scale * LOG2E_F;
   f32x4 dka[8], dva[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) dka[db] = dva[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   stage(0, 0);
-  if (tid < PRC) {
-    float L, E, Gt;
-    load_st(0, L, E, Gt);
-    sL[0][tid] = L;
-    sE[0][tid] = E;
-    sG[0][tid] = Gt;
-  }
-  for (int h = 0; h < G; ++h) {
-    const int buf = h & 1;
+  if (tid < PRC) put_st(0, load_st(0));
+  for (int i = 0; i < nitems; ++i) {
+    const int buf = i & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    float nL = 0.f, nE = 0.f, nG = 0.f;
-    if (h + 1 < G) {
-      stage(buf ^ 1, h + 1);
-      if (tid < PRC) load_st(h + 1, nL, nE, nG);
+    PairSt nst{};
+    if (i + 1 < nitems) {
+      stage(buf ^ 1, i + 1);
+      if (tid < PRC) nst = load_st(i + 1);
     }
     const bf16* Qt = tq[buf];
     const bf16* Dt = tdo[buf];
@@ -833,7 +878,7 @@ __global__ void __launch_bounds__(512)
       const float4 L4 = *(const float4*)&sL[buf][rq];
       const float4 E4 = *(const float4*)&sE[buf][rq];
       const float4 G4 = *(const float4*)&sG[buf][rq];
-      const int4 T4 = *(const int4*)&sT[rq];
+      const int4 T4 = *(const int4*)&sT[buf][rq];
       const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Ev[4] = {E4.x, E4.y, E4.z, E4.w};
       const float Gv[4] = {G4.x, G4.y, G4.z, G4.w};
       const int Tv[4] = {T4.x, T4.y, T4.z, T4.w};
@@ -855,11 +900,7 @@ __global__ void __launch_bounds__(512)
       dka[db] = mfma16(aq, sh, dka[db]);
       dka[db] = mfma16(aq, sl, dka[db]);
     }
-    if (h + 1 < G && tid < PRC) {
-      sL[buf ^ 1][tid] = nL;
-      sE[buf ^ 1][tid] = nE;
-      sG[buf ^ 1][tid] = nG;
-    }
+    if (i + 1 < nitems && tid < PRC) put_st(buf ^ 1, nst);
   }
   if (!uvalid) return;
   float* dkp = dk + ((b * dm.T + u) * dm.Hkv + g) * (int64_t)HD + 4 * gi;
@@ -888,6 +929,7 @@ struct BwdWs {
   float *dkc, *dvc, *st_l, *st_e;
   uint32_t* tbits;
   float4* rec;
+  float* dqrec;
   void* buckets;
   size_t total;
 };
@@ -914,6 +956,7 @@ static BwdWs bwd_fast_carve(const Dims& dm, void* ws) {
   w.st_e = (float*)take(rows * 4);
   w.tbits = (uint32_t*)take((size_t)dm.B * ((dm.Tq + 31) / 32) * 4);
   w.rec = (float4*)take((size_t)dm.B * dm.Tq * dm.Hkv * dm.n * dm.G * 16);
+  w.dqrec = (float*)take((size_t)dm.B * dm.Tq * dm.Hkv * dm.n * dm.G * HD * 4);
   w.buckets = take(slc_bucket_bytes(dm));
   w.total = o;
   return w;
@@ -942,12 +985,15 @@ static hipError_t launch_sel_bwd(const Dims& dm, const bf16* q, const bf16* dout
 
 template <int SB>
 static hipError_t launch_sel_bwd_grads(const Dims& dm, const bf16* q, const bf16* dout, const bf16* k,
-                                       const bf16* v, const float* gates, const SlcPairLists& pl, const BwdWs& w,
-                                       float* dq, float* dk, float* dv, hipStream_t s) {
+                                       const bf16* v, const float* gates, const int32_t* idx, const uint8_t* vid,
+                                       const SlcPairLists& pl, const BwdWs& w, float* dq, float* dk, float* dv,
+                                       hipStream_t s) {
   const unsigned grid = (unsigned)(dm.B * dm.Hkv) * (unsigned)pl.cap_c;
   const int shm = 2 * SB * HD * 2;
-  bwdf_sel_dq_kernel<SB><<<dim3(grid), dim3(dm.G * 64), shm, s>>>(q, dout, k, v, gates, w.st_l, w.st_e, pl, dq,
-                                                                   dm);
+  bwdf_sel_dq_kernel<SB><<<dim3(grid), dim3(dm.G * 64), shm, s>>>(q, dout, k, v, gates, w.st_l, w.st_e, pl,
+                                                                   w.dqrec, dm);
+  const int64_t nth = dm.B * dm.Tq * dm.Hq * (HD / 4);
+  bwdf_sel_dq_merge_kernel<<<dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, s>>>(w.dqrec, idx, vid, dq, dm);
   bwdf_sel_kv_kernel<SB><<<dim3(grid), dim3(SB / 16 * 64), 0, s>>>(q, dout, k, v, gates, w.st_l, w.st_e, pl, dk,
                                                                     dv, dm);
   return hipGetLastError();
@@ -1003,9 +1049,9 @@ hipError_t launch_layer_bwd_fast(const Dims& dm, const void* q_, const void* k_,
   bwdf_sel_merge_kernel<<<dim3((unsigned)((nrh + 255) / 256)), dim3(256), 0, s>>>(w.rec, idx, vid, w.st_l, w.st_e,
                                                                                   dgates, dm);
   if (dm.n > 0) {
-    e = dm.ls == 32 ? launch_sel_bwd_grads<32>(dm, q, dout, k, v, gates, pl, w, dq, dk, dv, s)
-                    : dm.ls == 128 ? launch_sel_bwd_grads<128>(dm, q, dout, k, v, gates, pl, w, dq, dk, dv, s)
-                                   : launch_sel_bwd_grads<64>(dm, q, dout, k, v, gates, pl, w, dq, dk, dv, s);
+    e = dm.ls == 32 ? launch_sel_bwd_grads<32>(dm, q, dout, k, v, gates, idx, vid, pl, w, dq, dk, dv, s)
+                    : dm.ls == 128 ? launch_sel_bwd_grads<128>(dm, q, dout, k, v, gates, idx, vid, pl, w, dq, dk, dv, s)
+                                   : launch_sel_bwd_grads<64>(dm, q, dout, k, v, gates, idx, vid, pl, w, dq, dk, dv, s);
     if (e != hipSuccess) return e;
   }
   // key kernels: window / text rows over the full-resolution keys, compression over the compressed ones

@@ -79,10 +79,12 @@ hipError_t launch_sparse_select(const Dims& dm, const void* q, const void* ks, c
 // The kept (row, slot) pairs of the video rows bucketed by chosen block (every pair whose block holds a
 // key at or before its row): chunk c of (batch, group) bg covers block chunk_blk[bg * cap_c + c]
 // (-1: unused) and its 32 pairs pairs[(bg * cap_c + c) * 32 + i] = (row << 5) | slot (-1 past the
-// list's end).  The arrays sit at the start of ws (slc_bucket_bytes(dm) bytes).
+// list's end); a block's chunks are consecutive from cfirst[bg * Ns + j].  The arrays sit at the
+// start of ws (slc_bucket_bytes(dm) bytes).
 struct SlcPairLists {
   const int* chunk_blk;
   const int* pairs;
+  const int* cfirst;  // [bg][Ns]: the first chunk of each block's list
   int cap_c;
 };
 size_t slc_bucket_bytes(const Dims& dm);

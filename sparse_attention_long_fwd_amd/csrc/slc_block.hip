@@ -513,6 +513,7 @@ hipError_t launch_slc_pair_lists(const Dims& dm, const int32_t* idx, const uint8
   const hipError_t e = slc_buckets(dm, idx, vid, ws, false, &bk, s);
   pl->chunk_blk = bk.chunk_blk;
   pl->pairs = bk.pairs;
+  pl->cfirst = bk.cfirst;
   pl->cap_c = bk.cap_c;
   return e;
 }
