@@ -479,8 +479,9 @@ def branch_kv(args, wl, inp):
 
 
 def backward(args):
-    """Backward pass (generic kernels) of the 36K layer: gradients of sum(d_out * out) for q, k,
-    v, the gates and the compression weights, the forward's chosen blocks held fixed."""
+    """Backward pass of the 36K layer (the matrix-core kernels; the generic VALU kernels timed once
+    beside them): gradients of sum(d_out * out) for q, k, v, the gates and the compression weights,
+    the forward's chosen blocks held fixed."""
     import torch
     from sparse_attention_long_fwd_amd import accounting, nsa, synth
 
@@ -502,11 +503,20 @@ def backward(args):
                                  w_v=inp["w_v"], is_video=inp["is_video"], workspace=ws, stream=stream)
 
     step()
-    ms = time_calls(step, 1, stream)
+    steps = 5
+    ms = time_calls(step, steps, stream)
+    prev = nsa.set_force_generic(True)
+    try:
+        ws = torch.empty(nsa.nsa_hybrid_layer_bwd_workspace_size(sh, pr, nsa.NSA_BF16), dtype=torch.uint8,
+                         device="cuda")
+        ms_generic = time_calls(step, 1, stream)
+    finally:
+        nsa.set_force_generic(prev)
     fl = accounting.backward_flops(wl)["total"]
     del inp, ws
-    return dict(workload=wl.name, kernels="generic (VALU)", ms_per_step=ms, algo_flops=fl,
-                tflops=fl / (ms * 1e-3) / 1e12, mfma_frac=fl / (ms * 1e-3) / PEAK_BF16_MFMA, steps=1)
+    return dict(workload=wl.name, kernels="matrix cores (bf16 MFMA)", ms_per_step=ms, algo_flops=fl,
+                tflops=fl / (ms * 1e-3) / 1e12, mfma_frac=fl / (ms * 1e-3) / PEAK_BF16_MFMA, steps=steps,
+                ms_generic_kernels=ms_generic)
 
 
 def decode(args):

@@ -10,6 +10,7 @@
 #include <cmath>
 
 #include "../../include/nsa.h"
+#include "backward.hpp"
 #include "common.hpp"
 #include "fast.hpp"
 

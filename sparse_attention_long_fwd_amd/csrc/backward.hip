@@ -24,7 +24,7 @@
 //     the same for 32 compressed keys (dkc, dvc).
 //  3. bwd_compress_kernel adds the compression's share to dk, dv;
 //     bwd_dw_kernel reduces dw_k, dw_v.
-#include "common.hpp"
+#include "backward.hpp"
 
 #define BWD_THREADS 256
 

@@ -32,6 +32,7 @@
 //    gates); bwdf_sel_dq_kernel adds dq and bwdf_sel_kv_kernel dk, dv (atomic adds).
 // The order of the atomic adds depends on scheduling: the last bits of dq, dk and dv can differ
 // from one call to the next.
+#include "backward.hpp"
 #include "fast_common.hpp"
 
 namespace {
