@@ -313,7 +313,7 @@ __global__ void __launch_bounds__(512)
 // the rows that see them.  S = Q K^T (the rows on M: lane (c, gi) holds rows 16 mb + 4 gi + j,
 // key c), dv^T += d_out^T (g P), dk^T += Q^T ds with Q and d_out read transposed from LDS.
 template <bool CMP>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
     bwdf_key_kernel(const bf16* __restrict__ q, const bf16* __restrict__ dout, const bf16* __restrict__ kh,
                     const bf16* __restrict__ kl, const bf16* __restrict__ vh, const bf16* __restrict__ vl,
                     const uint8_t* __restrict__ vid, const float* __restrict__ gates, const float* __restrict__ st_l,
