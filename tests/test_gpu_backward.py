@@ -2,9 +2,12 @@
 backward, through the C ABI.  The chosen blocks come from the oracle's forward and feed
 both sides (selection passes no gradient).
 
-Tolerance (fp32 accumulation on both fp32 and bf16 inputs, which widen exactly): per
-output, max-abs error <= 1e-4 x max|reference| + 1e-5; the compression weight gradients
-sum over every (block, KV head, channel) and get 3e-4 x max|reference| + 1e-5.
+Tolerance (fp32 accumulation on both fp32 and bf16 inputs, which widen exactly; the
+matrix-core kernels take the probabilities, ds and the compressed keys and values as a bf16
+high part plus a bf16 remainder, within 2^-17 of their fp32 values, so the same bound holds):
+per output, max-abs error <= 1e-4 x max|reference| + 1e-5; the compression weight gradients
+sum over every (block, KV head, channel) and get 3e-4 x max|reference| + 1e-5.  bf16 cases run
+both on the default (matrix-core) path and on the generic VALU kernels.
 """
 import numpy as np
 import pytest
@@ -45,9 +48,25 @@ def _run(wl, inp, dout, idx):
     return g
 
 
-@pytest.mark.parametrize("case", ["f32-tiny", "bf16-ragged", "bf16-batch2", "bf16-short", "bf16-no-cmp-block",
-                                  "bf16-all-text", "bf16-q-start", "bf16-row-chunks"])
-def test_layer_backward(case):
+CASES = ["f32-tiny", "bf16-ragged", "bf16-batch2", "bf16-short", "bf16-no-cmp-block", "bf16-all-text",
+         "bf16-q-start", "bf16-row-chunks", "bf16-sel32", "bf16-sel128", "bf16-g8", "bf16-g1"]
+
+
+@pytest.mark.parametrize("generic", [False, True], ids=["default", "generic"])
+@pytest.mark.parametrize("case", CASES)
+def test_layer_backward(case, generic):
+    """bf16 with head_dim 128 and 1..8 heads per KV group takes the matrix-core kernels by default;
+    `generic` forces the VALU kernels (nsa_set_force_generic) on the same case."""
+    if generic and case in ("f32-tiny", "bf16-sel32", "bf16-sel128", "bf16-g1"):
+        pytest.skip("fp32 runs the generic kernels on the default path; the new shapes test the matrix-core path")
+    prev = nsa.set_force_generic(generic)
+    try:
+        _check_case(case)
+    finally:
+        nsa.set_force_generic(prev)
+
+
+def _check_case(case):
     if case == "f32-tiny":
         wl = _wl(dtype="f32", T=300, Hq=4, Hkv=1, D=64, n=4, w=128, lead=16, corr=False)
     elif case == "bf16-ragged":
@@ -62,7 +81,15 @@ def test_layer_backward(case):
         wl = _wl(T=200, Hq=8, Hkv=2, lead=200, n=4, w=64)
     elif case == "bf16-q-start":  # a block of query rows at the end of the sequence
         wl = _wl(T=900, Hq=14, Hkv=2, q_start=600, q_len=300, lead=0, tail=20, n=6, w=128)
-    else:  # enough rows that the key kernels split them into several chunks (3 and 5)
+    elif case == "bf16-sel32":  # 32-token selection blocks, text rows at both ends
+        wl = _wl(T=1500 + 11, Hq=14, Hkv=2, lead=48, tail=30, n=12, w=96, sel_block=32)
+    elif case == "bf16-sel128":  # 128-token selection blocks, a block of query rows at the end
+        wl = _wl(T=2100, Hq=10, Hkv=2, q_start=900, lead=0, tail=17, n=6, w=160, sel_block=128)
+    elif case == "bf16-g8":  # eight heads per KV group
+        wl = _wl(T=1300, Hq=16, Hkv=2, lead=40, tail=9, n=8, w=128)
+    elif case == "bf16-g1":  # one head per KV group
+        wl = _wl(T=1100 + 5, Hq=3, Hkv=3, lead=20, tail=20, n=6, w=70)
+    else:  # enough rows that the generic key kernels split them into several chunks (3 and 5)
         wl = _wl(T=4500, Hq=8, Hkv=2, lead=32, tail=40, n=6, w=200)
     flush("backward %s" % case)
     inp, dout, idx = _setup(wl)
