@@ -936,6 +936,23 @@ struct BwdWs {
 };
 }  // namespace
 
+// The selection branch runs per sub-problem: one sequence and a run of at most sel_rows(dm) rows,
+// so that its per-(row, slot, head) dq records (512 bytes each) stay within kSelRecCap bytes.
+constexpr size_t kSelRecCap = (size_t)2 << 30;
+static int64_t sel_rows(const Dims& dm) {
+  const size_t per_row = (size_t)dm.Hkv * (dm.n > 0 ? dm.n : 1) * dm.G * HD * 4;
+  int64_t rc = (int64_t)(kSelRecCap / per_row);
+  if (rc < 32) rc = 32;
+  return rc < dm.Tq ? rc : dm.Tq;
+}
+static Dims sel_dims(const Dims& dm, int64_t rows, int64_t r0) {
+  Dims d = dm;
+  d.B = 1;
+  d.Tq = rows;
+  d.q0 = dm.q0 + r0;
+  return d;
+}
+
 static BwdWs bwd_fast_carve(const Dims& dm, void* ws) {
   BwdWs w{};
   char* p = (char*)ws;
@@ -956,9 +973,10 @@ static BwdWs bwd_fast_carve(const Dims& dm, void* ws) {
   w.st_l = (float*)take(rows * 4);
   w.st_e = (float*)take(rows * 4);
   w.tbits = (uint32_t*)take((size_t)dm.B * ((dm.Tq + 31) / 32) * 4);
-  w.rec = (float4*)take((size_t)dm.B * dm.Tq * dm.Hkv * dm.n * dm.G * 16);
-  w.dqrec = (float*)take((size_t)dm.B * dm.Tq * dm.Hkv * dm.n * dm.G * HD * 4);
-  w.buckets = take(slc_bucket_bytes(dm));
+  const Dims ds = sel_dims(dm, sel_rows(dm), 0);
+  w.rec = (float4*)take((size_t)ds.Tq * ds.Hkv * ds.n * ds.G * 16);
+  w.dqrec = (float*)take((size_t)ds.Tq * ds.Hkv * ds.n * ds.G * HD * 4);
+  w.buckets = take(slc_bucket_bytes(ds));
   w.total = o;
   return w;
 }
@@ -970,34 +988,81 @@ static void zero_f32(float* p, int64_t n, hipStream_t s) {
   bwdf_zero_kernel<<<dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, s>>>(p, n);
 }
 
+// Selection arrays of one sub-problem (its rows' offsets applied).
+struct SelArgs {
+  const bf16 *q, *dout, *k, *v;
+  const float* gates;
+  const int32_t* idx;
+  const uint8_t* vid;
+  float *st_l, *st_e, *dgates, *dq, *dk, *dv;
+  float4* rec;
+  float* dqrec;
+};
+
 template <int SB>
-static hipError_t launch_sel_bwd(const Dims& dm, const bf16* q, const bf16* dout, const bf16* k, const bf16* v,
-                                 const float* gates, const SlcPairLists& pl, const BwdWs& w, float* dq, float* dk,
-                                 float* dv, hipStream_t s) {
-  const unsigned grid = (unsigned)(dm.B * dm.Hkv) * (unsigned)pl.cap_c;
+static hipError_t launch_sel_bwd(const Dims& ds, const SlcPairLists& pl, const SelArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)(ds.B * ds.Hkv) * (unsigned)pl.cap_c;
   const int shm = 2 * SB * HD * 2;
   for (const void* fn : {(const void*)bwdf_sel_stats_kernel<SB>, (const void*)bwdf_sel_dq_kernel<SB>}) {
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, shm);
     if (e != hipSuccess) return e;
   }
-  bwdf_sel_stats_kernel<SB><<<dim3(grid), dim3(dm.G * 64), shm, s>>>(q, dout, k, v, pl, w.rec, dm);
+  bwdf_sel_stats_kernel<SB><<<dim3(grid), dim3(ds.G * 64), shm, s>>>(a.q, a.dout, a.k, a.v, pl, a.rec, ds);
+  const int64_t nrh = ds.B * ds.Tq * ds.Hq;
+  bwdf_sel_merge_kernel<<<dim3((unsigned)((nrh + 255) / 256)), dim3(256), 0, s>>>(a.rec, a.idx, a.vid, a.st_l,
+                                                                                  a.st_e, a.dgates, ds);
+  bwdf_sel_dq_kernel<SB><<<dim3(grid), dim3(ds.G * 64), shm, s>>>(a.q, a.dout, a.k, a.v, a.gates, a.st_l, a.st_e,
+                                                                   pl, a.dqrec, ds);
+  const int64_t nth = ds.B * ds.Tq * ds.Hq * (HD / 4);
+  bwdf_sel_dq_merge_kernel<<<dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, s>>>(a.dqrec, a.idx, a.vid, a.dq,
+                                                                                    ds);
+  bwdf_sel_kv_kernel<SB><<<dim3(grid), dim3(SB / 16 * 64), 0, s>>>(a.q, a.dout, a.k, a.v, a.gates, a.st_l, a.st_e,
+                                                                    pl, a.dk, a.dv, ds);
   return hipGetLastError();
 }
 
-template <int SB>
-static hipError_t launch_sel_bwd_grads(const Dims& dm, const bf16* q, const bf16* dout, const bf16* k,
-                                       const bf16* v, const float* gates, const int32_t* idx, const uint8_t* vid,
-                                       const SlcPairLists& pl, const BwdWs& w, float* dq, float* dk, float* dv,
-                                       hipStream_t s) {
-  const unsigned grid = (unsigned)(dm.B * dm.Hkv) * (unsigned)pl.cap_c;
-  const int shm = 2 * SB * HD * 2;
-  bwdf_sel_dq_kernel<SB><<<dim3(grid), dim3(dm.G * 64), shm, s>>>(q, dout, k, v, gates, w.st_l, w.st_e, pl,
-                                                                   w.dqrec, dm);
-  const int64_t nth = dm.B * dm.Tq * dm.Hq * (HD / 4);
-  bwdf_sel_dq_merge_kernel<<<dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, s>>>(w.dqrec, idx, vid, dq, dm);
-  bwdf_sel_kv_kernel<SB><<<dim3(grid), dim3(SB / 16 * 64), 0, s>>>(q, dout, k, v, gates, w.st_l, w.st_e, pl, dk,
-                                                                    dv, dm);
-  return hipGetLastError();
+// The selection branch of every (sequence, run of rows) sub-problem: pair lists, statistics (slot 1
+// and d gates), dq, dk, dv.
+static hipError_t launch_sel_all(const Dims& dm, const bf16* q, const bf16* dout, const bf16* k, const bf16* v,
+                                 const float* gates, const int32_t* idx, const uint8_t* vid, const BwdWs& w,
+                                 float* dq, float* dk, float* dv, float* dgates, hipStream_t s) {
+  const int64_t rc = sel_rows(dm);
+  for (int64_t b = 0; b < dm.B; ++b)
+    for (int64_t ra = 0; ra < dm.Tq; ra += rc) {
+      const Dims ds = sel_dims(dm, rc < dm.Tq - ra ? rc : dm.Tq - ra, ra);
+      const int64_t row0 = b * dm.Tq + ra;  // the sub-problem's first (sequence, row)
+      SelArgs a;
+      a.q = q + row0 * dm.Hq * HD;
+      a.dout = dout + row0 * dm.Hq * HD;
+      a.k = k + b * dm.T * dm.Hkv * HD;
+      a.v = v + b * dm.T * dm.Hkv * HD;
+      a.gates = gates + row0 * dm.Hq * 3;
+      a.idx = idx + row0 * dm.Hkv * dm.n;
+      a.vid = vid ? vid + row0 : nullptr;
+      a.st_l = w.st_l + row0 * dm.Hq * 3;
+      a.st_e = w.st_e + row0 * dm.Hq * 3;
+      a.dgates = dgates + row0 * dm.Hq * 3;
+      a.dq = dq + row0 * dm.Hq * HD;
+      a.dk = dk + b * dm.T * dm.Hkv * HD;
+      a.dv = dv + b * dm.T * dm.Hkv * HD;
+      a.rec = w.rec;
+      a.dqrec = w.dqrec;
+      hipError_t e;
+      if (ds.n <= 0) {
+        const int64_t nrh = ds.Tq * ds.Hq;
+        bwdf_sel_merge_kernel<<<dim3((unsigned)((nrh + 255) / 256)), dim3(256), 0, s>>>(a.rec, a.idx, a.vid, a.st_l,
+                                                                                        a.st_e, a.dgates, ds);
+        e = hipGetLastError();
+      } else {
+        SlcPairLists pl{};
+        e = launch_slc_pair_lists(ds, a.idx, a.vid, w.buckets, &pl, s);
+        if (e == hipSuccess)
+          e = ds.ls == 32 ? launch_sel_bwd<32>(ds, pl, a, s)
+                          : ds.ls == 128 ? launch_sel_bwd<128>(ds, pl, a, s) : launch_sel_bwd<64>(ds, pl, a, s);
+      }
+      if (e != hipSuccess) return e;
+    }
+  return hipSuccess;
 }
 
 hipError_t launch_layer_bwd_fast(const Dims& dm, const void* q_, const void* k_, const void* v_, const float* w_k,
@@ -1036,25 +1101,9 @@ hipError_t launch_layer_bwd_fast(const Dims& dm, const void* q_, const void* k_,
     bwdf_row_kernel<false><<<grid, dim3(dm.G * 64), shw, s>>>(q, dout, k, nullptr, v, nullptr, vid, gates, dq,
                                                               dgates, w.st_l, w.st_e, dm);
   }
-  // selection branch
-  SlcPairLists pl{};
-  if (dm.n > 0) {
-    e = launch_slc_pair_lists(dm, idx, vid, w.buckets, &pl, s);
-    if (e != hipSuccess) return e;
-    e = dm.ls == 32 ? launch_sel_bwd<32>(dm, q, dout, k, v, gates, pl, w, dq, dk, dv, s)
-                    : dm.ls == 128 ? launch_sel_bwd<128>(dm, q, dout, k, v, gates, pl, w, dq, dk, dv, s)
-                                   : launch_sel_bwd<64>(dm, q, dout, k, v, gates, pl, w, dq, dk, dv, s);
-    if (e != hipSuccess) return e;
-  }
-  const int64_t nrh = dm.B * dm.Tq * dm.Hq;
-  bwdf_sel_merge_kernel<<<dim3((unsigned)((nrh + 255) / 256)), dim3(256), 0, s>>>(w.rec, idx, vid, w.st_l, w.st_e,
-                                                                                  dgates, dm);
-  if (dm.n > 0) {
-    e = dm.ls == 32 ? launch_sel_bwd_grads<32>(dm, q, dout, k, v, gates, idx, vid, pl, w, dq, dk, dv, s)
-                    : dm.ls == 128 ? launch_sel_bwd_grads<128>(dm, q, dout, k, v, gates, idx, vid, pl, w, dq, dk, dv, s)
-                                   : launch_sel_bwd_grads<64>(dm, q, dout, k, v, gates, idx, vid, pl, w, dq, dk, dv, s);
-    if (e != hipSuccess) return e;
-  }
+  // selection branch (after the row kernels: its dq merge adds to their dq)
+  e = launch_sel_all(dm, q, dout, k, v, gates, idx, vid, w, dq, dk, dv, dgates, s);
+  if (e != hipSuccess) return e;
   // key kernels: window / text rows over the full-resolution keys, compression over the compressed ones
   {
     const int nchw = (int)((ntr + RTC_WIN - 1) / RTC_WIN);
