@@ -873,14 +873,19 @@ int32_t nsa_gate_proj(const void* x, const void* w_g, const float* b_g, int32_t 
   return NSA_OK;
 }
 
-size_t nsa_hybrid_layer_bwd_workspace_size(const nsa_shape* shape, const nsa_params* params, int32_t dtype) {
-  Dims dm;
-  if (check_dims(shape, params, dtype, &dm, true) != NSA_OK) return 0;
-  // enough for either set of kernels (the matrix-core one needs 16-byte aligned tensors)
+// Backward workspace: enough for either set of kernels when the matrix-core one applies (it also
+// needs 16-byte aligned tensors, which only the call sees).
+static size_t bwd_need(int32_t dtype, const Dims& dm) {
   const size_t gen = bwd_workspace(dm);
   if (g_force_generic.load() || !bwd_fast_supported(dtype, dm)) return gen;
   const size_t fast = bwd_fast_workspace(dm);
   return fast > gen ? fast : gen;
+}
+
+size_t nsa_hybrid_layer_bwd_workspace_size(const nsa_shape* shape, const nsa_params* params, int32_t dtype) {
+  Dims dm;
+  if (check_dims(shape, params, dtype, &dm, true) != NSA_OK) return 0;
+  return bwd_need(dtype, dm);
 }
 
 int32_t nsa_hybrid_layer_bwd(const void* q, const void* k, const void* v, const float* w_k, const float* w_v,
@@ -900,7 +905,7 @@ int32_t nsa_hybrid_layer_bwd(const void* q, const void* k, const void* v, const 
                     aligned16(v) && aligned16(d_out) && aligned16(dq) && aligned16(dk) && aligned16(dv);
   if (!fast && !bwd_supported(dm))
     return fail(NSA_ERR_UNSUPPORTED, "backward kernels cover head_dim 64, 128, 192, 256");
-  const size_t need = fast ? bwd_fast_workspace(dm) : bwd_workspace(dm);
+  const size_t need = bwd_need(dtype, dm);
   if (workspace_bytes < need)
     return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, need);
   if (need > 0 && !workspace) return fail(NSA_ERR_INVALID_ARG, "NULL workspace");
