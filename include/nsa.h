@@ -333,8 +333,8 @@ int32_t nsa_hybrid_layer_fwd_branch_kv(const void* q, const void* k_c, const voi
  *  [B, kv_len, Hkv, D], d_gates [B, q_len, Hq, 3] (0 for text rows), dw_k,
  *  dw_v [cmp_block] (summed over the batch).  bf16 with head_dim 128, 1..8 heads
  *  per KV head, selection blocks of 32, 64 or 128 tokens and 16-byte aligned
- *  tensors: matrix-core kernels, whose atomic adds make the last bits of dq, dk
- *  and dv depend on scheduling; otherwise generic kernels: head_dim a multiple
+ *  tensors: matrix-core kernels, whose atomic adds make the last bits of dk and
+ *  dv depend on scheduling; otherwise generic kernels: head_dim a multiple
  *  of 64 up to 256 (else NSA_ERR_UNSUPPORTED), fp32 or bf16.  workspace:
  *  nsa_hybrid_layer_bwd_workspace_size() bytes (enough for either set).
  */

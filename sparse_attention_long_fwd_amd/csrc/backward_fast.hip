@@ -29,9 +29,10 @@
 //  Selection, block-major over the pair lists of launch_slc_pair_lists (32 (row, slot) pairs of one
 //    chosen block per workgroup): bwdf_sel_stats_kernel leaves per (row, slot, head) the block's
 //    max, sum and sum P dP; bwdf_sel_merge_kernel combines a row's slots (statistics slot 1, d
-//    gates); bwdf_sel_dq_kernel adds dq and bwdf_sel_kv_kernel dk, dv (atomic adds).
-// The order of the atomic adds depends on scheduling: the last bits of dq, dk and dv can differ
-// from one call to the next.
+//    gates); bwdf_sel_grad_kernel adds dk, dv (atomic adds) and writes per-pair dq records that
+//    bwdf_sel_dq_merge_kernel adds to dq in slot order.
+// The order of the atomic adds depends on scheduling: the last bits of dk and dv can differ from
+// one call to the next (dq and the d gates are summed in a fixed order).
 #include "backward.hpp"
 #include "fast_common.hpp"
 
@@ -673,65 +674,6 @@ __global__ void __launch_bounds__(256)
   dgates[x * 3 + 1] = isv ? E : 0.f;
 }
 
-// Per (pair, head): scale K^T ds^T over the block's keys, into the pair's fp32 record
-// dqrec[((b Tq + row) Hkv + g) n + slot][head][128] (summed per row by bwdf_sel_dq_merge_kernel).
-template <int SB>
-__global__ void __launch_bounds__(512)
-    bwdf_sel_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ dout, const bf16* __restrict__ k,
-                       const bf16* __restrict__ v, const float* __restrict__ gates, const float* __restrict__ st_l,
-                       const float* __restrict__ st_e, SlcPairLists pl, float* __restrict__ dqrec, Dims dm) {
-  constexpr int NKB = SB / 32;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  bf16* kt = (bf16*)smem;
-  bf16* vt = kt + SB * HD;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, n = l & 31;
-  const int g16 = l >> 4, i16 = l & 15;
-  SelChunk<SB> sc;
-  if (!sel_chunk_setup<SB>(pl, dm, w, n, sc)) return;
-  const int64_t stride = (int64_t)dm.Hkv * HD;
-  const int64_t kvb = (sc.b * dm.T * dm.Hkv + sc.g) * (int64_t)HD;
-  stage_rows_bw<SB>(kt, k + kvb, stride, (int64_t)sc.j * SB, dm.T, w, dm.G, l);
-  stage_rows_bw<SB>(vt, v + kvb, stride, (int64_t)sc.j * SB, dm.T, w, dm.G, l);
-  bf16x8 qf[8], df[8];
-  sel_load_rows<SB>(q, dout, sc, hl, qf, df);
-  const float L2 = st_l[sc.rowi * 3 + 1], E = st_e[sc.rowi * 3 + 1], gate = gates[sc.rowi * 3 + 1];
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  f32x16 s[NKB], dp[NKB];
-  sel_scores<SB>(kt, vt, qf, df, sc, dm, n, hl, dm.scale * LOG2E_F, s, dp);
-  f32x16 dqa[4] = {};
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      bf16x8 bh, bl;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = fexp2(s[kb][8 * st + e] - L2);
-        split2(gate * p * (dp[kb][8 * st + e] - E), bh, bl, e);
-      }
-      // K^T operand: dims 32 db + l % 32, the 16 keys of (kb, st) in the order of the B operand
-      const int vr = kb * 32 + 16 * st + 4 * (g16 >> 1) + (i16 >> 2);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int col = 32 * db + (g16 & 1) * 16 + 4 * (i16 & 3);
-        const bf16x8 a = cat(lds_read_tr(kt + swz128(vr, col >> 3) + (col & 7)),
-                             lds_read_tr(kt + swz128(vr + 8, col >> 3) + (col & 7)));
-        dqa[db] = mfma32(a, bh, dqa[db]);
-        dqa[db] = mfma32(a, bl, dqa[db]);
-      }
-    }
-  if (!sc.valid) return;
-  // dq^T register jj of dims block db holds dim 32 db + 8 (jj / 4) + 4 hl + jj % 4 of row n
-  float* dst = dqrec + ((((sc.b * dm.Tq + sc.row) * dm.Hkv + sc.g) * dm.n + sc.slot) * dm.G + w) * HD + 4 * hl;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd)
-      *(float4*)(dst + 32 * db + 8 * qd) = make_float4(dqa[db][4 * qd] * dm.scale, dqa[db][4 * qd + 1] * dm.scale,
-                                                        dqa[db][4 * qd + 2] * dm.scale, dqa[db][4 * qd + 3] * dm.scale);
-}
-
 // dq[row, head] += the records of the row's kept slots, in slot order: a thread per 4 channels.
 __global__ void __launch_bounds__(256)
     bwdf_sel_dq_merge_kernel(const float* __restrict__ dqrec, const int32_t* __restrict__ idx,
@@ -764,23 +706,36 @@ __global__ void __launch_bounds__(256)
   *d = o;
 }
 
-// dk, dv of a block's keys: one workgroup per run of up to CPW consecutive chunks of the block (the
-// workgroup of the run's first chunk; the others exit), SB / 16 waves of 16 keys each, the (chunk,
-// head) items one after the other with the pairs' q and d_out rows gathered into LDS (rows on M, as
-// in the key kernel); one atomic add per key and channel at the end.
+// dk, dv of a block's keys and the pairs' dq records: one workgroup per run of up to CPW
+// consecutive chunks of the block (the workgroup of the run's first chunk; the others exit), SB / 16
+// waves of 16 keys each, the (chunk, head) items one after the other with the pairs' q and d_out
+// rows gathered into LDS.  Per item: S = Q K^T with the rows on M (as in the key kernel),
+// dv^T += d_out^T (g P), dk^T += Q^T ds; ds goes through LDS ([row][key], high part and remainder)
+// so that wave w forms dq^T = K^T ds^T for dims 32 db (db = w, w + NW, .. < 4) over all the block's
+// keys, K^T read transposed from the block's key tile; those go to the pairs' fp32 dq records.
+// One atomic add per key and channel for dk, dv at the end of the run.
 constexpr int CPW = 32;
 template <int SB>
+constexpr int sel_grad_lds() {
+  return (2 * 2 * PRC * HD + SB * HD + 2 * 2 * PRC * (SB + 8)) * 2;
+}
+template <int SB>
 __global__ void __launch_bounds__(512)
-    bwdf_sel_kv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ dout, const bf16* __restrict__ k,
-                       const bf16* __restrict__ v, const float* __restrict__ gates, const float* __restrict__ st_l,
-                       const float* __restrict__ st_e, SlcPairLists pl, float* __restrict__ dk,
-                       float* __restrict__ dv, Dims dm) {
+    bwdf_sel_grad_kernel(const bf16* __restrict__ q, const bf16* __restrict__ dout, const bf16* __restrict__ k,
+                         const bf16* __restrict__ v, const float* __restrict__ gates, const float* __restrict__ st_l,
+                         const float* __restrict__ st_e, SlcPairLists pl, float* __restrict__ dk,
+                         float* __restrict__ dv, float* __restrict__ dqrec, Dims dm) {
   constexpr int NW = SB / 16;
-  __shared__ __attribute__((aligned(16))) bf16 tq[2][PRC * HD];
-  __shared__ __attribute__((aligned(16))) bf16 tdo[2][PRC * HD];
+  constexpr int DSW = SB + 8;  // row stride of the ds tiles (elements; 16 bytes of padding)
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  bf16* tq = (bf16*)smem;             // [2][PRC][HD] swizzled
+  bf16* tdo = tq + 2 * PRC * HD;      // [2][PRC][HD] swizzled
+  bf16* tk = tdo + 2 * PRC * HD;      // [SB][HD] swizzled: the block's keys
+  bf16* tds = tk + SB * HD;           // [2 items][2 parts][PRC][DSW]
   __shared__ __attribute__((aligned(16))) float sL[2][PRC], sE[2][PRC], sG[2][PRC];
   __shared__ __attribute__((aligned(16))) int sT[2][PRC];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gi = l >> 4;
+  const int hl = l >> 5, n32 = l & 31, g16 = l >> 4, i16 = l & 15;
   const int bg = blockIdx.x / pl.cap_c, cc = blockIdx.x % pl.cap_c;
   const int64_t ci = (int64_t)bg * pl.cap_c + cc;
   const int j = pl.chunk_blk[ci];
@@ -794,9 +749,11 @@ __global__ void __launch_bounds__(512)
   const int nitems = nchk * G;
   const int64_t u = (int64_t)j * SB + 16 * w + c;
   const bool uvalid = u < dm.T;
+  const int64_t kvb = (b * dm.T * dm.Hkv + g) * (int64_t)HD;
+  stage_rows_bw<SB>(tk, k + kvb, (int64_t)dm.Hkv * HD, (int64_t)j * SB, dm.T, w, NW, l);
   bf16x8 kf[4], vf[4];
   {
-    const int64_t o = ((b * dm.T + (uvalid ? u : dm.T - 1)) * dm.Hkv + g) * (int64_t)HD + 8 * gi;
+    const int64_t o = kvb + (uvalid ? u : dm.T - 1) * dm.Hkv * (int64_t)HD + 8 * gi;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       kf[ks] = *(const bf16x8*)(k + o + 32 * ks);
@@ -815,9 +772,11 @@ __global__ void __launch_bounds__(512)
       const int64_t rw = pw >= 0 ? (pw >> 5) : 0;
       const int64_t o = ((b * dm.Tq + rw) * dm.Hq + hq) * (int64_t)HD + cl * 8;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(q + o),
-                                       (__attribute__((address_space(3))) void*)(tq[buf] + ins * 512), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(tq + buf * PRC * HD + ins * 512),
+                                       16, 0, 0);
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(dout + o),
-                                       (__attribute__((address_space(3))) void*)(tdo[buf] + ins * 512), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(tdo + buf * PRC * HD + ins * 512),
+                                       16, 0, 0);
     }
   };
   struct PairSt {
@@ -859,8 +818,9 @@ __global__ void __launch_bounds__(512)
       stage(buf ^ 1, i + 1);
       if (tid < PRC) nst = load_st(i + 1);
     }
-    const bf16* Qt = tq[buf];
-    const bf16* Dt = tdo[buf];
+    const int pw = pl.pairs[(ci + i / G) * PRC + n32];  // the pair of row n32 of the item (dq records)
+    const bf16* Qt = tq + buf * PRC * HD;
+    const bf16* Dt = tdo + buf * PRC * HD;
     f32x4 S[2], P[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) S[mb] = P[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -900,6 +860,41 @@ __global__ void __launch_bounds__(512)
       const bf16x8 aq = tr_a16(Qt, 0, db, c, gi);
       dka[db] = mfma16(aq, sh, dka[db]);
       dka[db] = mfma16(aq, sl, dka[db]);
+    }
+    // ds of this wave's 16 keys into the item's [row][key] tiles (rows 16 mb + 4 gi + jj, key 16 w + c)
+    bf16* dsh = tds + (size_t)buf * 2 * PRC * DSW;
+    bf16* dsl = dsh + PRC * DSW;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int o = (16 * mb + 4 * gi + jj) * DSW + 16 * w + c;
+        dsh[o] = sh[4 * mb + jj];
+        dsl[o] = sl[4 * mb + jj];
+      }
+    __syncthreads();
+    // dq^T (dims 32 db + l % 32, the item's 32 rows) = K^T ds^T over the block's keys
+    for (int db = w; db < 4; db += NW) {
+      f32x16 dqa = {};
+#pragma unroll
+      for (int ks = 0; ks < SB / 16; ++ks) {
+        const int r0 = 16 * ks + 8 * hl + (i16 >> 2);
+        const int col = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
+        const bf16x8 a = cat(lds_read_tr(tk + swz128(r0, col >> 3) + (col & 7)),
+                             lds_read_tr(tk + swz128(r0 + 4, col >> 3) + (col & 7)));
+        const int ob = n32 * DSW + 16 * ks + 8 * hl;
+        dqa = mfma32(a, *(const bf16x8*)(dsh + ob), dqa);
+        dqa = mfma32(a, *(const bf16x8*)(dsl + ob), dqa);
+      }
+      // register jj holds dim 32 db + 8 (jj / 4) + 4 hl + jj % 4 of row n32
+      if (pw >= 0) {
+        float* dst = dqrec + (((((b * dm.Tq + (pw >> 5)) * dm.Hkv + g) * dm.n + (pw & 31)) * G + i % G) * HD) +
+                     32 * db + 4 * hl;
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          *(float4*)(dst + 8 * qd) = make_float4(dqa[4 * qd] * dm.scale, dqa[4 * qd + 1] * dm.scale,
+                                                 dqa[4 * qd + 2] * dm.scale, dqa[4 * qd + 3] * dm.scale);
+      }
     }
     if (i + 1 < nitems && tid < PRC) put_st(buf ^ 1, nst);
   }
@@ -1003,21 +998,21 @@ template <int SB>
 static hipError_t launch_sel_bwd(const Dims& ds, const SlcPairLists& pl, const SelArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)(ds.B * ds.Hkv) * (unsigned)pl.cap_c;
   const int shm = 2 * SB * HD * 2;
-  for (const void* fn : {(const void*)bwdf_sel_stats_kernel<SB>, (const void*)bwdf_sel_dq_kernel<SB>}) {
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, shm);
-    if (e != hipSuccess) return e;
-  }
+  constexpr int shg = sel_grad_lds<SB>();
+  hipError_t e = hipFuncSetAttribute((const void*)bwdf_sel_stats_kernel<SB>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, shm);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute((const void*)bwdf_sel_grad_kernel<SB>, hipFuncAttributeMaxDynamicSharedMemorySize, shg);
+  if (e != hipSuccess) return e;
   bwdf_sel_stats_kernel<SB><<<dim3(grid), dim3(ds.G * 64), shm, s>>>(a.q, a.dout, a.k, a.v, pl, a.rec, ds);
   const int64_t nrh = ds.B * ds.Tq * ds.Hq;
   bwdf_sel_merge_kernel<<<dim3((unsigned)((nrh + 255) / 256)), dim3(256), 0, s>>>(a.rec, a.idx, a.vid, a.st_l,
                                                                                   a.st_e, a.dgates, ds);
-  bwdf_sel_dq_kernel<SB><<<dim3(grid), dim3(ds.G * 64), shm, s>>>(a.q, a.dout, a.k, a.v, a.gates, a.st_l, a.st_e,
-                                                                   pl, a.dqrec, ds);
+  bwdf_sel_grad_kernel<SB><<<dim3(grid), dim3(SB / 16 * 64), shg, s>>>(a.q, a.dout, a.k, a.v, a.gates, a.st_l,
+                                                                         a.st_e, pl, a.dk, a.dv, a.dqrec, ds);
   const int64_t nth = ds.B * ds.Tq * ds.Hq * (HD / 4);
   bwdf_sel_dq_merge_kernel<<<dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, s>>>(a.dqrec, a.idx, a.vid, a.dq,
                                                                                     ds);
-  bwdf_sel_kv_kernel<SB><<<dim3(grid), dim3(SB / 16 * 64), 0, s>>>(a.q, a.dout, a.k, a.v, a.gates, a.st_l, a.st_e,
-                                                                    pl, a.dk, a.dv, ds);
   return hipGetLastError();
 }
 
