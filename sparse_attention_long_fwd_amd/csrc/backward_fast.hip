@@ -734,6 +734,7 @@ __global__ void __launch_bounds__(512)
   bf16* tds = tk + SB * HD;           // [2 items][2 parts][PRC][DSW]
   __shared__ __attribute__((aligned(16))) float sL[2][PRC], sE[2][PRC], sG[2][PRC];
   __shared__ __attribute__((aligned(16))) int sT[2][PRC];
+  __shared__ int sPr[CPW * PRC];  // the run's pairs
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gi = l >> 4;
   const int hl = l >> 5, n32 = l & 31, g16 = l >> 4, i16 = l & 15;
   const int bg = blockIdx.x / pl.cap_c, cc = blockIdx.x % pl.cap_c;
@@ -747,10 +748,12 @@ __global__ void __launch_bounds__(512)
   int nchk = 1;
   while (nchk < CPW && cc + nchk < pl.cap_c && pl.chunk_blk[ci + nchk] == j) ++nchk;
   const int nitems = nchk * G;
+  for (int x = tid; x < nchk * PRC; x += NW * 64) sPr[x] = pl.pairs[ci * PRC + x];
   const int64_t u = (int64_t)j * SB + 16 * w + c;
   const bool uvalid = u < dm.T;
   const int64_t kvb = (b * dm.T * dm.Hkv + g) * (int64_t)HD;
   stage_rows_bw<SB>(tk, k + kvb, (int64_t)dm.Hkv * HD, (int64_t)j * SB, dm.T, w, NW, l);
+  __syncthreads();  // sPr
   bf16x8 kf[4], vf[4];
   {
     const int64_t o = kvb + (uvalid ? u : dm.T - 1) * dm.Hkv * (int64_t)HD + 8 * gi;
@@ -763,7 +766,7 @@ __global__ void __launch_bounds__(512)
   // item i: chunk ci + i / G, head g G + i % G.  Gathered rows: instruction ins fills LDS chunks
   // [64 ins, +64) = pair rows 4 ins .. 4 ins + 3 (an empty pair reads row 0, masked).
   auto stage = [&](int buf, int i) {
-    const int* prs = pl.pairs + (ci + i / G) * PRC;
+    const int* prs = sPr + (i / G) * PRC;
     const int hq = g * G + i % G;
     for (int ins = w; ins < PRC / 4; ins += NW) {
       const int p = ins * 64 + l;
@@ -786,7 +789,7 @@ __global__ void __launch_bounds__(512)
   // statistics of pair tid (tid < PRC) of item i
   auto load_st = [&](int i) -> PairSt {
     PairSt st{INFINITY, 0.f, 0.f, -1};
-    const int pw = pl.pairs[(ci + i / G) * PRC + tid];
+    const int pw = sPr[(i / G) * PRC + tid];
     if (pw >= 0) {
       const int64_t row = pw >> 5;
       const int64_t ri = (b * dm.Tq + row) * dm.Hq + g * G + i % G;
@@ -818,7 +821,7 @@ __global__ void __launch_bounds__(512)
       stage(buf ^ 1, i + 1);
       if (tid < PRC) nst = load_st(i + 1);
     }
-    const int pw = pl.pairs[(ci + i / G) * PRC + n32];  // the pair of row n32 of the item (dq records)
+    const int pw = sPr[(i / G) * PRC + n32];  // the pair of row n32 of the item (dq records)
     const bf16* Qt = tq + buf * PRC * HD;
     const bf16* Dt = tdo + buf * PRC * HD;
     f32x4 S[2], P[2];
