@@ -524,16 +524,14 @@ __global__ void __launch_bounds__(256) bwdf_zero_kernel(float* __restrict__ p, i
 // Selection, block-major.  One workgroup per chunk of up to 32 (row, slot) pairs of one block of SB
 // tokens.  The stats and dq kernels take a wave per head (wave w = head g G + w) with the block's K
 // and V staged in LDS and the pair's row on N (lane n = l % 32): S^T = K Q^T, dP^T = V d_out^T.
-template <int SB>
 struct SelChunk {
   int64_t b, row, t, rowi;
   int g, slot, j;
   bool valid;
 };
 
-template <int SB>
 __device__ __forceinline__ bool sel_chunk_setup(const SlcPairLists& pl, const Dims& dm, int w, int n,
-                                                SelChunk<SB>& sc) {
+                                                SelChunk& sc) {
   const int bg = blockIdx.x / pl.cap_c, cc = blockIdx.x % pl.cap_c;
   const int64_t ci = (int64_t)bg * pl.cap_c + cc;
   sc.j = pl.chunk_blk[ci];
@@ -553,7 +551,7 @@ __device__ __forceinline__ bool sel_chunk_setup(const SlcPairLists& pl, const Di
 // scaled to log2 units, keys after the row or past the sequence at -inf.
 template <int SB>
 __device__ __forceinline__ void sel_scores(const bf16* kt, const bf16* vt, const bf16x8 (&qf)[8],
-                                           const bf16x8 (&df)[8], const SelChunk<SB>& sc, const Dims& dm, int n,
+                                           const bf16x8 (&df)[8], const SelChunk& sc, const Dims& dm, int n,
                                            int hl, float cs, f32x16 (&s)[SB / 32], f32x16 (&dp)[SB / 32]) {
   constexpr int NKB = SB / 32;
 #pragma unroll
@@ -583,7 +581,7 @@ __device__ __forceinline__ void sel_scores(const bf16* kt, const bf16* vt, const
 }
 
 template <int SB>
-__device__ __forceinline__ void sel_load_rows(const bf16* q, const bf16* dout, const SelChunk<SB>& sc, int hl,
+__device__ __forceinline__ void sel_load_rows(const bf16* q, const bf16* dout, const SelChunk& sc, int hl,
                                               bf16x8 (&qf)[8], bf16x8 (&df)[8]) {
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
@@ -602,8 +600,8 @@ __global__ void __launch_bounds__(512)
   bf16* kt = (bf16*)smem;
   bf16* vt = kt + SB * HD;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, n = l & 31;
-  SelChunk<SB> sc;
-  if (!sel_chunk_setup<SB>(pl, dm, w, n, sc)) return;
+  SelChunk sc;
+  if (!sel_chunk_setup(pl, dm, w, n, sc)) return;
   const int64_t stride = (int64_t)dm.Hkv * HD;
   const int64_t kvb = (sc.b * dm.T * dm.Hkv + sc.g) * (int64_t)HD;
   stage_rows_bw<SB>(kt, k + kvb, stride, (int64_t)sc.j * SB, dm.T, w, dm.G, l);
