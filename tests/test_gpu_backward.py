@@ -139,18 +139,25 @@ def _block_sets(wl, rng):
     return idx
 
 
-def test_layer_backward_36k_sampled_rows():
-    """The 36K backward in the bench's launch configuration with the upstream gradient zero except
-    on sampled rows: those rows' dq and d gates (every other row's exactly zero) and the whole dk,
-    dv, dw_k, dw_v (which then hold only the sampled rows' contributions) against the oracle
-    restricted to the same rows.  Rows sit at the row-chunk boundaries of both key kernels, at the
-    text/video edges and at random; every other row carries a seeded valid block set."""
-    wl = synth.WORKLOADS["36k"]
-    flush("backward 36k sampled rows")
+@pytest.mark.parametrize("name", ["36k", "128k"])
+def test_layer_backward_sampled_rows(name):
+    """The 36K backward in the bench's launch configuration (and the 128K one) with the upstream
+    gradient zero except on sampled rows: those rows' dq and d gates (every other row's exactly zero)
+    and the whole dk, dv, dw_k, dw_v (which then hold only the sampled rows' contributions) against
+    the oracle restricted to the same rows.  Rows sit at the row-chunk boundaries of the generic key
+    kernels and at the row runs of the matrix-core selection (9,362 rows) and key kernels (4,096 and
+    1,024 rows), at the text/video edges and at random; every other row carries a seeded valid block
+    set."""
+    wl = synth.WORKLOADS[name]
+    flush("backward %s sampled rows" % name)
     inp = synth.make_inputs(wl, DEV)
     B, Tq, Hq, D = inp["q"].shape
     rng = np.random.default_rng(4321)
-    rows = {3, 255, 256, 300, 1151, 1152, 9087, 9088, 18175, 18176, 27263, 27264, 36095, 36096, Tq - 1}
+    rows = {3, 255, 256, 300, 1151, 1152, 4095, 4096, 9087, 9088, 9361, 9362, 18175, 18176, 18723, 18724,
+            27263, 27264, 36095, 36096, Tq - 1}
+    if name == "128k":
+        rows |= {65535, 65536, 93633, 93634, 131071 - 300, Tq - 257, Tq - 256}
+    rows = {r for r in rows if r < Tq}
     rows |= set(int(x) for x in rng.integers(256, Tq - 256, 6))
     rows = np.array(sorted(rows), dtype=np.int64)
     idx = _block_sets(wl, rng)
