@@ -117,15 +117,18 @@ __global__ void __launch_bounds__(512)
                     const uint8_t* __restrict__ vid, const float* __restrict__ gates, float* __restrict__ dq,
                     float* __restrict__ dgates, float* __restrict__ st_l, float* __restrict__ st_e, Dims dm) {
   constexpr int NT = CMP ? 4 : 2;  // LDS tiles per key tile: K, V (and their remainders)
+  const int ntile = (int)((dm.Tq + RT - 1) / RT);
+  // the row tiles of one (sequence, KV group) stay on as few XCDs as possible (their keys overlap)
+  int unit, rank;
+  if (!xcd_remap(blockIdx.x, (int)(dm.B * dm.Hkv), ntile, &unit, &rank)) return;
   constexpr int SLOT = CMP ? 0 : 2;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   bf16* lds = (bf16*)smem;
   const int G = dm.G;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gi = l >> 4;
-  const int ntile = (int)((dm.Tq + RT - 1) / RT);
-  const int64_t r0 = (int64_t)(ntile - 1 - (int)blockIdx.x) * RT;  // later (longer) tiles first
-  const int g = blockIdx.y;
-  const int64_t b = blockIdx.z;
+  const int64_t r0 = (int64_t)(ntile - 1 - rank) * RT;  // later (longer) tiles first
+  const int g = unit % dm.Hkv;
+  const int64_t b = unit / dm.Hkv;
   const int64_t r = r0 + c;
   const bool rvalid = r < dm.Tq;
   const int64_t rr = rvalid ? r : dm.Tq - 1;
@@ -327,12 +330,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
   __shared__ __attribute__((aligned(16))) float sL[2][KR], sE[2][KR], sG[2][KR];
   __shared__ __attribute__((aligned(16))) int sLo[2][KR], sHi[2][KR];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gi = l >> 4;
-  const int64_t ktile = blockIdx.x / nch;
-  const int ch = (int)(blockIdx.x % nch);
-  const int g = blockIdx.y;
-  const int64_t b = blockIdx.z;
   const int G = dm.G;
   const int64_t N = CMP ? dm.Nc : dm.T;
+  // consecutive key tiles of one (sequence, KV group) see nearly the same rows: kept on as few XCDs
+  // as possible so that their q / d_out tiles come from the XCD's L2
+  int unit, rank;
+  if (!xcd_remap(blockIdx.x, (int)(dm.B * dm.Hkv), (int)(((N + KT - 1) / KT) * nch), &unit, &rank)) return;
+  const int64_t ktile = rank / nch;
+  const int ch = rank % nch;
+  const int g = unit % dm.Hkv;
+  const int64_t b = unit / dm.Hkv;
   const int64_t kbase = ktile * KT;
   const int64_t ntr = (dm.Tq + KR - 1) / KR;
   // the first position that sees a key of the tile, the chunk's row tiles from there
@@ -1086,7 +1093,7 @@ hipError_t launch_layer_bwd_fast(const Dims& dm, const void* q_, const void* k_,
   bwdf_tbits_kernel<<<dim3((unsigned)((dm.B * ntr + 255) / 256)), dim3(256), 0, s>>>(vid, w.tbits, dm);
   // row kernels: the compression branch first (it writes dq), then the window / text rows
   {
-    const dim3 grid((unsigned)((dm.Tq + RT - 1) / RT), (unsigned)dm.Hkv, (unsigned)dm.B);
+    const dim3 grid(xcd_grid((int)(dm.B * dm.Hkv), (int)((dm.Tq + RT - 1) / RT)));
     const int shc = 4 * 2 * KT * HD * 2, shw = 2 * 2 * KT * HD * 2;
     e = hipFuncSetAttribute((const void*)bwdf_row_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, shc);
     if (e == hipSuccess)
@@ -1103,12 +1110,12 @@ hipError_t launch_layer_bwd_fast(const Dims& dm, const void* q_, const void* k_,
   // key kernels: window / text rows over the full-resolution keys, compression over the compressed ones
   {
     const int nchw = (int)((ntr + RTC_WIN - 1) / RTC_WIN);
-    const dim3 gw((unsigned)(((dm.T + KT - 1) / KT) * nchw), (unsigned)dm.Hkv, (unsigned)dm.B);
+    const dim3 gw(xcd_grid((int)(dm.B * dm.Hkv), (int)(((dm.T + KT - 1) / KT) * nchw)));
     bwdf_key_kernel<false><<<gw, dim3(256), 0, s>>>(q, dout, k, nullptr, v, nullptr, vid, gates, w.st_l, w.st_e,
                                                     w.tbits, dk, dv, dm, nchw);
     if (dm.Nc > 0) {
       const int nchc = (int)((ntr + RTC_CMP - 1) / RTC_CMP);
-      const dim3 gc((unsigned)(((dm.Nc + KT - 1) / KT) * nchc), (unsigned)dm.Hkv, (unsigned)dm.B);
+      const dim3 gc(xcd_grid((int)(dm.B * dm.Hkv), (int)(((dm.Nc + KT - 1) / KT) * nchc)));
       bwdf_key_kernel<true><<<gc, dim3(256), 0, s>>>(q, dout, w.kch, w.kcl, w.vch, w.vcl, vid, gates, w.st_l,
                                                      w.st_e, w.tbits, w.dkc, w.dvc, dm, nchc);
     }
