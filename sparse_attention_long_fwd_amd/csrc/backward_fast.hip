@@ -332,12 +332,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c = l & 15, gi = l >> 4;
   const int G = dm.G;
   const int64_t N = CMP ? dm.Nc : dm.T;
-  // consecutive key tiles of one (sequence, KV group) see nearly the same rows: kept on as few XCDs
-  // as possible so that their q / d_out tiles come from the XCD's L2
+  // the work of one (sequence, KV group) is kept on as few XCDs as possible, in an order whose
+  // neighbours read the same q / d_out tiles from the XCD's L2: window keys key-tile-major (the
+  // bands of neighbouring key tiles overlap), compressed keys chunk-major (every key tile of a
+  // row chunk reads all its rows)
+  const int nkt = (int)((N + KT - 1) / KT);
   int unit, rank;
-  if (!xcd_remap(blockIdx.x, (int)(dm.B * dm.Hkv), (int)(((N + KT - 1) / KT) * nch), &unit, &rank)) return;
-  const int64_t ktile = rank / nch;
-  const int ch = rank % nch;
+  if (!xcd_remap(blockIdx.x, (int)(dm.B * dm.Hkv), nkt * nch, &unit, &rank)) return;
+  const int64_t ktile = CMP ? rank % nkt : rank / nch;
+  const int ch = CMP ? rank / nkt : rank % nch;
   const int g = unit % dm.Hkv;
   const int64_t b = unit / dm.Hkv;
   const int64_t kbase = ktile * KT;
