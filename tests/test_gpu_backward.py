@@ -37,19 +37,19 @@ def _setup(wl, seed_dout=900):
     return inp, dout, idx.to(DEV)
 
 
-def _run(wl, inp, dout, idx):
+def _run(wl, inp, dout, idx, vid_null=False):
     q = inp["q"]
     B, Tq, Hq, D = q.shape
     sh = nsa.make_shape(B, Tq, wl.kv_len, wl.q_start, Hq, wl.num_kv_heads, D)
     pr = nsa.make_params(**wl.params())
     g = nsa.nsa_hybrid_layer_bwd(q, inp["k"], inp["v"], inp["gates"], idx, dout, sh, pr, w_k=inp["w_k"],
-                                 w_v=inp["w_v"], is_video=inp["is_video"])
+                                 w_v=inp["w_v"], is_video=None if vid_null else inp["is_video"])
     torch.cuda.synchronize()
     return g
 
 
 CASES = ["f32-tiny", "bf16-ragged", "bf16-batch2", "bf16-short", "bf16-no-cmp-block", "bf16-all-text",
-         "bf16-q-start", "bf16-row-chunks", "bf16-sel32", "bf16-sel128", "bf16-g8", "bf16-g1"]
+         "bf16-q-start", "bf16-row-chunks", "bf16-sel32", "bf16-sel128", "bf16-g8", "bf16-g1", "bf16-no-flags"]
 
 
 @pytest.mark.parametrize("generic", [False, True], ids=["default", "generic"])
@@ -89,11 +89,15 @@ def _check_case(case):
         wl = _wl(T=1300, Hq=16, Hkv=2, lead=40, tail=9, n=8, w=128)
     elif case == "bf16-g1":  # one head per KV group
         wl = _wl(T=1100 + 5, Hq=3, Hkv=3, lead=20, tail=20, n=6, w=70)
+    elif case == "bf16-no-flags":  # every row a video row, passed as a NULL row-flag pointer
+        wl = _wl(T=1200 + 3, Hq=14, Hkv=2, lead=0, tail=0, n=8, w=128)
     else:  # enough rows that the generic key kernels split them into several chunks (3 and 5)
         wl = _wl(T=4500, Hq=8, Hkv=2, lead=32, tail=40, n=6, w=200)
     flush("backward %s" % case)
     inp, dout, idx = _setup(wl)
-    got = _run(wl, inp, dout, idx)
+    if case == "bf16-no-flags":
+        assert bool(inp["is_video"].all())
+    got = _run(wl, inp, dout, idx, vid_null=case == "bf16-no-flags")
     stats = {}
     tot = {"dk": 0.0, "dv": 0.0}
     for b in range(wl.batch):
