@@ -26,11 +26,14 @@
 //  bwdf_key_kernel<CMP>: 64 keys (16 a wave) x the rows that can see them, 32 rows of one head at a
 //    time with their q and d_out staged in LDS: S = Q K^T, dv^T += d_out^T (g P),
 //    dk^T += Q^T ds.  Row tiles are split into chunks whose sums go out with atomic adds.
-//  Selection, block-major over the pair lists of launch_slc_pair_lists (32 (row, slot) pairs of one
-//    chosen block per workgroup): bwdf_sel_stats_kernel leaves per (row, slot, head) the block's
-//    max, sum and sum P dP; bwdf_sel_merge_kernel combines a row's slots (statistics slot 1, d
-//    gates); bwdf_sel_grad_kernel adds dk, dv (atomic adds) and writes per-pair dq records that
-//    bwdf_sel_dq_merge_kernel adds to dq in slot order.
+//    Row and key tiles of one (sequence, KV group) run on as few XCDs as possible, neighbours
+//    (which share keys or rows) together.
+//  Selection, per (sequence, run of rows) sub-problem, block-major over the pair lists of
+//    launch_slc_pair_lists (chunks of 32 (row, slot) pairs of one chosen block):
+//    bwdf_sel_stats_kernel leaves per (row, slot, head) the block's max, sum and sum P dP;
+//    bwdf_sel_merge_kernel combines a row's slots (statistics slot 1, d gates);
+//    bwdf_sel_grad_kernel (a workgroup per run of up to 32 chunks of a block) adds dk, dv (atomic
+//    adds) and writes per-pair dq records that bwdf_sel_dq_merge_kernel adds to dq in slot order.
 // The order of the atomic adds depends on scheduling: the last bits of dk and dv can differ from
 // one call to the next (dq and the d gates are summed in a fixed order).
 #include "backward.hpp"
