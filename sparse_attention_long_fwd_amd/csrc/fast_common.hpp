@@ -112,3 +112,77 @@ __device__ __forceinline__ float load_pieces(const bf16* __restrict__ x, int o0,
     for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)v[i][e]));
   return m;
 }
+
+// Selection partial records (the value sum of one (row, slot, head) partial) in a block
+// floating-point form: 128 signed 12-bit integers X sharing one power-of-two step, 192 bytes (a
+// quarter fewer than fp16, for the same 11 bits of magnitude relative to the record's largest
+// value).  The step 2^(e - 11) is not stored: it is folded into the partial's (max, sum) pair as
+// (m + e - 11, l 2^(11 - e)), which leaves the merge weights 2^(m - M) l / L unchanged and scales
+// the value weights by exactly the step (see rec12_ml).  e is held to [-20, 128]: records whose
+// largest magnitude is below 2^-20 round to a step of 2^-31.
+//
+// Lane (row, hl) of an O^T accumulator owns dims 32 db + 8 j4 + 4 hl + e (db, j4, e in 0..3) as
+// acc[db][4 j4 + e].  It writes 8 packs of 8 values at bytes [96 hl + 12 p, +12): pack p = 2 db + c
+// holds acc[db][8 c .. 8 c + 7], i.e. dims 32 db + 16 c + 4 hl + {0..3} and the same + 8, as a
+// little-endian 96-bit string with value i at bit 12 i.
+constexpr int SLC_REC_BYTES = 192;
+
+__host__ __device__ inline int rec12_exp(float amax) {
+  int e = 0;
+  (void)frexpf(amax * 1.00048828125f, &e);  // amax (1 + 2^-11) < 2^e: scaled values round to |X| <= 2047
+  return e < -20 ? -20 : (e > 128 ? 128 : e);
+}
+
+// (max, sum) of a partial whose values were stored with exponent e.
+__host__ __device__ inline float2 rec12_ml(float m, float l, int e) {
+  return make_float2(m + (float)(e - 11), ldexpf(l, 11 - e));
+}
+
+// Eight values times `scale` (2^(11 - e)) rounded to the nearest integer, packed into three words.
+__host__ __device__ inline void rec12_pack8(const float* x, float scale, uint32_t* w3) {
+  uint32_t u[8];
+  for (int i = 0; i < 8; ++i) {
+    // adding 1.5 * 2^23 rounds to an integer held in the low mantissa bits (two's complement mod 2^12)
+    const float f = fmaf(x[i], scale, 12582912.0f);
+    uint32_t b;
+    __builtin_memcpy(&b, &f, 4);
+    u[i] = b & 0xFFFu;
+  }
+  w3[0] = u[0] | (u[1] << 12) | (u[2] << 24);
+  w3[1] = (u[2] >> 8) | (u[3] << 4) | (u[4] << 16) | (u[5] << 28);
+  w3[2] = (u[5] >> 4) | (u[6] << 8) | (u[7] << 20);
+}
+
+__host__ __device__ inline int rec12_sx(uint32_t w, int bit) { return (int)(w << (20 - bit)) >> 20; }
+
+// The eight integers of a pack, as floats.
+__host__ __device__ inline void rec12_unpack8(uint32_t a, uint32_t b, uint32_t c, float* x) {
+  x[0] = (float)rec12_sx(a, 0);
+  x[1] = (float)rec12_sx(a, 12);
+  x[2] = (float)rec12_sx((a >> 24) | (b << 8), 0);
+  x[3] = (float)rec12_sx(b, 4);
+  x[4] = (float)rec12_sx(b, 16);
+  x[5] = (float)rec12_sx((b >> 28) | (c << 4), 0);
+  x[6] = (float)rec12_sx(c, 8);
+  x[7] = (float)rec12_sx(c, 20);
+}
+
+// Writes lane (row, hl)'s half of a record from its accumulators acc[4][16] times `mul`, with the
+// record's exponent e (both halves must use the same e).
+template <typename Acc>
+__device__ __forceinline__ void rec12_store_half(unsigned char* rec, int hl, const Acc (&acc)[4], float mul, int e) {
+  const float scale = ldexpf(mul, 11 - e);
+  uint32_t w[24];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = acc[db][8 * c + i];
+      rec12_pack8(x, scale, w + 3 * (2 * db + c));
+    }
+  uint4* dst = (uint4*)(rec + 96 * hl);
+#pragma unroll
+  for (int i = 0; i < 6; ++i) dst[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+}

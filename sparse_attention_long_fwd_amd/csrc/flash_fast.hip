@@ -38,7 +38,7 @@ __device__ __forceinline__ void fwait_loads() { asm volatile("s_waitcnt vmcnt(0)
 
 struct FlashOut {
   float2* lml;    // selection partials (max, sum) per (row, group, slot, head), or NULL (no local pass)
-  _Float16* lo;   // their value records [.. , D] fp16
+  unsigned char* lo;  // their value records (12-bit, SLC_REC_BYTES each)
   float* swa32;   // [B, Tq, Hq, D] fp32 window output (may be NULL)
   bf16* swa_bf;   // bf16 window output (may be NULL)
   bf16* text;     // dense output of text rows (the layer's out)
@@ -260,23 +260,22 @@ flash_fast_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       flash_pass2(kbase, vbase, stride, dm.T, ktl, kt1, kt0, ktl, qf, klo, t, isv, c2, buf0, w, FW, l, hact, m_run,
                   l_run, oacc, [&] {
         const float lt = l_run + __shfl_xor(l_run, 32, 64);
+        // normalised to sum 1 (the maximum is kept lazily), as a 12-bit record whose exponent comes
+        // from both lane halves' largest value
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        float amax = 0.f;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) amax = fmaxf(amax, fabsf(oacc[db][jj]));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64)) * inv;
+        const int ex = rec12_exp(amax);
         if (isv && hact) {
           const int nvalid = dm.n < jt + 1 ? dm.n : jt + 1;
           const int64_t rec0 = (((b * dm.Tq + r) * dm.Hkv + g) * dm.n + (nvalid - nle)) * G + hw;
-          // normalised to sum 1 (the maximum is kept lazily and the fp16 record needs bounded values)
-          const float inv = lt > 0.f ? 1.f / lt : 0.f;
-          typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int j4 = 0; j4 < 4; ++j4) {
-              h4 x;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) x[e] = (_Float16)(oacc[db][4 * j4 + e] * inv);
-              *(h4*)(fo.lo + rec0 * HD + 32 * db + 8 * j4 + 4 * hl) = x;
-            }
+          rec12_store_half(fo.lo + rec0 * SLC_REC_BYTES, hl, oacc, inv, ex);
           if (hl == 0) {
-            fo.lml[rec0] = lt > 0.f ? make_float2(m_run + flog2(lt), 1.f) : make_float2(-INFINITY, 0.f);
+            fo.lml[rec0] = lt > 0.f ? rec12_ml(m_run + flog2(lt), 1.f, ex) : make_float2(-INFINITY, 0.f);
             for (int e = 1; e < nle; ++e) fo.lml[rec0 + (int64_t)e * G] = make_float2(-INFINITY, 0.f);
           }
         }
@@ -437,7 +436,7 @@ hipError_t launch_flash_fast(const Dims& dm, const void* q, const void* k, const
   FlashOut fo;
   if ((local_ml != nullptr) != (local_o != nullptr) || (local_ml && !local_fusable(dm))) return hipErrorInvalidValue;
   fo.lml = (float2*)local_ml;
-  fo.lo = (_Float16*)local_o;
+  fo.lo = (unsigned char*)local_o;
   fo.swa32 = swa32;
   fo.swa_bf = (bf16*)swa_bf;
   fo.text = (bf16*)text;

@@ -222,7 +222,7 @@ __device__ __forceinline__ void stage_rows(bf16* lds_tile, const bf16* src, int6
 template <int SB>
 __global__ void __launch_bounds__(512) slc_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                         const bf16* __restrict__ v, SlcBuckets bk,
-                                                        float2* __restrict__ pml, _Float16* __restrict__ po, Dims dm) {
+                                                        float2* __restrict__ pml, unsigned char* __restrict__ po, Dims dm) {
   constexpr int NKB = SB / 32;  // 32-key blocks of the score tile
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   bf16* kt = (bf16*)smem;
@@ -315,48 +315,30 @@ __global__ void __launch_bounds__(512) slc_chunk_kernel(const bf16* __restrict__
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ls), __float_as_uint(ls), false, false);
     ls += __uint_as_float(hl ? r[0] : r[1]);
   }
-  // O^T register j of dims block db holds dim 32 db + 8 (j >> 2) + 4 hl + (j & 3) of row n.
-  // Lanes n and n + 32 swap halves so that each stores 16 contiguous bytes: lane half hl
-  // writes dims 32 db + 8 (2 qp + hl) .. +8.
-  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-  uint4 st[4][2];
+  // O^T register j of dims block db holds dim 32 db + 8 (j >> 2) + 4 hl + (j & 3) of row n: the
+  // layout of a 12-bit record half; the record's exponent comes from both halves' largest value.
+  float amax = 0.f;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int qp = 0; qp < 2; ++qp) {
-      h4 x0, x1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x0[e] = (_Float16)oacc[db][8 * qp + e];      // dim 8 (2 qp) + 4 hl + e
-        x1[e] = (_Float16)oacc[db][8 * qp + 4 + e];  // dim 8 (2 qp + 1) + 4 hl + e
-      }
-      const uint2 own0 = __builtin_bit_cast(uint2, x0), own1 = __builtin_bit_cast(uint2, x1);
-      const uint2 send = hl ? own0 : own1, keep = hl ? own1 : own0;
-      uint2 recv;
-      {
-        const auto r0 = __builtin_amdgcn_permlane32_swap(send.x, send.x, false, false);
-        const auto r1 = __builtin_amdgcn_permlane32_swap(send.y, send.y, false, false);
-        recv.x = hl ? r0[0] : r0[1];
-        recv.y = hl ? r1[0] : r1[1];
-      }
-      st[db][qp] = hl ? make_uint4(recv.x, recv.y, keep.x, keep.y) : make_uint4(keep.x, keep.y, recv.x, recv.y);
-    }
+    for (int jj = 0; jj < 16; ++jj) amax = fmaxf(amax, fabsf(oacc[db][jj]));
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax), __float_as_uint(amax), false, false);
+    amax = fmaxf(amax, __uint_as_float(hl ? r[0] : r[1]));
+  }
+  const int ex = rec12_exp(amax);
   if (!valid) return;
   const int64_t ri = (((b * dm.Tq + row) * dm.Hkv + g) * dm.n + slot) * G + w;
-  if (hl == 0) pml[ri] = make_float2(mx * c2, ls);
-  _Float16* o16 = po + ri * HD;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int qp = 0; qp < 2; ++qp) *(uint4*)(o16 + 32 * db + 8 * (2 * qp + hl)) = st[db][qp];
+  if (hl == 0) pml[ri] = rec12_ml(mx * c2, ls, ex);
+  rec12_store_half(po + ri * SLC_REC_BYTES, hl, oacc, 1.f, ex);
 }
 
 // ---------------------------------------------------------------------------
-// One wave per (video row, group): merge the slots per head, gated combine.  Lane l owns
-// dims 2l, 2l+1.
+// One wave per (video row, group): merge the slots per head, gated combine.  Lane l takes pack
+// l & 15 (8 dims) of the records of head w0 + (l >> 4), four heads a pass.
 template <bool OCMP_F32>
 __global__ void __launch_bounds__(256) slc_merge_kernel(const float2* __restrict__ pml,
-                                                        const _Float16* __restrict__ po,
+                                                        const unsigned char* __restrict__ po,
                                                         const int32_t* __restrict__ idx,
                                                         const uint8_t* __restrict__ vid, const void* __restrict__ ocmp,
                                                         const float* __restrict__ swa32,
@@ -372,7 +354,7 @@ __global__ void __launch_bounds__(256) slc_merge_kernel(const float2* __restrict
   const int G = dm.G;
   const int32_t* sel = idx + item * dm.n;
   const float2* mls = pml + item * dm.n * G;
-  const _Float16* ors = po + item * dm.n * G * (int64_t)HD;
+  const unsigned char* ors = po + item * dm.n * G * (int64_t)SLC_REC_BYTES;
   // weights: lane s (< n) holds slot s; one load round for the (max, sum) of every head.  Slots
   // whose block lies after the row (no key, no partial: see slc_pair_kept) weigh nothing.
   {
@@ -399,53 +381,64 @@ __global__ void __launch_bounds__(256) slc_merge_kernel(const float2* __restrict
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // values: lane l owns dims 2l, 2l+1; heads in pairs, 16 slots a pass, all loads of a pass in flight
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  for (int w0 = 0; w0 < G; w0 += 2) {
-    float o[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  // values: 16 slots a pass, all loads of a pass in flight.  Integer records hold no NaN or
+  // infinity, so unused slots (stale data) need only their zero weight.
+  const int P = l & 15, hsub = l >> 4;
+  const int d0 = 32 * ((P & 7) >> 1) + 16 * (P & 1) + 4 * (P >> 3);  // dims d0 .. d0+3, d0+8 .. d0+11
+  for (int w0 = 0; w0 < G; w0 += 4) {
+    const int w = w0 + hsub;
+    const int wc = w < G ? w : G - 1;
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < dm.n; s0 += 16) {
-      h2 x[2][16];
+      uint32_t x[16][3];
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int u = 0; u < 16; ++u) {
+        const int s = s0 + u < dm.n ? s0 + u : dm.n - 1;
+        const uint32_t* src = (const uint32_t*)(ors + ((int64_t)s * G + wc) * SLC_REC_BYTES + 12 * P);
+        x[u][0] = src[0];
+        x[u][1] = src[1];
+        x[u][2] = src[2];
+      }
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int s = s0 + u < dm.n ? s0 + u : dm.n - 1;
-          const int w = w0 + a < G ? w0 + a : G - 1;
-          x[a][u] = *(const h2*)(ors + ((int64_t)s * G + w) * HD + 2 * l);
-        }
+      for (int u = 0; u < 16; ++u) {
+        const float ws = (s0 + u < dm.n) ? s_wt[wv][wc][s0 + u] : 0.f;
+        float y[8];
+        rec12_unpack8(x[u][0], x[u][1], x[u][2], y);
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const float ws = (s0 + u < dm.n && w0 + a < G) ? s_wt[wv][w0 + a][s0 + u] : 0.f;
-          o[a][0] += ws != 0.f ? ws * (float)x[a][u][0] : 0.f;  // unused slots: stale data, weight 0
-          o[a][1] += ws != 0.f ? ws * (float)x[a][u][1] : 0.f;
-        }
+        for (int i = 0; i < 8; ++i) o[i] = fmaf(ws, y[i], o[i]);
+      }
     }
+    if (w >= G) continue;
+    const int hq = g * G + w;
+    const int64_t rowoff = (br * dm.Hq + hq) * (int64_t)HD;
+    const float* gg = gates + (br * dm.Hq + hq) * 3;
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int w = w0 + a;
-      if (w >= G) break;
-      const int hq = g * G + w;
-      const int64_t off = (br * dm.Hq + hq) * (int64_t)HD + 2 * l;
+    for (int half = 0; half < 2; ++half) {
+      const int64_t off = rowoff + d0 + 8 * half;
+      const float* oh = o + 4 * half;
       if (o_slc) {
-        o_slc[off] = (bf16)o[a][0];
-        o_slc[off + 1] = (bf16)o[a][1];
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (bf16)oh[e];
+        *(bf16x4*)(o_slc + off) = v4;
       }
       if (out) {
-        float c0, c1;
+        float c[4];
         if constexpr (OCMP_F32) {
-          const float2 c = *(const float2*)((const float*)ocmp + off);
-          c0 = c.x;
-          c1 = c.y;
+          const float4 c4 = *(const float4*)((const float*)ocmp + off);
+          c[0] = c4.x; c[1] = c4.y; c[2] = c4.z; c[3] = c4.w;
         } else {
-          c0 = (float)((const bf16*)ocmp)[off];
-          c1 = (float)((const bf16*)ocmp)[off + 1];
+          const bf16x4 c4 = *(const bf16x4*)((const bf16*)ocmp + off);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) c[e] = (float)c4[e];
         }
-        const float2 sw = *(const float2*)(swa32 + off);
-        const float* gg = gates + (br * dm.Hq + hq) * 3;
-        out[off] = (bf16)(gg[0] * c0 + gg[1] * o[a][0] + gg[2] * sw.x);
-        out[off + 1] = (bf16)(gg[0] * c1 + gg[1] * o[a][1] + gg[2] * sw.y);
+        const float4 sw = *(const float4*)(swa32 + off);
+        const float swv[4] = {sw.x, sw.y, sw.z, sw.w};
+        const float g0 = gg[0], g1 = gg[1], g2 = gg[2];
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (bf16)(g0 * c[e] + g1 * oh[e] + g2 * swv[e]);
+        *(bf16x4*)(out + off) = v4;
       }
     }
   }
@@ -463,7 +456,7 @@ size_t slc_bucket_bytes(const Dims& dm) {
 
 size_t slc_block_workspace(const Dims& dm) {
   const size_t recs = (size_t)dm.B * dm.Tq * dm.Hkv * dm.n * dm.G;
-  return slc_bucket_bytes(dm) + srup(recs * 8) + srup(recs * HD * 2);
+  return slc_bucket_bytes(dm) + srup(recs * 8) + srup(recs * SLC_REC_BYTES);
 }
 
 // The (max, sum) and value-record arrays of the selection partials inside the workspace.
@@ -529,7 +522,7 @@ hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const 
   if (e != hipSuccess) return e;
   const size_t recs = (size_t)dm.B * dm.Tq * dm.Hkv * dm.n * dm.G;
   float2* pml = (float2*)((char*)ws + slc_bucket_bytes(dm));
-  _Float16* po = (_Float16*)((char*)pml + srup(recs * 8));
+  unsigned char* po = (unsigned char*)pml + srup(recs * 8);
   auto chunk = [&](auto kernel, int sb) -> hipError_t {
     const int shm = 2 * sb * HD * 2;
     hipError_t e2 = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, shm);
