@@ -35,8 +35,8 @@ hipError_t launch_compress_kv16(const Dims& dm, const void* k, const float* w_k,
 hipError_t launch_cmp_group(const Dims& dm, const void* q, const void* kv16, const uint8_t* vid, void* o_bf,
                             float* o32, float* lse, float* imp, hipStream_t s);
 
-// Window branch, text rows, selection branch and the gated combine.  o_cmp is
-// fp32 when ocmp_f32, else bf16.  ws: fast_sparse_workspace(dm) bytes.  ks / vs: keys and values
+// Window branch, text rows, selection branch and the gated combine of the compression output
+// o_cmp (bf16), the selection output and the window output (bf16, in o_swa or the workspace).  ws: fast_sparse_workspace(dm) bytes.  ks / vs: keys and values
 // of the selection branch; kw / vw: of the window branch and text rows.  forced_local: idx comes
 // from the layer's own top-n, so each video row's last min(n_local, jt + 1) entries are its forced
 // local blocks jt - n_local + 1 .. jt (the window pass may then take them over).
@@ -44,7 +44,7 @@ hipError_t launch_cmp_group(const Dims& dm, const void* q, const void* kv16, con
 // selection kernels; otherwise the two passes run in order on s (mark is called between them).
 hipError_t launch_sparse_fast(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
                               const void* vw, const int32_t* idx,
-                              const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out,
+                              const uint8_t* vid, const void* o_cmp, const float* gates, void* out,
                               void* o_slc, void* o_swa, void* ws, hipStream_t s,
                               void (*mark)(hipStream_t) = nullptr, bool forced_local = false,
                               bool concurrent = false);
@@ -64,7 +64,8 @@ SideStream* side_stream(hipStream_t caller);
 // The two passes of launch_sparse_fast.  With side, the window pass runs on side->s once the
 // caller's stream reaches the launch (side->fork) and records side->join when done; the selection
 // pass's merge waits for side->join on the caller's stream.  Both passes take the same side (or
-// null) and the same workspace.
+// null), the same workspace and the same o_swa: the window output of the video rows in bf16 goes
+// there when given, else to the workspace, and the combine reads it back.
 hipError_t launch_sparse_window(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
                                 const void* vw, const uint8_t* vid, void* out, void* o_swa, void* ws, hipStream_t s,
                                 const SideStream* side, bool forced_local);
@@ -73,8 +74,8 @@ hipError_t launch_sparse_window(const Dims& dm, const void* q, const void* ks, c
 hipError_t join_side_stream(const SideStream* side, hipStream_t s);
 hipError_t launch_sparse_select(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
                                 const void* vw, const int32_t* idx, const uint8_t* vid, const void* o_cmp,
-                                bool ocmp_f32, const float* gates, void* out, void* o_slc, void* ws, hipStream_t s,
-                                const SideStream* side, bool forced_local);
+                                const float* gates, void* out, void* o_slc, const void* o_swa,
+                                void* ws, hipStream_t s, const SideStream* side, bool forced_local);
 
 // The kept (row, slot) pairs of the video rows bucketed by chosen block (every pair whose block holds a
 // key at or before its row): chunk c of (batch, group) bg covers block chunk_blk[bg * cap_c + c]

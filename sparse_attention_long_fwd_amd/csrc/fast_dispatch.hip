@@ -4,7 +4,7 @@
 size_t slc_block_workspace(const Dims& dm);
 void slc_partial_arrays(const Dims& dm, void* ws, void** ml, void** o);
 hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
-                            const uint8_t* vid, const void* ocmp, bool ocmp_f32, const float* swa32,
+                            const uint8_t* vid, const void* ocmp, const void* swa,
                             const float* gates, void* out, void* o_slc, void* ws, hipStream_t s,
                             bool local_fused, hipEvent_t before_merge);
 
@@ -19,9 +19,12 @@ bool fast_supported(int32_t dtype, const Dims& dm) {
 
 static size_t rup(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// [window output, fp32][split partials of long text rows][block-major selection]
+// [window output of the video rows, bf16 (the caller's o_swa instead when given)][split partials of
+// long text rows][block-major selection]
+static size_t swa_bytes(const Dims& dm) { return rup((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 2); }
+
 size_t fast_sparse_workspace(const Dims& dm) {
-  return rup((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 4) + rup(flash_workspace(dm)) + rup(slc_block_workspace(dm));
+  return swa_bytes(dm) + rup(flash_workspace(dm)) + rup(slc_block_workspace(dm));
 }
 
 // The window pass takes over the forced local blocks of the selection (they lie inside the window
@@ -59,8 +62,8 @@ SideStream* side_stream(hipStream_t caller) {
 hipError_t launch_sparse_window(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
                                 const void* vw, const uint8_t* vid, void* out, void* o_swa, void* ws, hipStream_t s,
                                 const SideStream* side, bool forced_local) {
-  float* swa32 = (float*)ws;
-  char* fws = (char*)ws + rup((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 4);
+  void* swa = o_swa ? o_swa : ws;
+  char* fws = (char*)ws + swa_bytes(dm);
   char* sws = fws + rup(flash_workspace(dm));
   void *lml = nullptr, *lo = nullptr;
   if (fuse_local(dm, ks, vs, kw, vw, forced_local)) slc_partial_arrays(dm, sws, &lml, &lo);
@@ -71,9 +74,9 @@ hipError_t launch_sparse_window(const Dims& dm, const void* q, const void* ks, c
     if (e != hipSuccess) return e;
     sw = side->s;
   }
-  // window branch (fp32 for the combine, bf16 copy if asked) and dense text rows; the join event
+  // window branch (bf16, read by the combine) and dense text rows; the join event
   // is recorded even when the launch failed, so that the caller can always rejoin the side stream
-  hipError_t e = launch_flash_fast(dm, q, kw, vw, vid, swa32, o_swa, out, fws, sw, lml, lo);
+  hipError_t e = launch_flash_fast(dm, q, kw, vw, vid, nullptr, swa, out, fws, sw, lml, lo);
   if (side) {
     const hipError_t ej = hipEventRecord(side->join, sw);
     if (e == hipSuccess) e = ej;
@@ -87,26 +90,26 @@ hipError_t join_side_stream(const SideStream* side, hipStream_t s) {
 
 hipError_t launch_sparse_select(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
                                 const void* vw, const int32_t* idx, const uint8_t* vid, const void* o_cmp,
-                                bool ocmp_f32, const float* gates, void* out, void* o_slc, void* ws, hipStream_t s,
-                                const SideStream* side, bool forced_local) {
-  float* swa32 = (float*)ws;
-  char* sws = (char*)ws + rup((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 4) + rup(flash_workspace(dm));
+                                const float* gates, void* out, void* o_slc, const void* o_swa,
+                                void* ws, hipStream_t s, const SideStream* side, bool forced_local) {
+  const void* swa = o_swa ? o_swa : ws;
+  char* sws = (char*)ws + swa_bytes(dm) + rup(flash_workspace(dm));
   // selection branch and the gated combine of video rows
-  return launch_slc_block(dm, q, ks, vs, idx, vid, o_cmp, ocmp_f32, swa32, gates, out, o_slc, sws, s,
+  return launch_slc_block(dm, q, ks, vs, idx, vid, o_cmp, swa, gates, out, o_slc, sws, s,
                           fuse_local(dm, ks, vs, kw, vw, forced_local), side ? side->join : nullptr);
 }
 
 hipError_t launch_sparse_fast(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
                               const void* vw, const int32_t* idx,
-                              const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out,
+                              const uint8_t* vid, const void* o_cmp, const float* gates, void* out,
                               void* o_slc, void* o_swa, void* ws, hipStream_t s, void (*mark)(hipStream_t),
                               bool forced_local, bool concurrent) {
   const SideStream* side = concurrent ? side_stream(s) : nullptr;
   hipError_t e = launch_sparse_window(dm, q, ks, vs, kw, vw, vid, out, o_swa, ws, s, side, forced_local);
   if (e == hipSuccess) {
     if (mark && !side) mark(s);
-    e = launch_sparse_select(dm, q, ks, vs, kw, vw, idx, vid, o_cmp, ocmp_f32, gates, out, o_slc, ws, s, side,
-                             forced_local);
+    e = launch_sparse_select(dm, q, ks, vs, kw, vw, idx, vid, o_cmp, gates, out, o_slc, o_swa, ws, s,
+                             side, forced_local);
   }
   // on failure the caller's stream still waits for the window pass (a no-op once the merge did)
   if (e != hipSuccess) (void)join_side_stream(side, s);
