@@ -33,7 +33,8 @@ PHASE_SOURCES = {
     "cmp_attn_importance": ["sparse_attention_long_fwd_amd/csrc/cmp_group.hip",
                             "sparse_attention_long_fwd_amd/csrc/fast_common.hpp",
                             "sparse_attention_long_fwd_amd/csrc/mfma.hpp",
-                            "sparse_attention_long_fwd_amd/csrc/common.hpp"],
+                            "sparse_attention_long_fwd_amd/csrc/common.hpp",
+                            "sparse_attention_long_fwd_amd/csrc/api.cpp"],
 }
 # the kernels of each phase (name fragments); the compression branch runs its first sweep
 # (log-sum-exp) and its second sweep (probabilities, value sum, importance) as two kernels
@@ -47,10 +48,14 @@ COUNTER_KERNELS = {
     "cmp_group_kernel": PHASE_SOURCES["cmp_attn_importance"],
     "flash_fast_kernel": ["sparse_attention_long_fwd_amd/csrc/flash_fast.hip",
                           "sparse_attention_long_fwd_amd/csrc/fast_common.hpp",
-                          "sparse_attention_long_fwd_amd/csrc/mfma.hpp"],
+                          "sparse_attention_long_fwd_amd/csrc/mfma.hpp",
+                          "sparse_attention_long_fwd_amd/csrc/fast_dispatch.hip"],
     "slc_chunk_kernel": ["sparse_attention_long_fwd_amd/csrc/slc_block.hip",
                          "sparse_attention_long_fwd_amd/csrc/fast_common.hpp"],
-    "slc_merge_kernel": ["sparse_attention_long_fwd_amd/csrc/slc_block.hip"],
+    "slc_merge_kernel": ["sparse_attention_long_fwd_amd/csrc/slc_block.hip",
+                         "sparse_attention_long_fwd_amd/csrc/fast_common.hpp",
+                         "sparse_attention_long_fwd_amd/csrc/fast_dispatch.hip",
+                         "sparse_attention_long_fwd_amd/csrc/api.cpp"],
     "dcmp_pipe_kernel": ["sparse_attention_long_fwd_amd/csrc/decode_fast.hip",
                          "sparse_attention_long_fwd_amd/csrc/topk_wave.hpp"],
     "dsel_kernel": ["sparse_attention_long_fwd_amd/csrc/decode_fast.hip",
@@ -212,10 +217,16 @@ def record_counters(mfma_dir, ea_r_dir, ea_w_dir):
         per = {}
         for i, d in enumerate(dirs.split(",")):
             path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+            run = {}
             for r in csv.DictReader(open(path)):
-                key = (i, r["Dispatch_Id"], r["Kernel_Name"])
-                c = per.setdefault(key, {})
+                key = (i, int(r["Dispatch_Id"]), r["Kernel_Name"])
+                c = run.setdefault(key, {})
                 c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            # with more than one layer call in the run, only the last call's dispatches count (the
+            # first launch of a kernel in a process carries its start-up in the active cycles)
+            calls = sorted(k[1] for k in run if CALL_KERNEL in k[2])
+            first = calls[-1] if len(calls) > 1 else -1
+            per.update({k: v for k, v in run.items() if k[1] >= first})
         return per
 
     out = {}

@@ -161,8 +161,8 @@ LayerWs layer_ws(const Dims& dm, int32_t dtype) {
       w.kc = w.vc = 0;
       w.kv16 = round_up(kv16_tiles_bytes(dm));
     }
-    // branch output of the compression path in dtype (read by the combine)
-    w.o_cmp = round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * es);
+    // fp32 branch output of the compression path (read by the combine)
+    w.o_cmp = round_up((size_t)dm.B * dm.Tq * dm.Hq * dm.D * 4);
     w.imp = round_up((size_t)dm.B * dm.Tq * dm.Hkv * dm.Ns * 4);
     w.sparse = sparse_ws(dm, dtype).total;
   } else {
@@ -242,7 +242,8 @@ int64_t default_chunk_rows(const Dims& dm, int32_t dtype) {
 // and their scales and the values' bf16 low parts; kv16: instead of all these, the group kernel's
 // fp16 key / value tiles.
 // The MFMA compression kernels take 64-token selection blocks from row-major compressed keys and
-// 32-, 64- or 128-token blocks from the group kernel's tiles; other calls run the generic kernel.
+// 32-, 64- or 128-token blocks from the group kernel's tiles; other calls run the generic kernel
+// (its output in dtype, no fp32 copy).
 bool cmp_on_fast(int32_t dtype, const Dims& dm, bool kv16) { return use_fast(dtype, dm) && (kv16 || dm.ls == 64); }
 
 int run_cmp(int32_t dtype, int32_t cdtype, const Dims& dm, const void* q, const void* kc, const void* kl8,
@@ -269,10 +270,10 @@ struct BranchKV {
 
 // forced_local: idx is the layer's own top-n (its forced blocks present), not a caller's set.
 int run_sparse(int32_t dtype, const Dims& dm, const void* q, const BranchKV& kv, const int32_t* idx,
-               const uint8_t* vid, const void* o_cmp, const float* gates, void* out, void* o_slc,
+               const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out, void* o_slc,
                void* o_swa, void* ws, hipStream_t s, bool forced_local = false) {
   hipError_t e = use_fast(dtype, dm)
-                     ? launch_sparse_fast(dm, q, kv.ks, kv.vs, kv.kw, kv.vw, idx, vid, o_cmp, gates, out,
+                     ? launch_sparse_fast(dm, q, kv.ks, kv.vs, kv.kw, kv.vw, idx, vid, o_cmp, ocmp_f32, gates, out,
                                           o_slc, o_swa, ws, s, prof_mark, forced_local, !g_profiling)
                      : launch_sparse_generic(dtype, dm, q, kv.ks, kv.vs, kv.kw, kv.vw, idx, vid, o_cmp, gates, out,
                                              o_slc, o_swa, s);
@@ -425,7 +426,7 @@ int32_t nsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t
   if (fast && workspace_bytes < w.total)
     return fail(NSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, w.total);
   if (fast && w.total > 0 && !workspace) return fail(NSA_ERR_INVALID_ARG, "NULL workspace");
-  return run_sparse(dtype, dm, q, BranchKV{k, v, k, v, k, v}, block_idx, is_video, o_cmp, gates, out, o_slc,
+  return run_sparse(dtype, dm, q, BranchKV{k, v, k, v, k, v}, block_idx, is_video, o_cmp, false, gates, out, o_slc,
                     o_swa, workspace,
                     (hipStream_t)stream);
 }
@@ -544,13 +545,17 @@ int32_t layer_pass(const Dims& dm, int32_t dtype, const LayerIO& io, const float
     return NSA_OK;
   }
   const bool fast = use_fast(dtype, dm);
-  // The combine reads the compression output in dtype: the caller's o_cmp when given, else a copy
-  // in the workspace (the MFMA path's kernels accumulate in fp32 and round once).
+  // MFMA path: the combine reads an fp32 copy of the compression output; the caller's bf16 copy is
+  // optional.  Compression on the generic kernel (caller's compressed keys with 32- or 128-token
+  // selection blocks): its output in dtype, in the fp32 buffer's space when the caller gives none.
+  const bool c32 = cmp_on_fast(dtype, dm, kv16 != nullptr);
   prof_mark(s);
-  void* ocmp = o_cmp ? o_cmp : ocmp_ws;
+  void* ocmp = c32 ? o_cmp : (o_cmp ? o_cmp : ocmp_ws);
+  float* ocmp32 = c32 ? (float*)ocmp_ws : nullptr;
+  const void* ocmb = c32 ? (const void*)ocmp32 : ocmp;  // what the combine reads
   int32_t* idx = block_idx_out ? block_idx_out : idx_ws;
   st = run_cmp(dtype, cdtype, dm, q, kc_use, kl_use, ksc_use, vc_use, vl_use, kv16, is_video,
-               ocmp, nullptr, lse, imp, s);
+               ocmp, ocmp32, lse, imp, s);
   if (st != NSA_OK) return st;
   prof_mark(s);
   // The window pass needs neither the compression branch nor the top-n: outside phase timing it
@@ -565,7 +570,7 @@ int32_t layer_pass(const Dims& dm, int32_t dtype, const LayerIO& io, const float
       where = "top-n kernel";
     }
     if (e == hipSuccess) {
-      e = launch_sparse_select(dm, q, kv.ks, kv.vs, kv.kw, kv.vw, idx, is_video, ocmp, gates, out, o_slc,
+      e = launch_sparse_select(dm, q, kv.ks, kv.vs, kv.kw, kv.vw, idx, is_video, ocmb, c32, gates, out, o_slc,
                                o_swa, sparse_ws_ptr, s, side, true);
       where = "selection kernels";
     }
@@ -579,13 +584,13 @@ int32_t layer_pass(const Dims& dm, int32_t dtype, const LayerIO& io, const float
   if (e != hipSuccess) return hip_fail(e, "top-n kernel");
   prof_mark(s);
   if (fast) {
-    st = run_sparse(dtype, dm, q, kv, idx, is_video, ocmp, gates, out, o_slc, o_swa, sparse_ws_ptr, s,
+    st = run_sparse(dtype, dm, q, kv, idx, is_video, ocmb, c32, gates, out, o_slc, o_swa, sparse_ws_ptr, s,
                     true);
     prof_mark(s);
     return st;
   }
   void* oswa = o_swa ? o_swa : oswa_ws;
-  return run_sparse(dtype, dm, q, kv, idx, is_video, ocmp, gates, out, o_slc, oswa, sparse_ws_ptr, s);
+  return run_sparse(dtype, dm, q, kv, idx, is_video, ocmp, false, gates, out, o_slc, oswa, sparse_ws_ptr, s);
 }
 
 // The whole layer (nsa_hybrid_layer_fwd and its per-branch K/V form).

@@ -36,7 +36,8 @@ hipError_t launch_cmp_group(const Dims& dm, const void* q, const void* kv16, con
                             float* o32, float* lse, float* imp, hipStream_t s);
 
 // Window branch, text rows, selection branch and the gated combine of the compression output
-// o_cmp (bf16), the selection output and the window output (bf16, in o_swa or the workspace).  ws: fast_sparse_workspace(dm) bytes.  ks / vs: keys and values
+// o_cmp (fp32 when ocmp_f32, else bf16), the selection output and the window output (bf16, in
+// o_swa or the workspace).  ws: fast_sparse_workspace(dm) bytes.  ks / vs: keys and values
 // of the selection branch; kw / vw: of the window branch and text rows.  forced_local: idx comes
 // from the layer's own top-n, so each video row's last min(n_local, jt + 1) entries are its forced
 // local blocks jt - n_local + 1 .. jt (the window pass may then take them over).
@@ -44,7 +45,7 @@ hipError_t launch_cmp_group(const Dims& dm, const void* q, const void* kv16, con
 // selection kernels; otherwise the two passes run in order on s (mark is called between them).
 hipError_t launch_sparse_fast(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
                               const void* vw, const int32_t* idx,
-                              const uint8_t* vid, const void* o_cmp, const float* gates, void* out,
+                              const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out,
                               void* o_slc, void* o_swa, void* ws, hipStream_t s,
                               void (*mark)(hipStream_t) = nullptr, bool forced_local = false,
                               bool concurrent = false);
@@ -74,7 +75,7 @@ hipError_t launch_sparse_window(const Dims& dm, const void* q, const void* ks, c
 hipError_t join_side_stream(const SideStream* side, hipStream_t s);
 hipError_t launch_sparse_select(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
                                 const void* vw, const int32_t* idx, const uint8_t* vid, const void* o_cmp,
-                                const float* gates, void* out, void* o_slc, const void* o_swa,
+                                bool ocmp_f32, const float* gates, void* out, void* o_slc, const void* o_swa,
                                 void* ws, hipStream_t s, const SideStream* side, bool forced_local);
 
 // The kept (row, slot) pairs of the video rows bucketed by chosen block (every pair whose block holds a

@@ -4,7 +4,7 @@
 size_t slc_block_workspace(const Dims& dm);
 void slc_partial_arrays(const Dims& dm, void* ws, void** ml, void** o);
 hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
-                            const uint8_t* vid, const void* ocmp, const void* swa,
+                            const uint8_t* vid, const void* ocmp, bool ocmp_f32, const void* swa,
                             const float* gates, void* out, void* o_slc, void* ws, hipStream_t s,
                             bool local_fused, hipEvent_t before_merge);
 
@@ -90,25 +90,25 @@ hipError_t join_side_stream(const SideStream* side, hipStream_t s) {
 
 hipError_t launch_sparse_select(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
                                 const void* vw, const int32_t* idx, const uint8_t* vid, const void* o_cmp,
-                                const float* gates, void* out, void* o_slc, const void* o_swa,
+                                bool ocmp_f32, const float* gates, void* out, void* o_slc, const void* o_swa,
                                 void* ws, hipStream_t s, const SideStream* side, bool forced_local) {
   const void* swa = o_swa ? o_swa : ws;
   char* sws = (char*)ws + swa_bytes(dm) + rup(flash_workspace(dm));
   // selection branch and the gated combine of video rows
-  return launch_slc_block(dm, q, ks, vs, idx, vid, o_cmp, swa, gates, out, o_slc, sws, s,
+  return launch_slc_block(dm, q, ks, vs, idx, vid, o_cmp, ocmp_f32, swa, gates, out, o_slc, sws, s,
                           fuse_local(dm, ks, vs, kw, vw, forced_local), side ? side->join : nullptr);
 }
 
 hipError_t launch_sparse_fast(const Dims& dm, const void* q, const void* ks, const void* vs, const void* kw,
                               const void* vw, const int32_t* idx,
-                              const uint8_t* vid, const void* o_cmp, const float* gates, void* out,
+                              const uint8_t* vid, const void* o_cmp, bool ocmp_f32, const float* gates, void* out,
                               void* o_slc, void* o_swa, void* ws, hipStream_t s, void (*mark)(hipStream_t),
                               bool forced_local, bool concurrent) {
   const SideStream* side = concurrent ? side_stream(s) : nullptr;
   hipError_t e = launch_sparse_window(dm, q, ks, vs, kw, vw, vid, out, o_swa, ws, s, side, forced_local);
   if (e == hipSuccess) {
     if (mark && !side) mark(s);
-    e = launch_sparse_select(dm, q, ks, vs, kw, vw, idx, vid, o_cmp, gates, out, o_slc, o_swa, ws, s,
+    e = launch_sparse_select(dm, q, ks, vs, kw, vw, idx, vid, o_cmp, ocmp_f32, gates, out, o_slc, o_swa, ws, s,
                              side, forced_local);
   }
   // on failure the caller's stream still waits for the window pass (a no-op once the merge did)

@@ -336,10 +336,11 @@ __global__ void __launch_bounds__(512) slc_chunk_kernel(const bf16* __restrict__
 // ---------------------------------------------------------------------------
 // One wave per (video row, group): merge the slots per head, gated combine.  Lane l takes pack
 // l & 15 (8 dims) of the records of head w0 + (l >> 4), four heads a pass.
+template <bool OCMP_F32>
 __global__ void __launch_bounds__(256) slc_merge_kernel(const float2* __restrict__ pml,
                                                         const unsigned char* __restrict__ po,
                                                         const int32_t* __restrict__ idx,
-                                                        const uint8_t* __restrict__ vid, const bf16* __restrict__ ocmp,
+                                                        const uint8_t* __restrict__ vid, const void* __restrict__ ocmp,
                                                         const bf16* __restrict__ swa,
                                                         const float* __restrict__ gates, bf16* __restrict__ out,
                                                         bf16* __restrict__ o_slc, Dims dm) {
@@ -422,8 +423,15 @@ __global__ void __launch_bounds__(256) slc_merge_kernel(const float2* __restrict
         *(bf16x4*)(o_slc + off) = v4;
       }
       if (out) {
-        const bf16x4 c4 = *(const bf16x4*)(ocmp + off);
-        const float c[4] = {(float)c4[0], (float)c4[1], (float)c4[2], (float)c4[3]};
+        float c[4];
+        if constexpr (OCMP_F32) {
+          const float4 c4 = *(const float4*)((const float*)ocmp + off);
+          c[0] = c4.x; c[1] = c4.y; c[2] = c4.z; c[3] = c4.w;
+        } else {
+          const bf16x4 c4 = *(const bf16x4*)((const bf16*)ocmp + off);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) c[e] = (float)c4[e];
+        }
         const bf16x4 sw = *(const bf16x4*)(swa + off);
         const float swv[4] = {(float)sw[0], (float)sw[1], (float)sw[2], (float)sw[3]};
         const float g0 = gg[0], g1 = gg[1], g2 = gg[2];
@@ -504,7 +512,7 @@ hipError_t launch_slc_pair_lists(const Dims& dm, const int32_t* idx, const uint8
 }
 
 hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const void* v, const int32_t* idx,
-                            const uint8_t* vid, const void* ocmp, const void* swa,
+                            const uint8_t* vid, const void* ocmp, bool ocmp_f32, const void* swa,
                             const float* gates, void* out, void* o_slc, void* ws, hipStream_t s, bool local_fused,
                             hipEvent_t before_merge) {
   if (dm.B <= 0 || dm.Tq <= 0) return hipSuccess;
@@ -533,7 +541,11 @@ hipError_t launch_slc_block(const Dims& dm, const void* q, const void* k, const 
   }
   const int64_t items = dm.B * dm.Tq * dm.Hkv;
   const dim3 mg((unsigned)((items + 3) / 4));
-  slc_merge_kernel<<<mg, dim3(256), 0, s>>>(pml, po, idx, vid, (const bf16*)ocmp, (const bf16*)swa, gates,
-                                            (bf16*)out, (bf16*)o_slc, dm);
+  if (ocmp_f32)
+    slc_merge_kernel<true><<<mg, dim3(256), 0, s>>>(pml, po, idx, vid, ocmp, (const bf16*)swa, gates, (bf16*)out,
+                                                    (bf16*)o_slc, dm);
+  else
+    slc_merge_kernel<false><<<mg, dim3(256), 0, s>>>(pml, po, idx, vid, ocmp, (const bf16*)swa, gates, (bf16*)out,
+                                                     (bf16*)o_slc, dm);
   return hipGetLastError();
 }
