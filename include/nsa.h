@@ -195,8 +195,9 @@ int32_t nsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t
  * other dispatch needs the one-pass size).
  * nsa_hybrid_layer_workspace_size_rows: the scratch when at most
  * rows_per_chunk query rows run in one pass (0: all rows; < 0: returns 0).
- * nsa_hybrid_layer_workspace_size: the size for the default chunk, the
- * largest whose scratch stays within 7 GiB (all rows when they fit).
+ * nsa_hybrid_layer_workspace_size: the size for the default chunk: all rows
+ * when their scratch stays within 7 GiB, else the largest chunk that does,
+ * rounded down to a multiple of 16384 rows when it is at least that long.
  * Both return 0 for invalid arguments.
  */
 size_t nsa_hybrid_layer_workspace_size(const nsa_shape* shape, const nsa_params* params, int32_t dtype);

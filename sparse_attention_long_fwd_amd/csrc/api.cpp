@@ -231,10 +231,14 @@ int64_t fit_chunk_rows(const Dims& dm, int32_t dtype, size_t bytes) {
 }
 
 // Default: every row in one pass when that needs at most kDefaultWsCap bytes, else the largest
-// chunk that stays within it.
+// chunk that stays within it, rounded down to whole kChunkRound rows when it holds any (at 128K
+// the compression kernels ran ~3 % slower in passes of 43,712 rows than of 32,768 or 65,536).
+constexpr int64_t kChunkRound = 16384;
+
 int64_t default_chunk_rows(const Dims& dm, int32_t dtype) {
   const int64_t r = fit_chunk_rows(dm, dtype, kDefaultWsCap);
-  return r > 0 ? r : chunk_rows(dm, dtype, kChunkAlign);
+  if (r <= 0) return chunk_rows(dm, dtype, kChunkAlign);
+  return (r < dm.Tq && r >= kChunkRound) ? r / kChunkRound * kChunkRound : r;
 }
 
 // kc/vc: compressed keys/values (bf16 high parts on the MFMA path, or cdtype on the generic path);

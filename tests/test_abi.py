@@ -236,8 +236,9 @@ def test_backward_validates_first():
 
 
 def test_layer_workspace_rows():
-    """Row chunks: at 128K the default workspace stays within 7 GiB (one pass needs about 24 GB), the
-    size grows with the chunk, and a workspace below the 64-row size is refused before any launch."""
+    """Row chunks: at 128K the default workspace stays within 7 GiB (one pass needs about 19 GB) and
+    is the size of a whole number of 16K-row chunks (32K rows), the size grows with the chunk, and a
+    workspace below the 64-row size is refused before any launch."""
     sh = _dshape(batch=1, q_len=131072, kv_len=131072)
     pr = _params(top_n=16, window=512)
     bf = nsa.NSA_BF16
@@ -247,6 +248,7 @@ def test_layer_workspace_rows():
     sizes = [nsa.nsa_hybrid_layer_workspace_size_rows(sh, pr, bf, r) for r in (64, 1000, 1024, 32768, 131072)]
     assert sizes[0] < sizes[2] < sizes[3] < sizes[4] == full
     assert sizes[1] == nsa.nsa_hybrid_layer_workspace_size_rows(sh, pr, bf, 960)   # chunks are multiples of 64
+    assert dflt == sizes[3]  # the largest chunk within 7 GiB (43,712 rows), rounded down to 16K rows
     assert nsa.nsa_hybrid_layer_workspace_size_rows(sh, pr, bf, -1) == 0
     L = nsa.lib()
     st = L.nsa_hybrid_layer_fwd(FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, bf, ctypes.byref(sh),
