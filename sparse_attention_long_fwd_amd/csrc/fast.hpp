@@ -93,14 +93,14 @@ size_t slc_bucket_bytes(const Dims& dm);
 hipError_t launch_slc_pair_lists(const Dims& dm, const int32_t* idx, const uint8_t* vid, void* ws, SlcPairLists* pl,
                                  hipStream_t s);
 
-// Window / text-row flash kernel: swa32 / swa_bf window outputs (either may be
-// NULL), text: output of text rows (NULL: skip them); ws: flash_workspace(dm).
+// Window / text-row flash kernel: swa_bf the bf16 window output of the video rows (may be NULL),
+// text: output of text rows (NULL: skip them); ws: flash_workspace(dm).
 // local_ml / local_o (both or neither): the selection partial arrays of the selection kernels;
 // when given, the window pass also forms each video row's selection partial over its forced local
 // blocks (local_fusable(dm) must hold) and stores it in the row's first local slot (the others
 // are marked empty).
 hipError_t launch_flash_fast(const Dims& dm, const void* q, const void* k, const void* v, const uint8_t* vid,
-                             float* swa32, void* swa_bf, void* text, void* ws, hipStream_t s,
+                             void* swa_bf, void* text, void* ws, hipStream_t s,
                              void* local_ml = nullptr, void* local_o = nullptr);
 // The forced local blocks of every video row lie inside its window and the query tiles of 32 rows
 // never straddle a 64-token block.

@@ -76,7 +76,7 @@ hipError_t launch_sparse_window(const Dims& dm, const void* q, const void* ks, c
   }
   // window branch (bf16, read by the combine) and dense text rows; the join event
   // is recorded even when the launch failed, so that the caller can always rejoin the side stream
-  hipError_t e = launch_flash_fast(dm, q, kw, vw, vid, nullptr, swa, out, fws, sw, lml, lo);
+  hipError_t e = launch_flash_fast(dm, q, kw, vw, vid, swa, out, fws, sw, lml, lo);
   if (side) {
     const hipError_t ej = hipEventRecord(side->join, sw);
     if (e == hipSuccess) e = ej;

@@ -39,7 +39,6 @@ __device__ __forceinline__ void fwait_loads() { asm volatile("s_waitcnt vmcnt(0)
 struct FlashOut {
   float2* lml;    // selection partials (max, sum) per (row, group, slot, head), or NULL (no local pass)
   unsigned char* lo;  // their value records (12-bit, SLC_REC_BYTES each)
-  float* swa32;   // [B, Tq, Hq, D] fp32 window output (may be NULL)
   bf16* swa_bf;   // bf16 window output (may be NULL)
   bf16* text;     // dense output of text rows (the layer's out)
   float* part;    // split partials: [slot][chunk][G*32 columns][D + 2] (may be NULL)
@@ -292,15 +291,10 @@ flash_fast_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4) {
           const int d0 = 32 * db + 8 * j4 + 4 * hl;
-          const float4 o4 = make_float4(oacc[db][4 * j4] * inv, oacc[db][4 * j4 + 1] * inv,
-                                        oacc[db][4 * j4 + 2] * inv, oacc[db][4 * j4 + 3] * inv);
-          if (fo.swa32) *(float4*)(fo.swa32 + orow + d0) = o4;
           if (fo.swa_bf) {
             bf16x4 v4;
-            v4[0] = (bf16)o4.x;
-            v4[1] = (bf16)o4.y;
-            v4[2] = (bf16)o4.z;
-            v4[3] = (bf16)o4.w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v4[e] = (bf16)(oacc[db][4 * j4 + e] * inv);
             *(bf16x4*)(fo.swa_bf + orow + d0) = v4;
           }
         }
@@ -422,13 +416,13 @@ size_t flash_workspace(const Dims& dm) {
   return (size_t)dm.B * dm.Hkv * MAX_SPLIT_TILES * ns * dm.G * FQ * (HD + 2) * sizeof(float);
 }
 
-// swa32 / swa_bf: window outputs (either may be NULL); text: output of text rows (NULL: skip them).
+// swa_bf: window output (may be NULL); text: output of text rows (NULL: skip them).
 bool local_fusable(const Dims& dm) {
   return dm.ls == FK && dm.n_local >= 1 && dm.w >= FK * dm.n_local && dm.q0 % FQ == 0;
 }
 
 hipError_t launch_flash_fast(const Dims& dm, const void* q, const void* k, const void* v, const uint8_t* vid,
-                             float* swa32, void* swa_bf, void* text, void* ws, hipStream_t s, void* local_ml,
+                             void* swa_bf, void* text, void* ws, hipStream_t s, void* local_ml,
                              void* local_o) {
   if (dm.Tq <= 0 || dm.B <= 0) return hipSuccess;
   const int ntq = (int)((dm.Tq + FQ - 1) / FQ);
@@ -437,14 +431,13 @@ hipError_t launch_flash_fast(const Dims& dm, const void* q, const void* k, const
   if ((local_ml != nullptr) != (local_o != nullptr) || (local_ml && !local_fusable(dm))) return hipErrorInvalidValue;
   fo.lml = (float2*)local_ml;
   fo.lo = (unsigned char*)local_o;
-  fo.swa32 = swa32;
   fo.swa_bf = (bf16*)swa_bf;
   fo.text = (bf16*)text;
   fo.nsplit = (text && vid) ? flash_nsplit(dm) : 1;
   fo.max_split = fo.nsplit > 1 ? (ntq < MAX_SPLIT_TILES ? ntq : MAX_SPLIT_TILES) : 0;
   fo.part = (float*)ws;
   if (fo.nsplit > 1 && !ws) fo.nsplit = 1, fo.max_split = 0;
-  const int do_swa = (swa32 || swa_bf || local_ml) ? 1 : 0;
+  const int do_swa = (swa_bf || local_ml) ? 1 : 0;
   const int do_text = text ? 1 : 0;
   if (!do_swa && !do_text) return hipSuccess;
   const int nhs = (dm.G + FW - 1) / FW;
